@@ -1,0 +1,305 @@
+#!/usr/bin/env python3
+"""Throughput of the row-reduce hot path on one MI355X, as achieved HBM GB/s.
+
+One step runs every large workload once, in this order, each on its own
+buffers with inputs already resident in HBM:
+
+  fused      fused residual add + RMSNorm, bf16 I/O, 8192 x 4096
+  rms_bf16   RMSNorm bf16, 8192 x 4096 (the fused workload's x and gamma)
+  sm_wave    softmax fp32 -> fp32, 16384 x 1024 (a wavefront per row)
+  sm_vocab   softmax bf16 -> fp32, 256 x 152064 (split row: stats + apply)
+  sm_causal  softmax fp32 -> fp32, 28*4096 x 4096, causal -inf mask (a workgroup per row)
+
+value = algorithmic bytes of one step (each input read once, each output
+written once, gamma once) / measured time of one step.  The 3.76 GB causal
+softmax in every step pushes the other workloads' buffers out of the 256 MB
+last-level cache between their repetitions, so every kernel starts cold.
+The fused op updates its residual in place each step; that changes the
+values, not the work.
+
+Per-kernel durations come from HIP events recorded on the launch stream
+between the operations inside the timed region.  The roofline object is for
+the dominant operation (largest share of the step time).
+
+cpu_baseline: the fp64 CPU oracle, timed on the host cores on the first rows
+of every workload (a fixed fraction of each), reported in the same unit.
+"""
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "achieved HBM GB/s and % of MI355X peak, RMSNorm 8192x4096 bf16 + softmax rows"
+PEAK_HBM_GBS = 8000.0   # MI355X HBM3E, published
+KERNEL_SOURCES = ("row_reduction_rmsnorm_amd/csrc/rr_kernels.hip",
+                  "row_reduction_rmsnorm_amd/csrc/rr_device.h",
+                  "row_reduction_rmsnorm_amd/csrc/rr_api.cpp")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_sm_causal_softmax_block.json")
+
+OPS = ("fused", "rms_bf16", "sm_wave", "sm_vocab", "sm_causal")
+
+
+def kernel_source_sha():
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def algorithmic_bytes(op, M, N):
+    """Read each input once, write each output once, gamma once."""
+    if op == "fused":
+        return 4 * M * N * 2 + N * 2
+    if op == "rms_bf16":
+        return 2 * M * N * 2 + N * 2
+    if op == "rms_f32":
+        return 2 * M * N * 4 + N * 4
+    if op == "sm_wave" or op == "sm_causal":
+        return M * N * (4 + 4)
+    if op == "sm_vocab":
+        return M * N * (2 + 4)
+    raise KeyError(op)
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def setup(torch, dev):
+    import workloads
+    import row_reduction_rmsnorm_amd as rr
+    bufs = {}
+    t0 = time.time()
+    w = workloads.make("fused")
+    x = w.arrays["x"].to(dev)
+    bufs["fused"] = dict(x=x, r=w.arrays["residual"].to(dev), g=w.arrays["gamma"].to(dev),
+                         y=torch.empty_like(x), M=w.M, N=w.N, eps=w.eps,
+                         r0=w.arrays["residual"])
+    bufs["rms_bf16"] = dict(x=x, g=bufs["fused"]["g"], y=torch.empty_like(x), M=w.M, N=w.N,
+                            eps=w.eps)
+    for name in ("sm_wave", "sm_vocab", "sm_causal"):
+        w = workloads.make(name)
+        xs = w.arrays["x"].to(dev)
+        y = torch.empty(xs.shape, dtype=torch.float32, device=dev)
+        bufs[name] = dict(x=xs, y=y, ws=rr.softmax_workspace(xs, torch.float32), M=w.M, N=w.N)
+    torch.cuda.synchronize()
+    log(f"[bench] inputs generated and resident in HBM ({time.time() - t0:.1f} s)")
+    return bufs
+
+
+def make_ops(rr, bufs):
+    b = bufs
+    return {
+        "fused": lambda: rr.rr_fused_add_rmsnorm(b["fused"]["y"], b["fused"]["r"], b["fused"]["x"],
+                                                 b["fused"]["g"], b["fused"]["eps"]),
+        "rms_bf16": lambda: rr.rr_rmsnorm(b["rms_bf16"]["y"], b["rms_bf16"]["x"],
+                                          b["rms_bf16"]["g"], b["rms_bf16"]["eps"]),
+        "sm_wave": lambda: rr.rr_softmax_rows(b["sm_wave"]["y"], b["sm_wave"]["x"], b["sm_wave"]["ws"]),
+        "sm_vocab": lambda: rr.rr_softmax_rows(b["sm_vocab"]["y"], b["sm_vocab"]["x"], b["sm_vocab"]["ws"]),
+        "sm_causal": lambda: rr.rr_softmax_rows(b["sm_causal"]["y"], b["sm_causal"]["x"],
+                                                b["sm_causal"]["ws"]),
+    }
+
+
+def sanity(torch, bufs):
+    """Cheap checks after the first step (torch arithmetic, no oracle): the new
+    residual is bf16(x + r0) and softmax rows sum to one."""
+    f = bufs["fused"]
+    rows = slice(0, 64)
+    expect = (f["x"][rows].cpu() + f["r0"][rows])
+    assert torch.equal(f["r"][rows].cpu(), expect), "fused residual mismatch"
+    for name in ("sm_wave", "sm_vocab", "sm_causal"):
+        s = bufs[name]["y"][:64].double().sum(dim=1)
+        err = float((s - 1).abs().max())
+        assert err < 1e-4, f"{name}: row sums off by {err}"
+
+
+def cpu_baseline(bufs, fraction):
+    """Time the fp64 oracle on the first ceil(M * fraction) rows of every
+    workload; returns the equivalent GB/s over the same algorithmic bytes."""
+    import numpy as np
+    import oracle
+    total_t = 0.0
+    total_b = 0
+    parts = []
+    for name in OPS:
+        b = bufs[name]
+        M, N = b["M"], b["N"]
+        m = max(1, int(math.ceil(M * fraction)))
+        xs = b["x"][:m].float().cpu().double().numpy()
+        if name == "fused":
+            rs = b["r0"][:m].double().numpy()
+            g = b["g"].float().cpu().double().numpy()
+            t0 = time.perf_counter()
+            oracle.fused_add_rmsnorm(xs, rs, g, b["eps"], "bf16")
+            dt = time.perf_counter() - t0
+        elif name == "rms_bf16":
+            g = b["g"].float().cpu().double().numpy()
+            t0 = time.perf_counter()
+            oracle.rmsnorm(xs, g, b["eps"])
+            dt = time.perf_counter() - t0
+        else:
+            t0 = time.perf_counter()
+            oracle.softmax(xs)
+            dt = time.perf_counter() - t0
+        nb = algorithmic_bytes(name, m, N)
+        total_t += dt
+        total_b += nb
+        parts.append(f"{name} {m}/{M} rows")
+        del xs
+    return {
+        "value": round(total_b / total_t / 1e9, 3),
+        "unit": "GB/s",
+        "cores": oracle.num_threads(),
+        "kind": "oracle",
+        "sample": f"first {fraction:.4g} of the rows of every workload ({', '.join(parts)}); "
+                  f"{total_b / 1e9:.3f} GB algorithmic, {total_t:.2f} s on the host",
+        "seconds": round(total_t, 3),
+    }
+
+
+def traffic_for(per_launch_ok):
+    """HBM bytes per launch of the dominant kernel from the committed
+    rocprofv3 FETCH_SIZE / WRITE_SIZE summary, if it was taken on the kernel
+    sources as they are now."""
+    if not per_launch_ok or not os.path.exists(TRAFFIC_FILE):
+        return None
+    with open(TRAFFIC_FILE) as f:
+        t = json.load(f)
+    if t.get("kernel_source_sha") != kernel_source_sha():
+        return None
+    return t.get("traffic_bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--cpu-fraction", type=float, default=1.0 / 8)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run a plain 512 MiB device copy (for counter calibration)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}): "
+              "rows are independent, so a multi-GPU run is the same kernel on each GPU's share of "
+              "the rows with no exchange; it is not part of this build.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import row_reduction_rmsnorm_amd as rr
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    rr.lib()
+    bufs = setup(torch, dev)
+    ops = make_ops(rr, bufs)
+
+    if args.calibrate_copy:
+        src = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    # warmup (the first step is checked)
+    for i in range(args.warmup):
+        for name in OPS:
+            ops[name]()
+        if i == 0:
+            torch.cuda.synchronize()
+            sanity(torch, bufs)
+    torch.cuda.synchronize()
+
+    K = args.steps
+    stream = torch.cuda.current_stream(dev)
+    marks = [[torch.cuda.Event(enable_timing=True) for _ in range(len(OPS) + 1)] for _ in range(K)]
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for k in range(K):
+        marks[k][0].record(stream)
+        for j, name in enumerate(OPS):
+            ops[name]()
+            marks[k][j + 1].record(stream)
+    end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(end)
+    ms_step = total_ms / K
+
+    per_op_ms = {name: sum(marks[k][j].elapsed_time(marks[k][j + 1]) for k in range(K)) / K
+                 for j, name in enumerate(OPS)}
+    step_bytes = sum(algorithmic_bytes(n, bufs[n]["M"], bufs[n]["N"]) for n in OPS)
+    value = step_bytes / (ms_step * 1e-3) / 1e9
+
+    breakdown = {}
+    for name in OPS:
+        nb = algorithmic_bytes(name, bufs[name]["M"], bufs[name]["N"])
+        t = per_op_ms[name]
+        breakdown[name] = {"M": bufs[name]["M"], "N": bufs[name]["N"], "bytes": nb,
+                           "us": round(t * 1e3, 2), "GBps": round(nb / (t * 1e-3) / 1e9, 1),
+                           "frac_peak": round(nb / (t * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                           "rows_per_s": round(bufs[name]["M"] / (t * 1e-3), 1)}
+    dom = max(OPS, key=lambda n: per_op_ms[n])
+    dom_bytes = algorithmic_bytes(dom, bufs[dom]["M"], bufs[dom]["N"])
+    achieved = dom_bytes / (per_op_ms[dom] * 1e-3) / 1e9
+    plan = rr.rr_query_plan(rr.RR_OP_SOFTMAX, bufs[dom]["M"], bufs[dom]["N"], rr.RR_F32, rr.RR_F32) \
+        if dom.startswith("sm_") else None
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(achieved / PEAK_HBM_GBS, 4),
+                "traffic": traffic_for(dom == "sm_causal"),
+                "kernel": dom, "bytes_per_launch": dom_bytes,
+                "us_per_launch": round(per_op_ms[dom] * 1e3, 2),
+                "plan": plan["variant_name"] if plan else None}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle on a sample ...")
+        cpu = cpu_baseline(bufs, args.cpu_fraction)
+
+    line = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": "one step = fused add+RMSNorm bf16 8192x4096 + RMSNorm bf16 8192x4096 + "
+                        "softmax f32 16384x1024 + softmax bf16->f32 256x152064 (split row) + "
+                        "causal softmax f32 114688x4096",
+            "io_dtypes": "bf16 norms; softmax f32->f32, bf16->f32",
+            "bytes_per_step": step_bytes,
+            "parallelism": "single GPU",
+        },
+        "pct_of_peak": round(100.0 * value / PEAK_HBM_GBS, 2),
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "breakdown": breakdown,
+        "device": torch.cuda.get_device_name(dev),
+        "kernel_source_sha": kernel_source_sha(),
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,214 @@
+/*
+ * rowreduce.h -- C ABI of librowreduce.so: row-wise reduce-then-rescale
+ * kernels for AMD MI355X (gfx950, CDNA4).
+ *
+ * Operations (each row of a row-major [M, N] matrix is independent):
+ *   rr_rmsnorm            y = x * rsqrt(mean(x^2) + eps) * gamma
+ *   rr_fused_add_rmsnorm  residual <- residual + x;  y = rmsnorm(residual) * gamma
+ *   rr_softmax_rows       y = exp(x - m) / d with the online normaliser (m, d)
+ *
+ * Sources (web pages, cited by title and section):
+ *   [P1] "两个融合算子：RMSNorm 与 online softmax" (daleiyang.github.io)
+ *   [P2] "GPU Kernel 工程（04）：共享内存与 reduction——softmax、LayerNorm 与
+ *        online softmax" (arganzheng.life)
+ *   [P4] "Softmax 与归一化" (anrans.github.io ai-infra-handbooks)
+ *   [P5] "RMSNorm、Softmax 与在线归约" (notes.kuangjux.top)
+ *
+ * Conventions shared by every entry point
+ *   - Memory: every data pointer is a DEVICE pointer owned by the caller
+ *     (allocated on the device that is current when the call is made).  The
+ *     library allocates nothing, frees nothing and keeps no per-call state.
+ *   - Layout: row-major and contiguous; element (i, j) of an [M, N] matrix is
+ *     at offset i * N + j; gamma is a vector of N (or H) elements.
+ *   - dtype: RR_F32 (IEEE binary32) or RR_BF16 (bfloat16).  All arithmetic is
+ *     fp32; bf16 inputs widen exactly and outputs round to nearest even once.
+ *   - Streams: `stream` is a hipStream_t (NULL = the null stream).  Calls are
+ *     asynchronous: they enqueue kernels and return; the caller synchronises.
+ *     Same-stream order is the only ordering the library relies on.
+ *   - Errors: arguments are checked on the host before anything is enqueued;
+ *     a failed check returns a non-zero rr_status and enqueues nothing.
+ *     M == 0 is a successful no-op.  An empty row (N or H < 1) is the
+ *     caller's error ([P1] section "四、数值上到底安不安全": the normaliser is
+ *     only defined for a non-empty row).  A failure reported by the HIP
+ *     runtime when launching returns RR_ERR_HIP.  rr_last_error_message()
+ *     gives the detail for the calling thread.
+ *   - Alignment: rows whose pointers are 16-byte aligned and whose width is a
+ *     multiple of 4 (fp32) or 8 (bf16) elements use 16-byte vector accesses;
+ *     anything else runs a scalar path with the same results up to rounding
+ *     order.  Any N >= 1 is accepted.
+ *   - Determinism: a given (op, M, N, dtypes, alignment) always runs the same
+ *     kernel with the same reduction order, so results are bitwise
+ *     reproducible run to run; no floating-point atomics are used.
+ */
+#ifndef ROWREDUCE_H
+#define ROWREDUCE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum rr_dtype {
+  RR_F32 = 0,
+  RR_BF16 = 1
+} rr_dtype;
+
+typedef enum rr_status {
+  RR_OK = 0,
+  RR_ERR_INVALID_ARG = 1,  /* null pointer, bad size, unknown dtype, bad aliasing */
+  RR_ERR_UNSUPPORTED = 2,  /* valid request this build cannot run (size limits, forced variant) */
+  RR_ERR_WORKSPACE = 3,    /* workspace missing or smaller than rr_softmax_rows_workspace_bytes */
+  RR_ERR_HIP = 4           /* the HIP runtime reported an error */
+} rr_status;
+
+/*
+ * rr_rmsnorm -- RMSNorm of each row.
+ *   y[i, j] = x[i, j] * r_i * gamma[j],  r_i = 1 / sqrt( (1/H) * sum_j x[i, j]^2 + eps )
+ * eps is added to the mean square inside the square root and nothing is
+ * subtracted from x ([P5] section "RMSNorm 归约什么"; [P2] sections 二.1 and
+ * 八.1; [P4] section "LayerNorm 与 RMSNorm").
+ *   y      [M, H] output, dtype `dtype`; may be the same pointer as x (in place)
+ *   x      [M, H] input, dtype `dtype`
+ *   gamma  [H] scale, dtype `dtype`
+ *   M >= 0 rows, H >= 1 elements per row (H < 2^31), eps >= 0 finite
+ * The sum of squares is accumulated in fp32.  Returns RR_ERR_INVALID_ARG for
+ * null pointers (M > 0), M < 0, H < 1, a bad eps, an unknown dtype, or y
+ * overlapping x without being equal to it, or gamma overlapping y.
+ */
+rr_status rr_rmsnorm(void* y, const void* x, const void* gamma, int64_t M, int64_t H,
+                     float eps, rr_dtype dtype, void* stream);
+
+/*
+ * rr_fused_add_rmsnorm -- residual add followed by RMSNorm, in one pass.
+ *   h[i, j]        = round_dtype( x[i, j] + residual[i, j] )   (sum in fp32)
+ *   residual[i, j] <- h[i, j]
+ *   y[i, j]        = h[i, j] * r_i * gamma[j],  r_i from the stored h
+ * ([P4] section "算子融合：fused_add_rms_norm"; [P2] section 八.3: read x and
+ * the residual once, write the new residual and the normalised output.)
+ * y is computed from the residual as stored, so the result equals an add
+ * followed by rr_rmsnorm.
+ *   y         [M, H] output; may be the same pointer as x
+ *   residual  [M, H] input and output (updated in place)
+ *   x         [M, H] input
+ *   gamma     [H]
+ * All four have dtype `dtype`.  residual must not overlap x, y or gamma;
+ * y may equal x but must not partly overlap it.  Other errors as rr_rmsnorm.
+ */
+rr_status rr_fused_add_rmsnorm(void* y, void* residual, const void* x, const void* gamma,
+                               int64_t M, int64_t H, float eps, rr_dtype dtype,
+                               void* stream);
+
+/*
+ * rr_softmax_rows_workspace_bytes -- device workspace rr_softmax_rows needs
+ * for this shape (0 when the chosen kernel needs none).  Very long rows with
+ * few rows are split over several workgroups; each writes its chunk's
+ * (m, d) pair (8 bytes) to the workspace and a second kernel merges them
+ * ([P4] section "练习", the vocabulary-split exercise).  Host-only; returns 0
+ * for invalid arguments.
+ */
+size_t rr_softmax_rows_workspace_bytes(int64_t M, int64_t N, rr_dtype in_dtype,
+                                       rr_dtype out_dtype);
+
+/*
+ * rr_softmax_rows -- softmax of each row.
+ *   m_i = max_j x[i, j],  d_i = sum_j exp(x[i, j] - m_i),  y[i, j] = exp(x[i, j] - m_i) / d_i
+ * computed with the online normaliser: partial pairs (m, d) over parts of a
+ * row combine by (m1,d1) (+) (m2,d2) = (m, d1 e^(m1-m) + d2 e^(m2-m)),
+ * m = max(m1, m2), identity (-inf, 0) ([P1] sections "二、递推式怎么来的" and
+ * "三、结合律"; [P5] sections "Online Softmax 为什么要重缩放旧的和" and
+ * "从逐元素更新到合并两个 tile"; [P2] section 七.3).
+ *   y          [M, N] output, dtype out_dtype
+ *   x          [M, N] input, dtype in_dtype; entries may be -inf (masked);
+ *              +inf and NaN inputs are not supported
+ *   workspace  device buffer of at least rr_softmax_rows_workspace_bytes(M, N,
+ *              in_dtype, out_dtype) bytes, 8-byte aligned (may be NULL when
+ *              that size is 0); contents on entry are ignored
+ * Masked entries produce exactly 0; a row whose entries are all -inf
+ * produces NaN everywhere (-inf - (-inf)).  In place (y == x) is allowed
+ * when in_dtype == out_dtype; otherwise x and y must not overlap.
+ * Returns RR_ERR_WORKSPACE when the workspace is needed and missing or too
+ * small; other errors as rr_rmsnorm.
+ */
+rr_status rr_softmax_rows(void* y, const void* x, int64_t M, int64_t N, rr_dtype in_dtype,
+                          rr_dtype out_dtype, void* workspace, size_t workspace_bytes,
+                          void* stream);
+
+/* Static English name of a status code ("RR_OK", ...). */
+const char* rr_status_string(rr_status status);
+
+/* Detail of the last non-OK status returned on the calling thread ("" if none). */
+const char* rr_last_error_message(void);
+
+/* ------------------------------------------------------------------------
+ * Dispatch introspection and diagnostics (host-only unless stated).
+ * ------------------------------------------------------------------------ */
+
+typedef enum rr_op {
+  RR_OP_RMSNORM = 0,
+  RR_OP_FUSED_ADD_RMSNORM = 1,
+  RR_OP_SOFTMAX = 2
+} rr_op;
+
+/* Kernel variants, chosen by row length ([P2] section 六; [P4] section
+ * "按行长度选择并行方式"):
+ *   WAVE  one 64-lane wavefront per row, row held in VGPRs (N <= 2048)
+ *   BLOCK one workgroup of up to 16 wavefronts per row, row held in VGPRs,
+ *         wavefront totals combined through LDS (N <= 32768)
+ *   SPLIT several workgroups per row, each writes its chunk's (m, d) to the
+ *         workspace; a second kernel merges them and normalises (softmax, long
+ *         rows with few rows)
+ *   LOOP  one workgroup per row streaming the row twice (any N, unaligned
+ *         rows, long rows with many rows) */
+typedef enum rr_variant {
+  RR_VARIANT_AUTO = 0,
+  RR_VARIANT_WAVE = 1,
+  RR_VARIANT_BLOCK = 2,
+  RR_VARIANT_SPLIT = 3,
+  RR_VARIANT_LOOP = 4
+} rr_variant;
+
+typedef struct rr_plan {
+  int32_t variant;          /* rr_variant actually used */
+  int32_t waves_per_row;    /* wavefronts cooperating on one row */
+  int32_t rows_per_group;   /* rows handled by one workgroup per step */
+  int32_t vecs_per_lane;    /* vector accesses per lane held in registers */
+  int32_t vec_elems;        /* elements per vector access (4 fp32, 8 bf16, 1 scalar) */
+  int32_t block_threads;    /* workgroup size */
+  int64_t chunks_per_row;   /* SPLIT: workgroups per row; otherwise 1 */
+  int64_t work_items;       /* workgroup-steps needed (rows / rows_per_group x chunks) */
+  size_t workspace_bytes;   /* SPLIT: M * chunks_per_row * 8; otherwise 0 */
+} rr_plan;
+
+/*
+ * The launch plan the library would use.  aligned16 != 0 states that every
+ * pointer of the call will be 16-byte aligned.  Honours the variant
+ * override below.  Returns RR_ERR_INVALID_ARG / RR_ERR_UNSUPPORTED as the
+ * corresponding call would.
+ */
+rr_status rr_query_plan(rr_op op, int64_t M, int64_t N, rr_dtype in_dtype, rr_dtype out_dtype,
+                        int aligned16, rr_plan* plan);
+
+/* Process-wide forced variant for tests and measurement (RR_VARIANT_AUTO
+ * restores automatic choice).  A forced variant that cannot run a shape makes
+ * that call return RR_ERR_UNSUPPORTED.  Not thread-safe with respect to calls
+ * in flight on other threads. */
+rr_status rr_set_variant_override(rr_variant variant);
+
+/*
+ * Self-test of the wave64 all-reduce (device work; used by the test suite).
+ * kind 0: in and out hold count groups of 64 floats; every lane of a group
+ * receives the group's sum.  kind 1: the same with the maximum.  kind 2: in
+ * and out hold count groups of 128 floats, 64 m values then 64 d values;
+ * every lane receives the merge of the group's 64 (m, d) pairs.  One
+ * wavefront per group; count >= 1.
+ */
+rr_status rr_selftest_wave_allreduce(const float* in, float* out, int64_t count, int kind,
+                                     void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ROWREDUCE_H */

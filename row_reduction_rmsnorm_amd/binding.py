@@ -1,0 +1,279 @@
+"""ctypes binding of librowreduce.so (the C ABI declared in include/rowreduce.h).
+
+Argument marshalling only: every operation runs in the library's HIP kernels.
+PyTorch supplies device memory (tensors' data pointers) and the stream
+(``torch.cuda.current_stream().cuda_stream``).  There is no fallback: if the
+library is missing or cannot be loaded, importing it raises.
+"""
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "librowreduce.so")
+
+RR_F32 = 0
+RR_BF16 = 1
+F32 = RR_F32
+BF16 = RR_BF16
+
+RR_OK = 0
+RR_ERR_INVALID_ARG = 1
+RR_ERR_UNSUPPORTED = 2
+RR_ERR_WORKSPACE = 3
+RR_ERR_HIP = 4
+
+RR_OP_RMSNORM = 0
+RR_OP_FUSED_ADD_RMSNORM = 1
+RR_OP_SOFTMAX = 2
+
+RR_VARIANT_AUTO = 0
+RR_VARIANT_WAVE = 1
+RR_VARIANT_BLOCK = 2
+RR_VARIANT_SPLIT = 3
+RR_VARIANT_LOOP = 4
+VARIANT_NAMES = {0: "auto", 1: "wave", 2: "block", 3: "split", 4: "loop"}
+
+# Every function include/rowreduce.h declares.
+EXPORTS = (
+    "rr_rmsnorm", "rr_fused_add_rmsnorm", "rr_softmax_rows_workspace_bytes",
+    "rr_softmax_rows", "rr_status_string", "rr_last_error_message", "rr_query_plan",
+    "rr_set_variant_override", "rr_selftest_wave_allreduce",
+)
+
+
+class RowReduceError(RuntimeError):
+    def __init__(self, status, message):
+        super().__init__(message)
+        self.status = status
+
+
+class rr_plan(ctypes.Structure):
+    _fields_ = [
+        ("variant", ctypes.c_int32),
+        ("waves_per_row", ctypes.c_int32),
+        ("rows_per_group", ctypes.c_int32),
+        ("vecs_per_lane", ctypes.c_int32),
+        ("vec_elems", ctypes.c_int32),
+        ("block_threads", ctypes.c_int32),
+        ("chunks_per_row", ctypes.c_int64),
+        ("work_items", ctypes.c_int64),
+        ("workspace_bytes", ctypes.c_size_t),
+    ]
+
+    def as_dict(self):
+        d = {name: getattr(self, name) for name, _ in self._fields_}
+        d["variant_name"] = VARIANT_NAMES.get(self.variant, "?")
+        return d
+
+
+_LIB = None
+
+
+def lib():
+    """The loaded library (built in-tree on first use if it is not there)."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    if not os.path.exists(LIB_PATH):
+        from . import build as _build
+        _build.build()
+    try:
+        L = ctypes.CDLL(LIB_PATH)
+    except OSError as e:
+        raise ImportError(f"cannot load {LIB_PATH}: {e}") from e
+    vp, i64, f32, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_float, ctypes.c_int
+    L.rr_rmsnorm.argtypes = [vp, vp, vp, i64, i64, f32, i32, vp]
+    L.rr_fused_add_rmsnorm.argtypes = [vp, vp, vp, vp, i64, i64, f32, i32, vp]
+    L.rr_softmax_rows_workspace_bytes.argtypes = [i64, i64, i32, i32]
+    L.rr_softmax_rows_workspace_bytes.restype = ctypes.c_size_t
+    L.rr_softmax_rows.argtypes = [vp, vp, i64, i64, i32, i32, vp, ctypes.c_size_t, vp]
+    L.rr_status_string.argtypes = [i32]
+    L.rr_status_string.restype = ctypes.c_char_p
+    L.rr_last_error_message.argtypes = []
+    L.rr_last_error_message.restype = ctypes.c_char_p
+    L.rr_query_plan.argtypes = [i32, i64, i64, i32, i32, i32, ctypes.POINTER(rr_plan)]
+    L.rr_set_variant_override.argtypes = [i32]
+    L.rr_selftest_wave_allreduce.argtypes = [vp, vp, i64, i32, vp]
+    for f in ("rr_rmsnorm", "rr_fused_add_rmsnorm", "rr_softmax_rows", "rr_query_plan",
+              "rr_set_variant_override", "rr_selftest_wave_allreduce"):
+        getattr(L, f).restype = i32
+    _LIB = L
+    return L
+
+
+def status_string(status: int) -> str:
+    return lib().rr_status_string(int(status)).decode()
+
+
+def last_error_message() -> str:
+    return lib().rr_last_error_message().decode()
+
+
+def check(status: int, what: str = "") -> None:
+    if status != RR_OK:
+        raise RowReduceError(status, f"{what}: {status_string(status)}: {last_error_message()}")
+
+
+# ----------------------------------------------------------------------------
+# raw C-ABI calls (integers for pointers and streams)
+# ----------------------------------------------------------------------------
+
+def raw_rmsnorm(y, x, gamma, M, H, eps, dtype, stream):
+    return lib().rr_rmsnorm(y, x, gamma, M, H, eps, dtype, stream)
+
+
+def raw_fused_add_rmsnorm(y, residual, x, gamma, M, H, eps, dtype, stream):
+    return lib().rr_fused_add_rmsnorm(y, residual, x, gamma, M, H, eps, dtype, stream)
+
+
+def raw_softmax_rows(y, x, M, N, in_dtype, out_dtype, workspace, workspace_bytes, stream):
+    return lib().rr_softmax_rows(y, x, M, N, in_dtype, out_dtype, workspace, workspace_bytes,
+                                 stream)
+
+
+def rr_softmax_rows_workspace_bytes(M: int, N: int, in_dtype: int, out_dtype: int) -> int:
+    return int(lib().rr_softmax_rows_workspace_bytes(M, N, in_dtype, out_dtype))
+
+
+def rr_query_plan(op: int, M: int, N: int, in_dtype: int, out_dtype: int, aligned16: bool = True):
+    p = rr_plan()
+    check(lib().rr_query_plan(op, M, N, in_dtype, out_dtype, 1 if aligned16 else 0,
+                              ctypes.byref(p)), "rr_query_plan")
+    return p.as_dict()
+
+
+def rr_set_variant_override(variant: int) -> None:
+    check(lib().rr_set_variant_override(int(variant)), "rr_set_variant_override")
+
+
+# ----------------------------------------------------------------------------
+# tensor-level calls (marshalling only)
+# ----------------------------------------------------------------------------
+
+def _torch():
+    import torch
+    return torch
+
+
+def dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return RR_F32
+    if t.dtype == torch.bfloat16:
+        return RR_BF16
+    raise TypeError(f"unsupported dtype {t.dtype} (float32 or bfloat16)")
+
+
+def _stream_of(t, stream):
+    torch = _torch()
+    if stream is None:
+        return torch.cuda.current_stream(t.device).cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _need_cuda(*ts):
+    for t in ts:
+        if not t.is_cuda:
+            raise ValueError("tensors must live on a GPU device")
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+
+
+def _rows(t):
+    if t.dim() == 0:
+        raise ValueError("need at least one dimension")
+    n = t.shape[-1]
+    m = t.numel() // n if n else 0
+    return m, n
+
+
+def rr_rmsnorm(y, x, gamma, eps: float, stream=None) -> None:
+    """y = x * rsqrt(mean(x^2) + eps) * gamma over the last dimension."""
+    _need_cuda(y, x, gamma)
+    M, H = _rows(x)
+    if y.shape != x.shape or gamma.shape != (H,):
+        raise ValueError("y must match x and gamma must be [H]")
+    dt = dtype_code(x)
+    if dtype_code(y) != dt or dtype_code(gamma) != dt:
+        raise TypeError("x, y and gamma must share one dtype")
+    check(raw_rmsnorm(y.data_ptr(), x.data_ptr(), gamma.data_ptr(), M, H, float(eps), dt,
+                      _stream_of(x, stream)), "rr_rmsnorm")
+
+
+def rr_fused_add_rmsnorm(y, residual, x, gamma, eps: float, stream=None) -> None:
+    """residual <- residual + x (rounded to the dtype); y = rmsnorm(residual) * gamma."""
+    _need_cuda(y, residual, x, gamma)
+    M, H = _rows(x)
+    if y.shape != x.shape or residual.shape != x.shape or gamma.shape != (H,):
+        raise ValueError("y and residual must match x and gamma must be [H]")
+    dt = dtype_code(x)
+    if any(dtype_code(t) != dt for t in (y, residual, gamma)):
+        raise TypeError("all tensors must share one dtype")
+    check(raw_fused_add_rmsnorm(y.data_ptr(), residual.data_ptr(), x.data_ptr(),
+                                gamma.data_ptr(), M, H, float(eps), dt,
+                                _stream_of(x, stream)), "rr_fused_add_rmsnorm")
+
+
+def rr_softmax_rows(y, x, workspace=None, stream=None) -> None:
+    """Row softmax of x into y over the last dimension (y may be x when dtypes match).
+
+    workspace: a uint8 device tensor of at least rr_softmax_rows_workspace_bytes
+    bytes when that is non-zero."""
+    _need_cuda(y, x)
+    M, N = _rows(x)
+    if y.shape != x.shape:
+        raise ValueError("y must match x")
+    din, dout = dtype_code(x), dtype_code(y)
+    ws_ptr, ws_bytes = None, 0
+    if workspace is not None:
+        _need_cuda(workspace)
+        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    check(raw_softmax_rows(y.data_ptr(), x.data_ptr(), M, N, din, dout, ws_ptr, ws_bytes,
+                           _stream_of(x, stream)), "rr_softmax_rows")
+
+
+def rr_selftest_wave_allreduce(out, inp, kind: int, stream=None) -> None:
+    _need_cuda(out, inp)
+    per = 128 if kind == 2 else 64
+    if inp.numel() % per or out.numel() != inp.numel():
+        raise ValueError("bad self-test sizes")
+    check(lib().rr_selftest_wave_allreduce(inp.data_ptr(), out.data_ptr(), inp.numel() // per,
+                                           int(kind), _stream_of(inp, stream)),
+          "rr_selftest_wave_allreduce")
+
+
+# ----------------------------------------------------------------------------
+# allocating conveniences (outputs and workspace come from torch)
+# ----------------------------------------------------------------------------
+
+def rmsnorm(x, gamma, eps: float, out=None):
+    y = _torch().empty_like(x) if out is None else out
+    rr_rmsnorm(y, x, gamma, eps)
+    return y
+
+
+def fused_add_rmsnorm(x, residual, gamma, eps: float, out=None):
+    """Updates residual in place and returns y."""
+    y = _torch().empty_like(x) if out is None else out
+    rr_fused_add_rmsnorm(y, residual, x, gamma, eps)
+    return y
+
+
+def softmax_workspace(x, out_dtype):
+    torch = _torch()
+    M, N = _rows(x)
+    n = rr_softmax_rows_workspace_bytes(M, N, dtype_code(x),
+                                        RR_F32 if out_dtype == torch.float32 else RR_BF16)
+    return torch.empty(n, dtype=torch.uint8, device=x.device) if n else None
+
+
+def softmax_rows(x, out_dtype=None, out=None, workspace=None):
+    torch = _torch()
+    if out is None:
+        out = torch.empty(x.shape, dtype=out_dtype or x.dtype, device=x.device)
+    if workspace is None:
+        workspace = softmax_workspace(x, out.dtype)
+    rr_softmax_rows(out, x, workspace)
+    return out

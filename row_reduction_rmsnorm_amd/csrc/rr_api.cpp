@@ -1,0 +1,356 @@
+// C ABI of librowreduce.so: argument checks, kernel-variant choice and
+// launch sizing.  The arithmetic is all in rr_kernels.hip.
+//
+// Variant choice by row length follows [P2] "GPU Kernel 工程（04）" section 六
+// (a wavefront per row when the row fits a wavefront's registers, a workgroup
+// per row for thousands of elements) and [P4] "Softmax 与归一化" section
+// "按行长度选择并行方式" (several workgroups per row for very long rows with
+// few rows).  The thresholds are this library's: a wavefront holds up to 32
+// fp32 values per lane, a workgroup up to 16 wavefronts.
+#include <hip/hip_runtime.h>
+#include <stdarg.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <atomic>
+
+#include "rowreduce.h"
+#include "rr_launch.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+std::atomic<int> g_override{RR_VARIANT_AUTO};
+
+rr_status fail(rr_status s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+rr_status fail(rr_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+bool valid_dtype(int d) { return d == RR_F32 || d == RR_BF16; }
+size_t dtype_size(int d) { return d == RR_F32 ? 4 : 2; }
+int vec_width(int d) { return d == RR_F32 ? 4 : 8; }  // elements per 16 bytes
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// [a, a + na) and [b, b + nb) share a byte.
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t pa = reinterpret_cast<uintptr_t>(a);
+  const uintptr_t pb = reinterpret_cast<uintptr_t>(b);
+  return pa < pb + nb && pb < pa + na;
+}
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+int pow2_at_least(int64_t v) {
+  int p = 1;
+  while (p < v) p <<= 1;
+  return p;
+}
+
+constexpr int64_t kMaxN = (int64_t)1 << 30;  // keeps every in-row index in int32
+constexpr int kWaveMaxFloats = 32;           // per-lane register budget (fp32 values)
+constexpr int kBlockFloats = 16;             // preferred per-lane share in a block
+constexpr int kMaxWaves = rr::kMaxWavesPerGroup;
+constexpr int kWaveRowsPerGroup = 4;         // rows per 256-thread workgroup (WAVE)
+constexpr int64_t kSplitMaxRows = 1024;      // SPLIT only below this many rows
+
+void plan_wave(rr_plan* p, int vec, int64_t nvec) {
+  p->variant = RR_VARIANT_WAVE;
+  p->vec_elems = vec;
+  p->waves_per_row = 1;
+  p->rows_per_group = kWaveRowsPerGroup;
+  p->vecs_per_lane = pow2_at_least(ceil_div(nvec, 64));
+  p->block_threads = 64 * kWaveRowsPerGroup;
+}
+
+// Register budget per lane, in fp32 values held for the row: softmax keeps
+// one array (x, then e_i), the fused norm two (x and the residual) plus gamma,
+// so the norms stop at 16 values per lane and longer rows stream (LOOP).
+int wave_max_floats(rr_op op) { return op == RR_OP_SOFTMAX ? kWaveMaxFloats : kBlockFloats; }
+
+bool wave_fits(rr_op op, int vec, int64_t nvec) { return nvec <= 64 * (wave_max_floats(op) / vec); }
+
+// Workgroup-per-row: NV vectors per lane giving 16 fp32 values per lane;
+// softmax may double that once if the row needs more than 16 wavefronts.
+bool plan_block(rr_op op, rr_plan* p, int vec, int64_t nvec) {
+  const int max_nv = (op == RR_OP_SOFTMAX ? 2 : 1) * kBlockFloats / vec;
+  for (int nv = kBlockFloats / vec; nv <= max_nv; nv *= 2) {
+    const int64_t wpr = ceil_div(nvec, 64 * (int64_t)nv);
+    if (wpr <= kMaxWaves) {
+      p->variant = RR_VARIANT_BLOCK;
+      p->vec_elems = vec;
+      p->waves_per_row = (int32_t)wpr;
+      p->rows_per_group = 1;
+      p->vecs_per_lane = nv;
+      p->block_threads = (int32_t)(64 * wpr);
+      return true;
+    }
+  }
+  return false;
+}
+
+void plan_split(rr_plan* p, int vec, int64_t nvec) {
+  p->variant = RR_VARIANT_SPLIT;
+  p->vec_elems = vec;
+  p->waves_per_row = 4;
+  p->rows_per_group = 1;
+  p->vecs_per_lane = kBlockFloats / vec;
+  p->block_threads = 256;
+  p->chunks_per_row = ceil_div(nvec, 256 * (int64_t)p->vecs_per_lane);
+}
+
+void plan_loop(rr_plan* p, int vec, int64_t nvec) {
+  p->variant = RR_VARIANT_LOOP;
+  p->vec_elems = vec;
+  p->waves_per_row = nvec > 4096 ? 16 : 4;
+  p->rows_per_group = 1;
+  p->vecs_per_lane = 1;
+  p->block_threads = 64 * p->waves_per_row;
+}
+
+// Host-only plan.  `is_aligned`: every pointer of the call is 16-byte aligned.
+rr_status make_plan(rr_op op, int64_t M, int64_t N, int din, int dout, bool is_aligned,
+                    rr_plan* p) {
+  memset(p, 0, sizeof(*p));
+  if (op != RR_OP_RMSNORM && op != RR_OP_FUSED_ADD_RMSNORM && op != RR_OP_SOFTMAX)
+    return fail(RR_ERR_INVALID_ARG, "unknown op %d", (int)op);
+  if (!valid_dtype(din) || !valid_dtype(dout))
+    return fail(RR_ERR_INVALID_ARG, "unknown dtype (%d, %d)", din, dout);
+  if (op != RR_OP_SOFTMAX && din != dout)
+    return fail(RR_ERR_INVALID_ARG, "RMSNorm input and output dtypes must match");
+  if (M < 0) return fail(RR_ERR_INVALID_ARG, "M = %lld < 0", (long long)M);
+  if (N < 1) return fail(RR_ERR_INVALID_ARG, "row width %lld < 1 (empty rows have no statistic)", (long long)N);
+  if (N > kMaxN) return fail(RR_ERR_UNSUPPORTED, "row width %lld > 2^30", (long long)N);
+
+  const int vw = vec_width(din);
+  const int vec = (is_aligned && N % vw == 0) ? vw : 1;
+  const int64_t nvec = N / vec;
+  const int forced = g_override.load(std::memory_order_relaxed);
+
+  bool ok = false;
+  switch (forced) {
+    case RR_VARIANT_AUTO:
+      if (vec == 1) {
+        plan_loop(p, vec, nvec);
+      } else if (wave_fits(op, vec, nvec)) {
+        plan_wave(p, vec, nvec);
+      } else if (plan_block(op, p, vec, nvec)) {
+      } else if (op == RR_OP_SOFTMAX && M < kSplitMaxRows) {
+        plan_split(p, vec, nvec);
+      } else {
+        plan_loop(p, vec, nvec);
+      }
+      ok = true;
+      break;
+    case RR_VARIANT_WAVE:
+      ok = vec > 1 && wave_fits(op, vec, nvec);
+      if (ok) plan_wave(p, vec, nvec);
+      break;
+    case RR_VARIANT_BLOCK:
+      ok = vec > 1 && plan_block(op, p, vec, nvec);
+      break;
+    case RR_VARIANT_SPLIT:
+      ok = vec > 1 && op == RR_OP_SOFTMAX;
+      if (ok) plan_split(p, vec, nvec);
+      break;
+    case RR_VARIANT_LOOP:
+      plan_loop(p, vec, nvec);
+      ok = true;
+      break;
+    default:
+      break;
+  }
+  if (!ok) {
+    return fail(RR_ERR_UNSUPPORTED, "forced variant %d cannot run op %d with N = %lld (vector width %d)",
+                forced, (int)op, (long long)N, vec);
+  }
+  if (p->chunks_per_row == 0) p->chunks_per_row = 1;
+  if (p->variant == RR_VARIANT_SPLIT) {
+    if (p->chunks_per_row > (int64_t)1 << 30) return fail(RR_ERR_UNSUPPORTED, "too many chunks");
+    p->work_items = M * p->chunks_per_row;
+    p->workspace_bytes = (size_t)M * (size_t)p->chunks_per_row * 8u;
+  } else {
+    p->work_items = ceil_div(M, p->rows_per_group);
+  }
+  return RR_OK;
+}
+
+// Grid size: one workgroup per work item, optionally capped at a multiple of
+// the number of workgroups the device can hold at once (a persistent grid
+// walking the remaining rows).  RR_GRID_WAVES=<k> (read once) sets the cap to
+// k full-residency waves of workgroups; 0 or unset means no cap.
+int grid_waves_setting() {
+  static const int v = [] {
+    const char* e = getenv("RR_GRID_WAVES");
+    return e ? atoi(e) : 0;
+  }();
+  return v;
+}
+
+int device_cus() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int v = cache[dev].load(std::memory_order_relaxed);
+  if (v == 0) {
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0)
+      v = 256;
+    cache[dev].store(v, std::memory_order_relaxed);
+  }
+  return v;
+}
+
+int64_t grid_for(const rr_plan& p) {
+  int64_t g = p.work_items;
+  const int waves = grid_waves_setting();
+  if (waves > 0) {
+    const int64_t per_cu = 2048 / p.block_threads > 0 ? 2048 / p.block_threads : 1;
+    const int64_t cap = (int64_t)device_cus() * per_cu * waves;
+    if (g > cap) g = cap;
+  }
+  const int64_t kMaxGrid = 0x7fffffffLL;
+  return g > kMaxGrid ? kMaxGrid : g;
+}
+
+rr_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return RR_OK;
+  return fail(RR_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool valid_eps(float eps) { return eps >= 0.0f && eps <= 3.0e38f; }
+
+rr_status norm_entry(bool fused, void* y, void* residual, const void* x, const void* gamma,
+                     int64_t M, int64_t H, float eps, rr_dtype dtype, void* stream) {
+  g_err[0] = '\0';
+  const char* name = fused ? "rr_fused_add_rmsnorm" : "rr_rmsnorm";
+  if (!valid_dtype(dtype)) return fail(RR_ERR_INVALID_ARG, "%s: unknown dtype %d", name, (int)dtype);
+  if (M < 0) return fail(RR_ERR_INVALID_ARG, "%s: M = %lld < 0", name, (long long)M);
+  if (H < 1) return fail(RR_ERR_INVALID_ARG, "%s: H = %lld < 1", name, (long long)H);
+  if (!valid_eps(eps)) return fail(RR_ERR_INVALID_ARG, "%s: eps must be finite and >= 0", name);
+  if (M == 0) return RR_OK;
+  if (!y || !x || !gamma || (fused && !residual))
+    return fail(RR_ERR_INVALID_ARG, "%s: null pointer", name);
+  if (H > kMaxN) return fail(RR_ERR_UNSUPPORTED, "%s: H = %lld > 2^30", name, (long long)H);
+  const size_t es = dtype_size(dtype);
+  if ((uint64_t)M > (uint64_t)(SIZE_MAX / 8) / (uint64_t)H)
+    return fail(RR_ERR_INVALID_ARG, "%s: M * H overflows", name);
+  const size_t bytes = (size_t)M * (size_t)H * es;
+  const size_t gbytes = (size_t)H * es;
+  if (y != x && overlaps(y, bytes, x, bytes))
+    return fail(RR_ERR_INVALID_ARG, "%s: y partly overlaps x", name);
+  if (overlaps(gamma, gbytes, y, bytes)) return fail(RR_ERR_INVALID_ARG, "%s: gamma overlaps y", name);
+  if (fused) {
+    if (overlaps(residual, bytes, x, bytes) || overlaps(residual, bytes, y, bytes) ||
+        overlaps(residual, bytes, gamma, gbytes))
+      return fail(RR_ERR_INVALID_ARG, "%s: residual overlaps x, y or gamma", name);
+  }
+  const bool al = aligned16(y) && aligned16(x) && aligned16(gamma) && (!fused || aligned16(residual));
+  rr_plan p;
+  const rr_status st = make_plan(fused ? RR_OP_FUSED_ADD_RMSNORM : RR_OP_RMSNORM, M, H, dtype, dtype, al, &p);
+  if (st != RR_OK) return st;
+  const hipError_t e = rr::launch_norm(p, dtype, fused, y, residual, x, gamma, M, (int32_t)H, eps,
+                                       grid_for(p), static_cast<hipStream_t>(stream));
+  return hip_status(e, name);
+}
+
+}  // namespace
+
+extern "C" {
+
+rr_status rr_rmsnorm(void* y, const void* x, const void* gamma, int64_t M, int64_t H, float eps,
+                     rr_dtype dtype, void* stream) {
+  return norm_entry(false, y, nullptr, x, gamma, M, H, eps, dtype, stream);
+}
+
+rr_status rr_fused_add_rmsnorm(void* y, void* residual, const void* x, const void* gamma,
+                               int64_t M, int64_t H, float eps, rr_dtype dtype, void* stream) {
+  return norm_entry(true, y, residual, x, gamma, M, H, eps, dtype, stream);
+}
+
+size_t rr_softmax_rows_workspace_bytes(int64_t M, int64_t N, rr_dtype in_dtype,
+                                       rr_dtype out_dtype) {
+  rr_plan p;
+  if (make_plan(RR_OP_SOFTMAX, M, N, in_dtype, out_dtype, true, &p) != RR_OK) return 0;
+  return p.workspace_bytes;
+}
+
+rr_status rr_softmax_rows(void* y, const void* x, int64_t M, int64_t N, rr_dtype in_dtype,
+                          rr_dtype out_dtype, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+  g_err[0] = '\0';
+  if (!valid_dtype(in_dtype) || !valid_dtype(out_dtype))
+    return fail(RR_ERR_INVALID_ARG, "rr_softmax_rows: unknown dtype (%d, %d)", (int)in_dtype, (int)out_dtype);
+  if (M < 0) return fail(RR_ERR_INVALID_ARG, "rr_softmax_rows: M = %lld < 0", (long long)M);
+  if (N < 1) return fail(RR_ERR_INVALID_ARG, "rr_softmax_rows: N = %lld < 1", (long long)N);
+  if (M == 0) return RR_OK;
+  if (!y || !x) return fail(RR_ERR_INVALID_ARG, "rr_softmax_rows: null pointer");
+  if (N > kMaxN) return fail(RR_ERR_UNSUPPORTED, "rr_softmax_rows: N = %lld > 2^30", (long long)N);
+  if ((uint64_t)M > (uint64_t)(SIZE_MAX / 8) / (uint64_t)N)
+    return fail(RR_ERR_INVALID_ARG, "rr_softmax_rows: M * N overflows");
+  const size_t xb = (size_t)M * (size_t)N * dtype_size(in_dtype);
+  const size_t yb = (size_t)M * (size_t)N * dtype_size(out_dtype);
+  if (overlaps(x, xb, y, yb) && !(x == y && in_dtype == out_dtype))
+    return fail(RR_ERR_INVALID_ARG, "rr_softmax_rows: x and y overlap (in place needs equal pointers and dtypes)");
+  const bool al = aligned16(x) && aligned16(y);
+  rr_plan p;
+  const rr_status st = make_plan(RR_OP_SOFTMAX, M, N, in_dtype, out_dtype, al, &p);
+  if (st != RR_OK) return st;
+  if (p.workspace_bytes > 0) {
+    if (!workspace || workspace_bytes < p.workspace_bytes)
+      return fail(RR_ERR_WORKSPACE, "rr_softmax_rows: needs a workspace of %zu bytes, got %zu",
+                  p.workspace_bytes, workspace ? workspace_bytes : (size_t)0);
+    if ((reinterpret_cast<uintptr_t>(workspace) & 7u) != 0)
+      return fail(RR_ERR_INVALID_ARG, "rr_softmax_rows: workspace must be 8-byte aligned");
+    if (overlaps(workspace, p.workspace_bytes, x, xb) || overlaps(workspace, p.workspace_bytes, y, yb))
+      return fail(RR_ERR_INVALID_ARG, "rr_softmax_rows: workspace overlaps x or y");
+  }
+  const hipError_t e = rr::launch_softmax(p, in_dtype, out_dtype, y, x, workspace, M, (int32_t)N,
+                                          grid_for(p), static_cast<hipStream_t>(stream));
+  return hip_status(e, "rr_softmax_rows");
+}
+
+const char* rr_status_string(rr_status s) {
+  switch (s) {
+    case RR_OK: return "RR_OK";
+    case RR_ERR_INVALID_ARG: return "RR_ERR_INVALID_ARG";
+    case RR_ERR_UNSUPPORTED: return "RR_ERR_UNSUPPORTED";
+    case RR_ERR_WORKSPACE: return "RR_ERR_WORKSPACE";
+    case RR_ERR_HIP: return "RR_ERR_HIP";
+  }
+  return "RR_UNKNOWN_STATUS";
+}
+
+const char* rr_last_error_message(void) { return g_err; }
+
+rr_status rr_query_plan(rr_op op, int64_t M, int64_t N, rr_dtype in_dtype, rr_dtype out_dtype,
+                        int is_aligned16, rr_plan* plan) {
+  g_err[0] = '\0';
+  if (!plan) return fail(RR_ERR_INVALID_ARG, "rr_query_plan: null plan");
+  return make_plan(op, M, N, in_dtype, out_dtype, is_aligned16 != 0, plan);
+}
+
+rr_status rr_set_variant_override(rr_variant v) {
+  g_err[0] = '\0';
+  if (v < RR_VARIANT_AUTO || v > RR_VARIANT_LOOP)
+    return fail(RR_ERR_INVALID_ARG, "rr_set_variant_override: unknown variant %d", (int)v);
+  g_override.store(v, std::memory_order_relaxed);
+  return RR_OK;
+}
+
+rr_status rr_selftest_wave_allreduce(const float* in, float* out, int64_t count, int kind,
+                                     void* stream) {
+  g_err[0] = '\0';
+  if (!in || !out || count < 1 || count > 0x7fffffffLL || kind < 0 || kind > 2)
+    return fail(RR_ERR_INVALID_ARG, "rr_selftest_wave_allreduce: bad arguments");
+  return hip_status(rr::launch_selftest_wave(in, out, count, kind, static_cast<hipStream_t>(stream)),
+                    "rr_selftest_wave_allreduce");
+}
+
+}  // extern "C"

@@ -1,0 +1,594 @@
+// Row-reduce kernels for MI355X (gfx950): RMSNorm, fused residual add +
+// RMSNorm, and row softmax on the online normaliser.
+//
+// Every kernel follows the same shape: each lane reduces the elements it
+// holds to a partial statistic (the sum of squares, or the online pair
+// (m, d)); a wave64 all-reduce gives every lane the wavefront's statistic;
+// when several wavefronts share a row, one LDS slot per wavefront and one
+// barrier combine them, every lane folding the slots in the same order; then
+// each lane rescales its own elements and stores them.
+//
+// Sources (web pages, cited by title and section):
+//  [P1] "两个融合算子：RMSNorm 与 online softmax" (daleiyang.github.io)
+//  [P2] "GPU Kernel 工程（04）：共享内存与 reduction——softmax、LayerNorm 与
+//       online softmax" (arganzheng.life)
+//  [P4] "Softmax 与归一化" (anrans.github.io ai-infra-handbooks)
+//  [P5] "RMSNorm、Softmax 与在线归约" (notes.kuangjux.top)
+//
+// Launch shapes (chosen on the host, see rr_api.cpp):
+//  * register kernels: blockDim = 64 * waves_per_row * rows_per_group with
+//    either waves_per_row == 1 (a wavefront per row, no LDS, no barrier) or
+//    rows_per_group == 1 (a workgroup per row).  Lane t of a row owns vectors
+//    t, t + T, t + 2T, ... (T = 64 * waves_per_row) so every 16-byte access
+//    of a wavefront is one contiguous 1 KiB segment.
+//  * the grid may be smaller than the number of rows: workgroups then walk
+//    rows with a stride of gridDim.x (a persistent grid); gamma stays in
+//    registers across rows.
+#include "rr_device.h"
+#include "rr_launch.h"
+
+namespace rr {
+
+namespace {
+
+// LDS stage for one float per wavefront ([P2] section 四 and [P5] section
+// "原 RMSNorm 草稿的两个关键错误": one slot per wavefront, a barrier, then a
+// single combine).  Every lane reads all `nw` slots and adds them in index
+// order, so every lane of the workgroup ends with the same bits and no
+// broadcast step is needed.  `parity` selects one of two slot sets: a loop
+// that reduces once per row alternates them, which makes the single barrier
+// per row enough (a wavefront can only write a slot set again after the next
+// barrier, which every wavefront reaches after finishing its reads of that
+// set) -- the reuse hazard [P2] section 十 and [P4] section "实现" close with
+// a trailing barrier.
+__device__ __forceinline__ float group_sum(float v, int nw, int w, int lane,
+                                           float (*slots)[kMaxWavesPerGroup], int parity) {
+  if (lane == 0) slots[parity][w] = v;
+  __syncthreads();
+  float t = slots[parity][0];
+  for (int j = 1; j < nw; ++j) t += slots[parity][j];
+  return t;
+}
+
+__device__ __forceinline__ MD group_md(MD v, int nw, int w, int lane,
+                                       MD (*slots)[kMaxWavesPerGroup], int parity) {
+  if (lane == 0) slots[parity][w] = v;
+  __syncthreads();
+  MD t = slots[parity][0];
+  for (int j = 1; j < nw; ++j) t = md_merge(t, slots[parity][j]);
+  return t;
+}
+
+// Thread coordinates inside a launch of the register kernels.
+struct RowLane {
+  int lane;   // 0..63
+  int w;      // wavefront within the row
+  int g;      // row slot within the workgroup
+  int t;      // lane within the row (0 .. T-1)
+  int T;      // lanes per row
+  int rpg;    // rows per workgroup step
+};
+
+__device__ __forceinline__ RowLane row_lane(int wpr) {
+  RowLane r;
+  const int wave = threadIdx.x >> 6;
+  r.lane = threadIdx.x & 63;
+  r.rpg = (blockDim.x >> 6) / wpr;
+  r.g = wave / wpr;
+  r.w = wave - r.g * wpr;
+  r.T = wpr * kWave;
+  r.t = r.w * kWave + r.lane;
+  return r;
+}
+
+}  // namespace
+
+// ===========================================================================
+// RMSNorm / fused add + RMSNorm, row held in registers (WAVE and BLOCK)
+//
+// [P1] section "三、N3：把 x 留在寄存器": keeping the row in registers with
+// fully unrolled constant indices is what makes the kernel read x once.
+// Fused: [P4] section "算子融合：fused_add_rms_norm", [P2] section 八.3.
+// The fp32 sum x + r is rounded once to the I/O dtype; that rounded value is
+// stored as the new residual and is the h whose squares are summed and which
+// is rescaled.  Widening bf16 is exact and fp32 carries more than twice bf16's
+// precision plus two bits, so rounding the fp32 sum to bf16 gives the
+// correctly rounded sum.
+// ===========================================================================
+template <typename T, int NV, bool FUSED>
+__global__ __launch_bounds__(1024) void norm_regs_kernel(T* y, T* residual, const T* x,
+                                                         const T* __restrict__ gamma, int64_t M,
+                                                         int N, float eps, int wpr) {
+  constexpr int VEC = Elem<T>::kVec;
+  __shared__ float slots[2][kMaxWavesPerGroup];
+  const RowLane rl = row_lane(wpr);
+  const int nvec = N / VEC;
+
+  Packed<T, VEC> gv[NV];
+#pragma unroll
+  for (int k = 0; k < NV; ++k) {
+    const int vi = k * rl.T + rl.t;
+    if (vi < nvec) gv[k].load(gamma + (int64_t)vi * VEC);
+    else gv[k].zero();
+  }
+
+  const int64_t stride = (int64_t)gridDim.x * rl.rpg;
+  int parity = 0;
+  for (int64_t row = (int64_t)blockIdx.x * rl.rpg + rl.g; row < M; row += stride) {
+    const int64_t off = row * (int64_t)N;
+    float h[NV][VEC];
+    if constexpr (FUSED) {
+      float r[NV][VEC];
+#pragma unroll
+      for (int k = 0; k < NV; ++k) {
+        const int vi = k * rl.T + rl.t;
+        if (vi < nvec) {
+          load_vec<T, VEC>(x + off + (int64_t)vi * VEC, h[k]);
+          load_vec<T, VEC>(residual + off + (int64_t)vi * VEC, r[k]);
+        } else {
+#pragma unroll
+          for (int i = 0; i < VEC; ++i) h[k][i] = r[k][i] = 0.0f;
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < NV; ++k) {
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) h[k][i] = round_to<T>(h[k][i] + r[k][i]);
+        const int vi = k * rl.T + rl.t;
+        if (vi < nvec) store_vec<T, VEC>(residual + off + (int64_t)vi * VEC, h[k]);
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < NV; ++k) {
+        const int vi = k * rl.T + rl.t;
+        if (vi < nvec) {
+          load_vec<T, VEC>(x + off + (int64_t)vi * VEC, h[k]);
+        } else {
+#pragma unroll
+          for (int i = 0; i < VEC; ++i) h[k][i] = 0.0f;
+        }
+      }
+    }
+
+    float ss = 0.0f;
+#pragma unroll
+    for (int k = 0; k < NV; ++k)
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) ss += h[k][i] * h[k][i];
+    ss = wave_sum(ss);
+    if (wpr > 1) {
+      ss = group_sum(ss, wpr, rl.w, rl.lane, slots, parity);
+      parity ^= 1;
+    }
+    // eps inside the root, mean over N ([P5] section "RMSNorm 归约什么").
+    const float rstd = 1.0f / __builtin_sqrtf(ss / (float)N + eps);
+
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {
+      const int vi = k * rl.T + rl.t;
+      float o[VEC];
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) o[i] = (h[k][i] * rstd) * gv[k].get(i);
+      if (vi < nvec) store_vec<T, VEC>(y + off + (int64_t)vi * VEC, o);
+    }
+  }
+}
+
+// ===========================================================================
+// RMSNorm / fused, streaming (LOOP): any N, any alignment (VEC may be 1).
+// Pass 1 reads the row (and for the fused op writes the new residual) and
+// sums squares; pass 2 reads it again -- x, or the stored residual -- and
+// writes y.  Each lane revisits exactly the elements it handled in pass 1.
+// ===========================================================================
+template <typename T, int VEC, bool FUSED>
+__global__ __launch_bounds__(1024) void norm_loop_kernel(T* y, T* residual, const T* x,
+                                                         const T* __restrict__ gamma, int64_t M,
+                                                         int N, float eps) {
+  __shared__ float slots[2][kMaxWavesPerGroup];
+  const RowLane rl = row_lane(blockDim.x >> 6);
+  const int nvec = N / VEC;
+  int parity = 0;
+  for (int64_t row = blockIdx.x; row < M; row += gridDim.x) {
+    const int64_t off = row * (int64_t)N;
+    float ss = 0.0f;
+    for (int vi = rl.t; vi < nvec; vi += rl.T) {
+      float h[VEC];
+      load_vec<T, VEC>(x + off + (int64_t)vi * VEC, h);
+      if constexpr (FUSED) {
+        float r[VEC];
+        load_vec<T, VEC>(residual + off + (int64_t)vi * VEC, r);
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) h[i] = round_to<T>(h[i] + r[i]);
+        store_vec<T, VEC>(residual + off + (int64_t)vi * VEC, h);
+      }
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) ss += h[i] * h[i];
+    }
+    ss = wave_sum(ss);
+    ss = group_sum(ss, rl.T / kWave, rl.w, rl.lane, slots, parity);
+    parity ^= 1;
+    const float rstd = 1.0f / __builtin_sqrtf(ss / (float)N + eps);
+    const T* src = FUSED ? residual : x;
+    for (int vi = rl.t; vi < nvec; vi += rl.T) {
+      float h[VEC], g[VEC];
+      load_vec<T, VEC>(src + off + (int64_t)vi * VEC, h);
+      load_vec<T, VEC>(gamma + (int64_t)vi * VEC, g);
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) h[i] = (h[i] * rstd) * g[i];
+      store_vec<T, VEC>(y + off + (int64_t)vi * VEC, h);
+    }
+  }
+}
+
+// ===========================================================================
+// Softmax, row held in registers (WAVE and BLOCK).
+//
+// Each lane summarises the NV*VEC values it holds as a pair (m_l, d_l): its
+// maximum, then the sum of e_i = exp(x_i - m_l), keeping the e_i in the
+// registers that held x ([P1] section "四、S4：float4，顺便演示了分块合并": a
+// chunk summary merged into the running pair).  The pairs are combined with
+// the merge across the wavefront and, for BLOCK, across wavefronts, which
+// gives the row's (m, d) in every lane.  The outputs are then
+//   y_i = e_i * c_l,  c_l = exp(m_l - m) / d,
+// one exponential per element plus one per lane: e_i * exp(m_l - m) =
+// exp(x_i - m) is the rescale of [P1] section "二、递推式怎么来的".
+// Entries equal to -inf give e_i = 0 and so y_i = 0 exactly.  A lane whose
+// entries are all -inf has m_l = -inf and c_l = 0; a row whose entries are
+// all -inf has m = -inf and every output is NaN, as exp(x - m)/d is.
+// ===========================================================================
+template <typename Tin, typename Tout, int NV>
+__global__ __launch_bounds__(1024) void softmax_regs_kernel(const Tin* x, Tout* y, int64_t M,
+                                                            int N, int wpr) {
+  constexpr int VEC = Elem<Tin>::kVec;
+  __shared__ MD slots[2][kMaxWavesPerGroup];
+  const RowLane rl = row_lane(wpr);
+  const int nvec = N / VEC;
+  const int64_t stride = (int64_t)gridDim.x * rl.rpg;
+  int parity = 0;
+  for (int64_t row = (int64_t)blockIdx.x * rl.rpg + rl.g; row < M; row += stride) {
+    const int64_t off = row * (int64_t)N;
+    float v[NV][VEC];
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {
+      const int vi = k * rl.T + rl.t;
+      if (vi < nvec) {
+        load_vec<Tin, VEC>(x + off + (int64_t)vi * VEC, v[k]);
+      } else {
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) v[k][i] = kNegInf;
+      }
+    }
+    float ml = kNegInf;
+#pragma unroll
+    for (int k = 0; k < NV; ++k)
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) ml = __builtin_fmaxf(ml, v[k][i]);
+    // shift by 0 when the lane holds only -inf so that exp(-inf - 0) = 0
+    const float shift = (ml == kNegInf) ? 0.0f : ml;
+    float dl = 0.0f;
+#pragma unroll
+    for (int k = 0; k < NV; ++k)
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) {
+        v[k][i] = exp_shifted(v[k][i] - shift);
+        dl += v[k][i];
+      }
+    MD p;
+    p.m = ml;
+    p.d = dl;
+    p = wave_md(p);
+    if (wpr > 1) {
+      p = group_md(p, wpr, rl.w, rl.lane, slots, parity);
+      parity ^= 1;
+    }
+    float c = (ml == kNegInf) ? 0.0f : exp_shifted(ml - p.m) / p.d;
+    if (p.m == kNegInf) c = __builtin_nanf("");
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {
+      const int vi = k * rl.T + rl.t;
+      float o[VEC];
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) o[i] = v[k][i] * c;
+      if (vi < nvec) store_vec<Tout, VEC>(y + off + (int64_t)vi * VEC, o);
+    }
+  }
+}
+
+// ===========================================================================
+// Softmax, streaming (LOOP): any N, any alignment.  Pass 1 runs the online
+// recurrence per lane, one vector (chunk) at a time: the chunk's own summary
+// merged into the lane's running pair ([P1] section "四、S4"; [P2] section
+// 七.3; [P4] section "Online softmax：一次遍历求出最大值和指数和").  The
+// lanes' pairs are merged into the row's (m, d); pass 2 reads the row again
+// and writes exp(x - m) / d.  HBM traffic: two reads and one write per
+// element ([P2] section 七.3: "read twice, write once").
+// ===========================================================================
+template <typename Tin, typename Tout, int VEC>
+__global__ __launch_bounds__(1024) void softmax_loop_kernel(const Tin* x, Tout* y, int64_t M,
+                                                            int N) {
+  __shared__ MD slots[2][kMaxWavesPerGroup];
+  const RowLane rl = row_lane(blockDim.x >> 6);
+  const int nvec = N / VEC;
+  int parity = 0;
+  for (int64_t row = blockIdx.x; row < M; row += gridDim.x) {
+    const int64_t off = row * (int64_t)N;
+    MD p;
+    p.m = kNegInf;
+    p.d = 0.0f;
+    for (int vi = rl.t; vi < nvec; vi += rl.T) {
+      float v[VEC];
+      load_vec<Tin, VEC>(x + off + (int64_t)vi * VEC, v);
+      p = md_merge(p, chunk_summary<VEC>(v));
+    }
+    p = wave_md(p);
+    p = group_md(p, rl.T / kWave, rl.w, rl.lane, slots, parity);
+    parity ^= 1;
+    const float inv_d = (p.m == kNegInf) ? __builtin_nanf("") : 1.0f / p.d;
+    for (int vi = rl.t; vi < nvec; vi += rl.T) {
+      float v[VEC];
+      load_vec<Tin, VEC>(x + off + (int64_t)vi * VEC, v);
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) v[i] = exp_shifted(v[i] - p.m) * inv_d;
+      store_vec<Tout, VEC>(y + off + (int64_t)vi * VEC, v);
+    }
+  }
+}
+
+// ===========================================================================
+// Softmax, split row (SPLIT): a row is cut into S chunks of CV vectors, one
+// workgroup per (row, chunk).  [P4] section "练习" (the vocabulary-split
+// exercise): each workgroup writes its chunk's (m, d) to a buffer, a second
+// kernel merges them; the merge is associative and commutative ([P1] section
+// "三、结合律"), so the chunks may be combined in any grouping.
+//
+// Pass A writes workspace[row * S + c] = (m_c, d_c).
+// Pass B: every wavefront merges the row's S pairs itself (lane j folds pairs
+// j, j + 64, ... in order, then the wave all-reduce), so every workgroup of
+// a row obtains the same bits without another barrier; it then rescales its
+// chunk.  The chunk's vectors are loaded before the pairs are merged so the
+// HBM reads are in flight during the merge.
+// ===========================================================================
+template <typename Tin, int NV>
+__global__ __launch_bounds__(256) void softmax_split_stats_kernel(const Tin* x, float2* ws,
+                                                                  int64_t M, int N, int S) {
+  constexpr int VEC = Elem<Tin>::kVec;
+  constexpr int kThreads = 256;
+  constexpr int CV = kThreads * NV;
+  __shared__ MD slots[2][kMaxWavesPerGroup];
+  const RowLane rl = row_lane(kThreads / kWave);
+  const int nvec = N / VEC;
+  const int64_t items = M * (int64_t)S;
+  int parity = 0;
+  for (int64_t item = blockIdx.x; item < items; item += gridDim.x) {
+    const int64_t row = item / S;
+    const int c = (int)(item - row * S);
+    const int64_t off = row * (int64_t)N;
+    float v[NV][VEC];
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {
+      const int vi = c * CV + k * kThreads + rl.t;
+      if (vi < nvec) {
+        load_vec<Tin, VEC>(x + off + (int64_t)vi * VEC, v[k]);
+      } else {
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) v[k][i] = kNegInf;
+      }
+    }
+    float ml = kNegInf;
+#pragma unroll
+    for (int k = 0; k < NV; ++k)
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) ml = __builtin_fmaxf(ml, v[k][i]);
+    const float shift = (ml == kNegInf) ? 0.0f : ml;
+    float dl = 0.0f;
+#pragma unroll
+    for (int k = 0; k < NV; ++k)
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) dl += exp_shifted(v[k][i] - shift);
+    MD p;
+    p.m = ml;
+    p.d = dl;
+    p = wave_md(p);
+    p = group_md(p, kThreads / kWave, rl.w, rl.lane, slots, parity);
+    parity ^= 1;
+    if (threadIdx.x == 0) ws[item] = make_float2(p.m, p.d);
+  }
+}
+
+template <typename Tin, typename Tout, int NV>
+__global__ __launch_bounds__(256) void softmax_split_apply_kernel(const Tin* x, Tout* y,
+                                                                  const float2* __restrict__ ws,
+                                                                  int64_t M, int N, int S) {
+  constexpr int VEC = Elem<Tin>::kVec;
+  constexpr int kThreads = 256;
+  constexpr int CV = kThreads * NV;
+  const RowLane rl = row_lane(kThreads / kWave);
+  const int nvec = N / VEC;
+  const int64_t items = M * (int64_t)S;
+  for (int64_t item = blockIdx.x; item < items; item += gridDim.x) {
+    const int64_t row = item / S;
+    const int c = (int)(item - row * S);
+    const int64_t off = row * (int64_t)N;
+    float v[NV][VEC];
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {
+      const int vi = c * CV + k * kThreads + rl.t;
+      if (vi < nvec) {
+        load_vec<Tin, VEC>(x + off + (int64_t)vi * VEC, v[k]);
+      } else {
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) v[k][i] = kNegInf;
+      }
+    }
+    MD p;
+    p.m = kNegInf;
+    p.d = 0.0f;
+    for (int s = rl.lane; s < S; s += kWave) {
+      const float2 q = ws[row * S + s];
+      MD b;
+      b.m = q.x;
+      b.d = q.y;
+      p = md_merge(p, b);
+    }
+    p = wave_md(p);
+    const float inv_d = (p.m == kNegInf) ? __builtin_nanf("") : 1.0f / p.d;
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {
+      const int vi = c * CV + k * kThreads + rl.t;
+      float o[VEC];
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) o[i] = exp_shifted(v[k][i] - p.m) * inv_d;
+      if (vi < nvec) store_vec<Tout, VEC>(y + off + (int64_t)vi * VEC, o);
+    }
+  }
+}
+
+// ===========================================================================
+// self-test of the wave all-reduce: one wavefront per 64-value group
+// ===========================================================================
+__global__ __launch_bounds__(64) void selftest_wave_kernel(const float* in, float* out, int kind) {
+  const int64_t gidx = blockIdx.x;
+  const int lane = threadIdx.x;
+  if (kind == 0) {
+    out[gidx * 64 + lane] = wave_sum(in[gidx * 64 + lane]);
+  } else if (kind == 1) {
+    out[gidx * 64 + lane] = wave_max(in[gidx * 64 + lane]);
+  } else {
+    MD p;
+    p.m = in[gidx * 128 + lane];
+    p.d = in[gidx * 128 + 64 + lane];
+    p = wave_md(p);
+    out[gidx * 128 + lane] = p.m;
+    out[gidx * 128 + 64 + lane] = p.d;
+  }
+}
+
+// ===========================================================================
+// launchers
+// ===========================================================================
+namespace {
+
+inline dim3 grid1(int64_t g) { return dim3((unsigned)g, 1, 1); }
+
+template <typename T, bool FUSED>
+hipError_t norm_regs(const rr_plan& p, void* y, void* res, const void* x, const void* gamma,
+                     int64_t M, int N, float eps, int64_t grid, hipStream_t s) {
+  T* yy = static_cast<T*>(y);
+  T* rr_ = static_cast<T*>(res);
+  const T* xx = static_cast<const T*>(x);
+  const T* gg = static_cast<const T*>(gamma);
+  const dim3 b(p.block_threads);
+  // The host never plans more than 16 values per lane for the norms
+  // (NV * VEC <= 16), so only those instantiations exist.
+  switch (p.vecs_per_lane) {
+    case 1: norm_regs_kernel<T, 1, FUSED><<<grid1(grid), b, 0, s>>>(yy, rr_, xx, gg, M, N, eps, p.waves_per_row); break;
+    case 2: norm_regs_kernel<T, 2, FUSED><<<grid1(grid), b, 0, s>>>(yy, rr_, xx, gg, M, N, eps, p.waves_per_row); break;
+    case 4:
+      if constexpr (Elem<T>::kVec * 4 <= 16) {
+        norm_regs_kernel<T, 4, FUSED><<<grid1(grid), b, 0, s>>>(yy, rr_, xx, gg, M, N, eps, p.waves_per_row);
+        break;
+      }
+      return hipErrorInvalidValue;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+template <typename T, bool FUSED>
+hipError_t norm_loop(const rr_plan& p, void* y, void* res, const void* x, const void* gamma,
+                     int64_t M, int N, float eps, int64_t grid, hipStream_t s) {
+  T* yy = static_cast<T*>(y);
+  T* rr_ = static_cast<T*>(res);
+  const T* xx = static_cast<const T*>(x);
+  const T* gg = static_cast<const T*>(gamma);
+  const dim3 b(p.block_threads);
+  if (p.vec_elems == 1)
+    norm_loop_kernel<T, 1, FUSED><<<grid1(grid), b, 0, s>>>(yy, rr_, xx, gg, M, N, eps);
+  else
+    norm_loop_kernel<T, Elem<T>::kVec, FUSED><<<grid1(grid), b, 0, s>>>(yy, rr_, xx, gg, M, N, eps);
+  return hipGetLastError();
+}
+
+template <typename T, bool FUSED>
+hipError_t norm_any(const rr_plan& p, void* y, void* res, const void* x, const void* gamma,
+                    int64_t M, int N, float eps, int64_t grid, hipStream_t s) {
+  if (p.variant == RR_VARIANT_LOOP) return norm_loop<T, FUSED>(p, y, res, x, gamma, M, N, eps, grid, s);
+  return norm_regs<T, FUSED>(p, y, res, x, gamma, M, N, eps, grid, s);
+}
+
+template <typename Tin, typename Tout>
+hipError_t softmax_typed(const rr_plan& p, void* y, const void* x, void* ws, int64_t M, int N,
+                         int64_t grid, hipStream_t s) {
+  const Tin* xx = static_cast<const Tin*>(x);
+  Tout* yy = static_cast<Tout*>(y);
+  const dim3 b(p.block_threads);
+  if (p.variant == RR_VARIANT_LOOP) {
+    if (p.vec_elems == 1)
+      softmax_loop_kernel<Tin, Tout, 1><<<grid1(grid), b, 0, s>>>(xx, yy, M, N);
+    else
+      softmax_loop_kernel<Tin, Tout, Elem<Tin>::kVec><<<grid1(grid), b, 0, s>>>(xx, yy, M, N);
+    return hipGetLastError();
+  }
+  if (p.variant == RR_VARIANT_SPLIT) {
+    float2* w = static_cast<float2*>(ws);
+    const int S = (int)p.chunks_per_row;
+    switch (p.vecs_per_lane) {
+      case 2:
+        softmax_split_stats_kernel<Tin, 2><<<grid1(grid), b, 0, s>>>(xx, w, M, N, S);
+        softmax_split_apply_kernel<Tin, Tout, 2><<<grid1(grid), b, 0, s>>>(xx, yy, w, M, N, S);
+        break;
+      case 4:
+        softmax_split_stats_kernel<Tin, 4><<<grid1(grid), b, 0, s>>>(xx, w, M, N, S);
+        softmax_split_apply_kernel<Tin, Tout, 4><<<grid1(grid), b, 0, s>>>(xx, yy, w, M, N, S);
+        break;
+      default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+  }
+  // At most 32 values per lane (NV * VEC <= 32).
+  switch (p.vecs_per_lane) {
+    case 1: softmax_regs_kernel<Tin, Tout, 1><<<grid1(grid), b, 0, s>>>(xx, yy, M, N, p.waves_per_row); break;
+    case 2: softmax_regs_kernel<Tin, Tout, 2><<<grid1(grid), b, 0, s>>>(xx, yy, M, N, p.waves_per_row); break;
+    case 4: softmax_regs_kernel<Tin, Tout, 4><<<grid1(grid), b, 0, s>>>(xx, yy, M, N, p.waves_per_row); break;
+    case 8:
+      if constexpr (Elem<Tin>::kVec * 8 <= 32) {
+        softmax_regs_kernel<Tin, Tout, 8><<<grid1(grid), b, 0, s>>>(xx, yy, M, N, p.waves_per_row);
+        break;
+      }
+      return hipErrorInvalidValue;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_norm(const rr_plan& plan, rr_dtype dtype, bool fused, void* y, void* residual,
+                       const void* x, const void* gamma, int64_t M, int32_t N, float eps,
+                       int64_t grid, hipStream_t stream) {
+  if (dtype == RR_F32) {
+    return fused ? norm_any<float, true>(plan, y, residual, x, gamma, M, N, eps, grid, stream)
+                 : norm_any<float, false>(plan, y, residual, x, gamma, M, N, eps, grid, stream);
+  }
+  return fused ? norm_any<bf16_t, true>(plan, y, residual, x, gamma, M, N, eps, grid, stream)
+               : norm_any<bf16_t, false>(plan, y, residual, x, gamma, M, N, eps, grid, stream);
+}
+
+hipError_t launch_softmax(const rr_plan& plan, rr_dtype in_dtype, rr_dtype out_dtype, void* y,
+                          const void* x, void* workspace, int64_t M, int32_t N, int64_t grid,
+                          hipStream_t stream) {
+  if (in_dtype == RR_F32) {
+    if (out_dtype == RR_F32) return softmax_typed<float, float>(plan, y, x, workspace, M, N, grid, stream);
+    return softmax_typed<float, bf16_t>(plan, y, x, workspace, M, N, grid, stream);
+  }
+  if (out_dtype == RR_F32) return softmax_typed<bf16_t, float>(plan, y, x, workspace, M, N, grid, stream);
+  return softmax_typed<bf16_t, bf16_t>(plan, y, x, workspace, M, N, grid, stream);
+}
+
+hipError_t launch_selftest_wave(const float* in, float* out, int64_t count, int kind,
+                                hipStream_t stream) {
+  selftest_wave_kernel<<<grid1(count), dim3(64), 0, stream>>>(in, out, kind);
+  return hipGetLastError();
+}
+
+}  // namespace rr

@@ -1,0 +1,30 @@
+// Internal interface between the C ABI (rr_api.cpp) and the kernels
+// (rr_kernels.hip).  Not installed; not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "rowreduce.h"
+
+namespace rr {
+
+// Largest number of wavefronts one workgroup may hold (1024 threads).
+constexpr int kMaxWavesPerGroup = 16;
+
+// Enqueue the RMSNorm (fused == false) or fused add + RMSNorm kernel that
+// `plan` names, with `grid` workgroups, on `stream`.
+hipError_t launch_norm(const rr_plan& plan, rr_dtype dtype, bool fused, void* y, void* residual,
+                       const void* x, const void* gamma, int64_t M, int32_t N, float eps,
+                       int64_t grid, hipStream_t stream);
+
+// Enqueue the softmax kernel(s) that `plan` names (two for SPLIT).
+hipError_t launch_softmax(const rr_plan& plan, rr_dtype in_dtype, rr_dtype out_dtype, void* y,
+                          const void* x, void* workspace, int64_t M, int32_t N, int64_t grid,
+                          hipStream_t stream);
+
+// Enqueue the wave all-reduce self-test kernel.
+hipError_t launch_selftest_wave(const float* in, float* out, int64_t count, int kind,
+                                hipStream_t stream);
+
+}  // namespace rr

@@ -1,0 +1,112 @@
+"""Comparison rules between the GPU results and the fp64 oracle.
+
+Bars (stated once here, used by every parity test):
+  * fp32 RMSNorm / fused y: max |g - r| / |r| <= 1e-5, and g == 0 where r == 0.
+  * fp32 softmax: max |g - r| <= 2e-6 per probability; every output finite and
+    >= 0; masked (-inf) inputs give exactly 0; |sum_j g_j - 1| <= 1e-5 per row;
+    rows that are entirely -inf give NaN in every position.
+  * bf16 outputs: at most 1 bf16 ulp from the oracle rounded to bf16 (round to
+    nearest even), measured as a distance between order-preserving integer
+    images of the bit patterns, with +0 and -0 equal.
+  * bf16 residual_out of the fused op: bit-exact (the rounded sum is unique).
+"""
+import numpy as np
+
+import oracle
+
+RMS_F32_RTOL = 1e-5
+SOFTMAX_F32_ATOL = 2e-6
+SOFTMAX_ROWSUM_ATOL = 1e-5
+BF16_MAX_ULP = 1
+
+
+def to_f64(t) -> np.ndarray:
+    """torch tensor (any device, f32/bf16) -> float64 numpy (exact)."""
+    import torch
+    return t.detach().to("cpu").to(torch.float64).numpy()
+
+
+def bf16_bits_of_tensor(t) -> np.ndarray:
+    import torch
+    return t.detach().to("cpu").contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+def bf16_bits_of_values(v: np.ndarray) -> np.ndarray:
+    """fp64 values that are exactly bf16 -> their 16-bit patterns."""
+    f = np.ascontiguousarray(v, dtype=np.float64).astype(np.float32)
+    return (f.view(np.uint32) >> 16).astype(np.uint16)
+
+
+def ordered_int(bits: np.ndarray) -> np.ndarray:
+    b = bits.astype(np.int64)
+    mag = b & 0x7FFF
+    return np.where(b & 0x8000, -mag, mag)
+
+
+def bf16_ulp_distance(got_bits: np.ndarray, ref_bits: np.ndarray) -> np.ndarray:
+    return np.abs(ordered_int(got_bits) - ordered_int(ref_bits))
+
+
+def check_bf16(got_tensor, ref_f64: np.ndarray, what: str, max_ulp: int = BF16_MAX_ULP):
+    """got: bf16 tensor; ref: fp64 oracle values (rounded here to bf16)."""
+    ref_bits = bf16_bits_of_values(oracle.round_bf16(ref_f64))
+    got_bits = bf16_bits_of_tensor(got_tensor).reshape(ref_bits.shape)
+    ref_nan = np.isnan(ref_f64)
+    got_f = to_f64(got_tensor).reshape(ref_f64.shape)
+    assert np.array_equal(np.isnan(got_f), ref_nan), f"{what}: NaN pattern differs"
+    fin = ~ref_nan
+    dist = bf16_ulp_distance(got_bits[fin], ref_bits[fin])
+    worst = int(dist.max()) if dist.size else 0
+    assert worst <= max_ulp, f"{what}: {worst} bf16 ulp (> {max_ulp}); count>0: {int((dist > 0).sum())}"
+    return {"max_ulp": worst, "n_1ulp": int((dist == 1).sum()), "n": int(dist.size)}
+
+
+def check_bf16_exact(got_tensor, ref_f64: np.ndarray, what: str):
+    return check_bf16(got_tensor, ref_f64, what, max_ulp=0)
+
+
+def check_rms_f32(got_tensor, ref_f64: np.ndarray, what: str):
+    g = to_f64(got_tensor).reshape(ref_f64.shape)
+    assert np.all(np.isfinite(g)), f"{what}: non-finite output"
+    zero = ref_f64 == 0.0
+    assert np.all(g[zero] == 0.0), f"{what}: nonzero where the oracle is 0"
+    nz = ~zero
+    rel = np.abs(g[nz] - ref_f64[nz]) / np.abs(ref_f64[nz])
+    worst = float(rel.max()) if rel.size else 0.0
+    assert worst <= RMS_F32_RTOL, f"{what}: max rel err {worst:.3e} > {RMS_F32_RTOL}"
+    return {"max_rel": worst}
+
+
+def check_softmax(got_tensor, x_f64: np.ndarray, ref_f64: np.ndarray, what: str):
+    """Softmax bars; dispatches on the output dtype."""
+    import torch
+    M = ref_f64.shape[0]
+    nan_rows = np.all(np.isneginf(x_f64), axis=1)
+    if got_tensor.dtype == torch.bfloat16:
+        info = check_bf16(got_tensor, ref_f64, what)
+        g = to_f64(got_tensor).reshape(ref_f64.shape)
+    else:
+        g = to_f64(got_tensor).reshape(ref_f64.shape)
+        ok = ~nan_rows
+        if ok.any():
+            err = np.abs(g[ok] - ref_f64[ok])
+            worst = float(err.max())
+            assert worst <= SOFTMAX_F32_ATOL, f"{what}: max abs err {worst:.3e} > {SOFTMAX_F32_ATOL}"
+        else:
+            worst = 0.0
+        info = {"max_abs": worst}
+    # properties that hold whatever the dtype
+    if nan_rows.any():
+        assert np.all(np.isnan(g[nan_rows])), f"{what}: fully masked rows must be NaN"
+    ok = ~nan_rows
+    gk = g[ok]
+    assert np.all(np.isfinite(gk)), f"{what}: non-finite probability"
+    assert np.all(gk >= 0.0), f"{what}: negative probability"
+    masked = np.isneginf(x_f64[ok])
+    assert np.all(gk[masked] == 0.0), f"{what}: masked entry not exactly 0"
+    if got_tensor.dtype != torch.bfloat16 and gk.size:
+        rs = np.abs(gk.sum(axis=1) - 1.0)
+        assert rs.max() <= SOFTMAX_ROWSUM_ATOL, f"{what}: row sum off by {rs.max():.3e}"
+        info["max_rowsum_err"] = float(rs.max())
+    info["rows"] = M
+    return info

@@ -1,0 +1,170 @@
+"""Host-side tests of the C ABI (no GPU needed).
+
+* the shared library loads and exports every function include/rowreduce.h
+  declares;
+* argument validation returns the documented status before any device work
+  (every call here fails validation, so nothing is enqueued);
+* the variant dispatch picks the documented kernel for the named workloads
+  and across the row-length boundaries (integer logic, compared exactly).
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import row_reduction_rmsnorm_amd as rr
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "rowreduce.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"\b(rr_[a-z0-9_]+)\s*\(", text)
+    return sorted(set(names))
+
+
+def test_library_exports_every_declared_function():
+    names = _declared_functions()
+    assert len(names) >= 9
+    L = rr.lib()
+    missing = [n for n in names if not hasattr(L, n)]
+    assert not missing, missing
+    assert sorted(rr.EXPORTS) == names
+
+
+def test_library_exports_nothing_undeclared():
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--defined-only", rr.binding.LIB_PATH],
+                         capture_output=True, text=True, check=True).stdout
+    exported = sorted({l.split()[-1] for l in out.splitlines() if " T rr_" in l})
+    assert exported == _declared_functions()
+
+
+def test_status_strings():
+    assert rr.status_string(rr.RR_OK) == "RR_OK"
+    assert rr.status_string(rr.RR_ERR_WORKSPACE) == "RR_ERR_WORKSPACE"
+    assert rr.status_string(99) == "RR_UNKNOWN_STATUS"
+
+
+# A fake "device" address: validation must reject the call before touching it.
+P = 1 << 32
+
+
+@pytest.mark.parametrize("args,status", [
+    ((P, P, P, 4, 0, 1e-6, rr.RR_F32, None), rr.RR_ERR_INVALID_ARG),      # H < 1
+    ((P, P, P, -1, 8, 1e-6, rr.RR_F32, None), rr.RR_ERR_INVALID_ARG),     # M < 0
+    ((None, P, P, 4, 8, 1e-6, rr.RR_F32, None), rr.RR_ERR_INVALID_ARG),   # null y
+    ((P, P, P, 4, 8, -1.0, rr.RR_F32, None), rr.RR_ERR_INVALID_ARG),      # eps < 0
+    ((P, P, P, 4, 8, float("nan"), rr.RR_F32, None), rr.RR_ERR_INVALID_ARG),
+    ((P, P, P, 4, 8, 1e-6, 7, None), rr.RR_ERR_INVALID_ARG),              # dtype
+    ((P, P + 4, P << 4, 4, 8, 1e-6, rr.RR_F32, None), rr.RR_ERR_INVALID_ARG),  # y partly overlaps x
+    ((P, P << 2, P + 8, 4, 8, 1e-6, rr.RR_F32, None), rr.RR_ERR_INVALID_ARG),  # gamma inside y
+    ((P, P, P << 4, 4, (1 << 30) + 8, 1e-6, rr.RR_F32, None), rr.RR_ERR_UNSUPPORTED),
+])
+def test_rmsnorm_validation(args, status):
+    assert rr.raw_rmsnorm(*args) == status
+    assert rr.last_error_message()
+
+
+def test_m_zero_is_a_noop_even_with_null_pointers():
+    assert rr.raw_rmsnorm(None, None, None, 0, 8, 1e-6, rr.RR_F32, None) == rr.RR_OK
+    assert rr.raw_softmax_rows(None, None, 0, 8, rr.RR_F32, rr.RR_F32, None, 0, None) == rr.RR_OK
+    assert rr.raw_fused_add_rmsnorm(None, None, None, None, 0, 8, 1e-6, rr.RR_BF16, None) == rr.RR_OK
+
+
+def test_fused_validation():
+    X, R, G, Y = P, P << 2, P << 4, P << 6
+    ok = dict(y=Y, residual=R, x=X, gamma=G)
+    call = lambda d, M=4, H=8, dt=rr.RR_BF16: rr.raw_fused_add_rmsnorm(
+        d["y"], d["residual"], d["x"], d["gamma"], M, H, 1e-6, dt, None)
+    assert call({**ok, "residual": None}) == rr.RR_ERR_INVALID_ARG
+    assert call({**ok, "residual": X}) == rr.RR_ERR_INVALID_ARG          # residual == x
+    assert call({**ok, "residual": Y + 2}) == rr.RR_ERR_INVALID_ARG      # residual overlaps y
+    assert call({**ok, "y": X + 2}) == rr.RR_ERR_INVALID_ARG             # y partly overlaps x
+    assert call({**ok, "gamma": R + 4}) == rr.RR_ERR_INVALID_ARG         # gamma inside residual
+
+
+def test_softmax_validation():
+    X, Y, W = P, P << 4, P << 8
+    f = rr.raw_softmax_rows
+    assert f(Y, X, 4, 0, rr.RR_F32, rr.RR_F32, None, 0, None) == rr.RR_ERR_INVALID_ARG
+    assert f(Y, X, 4, 8, 3, rr.RR_F32, None, 0, None) == rr.RR_ERR_INVALID_ARG
+    # in place with different dtypes
+    assert f(X, X, 4, 8, rr.RR_BF16, rr.RR_F32, None, 0, None) == rr.RR_ERR_INVALID_ARG
+    # long rows with few rows need the split workspace
+    need = rr.rr_softmax_rows_workspace_bytes(256, 152064, rr.RR_BF16, rr.RR_F32)
+    assert need == 256 * 38 * 8
+    assert f(Y, X, 256, 152064, rr.RR_BF16, rr.RR_F32, None, 0, None) == rr.RR_ERR_WORKSPACE
+    assert f(Y, X, 256, 152064, rr.RR_BF16, rr.RR_F32, W, need - 8, None) == rr.RR_ERR_WORKSPACE
+    assert f(Y, X, 256, 152064, rr.RR_BF16, rr.RR_F32, W + 4, need, None) == rr.RR_ERR_INVALID_ARG
+    assert "workspace" in rr.last_error_message()
+
+
+# ----------------------------------------------------------------------------
+# dispatch (the variant choice by row length)
+# ----------------------------------------------------------------------------
+
+WORKLOAD_PLANS = [
+    # op, M, N, in, out -> variant, waves_per_row, vecs_per_lane, vec_elems, chunks
+    ((rr.RR_OP_RMSNORM, 64, 3584, rr.RR_F32, rr.RR_F32), ("block", 4, 4, 4, 1)),
+    ((rr.RR_OP_FUSED_ADD_RMSNORM, 8192, 4096, rr.RR_BF16, rr.RR_BF16), ("block", 4, 2, 8, 1)),
+    ((rr.RR_OP_RMSNORM, 8192, 4096, rr.RR_BF16, rr.RR_BF16), ("block", 4, 2, 8, 1)),
+    ((rr.RR_OP_SOFTMAX, 16384, 1024, rr.RR_F32, rr.RR_F32), ("wave", 1, 4, 4, 1)),
+    ((rr.RR_OP_SOFTMAX, 256, 152064, rr.RR_BF16, rr.RR_F32), ("split", 4, 2, 8, 38)),
+    ((rr.RR_OP_SOFTMAX, 28 * 4096, 4096, rr.RR_F32, rr.RR_F32), ("block", 4, 4, 4, 1)),
+]
+
+
+@pytest.mark.parametrize("args,expect", WORKLOAD_PLANS)
+def test_dispatch_named_workloads(args, expect):
+    p = rr.rr_query_plan(*args)
+    got = (p["variant_name"], p["waves_per_row"], p["vecs_per_lane"], p["vec_elems"],
+           p["chunks_per_row"])
+    assert got == expect
+
+
+def test_dispatch_boundaries():
+    S, F, B = rr.RR_OP_SOFTMAX, rr.RR_F32, rr.RR_BF16
+    v = lambda op, M, N, a=F, b=F, al=True: rr.rr_query_plan(op, M, N, a, b, al)["variant_name"]
+    # softmax: a wavefront per row up to 2048 elements (32 fp32 per lane)
+    assert v(S, 100, 2048) == "wave"
+    assert v(S, 100, 2052) == "block"
+    assert v(S, 100, 2048, B, B) == "wave"
+    # norms keep 16 values per lane: a wavefront up to 1024, then a block
+    assert v(rr.RR_OP_RMSNORM, 100, 1024) == "wave"
+    assert v(rr.RR_OP_RMSNORM, 100, 1028) == "block"
+    # block capacity: 16 wavefronts x 64 lanes x 16 (norm) or 32 (softmax) values
+    assert v(rr.RR_OP_RMSNORM, 100, 16384) == "block"
+    assert v(rr.RR_OP_RMSNORM, 100, 16388) == "loop"
+    assert v(S, 100, 32768) == "block"
+    # longer softmax rows: split when rows are few, stream when many
+    assert v(S, 1023, 32772) == "split"
+    assert v(S, 1024, 32772) == "loop"
+    # unaligned widths or pointers take the scalar streaming path
+    assert v(S, 10, 1023) == "loop"
+    assert v(S, 10, 1024, al=False) == "loop"
+    assert rr.rr_query_plan(S, 10, 1023, F, F)["vec_elems"] == 1
+    assert v(rr.RR_OP_RMSNORM, 10, 4100, B, B) == "loop"   # 4100 % 8 != 0
+
+
+def test_forced_variants():
+    S, F = rr.RR_OP_SOFTMAX, rr.RR_F32
+    try:
+        rr.rr_set_variant_override(rr.RR_VARIANT_LOOP)
+        assert rr.rr_query_plan(S, 10, 1024, F, F)["variant_name"] == "loop"
+        rr.rr_set_variant_override(rr.RR_VARIANT_SPLIT)
+        p = rr.rr_query_plan(S, 10, 1024, F, F)
+        assert p["variant_name"] == "split" and p["workspace_bytes"] == 10 * 1 * 8
+        assert rr.rr_softmax_rows_workspace_bytes(10, 1024, F, F) == 80
+        with pytest.raises(rr.RowReduceError):
+            rr.rr_query_plan(rr.RR_OP_RMSNORM, 10, 1024, F, F)   # no split RMSNorm
+        rr.rr_set_variant_override(rr.RR_VARIANT_WAVE)
+        with pytest.raises(rr.RowReduceError):
+            rr.rr_query_plan(S, 10, 4096, F, F)                  # row too long for a wave
+    finally:
+        rr.rr_set_variant_override(rr.RR_VARIANT_AUTO)
+    with pytest.raises(rr.RowReduceError):
+        rr.rr_set_variant_override(9)

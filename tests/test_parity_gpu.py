@@ -1,0 +1,462 @@
+"""GPU parity: the HIP kernels (through the C ABI) against the fp64 oracle.
+
+Inputs come from ``workloads`` (seeded, shared by both sides); expected values
+come only from ``oracle``.  Bars are in tests/compare.py.  Shapes straddle
+every dispatch boundary (a wavefront per row up to 1024/2048 elements, a
+workgroup per row up to 16384/32768, split and streaming beyond), with ragged
+tails, partial workgroups (M = 7), unaligned rows, masked and fully masked
+rows, +1000 offsets and spikes, each variant forced on shapes it supports,
+the named workloads at full size, and run-to-run bitwise determinism.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from tests import compare
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import row_reduction_rmsnorm_amd as rr
+    rr.lib()
+    rr.rr_set_variant_override(rr.RR_VARIANT_AUTO)
+    yield
+    rr.rr_set_variant_override(rr.RR_VARIANT_AUTO)
+
+
+def _rr():
+    import row_reduction_rmsnorm_amd as rr
+    return rr
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+def _tdt(name):
+    return torch.float32 if name == "f32" else torch.bfloat16
+
+
+def _as(x32: np.ndarray, dt: str):
+    return workloads.to_dtype(x32, dt)
+
+
+# ----------------------------------------------------------------------------
+# runners
+# ----------------------------------------------------------------------------
+
+def run_rmsnorm(x_cpu, g_cpu, eps, inplace=False):
+    rr = _rr()
+    x = x_cpu.cuda()
+    g = g_cpu.cuda()
+    y = x if inplace else torch.empty_like(x)
+    rr.rr_rmsnorm(y, x, g, eps)
+    torch.cuda.synchronize()
+    return y.cpu()
+
+
+def run_fused(x_cpu, r_cpu, g_cpu, eps, y_is_x=False):
+    rr = _rr()
+    x = x_cpu.cuda()
+    r = r_cpu.cuda()
+    g = g_cpu.cuda()
+    y = x if y_is_x else torch.empty_like(x)
+    rr.rr_fused_add_rmsnorm(y, r, x, g, eps)
+    torch.cuda.synchronize()
+    return y.cpu(), r.cpu()
+
+
+def run_softmax(x_cpu, out_dt, inplace=False):
+    rr = _rr()
+    x = x_cpu.cuda()
+    y = x if inplace else torch.empty(x.shape, dtype=out_dt, device=x.device)
+    ws = rr.softmax_workspace(x, out_dt)
+    rr.rr_softmax_rows(y, x, ws)
+    torch.cuda.synchronize()
+    return y.cpu()
+
+
+def check_norm(x_cpu, g_cpu, eps, dt, y_cpu, what):
+    ref = oracle.rmsnorm(compare.to_f64(x_cpu), compare.to_f64(g_cpu), eps)
+    if dt == "bf16":
+        return compare.check_bf16(y_cpu, ref, what)
+    return compare.check_rms_f32(y_cpu, ref, what)
+
+
+def check_fused(x_cpu, r_cpu, g_cpu, eps, dt, y_cpu, r_out_cpu, what):
+    h_ref, y_ref = oracle.fused_add_rmsnorm(compare.to_f64(x_cpu), compare.to_f64(r_cpu),
+                                            compare.to_f64(g_cpu), eps, dt)
+    # the new residual is the correctly rounded sum: bit-exact
+    if dt == "bf16":
+        compare.check_bf16_exact(r_out_cpu, h_ref, what + " residual")
+        return compare.check_bf16(y_cpu, y_ref, what + " y")
+    assert np.array_equal(compare.to_f64(r_out_cpu), h_ref), what + " residual"
+    return compare.check_rms_f32(y_cpu, y_ref, what + " y")
+
+
+def check_softmax(x_cpu, y_cpu, what):
+    xf = compare.to_f64(x_cpu)
+    ref = oracle.softmax(xf)
+    return compare.check_softmax(y_cpu, xf.reshape(ref.shape), ref, what)
+
+
+def softmax_input(M, N, seed, dt):
+    """N(0, 8) rows; every third row +1000; rows with 30% masked entries;
+    row 2 fully masked (when it exists) and one spike per row."""
+    x = workloads.random_rows(M, N, seed, scale=8.0, offset_every=3, offset=1000.0)
+    rng = np.random.default_rng(seed + 1)
+    if M > 1 and N > 1:
+        mask = rng.random((M, N)) < 0.3
+        mask[:, 0] = False
+        mask[::2] = False
+        x[mask] = -np.inf
+    if N > 4:
+        cols = rng.integers(0, N, M)
+        x[np.arange(M), cols] = rng.uniform(20, 30, M).astype(np.float32)
+    if M > 2:
+        x[2, :] = -np.inf
+    return _as(x, dt)
+
+
+# ----------------------------------------------------------------------------
+# the wave64 all-reduce primitive
+# ----------------------------------------------------------------------------
+
+def test_wave_allreduce_lane_ids_spikes_and_bitwise_equal_lanes():
+    rr = _rr()
+    groups = []
+    groups.append(np.arange(64, dtype=np.float32))                 # lane ids
+    for k in range(64):                                            # a spike in each lane
+        g = np.zeros(64, np.float32)
+        g[k] = 1.0
+        groups.append(g)
+    groups.append(np.ones(64, np.float32))                         # 64 lanes x 1 -> 64
+    rng = np.random.default_rng(5)
+    for _ in range(32):
+        groups.append(rng.standard_normal(64).astype(np.float32) * 100)
+    inp = torch.from_numpy(np.concatenate(groups)).cuda()
+    out = torch.empty_like(inp)
+    rr.rr_selftest_wave_allreduce(out, inp, 0)
+    s = out.cpu().numpy().reshape(-1, 64)
+    assert np.all(s == s[:, :1]), "lanes differ after the sum all-reduce"
+    ref = np.array([np.sum(g.astype(np.float64)) for g in groups])
+    assert s[0, 0] == 2016.0 and np.all(s[1:65, 0] == 1.0) and s[65, 0] == 64.0
+    assert np.allclose(s[:, 0], ref, rtol=1e-5, atol=1e-2)
+    rr.rr_selftest_wave_allreduce(out, inp, 1)
+    mx = out.cpu().numpy().reshape(-1, 64)
+    assert np.all(mx == mx[:, :1])
+    assert np.array_equal(mx[:, 0], np.array([g.max() for g in groups]))
+
+
+def test_wave_allreduce_md_pairs():
+    from oracle import online_ref
+    rr = _rr()
+    rng = np.random.default_rng(6)
+    cases = []
+    for _ in range(40):
+        m = (rng.standard_normal(64) * 10).astype(np.float32)
+        d = rng.uniform(1, 3, 64).astype(np.float32)
+        cases.append((m, d))
+    m = np.full(64, -np.inf, np.float32)
+    cases.append((m, np.zeros(64, np.float32)))                    # all identity
+    m = (rng.standard_normal(64) * 5).astype(np.float32)
+    d = np.ones(64, np.float32)
+    m[::3] = -np.inf
+    d[::3] = 0.0
+    cases.append((m, d))                                           # mixed identity
+    for k in (0, 17, 63):                                          # one finite lane
+        m = np.full(64, -np.inf, np.float32)
+        d = np.zeros(64, np.float32)
+        m[k], d[k] = 1000.0, 2.0
+        cases.append((m, d))
+    inp = torch.from_numpy(np.concatenate([np.concatenate(c) for c in cases])).cuda()
+    out = torch.empty_like(inp)
+    rr.rr_selftest_wave_allreduce(out, inp, 2)
+    res = out.cpu().numpy().reshape(-1, 2, 64)
+    for i, (m, d) in enumerate(cases):
+        gm, gd = res[i, 0], res[i, 1]
+        assert np.all(gm == gm[0]) and np.all(gd == gd[0]), f"case {i}: lanes differ"
+        acc = online_ref.IDENTITY
+        for a, b in zip(m.astype(float), d.astype(float)):
+            acc = online_ref.merge(acc, (a, b))
+        assert gm[0] == np.float32(acc[0])
+        if acc[0] == -np.inf:
+            assert gd[0] == 0.0
+        else:
+            assert abs(gd[0] - acc[1]) <= 1e-5 * acc[1], (i, gd[0], acc)
+
+
+# ----------------------------------------------------------------------------
+# RMSNorm and fused add + RMSNorm over the shape grid
+# ----------------------------------------------------------------------------
+
+NORM_N = [1, 7, 64, 65, 1000, 1024, 1028, 2048, 3584, 4096, 8191, 16384, 16392]
+NORM_M = [1, 7, 64]
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("N", NORM_N)
+def test_rmsnorm_grid(dt, N):
+    for M in NORM_M:
+        _say(f"rmsnorm {dt} M={M} N={N}")
+        x = _as(workloads.random_rows(M, N, seed=N + M, scale=2.0), dt)
+        g = _as(workloads.gamma_vector(N, seed=N), dt)
+        y = run_rmsnorm(x, g, 1e-6)
+        check_norm(x, g, 1e-6, dt, y, f"rmsnorm {dt} {M}x{N}")
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("N", NORM_N)
+def test_fused_grid(dt, N):
+    for M in NORM_M:
+        _say(f"fused {dt} M={M} N={N}")
+        x = _as(workloads.random_rows(M, N, seed=N + M), dt)
+        r = _as(workloads.random_rows(M, N, seed=N + M + 100, scale=3.0), dt)
+        g = _as(workloads.gamma_vector(N, seed=N + 1), dt)
+        y, r_out = run_fused(x, r, g, 1e-6)
+        check_fused(x, r, g, 1e-6, dt, y, r_out, f"fused {dt} {M}x{N}")
+
+
+def test_norm_edge_cases():
+    rr = _rr()
+    # zero rows, constant rows, huge and tiny magnitudes, eps = 0
+    for dt in ("f32", "bf16"):
+        M, N = 6, 4096
+        x = workloads.random_rows(M, N, seed=1)
+        x[0] = 0.0                       # all-zero row with eps > 0 -> y = 0
+        x[1] = 3.0                       # constant row
+        x[2] *= 1e15                     # large magnitudes (sum of squares ~4e33, inside fp32)
+        x[3] *= 1e-15                    # small magnitudes (squares well above fp32 subnormals)
+        xt, g = _as(x, dt), _as(workloads.gamma_vector(N, 2), dt)
+        check_norm(xt, g, 1e-6, dt, run_rmsnorm(xt, g, 1e-6), f"edge {dt}")
+        x[0] = 1.0
+        xt = _as(x, dt)
+        check_norm(xt, g, 0.0, dt, run_rmsnorm(xt, g, 0.0), f"edge eps0 {dt}")
+    # M = 0 leaves the output untouched
+    y = torch.full((0, 64), 7.0, device="cuda")
+    rr.rr_rmsnorm(y, torch.empty((0, 64), device="cuda"), torch.ones(64, device="cuda"), 1e-6)
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_norm_in_place_and_unaligned(dt):
+    rr = _rr()
+    M, N = 9, 4096
+    x = _as(workloads.random_rows(M, N, seed=3), dt)
+    g = _as(workloads.gamma_vector(N, 4), dt)
+    check_norm(x, g, 1e-6, dt, run_rmsnorm(x, g, 1e-6, inplace=True), "in place")
+    r = _as(workloads.random_rows(M, N, seed=5), dt)
+    y, r_out = run_fused(x, r, g, 1e-6, y_is_x=True)
+    check_fused(x, r, g, 1e-6, dt, y, r_out, "fused y is x")
+    # unaligned rows: views one element into a buffer
+    base = torch.empty(M * N + 1, dtype=_tdt(dt), device="cuda")
+    xv = base[1:].view(M, N)
+    xv.copy_(x.cuda())
+    y = torch.empty(M * N + 1, dtype=_tdt(dt), device="cuda")[1:].view(M, N)
+    plan = rr.rr_query_plan(rr.RR_OP_RMSNORM, M, N, rr.dtype_code(xv), rr.dtype_code(xv), False)
+    assert plan["variant_name"] == "loop" and plan["vec_elems"] == 1
+    rr.rr_rmsnorm(y, xv, g.cuda(), 1e-6)
+    torch.cuda.synchronize()
+    check_norm(x, g, 1e-6, dt, y.cpu(), "unaligned")
+
+
+@pytest.mark.parametrize("variant", ["wave", "block", "loop"])
+def test_norm_forced_variants(variant):
+    rr = _rr()
+    code = {"wave": rr.RR_VARIANT_WAVE, "block": rr.RR_VARIANT_BLOCK, "loop": rr.RR_VARIANT_LOOP}[variant]
+    shapes = {"wave": [8, 64, 520, 1024], "block": [8, 1024, 3584, 4096, 16384],
+              "loop": [8, 1024, 4096, 20000, 65536]}[variant]
+    try:
+        rr.rr_set_variant_override(code)
+        for dt in ("f32", "bf16"):
+            for N in shapes:
+                for M in (1, 7, 130):
+                    _say(f"norm forced {variant} {dt} M={M} N={N}")
+                    x = _as(workloads.random_rows(M, N, seed=M * 7 + N), dt)
+                    g = _as(workloads.gamma_vector(N, seed=N), dt)
+                    check_norm(x, g, 1e-6, dt, run_rmsnorm(x, g, 1e-6), f"{variant} {dt} {M}x{N}")
+                    r = _as(workloads.random_rows(M, N, seed=M + N), dt)
+                    y, r_out = run_fused(x, r, g, 1e-6)
+                    check_fused(x, r, g, 1e-6, dt, y, r_out, f"{variant} fused {dt} {M}x{N}")
+    finally:
+        rr.rr_set_variant_override(rr.RR_VARIANT_AUTO)
+
+
+# ----------------------------------------------------------------------------
+# softmax over the shape grid
+# ----------------------------------------------------------------------------
+
+SOFTMAX_N = [1, 7, 63, 64, 65, 1000, 1023, 1024, 1025, 2047, 2048, 2049, 2056, 3584, 4096,
+             8191, 16384, 16385, 32768, 50000, 152064]
+DTYPES = [("f32", "f32"), ("bf16", "f32"), ("f32", "bf16"), ("bf16", "bf16")]
+
+
+@pytest.mark.parametrize("din,dout", DTYPES)
+@pytest.mark.parametrize("N", SOFTMAX_N)
+def test_softmax_grid(din, dout, N):
+    for M in ([1, 7, 64] if N < 50000 else [1, 7, 40]):
+        _say(f"softmax {din}->{dout} M={M} N={N}")
+        x = softmax_input(M, N, seed=N + 3 * M, dt=din)
+        y = run_softmax(x, _tdt(dout))
+        check_softmax(x, y, f"softmax {din}->{dout} {M}x{N}")
+
+
+def test_softmax_many_rows_and_partial_groups():
+    for (M, N) in [(257, 1024), (1023, 33000), (1024, 33000), (4097, 64)]:
+        _say(f"softmax rows M={M} N={N}")
+        x = softmax_input(M, N, seed=M, dt="f32")
+        check_softmax(x, run_softmax(x, torch.float32), f"{M}x{N}")
+
+
+@pytest.mark.parametrize("variant", ["wave", "block", "split", "loop"])
+def test_softmax_forced_variants(variant):
+    rr = _rr()
+    code = {"wave": rr.RR_VARIANT_WAVE, "block": rr.RR_VARIANT_BLOCK,
+            "split": rr.RR_VARIANT_SPLIT, "loop": rr.RR_VARIANT_LOOP}[variant]
+    shapes = {"wave": [8, 64, 1024, 2048], "block": [8, 1024, 4096, 16384, 32768],
+              "split": [8, 1024, 4096, 4104, 65536], "loop": [8, 1024, 4096, 100000]}[variant]
+    try:
+        rr.rr_set_variant_override(code)
+        for din, dout in DTYPES:
+            for N in shapes:
+                if variant == "wave" and din == "bf16" and N > 2048:
+                    continue
+                for M in (1, 7, 33):
+                    _say(f"softmax forced {variant} {din}->{dout} M={M} N={N}")
+                    x = softmax_input(M, N, seed=M + N, dt=din)
+                    y = run_softmax(x, _tdt(dout))
+                    check_softmax(x, y, f"{variant} {din}->{dout} {M}x{N}")
+    finally:
+        rr.rr_set_variant_override(rr.RR_VARIANT_AUTO)
+
+
+def test_softmax_in_place_unaligned_and_tiny():
+    rr = _rr()
+    for dt in ("f32", "bf16"):
+        x = softmax_input(9, 4096, seed=11, dt=dt)
+        check_softmax(x, run_softmax(x, _tdt(dt), inplace=True), f"in place {dt}")
+    # unaligned input pointer
+    M, N = 5, 3000
+    x = softmax_input(M, N, seed=12, dt="f32")
+    base = torch.empty(M * N + 1, device="cuda")
+    xv = base[1:].view(M, N)
+    xv.copy_(x.cuda())
+    y = torch.empty(M, N, device="cuda")
+    rr.rr_softmax_rows(y, xv, None)
+    torch.cuda.synchronize()
+    check_softmax(x, y.cpu(), "unaligned")
+    # the pages' worked examples, through the kernels
+    for row in ([1000.0, 1001.0], [1.0, 3.0, 2.0], [2.0, 4.0, 1.0], [1.0, 2.0, 5.0, 3.0]):
+        x = torch.tensor([row], dtype=torch.float32)
+        y = run_softmax(x, torch.float32)
+        check_softmax(x, y, f"example {row}")
+    # N = 1: probability 1, or NaN for a masked entry
+    x = torch.tensor([[5.0], [-np.inf], [0.0]], dtype=torch.float32)
+    y = run_softmax(x, torch.float32).numpy()
+    assert y[0, 0] == 1.0 and np.isnan(y[1, 0]) and y[2, 0] == 1.0
+
+
+def test_softmax_shift_invariance_bitwise():
+    # adding an exact constant to every entry of a dyadic row changes no
+    # x - m and so no output bit (same kernel, same order)
+    M, N = 64, 4096
+    x = workloads.random_rows(M, N, seed=21)
+    x = np.round(x * 64) / 64
+    y1 = run_softmax(_as(x, "f32"), torch.float32)
+    y2 = run_softmax(_as(x + np.float32(512.0), "f32"), torch.float32)
+    assert torch.equal(y1, y2)
+
+
+def test_determinism_run_to_run():
+    rr = _rr()
+    for name in ("fused", "sm_wave"):
+        w = workloads.make(name, rows=1024)
+        outs = []
+        for _ in range(3):
+            if w.op == "fused_add_rmsnorm":
+                y, r = run_fused(w.arrays["x"], w.arrays["residual"], w.arrays["gamma"], w.eps)
+                outs.append(torch.cat([y.view(-1).float(), r.view(-1).float()]))
+            else:
+                outs.append(run_softmax(w.arrays["x"], torch.float32))
+        assert all(torch.equal(outs[0], o) for o in outs[1:]), name
+    x = softmax_input(8, 152064, seed=2, dt="bf16")
+    a = run_softmax(x, torch.float32)
+    b = run_softmax(x, torch.float32)
+    assert torch.equal(a, b)
+    rr.rr_set_variant_override(rr.RR_VARIANT_AUTO)
+
+
+# ----------------------------------------------------------------------------
+# the named workloads at full size, in the launch configuration the benchmark
+# times (automatic dispatch, default grid)
+# ----------------------------------------------------------------------------
+
+def test_workload_rms_f32_full():
+    w = workloads.make("rms_f32")
+    _say(w.description)
+    y = run_rmsnorm(w.arrays["x"], w.arrays["gamma"], w.eps)
+    info = check_norm(w.arrays["x"], w.arrays["gamma"], w.eps, "f32", y, w.name)
+    _say(info)
+
+
+def test_workload_fused_full():
+    w = workloads.make("fused")
+    _say(w.description)
+    y, r_out = run_fused(w.arrays["x"], w.arrays["residual"], w.arrays["gamma"], w.eps)
+    info = check_fused(w.arrays["x"], w.arrays["residual"], w.arrays["gamma"], w.eps, "bf16",
+                       y, r_out, w.name)
+    _say(info)
+
+
+def test_workload_rmsnorm_bf16_8192x4096_full():
+    w = workloads.make("fused")
+    _say("rmsnorm bf16 8192x4096 (the fused workload's x and gamma)")
+    y = run_rmsnorm(w.arrays["x"], w.arrays["gamma"], w.eps)
+    _say(check_norm(w.arrays["x"], w.arrays["gamma"], w.eps, "bf16", y, "rmsnorm bf16"))
+
+
+def test_workload_sm_wave_full():
+    w = workloads.make("sm_wave")
+    _say(w.description)
+    y = run_softmax(w.arrays["x"], torch.float32)
+    _say(check_softmax(w.arrays["x"], y, w.name))
+
+
+def test_workload_sm_vocab_full():
+    w = workloads.make("sm_vocab")
+    _say(w.description)
+    y = run_softmax(w.arrays["x"], torch.float32)
+    _say(check_softmax(w.arrays["x"], y, w.name))
+
+
+def test_workload_sm_causal_full_sampled():
+    """All 114688 rows run on the GPU; sampled rows against the oracle, and
+    properties checked on every row (sum 1, masked keys exactly 0, finite,
+    non-negative)."""
+    w = workloads.make("sm_causal")
+    _say(w.description)
+    x = w.arrays["x"].cuda()
+    y = torch.empty_like(x)
+    _rr().rr_softmax_rows(y, x, None)
+    torch.cuda.synchronize()
+    M, N = x.shape
+    rows = sorted({0, 1, 2, 63, 64, 1000, 2047, 2048, 4094, 4095, 4096, 4097, 8191,
+                   M // 2, M - 4096, M - 2, M - 1} |
+                  set(np.random.default_rng(7).integers(0, M, 48).tolist()))
+    xs = w.arrays["x"][rows]
+    ys = y[rows].cpu()
+    _say(check_softmax(xs, ys, "sm_causal sampled"))
+    # every row: sum to 1, masked entries exactly 0, finite and >= 0
+    rs = y.double().sum(dim=1)
+    assert float((rs - 1.0).abs().max()) <= compare.SOFTMAX_ROWSUM_ATOL
+    masked = torch.isneginf(x)
+    assert int((y[masked] != 0).sum()) == 0
+    assert bool(torch.isfinite(y).all()) and bool((y >= 0).all())
+    # the number of masked keys in row r is 4095 - (r mod 4096)
+    nm = masked.sum(dim=1).cpu().numpy()
+    assert np.array_equal(nm, 4095 - (np.arange(M) % 4096))
