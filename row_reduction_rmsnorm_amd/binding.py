@@ -9,7 +9,8 @@ import ctypes
 import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "librowreduce.so")
+# The in-tree build; ROWREDUCE_LIB may name another build of the same library.
+LIB_PATH = os.environ.get("ROWREDUCE_LIB") or os.path.join(HERE, "librowreduce.so")
 
 RR_F32 = 0
 RR_BF16 = 1
@@ -75,6 +76,8 @@ def lib():
     if _LIB is not None:
         return _LIB
     if not os.path.exists(LIB_PATH):
+        if os.environ.get("ROWREDUCE_LIB"):
+            raise ImportError(f"ROWREDUCE_LIB={LIB_PATH} does not exist")
         from . import build as _build
         _build.build()
     try:

@@ -55,11 +55,19 @@ int pow2_at_least(int64_t v) {
 }
 
 constexpr int64_t kMaxN = (int64_t)1 << 30;  // keeps every in-row index in int32
-constexpr int kWaveMaxFloats = 32;           // per-lane register budget (fp32 values)
-constexpr int kBlockFloats = 16;             // preferred per-lane share in a block
 constexpr int kMaxWaves = rr::kMaxWavesPerGroup;
 constexpr int kWaveRowsPerGroup = 4;         // rows per 256-thread workgroup (WAVE)
 constexpr int64_t kSplitMaxRows = 1024;      // SPLIT only below this many rows
+// 16-byte loads each lane keeps in flight per row in the workgroup-per-row
+// kernels (summed over the input tensors); more wavefronts per row rather
+// than more registers per lane measured faster on MI355X.
+constexpr int kLoadsPerLane = 2;
+
+// Register budget per lane, in fp32 values held for the row: softmax keeps
+// one array (x, then e_i); the norms keep x (and the residual) plus gamma,
+// so they stop at 16 values per lane and longer rows stream (LOOP).
+int max_floats(rr_op op) { return op == RR_OP_SOFTMAX ? 32 : 16; }
+int inputs_of(rr_op op) { return op == RR_OP_FUSED_ADD_RMSNORM ? 2 : 1; }
 
 void plan_wave(rr_plan* p, int vec, int64_t nvec) {
   p->variant = RR_VARIANT_WAVE;
@@ -70,18 +78,16 @@ void plan_wave(rr_plan* p, int vec, int64_t nvec) {
   p->block_threads = 64 * kWaveRowsPerGroup;
 }
 
-// Register budget per lane, in fp32 values held for the row: softmax keeps
-// one array (x, then e_i), the fused norm two (x and the residual) plus gamma,
-// so the norms stop at 16 values per lane and longer rows stream (LOOP).
-int wave_max_floats(rr_op op) { return op == RR_OP_SOFTMAX ? kWaveMaxFloats : kBlockFloats; }
+bool wave_fits(rr_op op, int vec, int64_t nvec) { return nvec <= 64 * (max_floats(op) / vec); }
 
-bool wave_fits(rr_op op, int vec, int64_t nvec) { return nvec <= 64 * (wave_max_floats(op) / vec); }
-
-// Workgroup-per-row: NV vectors per lane giving 16 fp32 values per lane;
-// softmax may double that once if the row needs more than 16 wavefronts.
+// Workgroup-per-row: NV vectors per lane such that each lane has
+// kLoadsPerLane loads in flight, then as many wavefronts as the row needs
+// (at most 16); NV doubles while the row needs more than 16 wavefronts and
+// the lane's register budget allows.
 bool plan_block(rr_op op, rr_plan* p, int vec, int64_t nvec) {
-  const int max_nv = (op == RR_OP_SOFTMAX ? 2 : 1) * kBlockFloats / vec;
-  for (int nv = kBlockFloats / vec; nv <= max_nv; nv *= 2) {
+  int nv = kLoadsPerLane / inputs_of(op);
+  if (nv < 1) nv = 1;
+  for (; nv * vec <= max_floats(op); nv *= 2) {
     const int64_t wpr = ceil_div(nvec, 64 * (int64_t)nv);
     if (wpr <= kMaxWaves) {
       p->variant = RR_VARIANT_BLOCK;
@@ -101,7 +107,7 @@ void plan_split(rr_plan* p, int vec, int64_t nvec) {
   p->vec_elems = vec;
   p->waves_per_row = 4;
   p->rows_per_group = 1;
-  p->vecs_per_lane = kBlockFloats / vec;
+  p->vecs_per_lane = 16 / vec;
   p->block_threads = 256;
   p->chunks_per_row = ceil_div(nvec, 256 * (int64_t)p->vecs_per_lane);
 }

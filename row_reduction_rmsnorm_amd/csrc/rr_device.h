@@ -53,6 +53,9 @@ struct Elem<bf16_t> {
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 hw_bf16x2 __attribute__((ext_vector_type(2)));
 typedef float hw_f32x2 __attribute__((ext_vector_type(2)));
 
@@ -75,28 +78,44 @@ __device__ __forceinline__ float round_to(float v) {
   else return v;
 }
 
+// Streaming accesses carry the non-temporal hint (the `nt` bit of the
+// global load/store): row data is touched once, so it should not displace
+// reusable lines (gamma, the split-row workspace) from the caches.  A load
+// whose data is read again soon (the split-row first pass, whose chunk the
+// second pass re-reads) uses NT = false.
+template <bool NT, typename V>
+__device__ __forceinline__ V ld(const V* p) {
+  if constexpr (NT) return __builtin_nontemporal_load(p);
+  else return *p;
+}
+template <bool NT, typename V>
+__device__ __forceinline__ void st(V* p, V v) {
+  if constexpr (NT) __builtin_nontemporal_store(v, p);
+  else *p = v;
+}
+
 // Load VEC consecutive elements at p into fp32.  VEC * sizeof(T) == 16 is
 // one 16-byte load (p must be 16-byte aligned); VEC == 1 is a scalar load.
-template <typename T, int VEC>
+template <typename T, int VEC, bool NT = true>
 __device__ __forceinline__ void load_vec(const T* __restrict__ p, float (&v)[VEC]) {
   if constexpr (std::is_same_v<T, float>) {
     if constexpr (VEC == 4) {
-      float4 q = *reinterpret_cast<const float4*>(p);
+      const f32x4_t q = ld<NT>(reinterpret_cast<const f32x4_t*>(p));
       v[0] = q.x; v[1] = q.y; v[2] = q.z; v[3] = q.w;
     } else {
       static_assert(VEC == 1, "fp32 loads are 1 or 4 wide");
-      v[0] = p[0];
+      v[0] = ld<NT>(p);
     }
   } else {
     if constexpr (VEC == 8) {
-      uint4 q = *reinterpret_cast<const uint4*>(p);
+      const u32x4_t q = ld<NT>(reinterpret_cast<const u32x4_t*>(p));
       v[0] = bf16_lo(q.x); v[1] = bf16_hi(q.x);
       v[2] = bf16_lo(q.y); v[3] = bf16_hi(q.y);
       v[4] = bf16_lo(q.z); v[5] = bf16_hi(q.z);
       v[6] = bf16_lo(q.w); v[7] = bf16_hi(q.w);
     } else {
       static_assert(VEC == 1, "bf16 loads are 1 or 8 wide");
-      v[0] = __uint_as_float(static_cast<uint32_t>(p[0]) << 16);
+      v[0] = __uint_as_float(static_cast<uint32_t>(ld<NT>(p)) << 16);
     }
   }
 }
@@ -129,36 +148,29 @@ struct Packed {
   }
 };
 
-// Store VEC fp32 values at p as T (bf16: round to nearest even).  Widths:
-// fp32 4 or 8 (one or two 16-byte stores), bf16 8 (16 bytes) or 4 (8 bytes),
-// or 1 (scalar).
-template <typename T, int VEC>
+// Store VEC fp32 values at p as T (bf16: round to nearest even), with the
+// non-temporal hint unless NT is false.  Widths: fp32 4 or 8 (one or two
+// 16-byte stores), bf16 8 (16 bytes) or 4 (8 bytes), or 1 (scalar).
+template <typename T, int VEC, bool NT = true>
 __device__ __forceinline__ void store_vec(T* __restrict__ p, const float (&v)[VEC]) {
   if constexpr (std::is_same_v<T, float>) {
     if constexpr (VEC % 4 == 0) {
 #pragma unroll
       for (int i = 0; i < VEC / 4; ++i)
-        reinterpret_cast<float4*>(p)[i] = make_float4(v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]);
+        st<NT>(reinterpret_cast<f32x4_t*>(p) + i, f32x4_t{v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]});
     } else {
       static_assert(VEC == 1, "fp32 stores are 1, 4 or 8 wide");
-      p[0] = v[0];
+      st<NT>(p, v[0]);
     }
   } else {
     if constexpr (VEC == 8) {
-      uint4 q;
-      q.x = pack_bf16x2(v[0], v[1]);
-      q.y = pack_bf16x2(v[2], v[3]);
-      q.z = pack_bf16x2(v[4], v[5]);
-      q.w = pack_bf16x2(v[6], v[7]);
-      *reinterpret_cast<uint4*>(p) = q;
+      st<NT>(reinterpret_cast<u32x4_t*>(p), u32x4_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
+                                                 pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7])});
     } else if constexpr (VEC == 4) {
-      uint2 q;
-      q.x = pack_bf16x2(v[0], v[1]);
-      q.y = pack_bf16x2(v[2], v[3]);
-      *reinterpret_cast<uint2*>(p) = q;
+      st<NT>(reinterpret_cast<u32x2_t*>(p), u32x2_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])});
     } else {
       static_assert(VEC == 1, "bf16 stores are 1, 4 or 8 wide");
-      p[0] = static_cast<bf16_t>(pack_bf16x2(v[0], 0.0f) & 0xffffu);
+      st<NT>(p, static_cast<bf16_t>(pack_bf16x2(v[0], 0.0f) & 0xffffu));
     }
   }
 }

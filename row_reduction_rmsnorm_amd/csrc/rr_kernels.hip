@@ -59,25 +59,39 @@ __device__ __forceinline__ MD group_md(MD v, int nw, int w, int lane,
   return t;
 }
 
-// Thread coordinates inside a launch of the register kernels.
+// Thread coordinates.  WAVE: each wavefront owns a row, the workgroup holds
+// blockDim/64 rows.  Otherwise the whole workgroup (blockDim/64 wavefronts)
+// owns one row.
 struct RowLane {
   int lane;   // 0..63
   int w;      // wavefront within the row
+  int nw;     // wavefronts per row
   int g;      // row slot within the workgroup
   int t;      // lane within the row (0 .. T-1)
   int T;      // lanes per row
   int rpg;    // rows per workgroup step
 };
 
-__device__ __forceinline__ RowLane row_lane(int wpr) {
+template <bool WAVE>
+__device__ __forceinline__ RowLane row_lane() {
   RowLane r;
   const int wave = threadIdx.x >> 6;
   r.lane = threadIdx.x & 63;
-  r.rpg = (blockDim.x >> 6) / wpr;
-  r.g = wave / wpr;
-  r.w = wave - r.g * wpr;
-  r.T = wpr * kWave;
-  r.t = r.w * kWave + r.lane;
+  if constexpr (WAVE) {
+    r.w = 0;
+    r.nw = 1;
+    r.g = wave;
+    r.t = r.lane;
+    r.T = kWave;
+    r.rpg = blockDim.x >> 6;
+  } else {
+    r.w = wave;
+    r.nw = blockDim.x >> 6;
+    r.g = 0;
+    r.t = threadIdx.x;
+    r.T = blockDim.x;
+    r.rpg = 1;
+  }
   return r;
 }
 
@@ -95,13 +109,13 @@ __device__ __forceinline__ RowLane row_lane(int wpr) {
 // precision plus two bits, so rounding the fp32 sum to bf16 gives the
 // correctly rounded sum.
 // ===========================================================================
-template <typename T, int NV, bool FUSED>
+template <typename T, int NV, bool FUSED, bool WAVE>
 __global__ __launch_bounds__(1024) void norm_regs_kernel(T* y, T* residual, const T* x,
                                                          const T* __restrict__ gamma, int64_t M,
-                                                         int N, float eps, int wpr) {
+                                                         int N, float eps) {
   constexpr int VEC = Elem<T>::kVec;
   __shared__ float slots[2][kMaxWavesPerGroup];
-  const RowLane rl = row_lane(wpr);
+  const RowLane rl = row_lane<WAVE>();
   const int nvec = N / VEC;
 
   Packed<T, VEC> gv[NV];
@@ -156,8 +170,8 @@ __global__ __launch_bounds__(1024) void norm_regs_kernel(T* y, T* residual, cons
 #pragma unroll
       for (int i = 0; i < VEC; ++i) ss += h[k][i] * h[k][i];
     ss = wave_sum(ss);
-    if (wpr > 1) {
-      ss = group_sum(ss, wpr, rl.w, rl.lane, slots, parity);
+    if constexpr (!WAVE) {
+      ss = group_sum(ss, rl.nw, rl.w, rl.lane, slots, parity);
       parity ^= 1;
     }
     // eps inside the root, mean over N ([P5] section "RMSNorm 归约什么").
@@ -185,7 +199,7 @@ __global__ __launch_bounds__(1024) void norm_loop_kernel(T* y, T* residual, cons
                                                          const T* __restrict__ gamma, int64_t M,
                                                          int N, float eps) {
   __shared__ float slots[2][kMaxWavesPerGroup];
-  const RowLane rl = row_lane(blockDim.x >> 6);
+  const RowLane rl = row_lane<false>();
   const int nvec = N / VEC;
   int parity = 0;
   for (int64_t row = blockIdx.x; row < M; row += gridDim.x) {
@@ -205,7 +219,7 @@ __global__ __launch_bounds__(1024) void norm_loop_kernel(T* y, T* residual, cons
       for (int i = 0; i < VEC; ++i) ss += h[i] * h[i];
     }
     ss = wave_sum(ss);
-    ss = group_sum(ss, rl.T / kWave, rl.w, rl.lane, slots, parity);
+    ss = group_sum(ss, rl.nw, rl.w, rl.lane, slots, parity);
     parity ^= 1;
     const float rstd = 1.0f / __builtin_sqrtf(ss / (float)N + eps);
     const T* src = FUSED ? residual : x;
@@ -236,12 +250,12 @@ __global__ __launch_bounds__(1024) void norm_loop_kernel(T* y, T* residual, cons
 // entries are all -inf has m_l = -inf and c_l = 0; a row whose entries are
 // all -inf has m = -inf and every output is NaN, as exp(x - m)/d is.
 // ===========================================================================
-template <typename Tin, typename Tout, int NV>
+template <typename Tin, typename Tout, int NV, bool WAVE>
 __global__ __launch_bounds__(1024) void softmax_regs_kernel(const Tin* x, Tout* y, int64_t M,
-                                                            int N, int wpr) {
+                                                            int N) {
   constexpr int VEC = Elem<Tin>::kVec;
   __shared__ MD slots[2][kMaxWavesPerGroup];
-  const RowLane rl = row_lane(wpr);
+  const RowLane rl = row_lane<WAVE>();
   const int nvec = N / VEC;
   const int64_t stride = (int64_t)gridDim.x * rl.rpg;
   int parity = 0;
@@ -277,8 +291,8 @@ __global__ __launch_bounds__(1024) void softmax_regs_kernel(const Tin* x, Tout* 
     p.m = ml;
     p.d = dl;
     p = wave_md(p);
-    if (wpr > 1) {
-      p = group_md(p, wpr, rl.w, rl.lane, slots, parity);
+    if constexpr (!WAVE) {
+      p = group_md(p, rl.nw, rl.w, rl.lane, slots, parity);
       parity ^= 1;
     }
     float c = (ml == kNegInf) ? 0.0f : exp_shifted(ml - p.m) / p.d;
@@ -307,7 +321,7 @@ template <typename Tin, typename Tout, int VEC>
 __global__ __launch_bounds__(1024) void softmax_loop_kernel(const Tin* x, Tout* y, int64_t M,
                                                             int N) {
   __shared__ MD slots[2][kMaxWavesPerGroup];
-  const RowLane rl = row_lane(blockDim.x >> 6);
+  const RowLane rl = row_lane<false>();
   const int nvec = N / VEC;
   int parity = 0;
   for (int64_t row = blockIdx.x; row < M; row += gridDim.x) {
@@ -321,7 +335,7 @@ __global__ __launch_bounds__(1024) void softmax_loop_kernel(const Tin* x, Tout* 
       p = md_merge(p, chunk_summary<VEC>(v));
     }
     p = wave_md(p);
-    p = group_md(p, rl.T / kWave, rl.w, rl.lane, slots, parity);
+    p = group_md(p, rl.nw, rl.w, rl.lane, slots, parity);
     parity ^= 1;
     const float inv_d = (p.m == kNegInf) ? __builtin_nanf("") : 1.0f / p.d;
     for (int vi = rl.t; vi < nvec; vi += rl.T) {
@@ -355,7 +369,7 @@ __global__ __launch_bounds__(256) void softmax_split_stats_kernel(const Tin* x, 
   constexpr int kThreads = 256;
   constexpr int CV = kThreads * NV;
   __shared__ MD slots[2][kMaxWavesPerGroup];
-  const RowLane rl = row_lane(kThreads / kWave);
+  const RowLane rl = row_lane<false>();
   const int nvec = N / VEC;
   const int64_t items = M * (int64_t)S;
   int parity = 0;
@@ -368,7 +382,8 @@ __global__ __launch_bounds__(256) void softmax_split_stats_kernel(const Tin* x, 
     for (int k = 0; k < NV; ++k) {
       const int vi = c * CV + k * kThreads + rl.t;
       if (vi < nvec) {
-        load_vec<Tin, VEC>(x + off + (int64_t)vi * VEC, v[k]);
+        // temporal load: pass B reads this chunk again right after
+        load_vec<Tin, VEC, false>(x + off + (int64_t)vi * VEC, v[k]);
       } else {
 #pragma unroll
         for (int i = 0; i < VEC; ++i) v[k][i] = kNegInf;
@@ -389,7 +404,7 @@ __global__ __launch_bounds__(256) void softmax_split_stats_kernel(const Tin* x, 
     p.m = ml;
     p.d = dl;
     p = wave_md(p);
-    p = group_md(p, kThreads / kWave, rl.w, rl.lane, slots, parity);
+    p = group_md(p, rl.nw, rl.w, rl.lane, slots, parity);
     parity ^= 1;
     if (threadIdx.x == 0) ws[item] = make_float2(p.m, p.d);
   }
@@ -402,7 +417,7 @@ __global__ __launch_bounds__(256) void softmax_split_apply_kernel(const Tin* x, 
   constexpr int VEC = Elem<Tin>::kVec;
   constexpr int kThreads = 256;
   constexpr int CV = kThreads * NV;
-  const RowLane rl = row_lane(kThreads / kWave);
+  const RowLane rl = row_lane<false>();
   const int nvec = N / VEC;
   const int64_t items = M * (int64_t)S;
   for (int64_t item = blockIdx.x; item < items; item += gridDim.x) {
@@ -438,7 +453,8 @@ __global__ __launch_bounds__(256) void softmax_split_apply_kernel(const Tin* x, 
       float o[VEC];
 #pragma unroll
       for (int i = 0; i < VEC; ++i) o[i] = exp_shifted(v[k][i] - p.m) * inv_d;
-      if (vi < nvec) store_vec<Tout, VEC>(y + off + (int64_t)vi * VEC, o);
+      // plain (write-back) stores: measured faster than non-temporal ones here
+      if (vi < nvec) store_vec<Tout, VEC, false>(y + off + (int64_t)vi * VEC, o);
     }
   }
 }
@@ -470,7 +486,7 @@ namespace {
 
 inline dim3 grid1(int64_t g) { return dim3((unsigned)g, 1, 1); }
 
-template <typename T, bool FUSED>
+template <typename T, bool FUSED, bool WAVE>
 hipError_t norm_regs(const rr_plan& p, void* y, void* res, const void* x, const void* gamma,
                      int64_t M, int N, float eps, int64_t grid, hipStream_t s) {
   T* yy = static_cast<T*>(y);
@@ -481,11 +497,11 @@ hipError_t norm_regs(const rr_plan& p, void* y, void* res, const void* x, const 
   // The host never plans more than 16 values per lane for the norms
   // (NV * VEC <= 16), so only those instantiations exist.
   switch (p.vecs_per_lane) {
-    case 1: norm_regs_kernel<T, 1, FUSED><<<grid1(grid), b, 0, s>>>(yy, rr_, xx, gg, M, N, eps, p.waves_per_row); break;
-    case 2: norm_regs_kernel<T, 2, FUSED><<<grid1(grid), b, 0, s>>>(yy, rr_, xx, gg, M, N, eps, p.waves_per_row); break;
+    case 1: norm_regs_kernel<T, 1, FUSED, WAVE><<<grid1(grid), b, 0, s>>>(yy, rr_, xx, gg, M, N, eps); break;
+    case 2: norm_regs_kernel<T, 2, FUSED, WAVE><<<grid1(grid), b, 0, s>>>(yy, rr_, xx, gg, M, N, eps); break;
     case 4:
       if constexpr (Elem<T>::kVec * 4 <= 16) {
-        norm_regs_kernel<T, 4, FUSED><<<grid1(grid), b, 0, s>>>(yy, rr_, xx, gg, M, N, eps, p.waves_per_row);
+        norm_regs_kernel<T, 4, FUSED, WAVE><<<grid1(grid), b, 0, s>>>(yy, rr_, xx, gg, M, N, eps);
         break;
       }
       return hipErrorInvalidValue;
@@ -513,7 +529,28 @@ template <typename T, bool FUSED>
 hipError_t norm_any(const rr_plan& p, void* y, void* res, const void* x, const void* gamma,
                     int64_t M, int N, float eps, int64_t grid, hipStream_t s) {
   if (p.variant == RR_VARIANT_LOOP) return norm_loop<T, FUSED>(p, y, res, x, gamma, M, N, eps, grid, s);
-  return norm_regs<T, FUSED>(p, y, res, x, gamma, M, N, eps, grid, s);
+  if (p.variant == RR_VARIANT_WAVE) return norm_regs<T, FUSED, true>(p, y, res, x, gamma, M, N, eps, grid, s);
+  return norm_regs<T, FUSED, false>(p, y, res, x, gamma, M, N, eps, grid, s);
+}
+
+template <typename Tin, typename Tout, bool WAVE>
+hipError_t softmax_regs(const rr_plan& p, const Tin* xx, Tout* yy, int64_t M, int N, int64_t grid,
+                        hipStream_t s) {
+  const dim3 b(p.block_threads);
+  // At most 32 values per lane (NV * VEC <= 32).
+  switch (p.vecs_per_lane) {
+    case 1: softmax_regs_kernel<Tin, Tout, 1, WAVE><<<grid1(grid), b, 0, s>>>(xx, yy, M, N); break;
+    case 2: softmax_regs_kernel<Tin, Tout, 2, WAVE><<<grid1(grid), b, 0, s>>>(xx, yy, M, N); break;
+    case 4: softmax_regs_kernel<Tin, Tout, 4, WAVE><<<grid1(grid), b, 0, s>>>(xx, yy, M, N); break;
+    case 8:
+      if constexpr (Elem<Tin>::kVec * 8 <= 32) {
+        softmax_regs_kernel<Tin, Tout, 8, WAVE><<<grid1(grid), b, 0, s>>>(xx, yy, M, N);
+        break;
+      }
+      return hipErrorInvalidValue;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
 }
 
 template <typename Tin, typename Tout>
@@ -545,20 +582,8 @@ hipError_t softmax_typed(const rr_plan& p, void* y, const void* x, void* ws, int
     }
     return hipGetLastError();
   }
-  // At most 32 values per lane (NV * VEC <= 32).
-  switch (p.vecs_per_lane) {
-    case 1: softmax_regs_kernel<Tin, Tout, 1><<<grid1(grid), b, 0, s>>>(xx, yy, M, N, p.waves_per_row); break;
-    case 2: softmax_regs_kernel<Tin, Tout, 2><<<grid1(grid), b, 0, s>>>(xx, yy, M, N, p.waves_per_row); break;
-    case 4: softmax_regs_kernel<Tin, Tout, 4><<<grid1(grid), b, 0, s>>>(xx, yy, M, N, p.waves_per_row); break;
-    case 8:
-      if constexpr (Elem<Tin>::kVec * 8 <= 32) {
-        softmax_regs_kernel<Tin, Tout, 8><<<grid1(grid), b, 0, s>>>(xx, yy, M, N, p.waves_per_row);
-        break;
-      }
-      return hipErrorInvalidValue;
-    default: return hipErrorInvalidValue;
-  }
-  return hipGetLastError();
+  if (p.variant == RR_VARIANT_WAVE) return softmax_regs<Tin, Tout, true>(p, xx, yy, M, N, grid, s);
+  return softmax_regs<Tin, Tout, false>(p, xx, yy, M, N, grid, s);
 }
 
 }  // namespace

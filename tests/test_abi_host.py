@@ -109,12 +109,13 @@ def test_softmax_validation():
 
 WORKLOAD_PLANS = [
     # op, M, N, in, out -> variant, waves_per_row, vecs_per_lane, vec_elems, chunks
-    ((rr.RR_OP_RMSNORM, 64, 3584, rr.RR_F32, rr.RR_F32), ("block", 4, 4, 4, 1)),
-    ((rr.RR_OP_FUSED_ADD_RMSNORM, 8192, 4096, rr.RR_BF16, rr.RR_BF16), ("block", 4, 2, 8, 1)),
+    # (workgroup-per-row plans keep two 16-byte loads in flight per lane)
+    ((rr.RR_OP_RMSNORM, 64, 3584, rr.RR_F32, rr.RR_F32), ("block", 7, 2, 4, 1)),
+    ((rr.RR_OP_FUSED_ADD_RMSNORM, 8192, 4096, rr.RR_BF16, rr.RR_BF16), ("block", 8, 1, 8, 1)),
     ((rr.RR_OP_RMSNORM, 8192, 4096, rr.RR_BF16, rr.RR_BF16), ("block", 4, 2, 8, 1)),
     ((rr.RR_OP_SOFTMAX, 16384, 1024, rr.RR_F32, rr.RR_F32), ("wave", 1, 4, 4, 1)),
     ((rr.RR_OP_SOFTMAX, 256, 152064, rr.RR_BF16, rr.RR_F32), ("split", 4, 2, 8, 38)),
-    ((rr.RR_OP_SOFTMAX, 28 * 4096, 4096, rr.RR_F32, rr.RR_F32), ("block", 4, 4, 4, 1)),
+    ((rr.RR_OP_SOFTMAX, 28 * 4096, 4096, rr.RR_F32, rr.RR_F32), ("block", 8, 2, 4, 1)),
 ]
 
 
