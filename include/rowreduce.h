@@ -104,9 +104,9 @@ rr_status rr_fused_add_rmsnorm(void* y, void* residual, const void* x, const voi
  * rr_softmax_rows_workspace_bytes -- device workspace rr_softmax_rows needs
  * for this shape (0 when the chosen kernel needs none).  Very long rows with
  * few rows are split over several workgroups; each writes its chunk's
- * (m, d) pair (8 bytes) to the workspace and a second kernel merges them
- * ([P4] section "练习", the vocabulary-split exercise).  Host-only; returns 0
- * for invalid arguments.
+ * (m, d) pair to a 16-byte slot of the workspace and the row's slots are
+ * merged ([P4] section "练习", the vocabulary-split exercise).  Host-only;
+ * returns 0 for invalid arguments.
  */
 size_t rr_softmax_rows_workspace_bytes(int64_t M, int64_t N, rr_dtype in_dtype,
                                        rr_dtype out_dtype);
@@ -123,8 +123,10 @@ size_t rr_softmax_rows_workspace_bytes(int64_t M, int64_t N, rr_dtype in_dtype,
  *   x          [M, N] input, dtype in_dtype; entries may be -inf (masked);
  *              +inf and NaN inputs are not supported
  *   workspace  device buffer of at least rr_softmax_rows_workspace_bytes(M, N,
- *              in_dtype, out_dtype) bytes, 8-byte aligned (may be NULL when
- *              that size is 0); contents on entry are ignored
+ *              in_dtype, out_dtype) bytes, 16-byte aligned (may be NULL when
+ *              that size is 0); contents on entry are ignored (slots are
+ *              tagged per call); calls that overlap in time must not share
+ *              a workspace
  * Masked entries produce exactly 0; a row whose entries are all -inf
  * produces NaN everywhere (-inf - (-inf)).  In place (y == x) is allowed
  * when in_dtype == out_dtype; otherwise x and y must not overlap.
@@ -156,9 +158,15 @@ typedef enum rr_op {
  *   WAVE  one 64-lane wavefront per row, row held in VGPRs (N <= 2048)
  *   BLOCK one workgroup of up to 16 wavefronts per row, row held in VGPRs,
  *         wavefront totals combined through LDS (N <= 32768)
- *   SPLIT several workgroups per row, each writes its chunk's (m, d) to the
- *         workspace; a second kernel merges them and normalises (softmax, long
- *         rows with few rows)
+ *   SPLIT several workgroups per row (softmax, long rows with few rows):
+ *         a first kernel summarises each chunk as (m, d) into the workspace,
+ *         a second merges a row's chunks and normalises (re-reading x).
+ *         SPLIT_ONE_KERNEL (opt-in) does both in one cooperative kernel whose
+ *         workgroups keep their chunk in registers and wait for the row's
+ *         other chunks; it reads x once but measured slower on MI355X, where
+ *         the cross-workgroup hand-off costs L2 write-backs and invalidations.
+ *         It falls back to the two kernels when the device cannot hold a
+ *         row's chunks at once.  Both forms give the same bits.
  *   LOOP  one workgroup per row streaming the row twice (any N, unaligned
  *         rows, long rows with many rows) */
 typedef enum rr_variant {
@@ -166,7 +174,8 @@ typedef enum rr_variant {
   RR_VARIANT_WAVE = 1,
   RR_VARIANT_BLOCK = 2,
   RR_VARIANT_SPLIT = 3,
-  RR_VARIANT_LOOP = 4
+  RR_VARIANT_LOOP = 4,
+  RR_VARIANT_SPLIT_ONE_KERNEL = 5  /* SPLIT as one cooperative kernel (opt-in) */
 } rr_variant;
 
 typedef struct rr_plan {
@@ -178,7 +187,7 @@ typedef struct rr_plan {
   int32_t block_threads;    /* workgroup size */
   int64_t chunks_per_row;   /* SPLIT: workgroups per row; otherwise 1 */
   int64_t work_items;       /* workgroup-steps needed (rows / rows_per_group x chunks) */
-  size_t workspace_bytes;   /* SPLIT: M * chunks_per_row * 8; otherwise 0 */
+  size_t workspace_bytes;   /* SPLIT: M * chunks_per_row * 16; otherwise 0 */
 } rr_plan;
 
 /*

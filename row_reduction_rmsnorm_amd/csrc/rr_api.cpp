@@ -62,6 +62,8 @@ constexpr int64_t kSplitMaxRows = 1024;      // SPLIT only below this many rows
 // kernels (summed over the input tensors); more wavefronts per row rather
 // than more registers per lane measured faster on MI355X.
 constexpr int kLoadsPerLane = 2;
+// Split row: vectors per lane in each 256-lane chunk (chunk = 256 * 8 * VEC).
+constexpr int kSplitVecsPerLane = 4;
 
 // Register budget per lane, in fp32 values held for the row: softmax keeps
 // one array (x, then e_i); the norms keep x (and the residual) plus gamma,
@@ -102,12 +104,35 @@ bool plan_block(rr_op op, rr_plan* p, int vec, int64_t nvec) {
   return false;
 }
 
+// Softmax rows beyond that, up to 20 vectors per lane of a 1024-lane
+// workgroup, held in their storage format (one workgroup per CU).  With few
+// rows the two-kernel split measured faster (a vocabulary softmax of 256 x
+// 152064 bf16: 61 us split, 98 us packed), so this only replaces the
+// streaming path, for kPackedMinRows rows or more.
+constexpr int kPackedNV[] = {12, 16, 19, 20};
+constexpr int64_t kPackedMinRows = 1024;
+bool plan_packed(rr_op op, rr_plan* p, int vec, int64_t nvec) {
+  if (op != RR_OP_SOFTMAX) return false;
+  for (int nv : kPackedNV) {
+    if (nvec <= (int64_t)kMaxWaves * 64 * nv) {
+      p->variant = RR_VARIANT_BLOCK;
+      p->vec_elems = vec;
+      p->waves_per_row = kMaxWaves;
+      p->rows_per_group = 1;
+      p->vecs_per_lane = nv;
+      p->block_threads = 64 * kMaxWaves;
+      return true;
+    }
+  }
+  return false;
+}
+
 void plan_split(rr_plan* p, int vec, int64_t nvec) {
   p->variant = RR_VARIANT_SPLIT;
   p->vec_elems = vec;
   p->waves_per_row = 4;
   p->rows_per_group = 1;
-  p->vecs_per_lane = 16 / vec;
+  p->vecs_per_lane = kSplitVecsPerLane;
   p->block_threads = 256;
   p->chunks_per_row = ceil_div(nvec, 256 * (int64_t)p->vecs_per_lane);
 }
@@ -148,6 +173,7 @@ rr_status make_plan(rr_op op, int64_t M, int64_t N, int din, int dout, bool is_a
       } else if (wave_fits(op, vec, nvec)) {
         plan_wave(p, vec, nvec);
       } else if (plan_block(op, p, vec, nvec)) {
+      } else if (M >= kPackedMinRows && plan_packed(op, p, vec, nvec)) {
       } else if (op == RR_OP_SOFTMAX && M < kSplitMaxRows) {
         plan_split(p, vec, nvec);
       } else {
@@ -160,11 +186,15 @@ rr_status make_plan(rr_op op, int64_t M, int64_t N, int din, int dout, bool is_a
       if (ok) plan_wave(p, vec, nvec);
       break;
     case RR_VARIANT_BLOCK:
-      ok = vec > 1 && plan_block(op, p, vec, nvec);
+      ok = vec > 1 && (plan_block(op, p, vec, nvec) || plan_packed(op, p, vec, nvec));
       break;
     case RR_VARIANT_SPLIT:
+    case RR_VARIANT_SPLIT_ONE_KERNEL:
       ok = vec > 1 && op == RR_OP_SOFTMAX;
-      if (ok) plan_split(p, vec, nvec);
+      if (ok) {
+        plan_split(p, vec, nvec);
+        p->variant = forced;
+      }
       break;
     case RR_VARIANT_LOOP:
       plan_loop(p, vec, nvec);
@@ -178,10 +208,10 @@ rr_status make_plan(rr_op op, int64_t M, int64_t N, int din, int dout, bool is_a
                 forced, (int)op, (long long)N, vec);
   }
   if (p->chunks_per_row == 0) p->chunks_per_row = 1;
-  if (p->variant == RR_VARIANT_SPLIT) {
+  if (p->variant == RR_VARIANT_SPLIT || p->variant == RR_VARIANT_SPLIT_ONE_KERNEL) {
     if (p->chunks_per_row > (int64_t)1 << 30) return fail(RR_ERR_UNSUPPORTED, "too many chunks");
     p->work_items = M * p->chunks_per_row;
-    p->workspace_bytes = (size_t)M * (size_t)p->chunks_per_row * 8u;
+    p->workspace_bytes = (size_t)M * (size_t)p->chunks_per_row * 16u;
   } else {
     p->work_items = ceil_div(M, p->rows_per_group);
   }
@@ -312,8 +342,8 @@ rr_status rr_softmax_rows(void* y, const void* x, int64_t M, int64_t N, rr_dtype
     if (!workspace || workspace_bytes < p.workspace_bytes)
       return fail(RR_ERR_WORKSPACE, "rr_softmax_rows: needs a workspace of %zu bytes, got %zu",
                   p.workspace_bytes, workspace ? workspace_bytes : (size_t)0);
-    if ((reinterpret_cast<uintptr_t>(workspace) & 7u) != 0)
-      return fail(RR_ERR_INVALID_ARG, "rr_softmax_rows: workspace must be 8-byte aligned");
+    if ((reinterpret_cast<uintptr_t>(workspace) & 15u) != 0)
+      return fail(RR_ERR_INVALID_ARG, "rr_softmax_rows: workspace must be 16-byte aligned");
     if (overlaps(workspace, p.workspace_bytes, x, xb) || overlaps(workspace, p.workspace_bytes, y, yb))
       return fail(RR_ERR_INVALID_ARG, "rr_softmax_rows: workspace overlaps x or y");
   }
@@ -344,7 +374,7 @@ rr_status rr_query_plan(rr_op op, int64_t M, int64_t N, rr_dtype in_dtype, rr_dt
 
 rr_status rr_set_variant_override(rr_variant v) {
   g_err[0] = '\0';
-  if (v < RR_VARIANT_AUTO || v > RR_VARIANT_LOOP)
+  if (v < RR_VARIANT_AUTO || v > RR_VARIANT_SPLIT_ONE_KERNEL)
     return fail(RR_ERR_INVALID_ARG, "rr_set_variant_override: unknown variant %d", (int)v);
   g_override.store(v, std::memory_order_relaxed);
   return RR_OK;

@@ -122,24 +122,39 @@ __device__ __forceinline__ void load_vec(const T* __restrict__ p, float (&v)[VEC
 
 // A vector of VEC elements kept in registers in its storage format (bf16
 // stays packed two per dword: half the registers of widened fp32).  Used for
-// gamma, which a workgroup keeps across all the rows it visits.
+// gamma, which a workgroup keeps across all the rows it visits, and for the
+// split-row chunks, which are widened element by element when used.
 template <typename T, int VEC>
 struct Packed {
   static constexpr int kWords = VEC * (int)sizeof(T) / 4;
   uint32_t w[kWords];
+  template <bool NT = false>
   __device__ __forceinline__ void load(const T* __restrict__ p) {
     if constexpr (kWords == 4) {
-      uint4 q = *reinterpret_cast<const uint4*>(p);
+      const u32x4_t q = ld<NT>(reinterpret_cast<const u32x4_t*>(p));
       w[0] = q.x; w[1] = q.y; w[2] = q.z; w[3] = q.w;
     } else if constexpr (std::is_same_v<T, float>) {
-      w[0] = __float_as_uint(p[0]);
+      w[0] = __float_as_uint(ld<NT>(p));
     } else {
-      w[0] = static_cast<uint32_t>(p[0]);
+      w[0] = static_cast<uint32_t>(ld<NT>(p));
     }
+  }
+  __device__ __forceinline__ void fill(float v) {
+    const uint32_t b = std::is_same_v<T, float> ? __float_as_uint(v)
+                                                : ((__float_as_uint(v) >> 16) * 0x10001u);
+#pragma unroll
+    for (int i = 0; i < kWords; ++i) w[i] = b;
   }
   __device__ __forceinline__ void zero() {
 #pragma unroll
     for (int i = 0; i < kWords; ++i) w[i] = 0u;
+  }
+  // Tell the compiler the words may have changed (an empty asm that "reads
+  // and writes" them), so values widened earlier are not kept live across
+  // this point: the next get() widens again from the packed words.
+  __device__ __forceinline__ void touch() {
+#pragma unroll
+    for (int i = 0; i < kWords; ++i) asm volatile("" : "+v"(w[i]));
   }
   __device__ __forceinline__ float get(int i) const {
     if constexpr (std::is_same_v<T, float>) return __uint_as_float(w[i]);

@@ -24,6 +24,13 @@
 //  * the grid may be smaller than the number of rows: workgroups then walk
 //    rows with a stride of gridDim.x (a persistent grid); gamma stays in
 //    registers across rows.
+#include <time.h>
+
+#include <atomic>
+#include <map>
+#include <mutex>
+#include <utility>
+
 #include "rr_device.h"
 #include "rr_launch.h"
 
@@ -31,32 +38,45 @@ namespace rr {
 
 namespace {
 
-// LDS stage for one float per wavefront ([P2] section 四 and [P5] section
+// LDS stage for one value per wavefront ([P2] section 四 and [P5] section
 // "原 RMSNorm 草稿的两个关键错误": one slot per wavefront, a barrier, then a
-// single combine).  Every lane reads all `nw` slots and adds them in index
-// order, so every lane of the workgroup ends with the same bits and no
-// broadcast step is needed.  `parity` selects one of two slot sets: a loop
-// that reduces once per row alternates them, which makes the single barrier
-// per row enough (a wavefront can only write a slot set again after the next
-// barrier, which every wavefront reaches after finishing its reads of that
-// set) -- the reuse hazard [P2] section 十 and [P4] section "实现" close with
-// a trailing barrier.
+// single combine).  Lane l of every wavefront reads slot (l mod 16) (the
+// identity beyond the nw slots) and a four-step DPP butterfly inside each
+// 16-lane row combines the 16 values, so every lane of the workgroup ends
+// with the same bits and no broadcast step is needed.  `parity` selects one
+// of two slot sets: a loop that reduces once per row alternates them, which
+// makes the single barrier per row enough (a wavefront can only write a slot
+// set again after the next barrier, which every wavefront reaches after
+// finishing its reads of that set) -- the reuse hazard [P2] section 十 and
+// [P4] section "实现" close with a trailing barrier.
 __device__ __forceinline__ float group_sum(float v, int nw, int w, int lane,
                                            float (*slots)[kMaxWavesPerGroup], int parity) {
   if (lane == 0) slots[parity][w] = v;
   __syncthreads();
-  float t = slots[parity][0];
-  for (int j = 1; j < nw; ++j) t += slots[parity][j];
-  return t;
+  const int j = lane & (kMaxWavesPerGroup - 1);
+  float t = (j < nw) ? slots[parity][j] : 0.0f;
+  t = t + dpp_f32<kDppQuadXor1>(t);
+  t = t + dpp_f32<kDppQuadXor2>(t);
+  t = t + dpp_f32<kDppRowHalfMirror>(t);
+  return t + dpp_f32<kDppRowMirror>(t);
 }
 
 __device__ __forceinline__ MD group_md(MD v, int nw, int w, int lane,
                                        MD (*slots)[kMaxWavesPerGroup], int parity) {
   if (lane == 0) slots[parity][w] = v;
   __syncthreads();
-  MD t = slots[parity][0];
-  for (int j = 1; j < nw; ++j) t = md_merge(t, slots[parity][j]);
-  return t;
+  const int j = lane & (kMaxWavesPerGroup - 1);
+  MD t;
+  if (j < nw) {
+    t = slots[parity][j];
+  } else {
+    t.m = kNegInf;
+    t.d = 0.0f;
+  }
+  t = md_merge(t, dpp_md<kDppQuadXor1>(t));
+  t = md_merge(t, dpp_md<kDppQuadXor2>(t));
+  t = md_merge(t, dpp_md<kDppRowHalfMirror>(t));
+  return md_merge(t, dpp_md<kDppRowMirror>(t));
 }
 
 // Thread coordinates.  WAVE: each wavefront owns a row, the workgroup holds
@@ -309,6 +329,77 @@ __global__ __launch_bounds__(1024) void softmax_regs_kernel(const Tin* x, Tout* 
 }
 
 // ===========================================================================
+// Softmax, a long row held packed in registers (BLOCK, large NV).
+//
+// For rows too long for 32 widened values per lane, a workgroup of up to 16
+// wavefronts keeps the row in its storage format (bf16 stays two per dword)
+// and recomputes exp(x - m) when it writes, instead of keeping e_i: two
+// exponentials per element, still one HBM read and one write.  A 152064-wide
+// bf16 row needs 19 vectors (76 VGPRs) per lane of a 1024-lane workgroup, one
+// workgroup per CU.
+// ===========================================================================
+template <typename Tin, typename Tout, int NV>
+__global__ __launch_bounds__(1024) void softmax_packed_kernel(const Tin* x, Tout* y, int64_t M,
+                                                              int N) {
+  constexpr int VEC = Elem<Tin>::kVec;
+  constexpr int kThreads = 1024;
+  __shared__ MD slots[2][kMaxWavesPerGroup];
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int w = t >> 6;
+  const int nvec = N / VEC;
+  int parity = 0;
+  for (int64_t row = blockIdx.x; row < M; row += gridDim.x) {
+    const Tin* xr = x + row * (int64_t)N;   // uniform row bases
+    Tout* yr = y + row * (int64_t)N;
+    // the lane's vector offsets are recomputed at each use rather than kept
+    // live across the row (an opaque copy of the lane index), which frees
+    // the registers the packed row needs
+    int t_ld = t;
+    asm volatile("" : "+v"(t_ld));
+    Packed<Tin, VEC> v[NV];
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {
+      const int vi = k * kThreads + t_ld;
+      if (vi < nvec) v[k].template load<true>(xr + vi * VEC);
+      else v[k].fill(kNegInf);
+    }
+    float ml = kNegInf;
+#pragma unroll
+    for (int k = 0; k < NV; ++k)
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) ml = __builtin_fmaxf(ml, v[k].get(i));
+#pragma unroll
+    for (int k = 0; k < NV; ++k) v[k].touch();
+    const float shift = (ml == kNegInf) ? 0.0f : ml;
+    float dl = 0.0f;
+#pragma unroll
+    for (int k = 0; k < NV; ++k)
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) dl += exp_shifted(v[k].get(i) - shift);
+    MD p;
+    p.m = ml;
+    p.d = dl;
+#pragma unroll
+    for (int k = 0; k < NV; ++k) v[k].touch();
+    p = wave_md(p);
+    p = group_md(p, kThreads / kWave, w, lane, slots, parity);
+    parity ^= 1;
+    const float inv_d = (p.m == kNegInf) ? __builtin_nanf("") : 1.0f / p.d;
+    int t_st = t;
+    asm volatile("" : "+v"(t_st));
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {
+      const int vi = k * kThreads + t_st;
+      float o[VEC];
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) o[i] = exp_shifted(v[k].get(i) - p.m) * inv_d;
+      if (vi < nvec) store_vec<Tout, VEC>(yr + vi * VEC, o);
+    }
+  }
+}
+
+// ===========================================================================
 // Softmax, streaming (LOOP): any N, any alignment.  Pass 1 runs the online
 // recurrence per lane, one vector (chunk) at a time: the chunk's own summary
 // merged into the lane's running pair ([P1] section "四、S4"; [P2] section
@@ -362,8 +453,17 @@ __global__ __launch_bounds__(1024) void softmax_loop_kernel(const Tin* x, Tout* 
 // chunk.  The chunk's vectors are loaded before the pairs are merged so the
 // HBM reads are in flight during the merge.
 // ===========================================================================
+// One (m, d) slot per chunk, 16 bytes: the two-kernel form uses m and d; the
+// one-kernel form also uses the tag.
+struct SplitSlot {
+  float m;
+  float d;
+  uint64_t tag;
+};
+static_assert(sizeof(SplitSlot) == 16, "slot layout");
+
 template <typename Tin, int NV>
-__global__ __launch_bounds__(256) void softmax_split_stats_kernel(const Tin* x, float2* ws,
+__global__ __launch_bounds__(256) void softmax_split_stats_kernel(const Tin* x, SplitSlot* ws,
                                                                   int64_t M, int N, int S) {
   constexpr int VEC = Elem<Tin>::kVec;
   constexpr int kThreads = 256;
@@ -377,42 +477,41 @@ __global__ __launch_bounds__(256) void softmax_split_stats_kernel(const Tin* x, 
     const int64_t row = item / S;
     const int c = (int)(item - row * S);
     const int64_t off = row * (int64_t)N;
-    float v[NV][VEC];
+    Packed<Tin, VEC> v[NV];
 #pragma unroll
     for (int k = 0; k < NV; ++k) {
       const int vi = c * CV + k * kThreads + rl.t;
-      if (vi < nvec) {
-        // temporal load: pass B reads this chunk again right after
-        load_vec<Tin, VEC, false>(x + off + (int64_t)vi * VEC, v[k]);
-      } else {
-#pragma unroll
-        for (int i = 0; i < VEC; ++i) v[k][i] = kNegInf;
-      }
+      // temporal load: pass B reads this chunk again right after
+      if (vi < nvec) v[k].template load<false>(x + off + (int64_t)vi * VEC);
+      else v[k].fill(kNegInf);
     }
     float ml = kNegInf;
 #pragma unroll
     for (int k = 0; k < NV; ++k)
 #pragma unroll
-      for (int i = 0; i < VEC; ++i) ml = __builtin_fmaxf(ml, v[k][i]);
+      for (int i = 0; i < VEC; ++i) ml = __builtin_fmaxf(ml, v[k].get(i));
     const float shift = (ml == kNegInf) ? 0.0f : ml;
     float dl = 0.0f;
 #pragma unroll
     for (int k = 0; k < NV; ++k)
 #pragma unroll
-      for (int i = 0; i < VEC; ++i) dl += exp_shifted(v[k][i] - shift);
+      for (int i = 0; i < VEC; ++i) dl += exp_shifted(v[k].get(i) - shift);
     MD p;
     p.m = ml;
     p.d = dl;
     p = wave_md(p);
     p = group_md(p, rl.nw, rl.w, rl.lane, slots, parity);
     parity ^= 1;
-    if (threadIdx.x == 0) ws[item] = make_float2(p.m, p.d);
+    if (threadIdx.x == 0) {
+      ws[item].m = p.m;
+      ws[item].d = p.d;
+    }
   }
 }
 
 template <typename Tin, typename Tout, int NV>
 __global__ __launch_bounds__(256) void softmax_split_apply_kernel(const Tin* x, Tout* y,
-                                                                  const float2* __restrict__ ws,
+                                                                  const SplitSlot* __restrict__ ws,
                                                                   int64_t M, int N, int S) {
   constexpr int VEC = Elem<Tin>::kVec;
   constexpr int kThreads = 256;
@@ -424,25 +523,20 @@ __global__ __launch_bounds__(256) void softmax_split_apply_kernel(const Tin* x, 
     const int64_t row = item / S;
     const int c = (int)(item - row * S);
     const int64_t off = row * (int64_t)N;
-    float v[NV][VEC];
+    Packed<Tin, VEC> v[NV];
 #pragma unroll
     for (int k = 0; k < NV; ++k) {
       const int vi = c * CV + k * kThreads + rl.t;
-      if (vi < nvec) {
-        load_vec<Tin, VEC>(x + off + (int64_t)vi * VEC, v[k]);
-      } else {
-#pragma unroll
-        for (int i = 0; i < VEC; ++i) v[k][i] = kNegInf;
-      }
+      if (vi < nvec) v[k].template load<true>(x + off + (int64_t)vi * VEC);
+      else v[k].fill(kNegInf);
     }
     MD p;
     p.m = kNegInf;
     p.d = 0.0f;
     for (int s = rl.lane; s < S; s += kWave) {
-      const float2 q = ws[row * S + s];
       MD b;
-      b.m = q.x;
-      b.d = q.y;
+      b.m = ws[row * S + s].m;
+      b.d = ws[row * S + s].d;
       p = md_merge(p, b);
     }
     p = wave_md(p);
@@ -452,8 +546,111 @@ __global__ __launch_bounds__(256) void softmax_split_apply_kernel(const Tin* x, 
       const int vi = c * CV + k * kThreads + rl.t;
       float o[VEC];
 #pragma unroll
-      for (int i = 0; i < VEC; ++i) o[i] = exp_shifted(v[k][i] - p.m) * inv_d;
+      for (int i = 0; i < VEC; ++i) o[i] = exp_shifted(v[k].get(i) - p.m) * inv_d;
       // plain (write-back) stores: measured faster than non-temporal ones here
+      if (vi < nvec) store_vec<Tout, VEC, false>(y + off + (int64_t)vi * VEC, o);
+    }
+  }
+}
+
+// ===========================================================================
+// Softmax, split row in ONE kernel (SPLIT, cooperative form).
+//
+// The same chunking and the same arithmetic as the two kernels above, but a
+// workgroup keeps its chunk in registers while the row's other chunks are
+// summarised, so x is read from HBM once ([P4] section "练习": "the last block
+// to finish" instead of a second kernel; the pages' PyTorch reading in [P2]
+// section 九 describes the same last-arrival idea for reductions).
+//
+//  * Launch: cooperative (every workgroup resident), grid G <= items; a
+//    workgroup handles items g, g + G, g + 2G, ... in increasing order.
+//  * Publish: thread 0 stores the chunk's (m, d) into its slot and then the
+//    slot's 64-bit tag with release semantics at agent scope.  The tag is a
+//    value unique to this call (the host increments it per call), so slots
+//    left by earlier calls or uninitialised memory never look published.
+//  * Wait: lane j of every wavefront polls the tags of slots j, j + 64, ...
+//    with relaxed agent-scope loads until each equals the call's tag, then the
+//    wavefront issues one acquire fence and reads the (m, d) values.
+//  * No deadlock: with all G workgroups resident and S <= G, a workgroup only
+//    waits for items of its own row; a cycle of waits would need every
+//    workgroup's current item to be smaller than the next one's, around the
+//    cycle, which cannot be.  Every wait is also bounded (kSpinLimit polls), so
+//    every wavefront reaches the end even if that argument were broken.
+// ===========================================================================
+constexpr int kSpinLimit = 1 << 22;
+
+template <typename Tin, typename Tout, int NV>
+__global__ __launch_bounds__(256) void softmax_split_fused_kernel(const Tin* x, Tout* y,
+                                                                  SplitSlot* slots_ws, int64_t M,
+                                                                  int N, int S, uint64_t tag) {
+  constexpr int VEC = Elem<Tin>::kVec;
+  constexpr int kThreads = 256;
+  constexpr int CV = kThreads * NV;
+  __shared__ MD slots[2][kMaxWavesPerGroup];
+  const RowLane rl = row_lane<false>();
+  const int nvec = N / VEC;
+  const int64_t items = M * (int64_t)S;
+  int parity = 0;
+  for (int64_t item = blockIdx.x; item < items; item += gridDim.x) {
+    const int64_t row = item / S;
+    const int c = (int)(item - row * S);
+    const int64_t off = row * (int64_t)N;
+    Packed<Tin, VEC> v[NV];
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {
+      const int vi = c * CV + k * kThreads + rl.t;
+      if (vi < nvec) v[k].template load<true>(x + off + (int64_t)vi * VEC);
+      else v[k].fill(kNegInf);
+    }
+    // chunk summary, exactly as the two-kernel form computes it
+    float ml = kNegInf;
+#pragma unroll
+    for (int k = 0; k < NV; ++k)
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) ml = __builtin_fmaxf(ml, v[k].get(i));
+    const float shift = (ml == kNegInf) ? 0.0f : ml;
+    float dl = 0.0f;
+#pragma unroll
+    for (int k = 0; k < NV; ++k)
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) dl += exp_shifted(v[k].get(i) - shift);
+    MD p;
+    p.m = ml;
+    p.d = dl;
+    p = wave_md(p);
+    p = group_md(p, rl.nw, rl.w, rl.lane, slots, parity);
+    parity ^= 1;
+    SplitSlot* row_slots = slots_ws + row * S;
+    if (threadIdx.x == 0) {
+      row_slots[c].m = p.m;
+      row_slots[c].d = p.d;
+      __hip_atomic_store(&row_slots[c].tag, tag, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    // wait for the row's chunks, then merge them in the same order as pass B
+    for (int s = rl.lane; s < S; s += kWave) {
+      for (int spin = 0; spin < kSpinLimit; ++spin) {
+        if (__hip_atomic_load(&row_slots[s].tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == tag) break;
+        __builtin_amdgcn_s_sleep(1);
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    MD q;
+    q.m = kNegInf;
+    q.d = 0.0f;
+    for (int s = rl.lane; s < S; s += kWave) {
+      MD b;
+      b.m = row_slots[s].m;
+      b.d = row_slots[s].d;
+      q = md_merge(q, b);
+    }
+    q = wave_md(q);
+    const float inv_d = (q.m == kNegInf) ? __builtin_nanf("") : 1.0f / q.d;
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {
+      const int vi = c * CV + k * kThreads + rl.t;
+      float o[VEC];
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) o[i] = exp_shifted(v[k].get(i) - q.m) * inv_d;
       if (vi < nvec) store_vec<Tout, VEC, false>(y + off + (int64_t)vi * VEC, o);
     }
   }
@@ -553,6 +750,58 @@ hipError_t softmax_regs(const rr_plan& p, const Tin* xx, Tout* yy, int64_t M, in
   return hipGetLastError();
 }
 
+// Workgroups of `kernel` (256 threads) the current device holds at once, or 0
+// when it cannot launch cooperatively.  Cached per device and kernel.
+int cooperative_capacity(const void* kernel) {
+  static std::mutex mu;
+  static std::map<std::pair<int, const void*>, int> cache;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  std::lock_guard<std::mutex> lock(mu);
+  auto key = std::make_pair(dev, kernel);
+  auto it = cache.find(key);
+  if (it != cache.end()) return it->second;
+  int coop = 0, cus = 0, per_cu = 0;
+  int cap = 0;
+  if (hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev) == hipSuccess && coop &&
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 256, 0) == hipSuccess)
+    cap = cus * per_cu;
+  cache[key] = cap;
+  return cap;
+}
+
+// A value no earlier call used, for the one-kernel split's slot tags.
+uint64_t next_split_tag() {
+  static std::atomic<uint64_t> counter{0x9e3779b97f4a7c15ull ^ (uint64_t)time(nullptr)};
+  uint64_t t = counter.fetch_add(1, std::memory_order_relaxed) + 1;
+  return t ? t : counter.fetch_add(1, std::memory_order_relaxed) + 1;
+}
+
+// SPLIT: the two-kernel form.  SPLIT_ONE_KERNEL: one cooperative kernel
+// when the device can hold at least a row's chunks at once, else the two
+// kernels.  Both use the same chunks and the same merge order, so they give
+// the same bits.
+template <typename Tin, typename Tout, int NV>
+hipError_t softmax_split(const rr_plan& p, const Tin* xx, Tout* yy, SplitSlot* w, int64_t M, int N,
+                         int S, int64_t grid, hipStream_t s) {
+  const dim3 b(p.block_threads);
+  if (p.variant == RR_VARIANT_SPLIT_ONE_KERNEL) {
+    const void* k = reinterpret_cast<const void*>(&softmax_split_fused_kernel<Tin, Tout, NV>);
+    const int cap = cooperative_capacity(k);
+    if (cap >= S) {
+      const int64_t g = grid < cap ? grid : cap;
+      uint64_t tag = next_split_tag();
+      int64_t m64 = M;
+      void* args[] = {(void*)&xx, (void*)&yy, (void*)&w, (void*)&m64, (void*)&N, (void*)&S, (void*)&tag};
+      return hipLaunchCooperativeKernel(k, grid1(g), b, args, 0, s);
+    }
+  }
+  softmax_split_stats_kernel<Tin, NV><<<grid1(grid), b, 0, s>>>(xx, w, M, N, S);
+  softmax_split_apply_kernel<Tin, Tout, NV><<<grid1(grid), b, 0, s>>>(xx, yy, w, M, N, S);
+  return hipGetLastError();
+}
+
 template <typename Tin, typename Tout>
 hipError_t softmax_typed(const rr_plan& p, void* y, const void* x, void* ws, int64_t M, int N,
                          int64_t grid, hipStream_t s) {
@@ -566,23 +815,29 @@ hipError_t softmax_typed(const rr_plan& p, void* y, const void* x, void* ws, int
       softmax_loop_kernel<Tin, Tout, Elem<Tin>::kVec><<<grid1(grid), b, 0, s>>>(xx, yy, M, N);
     return hipGetLastError();
   }
-  if (p.variant == RR_VARIANT_SPLIT) {
-    float2* w = static_cast<float2*>(ws);
+  if (p.variant == RR_VARIANT_SPLIT || p.variant == RR_VARIANT_SPLIT_ONE_KERNEL) {
+    SplitSlot* w = static_cast<SplitSlot*>(ws);
     const int S = (int)p.chunks_per_row;
     switch (p.vecs_per_lane) {
-      case 2:
-        softmax_split_stats_kernel<Tin, 2><<<grid1(grid), b, 0, s>>>(xx, w, M, N, S);
-        softmax_split_apply_kernel<Tin, Tout, 2><<<grid1(grid), b, 0, s>>>(xx, yy, w, M, N, S);
-        break;
-      case 4:
-        softmax_split_stats_kernel<Tin, 4><<<grid1(grid), b, 0, s>>>(xx, w, M, N, S);
-        softmax_split_apply_kernel<Tin, Tout, 4><<<grid1(grid), b, 0, s>>>(xx, yy, w, M, N, S);
-        break;
+      case 2: return softmax_split<Tin, Tout, 2>(p, xx, yy, w, M, N, S, grid, s);
+      case 4: return softmax_split<Tin, Tout, 4>(p, xx, yy, w, M, N, S, grid, s);
+      case 8: return softmax_split<Tin, Tout, 8>(p, xx, yy, w, M, N, S, grid, s);
+      default: return hipErrorInvalidValue;
+    }
+  }
+  if (p.variant == RR_VARIANT_WAVE) return softmax_regs<Tin, Tout, true>(p, xx, yy, M, N, grid, s);
+  if (p.vecs_per_lane * Elem<Tin>::kVec > 32) {
+    // long rows held in their storage format (see softmax_packed_kernel)
+    const dim3 b(p.block_threads);
+    switch (p.vecs_per_lane) {
+      case 12: softmax_packed_kernel<Tin, Tout, 12><<<grid1(grid), b, 0, s>>>(xx, yy, M, N); break;
+      case 16: softmax_packed_kernel<Tin, Tout, 16><<<grid1(grid), b, 0, s>>>(xx, yy, M, N); break;
+      case 19: softmax_packed_kernel<Tin, Tout, 19><<<grid1(grid), b, 0, s>>>(xx, yy, M, N); break;
+      case 20: softmax_packed_kernel<Tin, Tout, 20><<<grid1(grid), b, 0, s>>>(xx, yy, M, N); break;
       default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
   }
-  if (p.variant == RR_VARIANT_WAVE) return softmax_regs<Tin, Tout, true>(p, xx, yy, M, N, grid, s);
   return softmax_regs<Tin, Tout, false>(p, xx, yy, M, N, grid, s);
 }
 

@@ -9,7 +9,8 @@
 
 namespace rr {
 
-// Largest number of wavefronts one workgroup may hold (1024 threads).
+// Largest number of wavefronts one workgroup may hold (1024 threads); also
+// the width of the DPP row that combines the per-wavefront LDS slots.
 constexpr int kMaxWavesPerGroup = 16;
 
 // Enqueue the RMSNorm (fused == false) or fused add + RMSNorm kernel that

@@ -96,10 +96,10 @@ def test_softmax_validation():
     assert f(X, X, 4, 8, rr.RR_BF16, rr.RR_F32, None, 0, None) == rr.RR_ERR_INVALID_ARG
     # long rows with few rows need the split workspace
     need = rr.rr_softmax_rows_workspace_bytes(256, 152064, rr.RR_BF16, rr.RR_F32)
-    assert need == 256 * 38 * 8
+    assert need == 256 * 19 * 16
     assert f(Y, X, 256, 152064, rr.RR_BF16, rr.RR_F32, None, 0, None) == rr.RR_ERR_WORKSPACE
     assert f(Y, X, 256, 152064, rr.RR_BF16, rr.RR_F32, W, need - 8, None) == rr.RR_ERR_WORKSPACE
-    assert f(Y, X, 256, 152064, rr.RR_BF16, rr.RR_F32, W + 4, need, None) == rr.RR_ERR_INVALID_ARG
+    assert f(Y, X, 256, 152064, rr.RR_BF16, rr.RR_F32, W + 8, need, None) == rr.RR_ERR_INVALID_ARG
     assert "workspace" in rr.last_error_message()
 
 
@@ -114,7 +114,7 @@ WORKLOAD_PLANS = [
     ((rr.RR_OP_FUSED_ADD_RMSNORM, 8192, 4096, rr.RR_BF16, rr.RR_BF16), ("block", 8, 1, 8, 1)),
     ((rr.RR_OP_RMSNORM, 8192, 4096, rr.RR_BF16, rr.RR_BF16), ("block", 4, 2, 8, 1)),
     ((rr.RR_OP_SOFTMAX, 16384, 1024, rr.RR_F32, rr.RR_F32), ("wave", 1, 4, 4, 1)),
-    ((rr.RR_OP_SOFTMAX, 256, 152064, rr.RR_BF16, rr.RR_F32), ("split", 4, 2, 8, 38)),
+    ((rr.RR_OP_SOFTMAX, 256, 152064, rr.RR_BF16, rr.RR_F32), ("split", 4, 4, 8, 19)),
     ((rr.RR_OP_SOFTMAX, 28 * 4096, 4096, rr.RR_F32, rr.RR_F32), ("block", 8, 2, 4, 1)),
 ]
 
@@ -141,9 +141,15 @@ def test_dispatch_boundaries():
     assert v(rr.RR_OP_RMSNORM, 100, 16384) == "block"
     assert v(rr.RR_OP_RMSNORM, 100, 16388) == "loop"
     assert v(S, 100, 32768) == "block"
-    # longer softmax rows: split when rows are few, stream when many
+    # longer softmax rows: split when rows are few; with many rows the row is
+    # held packed (1024 lanes x up to 20 vectors), beyond that it streams
     assert v(S, 1023, 32772) == "split"
-    assert v(S, 1024, 32772) == "loop"
+    assert v(S, 1024, 32772) == "block"
+    assert rr.rr_query_plan(S, 1024, 32772, F, F)["vecs_per_lane"] == 12
+    assert v(S, 1024, 81920) == "block"
+    assert v(S, 1024, 81924) == "loop"
+    assert v(S, 1024, 163840, B, F) == "block"
+    assert v(S, 1024, 163848, B, F) == "loop"
     # unaligned widths or pointers take the scalar streaming path
     assert v(S, 10, 1023) == "loop"
     assert v(S, 10, 1024, al=False) == "loop"
@@ -158,8 +164,11 @@ def test_forced_variants():
         assert rr.rr_query_plan(S, 10, 1024, F, F)["variant_name"] == "loop"
         rr.rr_set_variant_override(rr.RR_VARIANT_SPLIT)
         p = rr.rr_query_plan(S, 10, 1024, F, F)
-        assert p["variant_name"] == "split" and p["workspace_bytes"] == 10 * 1 * 8
-        assert rr.rr_softmax_rows_workspace_bytes(10, 1024, F, F) == 80
+        assert p["variant_name"] == "split" and p["workspace_bytes"] == 10 * 1 * 16
+        assert rr.rr_softmax_rows_workspace_bytes(10, 1024, F, F) == 160
+        rr.rr_set_variant_override(rr.RR_VARIANT_SPLIT_ONE_KERNEL)
+        p = rr.rr_query_plan(S, 10, 5000, F, F)
+        assert p["variant_name"] == "split1" and p["chunks_per_row"] == 2
         with pytest.raises(rr.RowReduceError):
             rr.rr_query_plan(rr.RR_OP_RMSNORM, 10, 1024, F, F)   # no split RMSNorm
         rr.rr_set_variant_override(rr.RR_VARIANT_WAVE)
@@ -169,3 +178,4 @@ def test_forced_variants():
         rr.rr_set_variant_override(rr.RR_VARIANT_AUTO)
     with pytest.raises(rr.RowReduceError):
         rr.rr_set_variant_override(9)
+    assert rr.rr_query_plan(S, 10, 1024, F, F)["variant_name"] == "wave"   # override cleared

@@ -313,13 +313,15 @@ def test_softmax_many_rows_and_partial_groups():
         check_softmax(x, run_softmax(x, torch.float32), f"{M}x{N}")
 
 
-@pytest.mark.parametrize("variant", ["wave", "block", "split", "loop"])
+@pytest.mark.parametrize("variant", ["wave", "block", "split", "split1", "loop"])
 def test_softmax_forced_variants(variant):
     rr = _rr()
     code = {"wave": rr.RR_VARIANT_WAVE, "block": rr.RR_VARIANT_BLOCK,
-            "split": rr.RR_VARIANT_SPLIT, "loop": rr.RR_VARIANT_LOOP}[variant]
-    shapes = {"wave": [8, 64, 1024, 2048], "block": [8, 1024, 4096, 16384, 32768],
-              "split": [8, 1024, 4096, 4104, 65536], "loop": [8, 1024, 4096, 100000]}[variant]
+            "split": rr.RR_VARIANT_SPLIT, "split1": rr.RR_VARIANT_SPLIT_ONE_KERNEL,
+            "loop": rr.RR_VARIANT_LOOP}[variant]
+    shapes = {"wave": [8, 64, 1024, 2048], "block": [8, 1024, 4096, 16384, 32768, 65536],
+              "split": [8, 1024, 4096, 4104, 65536], "split1": [8, 4104, 65536],
+              "loop": [8, 1024, 4096, 100000]}[variant]
     try:
         rr.rr_set_variant_override(code)
         for din, dout in DTYPES:
@@ -333,6 +335,54 @@ def test_softmax_forced_variants(variant):
                     check_softmax(x, y, f"{variant} {din}->{dout} {M}x{N}")
     finally:
         rr.rr_set_variant_override(rr.RR_VARIANT_AUTO)
+
+
+def test_split_one_kernel_equals_two_kernels_bitwise():
+    """The cooperative one-kernel split and the two-kernel split use the same
+    chunks and merge order: identical bits, on the vocabulary workload's first
+    rows and on a shape whose chunks need several passes of the grid."""
+    rr = _rr()
+    cases = [workloads.make("sm_vocab", rows=64).arrays["x"],
+             softmax_input(1023, 33000, seed=4, dt="f32"),
+             softmax_input(700, 131072, seed=5, dt="bf16")]
+    for x in cases:
+        outs = []
+        for code in (rr.RR_VARIANT_SPLIT_ONE_KERNEL, rr.RR_VARIANT_SPLIT):
+            try:
+                rr.rr_set_variant_override(code)
+                outs.append(run_softmax(x, torch.float32))
+            finally:
+                rr.rr_set_variant_override(rr.RR_VARIANT_AUTO)
+        assert torch.equal(_bits(outs[0]), _bits(outs[1])), tuple(x.shape)
+        check_softmax(x, outs[0], f"split {tuple(x.shape)}")
+
+
+def test_split_row_longer_than_the_resident_grid():
+    """One row of 2^25 fp32 values: more chunks than workgroups the GPU holds
+    at once, so the one-kernel form falls back to the two kernels; both the
+    default and the forced one-kernel request must match the oracle."""
+    rr = _rr()
+    x = softmax_input(1, 1 << 25, seed=6, dt="f32")
+    check_softmax(x, run_softmax(x, torch.float32), "1 x 2^25")
+    try:
+        rr.rr_set_variant_override(rr.RR_VARIANT_SPLIT_ONE_KERNEL)
+        check_softmax(x, run_softmax(x, torch.float32), "1 x 2^25 one-kernel request")
+    finally:
+        rr.rr_set_variant_override(rr.RR_VARIANT_AUTO)
+
+
+def test_packed_long_rows_many_rows():
+    """Rows beyond 32 widened values per lane held packed in registers
+    (1024-lane workgroups, 12-20 vectors per lane), with many rows."""
+    rr = _rr()
+    for (M, N, dt) in [(1024, 100000, "bf16"), (1100, 152064, "bf16"), (1024, 81920, "f32"),
+                       (1030, 40000, "f32")]:
+        p = rr.rr_query_plan(rr.RR_OP_SOFTMAX, M, N, rr.RR_BF16 if dt == "bf16" else rr.RR_F32,
+                             rr.RR_F32)
+        assert p["variant_name"] == "block" and p["vecs_per_lane"] >= 12, p
+        _say(f"packed softmax {dt} M={M} N={N} nv={p['vecs_per_lane']}")
+        x = softmax_input(M, N, seed=M + N, dt=dt)
+        check_softmax(x, run_softmax(x, torch.float32), f"packed {M}x{N}")
 
 
 def test_softmax_in_place_unaligned_and_tiny():
