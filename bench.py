@@ -17,9 +17,11 @@ last-level cache between their repetitions, so every kernel starts cold.
 The fused op updates its residual in place each step; that changes the
 values, not the work.
 
-Per-kernel durations come from HIP events recorded on the launch stream
-between the operations inside the timed region.  The roofline object is for
-the dominant operation (largest share of the step time).
+Two timed regions of K steps each, on the launch stream: the first has HIP
+events only around the K steps and gives the value; the second records an
+event between operations and gives each operation's average duration (the
+breakdown and the roofline of the dominant operation, the one with the
+largest share of the step).
 
 cpu_baseline: the fp64 CPU oracle, timed on the host cores over the same
 workloads (all rows by default; --cpu-fraction takes the first rows of each),
@@ -229,21 +231,30 @@ def main():
 
     K = args.steps
     stream = torch.cuda.current_stream(dev)
-    marks = [[torch.cuda.Event(enable_timing=True) for _ in range(len(OPS) + 1)] for _ in range(K)]
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
+
+    # timed region 1: K whole steps, events only around them -> the value
     torch.cuda.synchronize()
     start.record(stream)
+    for _ in range(K):
+        for name in OPS:
+            ops[name]()
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms_step = start.elapsed_time(end) / K
+
+    # timed region 2: K more steps with an event between operations -> the
+    # per-operation durations (the event records add a little time of their
+    # own, so these are slight overestimates of the kernel times)
+    marks = [[torch.cuda.Event(enable_timing=True) for _ in range(len(OPS) + 1)] for _ in range(K)]
+    torch.cuda.synchronize()
     for k in range(K):
         marks[k][0].record(stream)
         for j, name in enumerate(OPS):
             ops[name]()
             marks[k][j + 1].record(stream)
-    end.record(stream)
     torch.cuda.synchronize()
-    total_ms = start.elapsed_time(end)
-    ms_step = total_ms / K
-
     per_op_ms = {name: sum(marks[k][j].elapsed_time(marks[k][j + 1]) for k in range(K)) / K
                  for j, name in enumerate(OPS)}
     step_bytes = sum(algorithmic_bytes(n, bufs[n]["M"], bufs[n]["N"]) for n in OPS)
