@@ -168,14 +168,19 @@ typedef enum rr_op {
  *         It falls back to the two kernels when the device cannot hold a
  *         row's chunks at once.  Both forms give the same bits.
  *   LOOP  one workgroup per row streaming the row twice (any N, unaligned
- *         rows, long rows with many rows) */
+ *         rows, long rows with many rows)
+ *   SUBWAVE short rows (at most 32 vectors, or 32 elements when unaligned):
+ *         L lanes per row, 64/L rows per wavefront, reduced inside each
+ *         L-lane group ([P4] section "按行长度选择并行方式")
+ * For SUBWAVE, rr_plan.waves_per_row holds the lanes per row L. */
 typedef enum rr_variant {
   RR_VARIANT_AUTO = 0,
   RR_VARIANT_WAVE = 1,
   RR_VARIANT_BLOCK = 2,
   RR_VARIANT_SPLIT = 3,
   RR_VARIANT_LOOP = 4,
-  RR_VARIANT_SPLIT_ONE_KERNEL = 5  /* SPLIT as one cooperative kernel (opt-in) */
+  RR_VARIANT_SPLIT_ONE_KERNEL = 5, /* SPLIT as one cooperative kernel (opt-in) */
+  RR_VARIANT_SUBWAVE = 6           /* short rows, several rows per wavefront */
 } rr_variant;
 
 typedef struct rr_plan {

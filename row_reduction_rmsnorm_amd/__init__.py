@@ -10,7 +10,7 @@ from .binding import (  # noqa: F401
     BF16, EXPORTS, F32, RR_BF16, RR_ERR_HIP, RR_ERR_INVALID_ARG, RR_ERR_UNSUPPORTED,
     RR_ERR_WORKSPACE, RR_F32, RR_OK, RR_OP_FUSED_ADD_RMSNORM, RR_OP_RMSNORM, RR_OP_SOFTMAX,
     RR_VARIANT_AUTO, RR_VARIANT_BLOCK, RR_VARIANT_LOOP, RR_VARIANT_SPLIT, RR_VARIANT_SPLIT_ONE_KERNEL,
-    RR_VARIANT_WAVE,
+    RR_VARIANT_SUBWAVE, RR_VARIANT_WAVE,
     RowReduceError, VARIANT_NAMES, check, dtype_code, fused_add_rmsnorm, last_error_message, lib,
     raw_fused_add_rmsnorm, raw_rmsnorm, raw_softmax_rows, rmsnorm, rr_fused_add_rmsnorm,
     rr_query_plan, rr_rmsnorm, rr_selftest_wave_allreduce, rr_set_variant_override,

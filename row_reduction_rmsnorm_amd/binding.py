@@ -33,7 +33,8 @@ RR_VARIANT_BLOCK = 2
 RR_VARIANT_SPLIT = 3
 RR_VARIANT_LOOP = 4
 RR_VARIANT_SPLIT_ONE_KERNEL = 5
-VARIANT_NAMES = {0: "auto", 1: "wave", 2: "block", 3: "split", 4: "loop", 5: "split1"}
+RR_VARIANT_SUBWAVE = 6
+VARIANT_NAMES = {0: "auto", 1: "wave", 2: "block", 3: "split", 4: "loop", 5: "split1", 6: "subwave"}
 
 # Every function include/rowreduce.h declares.
 EXPORTS = (

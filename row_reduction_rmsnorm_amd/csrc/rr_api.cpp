@@ -71,6 +71,20 @@ constexpr int kSplitVecsPerLane = 4;
 int max_floats(rr_op op) { return op == RR_OP_SOFTMAX ? 32 : 16; }
 int inputs_of(rr_op op) { return op == RR_OP_FUSED_ADD_RMSNORM ? 2 : 1; }
 
+// Short rows: L lanes per row (the smallest power of two covering the row's
+// vectors, at most 32), 256/L rows per 256-thread workgroup.
+constexpr int64_t kSubMaxVectors = 32;
+bool plan_sub(rr_plan* p, int vec, int64_t nvec) {
+  if (nvec > kSubMaxVectors) return false;
+  p->variant = RR_VARIANT_SUBWAVE;
+  p->vec_elems = vec;
+  p->waves_per_row = pow2_at_least(nvec);   // lanes per row
+  p->rows_per_group = 256 / p->waves_per_row;
+  p->vecs_per_lane = 1;
+  p->block_threads = 256;
+  return true;
+}
+
 void plan_wave(rr_plan* p, int vec, int64_t nvec) {
   p->variant = RR_VARIANT_WAVE;
   p->vec_elems = vec;
@@ -168,7 +182,8 @@ rr_status make_plan(rr_op op, int64_t M, int64_t N, int din, int dout, bool is_a
   bool ok = false;
   switch (forced) {
     case RR_VARIANT_AUTO:
-      if (vec == 1) {
+      if (plan_sub(p, vec, nvec)) {
+      } else if (vec == 1) {
         plan_loop(p, vec, nvec);
       } else if (wave_fits(op, vec, nvec)) {
         plan_wave(p, vec, nvec);
@@ -199,6 +214,9 @@ rr_status make_plan(rr_op op, int64_t M, int64_t N, int din, int dout, bool is_a
     case RR_VARIANT_LOOP:
       plan_loop(p, vec, nvec);
       ok = true;
+      break;
+    case RR_VARIANT_SUBWAVE:
+      ok = plan_sub(p, vec, nvec);
       break;
     default:
       break;
@@ -374,7 +392,7 @@ rr_status rr_query_plan(rr_op op, int64_t M, int64_t N, rr_dtype in_dtype, rr_dt
 
 rr_status rr_set_variant_override(rr_variant v) {
   g_err[0] = '\0';
-  if (v < RR_VARIANT_AUTO || v > RR_VARIANT_SPLIT_ONE_KERNEL)
+  if (v < RR_VARIANT_AUTO || v > RR_VARIANT_SUBWAVE)
     return fail(RR_ERR_INVALID_ARG, "rr_set_variant_override: unknown variant %d", (int)v);
   g_override.store(v, std::memory_order_relaxed);
   return RR_OK;

@@ -257,6 +257,24 @@ __device__ __forceinline__ float wave_max(float v) {
   return __builtin_fmaxf(a, b);
 }
 
+// The same butterfly restricted to groups of L consecutive lanes (L a power of
+// two, at most 32): the first log2(L) steps of the six above.  Every lane of a
+// group ends with the group's total, bit for bit; groups do not mix.
+template <int L>
+__device__ __forceinline__ float group_lanes_sum(float v) {
+  static_assert(L >= 1 && L <= 32 && (L & (L - 1)) == 0, "L must be a power of two <= 32");
+  if constexpr (L >= 2) v = v + dpp_f32<kDppQuadXor1>(v);
+  if constexpr (L >= 4) v = v + dpp_f32<kDppQuadXor2>(v);
+  if constexpr (L >= 8) v = v + dpp_f32<kDppRowHalfMirror>(v);
+  if constexpr (L >= 16) v = v + dpp_f32<kDppRowMirror>(v);
+  if constexpr (L >= 32) {
+    float a, b;
+    swap16(v, a, b);
+    v = a + b;
+  }
+  return v;
+}
+
 // ---------------------------------------------------------------------------
 // the online-softmax pair
 //
@@ -307,6 +325,23 @@ __device__ __forceinline__ MD wave_md(MD v) {
   swap32(v.m, e.m, o.m);
   swap32(v.d, e.d, o.d);
   return md_merge(e, o);
+}
+
+// The pair all-reduce restricted to groups of L consecutive lanes.
+template <int L>
+__device__ __forceinline__ MD group_lanes_md(MD v) {
+  static_assert(L >= 1 && L <= 32 && (L & (L - 1)) == 0, "L must be a power of two <= 32");
+  if constexpr (L >= 2) v = md_merge(v, dpp_md<kDppQuadXor1>(v));
+  if constexpr (L >= 4) v = md_merge(v, dpp_md<kDppQuadXor2>(v));
+  if constexpr (L >= 8) v = md_merge(v, dpp_md<kDppRowHalfMirror>(v));
+  if constexpr (L >= 16) v = md_merge(v, dpp_md<kDppRowMirror>(v));
+  if constexpr (L >= 32) {
+    MD e, o;
+    swap16(v.m, e.m, o.m);
+    swap16(v.d, e.d, o.d);
+    v = md_merge(e, o);
+  }
+  return v;
 }
 
 // Summary pair of VEC register values (the chunk summary of [P1] section

@@ -255,6 +255,99 @@ __global__ __launch_bounds__(1024) void norm_loop_kernel(T* y, T* residual, cons
 }
 
 // ===========================================================================
+// Short rows, several per wavefront (SUBWAVE).
+//
+// [P4] section "按行长度选择并行方式": rows of a few dozen elements should not
+// occupy a whole wavefront.  A wavefront holds 64/L rows of L lanes each;
+// lane j of a row owns vector j (one vector, VEC elements, or one element when
+// VEC = 1, so unaligned short rows take this path too).  The reductions run
+// only the butterfly steps inside an L-lane group, so no LDS and no barrier.
+// ===========================================================================
+template <typename T, int VEC, int L, bool FUSED>
+__global__ __launch_bounds__(256) void norm_sub_kernel(T* y, T* residual, const T* x,
+                                                       const T* __restrict__ gamma, int64_t M,
+                                                       int N, float eps) {
+  constexpr int kRowsPerGroup = 256 / L;
+  const int j = threadIdx.x & (L - 1);              // lane within the row
+  const int nvec = N / VEC;
+  const bool active = j < nvec;
+  Packed<T, VEC> g;
+  if (active) g.load(gamma + (int64_t)j * VEC);
+  else g.fill(0.0f);
+  for (int64_t row = (int64_t)blockIdx.x * kRowsPerGroup + (threadIdx.x / L); row < M;
+       row += (int64_t)gridDim.x * kRowsPerGroup) {
+    const int64_t off = row * (int64_t)N + (int64_t)j * VEC;
+    float h[VEC];
+    if (active) {
+      load_vec<T, VEC>(x + off, h);
+      if constexpr (FUSED) {
+        float r[VEC];
+        load_vec<T, VEC>(residual + off, r);
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) h[i] = round_to<T>(h[i] + r[i]);
+        store_vec<T, VEC>(residual + off, h);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) h[i] = 0.0f;
+    }
+    float ss = 0.0f;
+#pragma unroll
+    for (int i = 0; i < VEC; ++i) ss += h[i] * h[i];
+    ss = group_lanes_sum<L>(ss);
+    const float rstd = 1.0f / __builtin_sqrtf(ss / (float)N + eps);
+    if (active) {
+      float o[VEC];
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) o[i] = (h[i] * rstd) * g.get(i);
+      store_vec<T, VEC>(y + off, o);
+    }
+  }
+}
+
+template <typename Tin, typename Tout, int VEC, int L>
+__global__ __launch_bounds__(256) void softmax_sub_kernel(const Tin* x, Tout* y, int64_t M,
+                                                          int N) {
+  constexpr int kRowsPerGroup = 256 / L;
+  const int j = threadIdx.x & (L - 1);
+  const int nvec = N / VEC;
+  const bool active = j < nvec;
+  for (int64_t row = (int64_t)blockIdx.x * kRowsPerGroup + (threadIdx.x / L); row < M;
+       row += (int64_t)gridDim.x * kRowsPerGroup) {
+    const int64_t off = row * (int64_t)N + (int64_t)j * VEC;
+    float v[VEC];
+    if (active) {
+      load_vec<Tin, VEC>(x + off, v);
+    } else {
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) v[i] = kNegInf;
+    }
+    float ml = v[0];
+#pragma unroll
+    for (int i = 1; i < VEC; ++i) ml = __builtin_fmaxf(ml, v[i]);
+    const float shift = (ml == kNegInf) ? 0.0f : ml;
+    float dl = 0.0f;
+#pragma unroll
+    for (int i = 0; i < VEC; ++i) {
+      v[i] = exp_shifted(v[i] - shift);
+      dl += v[i];
+    }
+    MD p;
+    p.m = ml;
+    p.d = dl;
+    p = group_lanes_md<L>(p);
+    float c = (ml == kNegInf) ? 0.0f : exp_shifted(ml - p.m) / p.d;
+    if (p.m == kNegInf) c = __builtin_nanf("");
+    if (active) {
+      float o[VEC];
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) o[i] = v[i] * c;
+      store_vec<Tout, VEC>(y + off, o);
+    }
+  }
+}
+
+// ===========================================================================
 // Softmax, row held in registers (WAVE and BLOCK).
 //
 // Each lane summarises the NV*VEC values it holds as a pair (m_l, d_l): its
@@ -722,10 +815,34 @@ hipError_t norm_loop(const rr_plan& p, void* y, void* res, const void* x, const 
   return hipGetLastError();
 }
 
+template <typename T, int VEC, bool FUSED>
+hipError_t norm_sub(const rr_plan& p, void* y, void* res, const void* x, const void* gamma,
+                    int64_t M, int N, float eps, int64_t grid, hipStream_t s) {
+  T* yy = static_cast<T*>(y);
+  T* rr_ = static_cast<T*>(res);
+  const T* xx = static_cast<const T*>(x);
+  const T* gg = static_cast<const T*>(gamma);
+  const dim3 b(256);
+  switch (p.waves_per_row) {  // for SUBWAVE: lanes per row
+    case 1: norm_sub_kernel<T, VEC, 1, FUSED><<<grid1(grid), b, 0, s>>>(yy, rr_, xx, gg, M, N, eps); break;
+    case 2: norm_sub_kernel<T, VEC, 2, FUSED><<<grid1(grid), b, 0, s>>>(yy, rr_, xx, gg, M, N, eps); break;
+    case 4: norm_sub_kernel<T, VEC, 4, FUSED><<<grid1(grid), b, 0, s>>>(yy, rr_, xx, gg, M, N, eps); break;
+    case 8: norm_sub_kernel<T, VEC, 8, FUSED><<<grid1(grid), b, 0, s>>>(yy, rr_, xx, gg, M, N, eps); break;
+    case 16: norm_sub_kernel<T, VEC, 16, FUSED><<<grid1(grid), b, 0, s>>>(yy, rr_, xx, gg, M, N, eps); break;
+    case 32: norm_sub_kernel<T, VEC, 32, FUSED><<<grid1(grid), b, 0, s>>>(yy, rr_, xx, gg, M, N, eps); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 template <typename T, bool FUSED>
 hipError_t norm_any(const rr_plan& p, void* y, void* res, const void* x, const void* gamma,
                     int64_t M, int N, float eps, int64_t grid, hipStream_t s) {
   if (p.variant == RR_VARIANT_LOOP) return norm_loop<T, FUSED>(p, y, res, x, gamma, M, N, eps, grid, s);
+  if (p.variant == RR_VARIANT_SUBWAVE) {
+    if (p.vec_elems == 1) return norm_sub<T, 1, FUSED>(p, y, res, x, gamma, M, N, eps, grid, s);
+    return norm_sub<T, Elem<T>::kVec, FUSED>(p, y, res, x, gamma, M, N, eps, grid, s);
+  }
   if (p.variant == RR_VARIANT_WAVE) return norm_regs<T, FUSED, true>(p, y, res, x, gamma, M, N, eps, grid, s);
   return norm_regs<T, FUSED, false>(p, y, res, x, gamma, M, N, eps, grid, s);
 }
@@ -802,12 +919,32 @@ hipError_t softmax_split(const rr_plan& p, const Tin* xx, Tout* yy, SplitSlot* w
   return hipGetLastError();
 }
 
+template <typename Tin, typename Tout, int VEC>
+hipError_t softmax_sub(const rr_plan& p, const Tin* xx, Tout* yy, int64_t M, int N, int64_t grid,
+                       hipStream_t s) {
+  const dim3 b(256);
+  switch (p.waves_per_row) {  // for SUBWAVE: lanes per row
+    case 1: softmax_sub_kernel<Tin, Tout, VEC, 1><<<grid1(grid), b, 0, s>>>(xx, yy, M, N); break;
+    case 2: softmax_sub_kernel<Tin, Tout, VEC, 2><<<grid1(grid), b, 0, s>>>(xx, yy, M, N); break;
+    case 4: softmax_sub_kernel<Tin, Tout, VEC, 4><<<grid1(grid), b, 0, s>>>(xx, yy, M, N); break;
+    case 8: softmax_sub_kernel<Tin, Tout, VEC, 8><<<grid1(grid), b, 0, s>>>(xx, yy, M, N); break;
+    case 16: softmax_sub_kernel<Tin, Tout, VEC, 16><<<grid1(grid), b, 0, s>>>(xx, yy, M, N); break;
+    case 32: softmax_sub_kernel<Tin, Tout, VEC, 32><<<grid1(grid), b, 0, s>>>(xx, yy, M, N); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 template <typename Tin, typename Tout>
 hipError_t softmax_typed(const rr_plan& p, void* y, const void* x, void* ws, int64_t M, int N,
                          int64_t grid, hipStream_t s) {
   const Tin* xx = static_cast<const Tin*>(x);
   Tout* yy = static_cast<Tout*>(y);
   const dim3 b(p.block_threads);
+  if (p.variant == RR_VARIANT_SUBWAVE) {
+    if (p.vec_elems == 1) return softmax_sub<Tin, Tout, 1>(p, xx, yy, M, N, grid, s);
+    return softmax_sub<Tin, Tout, Elem<Tin>::kVec>(p, xx, yy, M, N, grid, s);
+  }
   if (p.variant == RR_VARIANT_LOOP) {
     if (p.vec_elems == 1)
       softmax_loop_kernel<Tin, Tout, 1><<<grid1(grid), b, 0, s>>>(xx, yy, M, N);

@@ -150,6 +150,14 @@ def test_dispatch_boundaries():
     assert v(S, 1024, 81924) == "loop"
     assert v(S, 1024, 163840, B, F) == "block"
     assert v(S, 1024, 163848, B, F) == "loop"
+    # short rows: several rows per wavefront, L lanes per row
+    assert v(S, 10, 128) == "subwave" and rr.rr_query_plan(S, 10, 128, F, F)["waves_per_row"] == 32
+    assert v(S, 10, 132) == "wave"
+    assert rr.rr_query_plan(S, 10, 8, F, F)["waves_per_row"] == 2
+    assert rr.rr_query_plan(S, 10, 1, F, F)["waves_per_row"] == 1
+    assert v(rr.RR_OP_FUSED_ADD_RMSNORM, 10, 256, B, B) == "subwave"
+    assert v(S, 10, 7) == "subwave" and rr.rr_query_plan(S, 10, 7, F, F)["vec_elems"] == 1
+    assert v(S, 10, 33) == "loop"          # unaligned and longer than 32 elements
     # unaligned widths or pointers take the scalar streaming path
     assert v(S, 10, 1023) == "loop"
     assert v(S, 10, 1024, al=False) == "loop"

@@ -265,12 +265,13 @@ def test_norm_in_place_and_unaligned(dt):
     check_norm(x, g, 1e-6, dt, y.cpu(), "unaligned")
 
 
-@pytest.mark.parametrize("variant", ["wave", "block", "loop"])
+@pytest.mark.parametrize("variant", ["wave", "block", "loop", "subwave"])
 def test_norm_forced_variants(variant):
     rr = _rr()
-    code = {"wave": rr.RR_VARIANT_WAVE, "block": rr.RR_VARIANT_BLOCK, "loop": rr.RR_VARIANT_LOOP}[variant]
+    code = {"wave": rr.RR_VARIANT_WAVE, "block": rr.RR_VARIANT_BLOCK, "loop": rr.RR_VARIANT_LOOP,
+            "subwave": rr.RR_VARIANT_SUBWAVE}[variant]
     shapes = {"wave": [8, 64, 520, 1024], "block": [8, 1024, 3584, 4096, 16384],
-              "loop": [8, 1024, 4096, 20000, 65536]}[variant]
+              "loop": [8, 1024, 4096, 20000, 65536], "subwave": [8, 16, 24, 64, 128]}[variant]
     try:
         rr.rr_set_variant_override(code)
         for dt in ("f32", "bf16"):
@@ -306,6 +307,22 @@ def test_softmax_grid(din, dout, N):
         check_softmax(x, y, f"softmax {din}->{dout} {M}x{N}")
 
 
+def test_short_rows_unaligned_and_partial_groups():
+    """Short rows (several per wavefront), including unaligned widths (scalar
+    lanes), row counts that leave a partial group, and fully masked rows."""
+    for N in (1, 2, 3, 5, 7, 17, 31, 32):
+        for M in (1, 3, 255, 257, 1000):
+            for dt in ("f32", "bf16"):
+                x = softmax_input(M, N, seed=N * 1000 + M, dt=dt)
+                check_softmax(x, run_softmax(x, _tdt(dt)), f"short softmax {dt} {M}x{N}")
+                xn = _as(workloads.random_rows(M, N, seed=N + M), dt)
+                g = _as(workloads.gamma_vector(N, seed=N), dt)
+                check_norm(xn, g, 1e-6, dt, run_rmsnorm(xn, g, 1e-6), f"short rms {dt} {M}x{N}")
+                r = _as(workloads.random_rows(M, N, seed=N + M + 1), dt)
+                yf, rf = run_fused(xn, r, g, 1e-6)
+                check_fused(xn, r, g, 1e-6, dt, yf, rf, f"short fused {dt} {M}x{N}")
+
+
 def test_softmax_many_rows_and_partial_groups():
     for (M, N) in [(257, 1024), (1023, 33000), (1024, 33000), (4097, 64)]:
         _say(f"softmax rows M={M} N={N}")
@@ -313,15 +330,15 @@ def test_softmax_many_rows_and_partial_groups():
         check_softmax(x, run_softmax(x, torch.float32), f"{M}x{N}")
 
 
-@pytest.mark.parametrize("variant", ["wave", "block", "split", "split1", "loop"])
+@pytest.mark.parametrize("variant", ["wave", "block", "split", "split1", "loop", "subwave"])
 def test_softmax_forced_variants(variant):
     rr = _rr()
     code = {"wave": rr.RR_VARIANT_WAVE, "block": rr.RR_VARIANT_BLOCK,
             "split": rr.RR_VARIANT_SPLIT, "split1": rr.RR_VARIANT_SPLIT_ONE_KERNEL,
-            "loop": rr.RR_VARIANT_LOOP}[variant]
+            "loop": rr.RR_VARIANT_LOOP, "subwave": rr.RR_VARIANT_SUBWAVE}[variant]
     shapes = {"wave": [8, 64, 1024, 2048], "block": [8, 1024, 4096, 16384, 32768, 65536],
               "split": [8, 1024, 4096, 4104, 65536], "split1": [8, 4104, 65536],
-              "loop": [8, 1024, 4096, 100000]}[variant]
+              "loop": [8, 1024, 4096, 100000], "subwave": [8, 16, 40, 64, 128]}[variant]
     try:
         rr.rr_set_variant_override(code)
         for din, dout in DTYPES:
