@@ -1,4 +1,4 @@
-"""CPU oracle for RMSNorm, fused residual-add + RMSNorm and row softmax.
+"""CPU oracle for RMSNorm, fused residual-add + RMSNorm, LayerNorm and row softmax.
 
 TEST INFRASTRUCTURE ONLY.  Only the test suite, the package smoke check and
 the benchmark's CPU-baseline leg may import this package.  It shares no code
@@ -42,12 +42,13 @@ def _lib():
         lib.oracle_round_f32.restype = ctypes.c_double
         lib.oracle_round_array.argtypes = [ctypes.c_int, i64, _dp, _dp]
         lib.oracle_rmsnorm.argtypes = [i64, i64, _dp, _dp, ctypes.c_double, _dp]
+        lib.oracle_layernorm.argtypes = [i64, i64, _dp, _dp, _dp, ctypes.c_double, _dp]
         lib.oracle_fused_add_rmsnorm.argtypes = [i64, i64, _dp, _dp, _dp, ctypes.c_double,
                                                  ctypes.c_int, _dp, _dp]
         lib.oracle_softmax.argtypes = [i64, i64, _dp, _dp]
         lib.oracle_softmax_stats.argtypes = [i64, i64, _dp, _dp, _dp]
         for f in ("oracle_rmsnorm", "oracle_fused_add_rmsnorm", "oracle_softmax",
-                  "oracle_softmax_stats"):
+                  "oracle_softmax_stats", "oracle_layernorm"):
             getattr(lib, f).restype = ctypes.c_int
         _LIB = lib
     return _LIB
@@ -101,6 +102,27 @@ def rmsnorm(x, gamma, eps):
         raise ValueError("gamma must have shape [H]")
     y = np.empty_like(x2)
     _check(_lib().oracle_rmsnorm(M, H, _ptr(x2), _ptr(gamma), float(eps), _ptr(y)), "rmsnorm")
+    return y.reshape(shape)
+
+
+def layernorm(x, gamma, beta, eps):
+    """y[M,H] in fp64 for x[M,H] (or [H]), gamma[H], beta[H] or None."""
+    x = _f64(x)
+    gamma = _f64(gamma)
+    shape = x.shape
+    x2 = x.reshape(-1, shape[-1])
+    M, H = x2.shape
+    if gamma.shape != (H,):
+        raise ValueError("gamma must have shape [H]")
+    bp = None
+    if beta is not None:
+        beta = _f64(beta)
+        if beta.shape != (H,):
+            raise ValueError("beta must have shape [H]")
+        bp = _ptr(beta)
+    y = np.empty_like(x2)
+    _check(_lib().oracle_layernorm(M, H, _ptr(x2), _ptr(gamma), bp, float(eps), _ptr(y)),
+           "layernorm")
     return y.reshape(shape)
 
 

@@ -142,6 +142,36 @@ int oracle_fused_add_rmsnorm(int64_t M, int64_t H, const double* x, const double
 }
 
 /*
+ * LayerNorm of one row, plain two-pass definition:
+ *   mu = (1/H) sum_j x_j,   var = (1/H) sum_j (x_j - mu)^2,
+ *   y_j = (x_j - mu) / sqrt(var + eps) * gamma_j + beta_j
+ * [P2] section 八.2 (the LayerNorm formula, the variance over d, eps inside
+ * the root); [P4] section "LayerNorm 与 RMSNorm" (the same formula) and its
+ * exercise (mean first, then the variance from the centred values).  beta may
+ * be NULL, meaning zero.
+ */
+static void layernorm_row(int64_t H, const double* x, const double* gamma, const double* beta,
+                          double eps, double* y) {
+    double sum = 0.0;
+    for (int64_t j = 0; j < H; ++j) sum += x[j];
+    double mu = sum / (double)H;
+    double ss = 0.0;
+    for (int64_t j = 0; j < H; ++j) ss += (x[j] - mu) * (x[j] - mu);
+    double var = ss / (double)H;
+    double r = 1.0 / sqrt(var + eps);
+    for (int64_t j = 0; j < H; ++j) y[j] = (x[j] - mu) * r * gamma[j] + (beta ? beta[j] : 0.0);
+}
+
+/* LayerNorm over M rows of width H. Returns 0, or -1 when H < 1. */
+int oracle_layernorm(int64_t M, int64_t H, const double* x, const double* gamma,
+                     const double* beta, double eps, double* y) {
+    if (H < 1 || M < 0) return -1;
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < M; ++i) layernorm_row(H, x + i * H, gamma, beta, eps, y + i * H);
+    return 0;
+}
+
+/*
  * Safe softmax of one row, three passes over the row:
  *   m = max_j x_j,   d = sum_j exp(x_j - m),   y_j = exp(x_j - m) / d
  * [P1] section "一、为什么要减 max" (subtract the row maximum; the shift

@@ -30,6 +30,10 @@ MUTANTS = {
                              "v = (double)(float)v;\n    if (isnan(v) || isinf(v) || v == 0.0) return v;"),
     "bf16_ties_away": ("double q = rint(v / spacing);", "double q = round(v / spacing);"),
     "bf16_one_bit_short": ("double spacing = ldexp(1.0, e - 7);", "double spacing = ldexp(1.0, e - 6);"),
+    "ln_var_over_H_minus_1": ("double var = ss / (double)H;", "double var = ss / (double)(H > 1 ? H - 1 : 1);"),
+    "ln_no_centering": ("y[j] = (x[j] - mu) * r * gamma[j]", "y[j] = x[j] * r * gamma[j]"),
+    "ln_beta_dropped": ("+ (beta ? beta[j] : 0.0);", "+ 0.0;"),
+    "ln_eps_outside": ("double r = 1.0 / sqrt(var + eps);", "double r = 1.0 / sqrt(var) + eps;"),
 }
 
 

@@ -138,6 +138,54 @@ def test_rmsnorm_rejects_empty_row():
 
 
 # ----------------------------------------------------------------------------
+# LayerNorm: closed forms, invariants, library routine
+# ----------------------------------------------------------------------------
+
+def test_layernorm_closed_forms():
+    # x = (1, 2, 3, 4): mean 2.5, variance (2.25 + 0.25 + 0.25 + 2.25) / 4 = 1.25
+    y = oracle.layernorm(np.array([[1.0, 2.0, 3.0, 4.0]]), np.ones(4), None, 0.0)[0]
+    expect = (np.array([1.0, 2.0, 3.0, 4.0]) - 2.5) / math.sqrt(1.25)
+    assert np.allclose(y, expect, rtol=1e-15, atol=1e-15)
+    # a constant row has x - mean = 0, so y = beta exactly, whatever eps and gamma
+    beta = np.linspace(-1, 1, 9)
+    y = oracle.layernorm(np.full((2, 9), 101.25), np.arange(1.0, 10.0), beta, 1e-5)
+    assert np.array_equal(y, np.stack([beta, beta]))
+    # eps inside the root and the 1/H divisor: two values +-a give var = a^2
+    a, eps = 0.5, 0.01
+    y = oracle.layernorm(np.array([[a, -a]]), np.ones(2), np.zeros(2), eps)[0]
+    assert np.allclose(y, [a / math.sqrt(a * a + eps), -a / math.sqrt(a * a + eps)], rtol=1e-15)
+
+
+def test_layernorm_invariants():
+    rng = np.random.default_rng(19)
+    x = rng.uniform(100.0, 102.0, (6, 5120))
+    y = oracle.layernorm(x, np.ones(5120), None, 0.0)
+    assert np.allclose(y.mean(axis=1), 0.0, atol=1e-12)
+    assert np.allclose((y * y).mean(axis=1), 1.0, atol=1e-12)
+    # translation invariance, bitwise for an exact shift of dyadic values
+    xd = np.round(rng.standard_normal((4, 64)) * 64) / 64
+    assert np.array_equal(oracle.layernorm(xd, np.ones(64), None, 1e-5),
+                          oracle.layernorm(xd + 256.0, np.ones(64), None, 1e-5))
+
+
+def test_layernorm_matches_torch_fp64():
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(20)
+    for (M, H, eps, lo, hi) in [(3, 5, 1e-5, -1, 1), (4, 5120, 1e-5, 100, 102), (2, 97, 0.3, -3, 9),
+                                (5, 1, 1e-5, -1, 1)]:
+        x = rng.uniform(lo, hi, (M, H))
+        g = rng.uniform(0.5, 1.5, H)
+        b = rng.uniform(-1, 1, H)
+        y = oracle.layernorm(x, g, b, eps)
+        ref = torch.nn.functional.layer_norm(torch.from_numpy(x), (H,), weight=torch.from_numpy(g),
+                                             bias=torch.from_numpy(b), eps=eps).numpy()
+        # two fp64 summation orders differ near 1e-12 when the mean is ~100x the spread
+        assert np.allclose(y, ref, rtol=1e-10, atol=1e-11), (M, H)
+        y0 = oracle.layernorm(x, g, None, eps)
+        assert np.allclose(y0, ref - b, rtol=1e-10, atol=1e-11)
+
+
+# ----------------------------------------------------------------------------
 # bf16 rounding: library routine, ties, single rounding, range ends
 # ----------------------------------------------------------------------------
 
