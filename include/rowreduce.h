@@ -5,6 +5,7 @@
  * Operations (each row of a row-major [M, N] matrix is independent):
  *   rr_rmsnorm            y = x * rsqrt(mean(x^2) + eps) * gamma
  *   rr_fused_add_rmsnorm  residual <- residual + x;  y = rmsnorm(residual) * gamma
+ *   rr_layernorm          y = (x - mean) * rsqrt(var + eps) * gamma + beta
  *   rr_softmax_rows       y = exp(x - m) / d with the online normaliser (m, d)
  *
  * Sources (web pages, cited by title and section):
@@ -101,6 +102,25 @@ rr_status rr_fused_add_rmsnorm(void* y, void* residual, const void* x, const voi
                                void* stream);
 
 /*
+ * rr_layernorm -- LayerNorm of each row.
+ *   mu_i = (1/H) sum_j x[i, j],   var_i = (1/H) sum_j (x[i, j] - mu_i)^2,
+ *   y[i, j] = (x[i, j] - mu_i) / sqrt(var_i + eps) * gamma[j] + beta[j]
+ * ([P2] section 八.2; [P4] section "LayerNorm 与 RMSNorm" and its LayerNorm
+ * exercise: the mean first, then the variance from the values held in
+ * registers.)  Rows up to 16384 elements are held in registers (two
+ * reductions per row); longer or unaligned rows are read three times.  The
+ * mean is accumulated about the row's first element, so rows whose mean is
+ * far larger than their spread keep their precision.
+ *   y      [M, H] output, dtype `dtype`; may be the same pointer as x
+ *   x      [M, H] input (finite values)
+ *   gamma  [H] scale
+ *   beta   [H] shift, or NULL for none
+ * All in dtype `dtype`.  Errors as rr_rmsnorm (beta must not overlap y).
+ */
+rr_status rr_layernorm(void* y, const void* x, const void* gamma, const void* beta, int64_t M,
+                       int64_t H, float eps, rr_dtype dtype, void* stream);
+
+/*
  * rr_softmax_rows_workspace_bytes -- device workspace rr_softmax_rows needs
  * for this shape (0 when the chosen kernel needs none).  Very long rows with
  * few rows are split over several workgroups; each writes its chunk's
@@ -150,7 +170,8 @@ const char* rr_last_error_message(void);
 typedef enum rr_op {
   RR_OP_RMSNORM = 0,
   RR_OP_FUSED_ADD_RMSNORM = 1,
-  RR_OP_SOFTMAX = 2
+  RR_OP_SOFTMAX = 2,
+  RR_OP_LAYERNORM = 3
 } rr_op;
 
 /* Kernel variants, chosen by row length ([P2] section 六; [P4] section

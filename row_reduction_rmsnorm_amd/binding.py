@@ -26,6 +26,7 @@ RR_ERR_HIP = 4
 RR_OP_RMSNORM = 0
 RR_OP_FUSED_ADD_RMSNORM = 1
 RR_OP_SOFTMAX = 2
+RR_OP_LAYERNORM = 3
 
 RR_VARIANT_AUTO = 0
 RR_VARIANT_WAVE = 1
@@ -38,7 +39,7 @@ VARIANT_NAMES = {0: "auto", 1: "wave", 2: "block", 3: "split", 4: "loop", 5: "sp
 
 # Every function include/rowreduce.h declares.
 EXPORTS = (
-    "rr_rmsnorm", "rr_fused_add_rmsnorm", "rr_softmax_rows_workspace_bytes",
+    "rr_rmsnorm", "rr_fused_add_rmsnorm", "rr_layernorm", "rr_softmax_rows_workspace_bytes",
     "rr_softmax_rows", "rr_status_string", "rr_last_error_message", "rr_query_plan",
     "rr_set_variant_override", "rr_selftest_wave_allreduce",
 )
@@ -89,6 +90,7 @@ def lib():
     vp, i64, f32, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_float, ctypes.c_int
     L.rr_rmsnorm.argtypes = [vp, vp, vp, i64, i64, f32, i32, vp]
     L.rr_fused_add_rmsnorm.argtypes = [vp, vp, vp, vp, i64, i64, f32, i32, vp]
+    L.rr_layernorm.argtypes = [vp, vp, vp, vp, i64, i64, f32, i32, vp]
     L.rr_softmax_rows_workspace_bytes.argtypes = [i64, i64, i32, i32]
     L.rr_softmax_rows_workspace_bytes.restype = ctypes.c_size_t
     L.rr_softmax_rows.argtypes = [vp, vp, i64, i64, i32, i32, vp, ctypes.c_size_t, vp]
@@ -99,7 +101,7 @@ def lib():
     L.rr_query_plan.argtypes = [i32, i64, i64, i32, i32, i32, ctypes.POINTER(rr_plan)]
     L.rr_set_variant_override.argtypes = [i32]
     L.rr_selftest_wave_allreduce.argtypes = [vp, vp, i64, i32, vp]
-    for f in ("rr_rmsnorm", "rr_fused_add_rmsnorm", "rr_softmax_rows", "rr_query_plan",
+    for f in ("rr_rmsnorm", "rr_fused_add_rmsnorm", "rr_layernorm", "rr_softmax_rows", "rr_query_plan",
               "rr_set_variant_override", "rr_selftest_wave_allreduce"):
         getattr(L, f).restype = i32
     _LIB = L
@@ -129,6 +131,10 @@ def raw_rmsnorm(y, x, gamma, M, H, eps, dtype, stream):
 
 def raw_fused_add_rmsnorm(y, residual, x, gamma, M, H, eps, dtype, stream):
     return lib().rr_fused_add_rmsnorm(y, residual, x, gamma, M, H, eps, dtype, stream)
+
+
+def raw_layernorm(y, x, gamma, beta, M, H, eps, dtype, stream):
+    return lib().rr_layernorm(y, x, gamma, beta, M, H, eps, dtype, stream)
 
 
 def raw_softmax_rows(y, x, M, N, in_dtype, out_dtype, workspace, workspace_bytes, stream):
@@ -221,6 +227,26 @@ def rr_fused_add_rmsnorm(y, residual, x, gamma, eps: float, stream=None) -> None
                                 _stream_of(x, stream)), "rr_fused_add_rmsnorm")
 
 
+def rr_layernorm(y, x, gamma, beta, eps: float, stream=None) -> None:
+    """y = (x - mean) * rsqrt(var + eps) * gamma + beta over the last dimension
+    (beta may be None)."""
+    _need_cuda(y, x, gamma)
+    M, H = _rows(x)
+    if y.shape != x.shape or gamma.shape != (H,) or (beta is not None and beta.shape != (H,)):
+        raise ValueError("y must match x; gamma and beta must be [H]")
+    dt = dtype_code(x)
+    if dtype_code(y) != dt or dtype_code(gamma) != dt:
+        raise TypeError("x, y, gamma and beta must share one dtype")
+    bp = None
+    if beta is not None:
+        _need_cuda(beta)
+        if dtype_code(beta) != dt:
+            raise TypeError("x, y, gamma and beta must share one dtype")
+        bp = beta.data_ptr()
+    check(raw_layernorm(y.data_ptr(), x.data_ptr(), gamma.data_ptr(), bp, M, H, float(eps), dt,
+                        _stream_of(x, stream)), "rr_layernorm")
+
+
 def rr_softmax_rows(y, x, workspace=None, stream=None) -> None:
     """Row softmax of x into y over the last dimension (y may be x when dtypes match).
 
@@ -256,6 +282,12 @@ def rr_selftest_wave_allreduce(out, inp, kind: int, stream=None) -> None:
 def rmsnorm(x, gamma, eps: float, out=None):
     y = _torch().empty_like(x) if out is None else out
     rr_rmsnorm(y, x, gamma, eps)
+    return y
+
+
+def layernorm(x, gamma, beta, eps: float, out=None):
+    y = _torch().empty_like(x) if out is None else out
+    rr_layernorm(y, x, gamma, beta, eps)
     return y
 
 

@@ -164,12 +164,13 @@ void plan_loop(rr_plan* p, int vec, int64_t nvec) {
 rr_status make_plan(rr_op op, int64_t M, int64_t N, int din, int dout, bool is_aligned,
                     rr_plan* p) {
   memset(p, 0, sizeof(*p));
-  if (op != RR_OP_RMSNORM && op != RR_OP_FUSED_ADD_RMSNORM && op != RR_OP_SOFTMAX)
+  if (op != RR_OP_RMSNORM && op != RR_OP_FUSED_ADD_RMSNORM && op != RR_OP_SOFTMAX &&
+      op != RR_OP_LAYERNORM)
     return fail(RR_ERR_INVALID_ARG, "unknown op %d", (int)op);
   if (!valid_dtype(din) || !valid_dtype(dout))
     return fail(RR_ERR_INVALID_ARG, "unknown dtype (%d, %d)", din, dout);
   if (op != RR_OP_SOFTMAX && din != dout)
-    return fail(RR_ERR_INVALID_ARG, "RMSNorm input and output dtypes must match");
+    return fail(RR_ERR_INVALID_ARG, "norm input and output dtypes must match");
   if (M < 0) return fail(RR_ERR_INVALID_ARG, "M = %lld < 0", (long long)M);
   if (N < 1) return fail(RR_ERR_INVALID_ARG, "row width %lld < 1 (empty rows have no statistic)", (long long)N);
   if (N > kMaxN) return fail(RR_ERR_UNSUPPORTED, "row width %lld > 2^30", (long long)N);
@@ -280,10 +281,14 @@ rr_status hip_status(hipError_t e, const char* what) {
 
 bool valid_eps(float eps) { return eps >= 0.0f && eps <= 3.0e38f; }
 
-rr_status norm_entry(bool fused, void* y, void* residual, const void* x, const void* gamma,
-                     int64_t M, int64_t H, float eps, rr_dtype dtype, void* stream) {
+// kind: rr::kLaunchRms, kLaunchFused or kLaunchLayer.
+rr_status norm_entry(int kind, void* y, void* residual, const void* x, const void* gamma,
+                     const void* beta, int64_t M, int64_t H, float eps, rr_dtype dtype,
+                     void* stream) {
   g_err[0] = '\0';
-  const char* name = fused ? "rr_fused_add_rmsnorm" : "rr_rmsnorm";
+  const bool fused = kind == rr::kLaunchFused;
+  const bool layer = kind == rr::kLaunchLayer;
+  const char* name = fused ? "rr_fused_add_rmsnorm" : layer ? "rr_layernorm" : "rr_rmsnorm";
   if (!valid_dtype(dtype)) return fail(RR_ERR_INVALID_ARG, "%s: unknown dtype %d", name, (int)dtype);
   if (M < 0) return fail(RR_ERR_INVALID_ARG, "%s: M = %lld < 0", name, (long long)M);
   if (H < 1) return fail(RR_ERR_INVALID_ARG, "%s: H = %lld < 1", name, (long long)H);
@@ -300,17 +305,29 @@ rr_status norm_entry(bool fused, void* y, void* residual, const void* x, const v
   if (y != x && overlaps(y, bytes, x, bytes))
     return fail(RR_ERR_INVALID_ARG, "%s: y partly overlaps x", name);
   if (overlaps(gamma, gbytes, y, bytes)) return fail(RR_ERR_INVALID_ARG, "%s: gamma overlaps y", name);
+  if (layer && beta && overlaps(beta, gbytes, y, bytes))
+    return fail(RR_ERR_INVALID_ARG, "%s: beta overlaps y", name);
   if (fused) {
     if (overlaps(residual, bytes, x, bytes) || overlaps(residual, bytes, y, bytes) ||
         overlaps(residual, bytes, gamma, gbytes))
       return fail(RR_ERR_INVALID_ARG, "%s: residual overlaps x, y or gamma", name);
   }
-  const bool al = aligned16(y) && aligned16(x) && aligned16(gamma) && (!fused || aligned16(residual));
+  const bool al = aligned16(y) && aligned16(x) && aligned16(gamma) && (!fused || aligned16(residual)) &&
+                  (!layer || !beta || aligned16(beta));
+  const rr_op op = fused ? RR_OP_FUSED_ADD_RMSNORM : layer ? RR_OP_LAYERNORM : RR_OP_RMSNORM;
   rr_plan p;
-  const rr_status st = make_plan(fused ? RR_OP_FUSED_ADD_RMSNORM : RR_OP_RMSNORM, M, H, dtype, dtype, al, &p);
+  const rr_status st = make_plan(op, M, H, dtype, dtype, al, &p);
   if (st != RR_OK) return st;
-  const hipError_t e = rr::launch_norm(p, dtype, fused, y, residual, x, gamma, M, (int32_t)H, eps,
-                                       grid_for(p), static_cast<hipStream_t>(stream));
+  rr::NormArgs a;
+  a.y = y;
+  a.residual = residual;
+  a.x = x;
+  a.gamma = gamma;
+  a.beta = layer ? beta : nullptr;
+  a.M = M;
+  a.N = (int32_t)H;
+  a.eps = eps;
+  const hipError_t e = rr::launch_norm(p, dtype, kind, a, grid_for(p), static_cast<hipStream_t>(stream));
   return hip_status(e, name);
 }
 
@@ -320,12 +337,17 @@ extern "C" {
 
 rr_status rr_rmsnorm(void* y, const void* x, const void* gamma, int64_t M, int64_t H, float eps,
                      rr_dtype dtype, void* stream) {
-  return norm_entry(false, y, nullptr, x, gamma, M, H, eps, dtype, stream);
+  return norm_entry(rr::kLaunchRms, y, nullptr, x, gamma, nullptr, M, H, eps, dtype, stream);
 }
 
 rr_status rr_fused_add_rmsnorm(void* y, void* residual, const void* x, const void* gamma,
                                int64_t M, int64_t H, float eps, rr_dtype dtype, void* stream) {
-  return norm_entry(true, y, residual, x, gamma, M, H, eps, dtype, stream);
+  return norm_entry(rr::kLaunchFused, y, residual, x, gamma, nullptr, M, H, eps, dtype, stream);
+}
+
+rr_status rr_layernorm(void* y, const void* x, const void* gamma, const void* beta, int64_t M,
+                       int64_t H, float eps, rr_dtype dtype, void* stream) {
+  return norm_entry(rr::kLaunchLayer, y, nullptr, x, gamma, beta, M, H, eps, dtype, stream);
 }
 
 size_t rr_softmax_rows_workspace_bytes(int64_t M, int64_t N, rr_dtype in_dtype,

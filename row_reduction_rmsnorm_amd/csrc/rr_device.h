@@ -120,13 +120,23 @@ __device__ __forceinline__ void load_vec(const T* __restrict__ p, float (&v)[VEC
   }
 }
 
+// One element at p, widened to fp32 (a plain cached load: used where every
+// lane of a row reads the same element).
+template <typename T>
+__device__ __forceinline__ float load_one(const T* p) {
+  if constexpr (std::is_same_v<T, float>) return *p;
+  else return __uint_as_float(static_cast<uint32_t>(*p) << 16);
+}
+
 // A vector of VEC elements kept in registers in its storage format (bf16
 // stays packed two per dword: half the registers of widened fp32).  Used for
 // gamma, which a workgroup keeps across all the rows it visits, and for the
 // split-row chunks, which are widened element by element when used.
 template <typename T, int VEC>
 struct Packed {
-  static constexpr int kWords = VEC * (int)sizeof(T) / 4;
+  // whole dwords; a single bf16 element still takes one
+  static constexpr int kWords = (VEC * (int)sizeof(T) + 3) / 4;
+  static_assert(kWords >= 1, "at least one register");
   uint32_t w[kWords];
   template <bool NT = false>
   __device__ __forceinline__ void load(const T* __restrict__ p) {

@@ -36,6 +36,13 @@
 
 namespace rr {
 
+// The norm kernels' three operations.
+constexpr int kNormRms = 0;     // RMSNorm
+constexpr int kNormFused = 1;   // residual add, then RMSNorm of the stored sum
+constexpr int kNormLayer = 2;   // LayerNorm
+static_assert(kNormRms == kLaunchRms && kNormFused == kLaunchFused && kNormLayer == kLaunchLayer,
+              "operation codes");
+
 namespace {
 
 // LDS stage for one value per wavefront ([P2] section 四 and [P5] section
@@ -129,9 +136,10 @@ __device__ __forceinline__ RowLane row_lane() {
 // precision plus two bits, so rounding the fp32 sum to bf16 gives the
 // correctly rounded sum.
 // ===========================================================================
-template <typename T, int NV, bool FUSED, bool WAVE>
+template <typename T, int NV, int KIND, bool WAVE>
 __global__ __launch_bounds__(1024) void norm_regs_kernel(T* y, T* residual, const T* x,
-                                                         const T* __restrict__ gamma, int64_t M,
+                                                         const T* __restrict__ gamma,
+                                                         const T* __restrict__ beta, int64_t M,
                                                          int N, float eps) {
   constexpr int VEC = Elem<T>::kVec;
   __shared__ float slots[2][kMaxWavesPerGroup];
@@ -139,19 +147,33 @@ __global__ __launch_bounds__(1024) void norm_regs_kernel(T* y, T* residual, cons
   const int nvec = N / VEC;
 
   Packed<T, VEC> gv[NV];
+  Packed<T, VEC> bv[KIND == kNormLayer ? NV : 1];
 #pragma unroll
   for (int k = 0; k < NV; ++k) {
     const int vi = k * rl.T + rl.t;
     if (vi < nvec) gv[k].load(gamma + (int64_t)vi * VEC);
-    else gv[k].zero();
+    else gv[k].fill(0.0f);
+    if constexpr (KIND == kNormLayer) {
+      if (vi < nvec && beta) bv[k].load(beta + (int64_t)vi * VEC);
+      else bv[k].fill(0.0f);
+    }
   }
 
   const int64_t stride = (int64_t)gridDim.x * rl.rpg;
   int parity = 0;
+  // a reduction over the row: wave butterfly, then (BLOCK) the LDS stage
+  auto row_sum = [&](float v) {
+    v = wave_sum(v);
+    if constexpr (!WAVE) {
+      v = group_sum(v, rl.nw, rl.w, rl.lane, slots, parity);
+      parity ^= 1;
+    }
+    return v;
+  };
   for (int64_t row = (int64_t)blockIdx.x * rl.rpg + rl.g; row < M; row += stride) {
     const int64_t off = row * (int64_t)N;
     float h[NV][VEC];
-    if constexpr (FUSED) {
+    if constexpr (KIND == kNormFused) {
       float r[NV][VEC];
 #pragma unroll
       for (int k = 0; k < NV; ++k) {
@@ -184,26 +206,59 @@ __global__ __launch_bounds__(1024) void norm_regs_kernel(T* y, T* residual, cons
       }
     }
 
-    float ss = 0.0f;
+    if constexpr (KIND == kNormLayer) {
+      // [P4] section "练习" (LayerNorm): the mean first, then the variance from
+      // the values held in registers.  Everything is taken about the row's
+      // first element K: c = sum(x - K) / N is the mean's offset from K and
+      // x - mean = (x - K) - c, so neither the sum nor the centred values carry
+      // a rounding error relative to the mean itself, only to the row's spread
+      // ([P2] section 八.2 warns about rows whose mean is far larger than their
+      // spread).  The mean K + c is never formed.
+      const float K = load_one<T>(x + off);
+      float s1 = 0.0f;
 #pragma unroll
-    for (int k = 0; k < NV; ++k)
+      for (int k = 0; k < NV; ++k) {
+        const bool valid = k * rl.T + rl.t < nvec;
 #pragma unroll
-      for (int i = 0; i < VEC; ++i) ss += h[k][i] * h[k][i];
-    ss = wave_sum(ss);
-    if constexpr (!WAVE) {
-      ss = group_sum(ss, rl.nw, rl.w, rl.lane, slots, parity);
-      parity ^= 1;
-    }
-    // eps inside the root, mean over N ([P5] section "RMSNorm 归约什么").
-    const float rstd = 1.0f / __builtin_sqrtf(ss / (float)N + eps);
-
+        for (int i = 0; i < VEC; ++i) s1 += valid ? h[k][i] - K : 0.0f;
+      }
+      const float c = row_sum(s1) / (float)N;
+      float s2 = 0.0f;
 #pragma unroll
-    for (int k = 0; k < NV; ++k) {
-      const int vi = k * rl.T + rl.t;
-      float o[VEC];
+      for (int k = 0; k < NV; ++k) {
+        const bool valid = k * rl.T + rl.t < nvec;
 #pragma unroll
-      for (int i = 0; i < VEC; ++i) o[i] = (h[k][i] * rstd) * gv[k].get(i);
-      if (vi < nvec) store_vec<T, VEC>(y + off + (int64_t)vi * VEC, o);
+        for (int i = 0; i < VEC; ++i) {
+          h[k][i] = (h[k][i] - K) - c;
+          const float d = valid ? h[k][i] : 0.0f;
+          s2 += d * d;
+        }
+      }
+      const float rstd = 1.0f / __builtin_sqrtf(row_sum(s2) / (float)N + eps);
+#pragma unroll
+      for (int k = 0; k < NV; ++k) {
+        const int vi = k * rl.T + rl.t;
+        float o[VEC];
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) o[i] = (h[k][i] * rstd) * gv[k].get(i) + bv[k].get(i);
+        if (vi < nvec) store_vec<T, VEC>(y + off + (int64_t)vi * VEC, o);
+      }
+    } else {
+      float ss = 0.0f;
+#pragma unroll
+      for (int k = 0; k < NV; ++k)
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) ss += h[k][i] * h[k][i];
+      // eps inside the root, mean over N ([P5] section "RMSNorm 归约什么").
+      const float rstd = 1.0f / __builtin_sqrtf(row_sum(ss) / (float)N + eps);
+#pragma unroll
+      for (int k = 0; k < NV; ++k) {
+        const int vi = k * rl.T + rl.t;
+        float o[VEC];
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) o[i] = (h[k][i] * rstd) * gv[k].get(i);
+        if (vi < nvec) store_vec<T, VEC>(y + off + (int64_t)vi * VEC, o);
+      }
     }
   }
 }
@@ -214,42 +269,86 @@ __global__ __launch_bounds__(1024) void norm_regs_kernel(T* y, T* residual, cons
 // sums squares; pass 2 reads it again -- x, or the stored residual -- and
 // writes y.  Each lane revisits exactly the elements it handled in pass 1.
 // ===========================================================================
-template <typename T, int VEC, bool FUSED>
+template <typename T, int VEC, int KIND>
 __global__ __launch_bounds__(1024) void norm_loop_kernel(T* y, T* residual, const T* x,
-                                                         const T* __restrict__ gamma, int64_t M,
+                                                         const T* __restrict__ gamma,
+                                                         const T* __restrict__ beta, int64_t M,
                                                          int N, float eps) {
   __shared__ float slots[2][kMaxWavesPerGroup];
   const RowLane rl = row_lane<false>();
   const int nvec = N / VEC;
   int parity = 0;
+  auto row_sum = [&](float v) {
+    v = wave_sum(v);
+    v = group_sum(v, rl.nw, rl.w, rl.lane, slots, parity);
+    parity ^= 1;
+    return v;
+  };
   for (int64_t row = blockIdx.x; row < M; row += gridDim.x) {
     const int64_t off = row * (int64_t)N;
-    float ss = 0.0f;
-    for (int vi = rl.t; vi < nvec; vi += rl.T) {
-      float h[VEC];
-      load_vec<T, VEC>(x + off + (int64_t)vi * VEC, h);
-      if constexpr (FUSED) {
-        float r[VEC];
-        load_vec<T, VEC>(residual + off + (int64_t)vi * VEC, r);
+    if constexpr (KIND == kNormLayer) {
+      // three passes over the row: the mean's offset from the first element,
+      // the variance about the mean, then the output (centred as
+      // (x - K) - c, as in the register kernel)
+      const float K = load_one<T>(x + off);
+      float s1 = 0.0f;
+      for (int vi = rl.t; vi < nvec; vi += rl.T) {
+        float h[VEC];
+        load_vec<T, VEC, false>(x + off + (int64_t)vi * VEC, h);
 #pragma unroll
-        for (int i = 0; i < VEC; ++i) h[i] = round_to<T>(h[i] + r[i]);
-        store_vec<T, VEC>(residual + off + (int64_t)vi * VEC, h);
+        for (int i = 0; i < VEC; ++i) s1 += h[i] - K;
       }
+      const float c = row_sum(s1) / (float)N;
+      float s2 = 0.0f;
+      for (int vi = rl.t; vi < nvec; vi += rl.T) {
+        float h[VEC];
+        load_vec<T, VEC, false>(x + off + (int64_t)vi * VEC, h);
 #pragma unroll
-      for (int i = 0; i < VEC; ++i) ss += h[i] * h[i];
-    }
-    ss = wave_sum(ss);
-    ss = group_sum(ss, rl.nw, rl.w, rl.lane, slots, parity);
-    parity ^= 1;
-    const float rstd = 1.0f / __builtin_sqrtf(ss / (float)N + eps);
-    const T* src = FUSED ? residual : x;
-    for (int vi = rl.t; vi < nvec; vi += rl.T) {
-      float h[VEC], g[VEC];
-      load_vec<T, VEC>(src + off + (int64_t)vi * VEC, h);
-      load_vec<T, VEC>(gamma + (int64_t)vi * VEC, g);
+        for (int i = 0; i < VEC; ++i) {
+          const float d = (h[i] - K) - c;
+          s2 += d * d;
+        }
+      }
+      const float rstd = 1.0f / __builtin_sqrtf(row_sum(s2) / (float)N + eps);
+      for (int vi = rl.t; vi < nvec; vi += rl.T) {
+        float h[VEC], g[VEC], bb[VEC];
+        load_vec<T, VEC>(x + off + (int64_t)vi * VEC, h);
+        load_vec<T, VEC, false>(gamma + (int64_t)vi * VEC, g);
+        if (beta) {
+          load_vec<T, VEC, false>(beta + (int64_t)vi * VEC, bb);
+        } else {
 #pragma unroll
-      for (int i = 0; i < VEC; ++i) h[i] = (h[i] * rstd) * g[i];
-      store_vec<T, VEC>(y + off + (int64_t)vi * VEC, h);
+          for (int i = 0; i < VEC; ++i) bb[i] = 0.0f;
+        }
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) h[i] = (((h[i] - K) - c) * rstd) * g[i] + bb[i];
+        store_vec<T, VEC>(y + off + (int64_t)vi * VEC, h);
+      }
+    } else {
+      float ss = 0.0f;
+      for (int vi = rl.t; vi < nvec; vi += rl.T) {
+        float h[VEC];
+        load_vec<T, VEC>(x + off + (int64_t)vi * VEC, h);
+        if constexpr (KIND == kNormFused) {
+          float r[VEC];
+          load_vec<T, VEC>(residual + off + (int64_t)vi * VEC, r);
+#pragma unroll
+          for (int i = 0; i < VEC; ++i) h[i] = round_to<T>(h[i] + r[i]);
+          store_vec<T, VEC>(residual + off + (int64_t)vi * VEC, h);
+        }
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) ss += h[i] * h[i];
+      }
+      const float rstd = 1.0f / __builtin_sqrtf(row_sum(ss) / (float)N + eps);
+      const T* src = KIND == kNormFused ? residual : x;
+      for (int vi = rl.t; vi < nvec; vi += rl.T) {
+        float h[VEC], g[VEC];
+        load_vec<T, VEC>(src + off + (int64_t)vi * VEC, h);
+        load_vec<T, VEC, false>(gamma + (int64_t)vi * VEC, g);
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) h[i] = (h[i] * rstd) * g[i];
+        store_vec<T, VEC>(y + off + (int64_t)vi * VEC, h);
+      }
     }
   }
 }
@@ -263,24 +362,27 @@ __global__ __launch_bounds__(1024) void norm_loop_kernel(T* y, T* residual, cons
 // VEC = 1, so unaligned short rows take this path too).  The reductions run
 // only the butterfly steps inside an L-lane group, so no LDS and no barrier.
 // ===========================================================================
-template <typename T, int VEC, int L, bool FUSED>
+template <typename T, int VEC, int L, int KIND>
 __global__ __launch_bounds__(256) void norm_sub_kernel(T* y, T* residual, const T* x,
-                                                       const T* __restrict__ gamma, int64_t M,
+                                                       const T* __restrict__ gamma,
+                                                       const T* __restrict__ beta, int64_t M,
                                                        int N, float eps) {
   constexpr int kRowsPerGroup = 256 / L;
   const int j = threadIdx.x & (L - 1);              // lane within the row
   const int nvec = N / VEC;
   const bool active = j < nvec;
-  Packed<T, VEC> g;
+  Packed<T, VEC> g, bb;
   if (active) g.load(gamma + (int64_t)j * VEC);
   else g.fill(0.0f);
+  if (active && KIND == kNormLayer && beta) bb.load(beta + (int64_t)j * VEC);
+  else bb.fill(0.0f);
   for (int64_t row = (int64_t)blockIdx.x * kRowsPerGroup + (threadIdx.x / L); row < M;
        row += (int64_t)gridDim.x * kRowsPerGroup) {
     const int64_t off = row * (int64_t)N + (int64_t)j * VEC;
     float h[VEC];
     if (active) {
       load_vec<T, VEC>(x + off, h);
-      if constexpr (FUSED) {
+      if constexpr (KIND == kNormFused) {
         float r[VEC];
         load_vec<T, VEC>(residual + off, r);
 #pragma unroll
@@ -291,17 +393,33 @@ __global__ __launch_bounds__(256) void norm_sub_kernel(T* y, T* residual, const 
 #pragma unroll
       for (int i = 0; i < VEC; ++i) h[i] = 0.0f;
     }
-    float ss = 0.0f;
+    float o[VEC];
+    if constexpr (KIND == kNormLayer) {
+      const float K = load_one<T>(x + row * (int64_t)N);
+      float s1 = 0.0f;
 #pragma unroll
-    for (int i = 0; i < VEC; ++i) ss += h[i] * h[i];
-    ss = group_lanes_sum<L>(ss);
-    const float rstd = 1.0f / __builtin_sqrtf(ss / (float)N + eps);
-    if (active) {
-      float o[VEC];
+      for (int i = 0; i < VEC; ++i) s1 += active ? h[i] - K : 0.0f;
+      const float c = group_lanes_sum<L>(s1) / (float)N;
+      float s2 = 0.0f;
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) {
+        h[i] = (h[i] - K) - c;
+        const float d = active ? h[i] : 0.0f;
+        s2 += d * d;
+      }
+      const float rstd = 1.0f / __builtin_sqrtf(group_lanes_sum<L>(s2) / (float)N + eps);
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) o[i] = (h[i] * rstd) * g.get(i) + bb.get(i);
+    } else {
+      float ss = 0.0f;
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) ss += h[i] * h[i];
+      ss = group_lanes_sum<L>(ss);
+      const float rstd = 1.0f / __builtin_sqrtf(ss / (float)N + eps);
 #pragma unroll
       for (int i = 0; i < VEC; ++i) o[i] = (h[i] * rstd) * g.get(i);
-      store_vec<T, VEC>(y + off, o);
     }
+    if (active) store_vec<T, VEC>(y + off, o);
   }
 }
 
@@ -776,22 +894,22 @@ namespace {
 
 inline dim3 grid1(int64_t g) { return dim3((unsigned)g, 1, 1); }
 
-template <typename T, bool FUSED, bool WAVE>
-hipError_t norm_regs(const rr_plan& p, void* y, void* res, const void* x, const void* gamma,
-                     int64_t M, int N, float eps, int64_t grid, hipStream_t s) {
-  T* yy = static_cast<T*>(y);
-  T* rr_ = static_cast<T*>(res);
-  const T* xx = static_cast<const T*>(x);
-  const T* gg = static_cast<const T*>(gamma);
+template <typename T, int KIND, bool WAVE>
+hipError_t norm_regs(const rr_plan& p, const NormArgs& a, int64_t grid, hipStream_t s) {
+  T* yy = static_cast<T*>(a.y);
+  T* rr_ = static_cast<T*>(a.residual);
+  const T* xx = static_cast<const T*>(a.x);
+  const T* gg = static_cast<const T*>(a.gamma);
+  const T* bb = static_cast<const T*>(a.beta);
   const dim3 b(p.block_threads);
   // The host never plans more than 16 values per lane for the norms
   // (NV * VEC <= 16), so only those instantiations exist.
   switch (p.vecs_per_lane) {
-    case 1: norm_regs_kernel<T, 1, FUSED, WAVE><<<grid1(grid), b, 0, s>>>(yy, rr_, xx, gg, M, N, eps); break;
-    case 2: norm_regs_kernel<T, 2, FUSED, WAVE><<<grid1(grid), b, 0, s>>>(yy, rr_, xx, gg, M, N, eps); break;
+    case 1: norm_regs_kernel<T, 1, KIND, WAVE><<<grid1(grid), b, 0, s>>>(yy, rr_, xx, gg, bb, a.M, a.N, a.eps); break;
+    case 2: norm_regs_kernel<T, 2, KIND, WAVE><<<grid1(grid), b, 0, s>>>(yy, rr_, xx, gg, bb, a.M, a.N, a.eps); break;
     case 4:
       if constexpr (Elem<T>::kVec * 4 <= 16) {
-        norm_regs_kernel<T, 4, FUSED, WAVE><<<grid1(grid), b, 0, s>>>(yy, rr_, xx, gg, M, N, eps);
+        norm_regs_kernel<T, 4, KIND, WAVE><<<grid1(grid), b, 0, s>>>(yy, rr_, xx, gg, bb, a.M, a.N, a.eps);
         break;
       }
       return hipErrorInvalidValue;
@@ -800,51 +918,60 @@ hipError_t norm_regs(const rr_plan& p, void* y, void* res, const void* x, const 
   return hipGetLastError();
 }
 
-template <typename T, bool FUSED>
-hipError_t norm_loop(const rr_plan& p, void* y, void* res, const void* x, const void* gamma,
-                     int64_t M, int N, float eps, int64_t grid, hipStream_t s) {
-  T* yy = static_cast<T*>(y);
-  T* rr_ = static_cast<T*>(res);
-  const T* xx = static_cast<const T*>(x);
-  const T* gg = static_cast<const T*>(gamma);
+template <typename T, int KIND>
+hipError_t norm_loop(const rr_plan& p, const NormArgs& a, int64_t grid, hipStream_t s) {
+  T* yy = static_cast<T*>(a.y);
+  T* rr_ = static_cast<T*>(a.residual);
+  const T* xx = static_cast<const T*>(a.x);
+  const T* gg = static_cast<const T*>(a.gamma);
+  const T* bb = static_cast<const T*>(a.beta);
   const dim3 b(p.block_threads);
   if (p.vec_elems == 1)
-    norm_loop_kernel<T, 1, FUSED><<<grid1(grid), b, 0, s>>>(yy, rr_, xx, gg, M, N, eps);
+    norm_loop_kernel<T, 1, KIND><<<grid1(grid), b, 0, s>>>(yy, rr_, xx, gg, bb, a.M, a.N, a.eps);
   else
-    norm_loop_kernel<T, Elem<T>::kVec, FUSED><<<grid1(grid), b, 0, s>>>(yy, rr_, xx, gg, M, N, eps);
+    norm_loop_kernel<T, Elem<T>::kVec, KIND><<<grid1(grid), b, 0, s>>>(yy, rr_, xx, gg, bb, a.M, a.N, a.eps);
   return hipGetLastError();
 }
 
-template <typename T, int VEC, bool FUSED>
-hipError_t norm_sub(const rr_plan& p, void* y, void* res, const void* x, const void* gamma,
-                    int64_t M, int N, float eps, int64_t grid, hipStream_t s) {
-  T* yy = static_cast<T*>(y);
-  T* rr_ = static_cast<T*>(res);
-  const T* xx = static_cast<const T*>(x);
-  const T* gg = static_cast<const T*>(gamma);
+template <typename T, int VEC, int KIND>
+hipError_t norm_sub(const rr_plan& p, const NormArgs& a, int64_t grid, hipStream_t s) {
+  T* yy = static_cast<T*>(a.y);
+  T* rr_ = static_cast<T*>(a.residual);
+  const T* xx = static_cast<const T*>(a.x);
+  const T* gg = static_cast<const T*>(a.gamma);
+  const T* bb = static_cast<const T*>(a.beta);
   const dim3 b(256);
   switch (p.waves_per_row) {  // for SUBWAVE: lanes per row
-    case 1: norm_sub_kernel<T, VEC, 1, FUSED><<<grid1(grid), b, 0, s>>>(yy, rr_, xx, gg, M, N, eps); break;
-    case 2: norm_sub_kernel<T, VEC, 2, FUSED><<<grid1(grid), b, 0, s>>>(yy, rr_, xx, gg, M, N, eps); break;
-    case 4: norm_sub_kernel<T, VEC, 4, FUSED><<<grid1(grid), b, 0, s>>>(yy, rr_, xx, gg, M, N, eps); break;
-    case 8: norm_sub_kernel<T, VEC, 8, FUSED><<<grid1(grid), b, 0, s>>>(yy, rr_, xx, gg, M, N, eps); break;
-    case 16: norm_sub_kernel<T, VEC, 16, FUSED><<<grid1(grid), b, 0, s>>>(yy, rr_, xx, gg, M, N, eps); break;
-    case 32: norm_sub_kernel<T, VEC, 32, FUSED><<<grid1(grid), b, 0, s>>>(yy, rr_, xx, gg, M, N, eps); break;
+    case 1: norm_sub_kernel<T, VEC, 1, KIND><<<grid1(grid), b, 0, s>>>(yy, rr_, xx, gg, bb, a.M, a.N, a.eps); break;
+    case 2: norm_sub_kernel<T, VEC, 2, KIND><<<grid1(grid), b, 0, s>>>(yy, rr_, xx, gg, bb, a.M, a.N, a.eps); break;
+    case 4: norm_sub_kernel<T, VEC, 4, KIND><<<grid1(grid), b, 0, s>>>(yy, rr_, xx, gg, bb, a.M, a.N, a.eps); break;
+    case 8: norm_sub_kernel<T, VEC, 8, KIND><<<grid1(grid), b, 0, s>>>(yy, rr_, xx, gg, bb, a.M, a.N, a.eps); break;
+    case 16: norm_sub_kernel<T, VEC, 16, KIND><<<grid1(grid), b, 0, s>>>(yy, rr_, xx, gg, bb, a.M, a.N, a.eps); break;
+    case 32: norm_sub_kernel<T, VEC, 32, KIND><<<grid1(grid), b, 0, s>>>(yy, rr_, xx, gg, bb, a.M, a.N, a.eps); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
-template <typename T, bool FUSED>
-hipError_t norm_any(const rr_plan& p, void* y, void* res, const void* x, const void* gamma,
-                    int64_t M, int N, float eps, int64_t grid, hipStream_t s) {
-  if (p.variant == RR_VARIANT_LOOP) return norm_loop<T, FUSED>(p, y, res, x, gamma, M, N, eps, grid, s);
+template <typename T, int KIND>
+hipError_t norm_any(const rr_plan& p, const NormArgs& a, int64_t grid, hipStream_t s) {
+  if (p.variant == RR_VARIANT_LOOP) return norm_loop<T, KIND>(p, a, grid, s);
   if (p.variant == RR_VARIANT_SUBWAVE) {
-    if (p.vec_elems == 1) return norm_sub<T, 1, FUSED>(p, y, res, x, gamma, M, N, eps, grid, s);
-    return norm_sub<T, Elem<T>::kVec, FUSED>(p, y, res, x, gamma, M, N, eps, grid, s);
+    if (p.vec_elems == 1) return norm_sub<T, 1, KIND>(p, a, grid, s);
+    return norm_sub<T, Elem<T>::kVec, KIND>(p, a, grid, s);
   }
-  if (p.variant == RR_VARIANT_WAVE) return norm_regs<T, FUSED, true>(p, y, res, x, gamma, M, N, eps, grid, s);
-  return norm_regs<T, FUSED, false>(p, y, res, x, gamma, M, N, eps, grid, s);
+  if (p.variant == RR_VARIANT_WAVE) return norm_regs<T, KIND, true>(p, a, grid, s);
+  return norm_regs<T, KIND, false>(p, a, grid, s);
+}
+
+template <typename T>
+hipError_t norm_typed(const rr_plan& p, int kind, const NormArgs& a, int64_t grid, hipStream_t s) {
+  switch (kind) {
+    case kNormRms: return norm_any<T, kNormRms>(p, a, grid, s);
+    case kNormFused: return norm_any<T, kNormFused>(p, a, grid, s);
+    case kNormLayer: return norm_any<T, kNormLayer>(p, a, grid, s);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 template <typename Tin, typename Tout, bool WAVE>
@@ -980,15 +1107,10 @@ hipError_t softmax_typed(const rr_plan& p, void* y, const void* x, void* ws, int
 
 }  // namespace
 
-hipError_t launch_norm(const rr_plan& plan, rr_dtype dtype, bool fused, void* y, void* residual,
-                       const void* x, const void* gamma, int64_t M, int32_t N, float eps,
+hipError_t launch_norm(const rr_plan& plan, rr_dtype dtype, int kind, const NormArgs& args,
                        int64_t grid, hipStream_t stream) {
-  if (dtype == RR_F32) {
-    return fused ? norm_any<float, true>(plan, y, residual, x, gamma, M, N, eps, grid, stream)
-                 : norm_any<float, false>(plan, y, residual, x, gamma, M, N, eps, grid, stream);
-  }
-  return fused ? norm_any<bf16_t, true>(plan, y, residual, x, gamma, M, N, eps, grid, stream)
-               : norm_any<bf16_t, false>(plan, y, residual, x, gamma, M, N, eps, grid, stream);
+  if (dtype == RR_F32) return norm_typed<float>(plan, kind, args, grid, stream);
+  return norm_typed<bf16_t>(plan, kind, args, grid, stream);
 }
 
 hipError_t launch_softmax(const rr_plan& plan, rr_dtype in_dtype, rr_dtype out_dtype, void* y,

@@ -13,10 +13,27 @@ namespace rr {
 // the width of the DPP row that combines the per-wavefront LDS slots.
 constexpr int kMaxWavesPerGroup = 16;
 
-// Enqueue the RMSNorm (fused == false) or fused add + RMSNorm kernel that
-// `plan` names, with `grid` workgroups, on `stream`.
-hipError_t launch_norm(const rr_plan& plan, rr_dtype dtype, bool fused, void* y, void* residual,
-                       const void* x, const void* gamma, int64_t M, int32_t N, float eps,
+// Arguments of the norm kernels (residual only for the fused op, beta only
+// for LayerNorm and possibly null).
+struct NormArgs {
+  void* y;
+  void* residual;
+  const void* x;
+  const void* gamma;
+  const void* beta;
+  int64_t M;
+  int32_t N;
+  float eps;
+};
+
+// Operation codes for launch_norm.
+constexpr int kLaunchRms = 0;
+constexpr int kLaunchFused = 1;
+constexpr int kLaunchLayer = 2;
+
+// Enqueue the norm kernel (kind: kLaunchRms, kLaunchFused or kLaunchLayer)
+// that `plan` names, with `grid` workgroups, on `stream`.
+hipError_t launch_norm(const rr_plan& plan, rr_dtype dtype, int kind, const NormArgs& args,
                        int64_t grid, hipStream_t stream);
 
 // Enqueue the softmax kernel(s) that `plan` names (two for SPLIT).

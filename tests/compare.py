@@ -9,6 +9,12 @@ Bars (stated once here, used by every parity test):
     nearest even), measured as a distance between order-preserving integer
     images of the bit patterns, with +0 and -0 equal.
   * bf16 residual_out of the fused op: bit-exact (the rounded sum is unique).
+  * LayerNorm (f3): the output is (x - mean) * rstd * gamma + beta, so a
+    kernel's error scales with the row's spread, i.e. with |gamma_j| (1 + |z|)
+    where z is the normalised value, not with |y| itself (y is near beta for
+    x near the mean).  fp32: |g - r| <= 1e-5 (|r| + |gamma_j| + |beta_j|);
+    bf16: at most 1 ulp from RNE_bf16(r), or |g - r| <= 1e-5 (|gamma_j| +
+    |beta_j|).
 """
 import numpy as np
 
@@ -110,3 +116,25 @@ def check_softmax(got_tensor, x_f64: np.ndarray, ref_f64: np.ndarray, what: str)
         info["max_rowsum_err"] = float(rs.max())
     info["rows"] = M
     return info
+
+
+LN_TOL = 1e-5
+
+
+def check_layernorm(got_tensor, ref_f64: np.ndarray, gamma_f64: np.ndarray, beta_f64, what: str):
+    import torch
+    g = to_f64(got_tensor).reshape(ref_f64.shape)
+    scale = np.abs(gamma_f64)[None, :] + (np.abs(beta_f64)[None, :] if beta_f64 is not None else 0.0)
+    assert np.all(np.isfinite(g)), f"{what}: non-finite output"
+    if got_tensor.dtype == torch.bfloat16:
+        ref_bits = bf16_bits_of_values(oracle.round_bf16(ref_f64))
+        got_bits = bf16_bits_of_tensor(got_tensor).reshape(ref_bits.shape)
+        dist = bf16_ulp_distance(got_bits, ref_bits)
+        floor_ok = np.abs(g - ref_f64) <= LN_TOL * scale
+        bad = (dist > BF16_MAX_ULP) & ~floor_ok
+        assert not bad.any(), f"{what}: {int(bad.sum())} outputs beyond 1 ulp and the floor"
+        return {"max_ulp": int(dist.max()), "n_floor": int(((dist > 1) & floor_ok).sum())}
+    err = np.abs(g - ref_f64) / (np.abs(ref_f64) + scale)
+    worst = float(err.max())
+    assert worst <= LN_TOL, f"{what}: scaled error {worst:.3e} > {LN_TOL}"
+    return {"max_scaled_err": worst}

@@ -87,6 +87,20 @@ def test_fused_validation():
     assert call({**ok, "gamma": R + 4}) == rr.RR_ERR_INVALID_ARG         # gamma inside residual
 
 
+def test_layernorm_validation_and_plan():
+    Y, X, G, Bt = P, P << 4, P << 8, P << 9
+    f = rr.raw_layernorm
+    assert f(Y, X, G, None, 0, 8, 1e-5, rr.RR_F32, None) == rr.RR_OK          # M = 0
+    assert f(Y, X, G, Bt, 4, 0, 1e-5, rr.RR_F32, None) == rr.RR_ERR_INVALID_ARG
+    assert f(Y, X, None, Bt, 4, 8, 1e-5, rr.RR_F32, None) == rr.RR_ERR_INVALID_ARG
+    assert f(Y, X, G, Y + 4, 4, 8, 1e-5, rr.RR_F32, None) == rr.RR_ERR_INVALID_ARG  # beta in y
+    p = rr.rr_query_plan(rr.RR_OP_LAYERNORM, 256, 5120, rr.RR_F32, rr.RR_F32)
+    assert (p["variant_name"], p["waves_per_row"], p["vecs_per_lane"]) == ("block", 10, 2)
+    assert rr.rr_query_plan(rr.RR_OP_LAYERNORM, 8, 64, rr.RR_F32, rr.RR_F32)["variant_name"] == "subwave"
+    with pytest.raises(rr.RowReduceError):
+        rr.rr_query_plan(rr.RR_OP_LAYERNORM, 8, 64, rr.RR_BF16, rr.RR_F32)
+
+
 def test_softmax_validation():
     X, Y, W = P, P << 4, P << 8
     f = rr.raw_softmax_rows

@@ -289,6 +289,92 @@ def test_norm_forced_variants(variant):
 
 
 # ----------------------------------------------------------------------------
+# LayerNorm (f3)
+# ----------------------------------------------------------------------------
+
+def run_layernorm(x_cpu, g_cpu, b_cpu, eps, inplace=False):
+    rr = _rr()
+    x = x_cpu.cuda()
+    y = x if inplace else torch.empty_like(x)
+    rr.rr_layernorm(y, x, g_cpu.cuda(), None if b_cpu is None else b_cpu.cuda(), eps)
+    torch.cuda.synchronize()
+    return y.cpu()
+
+
+def check_ln(x_cpu, g_cpu, b_cpu, eps, y_cpu, what):
+    gf = compare.to_f64(g_cpu)
+    bf = None if b_cpu is None else compare.to_f64(b_cpu)
+    ref = oracle.layernorm(compare.to_f64(x_cpu), gf, bf, eps)
+    return compare.check_layernorm(y_cpu, ref, gf, bf, what)
+
+
+def ln_input(M, N, seed, dt, offset=0.0, spread=1.0):
+    rng = np.random.default_rng(seed)
+    x = (offset + spread * rng.standard_normal((M, N))).astype(np.float32)
+    g = rng.uniform(0.5, 1.5, N).astype(np.float32)
+    b = rng.uniform(-1.0, 1.0, N).astype(np.float32)
+    return _as(x, dt), _as(g, dt), _as(b, dt)
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("N", [1, 2, 7, 64, 65, 1000, 1024, 1028, 3584, 5120, 8191, 16384, 16392, 40000])
+def test_layernorm_grid(dt, N):
+    for M in (1, 7, 64):
+        for (offset, spread) in ((0.0, 1.0), (101.0, 0.6)):
+            _say(f"layernorm {dt} M={M} N={N} offset={offset}")
+            x, g, b = ln_input(M, N, seed=N + M, dt=dt, offset=offset, spread=spread)
+            check_ln(x, g, b, 1e-5, run_layernorm(x, g, b, 1e-5), f"ln {dt} {M}x{N} +{offset}")
+        x, g, _ = ln_input(M, N, seed=N + M + 1, dt=dt)
+        check_ln(x, g, None, 1e-5, run_layernorm(x, g, None, 1e-5), f"ln no beta {dt} {M}x{N}")
+
+
+@pytest.mark.parametrize("variant", ["wave", "block", "loop", "subwave"])
+def test_layernorm_forced_variants(variant):
+    rr = _rr()
+    code = {"wave": rr.RR_VARIANT_WAVE, "block": rr.RR_VARIANT_BLOCK, "loop": rr.RR_VARIANT_LOOP,
+            "subwave": rr.RR_VARIANT_SUBWAVE}[variant]
+    shapes = {"wave": [8, 64, 520, 1024], "block": [8, 1024, 5120, 16384],
+              "loop": [8, 1024, 5120, 20000], "subwave": [8, 24, 64, 128]}[variant]
+    try:
+        rr.rr_set_variant_override(code)
+        for dt in ("f32", "bf16"):
+            for N in shapes:
+                for M in (1, 7, 130):
+                    x, g, b = ln_input(M, N, seed=3 * N + M, dt=dt, offset=50.0, spread=2.0)
+                    check_ln(x, g, b, 1e-5, run_layernorm(x, g, b, 1e-5), f"{variant} ln {dt} {M}x{N}")
+    finally:
+        rr.rr_set_variant_override(rr.RR_VARIANT_AUTO)
+
+
+def test_layernorm_edge_cases():
+    # constant rows give beta (x - mean = 0 exactly when the sum is about the first element)
+    x = np.full((5, 4096), 101.25, np.float32)
+    g = workloads.gamma_vector(4096, 1)
+    b = np.linspace(-1, 1, 4096).astype(np.float32)
+    y = run_layernorm(_as(x, "f32"), _as(g, "f32"), _as(b, "f32"), 1e-5)
+    assert np.array_equal(y.numpy(), np.broadcast_to(b, (5, 4096)))
+    # in place, and unaligned rows
+    xt, gt, bt = ln_input(9, 4096, seed=8, dt="f32", offset=3.0)
+    check_ln(xt, gt, bt, 1e-5, run_layernorm(xt, gt, bt, 1e-5, inplace=True), "ln in place")
+    rr = _rr()
+    base = torch.empty(9 * 4096 + 1, device="cuda")
+    xv = base[1:].view(9, 4096)
+    xv.copy_(xt.cuda())
+    yv = torch.empty(9 * 4096 + 1, device="cuda")[1:].view(9, 4096)
+    rr.rr_layernorm(yv, xv, gt.cuda(), bt.cuda(), 1e-5)
+    torch.cuda.synchronize()
+    check_ln(xt, gt, bt, 1e-5, yv.cpu(), "ln unaligned")
+
+
+def test_workload_layernorm_full():
+    """The LayerNorm exercise's shape: 256 x 5120, x ~ U(100, 102)."""
+    w = workloads.make("layernorm")
+    _say(w.description)
+    y = run_layernorm(w.arrays["x"], w.arrays["gamma"], w.arrays["beta"], w.eps)
+    _say(check_ln(w.arrays["x"], w.arrays["gamma"], w.arrays["beta"], w.eps, y, w.name))
+
+
+# ----------------------------------------------------------------------------
 # softmax over the shape grid
 # ----------------------------------------------------------------------------
 

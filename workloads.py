@@ -31,6 +31,8 @@ sm_vocab  softmax bf16 -> fp32, x~N(0,3), 16 distinct columns per     256 x 1520
 sm_causal softmax fp32 -> fp32 attention scores, x~N(0,1); row r is   114688 x 4096
           query i = r mod 4096 and keys j > i hold -inf (diagonal
           kept)
+layernorm LayerNorm fp32, x~U(100,102) (mean far above the spread),    256 x 5120
+          gamma~U(0.5,1.5), beta~U(-1,1), eps 1e-5
 ========  ==========================================================  =========
 """
 from dataclasses import dataclass, field
@@ -38,7 +40,7 @@ from typing import Optional
 
 import numpy as np
 
-NAMES = ("rms_f32", "fused", "sm_wave", "sm_vocab", "sm_causal")
+NAMES = ("rms_f32", "fused", "sm_wave", "sm_vocab", "sm_causal", "layernorm")
 
 
 @dataclass
@@ -64,6 +66,7 @@ SHAPES = {
     "sm_wave": ("softmax", 16384, 1024, "f32", "f32", 0.0),
     "sm_vocab": ("softmax", 256, 152064, "bf16", "f32", 0.0),
     "sm_causal": ("softmax", 28 * 4096, 4096, "f32", "f32", 0.0),
+    "layernorm": ("layernorm", 256, 5120, "f32", "f32", 1e-5),
 }
 
 
@@ -126,6 +129,11 @@ def make(name: str, rows: Optional[int] = None, seed: int = 0) -> Workload:
         x = rng.standard_normal((M, N), dtype=np.float32)
         causal_mask_inplace(x, 4096)
         w.arrays = {"x": to_dtype(x, idt)}
+    elif name == "layernorm":
+        x = rng.uniform(100.0, 102.0, (M_full, N)).astype(np.float32)[:M]
+        g = rng.uniform(0.5, 1.5, N).astype(np.float32)
+        b = rng.uniform(-1.0, 1.0, N).astype(np.float32)
+        w.arrays = {"x": to_dtype(x, idt), "gamma": to_dtype(g, idt), "beta": to_dtype(b, idt)}
     else:
         raise KeyError(name)
     return w
