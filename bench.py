@@ -170,6 +170,51 @@ def cpu_baseline(bufs, fraction):
     }
 
 
+def measure_extras(torch, rr, dev, K):
+    """Operations outside the step, each timed on its own (K launches between
+    two events, after a warm-up launch): the 64 x 3584 fp32 RMSNorm (64 rows on
+    256 CUs: a latency case, reported as time and rows/s), LayerNorm at the
+    LayerNorm exercise's 256 x 5120 fp32 shape, and LayerNorm bf16 8192 x 4096
+    (the RMSNorm workload's shape, for bandwidth).  Inputs stay cached between
+    launches here (the largest is 134 MB), so these are not HBM-cold figures."""
+    import numpy as np
+    import workloads
+    out = {}
+
+    def timed(name, fn, nbytes, M):
+        fn()
+        torch.cuda.synchronize()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(K):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        us = a.elapsed_time(b) / K * 1e3
+        out[name] = {"us": round(us, 2), "bytes": nbytes, "GBps": round(nbytes / (us * 1e-6) / 1e9, 1),
+                     "rows_per_s": round(M / (us * 1e-6), 1)}
+
+    w = workloads.make("rms_f32")
+    x, g = w.arrays["x"].to(dev), w.arrays["gamma"].to(dev)
+    y = torch.empty_like(x)
+    timed("rms_f32_64x3584", lambda: rr.rr_rmsnorm(y, x, g, w.eps), algorithmic_bytes("rms_f32", w.M, w.N), w.M)
+    w = workloads.make("layernorm")
+    x, g, bt = (w.arrays[k].to(dev) for k in ("x", "gamma", "beta"))
+    y = torch.empty_like(x)
+    timed("layernorm_f32_256x5120", lambda: rr.rr_layernorm(y, x, g, bt, w.eps),
+          2 * w.M * w.N * 4 + 2 * w.N * 4, w.M)
+    rng = np.random.default_rng(0)
+    M, N = 8192, 4096
+    x = workloads.to_dtype(rng.standard_normal((M, N), dtype=np.float32), "bf16").to(dev)
+    g = workloads.to_dtype(workloads.gamma_vector(N, 1), "bf16").to(dev)
+    bt = workloads.to_dtype(workloads.gamma_vector(N, 2) - 1.0, "bf16").to(dev)
+    y = torch.empty_like(x)
+    timed("layernorm_bf16_8192x4096", lambda: rr.rr_layernorm(y, x, g, bt, 1e-5),
+          2 * M * N * 2 + 2 * N * 2, M)
+    return out
+
+
 def traffic_for(per_launch_ok):
     """HBM bytes per launch of the dominant kernel from the committed
     rocprofv3 FETCH_SIZE / WRITE_SIZE summary, if it was taken on the kernel
@@ -280,6 +325,8 @@ def main():
                 "us_per_launch": round(per_op_ms[dom] * 1e3, 2),
                 "plan": plan["variant_name"] if plan else None}
 
+    extras = measure_extras(torch, rr, dev, K)
+
     cpu = None
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a sample ...")
@@ -310,6 +357,7 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "breakdown": breakdown,
+        "extras": extras,
         "device": torch.cuda.get_device_name(dev),
         "kernel_source_sha": kernel_source_sha(),
     }

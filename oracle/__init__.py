@@ -46,9 +46,10 @@ def _lib():
         lib.oracle_fused_add_rmsnorm.argtypes = [i64, i64, _dp, _dp, _dp, ctypes.c_double,
                                                  ctypes.c_int, _dp, _dp]
         lib.oracle_softmax.argtypes = [i64, i64, _dp, _dp]
+        lib.oracle_log_softmax.argtypes = [i64, i64, _dp, _dp]
         lib.oracle_softmax_stats.argtypes = [i64, i64, _dp, _dp, _dp]
         for f in ("oracle_rmsnorm", "oracle_fused_add_rmsnorm", "oracle_softmax",
-                  "oracle_softmax_stats", "oracle_layernorm"):
+                  "oracle_softmax_stats", "oracle_layernorm", "oracle_log_softmax"):
             getattr(lib, f).restype = ctypes.c_int
         _LIB = lib
     return _LIB
@@ -155,6 +156,17 @@ def softmax(x):
     M, N = x2.shape
     y = np.empty_like(x2)
     _check(_lib().oracle_softmax(M, N, _ptr(x2), _ptr(y)), "softmax")
+    return y.reshape(shape)
+
+
+def log_softmax(x):
+    """Row log-softmax in fp64 over the last axis."""
+    x = _f64(x)
+    shape = x.shape
+    x2 = x.reshape(-1, shape[-1])
+    M, N = x2.shape
+    y = np.empty_like(x2)
+    _check(_lib().oracle_log_softmax(M, N, _ptr(x2), _ptr(y)), "log_softmax")
     return y.reshape(shape)
 
 

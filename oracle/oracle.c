@@ -200,6 +200,31 @@ int oracle_softmax(int64_t M, int64_t N, const double* x, double* y) {
 }
 
 /*
+ * Log-softmax of one row: y_j = log(exp(x_j - m) / d) = (x_j - m) - log(d),
+ * with m and d of the safe softmax above (the log of the definition; PyTorch's
+ * log-softmax switch is the form the pages cite: [P2] section 九, the
+ * dispatch of SoftMax.cu).  Masked entries (-inf) give -inf; a fully masked
+ * row gives NaN.
+ */
+static void log_softmax_row(int64_t N, const double* x, double* y) {
+    double m = -INFINITY;
+    for (int64_t j = 0; j < N; ++j)
+        if (x[j] > m) m = x[j];
+    double d = 0.0;
+    for (int64_t j = 0; j < N; ++j) d += exp(x[j] - m);
+    double ld = log(d);
+    for (int64_t j = 0; j < N; ++j) y[j] = (x[j] - m) - ld;
+}
+
+/* Log-softmax over M rows of width N. Returns 0, or -1 when N < 1. */
+int oracle_log_softmax(int64_t M, int64_t N, const double* x, double* y) {
+    if (N < 1 || M < 0) return -1;
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < M; ++i) log_softmax_row(N, x + i * N, y + i * N);
+    return 0;
+}
+
+/*
  * Row statistics (m, d) of the safe softmax for each row, from the same
  * three-pass definition: m = max_j x_j, d = sum_j exp(x_j - m).
  * Tests use it to check the normaliser invariants (d >= 1 for a row with a

@@ -34,6 +34,8 @@ MUTANTS = {
     "ln_no_centering": ("y[j] = (x[j] - mu) * r * gamma[j]", "y[j] = x[j] * r * gamma[j]"),
     "ln_beta_dropped": ("+ (beta ? beta[j] : 0.0);", "+ 0.0;"),
     "ln_eps_outside": ("double r = 1.0 / sqrt(var + eps);", "double r = 1.0 / sqrt(var) + eps;"),
+    "logsm_sign": ("y[j] = (x[j] - m) - ld;", "y[j] = (x[j] - m) + ld;"),
+    "logsm_log2": ("double ld = log(d);", "double ld = log2(d);"),
 }
 
 

@@ -313,6 +313,29 @@ def test_softmax_no_overflow_at_large_logits():
     assert abs(y.sum() - 1.0) < 1e-15
 
 
+def test_log_softmax_pins():
+    torch = pytest.importorskip("torch")
+    # the pages' example (1000, 1001): y = (0.2689414, 0.7310586), so
+    # log y = (-1.3132617, -0.3132617) to the printed precision
+    y = oracle.log_softmax(np.array([[1000.0, 1001.0]]))[0]
+    assert np.allclose(np.exp(y), [0.2689414, 0.7310586], atol=5e-8)
+    assert abs((y[1] - y[0]) - 1.0) < 1e-15
+    rng = np.random.default_rng(21)
+    x = rng.standard_normal((6, 300)) * 8.0 + 1000.0 * (np.arange(6)[:, None] % 2)
+    y = oracle.log_softmax(x)
+    ref = torch.log_softmax(torch.from_numpy(x), dim=-1).numpy()
+    assert np.allclose(y, ref, rtol=1e-13, atol=1e-12)
+    # logsumexp of the output is 0; it equals log of the softmax oracle
+    assert np.allclose(np.log(np.exp(y).sum(axis=1)), 0.0, atol=1e-13)
+    assert np.allclose(y, np.log(oracle.softmax(x)), rtol=1e-12, atol=1e-12)
+    # shift invariance, bitwise for exact shifts of dyadic values
+    xd = np.round(x * 64) / 64
+    assert np.array_equal(oracle.log_softmax(xd), oracle.log_softmax(xd + 512.0))
+    # masked entries give -inf; a fully masked row gives NaN
+    z = oracle.log_softmax(np.array([[0.5, -np.inf, 2.0], [-np.inf, -np.inf, -np.inf]]))
+    assert z[0, 1] == -np.inf and np.isfinite(z[0, [0, 2]]).all() and np.isnan(z[1]).all()
+
+
 ALPHABET = [float("-inf"), -2.0, 0.0, 0.5, 3.0, 1000.0]
 
 
