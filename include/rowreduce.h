@@ -7,6 +7,8 @@
  *   rr_fused_add_rmsnorm  residual <- residual + x;  y = rmsnorm(residual) * gamma
  *   rr_layernorm          y = (x - mean) * rsqrt(var + eps) * gamma + beta
  *   rr_softmax_rows       y = exp(x - m) / d with the online normaliser (m, d)
+ *   rr_softmax_rows_ex    the same, or log-softmax, optionally under a causal
+ *                         rule whose masked keys are never read
  *
  * Sources (web pages, cited by title and section):
  *   [P1] "两个融合算子：RMSNorm 与 online softmax" (daleiyang.github.io)
@@ -157,6 +159,57 @@ rr_status rr_softmax_rows(void* y, const void* x, int64_t M, int64_t N, rr_dtype
                           rr_dtype out_dtype, void* workspace, size_t workspace_bytes,
                           void* stream);
 
+/*
+ * Options of rr_softmax_rows_ex.  A NULL options pointer means all zero:
+ * plain softmax over every key.
+ *   log_output     0: y = exp(x - m) / d (probabilities).
+ *                  1: y = (x - m) - log(d), the log of the same quantity
+ *                  (PyTorch's softmax forward switches between the two
+ *                  with one flag: [P2] section 九, the SoftMax.cu dispatch).
+ *   causal         0: every key of a row takes part.
+ *                  1: row i keeps the keys j <= (i mod causal_period) +
+ *                  causal_offset and masks the rest.  With rows laid out as
+ *                  heads x queries and N keys, causal_period = queries and
+ *                  causal_offset = N - queries is the attention causal mask
+ *                  (the per-layer score softmax of [P1] section
+ *                  "二、它们在 Qwen2.5-7B 里的真实位置"; offset 0 when queries
+ *                  and keys coincide).  Masked keys are never read: the
+ *                  kernel loads only the kept prefix of each row, so the
+ *                  input there may hold anything.
+ *   causal_period  >= 1 when causal (ignored otherwise).
+ *   causal_offset  >= 0 when causal (ignored otherwise).
+ * Masked keys come out as exactly 0 (probabilities) or -inf (log output).
+ * Kept keys may themselves be -inf (a further mask in the data); they give 0
+ * or -inf the same way ([P2] section 十, the masked entries of the online
+ * softmax).  A row whose kept keys are all -inf gives NaN everywhere, as in
+ * rr_softmax_rows.
+ */
+typedef struct rr_softmax_opts {
+  int32_t log_output;
+  int32_t causal;
+  int64_t causal_period;
+  int64_t causal_offset;
+} rr_softmax_opts;
+
+/*
+ * rr_softmax_rows_ex_workspace_bytes -- workspace rr_softmax_rows_ex needs
+ * with these options (0 when none: a causal call never splits a row).
+ * Host-only; returns 0 for invalid arguments.
+ */
+size_t rr_softmax_rows_ex_workspace_bytes(int64_t M, int64_t N, rr_dtype in_dtype,
+                                          rr_dtype out_dtype, const rr_softmax_opts* opts);
+
+/*
+ * rr_softmax_rows_ex -- rr_softmax_rows with options (above).  Arguments,
+ * workspace rules, aliasing rules and errors as rr_softmax_rows; in
+ * addition RR_ERR_INVALID_ARG for log_output or causal outside {0, 1}, or a
+ * causal call with causal_period < 1 or causal_offset < 0.  With opts NULL
+ * or all zero it is exactly rr_softmax_rows (same kernels, same bits).
+ */
+rr_status rr_softmax_rows_ex(void* y, const void* x, int64_t M, int64_t N, rr_dtype in_dtype,
+                             rr_dtype out_dtype, const rr_softmax_opts* opts, void* workspace,
+                             size_t workspace_bytes, void* stream);
+
 /* Static English name of a status code ("RR_OK", ...). */
 const char* rr_status_string(rr_status status);
 
@@ -171,7 +224,8 @@ typedef enum rr_op {
   RR_OP_RMSNORM = 0,
   RR_OP_FUSED_ADD_RMSNORM = 1,
   RR_OP_SOFTMAX = 2,
-  RR_OP_LAYERNORM = 3
+  RR_OP_LAYERNORM = 3,
+  RR_OP_SOFTMAX_CAUSAL = 4 /* rr_softmax_rows_ex with causal = 1 */
 } rr_op;
 
 /* Kernel variants, chosen by row length ([P2] section 六; [P4] section
@@ -189,7 +243,7 @@ typedef enum rr_op {
  *         It falls back to the two kernels when the device cannot hold a
  *         row's chunks at once.  Both forms give the same bits.
  *   LOOP  one workgroup per row streaming the row twice (any N, unaligned
- *         rows, long rows with many rows)
+ *         rows, long rows with many rows; causal rows too long for BLOCK)
  *   SUBWAVE short rows (at most 32 vectors, or 32 elements when unaligned):
  *         L lanes per row, 64/L rows per wavefront, reduced inside each
  *         L-lane group ([P4] section "按行长度选择并行方式")

@@ -27,6 +27,7 @@ RR_OP_RMSNORM = 0
 RR_OP_FUSED_ADD_RMSNORM = 1
 RR_OP_SOFTMAX = 2
 RR_OP_LAYERNORM = 3
+RR_OP_SOFTMAX_CAUSAL = 4
 
 RR_VARIANT_AUTO = 0
 RR_VARIANT_WAVE = 1
@@ -40,7 +41,8 @@ VARIANT_NAMES = {0: "auto", 1: "wave", 2: "block", 3: "split", 4: "loop", 5: "sp
 # Every function include/rowreduce.h declares.
 EXPORTS = (
     "rr_rmsnorm", "rr_fused_add_rmsnorm", "rr_layernorm", "rr_softmax_rows_workspace_bytes",
-    "rr_softmax_rows", "rr_status_string", "rr_last_error_message", "rr_query_plan",
+    "rr_softmax_rows", "rr_softmax_rows_ex_workspace_bytes", "rr_softmax_rows_ex",
+    "rr_status_string", "rr_last_error_message", "rr_query_plan",
     "rr_set_variant_override", "rr_selftest_wave_allreduce",
 )
 
@@ -49,6 +51,26 @@ class RowReduceError(RuntimeError):
     def __init__(self, status, message):
         super().__init__(message)
         self.status = status
+
+
+class rr_softmax_opts(ctypes.Structure):
+    _fields_ = [
+        ("log_output", ctypes.c_int32),
+        ("causal", ctypes.c_int32),
+        ("causal_period", ctypes.c_int64),
+        ("causal_offset", ctypes.c_int64),
+    ]
+
+
+def make_softmax_opts(log_output=False, causal_period=None, causal_offset=0):
+    """Options struct; causal_period None means no causal rule."""
+    o = rr_softmax_opts()
+    o.log_output = int(log_output)
+    if causal_period is not None:
+        o.causal = 1
+        o.causal_period = int(causal_period)
+        o.causal_offset = int(causal_offset)
+    return o
 
 
 class rr_plan(ctypes.Structure):
@@ -94,6 +116,10 @@ def lib():
     L.rr_softmax_rows_workspace_bytes.argtypes = [i64, i64, i32, i32]
     L.rr_softmax_rows_workspace_bytes.restype = ctypes.c_size_t
     L.rr_softmax_rows.argtypes = [vp, vp, i64, i64, i32, i32, vp, ctypes.c_size_t, vp]
+    po = ctypes.POINTER(rr_softmax_opts)
+    L.rr_softmax_rows_ex_workspace_bytes.argtypes = [i64, i64, i32, i32, po]
+    L.rr_softmax_rows_ex_workspace_bytes.restype = ctypes.c_size_t
+    L.rr_softmax_rows_ex.argtypes = [vp, vp, i64, i64, i32, i32, po, vp, ctypes.c_size_t, vp]
     L.rr_status_string.argtypes = [i32]
     L.rr_status_string.restype = ctypes.c_char_p
     L.rr_last_error_message.argtypes = []
@@ -101,7 +127,8 @@ def lib():
     L.rr_query_plan.argtypes = [i32, i64, i64, i32, i32, i32, ctypes.POINTER(rr_plan)]
     L.rr_set_variant_override.argtypes = [i32]
     L.rr_selftest_wave_allreduce.argtypes = [vp, vp, i64, i32, vp]
-    for f in ("rr_rmsnorm", "rr_fused_add_rmsnorm", "rr_layernorm", "rr_softmax_rows", "rr_query_plan",
+    for f in ("rr_rmsnorm", "rr_fused_add_rmsnorm", "rr_layernorm", "rr_softmax_rows",
+              "rr_softmax_rows_ex", "rr_query_plan",
               "rr_set_variant_override", "rr_selftest_wave_allreduce"):
         getattr(L, f).restype = i32
     _LIB = L
@@ -144,6 +171,20 @@ def raw_softmax_rows(y, x, M, N, in_dtype, out_dtype, workspace, workspace_bytes
 
 def rr_softmax_rows_workspace_bytes(M: int, N: int, in_dtype: int, out_dtype: int) -> int:
     return int(lib().rr_softmax_rows_workspace_bytes(M, N, in_dtype, out_dtype))
+
+
+def _opts_ref(opts):
+    return ctypes.byref(opts) if opts is not None else None
+
+
+def raw_softmax_rows_ex(y, x, M, N, in_dtype, out_dtype, opts, workspace, workspace_bytes, stream):
+    """opts: an rr_softmax_opts or None."""
+    return lib().rr_softmax_rows_ex(y, x, M, N, in_dtype, out_dtype, _opts_ref(opts), workspace,
+                                    workspace_bytes, stream)
+
+
+def rr_softmax_rows_ex_workspace_bytes(M: int, N: int, in_dtype: int, out_dtype: int, opts=None) -> int:
+    return int(lib().rr_softmax_rows_ex_workspace_bytes(M, N, in_dtype, out_dtype, _opts_ref(opts)))
 
 
 def rr_query_plan(op: int, M: int, N: int, in_dtype: int, out_dtype: int, aligned16: bool = True):
@@ -265,6 +306,21 @@ def rr_softmax_rows(y, x, workspace=None, stream=None) -> None:
                            _stream_of(x, stream)), "rr_softmax_rows")
 
 
+def rr_softmax_rows_ex(y, x, opts=None, workspace=None, stream=None) -> None:
+    """rr_softmax_rows with an rr_softmax_opts (log output, causal rule)."""
+    _need_cuda(y, x)
+    M, N = _rows(x)
+    if y.shape != x.shape:
+        raise ValueError("y must match x")
+    din, dout = dtype_code(x), dtype_code(y)
+    ws_ptr, ws_bytes = None, 0
+    if workspace is not None:
+        _need_cuda(workspace)
+        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    check(raw_softmax_rows_ex(y.data_ptr(), x.data_ptr(), M, N, din, dout, opts, ws_ptr, ws_bytes,
+                              _stream_of(x, stream)), "rr_softmax_rows_ex")
+
+
 def rr_selftest_wave_allreduce(out, inp, kind: int, stream=None) -> None:
     _need_cuda(out, inp)
     per = 128 if kind == 2 else 64
@@ -304,6 +360,23 @@ def softmax_workspace(x, out_dtype):
     n = rr_softmax_rows_workspace_bytes(M, N, dtype_code(x),
                                         RR_F32 if out_dtype == torch.float32 else RR_BF16)
     return torch.empty(n, dtype=torch.uint8, device=x.device) if n else None
+
+
+def softmax_rows_ex(x, out_dtype=None, out=None, log_output=False, causal_period=None,
+                    causal_offset=0, workspace=None):
+    """Softmax or log-softmax of each row; with causal_period, row i keeps
+    the keys j <= (i mod causal_period) + causal_offset (the rest is never
+    read and comes out as 0, or -inf for log output)."""
+    torch = _torch()
+    opts = make_softmax_opts(log_output, causal_period, causal_offset)
+    if out is None:
+        out = torch.empty(x.shape, dtype=out_dtype or x.dtype, device=x.device)
+    if workspace is None:
+        M, N = _rows(x)
+        n = rr_softmax_rows_ex_workspace_bytes(M, N, dtype_code(x), dtype_code(out), opts)
+        workspace = torch.empty(n, dtype=torch.uint8, device=x.device) if n else None
+    rr_softmax_rows_ex(out, x, opts, workspace)
+    return out
 
 
 def softmax_rows(x, out_dtype=None, out=None, workspace=None):

@@ -165,8 +165,12 @@ rr_status make_plan(rr_op op, int64_t M, int64_t N, int din, int dout, bool is_a
                     rr_plan* p) {
   memset(p, 0, sizeof(*p));
   if (op != RR_OP_RMSNORM && op != RR_OP_FUSED_ADD_RMSNORM && op != RR_OP_SOFTMAX &&
-      op != RR_OP_LAYERNORM)
+      op != RR_OP_LAYERNORM && op != RR_OP_SOFTMAX_CAUSAL)
     return fail(RR_ERR_INVALID_ARG, "unknown op %d", (int)op);
+  // a causal softmax runs the softmax kernels but never splits a row (the
+  // split kernels keep every key)
+  const bool causal = op == RR_OP_SOFTMAX_CAUSAL;
+  if (causal) op = RR_OP_SOFTMAX;
   if (!valid_dtype(din) || !valid_dtype(dout))
     return fail(RR_ERR_INVALID_ARG, "unknown dtype (%d, %d)", din, dout);
   if (op != RR_OP_SOFTMAX && din != dout)
@@ -190,7 +194,7 @@ rr_status make_plan(rr_op op, int64_t M, int64_t N, int din, int dout, bool is_a
         plan_wave(p, vec, nvec);
       } else if (plan_block(op, p, vec, nvec)) {
       } else if (M >= kPackedMinRows && plan_packed(op, p, vec, nvec)) {
-      } else if (op == RR_OP_SOFTMAX && M < kSplitMaxRows) {
+      } else if (op == RR_OP_SOFTMAX && !causal && M < kSplitMaxRows) {
         plan_split(p, vec, nvec);
       } else {
         plan_loop(p, vec, nvec);
@@ -206,7 +210,7 @@ rr_status make_plan(rr_op op, int64_t M, int64_t N, int din, int dout, bool is_a
       break;
     case RR_VARIANT_SPLIT:
     case RR_VARIANT_SPLIT_ONE_KERNEL:
-      ok = vec > 1 && op == RR_OP_SOFTMAX;
+      ok = vec > 1 && op == RR_OP_SOFTMAX && !causal;
       if (ok) {
         plan_split(p, vec, nvec);
         p->variant = forced;
@@ -350,46 +354,113 @@ rr_status rr_layernorm(void* y, const void* x, const void* gamma, const void* be
   return norm_entry(rr::kLaunchLayer, y, nullptr, x, gamma, beta, M, H, eps, dtype, stream);
 }
 
+}  // extern "C"
+
+namespace {
+
+// Options of a softmax call, checked; NULL means all zero.
+rr_status softmax_options(const rr_softmax_opts* o, const char* who, rr_softmax_opts* out) {
+  memset(out, 0, sizeof(*out));
+  if (!o) return RR_OK;
+  if (o->log_output != 0 && o->log_output != 1)
+    return fail(RR_ERR_INVALID_ARG, "%s: log_output = %d (0 or 1)", who, (int)o->log_output);
+  if (o->causal != 0 && o->causal != 1)
+    return fail(RR_ERR_INVALID_ARG, "%s: causal = %d (0 or 1)", who, (int)o->causal);
+  *out = *o;
+  if (o->causal) {
+    if (o->causal_period < 1)
+      return fail(RR_ERR_INVALID_ARG, "%s: causal_period = %lld < 1", who, (long long)o->causal_period);
+    if (o->causal_offset < 0)
+      return fail(RR_ERR_INVALID_ARG, "%s: causal_offset = %lld < 0", who, (long long)o->causal_offset);
+  } else {
+    out->causal_period = 0;
+    out->causal_offset = 0;
+  }
+  return RR_OK;
+}
+
+rr_status softmax_entry(const char* who, void* y, const void* x, int64_t M, int64_t N,
+                        rr_dtype in_dtype, rr_dtype out_dtype, const rr_softmax_opts* opts,
+                        void* workspace, size_t workspace_bytes, void* stream) {
+  g_err[0] = '\0';
+  if (!valid_dtype(in_dtype) || !valid_dtype(out_dtype))
+    return fail(RR_ERR_INVALID_ARG, "%s: unknown dtype (%d, %d)", who, (int)in_dtype, (int)out_dtype);
+  rr_softmax_opts o;
+  const rr_status so = softmax_options(opts, who, &o);
+  if (so != RR_OK) return so;
+  if (M < 0) return fail(RR_ERR_INVALID_ARG, "%s: M = %lld < 0", who, (long long)M);
+  if (N < 1) return fail(RR_ERR_INVALID_ARG, "%s: N = %lld < 1", who, (long long)N);
+  if (M == 0) return RR_OK;
+  if (!y || !x) return fail(RR_ERR_INVALID_ARG, "%s: null pointer", who);
+  if (N > kMaxN) return fail(RR_ERR_UNSUPPORTED, "%s: N = %lld > 2^30", who, (long long)N);
+  if ((uint64_t)M > (uint64_t)(SIZE_MAX / 8) / (uint64_t)N)
+    return fail(RR_ERR_INVALID_ARG, "%s: M * N overflows", who);
+  const size_t xb = (size_t)M * (size_t)N * dtype_size(in_dtype);
+  const size_t yb = (size_t)M * (size_t)N * dtype_size(out_dtype);
+  if (overlaps(x, xb, y, yb) && !(x == y && in_dtype == out_dtype))
+    return fail(RR_ERR_INVALID_ARG, "%s: x and y overlap (in place needs equal pointers and dtypes)", who);
+  const bool al = aligned16(x) && aligned16(y);
+  rr_plan p;
+  const rr_status st = make_plan(o.causal ? RR_OP_SOFTMAX_CAUSAL : RR_OP_SOFTMAX, M, N, in_dtype,
+                                 out_dtype, al, &p);
+  if (st != RR_OK) return st;
+  if (p.workspace_bytes > 0) {
+    if (!workspace || workspace_bytes < p.workspace_bytes)
+      return fail(RR_ERR_WORKSPACE, "%s: needs a workspace of %zu bytes, got %zu", who,
+                  p.workspace_bytes, workspace ? workspace_bytes : (size_t)0);
+    if ((reinterpret_cast<uintptr_t>(workspace) & 15u) != 0)
+      return fail(RR_ERR_INVALID_ARG, "%s: workspace must be 16-byte aligned", who);
+    if (overlaps(workspace, p.workspace_bytes, x, xb) || overlaps(workspace, p.workspace_bytes, y, yb))
+      return fail(RR_ERR_INVALID_ARG, "%s: workspace overlaps x or y", who);
+  }
+  rr::SoftmaxArgs a;
+  a.y = y;
+  a.x = x;
+  a.workspace = workspace;
+  a.M = M;
+  a.N = (int32_t)N;
+  a.causal_period = o.causal ? o.causal_period : 0;
+  // keys kept by row i: min(N, (i mod P) + O + 1); an offset of N or more
+  // keeps every key, so clamp it to keep the kernels' sums in range
+  a.causal_offset = o.causal_offset < N ? o.causal_offset : N;
+  a.log_output = o.log_output;
+  const hipError_t e = rr::launch_softmax(p, in_dtype, out_dtype, a, grid_for(p),
+                                          static_cast<hipStream_t>(stream));
+  return hip_status(e, who);
+}
+
+}  // namespace
+
+extern "C" {
+
 size_t rr_softmax_rows_workspace_bytes(int64_t M, int64_t N, rr_dtype in_dtype,
                                        rr_dtype out_dtype) {
+  return rr_softmax_rows_ex_workspace_bytes(M, N, in_dtype, out_dtype, nullptr);
+}
+
+size_t rr_softmax_rows_ex_workspace_bytes(int64_t M, int64_t N, rr_dtype in_dtype,
+                                          rr_dtype out_dtype, const rr_softmax_opts* opts) {
+  rr_softmax_opts o;
+  if (softmax_options(opts, "rr_softmax_rows_ex_workspace_bytes", &o) != RR_OK) return 0;
   rr_plan p;
-  if (make_plan(RR_OP_SOFTMAX, M, N, in_dtype, out_dtype, true, &p) != RR_OK) return 0;
+  if (make_plan(o.causal ? RR_OP_SOFTMAX_CAUSAL : RR_OP_SOFTMAX, M, N, in_dtype, out_dtype, true,
+                &p) != RR_OK)
+    return 0;
   return p.workspace_bytes;
 }
 
 rr_status rr_softmax_rows(void* y, const void* x, int64_t M, int64_t N, rr_dtype in_dtype,
                           rr_dtype out_dtype, void* workspace, size_t workspace_bytes,
                           void* stream) {
-  g_err[0] = '\0';
-  if (!valid_dtype(in_dtype) || !valid_dtype(out_dtype))
-    return fail(RR_ERR_INVALID_ARG, "rr_softmax_rows: unknown dtype (%d, %d)", (int)in_dtype, (int)out_dtype);
-  if (M < 0) return fail(RR_ERR_INVALID_ARG, "rr_softmax_rows: M = %lld < 0", (long long)M);
-  if (N < 1) return fail(RR_ERR_INVALID_ARG, "rr_softmax_rows: N = %lld < 1", (long long)N);
-  if (M == 0) return RR_OK;
-  if (!y || !x) return fail(RR_ERR_INVALID_ARG, "rr_softmax_rows: null pointer");
-  if (N > kMaxN) return fail(RR_ERR_UNSUPPORTED, "rr_softmax_rows: N = %lld > 2^30", (long long)N);
-  if ((uint64_t)M > (uint64_t)(SIZE_MAX / 8) / (uint64_t)N)
-    return fail(RR_ERR_INVALID_ARG, "rr_softmax_rows: M * N overflows");
-  const size_t xb = (size_t)M * (size_t)N * dtype_size(in_dtype);
-  const size_t yb = (size_t)M * (size_t)N * dtype_size(out_dtype);
-  if (overlaps(x, xb, y, yb) && !(x == y && in_dtype == out_dtype))
-    return fail(RR_ERR_INVALID_ARG, "rr_softmax_rows: x and y overlap (in place needs equal pointers and dtypes)");
-  const bool al = aligned16(x) && aligned16(y);
-  rr_plan p;
-  const rr_status st = make_plan(RR_OP_SOFTMAX, M, N, in_dtype, out_dtype, al, &p);
-  if (st != RR_OK) return st;
-  if (p.workspace_bytes > 0) {
-    if (!workspace || workspace_bytes < p.workspace_bytes)
-      return fail(RR_ERR_WORKSPACE, "rr_softmax_rows: needs a workspace of %zu bytes, got %zu",
-                  p.workspace_bytes, workspace ? workspace_bytes : (size_t)0);
-    if ((reinterpret_cast<uintptr_t>(workspace) & 15u) != 0)
-      return fail(RR_ERR_INVALID_ARG, "rr_softmax_rows: workspace must be 16-byte aligned");
-    if (overlaps(workspace, p.workspace_bytes, x, xb) || overlaps(workspace, p.workspace_bytes, y, yb))
-      return fail(RR_ERR_INVALID_ARG, "rr_softmax_rows: workspace overlaps x or y");
-  }
-  const hipError_t e = rr::launch_softmax(p, in_dtype, out_dtype, y, x, workspace, M, (int32_t)N,
-                                          grid_for(p), static_cast<hipStream_t>(stream));
-  return hip_status(e, "rr_softmax_rows");
+  return softmax_entry("rr_softmax_rows", y, x, M, N, in_dtype, out_dtype, nullptr, workspace,
+                       workspace_bytes, stream);
+}
+
+rr_status rr_softmax_rows_ex(void* y, const void* x, int64_t M, int64_t N, rr_dtype in_dtype,
+                             rr_dtype out_dtype, const rr_softmax_opts* opts, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  return softmax_entry("rr_softmax_rows_ex", y, x, M, N, in_dtype, out_dtype, opts, workspace,
+                       workspace_bytes, stream);
 }
 
 const char* rr_status_string(rr_status s) {

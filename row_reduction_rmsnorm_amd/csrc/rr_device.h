@@ -159,6 +159,22 @@ struct Packed {
 #pragma unroll
     for (int i = 0; i < kWords; ++i) w[i] = 0u;
   }
+  // Elements `first` and above become -inf (first in [0, VEC)).
+  __device__ __forceinline__ void mask_from(int first) {
+    if constexpr (std::is_same_v<T, float>) {
+#pragma unroll
+      for (int i = 0; i < kWords; ++i)
+        if (i >= first) w[i] = 0xff800000u;
+    } else if constexpr (VEC == 1) {
+      if (first <= 0) w[0] = 0xff80u;
+    } else {
+#pragma unroll
+      for (int i = 0; i < kWords; ++i) {
+        if (2 * i >= first) w[i] = (w[i] & 0xffff0000u) | 0xff80u;
+        if (2 * i + 1 >= first) w[i] = (w[i] & 0x0000ffffu) | 0xff800000u;
+      }
+    }
+  }
   // Tell the compiler the words may have changed (an empty asm that "reads
   // and writes" them), so values widened earlier are not kept live across
   // this point: the next get() widens again from the packed words.

@@ -86,6 +86,24 @@ __device__ __forceinline__ MD group_md(MD v, int nw, int w, int lane,
   return md_merge(t, dpp_md<kDppRowMirror>(t));
 }
 
+// Keys row `row` keeps: all N, or under the causal rule (period cp >= 1)
+// those with index j <= (row mod cp) + co, i.e. min(N, (row mod cp) + co + 1).
+__device__ __forceinline__ int row_keys(int64_t row, int N, int64_t cp, int64_t co) {
+  if (cp <= 0) return N;
+  const int64_t k = row % cp + co + 1;
+  return k < (int64_t)N ? (int)k : N;
+}
+
+// Entries of the vector starting at element e0 that lie at or past `keys`
+// become -inf (they are masked keys; only the vector holding the last kept
+// key can contain any).
+template <int VEC>
+__device__ __forceinline__ void mask_keys(float (&v)[VEC], int e0, int keys) {
+#pragma unroll
+  for (int i = 0; i < VEC; ++i)
+    if (e0 + i >= keys) v[i] = kNegInf;
+}
+
 // Thread coordinates.  WAVE: each wavefront owns a row, the workgroup holds
 // blockDim/64 rows.  Otherwise the whole workgroup (blockDim/64 wavefronts)
 // owns one row.
@@ -423,19 +441,20 @@ __global__ __launch_bounds__(256) void norm_sub_kernel(T* y, T* residual, const 
   }
 }
 
-template <typename Tin, typename Tout, int VEC, int L>
-__global__ __launch_bounds__(256) void softmax_sub_kernel(const Tin* x, Tout* y, int64_t M,
-                                                          int N) {
+template <typename Tin, typename Tout, int VEC, int L, bool LOG>
+__global__ __launch_bounds__(256) void softmax_sub_kernel(const Tin* x, Tout* y, int64_t M, int N,
+                                                          int64_t cp, int64_t co) {
   constexpr int kRowsPerGroup = 256 / L;
   const int j = threadIdx.x & (L - 1);
   const int nvec = N / VEC;
-  const bool active = j < nvec;
   for (int64_t row = (int64_t)blockIdx.x * kRowsPerGroup + (threadIdx.x / L); row < M;
        row += (int64_t)gridDim.x * kRowsPerGroup) {
+    const int keys = row_keys(row, N, cp, co);
     const int64_t off = row * (int64_t)N + (int64_t)j * VEC;
     float v[VEC];
-    if (active) {
+    if (j * VEC < keys) {
       load_vec<Tin, VEC>(x + off, v);
+      mask_keys<VEC>(v, j * VEC, keys);
     } else {
 #pragma unroll
       for (int i = 0; i < VEC; ++i) v[i] = kNegInf;
@@ -447,21 +466,26 @@ __global__ __launch_bounds__(256) void softmax_sub_kernel(const Tin* x, Tout* y,
     float dl = 0.0f;
 #pragma unroll
     for (int i = 0; i < VEC; ++i) {
-      v[i] = exp_shifted(v[i] - shift);
-      dl += v[i];
+      const float e = exp_shifted(v[i] - shift);
+      dl += e;
+      if constexpr (!LOG) v[i] = e;
     }
     MD p;
     p.m = ml;
     p.d = dl;
     p = group_lanes_md<L>(p);
-    float c = (ml == kNegInf) ? 0.0f : exp_shifted(ml - p.m) / p.d;
-    if (p.m == kNegInf) c = __builtin_nanf("");
-    if (active) {
-      float o[VEC];
+    float o[VEC];
+    if constexpr (LOG) {
+      const float ld = __builtin_logf(p.d);
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) o[i] = (v[i] - p.m) - ld;
+    } else {
+      float c = (ml == kNegInf) ? 0.0f : exp_shifted(ml - p.m) / p.d;
+      if (p.m == kNegInf) c = __builtin_nanf("");
 #pragma unroll
       for (int i = 0; i < VEC; ++i) o[i] = v[i] * c;
-      store_vec<Tout, VEC>(y + off, o);
     }
+    if (j < nvec) store_vec<Tout, VEC>(y + off, o);
   }
 }
 
@@ -481,9 +505,9 @@ __global__ __launch_bounds__(256) void softmax_sub_kernel(const Tin* x, Tout* y,
 // entries are all -inf has m_l = -inf and c_l = 0; a row whose entries are
 // all -inf has m = -inf and every output is NaN, as exp(x - m)/d is.
 // ===========================================================================
-template <typename Tin, typename Tout, int NV, bool WAVE>
+template <typename Tin, typename Tout, int NV, bool WAVE, bool LOG>
 __global__ __launch_bounds__(1024) void softmax_regs_kernel(const Tin* x, Tout* y, int64_t M,
-                                                            int N) {
+                                                            int N, int64_t cp, int64_t co) {
   constexpr int VEC = Elem<Tin>::kVec;
   __shared__ MD slots[2][kMaxWavesPerGroup];
   const RowLane rl = row_lane<WAVE>();
@@ -491,13 +515,16 @@ __global__ __launch_bounds__(1024) void softmax_regs_kernel(const Tin* x, Tout* 
   const int64_t stride = (int64_t)gridDim.x * rl.rpg;
   int parity = 0;
   for (int64_t row = (int64_t)blockIdx.x * rl.rpg + rl.g; row < M; row += stride) {
+    const int keys = row_keys(row, N, cp, co);
+    const int nvec_keys = (keys + VEC - 1) / VEC;   // vectors holding kept keys
     const int64_t off = row * (int64_t)N;
     float v[NV][VEC];
 #pragma unroll
     for (int k = 0; k < NV; ++k) {
       const int vi = k * rl.T + rl.t;
-      if (vi < nvec) {
+      if (vi < nvec_keys) {
         load_vec<Tin, VEC>(x + off + (int64_t)vi * VEC, v[k]);
+        mask_keys<VEC>(v[k], vi * VEC, keys);
       } else {
 #pragma unroll
         for (int i = 0; i < VEC; ++i) v[k][i] = kNegInf;
@@ -515,8 +542,9 @@ __global__ __launch_bounds__(1024) void softmax_regs_kernel(const Tin* x, Tout* 
     for (int k = 0; k < NV; ++k)
 #pragma unroll
       for (int i = 0; i < VEC; ++i) {
-        v[k][i] = exp_shifted(v[k][i] - shift);
-        dl += v[k][i];
+        const float e = exp_shifted(v[k][i] - shift);
+        dl += e;
+        if constexpr (!LOG) v[k][i] = e;   // plain softmax keeps e_i, log-softmax keeps x_i
       }
     MD p;
     p.m = ml;
@@ -526,14 +554,19 @@ __global__ __launch_bounds__(1024) void softmax_regs_kernel(const Tin* x, Tout* 
       p = group_md(p, rl.nw, rl.w, rl.lane, slots, parity);
       parity ^= 1;
     }
-    float c = (ml == kNegInf) ? 0.0f : exp_shifted(ml - p.m) / p.d;
-    if (p.m == kNegInf) c = __builtin_nanf("");
+    float c = 0.0f, ld = 0.0f;
+    if constexpr (LOG) {
+      ld = __builtin_logf(p.d);
+    } else {
+      c = (ml == kNegInf) ? 0.0f : exp_shifted(ml - p.m) / p.d;
+      if (p.m == kNegInf) c = __builtin_nanf("");
+    }
 #pragma unroll
     for (int k = 0; k < NV; ++k) {
       const int vi = k * rl.T + rl.t;
       float o[VEC];
 #pragma unroll
-      for (int i = 0; i < VEC; ++i) o[i] = v[k][i] * c;
+      for (int i = 0; i < VEC; ++i) o[i] = LOG ? (v[k][i] - p.m) - ld : v[k][i] * c;
       if (vi < nvec) store_vec<Tout, VEC>(y + off + (int64_t)vi * VEC, o);
     }
   }
@@ -549,9 +582,9 @@ __global__ __launch_bounds__(1024) void softmax_regs_kernel(const Tin* x, Tout* 
 // bf16 row needs 19 vectors (76 VGPRs) per lane of a 1024-lane workgroup, one
 // workgroup per CU.
 // ===========================================================================
-template <typename Tin, typename Tout, int NV>
+template <typename Tin, typename Tout, int NV, bool LOG>
 __global__ __launch_bounds__(1024) void softmax_packed_kernel(const Tin* x, Tout* y, int64_t M,
-                                                              int N) {
+                                                              int N, int64_t cp, int64_t co) {
   constexpr int VEC = Elem<Tin>::kVec;
   constexpr int kThreads = 1024;
   __shared__ MD slots[2][kMaxWavesPerGroup];
@@ -561,6 +594,8 @@ __global__ __launch_bounds__(1024) void softmax_packed_kernel(const Tin* x, Tout
   const int nvec = N / VEC;
   int parity = 0;
   for (int64_t row = blockIdx.x; row < M; row += gridDim.x) {
+    const int keys = row_keys(row, N, cp, co);
+    const int nvec_keys = (keys + VEC - 1) / VEC;
     const Tin* xr = x + row * (int64_t)N;   // uniform row bases
     Tout* yr = y + row * (int64_t)N;
     // the lane's vector offsets are recomputed at each use rather than kept
@@ -572,14 +607,22 @@ __global__ __launch_bounds__(1024) void softmax_packed_kernel(const Tin* x, Tout
 #pragma unroll
     for (int k = 0; k < NV; ++k) {
       const int vi = k * kThreads + t_ld;
-      if (vi < nvec) v[k].template load<true>(xr + vi * VEC);
-      else v[k].fill(kNegInf);
+      if (vi < nvec_keys) {
+        v[k].template load<true>(xr + vi * VEC);
+        // keys past the row's count become -inf (only the vector holding
+        // the last kept key can contain any)
+        const int first = keys - vi * VEC;
+        if (first < VEC) v[k].mask_from(first);
+      } else {
+        v[k].fill(kNegInf);
+      }
     }
+    auto key = [&](int k, int i) { return v[k].get(i); };
     float ml = kNegInf;
 #pragma unroll
     for (int k = 0; k < NV; ++k)
 #pragma unroll
-      for (int i = 0; i < VEC; ++i) ml = __builtin_fmaxf(ml, v[k].get(i));
+      for (int i = 0; i < VEC; ++i) ml = __builtin_fmaxf(ml, key(k, i));
 #pragma unroll
     for (int k = 0; k < NV; ++k) v[k].touch();
     const float shift = (ml == kNegInf) ? 0.0f : ml;
@@ -587,7 +630,7 @@ __global__ __launch_bounds__(1024) void softmax_packed_kernel(const Tin* x, Tout
 #pragma unroll
     for (int k = 0; k < NV; ++k)
 #pragma unroll
-      for (int i = 0; i < VEC; ++i) dl += exp_shifted(v[k].get(i) - shift);
+      for (int i = 0; i < VEC; ++i) dl += exp_shifted(key(k, i) - shift);
     MD p;
     p.m = ml;
     p.d = dl;
@@ -597,6 +640,7 @@ __global__ __launch_bounds__(1024) void softmax_packed_kernel(const Tin* x, Tout
     p = group_md(p, kThreads / kWave, w, lane, slots, parity);
     parity ^= 1;
     const float inv_d = (p.m == kNegInf) ? __builtin_nanf("") : 1.0f / p.d;
+    const float ld = LOG ? __builtin_logf(p.d) : 0.0f;
     int t_st = t;
     asm volatile("" : "+v"(t_st));
 #pragma unroll
@@ -604,7 +648,8 @@ __global__ __launch_bounds__(1024) void softmax_packed_kernel(const Tin* x, Tout
       const int vi = k * kThreads + t_st;
       float o[VEC];
 #pragma unroll
-      for (int i = 0; i < VEC; ++i) o[i] = exp_shifted(v[k].get(i) - p.m) * inv_d;
+      for (int i = 0; i < VEC; ++i)
+        o[i] = LOG ? (key(k, i) - p.m) - ld : exp_shifted(key(k, i) - p.m) * inv_d;
       if (vi < nvec) store_vec<Tout, VEC>(yr + vi * VEC, o);
     }
   }
@@ -619,32 +664,42 @@ __global__ __launch_bounds__(1024) void softmax_packed_kernel(const Tin* x, Tout
 // and writes exp(x - m) / d.  HBM traffic: two reads and one write per
 // element ([P2] section 七.3: "read twice, write once").
 // ===========================================================================
-template <typename Tin, typename Tout, int VEC>
+template <typename Tin, typename Tout, int VEC, bool LOG>
 __global__ __launch_bounds__(1024) void softmax_loop_kernel(const Tin* x, Tout* y, int64_t M,
-                                                            int N) {
+                                                            int N, int64_t cp, int64_t co) {
   __shared__ MD slots[2][kMaxWavesPerGroup];
   const RowLane rl = row_lane<false>();
   const int nvec = N / VEC;
   int parity = 0;
   for (int64_t row = blockIdx.x; row < M; row += gridDim.x) {
+    const int keys = row_keys(row, N, cp, co);
+    const int nvec_keys = (keys + VEC - 1) / VEC;
     const int64_t off = row * (int64_t)N;
     MD p;
     p.m = kNegInf;
     p.d = 0.0f;
-    for (int vi = rl.t; vi < nvec; vi += rl.T) {
+    for (int vi = rl.t; vi < nvec_keys; vi += rl.T) {
       float v[VEC];
       load_vec<Tin, VEC>(x + off + (int64_t)vi * VEC, v);
+      mask_keys<VEC>(v, vi * VEC, keys);
       p = md_merge(p, chunk_summary<VEC>(v));
     }
     p = wave_md(p);
     p = group_md(p, rl.nw, rl.w, rl.lane, slots, parity);
     parity ^= 1;
     const float inv_d = (p.m == kNegInf) ? __builtin_nanf("") : 1.0f / p.d;
+    const float ld = LOG ? __builtin_logf(p.d) : 0.0f;
     for (int vi = rl.t; vi < nvec; vi += rl.T) {
       float v[VEC];
-      load_vec<Tin, VEC>(x + off + (int64_t)vi * VEC, v);
+      if (vi < nvec_keys) {
+        load_vec<Tin, VEC>(x + off + (int64_t)vi * VEC, v);
+        mask_keys<VEC>(v, vi * VEC, keys);
+      } else {
 #pragma unroll
-      for (int i = 0; i < VEC; ++i) v[i] = exp_shifted(v[i] - p.m) * inv_d;
+        for (int i = 0; i < VEC; ++i) v[i] = kNegInf;
+      }
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) v[i] = LOG ? (v[i] - p.m) - ld : exp_shifted(v[i] - p.m) * inv_d;
       store_vec<Tout, VEC>(y + off + (int64_t)vi * VEC, v);
     }
   }
@@ -720,7 +775,7 @@ __global__ __launch_bounds__(256) void softmax_split_stats_kernel(const Tin* x, 
   }
 }
 
-template <typename Tin, typename Tout, int NV>
+template <typename Tin, typename Tout, int NV, bool LOG>
 __global__ __launch_bounds__(256) void softmax_split_apply_kernel(const Tin* x, Tout* y,
                                                                   const SplitSlot* __restrict__ ws,
                                                                   int64_t M, int N, int S) {
@@ -752,12 +807,14 @@ __global__ __launch_bounds__(256) void softmax_split_apply_kernel(const Tin* x, 
     }
     p = wave_md(p);
     const float inv_d = (p.m == kNegInf) ? __builtin_nanf("") : 1.0f / p.d;
+    const float ld = LOG ? __builtin_logf(p.d) : 0.0f;
 #pragma unroll
     for (int k = 0; k < NV; ++k) {
       const int vi = c * CV + k * kThreads + rl.t;
       float o[VEC];
 #pragma unroll
-      for (int i = 0; i < VEC; ++i) o[i] = exp_shifted(v[k].get(i) - p.m) * inv_d;
+      for (int i = 0; i < VEC; ++i)
+        o[i] = LOG ? (v[k].get(i) - p.m) - ld : exp_shifted(v[k].get(i) - p.m) * inv_d;
       // plain (write-back) stores: measured faster than non-temporal ones here
       if (vi < nvec) store_vec<Tout, VEC, false>(y + off + (int64_t)vi * VEC, o);
     }
@@ -974,18 +1031,30 @@ hipError_t norm_typed(const rr_plan& p, int kind, const NormArgs& a, int64_t gri
   }
 }
 
-template <typename Tin, typename Tout, bool WAVE>
-hipError_t softmax_regs(const rr_plan& p, const Tin* xx, Tout* yy, int64_t M, int N, int64_t grid,
-                        hipStream_t s) {
+// One softmax launch: typed pointers plus the row rule (causal period cp,
+// offset co; cp == 0 keeps every key).
+template <typename Tin, typename Tout>
+struct SmCall {
+  const Tin* x;
+  Tout* y;
+  int64_t M;
+  int N;
+  int64_t cp;
+  int64_t co;
+};
+
+template <typename Tin, typename Tout, bool WAVE, bool LOG>
+hipError_t softmax_regs(const rr_plan& p, const SmCall<Tin, Tout>& c, int64_t grid, hipStream_t s) {
   const dim3 b(p.block_threads);
+  const dim3 g = grid1(grid);
   // At most 32 values per lane (NV * VEC <= 32).
   switch (p.vecs_per_lane) {
-    case 1: softmax_regs_kernel<Tin, Tout, 1, WAVE><<<grid1(grid), b, 0, s>>>(xx, yy, M, N); break;
-    case 2: softmax_regs_kernel<Tin, Tout, 2, WAVE><<<grid1(grid), b, 0, s>>>(xx, yy, M, N); break;
-    case 4: softmax_regs_kernel<Tin, Tout, 4, WAVE><<<grid1(grid), b, 0, s>>>(xx, yy, M, N); break;
+    case 1: softmax_regs_kernel<Tin, Tout, 1, WAVE, LOG><<<g, b, 0, s>>>(c.x, c.y, c.M, c.N, c.cp, c.co); break;
+    case 2: softmax_regs_kernel<Tin, Tout, 2, WAVE, LOG><<<g, b, 0, s>>>(c.x, c.y, c.M, c.N, c.cp, c.co); break;
+    case 4: softmax_regs_kernel<Tin, Tout, 4, WAVE, LOG><<<g, b, 0, s>>>(c.x, c.y, c.M, c.N, c.cp, c.co); break;
     case 8:
       if constexpr (Elem<Tin>::kVec * 8 <= 32) {
-        softmax_regs_kernel<Tin, Tout, 8, WAVE><<<grid1(grid), b, 0, s>>>(xx, yy, M, N);
+        softmax_regs_kernel<Tin, Tout, 8, WAVE, LOG><<<g, b, 0, s>>>(c.x, c.y, c.M, c.N, c.cp, c.co);
         break;
       }
       return hipErrorInvalidValue;
@@ -1025,84 +1094,102 @@ uint64_t next_split_tag() {
 // SPLIT: the two-kernel form.  SPLIT_ONE_KERNEL: one cooperative kernel
 // when the device can hold at least a row's chunks at once, else the two
 // kernels.  Both use the same chunks and the same merge order, so they give
-// the same bits.
-template <typename Tin, typename Tout, int NV>
-hipError_t softmax_split(const rr_plan& p, const Tin* xx, Tout* yy, SplitSlot* w, int64_t M, int N,
-                         int S, int64_t grid, hipStream_t s) {
+// the same bits.  Log-softmax always takes the two kernels.  The split
+// forms keep every key (the planner never splits a causal call).
+template <typename Tin, typename Tout, int NV, bool LOG>
+hipError_t softmax_split(const rr_plan& p, const SmCall<Tin, Tout>& c, SplitSlot* w, int S,
+                         int64_t grid, hipStream_t s) {
   const dim3 b(p.block_threads);
-  if (p.variant == RR_VARIANT_SPLIT_ONE_KERNEL) {
-    const void* k = reinterpret_cast<const void*>(&softmax_split_fused_kernel<Tin, Tout, NV>);
-    const int cap = cooperative_capacity(k);
-    if (cap >= S) {
-      const int64_t g = grid < cap ? grid : cap;
-      uint64_t tag = next_split_tag();
-      int64_t m64 = M;
-      void* args[] = {(void*)&xx, (void*)&yy, (void*)&w, (void*)&m64, (void*)&N, (void*)&S, (void*)&tag};
-      return hipLaunchCooperativeKernel(k, grid1(g), b, args, 0, s);
+  if (c.cp > 0) return hipErrorInvalidValue;
+  if constexpr (!LOG) {
+    if (p.variant == RR_VARIANT_SPLIT_ONE_KERNEL) {
+      const void* k = reinterpret_cast<const void*>(&softmax_split_fused_kernel<Tin, Tout, NV>);
+      const int cap = cooperative_capacity(k);
+      if (cap >= S) {
+        const int64_t g = grid < cap ? grid : cap;
+        uint64_t tag = next_split_tag();
+        const Tin* xx = c.x;
+        Tout* yy = c.y;
+        int64_t m64 = c.M;
+        int n32 = c.N;
+        void* args[] = {(void*)&xx, (void*)&yy, (void*)&w, (void*)&m64, (void*)&n32, (void*)&S, (void*)&tag};
+        return hipLaunchCooperativeKernel(k, grid1(g), b, args, 0, s);
+      }
     }
   }
-  softmax_split_stats_kernel<Tin, NV><<<grid1(grid), b, 0, s>>>(xx, w, M, N, S);
-  softmax_split_apply_kernel<Tin, Tout, NV><<<grid1(grid), b, 0, s>>>(xx, yy, w, M, N, S);
+  softmax_split_stats_kernel<Tin, NV><<<grid1(grid), b, 0, s>>>(c.x, w, c.M, c.N, S);
+  softmax_split_apply_kernel<Tin, Tout, NV, LOG><<<grid1(grid), b, 0, s>>>(c.x, c.y, w, c.M, c.N, S);
   return hipGetLastError();
 }
 
-template <typename Tin, typename Tout, int VEC>
-hipError_t softmax_sub(const rr_plan& p, const Tin* xx, Tout* yy, int64_t M, int N, int64_t grid,
-                       hipStream_t s) {
+template <typename Tin, typename Tout, int VEC, bool LOG>
+hipError_t softmax_sub(const rr_plan& p, const SmCall<Tin, Tout>& c, int64_t grid, hipStream_t s) {
   const dim3 b(256);
+  const dim3 g = grid1(grid);
   switch (p.waves_per_row) {  // for SUBWAVE: lanes per row
-    case 1: softmax_sub_kernel<Tin, Tout, VEC, 1><<<grid1(grid), b, 0, s>>>(xx, yy, M, N); break;
-    case 2: softmax_sub_kernel<Tin, Tout, VEC, 2><<<grid1(grid), b, 0, s>>>(xx, yy, M, N); break;
-    case 4: softmax_sub_kernel<Tin, Tout, VEC, 4><<<grid1(grid), b, 0, s>>>(xx, yy, M, N); break;
-    case 8: softmax_sub_kernel<Tin, Tout, VEC, 8><<<grid1(grid), b, 0, s>>>(xx, yy, M, N); break;
-    case 16: softmax_sub_kernel<Tin, Tout, VEC, 16><<<grid1(grid), b, 0, s>>>(xx, yy, M, N); break;
-    case 32: softmax_sub_kernel<Tin, Tout, VEC, 32><<<grid1(grid), b, 0, s>>>(xx, yy, M, N); break;
+    case 1: softmax_sub_kernel<Tin, Tout, VEC, 1, LOG><<<g, b, 0, s>>>(c.x, c.y, c.M, c.N, c.cp, c.co); break;
+    case 2: softmax_sub_kernel<Tin, Tout, VEC, 2, LOG><<<g, b, 0, s>>>(c.x, c.y, c.M, c.N, c.cp, c.co); break;
+    case 4: softmax_sub_kernel<Tin, Tout, VEC, 4, LOG><<<g, b, 0, s>>>(c.x, c.y, c.M, c.N, c.cp, c.co); break;
+    case 8: softmax_sub_kernel<Tin, Tout, VEC, 8, LOG><<<g, b, 0, s>>>(c.x, c.y, c.M, c.N, c.cp, c.co); break;
+    case 16: softmax_sub_kernel<Tin, Tout, VEC, 16, LOG><<<g, b, 0, s>>>(c.x, c.y, c.M, c.N, c.cp, c.co); break;
+    case 32: softmax_sub_kernel<Tin, Tout, VEC, 32, LOG><<<g, b, 0, s>>>(c.x, c.y, c.M, c.N, c.cp, c.co); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
-template <typename Tin, typename Tout>
-hipError_t softmax_typed(const rr_plan& p, void* y, const void* x, void* ws, int64_t M, int N,
-                         int64_t grid, hipStream_t s) {
-  const Tin* xx = static_cast<const Tin*>(x);
-  Tout* yy = static_cast<Tout*>(y);
+template <typename Tin, typename Tout, bool LOG>
+hipError_t softmax_typed(const rr_plan& p, const SmCall<Tin, Tout>& c, void* ws, int64_t grid,
+                         hipStream_t s) {
   const dim3 b(p.block_threads);
+  const dim3 g = grid1(grid);
   if (p.variant == RR_VARIANT_SUBWAVE) {
-    if (p.vec_elems == 1) return softmax_sub<Tin, Tout, 1>(p, xx, yy, M, N, grid, s);
-    return softmax_sub<Tin, Tout, Elem<Tin>::kVec>(p, xx, yy, M, N, grid, s);
+    if (p.vec_elems == 1) return softmax_sub<Tin, Tout, 1, LOG>(p, c, grid, s);
+    return softmax_sub<Tin, Tout, Elem<Tin>::kVec, LOG>(p, c, grid, s);
   }
   if (p.variant == RR_VARIANT_LOOP) {
     if (p.vec_elems == 1)
-      softmax_loop_kernel<Tin, Tout, 1><<<grid1(grid), b, 0, s>>>(xx, yy, M, N);
+      softmax_loop_kernel<Tin, Tout, 1, LOG><<<g, b, 0, s>>>(c.x, c.y, c.M, c.N, c.cp, c.co);
     else
-      softmax_loop_kernel<Tin, Tout, Elem<Tin>::kVec><<<grid1(grid), b, 0, s>>>(xx, yy, M, N);
+      softmax_loop_kernel<Tin, Tout, Elem<Tin>::kVec, LOG><<<g, b, 0, s>>>(c.x, c.y, c.M, c.N, c.cp, c.co);
     return hipGetLastError();
   }
   if (p.variant == RR_VARIANT_SPLIT || p.variant == RR_VARIANT_SPLIT_ONE_KERNEL) {
     SplitSlot* w = static_cast<SplitSlot*>(ws);
     const int S = (int)p.chunks_per_row;
     switch (p.vecs_per_lane) {
-      case 2: return softmax_split<Tin, Tout, 2>(p, xx, yy, w, M, N, S, grid, s);
-      case 4: return softmax_split<Tin, Tout, 4>(p, xx, yy, w, M, N, S, grid, s);
-      case 8: return softmax_split<Tin, Tout, 8>(p, xx, yy, w, M, N, S, grid, s);
+      case 2: return softmax_split<Tin, Tout, 2, LOG>(p, c, w, S, grid, s);
+      case 4: return softmax_split<Tin, Tout, 4, LOG>(p, c, w, S, grid, s);
+      case 8: return softmax_split<Tin, Tout, 8, LOG>(p, c, w, S, grid, s);
       default: return hipErrorInvalidValue;
     }
   }
-  if (p.variant == RR_VARIANT_WAVE) return softmax_regs<Tin, Tout, true>(p, xx, yy, M, N, grid, s);
+  if (p.variant == RR_VARIANT_WAVE) return softmax_regs<Tin, Tout, true, LOG>(p, c, grid, s);
   if (p.vecs_per_lane * Elem<Tin>::kVec > 32) {
     // long rows held in their storage format (see softmax_packed_kernel)
-    const dim3 b(p.block_threads);
     switch (p.vecs_per_lane) {
-      case 12: softmax_packed_kernel<Tin, Tout, 12><<<grid1(grid), b, 0, s>>>(xx, yy, M, N); break;
-      case 16: softmax_packed_kernel<Tin, Tout, 16><<<grid1(grid), b, 0, s>>>(xx, yy, M, N); break;
-      case 19: softmax_packed_kernel<Tin, Tout, 19><<<grid1(grid), b, 0, s>>>(xx, yy, M, N); break;
-      case 20: softmax_packed_kernel<Tin, Tout, 20><<<grid1(grid), b, 0, s>>>(xx, yy, M, N); break;
+      case 12: softmax_packed_kernel<Tin, Tout, 12, LOG><<<g, b, 0, s>>>(c.x, c.y, c.M, c.N, c.cp, c.co); break;
+      case 16: softmax_packed_kernel<Tin, Tout, 16, LOG><<<g, b, 0, s>>>(c.x, c.y, c.M, c.N, c.cp, c.co); break;
+      case 19: softmax_packed_kernel<Tin, Tout, 19, LOG><<<g, b, 0, s>>>(c.x, c.y, c.M, c.N, c.cp, c.co); break;
+      case 20: softmax_packed_kernel<Tin, Tout, 20, LOG><<<g, b, 0, s>>>(c.x, c.y, c.M, c.N, c.cp, c.co); break;
       default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
   }
-  return softmax_regs<Tin, Tout, false>(p, xx, yy, M, N, grid, s);
+  return softmax_regs<Tin, Tout, false, LOG>(p, c, grid, s);
+}
+
+template <typename Tin, typename Tout>
+hipError_t softmax_io(const rr_plan& p, const SoftmaxArgs& a, int64_t grid, hipStream_t s) {
+  SmCall<Tin, Tout> c;
+  c.x = static_cast<const Tin*>(a.x);
+  c.y = static_cast<Tout*>(a.y);
+  c.M = a.M;
+  c.N = a.N;
+  c.cp = a.causal_period;
+  c.co = a.causal_offset;
+  if (a.log_output) return softmax_typed<Tin, Tout, true>(p, c, a.workspace, grid, s);
+  return softmax_typed<Tin, Tout, false>(p, c, a.workspace, grid, s);
 }
 
 }  // namespace
@@ -1113,15 +1200,14 @@ hipError_t launch_norm(const rr_plan& plan, rr_dtype dtype, int kind, const Norm
   return norm_typed<bf16_t>(plan, kind, args, grid, stream);
 }
 
-hipError_t launch_softmax(const rr_plan& plan, rr_dtype in_dtype, rr_dtype out_dtype, void* y,
-                          const void* x, void* workspace, int64_t M, int32_t N, int64_t grid,
-                          hipStream_t stream) {
+hipError_t launch_softmax(const rr_plan& plan, rr_dtype in_dtype, rr_dtype out_dtype,
+                          const SoftmaxArgs& args, int64_t grid, hipStream_t stream) {
   if (in_dtype == RR_F32) {
-    if (out_dtype == RR_F32) return softmax_typed<float, float>(plan, y, x, workspace, M, N, grid, stream);
-    return softmax_typed<float, bf16_t>(plan, y, x, workspace, M, N, grid, stream);
+    if (out_dtype == RR_F32) return softmax_io<float, float>(plan, args, grid, stream);
+    return softmax_io<float, bf16_t>(plan, args, grid, stream);
   }
-  if (out_dtype == RR_F32) return softmax_typed<bf16_t, float>(plan, y, x, workspace, M, N, grid, stream);
-  return softmax_typed<bf16_t, bf16_t>(plan, y, x, workspace, M, N, grid, stream);
+  if (out_dtype == RR_F32) return softmax_io<bf16_t, float>(plan, args, grid, stream);
+  return softmax_io<bf16_t, bf16_t>(plan, args, grid, stream);
 }
 
 hipError_t launch_selftest_wave(const float* in, float* out, int64_t count, int kind,

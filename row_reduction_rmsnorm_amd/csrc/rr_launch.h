@@ -36,10 +36,22 @@ constexpr int kLaunchLayer = 2;
 hipError_t launch_norm(const rr_plan& plan, rr_dtype dtype, int kind, const NormArgs& args,
                        int64_t grid, hipStream_t stream);
 
+// Arguments of the softmax kernels.  causal_period == 0 keeps every key;
+// otherwise row r keeps keys j <= (r mod causal_period) + causal_offset.
+struct SoftmaxArgs {
+  void* y;
+  const void* x;
+  void* workspace;
+  int64_t M;
+  int32_t N;
+  int64_t causal_period;
+  int64_t causal_offset;
+  int log_output;
+};
+
 // Enqueue the softmax kernel(s) that `plan` names (two for SPLIT).
-hipError_t launch_softmax(const rr_plan& plan, rr_dtype in_dtype, rr_dtype out_dtype, void* y,
-                          const void* x, void* workspace, int64_t M, int32_t N, int64_t grid,
-                          hipStream_t stream);
+hipError_t launch_softmax(const rr_plan& plan, rr_dtype in_dtype, rr_dtype out_dtype,
+                          const SoftmaxArgs& args, int64_t grid, hipStream_t stream);
 
 // Enqueue the wave all-reduce self-test kernel.
 hipError_t launch_selftest_wave(const float* in, float* out, int64_t count, int kind,

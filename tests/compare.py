@@ -9,6 +9,14 @@ Bars (stated once here, used by every parity test):
     nearest even), measured as a distance between order-preserving integer
     images of the bit patterns, with +0 and -0 equal.
   * bf16 residual_out of the fused op: bit-exact (the rounded sum is unique).
+  * log-softmax: the output is (x - m) - log(d).  The subtraction x - m
+    and the final subtraction each round once (relative 2^-24 of their
+    results); log(d) carries the relative error of d as an absolute error,
+    which is the error the softmax bar allows on a probability near 1.
+    fp32: |g - r| <= 4e-6 + 1e-6 |r|; masked (-inf) inputs give exactly
+    -inf; fully masked rows give NaN.  bf16 output: at most 1 ulp from
+    RNE_bf16(r), or within the fp32 bar (outputs near 0, where a bf16 ulp
+    is smaller than the fp32 error of log(d)).
   * LayerNorm (f3): the output is (x - mean) * rstd * gamma + beta, so a
     kernel's error scales with the row's spread, i.e. with |gamma_j| (1 + |z|)
     where z is the normalised value, not with |y| itself (y is near beta for
@@ -138,3 +146,38 @@ def check_layernorm(got_tensor, ref_f64: np.ndarray, gamma_f64: np.ndarray, beta
     worst = float(err.max())
     assert worst <= LN_TOL, f"{what}: scaled error {worst:.3e} > {LN_TOL}"
     return {"max_scaled_err": worst}
+
+
+LOGSM_ATOL = 4e-6
+LOGSM_RTOL = 1e-6
+
+
+def check_log_softmax(got_tensor, x_f64: np.ndarray, ref_f64: np.ndarray, what: str):
+    import torch
+    g = to_f64(got_tensor).reshape(ref_f64.shape)
+    nan_rows = np.all(np.isneginf(x_f64), axis=1)
+    if nan_rows.any():
+        assert np.all(np.isnan(g[nan_rows])), f"{what}: fully masked rows must be NaN"
+    ok = ~nan_rows
+    gk, rk, xk = g[ok], ref_f64[ok], x_f64[ok]
+    masked = np.isneginf(xk)
+    assert np.all(np.isneginf(gk[masked])), f"{what}: masked entry not exactly -inf"
+    kept = ~masked
+    gv, rv = gk[kept], rk[kept]
+    assert np.all(np.isfinite(gv)), f"{what}: non-finite log-probability"
+    bar = LOGSM_ATOL + LOGSM_RTOL * np.abs(rv)
+    err = np.abs(gv - rv)
+    if got_tensor.dtype == torch.bfloat16:
+        ref_bits = bf16_bits_of_values(oracle.round_bf16(rv))
+        got_bits = bf16_bits_of_tensor(got_tensor).reshape(ref_f64.shape)[ok][kept]
+        dist = bf16_ulp_distance(got_bits, ref_bits)
+        bad = (dist > BF16_MAX_ULP) & (err > bar)
+        assert not bad.any(), f"{what}: {int(bad.sum())} outputs beyond 1 ulp and the fp32 bar"
+        return {"max_ulp": int(dist.max()) if dist.size else 0, "rows": int(ref_f64.shape[0])}
+    worst = float((err / bar).max()) if err.size else 0.0
+    assert worst <= 1.0, f"{what}: error {worst:.3f} x the bar (max abs {float(err.max()):.3e})"
+    # exp of the output is the softmax: its rows sum to 1
+    rs = np.abs(np.exp(gk).sum(axis=1) - 1.0)
+    if rs.size:
+        assert rs.max() <= SOFTMAX_ROWSUM_ATOL, f"{what}: exp rows sum off by {rs.max():.3e}"
+    return {"max_abs": float(err.max()) if err.size else 0.0, "rows": int(ref_f64.shape[0])}

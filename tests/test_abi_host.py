@@ -117,6 +117,64 @@ def test_softmax_validation():
     assert "workspace" in rr.last_error_message()
 
 
+def test_softmax_ex_validation():
+    X, Y, W = P, P << 4, P << 8
+    F, B = rr.RR_F32, rr.RR_BF16
+    f = rr.raw_softmax_rows_ex
+    o = rr.make_softmax_opts
+    # flags outside {0, 1}
+    bad = o()
+    bad.log_output = 2
+    assert f(Y, X, 4, 8, F, F, bad, None, 0, None) == rr.RR_ERR_INVALID_ARG
+    assert "log_output" in rr.last_error_message()
+    bad = o()
+    bad.causal = -1
+    assert f(Y, X, 4, 8, F, F, bad, None, 0, None) == rr.RR_ERR_INVALID_ARG
+    # causal rule bounds
+    assert f(Y, X, 4, 8, F, F, o(causal_period=0), None, 0, None) == rr.RR_ERR_INVALID_ARG
+    assert "causal_period" in rr.last_error_message()
+    assert f(Y, X, 4, 8, F, F, o(causal_period=4, causal_offset=-1), None, 0, None) == rr.RR_ERR_INVALID_ARG
+    assert "causal_offset" in rr.last_error_message()
+    # period and offset are ignored without the causal flag
+    ign = o()
+    ign.causal_period, ign.causal_offset = -5, -5
+    assert f(Y, X, 0, 8, F, F, ign, None, 0, None) == rr.RR_OK
+    # the plain checks still apply
+    assert f(Y, X, 4, 0, F, F, None, None, 0, None) == rr.RR_ERR_INVALID_ARG
+    assert f(X, X, 4, 8, B, F, o(log_output=True), None, 0, None) == rr.RR_ERR_INVALID_ARG
+    # an empty batch succeeds before the options' pointers are needed
+    assert f(None, None, 0, 8, F, F, o(causal_period=3), None, 0, None) == rr.RR_OK
+    # log-softmax of few long rows splits like softmax and needs the workspace
+    need = rr.rr_softmax_rows_ex_workspace_bytes(256, 152064, B, F, o(log_output=True))
+    assert need == rr.rr_softmax_rows_workspace_bytes(256, 152064, B, F) == 256 * 19 * 16
+    assert f(Y, X, 256, 152064, B, F, o(log_output=True), None, 0, None) == rr.RR_ERR_WORKSPACE
+    # a causal call never splits, so it needs no workspace
+    assert rr.rr_softmax_rows_ex_workspace_bytes(256, 152064, B, F, o(causal_period=256)) == 0
+    assert rr.rr_softmax_rows_ex_workspace_bytes(256, 152064, B, F, None) == need
+    assert rr.rr_softmax_rows_ex_workspace_bytes(4, 8, F, F, o(causal_period=0)) == 0
+
+
+def test_softmax_causal_plans():
+    S, C, F, B = rr.RR_OP_SOFTMAX, rr.RR_OP_SOFTMAX_CAUSAL, rr.RR_F32, rr.RR_BF16
+    q = lambda op, M, N, a=F, b=F: rr.rr_query_plan(op, M, N, a, b)
+    # rows that fit registers keep the softmax plan
+    for M, N in ((28 * 4096, 4096), (16384, 1024), (10, 64), (1024, 40000)):
+        assert q(C, M, N) == q(S, M, N)
+    # where softmax would split, the causal call streams instead
+    assert q(S, 256, 152064, B, F)["variant_name"] == "split"
+    p = q(C, 256, 152064, B, F)
+    assert p["variant_name"] == "loop" and p["workspace_bytes"] == 0
+    try:
+        rr.rr_set_variant_override(rr.RR_VARIANT_SPLIT)
+        with pytest.raises(rr.RowReduceError):
+            q(C, 10, 1024)
+        assert q(S, 10, 1024)["variant_name"] == "split"
+        rr.rr_set_variant_override(rr.RR_VARIANT_LOOP)
+        assert q(C, 10, 1024)["variant_name"] == "loop"
+    finally:
+        rr.rr_set_variant_override(rr.RR_VARIANT_AUTO)
+
+
 # ----------------------------------------------------------------------------
 # dispatch (the variant choice by row length)
 # ----------------------------------------------------------------------------
