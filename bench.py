@@ -170,13 +170,17 @@ def cpu_baseline(bufs, fraction):
     }
 
 
-def measure_extras(torch, rr, dev, K):
+def measure_extras(torch, rr, dev, K, bufs):
     """Operations outside the step, each timed on its own (K launches between
     two events, after a warm-up launch): the 64 x 3584 fp32 RMSNorm (64 rows on
     256 CUs: a latency case, reported as time and rows/s), LayerNorm at the
-    LayerNorm exercise's 256 x 5120 fp32 shape, and LayerNorm bf16 8192 x 4096
-    (the RMSNorm workload's shape, for bandwidth).  Inputs stay cached between
-    launches here (the largest is 134 MB), so these are not HBM-cold figures."""
+    LayerNorm exercise's 256 x 5120 fp32 shape, LayerNorm bf16 8192 x 4096
+    (the RMSNorm workload's shape, for bandwidth), the attention-score softmax
+    through the causal rule (only the kept keys are read: row i of a head reads
+    i + 1 keys and writes all 4096), and log-softmax on the vocabulary logits.
+    The LayerNorm and RMSNorm inputs stay cached between launches (the largest
+    is 134 MB), so those are not HBM-cold figures; the causal softmax moves
+    2.8 GB per launch and the log-softmax 234 MB."""
     import numpy as np
     import workloads
     out = {}
@@ -212,6 +216,17 @@ def measure_extras(torch, rr, dev, K):
     y = torch.empty_like(x)
     timed("layernorm_bf16_8192x4096", lambda: rr.rr_layernorm(y, x, g, bt, 1e-5),
           2 * M * N * 2 + 2 * N * 2, M)
+    del x, g, bt, y
+    b = bufs["sm_causal"]
+    M, N = b["M"], b["N"]
+    kept = int(np.minimum(N, np.arange(M) % 4096 + 1).sum())
+    causal = rr.make_softmax_opts(causal_period=4096, causal_offset=0)
+    timed("causal_softmax_f32_114688x4096_kept_keys_only",
+          lambda: rr.rr_softmax_rows_ex(b["y"], b["x"], causal, None), kept * 4 + M * N * 4, M)
+    b = bufs["sm_vocab"]
+    lg = rr.make_softmax_opts(log_output=True)
+    timed("log_softmax_bf16_f32_256x152064",
+          lambda: rr.rr_softmax_rows_ex(b["y"], b["x"], lg, b["ws"]), b["M"] * b["N"] * (2 + 4), b["M"])
     return out
 
 
@@ -325,7 +340,7 @@ def main():
                 "us_per_launch": round(per_op_ms[dom] * 1e3, 2),
                 "plan": plan["variant_name"] if plan else None}
 
-    extras = measure_extras(torch, rr, dev, K)
+    extras = measure_extras(torch, rr, dev, K, bufs)
 
     cpu = None
     if not args.no_cpu_baseline:

@@ -86,19 +86,39 @@ __device__ __forceinline__ MD group_md(MD v, int nw, int w, int lane,
   return md_merge(t, dpp_md<kDppRowMirror>(t));
 }
 
-// Keys row `row` keeps: all N, or under the causal rule (period cp >= 1)
-// those with index j <= (row mod cp) + co, i.e. min(N, (row mod cp) + co + 1).
-__device__ __forceinline__ int row_keys(int64_t row, int N, int64_t cp, int64_t co) {
-  if (cp <= 0) return N;
-  const int64_t k = row % cp + co + 1;
-  return k < (int64_t)N ? (int)k : N;
-}
+// The causal rule along a thread's rows: with period cp >= 1, row r keeps
+// the keys j <= (r mod cp) + co, i.e. min(N, (r mod cp) + co + 1); cp == 0
+// keeps every key.  A thread visits rows row0, row0 + stride, ...; the
+// residue r mod cp is carried from row to row by one add and one compare,
+// so the only division happens once, before the row loop.
+struct CausalRows {
+  int64_t cp, co, q, step;
+  __device__ __forceinline__ CausalRows(int64_t row0, int64_t stride, int64_t cp_, int64_t co_)
+      : cp(cp_), co(co_), q(0), step(0) {
+    if (cp > 0) {
+      q = row0 % cp;
+      step = stride % cp;
+    }
+  }
+  __device__ __forceinline__ int keys(int N) const {
+    if (cp <= 0) return N;
+    const int64_t k = q + co + 1;
+    return k < (int64_t)N ? (int)k : N;
+  }
+  __device__ __forceinline__ void next() {
+    if (cp > 0) {
+      q += step;
+      if (q >= cp) q -= cp;
+    }
+  }
+};
 
 // Entries of the vector starting at element e0 that lie at or past `keys`
 // become -inf (they are masked keys; only the vector holding the last kept
 // key can contain any).
 template <int VEC>
 __device__ __forceinline__ void mask_keys(float (&v)[VEC], int e0, int keys) {
+  if (e0 + VEC <= keys) return;   // the whole vector is kept (always, without the rule)
 #pragma unroll
   for (int i = 0; i < VEC; ++i)
     if (e0 + i >= keys) v[i] = kNegInf;
@@ -441,15 +461,17 @@ __global__ __launch_bounds__(256) void norm_sub_kernel(T* y, T* residual, const 
   }
 }
 
-template <typename Tin, typename Tout, int VEC, int L, bool LOG>
+template <typename Tin, typename Tout, int VEC, int L, bool LOG, bool CAUSAL>
 __global__ __launch_bounds__(256) void softmax_sub_kernel(const Tin* x, Tout* y, int64_t M, int N,
                                                           int64_t cp, int64_t co) {
   constexpr int kRowsPerGroup = 256 / L;
   const int j = threadIdx.x & (L - 1);
   const int nvec = N / VEC;
-  for (int64_t row = (int64_t)blockIdx.x * kRowsPerGroup + (threadIdx.x / L); row < M;
-       row += (int64_t)gridDim.x * kRowsPerGroup) {
-    const int keys = row_keys(row, N, cp, co);
+  const int64_t row0 = (int64_t)blockIdx.x * kRowsPerGroup + (threadIdx.x / L);
+  const int64_t stride = (int64_t)gridDim.x * kRowsPerGroup;
+  CausalRows cr(row0, stride, CAUSAL ? cp : 0, co);
+  for (int64_t row = row0; row < M; row += stride, cr.next()) {
+    const int keys = cr.keys(N);
     const int64_t off = row * (int64_t)N + (int64_t)j * VEC;
     float v[VEC];
     if (j * VEC < keys) {
@@ -505,7 +527,7 @@ __global__ __launch_bounds__(256) void softmax_sub_kernel(const Tin* x, Tout* y,
 // entries are all -inf has m_l = -inf and c_l = 0; a row whose entries are
 // all -inf has m = -inf and every output is NaN, as exp(x - m)/d is.
 // ===========================================================================
-template <typename Tin, typename Tout, int NV, bool WAVE, bool LOG>
+template <typename Tin, typename Tout, int NV, bool WAVE, bool LOG, bool CAUSAL>
 __global__ __launch_bounds__(1024) void softmax_regs_kernel(const Tin* x, Tout* y, int64_t M,
                                                             int N, int64_t cp, int64_t co) {
   constexpr int VEC = Elem<Tin>::kVec;
@@ -513,9 +535,11 @@ __global__ __launch_bounds__(1024) void softmax_regs_kernel(const Tin* x, Tout* 
   const RowLane rl = row_lane<WAVE>();
   const int nvec = N / VEC;
   const int64_t stride = (int64_t)gridDim.x * rl.rpg;
+  const int64_t row0 = (int64_t)blockIdx.x * rl.rpg + rl.g;
+  CausalRows cr(row0, stride, CAUSAL ? cp : 0, co);
   int parity = 0;
-  for (int64_t row = (int64_t)blockIdx.x * rl.rpg + rl.g; row < M; row += stride) {
-    const int keys = row_keys(row, N, cp, co);
+  for (int64_t row = row0; row < M; row += stride, cr.next()) {
+    const int keys = cr.keys(N);
     const int nvec_keys = (keys + VEC - 1) / VEC;   // vectors holding kept keys
     const int64_t off = row * (int64_t)N;
     float v[NV][VEC];
@@ -524,11 +548,16 @@ __global__ __launch_bounds__(1024) void softmax_regs_kernel(const Tin* x, Tout* 
       const int vi = k * rl.T + rl.t;
       if (vi < nvec_keys) {
         load_vec<Tin, VEC>(x + off + (int64_t)vi * VEC, v[k]);
-        mask_keys<VEC>(v[k], vi * VEC, keys);
       } else {
 #pragma unroll
         for (int i = 0; i < VEC; ++i) v[k][i] = kNegInf;
       }
+    }
+    // a row the causal rule cuts: keys past the count inside the vector
+    // holding the last kept key become -inf (after all loads are issued)
+    if (keys < N) {
+#pragma unroll
+      for (int k = 0; k < NV; ++k) mask_keys<VEC>(v[k], (k * rl.T + rl.t) * VEC, keys);
     }
     float ml = kNegInf;
 #pragma unroll
@@ -582,7 +611,7 @@ __global__ __launch_bounds__(1024) void softmax_regs_kernel(const Tin* x, Tout* 
 // bf16 row needs 19 vectors (76 VGPRs) per lane of a 1024-lane workgroup, one
 // workgroup per CU.
 // ===========================================================================
-template <typename Tin, typename Tout, int NV, bool LOG>
+template <typename Tin, typename Tout, int NV, bool LOG, bool CAUSAL>
 __global__ __launch_bounds__(1024) void softmax_packed_kernel(const Tin* x, Tout* y, int64_t M,
                                                               int N, int64_t cp, int64_t co) {
   constexpr int VEC = Elem<Tin>::kVec;
@@ -593,8 +622,9 @@ __global__ __launch_bounds__(1024) void softmax_packed_kernel(const Tin* x, Tout
   const int w = t >> 6;
   const int nvec = N / VEC;
   int parity = 0;
-  for (int64_t row = blockIdx.x; row < M; row += gridDim.x) {
-    const int keys = row_keys(row, N, cp, co);
+  CausalRows cr(blockIdx.x, gridDim.x, CAUSAL ? cp : 0, co);
+  for (int64_t row = blockIdx.x; row < M; row += gridDim.x, cr.next()) {
+    const int keys = cr.keys(N);
     const int nvec_keys = (keys + VEC - 1) / VEC;
     const Tin* xr = x + row * (int64_t)N;   // uniform row bases
     Tout* yr = y + row * (int64_t)N;
@@ -607,14 +637,16 @@ __global__ __launch_bounds__(1024) void softmax_packed_kernel(const Tin* x, Tout
 #pragma unroll
     for (int k = 0; k < NV; ++k) {
       const int vi = k * kThreads + t_ld;
-      if (vi < nvec_keys) {
-        v[k].template load<true>(xr + vi * VEC);
-        // keys past the row's count become -inf (only the vector holding
-        // the last kept key can contain any)
-        const int first = keys - vi * VEC;
-        if (first < VEC) v[k].mask_from(first);
-      } else {
-        v[k].fill(kNegInf);
+      if (vi < nvec_keys) v[k].template load<true>(xr + vi * VEC);
+      else v[k].fill(kNegInf);
+    }
+    // a row the causal rule cuts: keys past the count inside the vector
+    // holding the last kept key become -inf
+    if (keys < N) {
+#pragma unroll
+      for (int k = 0; k < NV; ++k) {
+        const int first = keys - (k * kThreads + t) * VEC;
+        if (first > 0 && first < VEC) v[k].mask_from(first);
       }
     }
     auto key = [&](int k, int i) { return v[k].get(i); };
@@ -664,15 +696,16 @@ __global__ __launch_bounds__(1024) void softmax_packed_kernel(const Tin* x, Tout
 // and writes exp(x - m) / d.  HBM traffic: two reads and one write per
 // element ([P2] section 七.3: "read twice, write once").
 // ===========================================================================
-template <typename Tin, typename Tout, int VEC, bool LOG>
+template <typename Tin, typename Tout, int VEC, bool LOG, bool CAUSAL>
 __global__ __launch_bounds__(1024) void softmax_loop_kernel(const Tin* x, Tout* y, int64_t M,
                                                             int N, int64_t cp, int64_t co) {
   __shared__ MD slots[2][kMaxWavesPerGroup];
   const RowLane rl = row_lane<false>();
   const int nvec = N / VEC;
   int parity = 0;
-  for (int64_t row = blockIdx.x; row < M; row += gridDim.x) {
-    const int keys = row_keys(row, N, cp, co);
+  CausalRows cr(blockIdx.x, gridDim.x, CAUSAL ? cp : 0, co);
+  for (int64_t row = blockIdx.x; row < M; row += gridDim.x, cr.next()) {
+    const int keys = cr.keys(N);
     const int nvec_keys = (keys + VEC - 1) / VEC;
     const int64_t off = row * (int64_t)N;
     MD p;
@@ -1043,18 +1076,18 @@ struct SmCall {
   int64_t co;
 };
 
-template <typename Tin, typename Tout, bool WAVE, bool LOG>
+template <typename Tin, typename Tout, bool WAVE, bool LOG, bool CAUSAL>
 hipError_t softmax_regs(const rr_plan& p, const SmCall<Tin, Tout>& c, int64_t grid, hipStream_t s) {
   const dim3 b(p.block_threads);
   const dim3 g = grid1(grid);
   // At most 32 values per lane (NV * VEC <= 32).
   switch (p.vecs_per_lane) {
-    case 1: softmax_regs_kernel<Tin, Tout, 1, WAVE, LOG><<<g, b, 0, s>>>(c.x, c.y, c.M, c.N, c.cp, c.co); break;
-    case 2: softmax_regs_kernel<Tin, Tout, 2, WAVE, LOG><<<g, b, 0, s>>>(c.x, c.y, c.M, c.N, c.cp, c.co); break;
-    case 4: softmax_regs_kernel<Tin, Tout, 4, WAVE, LOG><<<g, b, 0, s>>>(c.x, c.y, c.M, c.N, c.cp, c.co); break;
+    case 1: softmax_regs_kernel<Tin, Tout, 1, WAVE, LOG, CAUSAL><<<g, b, 0, s>>>(c.x, c.y, c.M, c.N, c.cp, c.co); break;
+    case 2: softmax_regs_kernel<Tin, Tout, 2, WAVE, LOG, CAUSAL><<<g, b, 0, s>>>(c.x, c.y, c.M, c.N, c.cp, c.co); break;
+    case 4: softmax_regs_kernel<Tin, Tout, 4, WAVE, LOG, CAUSAL><<<g, b, 0, s>>>(c.x, c.y, c.M, c.N, c.cp, c.co); break;
     case 8:
       if constexpr (Elem<Tin>::kVec * 8 <= 32) {
-        softmax_regs_kernel<Tin, Tout, 8, WAVE, LOG><<<g, b, 0, s>>>(c.x, c.y, c.M, c.N, c.cp, c.co);
+        softmax_regs_kernel<Tin, Tout, 8, WAVE, LOG, CAUSAL><<<g, b, 0, s>>>(c.x, c.y, c.M, c.N, c.cp, c.co);
         break;
       }
       return hipErrorInvalidValue;
@@ -1122,39 +1155,40 @@ hipError_t softmax_split(const rr_plan& p, const SmCall<Tin, Tout>& c, SplitSlot
   return hipGetLastError();
 }
 
-template <typename Tin, typename Tout, int VEC, bool LOG>
+template <typename Tin, typename Tout, int VEC, bool LOG, bool CAUSAL>
 hipError_t softmax_sub(const rr_plan& p, const SmCall<Tin, Tout>& c, int64_t grid, hipStream_t s) {
   const dim3 b(256);
   const dim3 g = grid1(grid);
   switch (p.waves_per_row) {  // for SUBWAVE: lanes per row
-    case 1: softmax_sub_kernel<Tin, Tout, VEC, 1, LOG><<<g, b, 0, s>>>(c.x, c.y, c.M, c.N, c.cp, c.co); break;
-    case 2: softmax_sub_kernel<Tin, Tout, VEC, 2, LOG><<<g, b, 0, s>>>(c.x, c.y, c.M, c.N, c.cp, c.co); break;
-    case 4: softmax_sub_kernel<Tin, Tout, VEC, 4, LOG><<<g, b, 0, s>>>(c.x, c.y, c.M, c.N, c.cp, c.co); break;
-    case 8: softmax_sub_kernel<Tin, Tout, VEC, 8, LOG><<<g, b, 0, s>>>(c.x, c.y, c.M, c.N, c.cp, c.co); break;
-    case 16: softmax_sub_kernel<Tin, Tout, VEC, 16, LOG><<<g, b, 0, s>>>(c.x, c.y, c.M, c.N, c.cp, c.co); break;
-    case 32: softmax_sub_kernel<Tin, Tout, VEC, 32, LOG><<<g, b, 0, s>>>(c.x, c.y, c.M, c.N, c.cp, c.co); break;
+    case 1: softmax_sub_kernel<Tin, Tout, VEC, 1, LOG, CAUSAL><<<g, b, 0, s>>>(c.x, c.y, c.M, c.N, c.cp, c.co); break;
+    case 2: softmax_sub_kernel<Tin, Tout, VEC, 2, LOG, CAUSAL><<<g, b, 0, s>>>(c.x, c.y, c.M, c.N, c.cp, c.co); break;
+    case 4: softmax_sub_kernel<Tin, Tout, VEC, 4, LOG, CAUSAL><<<g, b, 0, s>>>(c.x, c.y, c.M, c.N, c.cp, c.co); break;
+    case 8: softmax_sub_kernel<Tin, Tout, VEC, 8, LOG, CAUSAL><<<g, b, 0, s>>>(c.x, c.y, c.M, c.N, c.cp, c.co); break;
+    case 16: softmax_sub_kernel<Tin, Tout, VEC, 16, LOG, CAUSAL><<<g, b, 0, s>>>(c.x, c.y, c.M, c.N, c.cp, c.co); break;
+    case 32: softmax_sub_kernel<Tin, Tout, VEC, 32, LOG, CAUSAL><<<g, b, 0, s>>>(c.x, c.y, c.M, c.N, c.cp, c.co); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
-template <typename Tin, typename Tout, bool LOG>
+template <typename Tin, typename Tout, bool LOG, bool CAUSAL>
 hipError_t softmax_typed(const rr_plan& p, const SmCall<Tin, Tout>& c, void* ws, int64_t grid,
                          hipStream_t s) {
   const dim3 b(p.block_threads);
   const dim3 g = grid1(grid);
   if (p.variant == RR_VARIANT_SUBWAVE) {
-    if (p.vec_elems == 1) return softmax_sub<Tin, Tout, 1, LOG>(p, c, grid, s);
-    return softmax_sub<Tin, Tout, Elem<Tin>::kVec, LOG>(p, c, grid, s);
+    if (p.vec_elems == 1) return softmax_sub<Tin, Tout, 1, LOG, CAUSAL>(p, c, grid, s);
+    return softmax_sub<Tin, Tout, Elem<Tin>::kVec, LOG, CAUSAL>(p, c, grid, s);
   }
   if (p.variant == RR_VARIANT_LOOP) {
     if (p.vec_elems == 1)
-      softmax_loop_kernel<Tin, Tout, 1, LOG><<<g, b, 0, s>>>(c.x, c.y, c.M, c.N, c.cp, c.co);
+      softmax_loop_kernel<Tin, Tout, 1, LOG, CAUSAL><<<g, b, 0, s>>>(c.x, c.y, c.M, c.N, c.cp, c.co);
     else
-      softmax_loop_kernel<Tin, Tout, Elem<Tin>::kVec, LOG><<<g, b, 0, s>>>(c.x, c.y, c.M, c.N, c.cp, c.co);
+      softmax_loop_kernel<Tin, Tout, Elem<Tin>::kVec, LOG, CAUSAL><<<g, b, 0, s>>>(c.x, c.y, c.M, c.N, c.cp, c.co);
     return hipGetLastError();
   }
   if (p.variant == RR_VARIANT_SPLIT || p.variant == RR_VARIANT_SPLIT_ONE_KERNEL) {
+    if constexpr (CAUSAL) return hipErrorInvalidValue;   // the planner never splits a causal call
     SplitSlot* w = static_cast<SplitSlot*>(ws);
     const int S = (int)p.chunks_per_row;
     switch (p.vecs_per_lane) {
@@ -1164,19 +1198,19 @@ hipError_t softmax_typed(const rr_plan& p, const SmCall<Tin, Tout>& c, void* ws,
       default: return hipErrorInvalidValue;
     }
   }
-  if (p.variant == RR_VARIANT_WAVE) return softmax_regs<Tin, Tout, true, LOG>(p, c, grid, s);
+  if (p.variant == RR_VARIANT_WAVE) return softmax_regs<Tin, Tout, true, LOG, CAUSAL>(p, c, grid, s);
   if (p.vecs_per_lane * Elem<Tin>::kVec > 32) {
     // long rows held in their storage format (see softmax_packed_kernel)
     switch (p.vecs_per_lane) {
-      case 12: softmax_packed_kernel<Tin, Tout, 12, LOG><<<g, b, 0, s>>>(c.x, c.y, c.M, c.N, c.cp, c.co); break;
-      case 16: softmax_packed_kernel<Tin, Tout, 16, LOG><<<g, b, 0, s>>>(c.x, c.y, c.M, c.N, c.cp, c.co); break;
-      case 19: softmax_packed_kernel<Tin, Tout, 19, LOG><<<g, b, 0, s>>>(c.x, c.y, c.M, c.N, c.cp, c.co); break;
-      case 20: softmax_packed_kernel<Tin, Tout, 20, LOG><<<g, b, 0, s>>>(c.x, c.y, c.M, c.N, c.cp, c.co); break;
+      case 12: softmax_packed_kernel<Tin, Tout, 12, LOG, CAUSAL><<<g, b, 0, s>>>(c.x, c.y, c.M, c.N, c.cp, c.co); break;
+      case 16: softmax_packed_kernel<Tin, Tout, 16, LOG, CAUSAL><<<g, b, 0, s>>>(c.x, c.y, c.M, c.N, c.cp, c.co); break;
+      case 19: softmax_packed_kernel<Tin, Tout, 19, LOG, CAUSAL><<<g, b, 0, s>>>(c.x, c.y, c.M, c.N, c.cp, c.co); break;
+      case 20: softmax_packed_kernel<Tin, Tout, 20, LOG, CAUSAL><<<g, b, 0, s>>>(c.x, c.y, c.M, c.N, c.cp, c.co); break;
       default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
   }
-  return softmax_regs<Tin, Tout, false, LOG>(p, c, grid, s);
+  return softmax_regs<Tin, Tout, false, LOG, CAUSAL>(p, c, grid, s);
 }
 
 template <typename Tin, typename Tout>
@@ -1188,8 +1222,14 @@ hipError_t softmax_io(const rr_plan& p, const SoftmaxArgs& a, int64_t grid, hipS
   c.N = a.N;
   c.cp = a.causal_period;
   c.co = a.causal_offset;
-  if (a.log_output) return softmax_typed<Tin, Tout, true>(p, c, a.workspace, grid, s);
-  return softmax_typed<Tin, Tout, false>(p, c, a.workspace, grid, s);
+  // the causal rule and log output are compile-time switches, so the plain
+  // softmax kernels carry none of their code
+  if (c.cp > 0) {
+    if (a.log_output) return softmax_typed<Tin, Tout, true, true>(p, c, a.workspace, grid, s);
+    return softmax_typed<Tin, Tout, false, true>(p, c, a.workspace, grid, s);
+  }
+  if (a.log_output) return softmax_typed<Tin, Tout, true, false>(p, c, a.workspace, grid, s);
+  return softmax_typed<Tin, Tout, false, false>(p, c, a.workspace, grid, s);
 }
 
 }  // namespace
