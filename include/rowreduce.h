@@ -22,7 +22,8 @@
  *     (allocated on the device that is current when the call is made).  The
  *     library allocates nothing, frees nothing and keeps no per-call state.
  *   - Layout: row-major and contiguous; element (i, j) of an [M, N] matrix is
- *     at offset i * N + j; gamma is a vector of N (or H) elements.
+ *     at offset i * N + j; gamma is a vector of N (or H) elements.  The
+ *     *_strided entry points take a row stride per matrix instead.
  *   - dtype: RR_F32 (IEEE binary32) or RR_BF16 (bfloat16).  All arithmetic is
  *     fp32; bf16 inputs widen exactly and outputs round to nearest even once.
  *   - Streams: `stream` is a hipStream_t (NULL = the null stream).  Calls are
@@ -209,6 +210,43 @@ size_t rr_softmax_rows_ex_workspace_bytes(int64_t M, int64_t N, rr_dtype in_dtyp
 rr_status rr_softmax_rows_ex(void* y, const void* x, int64_t M, int64_t N, rr_dtype in_dtype,
                              rr_dtype out_dtype, const rr_softmax_opts* opts, void* workspace,
                              size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Strided rows.  The same operations on matrices whose rows are not packed
+ * back to back: row i of x starts at x + i * ldx elements (likewise y with
+ * ldy and the residual with ldr), as when x is a column slice of a wider
+ * activation (vLLM's normalisation kernels take such an input stride: [P2]
+ * section 九, the fused_add_rms_norm kernel's input_stride).  Every stride is
+ * in elements, at least the row width (H or N) and at most 2^40.  Vector
+ * (16-byte) accesses need every row start 16-byte aligned, i.e. aligned
+ * base pointers and strides that are multiples of 4 (fp32) or 8 (bf16)
+ * elements; otherwise the scalar path runs, with the same results up to
+ * rounding order.  With every stride equal to the width these are exactly
+ * the contiguous entry points above (same kernels, same bits).
+ * Aliasing: y may be x itself (same pointer and stride, same dtype); other
+ * matrices of a call must not share an element.  Two matrices with the same
+ * stride whose column windows are disjoint (two slices of one wider
+ * matrix) do not share one; other layouts count as overlapping when their
+ * first-to-last-byte spans intersect.  Errors as the contiguous forms, plus
+ * RR_ERR_INVALID_ARG for a stride out of range.
+ * ------------------------------------------------------------------------ */
+rr_status rr_rmsnorm_strided(void* y, int64_t ldy, const void* x, int64_t ldx, const void* gamma,
+                             int64_t M, int64_t H, float eps, rr_dtype dtype, void* stream);
+
+rr_status rr_fused_add_rmsnorm_strided(void* y, int64_t ldy, void* residual, int64_t ldr,
+                                       const void* x, int64_t ldx, const void* gamma, int64_t M,
+                                       int64_t H, float eps, rr_dtype dtype, void* stream);
+
+rr_status rr_layernorm_strided(void* y, int64_t ldy, const void* x, int64_t ldx, const void* gamma,
+                               const void* beta, int64_t M, int64_t H, float eps, rr_dtype dtype,
+                               void* stream);
+
+/* Workspace: rr_softmax_rows_ex_workspace_bytes(M, N, ...) with the same
+ * options (it does not depend on the strides). */
+rr_status rr_softmax_rows_strided(void* y, int64_t ldy, const void* x, int64_t ldx, int64_t M,
+                                  int64_t N, rr_dtype in_dtype, rr_dtype out_dtype,
+                                  const rr_softmax_opts* opts, void* workspace,
+                                  size_t workspace_bytes, void* stream);
 
 /* Static English name of a status code ("RR_OK", ...). */
 const char* rr_status_string(rr_status status);

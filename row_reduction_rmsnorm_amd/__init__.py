@@ -18,5 +18,8 @@ from .binding import (  # noqa: F401
     rr_query_plan, rr_rmsnorm, rr_selftest_wave_allreduce, rr_set_variant_override,
     rr_softmax_rows, rr_softmax_rows_workspace_bytes, softmax_rows, softmax_workspace,
     status_string, rr_softmax_opts, make_softmax_opts, raw_softmax_rows_ex, rr_softmax_rows_ex,
-    rr_softmax_rows_ex_workspace_bytes, softmax_rows_ex,
+    rr_softmax_rows_ex_workspace_bytes, softmax_rows_ex, raw_rmsnorm_strided,
+    raw_fused_add_rmsnorm_strided, raw_layernorm_strided, raw_softmax_rows_strided,
+    rr_rmsnorm_strided, rr_fused_add_rmsnorm_strided, rr_layernorm_strided,
+    rr_softmax_rows_strided,
 )

@@ -42,6 +42,8 @@ VARIANT_NAMES = {0: "auto", 1: "wave", 2: "block", 3: "split", 4: "loop", 5: "sp
 EXPORTS = (
     "rr_rmsnorm", "rr_fused_add_rmsnorm", "rr_layernorm", "rr_softmax_rows_workspace_bytes",
     "rr_softmax_rows", "rr_softmax_rows_ex_workspace_bytes", "rr_softmax_rows_ex",
+    "rr_rmsnorm_strided", "rr_fused_add_rmsnorm_strided", "rr_layernorm_strided",
+    "rr_softmax_rows_strided",
     "rr_status_string", "rr_last_error_message", "rr_query_plan",
     "rr_set_variant_override", "rr_selftest_wave_allreduce",
 )
@@ -120,6 +122,11 @@ def lib():
     L.rr_softmax_rows_ex_workspace_bytes.argtypes = [i64, i64, i32, i32, po]
     L.rr_softmax_rows_ex_workspace_bytes.restype = ctypes.c_size_t
     L.rr_softmax_rows_ex.argtypes = [vp, vp, i64, i64, i32, i32, po, vp, ctypes.c_size_t, vp]
+    L.rr_rmsnorm_strided.argtypes = [vp, i64, vp, i64, vp, i64, i64, f32, i32, vp]
+    L.rr_fused_add_rmsnorm_strided.argtypes = [vp, i64, vp, i64, vp, i64, vp, i64, i64, f32, i32, vp]
+    L.rr_layernorm_strided.argtypes = [vp, i64, vp, i64, vp, vp, i64, i64, f32, i32, vp]
+    L.rr_softmax_rows_strided.argtypes = [vp, i64, vp, i64, i64, i64, i32, i32, po, vp,
+                                          ctypes.c_size_t, vp]
     L.rr_status_string.argtypes = [i32]
     L.rr_status_string.restype = ctypes.c_char_p
     L.rr_last_error_message.argtypes = []
@@ -128,7 +135,8 @@ def lib():
     L.rr_set_variant_override.argtypes = [i32]
     L.rr_selftest_wave_allreduce.argtypes = [vp, vp, i64, i32, vp]
     for f in ("rr_rmsnorm", "rr_fused_add_rmsnorm", "rr_layernorm", "rr_softmax_rows",
-              "rr_softmax_rows_ex", "rr_query_plan",
+              "rr_softmax_rows_ex", "rr_query_plan", "rr_rmsnorm_strided",
+              "rr_fused_add_rmsnorm_strided", "rr_layernorm_strided", "rr_softmax_rows_strided",
               "rr_set_variant_override", "rr_selftest_wave_allreduce"):
         getattr(L, f).restype = i32
     _LIB = L
@@ -181,6 +189,25 @@ def raw_softmax_rows_ex(y, x, M, N, in_dtype, out_dtype, opts, workspace, worksp
     """opts: an rr_softmax_opts or None."""
     return lib().rr_softmax_rows_ex(y, x, M, N, in_dtype, out_dtype, _opts_ref(opts), workspace,
                                     workspace_bytes, stream)
+
+
+def raw_rmsnorm_strided(y, ldy, x, ldx, gamma, M, H, eps, dtype, stream):
+    return lib().rr_rmsnorm_strided(y, ldy, x, ldx, gamma, M, H, eps, dtype, stream)
+
+
+def raw_fused_add_rmsnorm_strided(y, ldy, residual, ldr, x, ldx, gamma, M, H, eps, dtype, stream):
+    return lib().rr_fused_add_rmsnorm_strided(y, ldy, residual, ldr, x, ldx, gamma, M, H, eps, dtype,
+                                              stream)
+
+
+def raw_layernorm_strided(y, ldy, x, ldx, gamma, beta, M, H, eps, dtype, stream):
+    return lib().rr_layernorm_strided(y, ldy, x, ldx, gamma, beta, M, H, eps, dtype, stream)
+
+
+def raw_softmax_rows_strided(y, ldy, x, ldx, M, N, in_dtype, out_dtype, opts, workspace,
+                             workspace_bytes, stream):
+    return lib().rr_softmax_rows_strided(y, ldy, x, ldx, M, N, in_dtype, out_dtype, _opts_ref(opts),
+                                         workspace, workspace_bytes, stream)
 
 
 def rr_softmax_rows_ex_workspace_bytes(M: int, N: int, in_dtype: int, out_dtype: int, opts=None) -> int:
@@ -239,6 +266,87 @@ def _rows(t):
     n = t.shape[-1]
     m = t.numel() // n if n else 0
     return m, n
+
+
+def _rows_ld(t):
+    """(M, N, row stride) of a tensor whose rows are contiguous and evenly
+    spaced: unit stride in the last dimension, and leading dimensions that
+    flatten to one (each stride the next one times its size)."""
+    if t.dim() == 0:
+        raise ValueError("need at least one dimension")
+    if not t.is_cuda:
+        raise ValueError("tensors must live on a GPU device")
+    n = t.shape[-1]
+    m = t.numel() // n if n else 0
+    if n > 1 and t.stride(-1) != 1:
+        raise ValueError("the last dimension must have unit stride")
+    if t.dim() == 1:
+        return m, n, n
+    for i in range(t.dim() - 2):
+        if t.shape[i] > 1 and t.stride(i) != t.stride(i + 1) * t.shape[i + 1]:
+            raise ValueError("leading dimensions must flatten to one row dimension")
+    ld = t.stride(-2) if t.shape[-2] > 1 else n
+    return m, n, max(ld, n) if m <= 1 else ld
+
+
+def rr_rmsnorm_strided(y, x, gamma, eps: float, stream=None) -> None:
+    """rr_rmsnorm on views whose rows are evenly spaced (a column slice)."""
+    _need_cuda(gamma)
+    M, H, ldx = _rows_ld(x)
+    My, Hy, ldy = _rows_ld(y)
+    if (My, Hy) != (M, H) or gamma.shape != (H,):
+        raise ValueError("y must match x and gamma must be [H]")
+    dt = dtype_code(x)
+    if dtype_code(y) != dt or dtype_code(gamma) != dt:
+        raise TypeError("x, y and gamma must share one dtype")
+    check(raw_rmsnorm_strided(y.data_ptr(), ldy, x.data_ptr(), ldx, gamma.data_ptr(), M, H,
+                              float(eps), dt, _stream_of(x, stream)), "rr_rmsnorm_strided")
+
+
+def rr_fused_add_rmsnorm_strided(y, residual, x, gamma, eps: float, stream=None) -> None:
+    _need_cuda(gamma)
+    M, H, ldx = _rows_ld(x)
+    My, Hy, ldy = _rows_ld(y)
+    Mr, Hr, ldr = _rows_ld(residual)
+    if (My, Hy) != (M, H) or (Mr, Hr) != (M, H) or gamma.shape != (H,):
+        raise ValueError("y and residual must match x and gamma must be [H]")
+    dt = dtype_code(x)
+    if any(dtype_code(t) != dt for t in (y, residual, gamma)):
+        raise TypeError("all tensors must share one dtype")
+    check(raw_fused_add_rmsnorm_strided(y.data_ptr(), ldy, residual.data_ptr(), ldr, x.data_ptr(),
+                                        ldx, gamma.data_ptr(), M, H, float(eps), dt,
+                                        _stream_of(x, stream)), "rr_fused_add_rmsnorm_strided")
+
+
+def rr_layernorm_strided(y, x, gamma, beta, eps: float, stream=None) -> None:
+    _need_cuda(gamma)
+    M, H, ldx = _rows_ld(x)
+    My, Hy, ldy = _rows_ld(y)
+    if (My, Hy) != (M, H) or gamma.shape != (H,) or (beta is not None and beta.shape != (H,)):
+        raise ValueError("y must match x and gamma, beta must be [H]")
+    dt = dtype_code(x)
+    if dtype_code(y) != dt or dtype_code(gamma) != dt or (beta is not None and dtype_code(beta) != dt):
+        raise TypeError("all tensors must share one dtype")
+    bp = None
+    if beta is not None:
+        _need_cuda(beta)
+        bp = beta.data_ptr()
+    check(raw_layernorm_strided(y.data_ptr(), ldy, x.data_ptr(), ldx, gamma.data_ptr(), bp, M, H,
+                                float(eps), dt, _stream_of(x, stream)), "rr_layernorm_strided")
+
+
+def rr_softmax_rows_strided(y, x, opts=None, workspace=None, stream=None) -> None:
+    M, N, ldx = _rows_ld(x)
+    My, Ny, ldy = _rows_ld(y)
+    if (My, Ny) != (M, N):
+        raise ValueError("y must match x")
+    ws_ptr, ws_bytes = None, 0
+    if workspace is not None:
+        _need_cuda(workspace)
+        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    check(raw_softmax_rows_strided(y.data_ptr(), ldy, x.data_ptr(), ldx, M, N, dtype_code(x),
+                                   dtype_code(y), opts, ws_ptr, ws_bytes, _stream_of(x, stream)),
+          "rr_softmax_rows_strided")
 
 
 def rr_rmsnorm(y, x, gamma, eps: float, stream=None) -> None:

@@ -46,6 +46,36 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
   return pa < pb + nb && pb < pa + na;
 }
 
+// A row-major matrix of M rows of w bytes, row i starting at p + i * ld
+// bytes (ld >= w).
+struct Mat {
+  const void* p;
+  size_t ld;
+  size_t w;
+};
+
+// Bytes from the first to one past the last byte of the matrix.
+size_t span(const Mat& a, int64_t M) { return (size_t)(M - 1) * a.ld + a.w; }
+
+// The two matrices share a byte.  Disjoint spans never do; with equal
+// strides, each matrix covers a fixed window of byte positions modulo the
+// stride, and the matrices are disjoint when those windows are (two column
+// slices of one wider matrix, say).  Anything else with overlapping spans
+// counts as overlapping.
+bool mats_overlap(const Mat& a, const Mat& b, int64_t M) {
+  if (!overlaps(a.p, span(a, M), b.p, span(b, M))) return false;
+  if (a.ld != b.ld || a.ld == 0) return true;
+  const uintptr_t pa = reinterpret_cast<uintptr_t>(a.p);
+  const uintptr_t pb = reinterpret_cast<uintptr_t>(b.p);
+  const size_t ld = a.ld;
+  // position of b's window relative to a's, in [0, ld)
+  const size_t d = pb >= pa ? (size_t)(pb - pa) % ld : (ld - (size_t)(pa - pb) % ld) % ld;
+  return !(d >= a.w && d + b.w <= ld);
+}
+
+// Rows of the matrix start 16-byte aligned.
+bool rows_aligned16(const Mat& a) { return aligned16(a.p) && a.ld % 16 == 0; }
+
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 int pow2_at_least(int64_t v) {
@@ -55,6 +85,7 @@ int pow2_at_least(int64_t v) {
 }
 
 constexpr int64_t kMaxN = (int64_t)1 << 30;  // keeps every in-row index in int32
+constexpr int64_t kMaxStride = (int64_t)1 << 40;  // row strides, in elements
 constexpr int kMaxWaves = rr::kMaxWavesPerGroup;
 constexpr int kWaveRowsPerGroup = 4;         // rows per 256-thread workgroup (WAVE)
 constexpr int64_t kSplitMaxRows = 1024;      // SPLIT only below this many rows
@@ -286,13 +317,28 @@ rr_status hip_status(hipError_t e, const char* what) {
 bool valid_eps(float eps) { return eps >= 0.0f && eps <= 3.0e38f; }
 
 // kind: rr::kLaunchRms, kLaunchFused or kLaunchLayer.
-rr_status norm_entry(int kind, void* y, void* residual, const void* x, const void* gamma,
-                     const void* beta, int64_t M, int64_t H, float eps, rr_dtype dtype,
-                     void* stream) {
+// Row strides of a call, in elements, checked: each at least the row width
+// (rows of one matrix never overlap) and small enough that the last row's
+// end fits in memory.
+rr_status check_strides(const char* name, int64_t M, int64_t H, const int64_t* lds, const char* const* what,
+                        int n) {
+  for (int i = 0; i < n; ++i) {
+    if (lds[i] < H)
+      return fail(RR_ERR_INVALID_ARG, "%s: %s = %lld < row width %lld", name, what[i], (long long)lds[i],
+                  (long long)H);
+    if (lds[i] > kMaxStride || (uint64_t)(M - 1) > (uint64_t)(SIZE_MAX / 8) / (uint64_t)lds[i])
+      return fail(RR_ERR_INVALID_ARG, "%s: %s = %lld too large for M = %lld", name, what[i],
+                  (long long)lds[i], (long long)M);
+  }
+  return RR_OK;
+}
+
+rr_status norm_entry(int kind, void* y, int64_t ldy, void* residual, int64_t ldr, const void* x,
+                     int64_t ldx, const void* gamma, const void* beta, int64_t M, int64_t H, float eps,
+                     rr_dtype dtype, void* stream, const char* name) {
   g_err[0] = '\0';
   const bool fused = kind == rr::kLaunchFused;
   const bool layer = kind == rr::kLaunchLayer;
-  const char* name = fused ? "rr_fused_add_rmsnorm" : layer ? "rr_layernorm" : "rr_rmsnorm";
   if (!valid_dtype(dtype)) return fail(RR_ERR_INVALID_ARG, "%s: unknown dtype %d", name, (int)dtype);
   if (M < 0) return fail(RR_ERR_INVALID_ARG, "%s: M = %lld < 0", name, (long long)M);
   if (H < 1) return fail(RR_ERR_INVALID_ARG, "%s: H = %lld < 1", name, (long long)H);
@@ -301,23 +347,27 @@ rr_status norm_entry(int kind, void* y, void* residual, const void* x, const voi
   if (!y || !x || !gamma || (fused && !residual))
     return fail(RR_ERR_INVALID_ARG, "%s: null pointer", name);
   if (H > kMaxN) return fail(RR_ERR_UNSUPPORTED, "%s: H = %lld > 2^30", name, (long long)H);
+  const int64_t lds[3] = {ldy, ldx, fused ? ldr : H};
+  const char* const what[3] = {"ldy", "ldx", "ldr"};
+  const rr_status sst = check_strides(name, M, H, lds, what, 3);
+  if (sst != RR_OK) return sst;
   const size_t es = dtype_size(dtype);
-  if ((uint64_t)M > (uint64_t)(SIZE_MAX / 8) / (uint64_t)H)
-    return fail(RR_ERR_INVALID_ARG, "%s: M * H overflows", name);
-  const size_t bytes = (size_t)M * (size_t)H * es;
-  const size_t gbytes = (size_t)H * es;
-  if (y != x && overlaps(y, bytes, x, bytes))
+  const size_t w = (size_t)H * es;
+  const Mat my{y, (size_t)ldy * es, w}, mx{x, (size_t)ldx * es, w}, mr{residual, (size_t)ldr * es, w};
+  const size_t gbytes = w;
+  // y may be x itself (same stride): each lane reads its elements before it
+  // writes them
+  if (!(y == x && ldy == ldx) && mats_overlap(my, mx, M))
     return fail(RR_ERR_INVALID_ARG, "%s: y partly overlaps x", name);
-  if (overlaps(gamma, gbytes, y, bytes)) return fail(RR_ERR_INVALID_ARG, "%s: gamma overlaps y", name);
-  if (layer && beta && overlaps(beta, gbytes, y, bytes))
+  if (overlaps(gamma, gbytes, y, span(my, M))) return fail(RR_ERR_INVALID_ARG, "%s: gamma overlaps y", name);
+  if (layer && beta && overlaps(beta, gbytes, y, span(my, M)))
     return fail(RR_ERR_INVALID_ARG, "%s: beta overlaps y", name);
   if (fused) {
-    if (overlaps(residual, bytes, x, bytes) || overlaps(residual, bytes, y, bytes) ||
-        overlaps(residual, bytes, gamma, gbytes))
+    if (mats_overlap(mr, mx, M) || mats_overlap(mr, my, M) || overlaps(residual, span(mr, M), gamma, gbytes))
       return fail(RR_ERR_INVALID_ARG, "%s: residual overlaps x, y or gamma", name);
   }
-  const bool al = aligned16(y) && aligned16(x) && aligned16(gamma) && (!fused || aligned16(residual)) &&
-                  (!layer || !beta || aligned16(beta));
+  const bool al = rows_aligned16(my) && rows_aligned16(mx) && aligned16(gamma) &&
+                  (!fused || rows_aligned16(mr)) && (!layer || !beta || aligned16(beta));
   const rr_op op = fused ? RR_OP_FUSED_ADD_RMSNORM : layer ? RR_OP_LAYERNORM : RR_OP_RMSNORM;
   rr_plan p;
   const rr_status st = make_plan(op, M, H, dtype, dtype, al, &p);
@@ -331,6 +381,7 @@ rr_status norm_entry(int kind, void* y, void* residual, const void* x, const voi
   a.M = M;
   a.N = (int32_t)H;
   a.eps = eps;
+  a.ld = rr::RowStrides{ldx, ldy, fused ? ldr : H};
   const hipError_t e = rr::launch_norm(p, dtype, kind, a, grid_for(p), static_cast<hipStream_t>(stream));
   return hip_status(e, name);
 }
@@ -341,17 +392,40 @@ extern "C" {
 
 rr_status rr_rmsnorm(void* y, const void* x, const void* gamma, int64_t M, int64_t H, float eps,
                      rr_dtype dtype, void* stream) {
-  return norm_entry(rr::kLaunchRms, y, nullptr, x, gamma, nullptr, M, H, eps, dtype, stream);
+  return norm_entry(rr::kLaunchRms, y, H, nullptr, H, x, H, gamma, nullptr, M, H, eps, dtype, stream,
+                    "rr_rmsnorm");
 }
 
 rr_status rr_fused_add_rmsnorm(void* y, void* residual, const void* x, const void* gamma,
                                int64_t M, int64_t H, float eps, rr_dtype dtype, void* stream) {
-  return norm_entry(rr::kLaunchFused, y, residual, x, gamma, nullptr, M, H, eps, dtype, stream);
+  return norm_entry(rr::kLaunchFused, y, H, residual, H, x, H, gamma, nullptr, M, H, eps, dtype, stream,
+                    "rr_fused_add_rmsnorm");
 }
 
 rr_status rr_layernorm(void* y, const void* x, const void* gamma, const void* beta, int64_t M,
                        int64_t H, float eps, rr_dtype dtype, void* stream) {
-  return norm_entry(rr::kLaunchLayer, y, nullptr, x, gamma, beta, M, H, eps, dtype, stream);
+  return norm_entry(rr::kLaunchLayer, y, H, nullptr, H, x, H, gamma, beta, M, H, eps, dtype, stream,
+                    "rr_layernorm");
+}
+
+rr_status rr_rmsnorm_strided(void* y, int64_t ldy, const void* x, int64_t ldx, const void* gamma,
+                             int64_t M, int64_t H, float eps, rr_dtype dtype, void* stream) {
+  return norm_entry(rr::kLaunchRms, y, ldy, nullptr, H, x, ldx, gamma, nullptr, M, H, eps, dtype, stream,
+                    "rr_rmsnorm_strided");
+}
+
+rr_status rr_fused_add_rmsnorm_strided(void* y, int64_t ldy, void* residual, int64_t ldr,
+                                       const void* x, int64_t ldx, const void* gamma, int64_t M,
+                                       int64_t H, float eps, rr_dtype dtype, void* stream) {
+  return norm_entry(rr::kLaunchFused, y, ldy, residual, ldr, x, ldx, gamma, nullptr, M, H, eps, dtype,
+                    stream, "rr_fused_add_rmsnorm_strided");
+}
+
+rr_status rr_layernorm_strided(void* y, int64_t ldy, const void* x, int64_t ldx, const void* gamma,
+                               const void* beta, int64_t M, int64_t H, float eps, rr_dtype dtype,
+                               void* stream) {
+  return norm_entry(rr::kLaunchLayer, y, ldy, nullptr, H, x, ldx, gamma, beta, M, H, eps, dtype, stream,
+                    "rr_layernorm_strided");
 }
 
 }  // extern "C"
@@ -379,8 +453,8 @@ rr_status softmax_options(const rr_softmax_opts* o, const char* who, rr_softmax_
   return RR_OK;
 }
 
-rr_status softmax_entry(const char* who, void* y, const void* x, int64_t M, int64_t N,
-                        rr_dtype in_dtype, rr_dtype out_dtype, const rr_softmax_opts* opts,
+rr_status softmax_entry(const char* who, void* y, int64_t ldy, const void* x, int64_t ldx, int64_t M,
+                        int64_t N, rr_dtype in_dtype, rr_dtype out_dtype, const rr_softmax_opts* opts,
                         void* workspace, size_t workspace_bytes, void* stream) {
   g_err[0] = '\0';
   if (!valid_dtype(in_dtype) || !valid_dtype(out_dtype))
@@ -393,13 +467,17 @@ rr_status softmax_entry(const char* who, void* y, const void* x, int64_t M, int6
   if (M == 0) return RR_OK;
   if (!y || !x) return fail(RR_ERR_INVALID_ARG, "%s: null pointer", who);
   if (N > kMaxN) return fail(RR_ERR_UNSUPPORTED, "%s: N = %lld > 2^30", who, (long long)N);
-  if ((uint64_t)M > (uint64_t)(SIZE_MAX / 8) / (uint64_t)N)
-    return fail(RR_ERR_INVALID_ARG, "%s: M * N overflows", who);
-  const size_t xb = (size_t)M * (size_t)N * dtype_size(in_dtype);
-  const size_t yb = (size_t)M * (size_t)N * dtype_size(out_dtype);
-  if (overlaps(x, xb, y, yb) && !(x == y && in_dtype == out_dtype))
-    return fail(RR_ERR_INVALID_ARG, "%s: x and y overlap (in place needs equal pointers and dtypes)", who);
-  const bool al = aligned16(x) && aligned16(y);
+  const int64_t lds[2] = {ldy, ldx};
+  const char* const what[2] = {"ldy", "ldx"};
+  const rr_status sst = check_strides(who, M, N, lds, what, 2);
+  if (sst != RR_OK) return sst;
+  const Mat mx{x, (size_t)ldx * dtype_size(in_dtype), (size_t)N * dtype_size(in_dtype)};
+  const Mat my{y, (size_t)ldy * dtype_size(out_dtype), (size_t)N * dtype_size(out_dtype)};
+  const size_t xb = span(mx, M), yb = span(my, M);
+  if (mats_overlap(mx, my, M) && !(x == y && ldx == ldy && in_dtype == out_dtype))
+    return fail(RR_ERR_INVALID_ARG,
+                "%s: x and y overlap (in place needs equal pointers, strides and dtypes)", who);
+  const bool al = rows_aligned16(mx) && rows_aligned16(my);
   rr_plan p;
   const rr_status st = make_plan(o.causal ? RR_OP_SOFTMAX_CAUSAL : RR_OP_SOFTMAX, M, N, in_dtype,
                                  out_dtype, al, &p);
@@ -424,6 +502,7 @@ rr_status softmax_entry(const char* who, void* y, const void* x, int64_t M, int6
   // keeps every key, so clamp it to keep the kernels' sums in range
   a.causal_offset = o.causal_offset < N ? o.causal_offset : N;
   a.log_output = o.log_output;
+  a.ld = rr::RowStrides{ldx, ldy, 0};
   const hipError_t e = rr::launch_softmax(p, in_dtype, out_dtype, a, grid_for(p),
                                           static_cast<hipStream_t>(stream));
   return hip_status(e, who);
@@ -452,15 +531,23 @@ size_t rr_softmax_rows_ex_workspace_bytes(int64_t M, int64_t N, rr_dtype in_dtyp
 rr_status rr_softmax_rows(void* y, const void* x, int64_t M, int64_t N, rr_dtype in_dtype,
                           rr_dtype out_dtype, void* workspace, size_t workspace_bytes,
                           void* stream) {
-  return softmax_entry("rr_softmax_rows", y, x, M, N, in_dtype, out_dtype, nullptr, workspace,
+  return softmax_entry("rr_softmax_rows", y, N, x, N, M, N, in_dtype, out_dtype, nullptr, workspace,
                        workspace_bytes, stream);
 }
 
 rr_status rr_softmax_rows_ex(void* y, const void* x, int64_t M, int64_t N, rr_dtype in_dtype,
                              rr_dtype out_dtype, const rr_softmax_opts* opts, void* workspace,
                              size_t workspace_bytes, void* stream) {
-  return softmax_entry("rr_softmax_rows_ex", y, x, M, N, in_dtype, out_dtype, opts, workspace,
+  return softmax_entry("rr_softmax_rows_ex", y, N, x, N, M, N, in_dtype, out_dtype, opts, workspace,
                        workspace_bytes, stream);
+}
+
+rr_status rr_softmax_rows_strided(void* y, int64_t ldy, const void* x, int64_t ldx, int64_t M,
+                                  int64_t N, rr_dtype in_dtype, rr_dtype out_dtype,
+                                  const rr_softmax_opts* opts, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+  return softmax_entry("rr_softmax_rows_strided", y, ldy, x, ldx, M, N, in_dtype, out_dtype, opts,
+                       workspace, workspace_bytes, stream);
 }
 
 const char* rr_status_string(rr_status s) {

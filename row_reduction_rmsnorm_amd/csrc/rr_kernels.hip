@@ -178,7 +178,7 @@ template <typename T, int NV, int KIND, bool WAVE>
 __global__ __launch_bounds__(1024) void norm_regs_kernel(T* y, T* residual, const T* x,
                                                          const T* __restrict__ gamma,
                                                          const T* __restrict__ beta, int64_t M,
-                                                         int N, float eps) {
+                                                         int N, float eps, RowStrides ld) {
   constexpr int VEC = Elem<T>::kVec;
   __shared__ float slots[2][kMaxWavesPerGroup];
   const RowLane rl = row_lane<WAVE>();
@@ -209,7 +209,7 @@ __global__ __launch_bounds__(1024) void norm_regs_kernel(T* y, T* residual, cons
     return v;
   };
   for (int64_t row = (int64_t)blockIdx.x * rl.rpg + rl.g; row < M; row += stride) {
-    const int64_t off = row * (int64_t)N;
+    const int64_t ox = row * ld.x, oy = row * ld.y, orr = row * ld.r;
     float h[NV][VEC];
     if constexpr (KIND == kNormFused) {
       float r[NV][VEC];
@@ -217,8 +217,8 @@ __global__ __launch_bounds__(1024) void norm_regs_kernel(T* y, T* residual, cons
       for (int k = 0; k < NV; ++k) {
         const int vi = k * rl.T + rl.t;
         if (vi < nvec) {
-          load_vec<T, VEC>(x + off + (int64_t)vi * VEC, h[k]);
-          load_vec<T, VEC>(residual + off + (int64_t)vi * VEC, r[k]);
+          load_vec<T, VEC>(x + ox + (int64_t)vi * VEC, h[k]);
+          load_vec<T, VEC>(residual + orr + (int64_t)vi * VEC, r[k]);
         } else {
 #pragma unroll
           for (int i = 0; i < VEC; ++i) h[k][i] = r[k][i] = 0.0f;
@@ -229,14 +229,14 @@ __global__ __launch_bounds__(1024) void norm_regs_kernel(T* y, T* residual, cons
 #pragma unroll
         for (int i = 0; i < VEC; ++i) h[k][i] = round_to<T>(h[k][i] + r[k][i]);
         const int vi = k * rl.T + rl.t;
-        if (vi < nvec) store_vec<T, VEC>(residual + off + (int64_t)vi * VEC, h[k]);
+        if (vi < nvec) store_vec<T, VEC>(residual + orr + (int64_t)vi * VEC, h[k]);
       }
     } else {
 #pragma unroll
       for (int k = 0; k < NV; ++k) {
         const int vi = k * rl.T + rl.t;
         if (vi < nvec) {
-          load_vec<T, VEC>(x + off + (int64_t)vi * VEC, h[k]);
+          load_vec<T, VEC>(x + ox + (int64_t)vi * VEC, h[k]);
         } else {
 #pragma unroll
           for (int i = 0; i < VEC; ++i) h[k][i] = 0.0f;
@@ -252,7 +252,7 @@ __global__ __launch_bounds__(1024) void norm_regs_kernel(T* y, T* residual, cons
       // a rounding error relative to the mean itself, only to the row's spread
       // ([P2] section 八.2 warns about rows whose mean is far larger than their
       // spread).  The mean K + c is never formed.
-      const float K = load_one<T>(x + off);
+      const float K = load_one<T>(x + ox);
       float s1 = 0.0f;
 #pragma unroll
       for (int k = 0; k < NV; ++k) {
@@ -279,7 +279,7 @@ __global__ __launch_bounds__(1024) void norm_regs_kernel(T* y, T* residual, cons
         float o[VEC];
 #pragma unroll
         for (int i = 0; i < VEC; ++i) o[i] = (h[k][i] * rstd) * gv[k].get(i) + bv[k].get(i);
-        if (vi < nvec) store_vec<T, VEC>(y + off + (int64_t)vi * VEC, o);
+        if (vi < nvec) store_vec<T, VEC>(y + oy + (int64_t)vi * VEC, o);
       }
     } else {
       float ss = 0.0f;
@@ -295,7 +295,7 @@ __global__ __launch_bounds__(1024) void norm_regs_kernel(T* y, T* residual, cons
         float o[VEC];
 #pragma unroll
         for (int i = 0; i < VEC; ++i) o[i] = (h[k][i] * rstd) * gv[k].get(i);
-        if (vi < nvec) store_vec<T, VEC>(y + off + (int64_t)vi * VEC, o);
+        if (vi < nvec) store_vec<T, VEC>(y + oy + (int64_t)vi * VEC, o);
       }
     }
   }
@@ -311,7 +311,7 @@ template <typename T, int VEC, int KIND>
 __global__ __launch_bounds__(1024) void norm_loop_kernel(T* y, T* residual, const T* x,
                                                          const T* __restrict__ gamma,
                                                          const T* __restrict__ beta, int64_t M,
-                                                         int N, float eps) {
+                                                         int N, float eps, RowStrides ld) {
   __shared__ float slots[2][kMaxWavesPerGroup];
   const RowLane rl = row_lane<false>();
   const int nvec = N / VEC;
@@ -323,16 +323,16 @@ __global__ __launch_bounds__(1024) void norm_loop_kernel(T* y, T* residual, cons
     return v;
   };
   for (int64_t row = blockIdx.x; row < M; row += gridDim.x) {
-    const int64_t off = row * (int64_t)N;
+    const int64_t ox = row * ld.x, oy = row * ld.y, orr = row * ld.r;
     if constexpr (KIND == kNormLayer) {
       // three passes over the row: the mean's offset from the first element,
       // the variance about the mean, then the output (centred as
       // (x - K) - c, as in the register kernel)
-      const float K = load_one<T>(x + off);
+      const float K = load_one<T>(x + ox);
       float s1 = 0.0f;
       for (int vi = rl.t; vi < nvec; vi += rl.T) {
         float h[VEC];
-        load_vec<T, VEC, false>(x + off + (int64_t)vi * VEC, h);
+        load_vec<T, VEC, false>(x + ox + (int64_t)vi * VEC, h);
 #pragma unroll
         for (int i = 0; i < VEC; ++i) s1 += h[i] - K;
       }
@@ -340,7 +340,7 @@ __global__ __launch_bounds__(1024) void norm_loop_kernel(T* y, T* residual, cons
       float s2 = 0.0f;
       for (int vi = rl.t; vi < nvec; vi += rl.T) {
         float h[VEC];
-        load_vec<T, VEC, false>(x + off + (int64_t)vi * VEC, h);
+        load_vec<T, VEC, false>(x + ox + (int64_t)vi * VEC, h);
 #pragma unroll
         for (int i = 0; i < VEC; ++i) {
           const float d = (h[i] - K) - c;
@@ -350,7 +350,7 @@ __global__ __launch_bounds__(1024) void norm_loop_kernel(T* y, T* residual, cons
       const float rstd = 1.0f / __builtin_sqrtf(row_sum(s2) / (float)N + eps);
       for (int vi = rl.t; vi < nvec; vi += rl.T) {
         float h[VEC], g[VEC], bb[VEC];
-        load_vec<T, VEC>(x + off + (int64_t)vi * VEC, h);
+        load_vec<T, VEC>(x + ox + (int64_t)vi * VEC, h);
         load_vec<T, VEC, false>(gamma + (int64_t)vi * VEC, g);
         if (beta) {
           load_vec<T, VEC, false>(beta + (int64_t)vi * VEC, bb);
@@ -360,32 +360,32 @@ __global__ __launch_bounds__(1024) void norm_loop_kernel(T* y, T* residual, cons
         }
 #pragma unroll
         for (int i = 0; i < VEC; ++i) h[i] = (((h[i] - K) - c) * rstd) * g[i] + bb[i];
-        store_vec<T, VEC>(y + off + (int64_t)vi * VEC, h);
+        store_vec<T, VEC>(y + oy + (int64_t)vi * VEC, h);
       }
     } else {
       float ss = 0.0f;
       for (int vi = rl.t; vi < nvec; vi += rl.T) {
         float h[VEC];
-        load_vec<T, VEC>(x + off + (int64_t)vi * VEC, h);
+        load_vec<T, VEC>(x + ox + (int64_t)vi * VEC, h);
         if constexpr (KIND == kNormFused) {
           float r[VEC];
-          load_vec<T, VEC>(residual + off + (int64_t)vi * VEC, r);
+          load_vec<T, VEC>(residual + orr + (int64_t)vi * VEC, r);
 #pragma unroll
           for (int i = 0; i < VEC; ++i) h[i] = round_to<T>(h[i] + r[i]);
-          store_vec<T, VEC>(residual + off + (int64_t)vi * VEC, h);
+          store_vec<T, VEC>(residual + orr + (int64_t)vi * VEC, h);
         }
 #pragma unroll
         for (int i = 0; i < VEC; ++i) ss += h[i] * h[i];
       }
       const float rstd = 1.0f / __builtin_sqrtf(row_sum(ss) / (float)N + eps);
-      const T* src = KIND == kNormFused ? residual : x;
+      const T* src = KIND == kNormFused ? residual + orr : x + ox;
       for (int vi = rl.t; vi < nvec; vi += rl.T) {
         float h[VEC], g[VEC];
-        load_vec<T, VEC>(src + off + (int64_t)vi * VEC, h);
+        load_vec<T, VEC>(src + (int64_t)vi * VEC, h);
         load_vec<T, VEC, false>(gamma + (int64_t)vi * VEC, g);
 #pragma unroll
         for (int i = 0; i < VEC; ++i) h[i] = (h[i] * rstd) * g[i];
-        store_vec<T, VEC>(y + off + (int64_t)vi * VEC, h);
+        store_vec<T, VEC>(y + oy + (int64_t)vi * VEC, h);
       }
     }
   }
@@ -404,7 +404,7 @@ template <typename T, int VEC, int L, int KIND>
 __global__ __launch_bounds__(256) void norm_sub_kernel(T* y, T* residual, const T* x,
                                                        const T* __restrict__ gamma,
                                                        const T* __restrict__ beta, int64_t M,
-                                                       int N, float eps) {
+                                                       int N, float eps, RowStrides ld) {
   constexpr int kRowsPerGroup = 256 / L;
   const int j = threadIdx.x & (L - 1);              // lane within the row
   const int nvec = N / VEC;
@@ -416,16 +416,17 @@ __global__ __launch_bounds__(256) void norm_sub_kernel(T* y, T* residual, const 
   else bb.fill(0.0f);
   for (int64_t row = (int64_t)blockIdx.x * kRowsPerGroup + (threadIdx.x / L); row < M;
        row += (int64_t)gridDim.x * kRowsPerGroup) {
-    const int64_t off = row * (int64_t)N + (int64_t)j * VEC;
+    const int64_t cj = (int64_t)j * VEC;
+    const int64_t ox = row * ld.x + cj, oy = row * ld.y + cj, orr = row * ld.r + cj;
     float h[VEC];
     if (active) {
-      load_vec<T, VEC>(x + off, h);
+      load_vec<T, VEC>(x + ox, h);
       if constexpr (KIND == kNormFused) {
         float r[VEC];
-        load_vec<T, VEC>(residual + off, r);
+        load_vec<T, VEC>(residual + orr, r);
 #pragma unroll
         for (int i = 0; i < VEC; ++i) h[i] = round_to<T>(h[i] + r[i]);
-        store_vec<T, VEC>(residual + off, h);
+        store_vec<T, VEC>(residual + orr, h);
       }
     } else {
 #pragma unroll
@@ -433,7 +434,7 @@ __global__ __launch_bounds__(256) void norm_sub_kernel(T* y, T* residual, const 
     }
     float o[VEC];
     if constexpr (KIND == kNormLayer) {
-      const float K = load_one<T>(x + row * (int64_t)N);
+      const float K = load_one<T>(x + row * ld.x);
       float s1 = 0.0f;
 #pragma unroll
       for (int i = 0; i < VEC; ++i) s1 += active ? h[i] - K : 0.0f;
@@ -457,13 +458,13 @@ __global__ __launch_bounds__(256) void norm_sub_kernel(T* y, T* residual, const 
 #pragma unroll
       for (int i = 0; i < VEC; ++i) o[i] = (h[i] * rstd) * g.get(i);
     }
-    if (active) store_vec<T, VEC>(y + off, o);
+    if (active) store_vec<T, VEC>(y + oy, o);
   }
 }
 
 template <typename Tin, typename Tout, int VEC, int L, bool LOG, bool CAUSAL>
 __global__ __launch_bounds__(256) void softmax_sub_kernel(const Tin* x, Tout* y, int64_t M, int N,
-                                                          int64_t cp, int64_t co) {
+                                                          int64_t cp, int64_t co, RowStrides ld) {
   constexpr int kRowsPerGroup = 256 / L;
   const int j = threadIdx.x & (L - 1);
   const int nvec = N / VEC;
@@ -472,10 +473,10 @@ __global__ __launch_bounds__(256) void softmax_sub_kernel(const Tin* x, Tout* y,
   CausalRows cr(row0, stride, CAUSAL ? cp : 0, co);
   for (int64_t row = row0; row < M; row += stride, cr.next()) {
     const int keys = cr.keys(N);
-    const int64_t off = row * (int64_t)N + (int64_t)j * VEC;
+    const int64_t ox = row * ld.x + (int64_t)j * VEC, oy = row * ld.y + (int64_t)j * VEC;
     float v[VEC];
     if (j * VEC < keys) {
-      load_vec<Tin, VEC>(x + off, v);
+      load_vec<Tin, VEC>(x + ox, v);
       mask_keys<VEC>(v, j * VEC, keys);
     } else {
 #pragma unroll
@@ -507,7 +508,7 @@ __global__ __launch_bounds__(256) void softmax_sub_kernel(const Tin* x, Tout* y,
 #pragma unroll
       for (int i = 0; i < VEC; ++i) o[i] = v[i] * c;
     }
-    if (j < nvec) store_vec<Tout, VEC>(y + off, o);
+    if (j < nvec) store_vec<Tout, VEC>(y + oy, o);
   }
 }
 
@@ -529,7 +530,7 @@ __global__ __launch_bounds__(256) void softmax_sub_kernel(const Tin* x, Tout* y,
 // ===========================================================================
 template <typename Tin, typename Tout, int NV, bool WAVE, bool LOG, bool CAUSAL>
 __global__ __launch_bounds__(1024) void softmax_regs_kernel(const Tin* x, Tout* y, int64_t M,
-                                                            int N, int64_t cp, int64_t co) {
+                                                            int N, int64_t cp, int64_t co, RowStrides ld) {
   constexpr int VEC = Elem<Tin>::kVec;
   __shared__ MD slots[2][kMaxWavesPerGroup];
   const RowLane rl = row_lane<WAVE>();
@@ -541,13 +542,13 @@ __global__ __launch_bounds__(1024) void softmax_regs_kernel(const Tin* x, Tout* 
   for (int64_t row = row0; row < M; row += stride, cr.next()) {
     const int keys = cr.keys(N);
     const int nvec_keys = (keys + VEC - 1) / VEC;   // vectors holding kept keys
-    const int64_t off = row * (int64_t)N;
+    const int64_t ox = row * ld.x, oy = row * ld.y;
     float v[NV][VEC];
 #pragma unroll
     for (int k = 0; k < NV; ++k) {
       const int vi = k * rl.T + rl.t;
       if (vi < nvec_keys) {
-        load_vec<Tin, VEC>(x + off + (int64_t)vi * VEC, v[k]);
+        load_vec<Tin, VEC>(x + ox + (int64_t)vi * VEC, v[k]);
       } else {
 #pragma unroll
         for (int i = 0; i < VEC; ++i) v[k][i] = kNegInf;
@@ -596,7 +597,7 @@ __global__ __launch_bounds__(1024) void softmax_regs_kernel(const Tin* x, Tout* 
       float o[VEC];
 #pragma unroll
       for (int i = 0; i < VEC; ++i) o[i] = LOG ? (v[k][i] - p.m) - ld : v[k][i] * c;
-      if (vi < nvec) store_vec<Tout, VEC>(y + off + (int64_t)vi * VEC, o);
+      if (vi < nvec) store_vec<Tout, VEC>(y + oy + (int64_t)vi * VEC, o);
     }
   }
 }
@@ -613,7 +614,7 @@ __global__ __launch_bounds__(1024) void softmax_regs_kernel(const Tin* x, Tout* 
 // ===========================================================================
 template <typename Tin, typename Tout, int NV, bool LOG, bool CAUSAL>
 __global__ __launch_bounds__(1024) void softmax_packed_kernel(const Tin* x, Tout* y, int64_t M,
-                                                              int N, int64_t cp, int64_t co) {
+                                                              int N, int64_t cp, int64_t co, RowStrides ld) {
   constexpr int VEC = Elem<Tin>::kVec;
   constexpr int kThreads = 1024;
   __shared__ MD slots[2][kMaxWavesPerGroup];
@@ -626,8 +627,8 @@ __global__ __launch_bounds__(1024) void softmax_packed_kernel(const Tin* x, Tout
   for (int64_t row = blockIdx.x; row < M; row += gridDim.x, cr.next()) {
     const int keys = cr.keys(N);
     const int nvec_keys = (keys + VEC - 1) / VEC;
-    const Tin* xr = x + row * (int64_t)N;   // uniform row bases
-    Tout* yr = y + row * (int64_t)N;
+    const Tin* xr = x + row * ld.x;   // uniform row bases
+    Tout* yr = y + row * ld.y;
     // the lane's vector offsets are recomputed at each use rather than kept
     // live across the row (an opaque copy of the lane index), which frees
     // the registers the packed row needs
@@ -698,7 +699,7 @@ __global__ __launch_bounds__(1024) void softmax_packed_kernel(const Tin* x, Tout
 // ===========================================================================
 template <typename Tin, typename Tout, int VEC, bool LOG, bool CAUSAL>
 __global__ __launch_bounds__(1024) void softmax_loop_kernel(const Tin* x, Tout* y, int64_t M,
-                                                            int N, int64_t cp, int64_t co) {
+                                                            int N, int64_t cp, int64_t co, RowStrides ld) {
   __shared__ MD slots[2][kMaxWavesPerGroup];
   const RowLane rl = row_lane<false>();
   const int nvec = N / VEC;
@@ -707,13 +708,13 @@ __global__ __launch_bounds__(1024) void softmax_loop_kernel(const Tin* x, Tout* 
   for (int64_t row = blockIdx.x; row < M; row += gridDim.x, cr.next()) {
     const int keys = cr.keys(N);
     const int nvec_keys = (keys + VEC - 1) / VEC;
-    const int64_t off = row * (int64_t)N;
+    const int64_t ox = row * ld.x, oy = row * ld.y;
     MD p;
     p.m = kNegInf;
     p.d = 0.0f;
     for (int vi = rl.t; vi < nvec_keys; vi += rl.T) {
       float v[VEC];
-      load_vec<Tin, VEC>(x + off + (int64_t)vi * VEC, v);
+      load_vec<Tin, VEC>(x + ox + (int64_t)vi * VEC, v);
       mask_keys<VEC>(v, vi * VEC, keys);
       p = md_merge(p, chunk_summary<VEC>(v));
     }
@@ -725,7 +726,7 @@ __global__ __launch_bounds__(1024) void softmax_loop_kernel(const Tin* x, Tout* 
     for (int vi = rl.t; vi < nvec; vi += rl.T) {
       float v[VEC];
       if (vi < nvec_keys) {
-        load_vec<Tin, VEC>(x + off + (int64_t)vi * VEC, v);
+        load_vec<Tin, VEC>(x + ox + (int64_t)vi * VEC, v);
         mask_keys<VEC>(v, vi * VEC, keys);
       } else {
 #pragma unroll
@@ -733,7 +734,7 @@ __global__ __launch_bounds__(1024) void softmax_loop_kernel(const Tin* x, Tout* 
       }
 #pragma unroll
       for (int i = 0; i < VEC; ++i) v[i] = LOG ? (v[i] - p.m) - ld : exp_shifted(v[i] - p.m) * inv_d;
-      store_vec<Tout, VEC>(y + off + (int64_t)vi * VEC, v);
+      store_vec<Tout, VEC>(y + oy + (int64_t)vi * VEC, v);
     }
   }
 }
@@ -763,7 +764,7 @@ static_assert(sizeof(SplitSlot) == 16, "slot layout");
 
 template <typename Tin, int NV>
 __global__ __launch_bounds__(256) void softmax_split_stats_kernel(const Tin* x, SplitSlot* ws,
-                                                                  int64_t M, int N, int S) {
+                                                                  int64_t M, int N, int S, RowStrides ld) {
   constexpr int VEC = Elem<Tin>::kVec;
   constexpr int kThreads = 256;
   constexpr int CV = kThreads * NV;
@@ -775,13 +776,13 @@ __global__ __launch_bounds__(256) void softmax_split_stats_kernel(const Tin* x, 
   for (int64_t item = blockIdx.x; item < items; item += gridDim.x) {
     const int64_t row = item / S;
     const int c = (int)(item - row * S);
-    const int64_t off = row * (int64_t)N;
+    const int64_t ox = row * ld.x;
     Packed<Tin, VEC> v[NV];
 #pragma unroll
     for (int k = 0; k < NV; ++k) {
       const int vi = c * CV + k * kThreads + rl.t;
       // temporal load: pass B reads this chunk again right after
-      if (vi < nvec) v[k].template load<false>(x + off + (int64_t)vi * VEC);
+      if (vi < nvec) v[k].template load<false>(x + ox + (int64_t)vi * VEC);
       else v[k].fill(kNegInf);
     }
     float ml = kNegInf;
@@ -811,7 +812,7 @@ __global__ __launch_bounds__(256) void softmax_split_stats_kernel(const Tin* x, 
 template <typename Tin, typename Tout, int NV, bool LOG>
 __global__ __launch_bounds__(256) void softmax_split_apply_kernel(const Tin* x, Tout* y,
                                                                   const SplitSlot* __restrict__ ws,
-                                                                  int64_t M, int N, int S) {
+                                                                  int64_t M, int N, int S, RowStrides ld) {
   constexpr int VEC = Elem<Tin>::kVec;
   constexpr int kThreads = 256;
   constexpr int CV = kThreads * NV;
@@ -821,12 +822,12 @@ __global__ __launch_bounds__(256) void softmax_split_apply_kernel(const Tin* x, 
   for (int64_t item = blockIdx.x; item < items; item += gridDim.x) {
     const int64_t row = item / S;
     const int c = (int)(item - row * S);
-    const int64_t off = row * (int64_t)N;
+    const int64_t ox = row * ld.x, oy = row * ld.y;
     Packed<Tin, VEC> v[NV];
 #pragma unroll
     for (int k = 0; k < NV; ++k) {
       const int vi = c * CV + k * kThreads + rl.t;
-      if (vi < nvec) v[k].template load<true>(x + off + (int64_t)vi * VEC);
+      if (vi < nvec) v[k].template load<true>(x + ox + (int64_t)vi * VEC);
       else v[k].fill(kNegInf);
     }
     MD p;
@@ -849,7 +850,7 @@ __global__ __launch_bounds__(256) void softmax_split_apply_kernel(const Tin* x, 
       for (int i = 0; i < VEC; ++i)
         o[i] = LOG ? (v[k].get(i) - p.m) - ld : exp_shifted(v[k].get(i) - p.m) * inv_d;
       // plain (write-back) stores: measured faster than non-temporal ones here
-      if (vi < nvec) store_vec<Tout, VEC, false>(y + off + (int64_t)vi * VEC, o);
+      if (vi < nvec) store_vec<Tout, VEC, false>(y + oy + (int64_t)vi * VEC, o);
     }
   }
 }
@@ -883,7 +884,7 @@ constexpr int kSpinLimit = 1 << 22;
 template <typename Tin, typename Tout, int NV>
 __global__ __launch_bounds__(256) void softmax_split_fused_kernel(const Tin* x, Tout* y,
                                                                   SplitSlot* slots_ws, int64_t M,
-                                                                  int N, int S, uint64_t tag) {
+                                                                  int N, int S, uint64_t tag, RowStrides ld) {
   constexpr int VEC = Elem<Tin>::kVec;
   constexpr int kThreads = 256;
   constexpr int CV = kThreads * NV;
@@ -895,12 +896,12 @@ __global__ __launch_bounds__(256) void softmax_split_fused_kernel(const Tin* x, 
   for (int64_t item = blockIdx.x; item < items; item += gridDim.x) {
     const int64_t row = item / S;
     const int c = (int)(item - row * S);
-    const int64_t off = row * (int64_t)N;
+    const int64_t ox = row * ld.x, oy = row * ld.y;
     Packed<Tin, VEC> v[NV];
 #pragma unroll
     for (int k = 0; k < NV; ++k) {
       const int vi = c * CV + k * kThreads + rl.t;
-      if (vi < nvec) v[k].template load<true>(x + off + (int64_t)vi * VEC);
+      if (vi < nvec) v[k].template load<true>(x + ox + (int64_t)vi * VEC);
       else v[k].fill(kNegInf);
     }
     // chunk summary, exactly as the two-kernel form computes it
@@ -952,7 +953,7 @@ __global__ __launch_bounds__(256) void softmax_split_fused_kernel(const Tin* x, 
       float o[VEC];
 #pragma unroll
       for (int i = 0; i < VEC; ++i) o[i] = exp_shifted(v[k].get(i) - q.m) * inv_d;
-      if (vi < nvec) store_vec<Tout, VEC, false>(y + off + (int64_t)vi * VEC, o);
+      if (vi < nvec) store_vec<Tout, VEC, false>(y + oy + (int64_t)vi * VEC, o);
     }
   }
 }
@@ -995,11 +996,11 @@ hipError_t norm_regs(const rr_plan& p, const NormArgs& a, int64_t grid, hipStrea
   // The host never plans more than 16 values per lane for the norms
   // (NV * VEC <= 16), so only those instantiations exist.
   switch (p.vecs_per_lane) {
-    case 1: norm_regs_kernel<T, 1, KIND, WAVE><<<grid1(grid), b, 0, s>>>(yy, rr_, xx, gg, bb, a.M, a.N, a.eps); break;
-    case 2: norm_regs_kernel<T, 2, KIND, WAVE><<<grid1(grid), b, 0, s>>>(yy, rr_, xx, gg, bb, a.M, a.N, a.eps); break;
+    case 1: norm_regs_kernel<T, 1, KIND, WAVE><<<grid1(grid), b, 0, s>>>(yy, rr_, xx, gg, bb, a.M, a.N, a.eps, a.ld); break;
+    case 2: norm_regs_kernel<T, 2, KIND, WAVE><<<grid1(grid), b, 0, s>>>(yy, rr_, xx, gg, bb, a.M, a.N, a.eps, a.ld); break;
     case 4:
       if constexpr (Elem<T>::kVec * 4 <= 16) {
-        norm_regs_kernel<T, 4, KIND, WAVE><<<grid1(grid), b, 0, s>>>(yy, rr_, xx, gg, bb, a.M, a.N, a.eps);
+        norm_regs_kernel<T, 4, KIND, WAVE><<<grid1(grid), b, 0, s>>>(yy, rr_, xx, gg, bb, a.M, a.N, a.eps, a.ld);
         break;
       }
       return hipErrorInvalidValue;
@@ -1017,9 +1018,9 @@ hipError_t norm_loop(const rr_plan& p, const NormArgs& a, int64_t grid, hipStrea
   const T* bb = static_cast<const T*>(a.beta);
   const dim3 b(p.block_threads);
   if (p.vec_elems == 1)
-    norm_loop_kernel<T, 1, KIND><<<grid1(grid), b, 0, s>>>(yy, rr_, xx, gg, bb, a.M, a.N, a.eps);
+    norm_loop_kernel<T, 1, KIND><<<grid1(grid), b, 0, s>>>(yy, rr_, xx, gg, bb, a.M, a.N, a.eps, a.ld);
   else
-    norm_loop_kernel<T, Elem<T>::kVec, KIND><<<grid1(grid), b, 0, s>>>(yy, rr_, xx, gg, bb, a.M, a.N, a.eps);
+    norm_loop_kernel<T, Elem<T>::kVec, KIND><<<grid1(grid), b, 0, s>>>(yy, rr_, xx, gg, bb, a.M, a.N, a.eps, a.ld);
   return hipGetLastError();
 }
 
@@ -1032,12 +1033,12 @@ hipError_t norm_sub(const rr_plan& p, const NormArgs& a, int64_t grid, hipStream
   const T* bb = static_cast<const T*>(a.beta);
   const dim3 b(256);
   switch (p.waves_per_row) {  // for SUBWAVE: lanes per row
-    case 1: norm_sub_kernel<T, VEC, 1, KIND><<<grid1(grid), b, 0, s>>>(yy, rr_, xx, gg, bb, a.M, a.N, a.eps); break;
-    case 2: norm_sub_kernel<T, VEC, 2, KIND><<<grid1(grid), b, 0, s>>>(yy, rr_, xx, gg, bb, a.M, a.N, a.eps); break;
-    case 4: norm_sub_kernel<T, VEC, 4, KIND><<<grid1(grid), b, 0, s>>>(yy, rr_, xx, gg, bb, a.M, a.N, a.eps); break;
-    case 8: norm_sub_kernel<T, VEC, 8, KIND><<<grid1(grid), b, 0, s>>>(yy, rr_, xx, gg, bb, a.M, a.N, a.eps); break;
-    case 16: norm_sub_kernel<T, VEC, 16, KIND><<<grid1(grid), b, 0, s>>>(yy, rr_, xx, gg, bb, a.M, a.N, a.eps); break;
-    case 32: norm_sub_kernel<T, VEC, 32, KIND><<<grid1(grid), b, 0, s>>>(yy, rr_, xx, gg, bb, a.M, a.N, a.eps); break;
+    case 1: norm_sub_kernel<T, VEC, 1, KIND><<<grid1(grid), b, 0, s>>>(yy, rr_, xx, gg, bb, a.M, a.N, a.eps, a.ld); break;
+    case 2: norm_sub_kernel<T, VEC, 2, KIND><<<grid1(grid), b, 0, s>>>(yy, rr_, xx, gg, bb, a.M, a.N, a.eps, a.ld); break;
+    case 4: norm_sub_kernel<T, VEC, 4, KIND><<<grid1(grid), b, 0, s>>>(yy, rr_, xx, gg, bb, a.M, a.N, a.eps, a.ld); break;
+    case 8: norm_sub_kernel<T, VEC, 8, KIND><<<grid1(grid), b, 0, s>>>(yy, rr_, xx, gg, bb, a.M, a.N, a.eps, a.ld); break;
+    case 16: norm_sub_kernel<T, VEC, 16, KIND><<<grid1(grid), b, 0, s>>>(yy, rr_, xx, gg, bb, a.M, a.N, a.eps, a.ld); break;
+    case 32: norm_sub_kernel<T, VEC, 32, KIND><<<grid1(grid), b, 0, s>>>(yy, rr_, xx, gg, bb, a.M, a.N, a.eps, a.ld); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -1074,6 +1075,7 @@ struct SmCall {
   int N;
   int64_t cp;
   int64_t co;
+  RowStrides ld;
 };
 
 template <typename Tin, typename Tout, bool WAVE, bool LOG, bool CAUSAL>
@@ -1082,12 +1084,12 @@ hipError_t softmax_regs(const rr_plan& p, const SmCall<Tin, Tout>& c, int64_t gr
   const dim3 g = grid1(grid);
   // At most 32 values per lane (NV * VEC <= 32).
   switch (p.vecs_per_lane) {
-    case 1: softmax_regs_kernel<Tin, Tout, 1, WAVE, LOG, CAUSAL><<<g, b, 0, s>>>(c.x, c.y, c.M, c.N, c.cp, c.co); break;
-    case 2: softmax_regs_kernel<Tin, Tout, 2, WAVE, LOG, CAUSAL><<<g, b, 0, s>>>(c.x, c.y, c.M, c.N, c.cp, c.co); break;
-    case 4: softmax_regs_kernel<Tin, Tout, 4, WAVE, LOG, CAUSAL><<<g, b, 0, s>>>(c.x, c.y, c.M, c.N, c.cp, c.co); break;
+    case 1: softmax_regs_kernel<Tin, Tout, 1, WAVE, LOG, CAUSAL><<<g, b, 0, s>>>(c.x, c.y, c.M, c.N, c.cp, c.co, c.ld); break;
+    case 2: softmax_regs_kernel<Tin, Tout, 2, WAVE, LOG, CAUSAL><<<g, b, 0, s>>>(c.x, c.y, c.M, c.N, c.cp, c.co, c.ld); break;
+    case 4: softmax_regs_kernel<Tin, Tout, 4, WAVE, LOG, CAUSAL><<<g, b, 0, s>>>(c.x, c.y, c.M, c.N, c.cp, c.co, c.ld); break;
     case 8:
       if constexpr (Elem<Tin>::kVec * 8 <= 32) {
-        softmax_regs_kernel<Tin, Tout, 8, WAVE, LOG, CAUSAL><<<g, b, 0, s>>>(c.x, c.y, c.M, c.N, c.cp, c.co);
+        softmax_regs_kernel<Tin, Tout, 8, WAVE, LOG, CAUSAL><<<g, b, 0, s>>>(c.x, c.y, c.M, c.N, c.cp, c.co, c.ld);
         break;
       }
       return hipErrorInvalidValue;
@@ -1145,13 +1147,15 @@ hipError_t softmax_split(const rr_plan& p, const SmCall<Tin, Tout>& c, SplitSlot
         Tout* yy = c.y;
         int64_t m64 = c.M;
         int n32 = c.N;
-        void* args[] = {(void*)&xx, (void*)&yy, (void*)&w, (void*)&m64, (void*)&n32, (void*)&S, (void*)&tag};
+        RowStrides ld = c.ld;
+        void* args[] = {(void*)&xx, (void*)&yy, (void*)&w, (void*)&m64, (void*)&n32, (void*)&S, (void*)&tag,
+                        (void*)&ld};
         return hipLaunchCooperativeKernel(k, grid1(g), b, args, 0, s);
       }
     }
   }
-  softmax_split_stats_kernel<Tin, NV><<<grid1(grid), b, 0, s>>>(c.x, w, c.M, c.N, S);
-  softmax_split_apply_kernel<Tin, Tout, NV, LOG><<<grid1(grid), b, 0, s>>>(c.x, c.y, w, c.M, c.N, S);
+  softmax_split_stats_kernel<Tin, NV><<<grid1(grid), b, 0, s>>>(c.x, w, c.M, c.N, S, c.ld);
+  softmax_split_apply_kernel<Tin, Tout, NV, LOG><<<grid1(grid), b, 0, s>>>(c.x, c.y, w, c.M, c.N, S, c.ld);
   return hipGetLastError();
 }
 
@@ -1160,12 +1164,12 @@ hipError_t softmax_sub(const rr_plan& p, const SmCall<Tin, Tout>& c, int64_t gri
   const dim3 b(256);
   const dim3 g = grid1(grid);
   switch (p.waves_per_row) {  // for SUBWAVE: lanes per row
-    case 1: softmax_sub_kernel<Tin, Tout, VEC, 1, LOG, CAUSAL><<<g, b, 0, s>>>(c.x, c.y, c.M, c.N, c.cp, c.co); break;
-    case 2: softmax_sub_kernel<Tin, Tout, VEC, 2, LOG, CAUSAL><<<g, b, 0, s>>>(c.x, c.y, c.M, c.N, c.cp, c.co); break;
-    case 4: softmax_sub_kernel<Tin, Tout, VEC, 4, LOG, CAUSAL><<<g, b, 0, s>>>(c.x, c.y, c.M, c.N, c.cp, c.co); break;
-    case 8: softmax_sub_kernel<Tin, Tout, VEC, 8, LOG, CAUSAL><<<g, b, 0, s>>>(c.x, c.y, c.M, c.N, c.cp, c.co); break;
-    case 16: softmax_sub_kernel<Tin, Tout, VEC, 16, LOG, CAUSAL><<<g, b, 0, s>>>(c.x, c.y, c.M, c.N, c.cp, c.co); break;
-    case 32: softmax_sub_kernel<Tin, Tout, VEC, 32, LOG, CAUSAL><<<g, b, 0, s>>>(c.x, c.y, c.M, c.N, c.cp, c.co); break;
+    case 1: softmax_sub_kernel<Tin, Tout, VEC, 1, LOG, CAUSAL><<<g, b, 0, s>>>(c.x, c.y, c.M, c.N, c.cp, c.co, c.ld); break;
+    case 2: softmax_sub_kernel<Tin, Tout, VEC, 2, LOG, CAUSAL><<<g, b, 0, s>>>(c.x, c.y, c.M, c.N, c.cp, c.co, c.ld); break;
+    case 4: softmax_sub_kernel<Tin, Tout, VEC, 4, LOG, CAUSAL><<<g, b, 0, s>>>(c.x, c.y, c.M, c.N, c.cp, c.co, c.ld); break;
+    case 8: softmax_sub_kernel<Tin, Tout, VEC, 8, LOG, CAUSAL><<<g, b, 0, s>>>(c.x, c.y, c.M, c.N, c.cp, c.co, c.ld); break;
+    case 16: softmax_sub_kernel<Tin, Tout, VEC, 16, LOG, CAUSAL><<<g, b, 0, s>>>(c.x, c.y, c.M, c.N, c.cp, c.co, c.ld); break;
+    case 32: softmax_sub_kernel<Tin, Tout, VEC, 32, LOG, CAUSAL><<<g, b, 0, s>>>(c.x, c.y, c.M, c.N, c.cp, c.co, c.ld); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -1182,9 +1186,9 @@ hipError_t softmax_typed(const rr_plan& p, const SmCall<Tin, Tout>& c, void* ws,
   }
   if (p.variant == RR_VARIANT_LOOP) {
     if (p.vec_elems == 1)
-      softmax_loop_kernel<Tin, Tout, 1, LOG, CAUSAL><<<g, b, 0, s>>>(c.x, c.y, c.M, c.N, c.cp, c.co);
+      softmax_loop_kernel<Tin, Tout, 1, LOG, CAUSAL><<<g, b, 0, s>>>(c.x, c.y, c.M, c.N, c.cp, c.co, c.ld);
     else
-      softmax_loop_kernel<Tin, Tout, Elem<Tin>::kVec, LOG, CAUSAL><<<g, b, 0, s>>>(c.x, c.y, c.M, c.N, c.cp, c.co);
+      softmax_loop_kernel<Tin, Tout, Elem<Tin>::kVec, LOG, CAUSAL><<<g, b, 0, s>>>(c.x, c.y, c.M, c.N, c.cp, c.co, c.ld);
     return hipGetLastError();
   }
   if (p.variant == RR_VARIANT_SPLIT || p.variant == RR_VARIANT_SPLIT_ONE_KERNEL) {
@@ -1202,10 +1206,10 @@ hipError_t softmax_typed(const rr_plan& p, const SmCall<Tin, Tout>& c, void* ws,
   if (p.vecs_per_lane * Elem<Tin>::kVec > 32) {
     // long rows held in their storage format (see softmax_packed_kernel)
     switch (p.vecs_per_lane) {
-      case 12: softmax_packed_kernel<Tin, Tout, 12, LOG, CAUSAL><<<g, b, 0, s>>>(c.x, c.y, c.M, c.N, c.cp, c.co); break;
-      case 16: softmax_packed_kernel<Tin, Tout, 16, LOG, CAUSAL><<<g, b, 0, s>>>(c.x, c.y, c.M, c.N, c.cp, c.co); break;
-      case 19: softmax_packed_kernel<Tin, Tout, 19, LOG, CAUSAL><<<g, b, 0, s>>>(c.x, c.y, c.M, c.N, c.cp, c.co); break;
-      case 20: softmax_packed_kernel<Tin, Tout, 20, LOG, CAUSAL><<<g, b, 0, s>>>(c.x, c.y, c.M, c.N, c.cp, c.co); break;
+      case 12: softmax_packed_kernel<Tin, Tout, 12, LOG, CAUSAL><<<g, b, 0, s>>>(c.x, c.y, c.M, c.N, c.cp, c.co, c.ld); break;
+      case 16: softmax_packed_kernel<Tin, Tout, 16, LOG, CAUSAL><<<g, b, 0, s>>>(c.x, c.y, c.M, c.N, c.cp, c.co, c.ld); break;
+      case 19: softmax_packed_kernel<Tin, Tout, 19, LOG, CAUSAL><<<g, b, 0, s>>>(c.x, c.y, c.M, c.N, c.cp, c.co, c.ld); break;
+      case 20: softmax_packed_kernel<Tin, Tout, 20, LOG, CAUSAL><<<g, b, 0, s>>>(c.x, c.y, c.M, c.N, c.cp, c.co, c.ld); break;
       default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
@@ -1222,6 +1226,7 @@ hipError_t softmax_io(const rr_plan& p, const SoftmaxArgs& a, int64_t grid, hipS
   c.N = a.N;
   c.cp = a.causal_period;
   c.co = a.causal_offset;
+  c.ld = a.ld;
   // the causal rule and log output are compile-time switches, so the plain
   // softmax kernels carry none of their code
   if (c.cp > 0) {

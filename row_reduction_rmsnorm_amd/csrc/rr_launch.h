@@ -13,6 +13,14 @@ namespace rr {
 // the width of the DPP row that combines the per-wavefront LDS slots.
 constexpr int kMaxWavesPerGroup = 16;
 
+// Row strides in elements: row i of x starts at x + i * x (likewise y and
+// the fused op's residual r).  A contiguous [M, N] matrix has stride N.
+struct RowStrides {
+  int64_t x;
+  int64_t y;
+  int64_t r;
+};
+
 // Arguments of the norm kernels (residual only for the fused op, beta only
 // for LayerNorm and possibly null).
 struct NormArgs {
@@ -24,6 +32,7 @@ struct NormArgs {
   int64_t M;
   int32_t N;
   float eps;
+  RowStrides ld;
 };
 
 // Operation codes for launch_norm.
@@ -47,6 +56,7 @@ struct SoftmaxArgs {
   int64_t causal_period;
   int64_t causal_offset;
   int log_output;
+  RowStrides ld;   // r unused
 };
 
 // Enqueue the softmax kernel(s) that `plan` names (two for SPLIT).

@@ -175,6 +175,46 @@ def test_softmax_causal_plans():
         rr.rr_set_variant_override(rr.RR_VARIANT_AUTO)
 
 
+def test_strided_validation():
+    """Stride bounds and the aliasing rules of the strided entry points (all
+    rejected on the host before anything is enqueued)."""
+    F, B, I = rr.RR_F32, rr.RR_BF16, rr.RR_ERR_INVALID_ARG
+    X, Y, R, G = P, P << 4, P << 8, P << 12
+    H = 64
+    rms = rr.raw_rmsnorm_strided
+    # strides below the row width, or absurdly large
+    assert rms(Y, H, X, H - 1, G, 4, H, 1e-6, F, None) == I and "ldx" in rr.last_error_message()
+    assert rms(Y, 0, X, H, G, 4, H, 1e-6, F, None) == I and "ldy" in rr.last_error_message()
+    assert rms(Y, 1 << 41, X, H, G, 4, H, 1e-6, F, None) == I
+    # y inside x's rows (same stride, overlapping column windows)
+    assert rms(X + 4, 2 * H, X, 2 * H, G, 4, H, 1e-6, F, None) == I
+    assert "overlaps" in rr.last_error_message()
+    # in place needs the same stride
+    assert rms(X, 2 * H, X, H, G, 4, H, 1e-6, F, None) == I
+    # different strides with intersecting spans count as overlapping
+    assert rms(X + 4 * H, 3 * H, X, 2 * H, G, 4, H, 1e-6, F, None) == I
+    # gamma inside y's span
+    assert rms(Y, 2 * H, X, H, Y + 4 * H, 4, H, 1e-6, F, None) == I
+    # fused: the residual's window overlaps x's
+    fz = rr.raw_fused_add_rmsnorm_strided
+    assert fz(Y, H, X + 8, 2 * H, X, 2 * H, G, 4, H, 1e-6, B, None) == I
+    assert "residual" in rr.last_error_message()
+    assert fz(Y, H, R, H - 8, X, H, G, 4, H, 1e-6, B, None) == I and "ldr" in rr.last_error_message()
+    # layernorm: beta inside y's span
+    ln = rr.raw_layernorm_strided
+    assert ln(Y, 2 * H, X, H, G, Y + 4, 4, H, 1e-5, F, None) == I
+    # softmax: in place needs equal pointers, strides and dtypes
+    sm = rr.raw_softmax_rows_strided
+    assert sm(X, 2 * H, X, H, 4, H, F, F, None, None, 0, None) == I
+    assert sm(X, H, X, H, 4, H, B, F, None, None, 0, None) == I
+    assert sm(Y, H, X, H - 1, 4, H, F, F, None, None, 0, None) == I
+    # options are still checked
+    assert sm(Y, H, X, H, 4, H, F, F, rr.make_softmax_opts(causal_period=0), None, 0, None) == I
+    # M == 0 is a no-op whatever the pointers
+    assert rms(None, H, None, H, None, 0, H, 1e-6, F, None) == rr.RR_OK
+    assert sm(None, H, None, H, 0, H, F, F, None, None, 0, None) == rr.RR_OK
+
+
 # ----------------------------------------------------------------------------
 # dispatch (the variant choice by row length)
 # ----------------------------------------------------------------------------

@@ -1,0 +1,181 @@
+"""GPU parity of the strided entry points: rows that are column slices of
+wider matrices (a row stride larger than the width), against the fp64
+oracle on the same rows gathered contiguously.
+
+Checked as well: the elements between the slices are never written, the
+strided calls with stride equal to the width give the bits of the
+contiguous calls, outputs into another column slice of the input's own
+buffer, the fused op writing its output back into its strided input, and
+unaligned strides (the scalar path).
+"""
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from tests import compare
+from tests.test_parity_gpu import (DTYPES, _as, _bits, _rr, _say, _tdt, check_fused, check_norm,
+                                   softmax_input)
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+SENTINEL = 7.25   # exact in fp32 and bf16
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    rr = _rr()
+    rr.lib()
+    rr.rr_set_variant_override(rr.RR_VARIANT_AUTO)
+    yield
+    rr.rr_set_variant_override(rr.RR_VARIANT_AUTO)
+
+
+def embed(rows_cpu, ld, col0, fill=SENTINEL):
+    """A [M, ld] device buffer holding rows_cpu in columns col0 .. col0+N-1
+    and `fill` elsewhere; returns (buffer, view of the rows)."""
+    M, N = rows_cpu.shape
+    buf = torch.full((M, ld), fill, dtype=rows_cpu.dtype, device="cuda")
+    buf[:, col0:col0 + N] = rows_cpu.cuda()
+    return buf, buf[:, col0:col0 + N]
+
+
+def untouched(buf, col0, N, what):
+    """Every element outside columns col0 .. col0+N-1 still holds SENTINEL."""
+    b = buf.float().cpu()
+    mask = torch.ones(b.shape, dtype=torch.bool)
+    mask[:, col0:col0 + N] = False
+    assert bool((b[mask] == SENTINEL).all()), f"{what}: wrote outside the slice"
+
+
+# (M, N, ld_x, col_x, ld_y, col_y): aligned strides on each path (short rows,
+# a wavefront per row, a workgroup per row, streaming), and unaligned strides
+# or column offsets (the scalar path)
+NORM_CASES = [
+    (100, 24, 64, 8, 40, 16),
+    (33, 1024, 3072, 1024, 1536, 512),
+    (9, 4096, 12288, 4096, 8192, 0),
+    (7, 20000, 20480, 0, 24576, 4096),
+    (17, 1000, 1003, 3, 1001, 1),
+    (5, 3584, 3592, 8, 3584, 0),
+]
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("case", NORM_CASES, ids=lambda c: "x".join(map(str, c)))
+def test_rmsnorm_and_layernorm_strided(case, dt):
+    rr = _rr()
+    M, N, ldx, cx, ldy, cy = case
+    _say(f"strided norms {dt} {case}")
+    x_cpu = _as(workloads.random_rows(M, N, seed=M + N), dt)
+    g_cpu = _as(workloads.gamma_vector(N, seed=N), dt)
+    b_cpu = _as(workloads.gamma_vector(N, seed=N + 1) - 1.0, dt)
+    xbuf, xv = embed(x_cpu, ldx, cx)
+    ybuf, yv = embed(torch.zeros(M, N, dtype=_tdt(dt)), ldy, cy)
+    rr.rr_rmsnorm_strided(yv, xv, g_cpu.cuda(), 1e-6)
+    torch.cuda.synchronize()
+    check_norm(x_cpu, g_cpu, 1e-6, dt, yv.cpu(), f"rms strided {dt} {case}")
+    untouched(ybuf, cy, N, "rms y")
+    untouched(xbuf, cx, N, "rms x")
+    rr.rr_layernorm_strided(yv, xv, g_cpu.cuda(), b_cpu.cuda(), 1e-5)
+    torch.cuda.synchronize()
+    ref = oracle.layernorm(compare.to_f64(x_cpu), compare.to_f64(g_cpu), compare.to_f64(b_cpu), 1e-5)
+    compare.check_layernorm(yv.cpu(), ref, compare.to_f64(g_cpu), compare.to_f64(b_cpu),
+                            f"layernorm strided {dt} {case}")
+    untouched(ybuf, cy, N, "layernorm y")
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("case", NORM_CASES, ids=lambda c: "x".join(map(str, c)))
+def test_fused_strided_output_into_input(case, dt):
+    """vLLM's layout: x is a strided slice, the residual is its own
+    (here also strided) matrix, and y is written back over x."""
+    rr = _rr()
+    M, N, ldx, cx, ldr, cr = case
+    _say(f"strided fused {dt} {case}")
+    x_cpu = _as(workloads.random_rows(M, N, seed=2 * M + N), dt)
+    r_cpu = _as(workloads.random_rows(M, N, seed=3 * M + N), dt)
+    g_cpu = _as(workloads.gamma_vector(N, seed=N + 2), dt)
+    xbuf, xv = embed(x_cpu, ldx, cx)
+    rbuf, rv = embed(r_cpu, ldr, cr)
+    rr.rr_fused_add_rmsnorm_strided(xv, rv, xv, g_cpu.cuda(), 1e-6)
+    torch.cuda.synchronize()
+    check_fused(x_cpu, r_cpu, g_cpu, 1e-6, dt, xv.cpu(), rv.cpu(), f"fused strided {dt} {case}")
+    untouched(xbuf, cx, N, "fused x/y")
+    untouched(rbuf, cr, N, "fused residual")
+
+
+STRIDED_SOFTMAX = [
+    # M, N, ld_x, col_x, ld_y, col_y
+    (300, 16, 48, 16, 16, 0),
+    (64, 1024, 4096, 2048, 1024, 0),
+    (20, 4096, 8192, 4096, 4104, 8),
+    (9, 40000, 40008, 8, 40000, 0),
+    (3, 152064, 152080, 16, 152072, 8),
+    (11, 999, 1000, 1, 1003, 2),
+]
+
+
+@pytest.mark.parametrize("log_output", [False, True])
+@pytest.mark.parametrize("din,dout", DTYPES)
+@pytest.mark.parametrize("case", STRIDED_SOFTMAX, ids=lambda c: "x".join(map(str, c)))
+def test_softmax_strided(case, din, dout, log_output):
+    rr = _rr()
+    M, N, ldx, cx, ldy, cy = case
+    _say(f"strided softmax {din}->{dout} log={log_output} {case}")
+    x_cpu = softmax_input(M, N, seed=M * 7 + N, dt=din)
+    xbuf, xv = embed(x_cpu, ldx, cx)
+    ybuf, yv = embed(torch.zeros(M, N, dtype=_tdt(dout)), ldy, cy)
+    opts = rr.make_softmax_opts(log_output=log_output)
+    n = rr.rr_softmax_rows_ex_workspace_bytes(M, N, rr.dtype_code(xv), rr.dtype_code(yv), opts)
+    ws = torch.empty(n, dtype=torch.uint8, device="cuda") if n else None
+    rr.rr_softmax_rows_strided(yv, xv, opts, ws)
+    torch.cuda.synchronize()
+    xf = compare.to_f64(x_cpu)
+    if log_output:
+        compare.check_log_softmax(yv.cpu(), xf, oracle.log_softmax(xf), f"log strided {case}")
+    else:
+        compare.check_softmax(yv.cpu(), xf, oracle.softmax(xf), f"softmax strided {case}")
+    untouched(ybuf, cy, N, "softmax y")
+
+
+def test_softmax_strided_causal_into_own_buffer():
+    """Scores as column slices of one buffer, probabilities written into the
+    buffer's other half: disjoint column windows with one stride are not an
+    overlap.  The causal rule reads only kept keys."""
+    rr = _rr()
+    M, N = 64, 1024
+    x_cpu = softmax_input(M, N, seed=77, dt="f32")
+    buf = torch.full((M, 2 * N), SENTINEL, device="cuda")
+    buf[:, :N] = x_cpu.cuda()
+    xv, yv = buf[:, :N], buf[:, N:]
+    rr.rr_softmax_rows_strided(yv, xv, rr.make_softmax_opts(causal_period=M, causal_offset=N - M))
+    torch.cuda.synchronize()
+    xf = compare.to_f64(x_cpu)
+    keys = np.minimum(N, np.arange(M) % M + (N - M) + 1)
+    xf[np.arange(N)[None, :] >= keys[:, None]] = -np.inf
+    compare.check_softmax(yv.cpu(), xf, oracle.softmax(xf), "causal strided own buffer")
+    assert torch.equal(buf[:, :N].cpu(), x_cpu), "input half changed"
+
+
+def test_stride_equal_to_width_is_the_contiguous_call_bitwise():
+    rr = _rr()
+    for dt in ("f32", "bf16"):
+        M, N = 64, 4096
+        x = _as(workloads.random_rows(M, N, seed=5), dt).cuda()
+        g = _as(workloads.gamma_vector(N, seed=6), dt).cuda()
+        a, b = torch.empty_like(x), torch.empty_like(x)
+        rr.rr_rmsnorm(a, x, g, 1e-6)
+        rr.rr_rmsnorm_strided(b, x, g, 1e-6)
+        torch.cuda.synchronize()
+        assert torch.equal(_bits(a), _bits(b))
+        s = softmax_input(M, N, seed=9, dt=dt).cuda()
+        a = torch.empty(M, N, device="cuda")
+        b = torch.empty_like(a)
+        rr.rr_softmax_rows(a, s, None)
+        rr.rr_softmax_rows_strided(b, s)
+        torch.cuda.synchronize()
+        assert torch.equal(_bits(a), _bits(b))
