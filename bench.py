@@ -185,7 +185,11 @@ def measure_extras(torch, rr, dev, K, bufs):
     import workloads
     out = {}
 
-    def timed(name, fn, nbytes, M):
+    def timed(name, fn, nbytes, M, graph=False):
+        """K launches between two events.  graph=True also replays the K
+        launches captured in one HIP graph, which removes the host's launch
+        cost between them: for the small latency-bound cases the eager figure
+        is the host's launch rate, the graph figure the device's."""
         fn()
         torch.cuda.synchronize()
         a = torch.cuda.Event(enable_timing=True)
@@ -198,16 +202,32 @@ def measure_extras(torch, rr, dev, K, bufs):
         us = a.elapsed_time(b) / K * 1e3
         out[name] = {"us": round(us, 2), "bytes": nbytes, "GBps": round(nbytes / (us * 1e-6) / 1e9, 1),
                      "rows_per_s": round(M / (us * 1e-6), 1)}
+        if graph:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for _ in range(K):
+                    fn()
+            g.replay()
+            torch.cuda.synchronize()
+            a.record()
+            g.replay()
+            b.record()
+            torch.cuda.synchronize()
+            gus = a.elapsed_time(b) / K * 1e3
+            out[name].update({"graph_us": round(gus, 2),
+                              "graph_GBps": round(nbytes / (gus * 1e-6) / 1e9, 1),
+                              "graph_rows_per_s": round(M / (gus * 1e-6), 1)})
 
     w = workloads.make("rms_f32")
     x, g = w.arrays["x"].to(dev), w.arrays["gamma"].to(dev)
     y = torch.empty_like(x)
-    timed("rms_f32_64x3584", lambda: rr.rr_rmsnorm(y, x, g, w.eps), algorithmic_bytes("rms_f32", w.M, w.N), w.M)
+    timed("rms_f32_64x3584", lambda: rr.rr_rmsnorm(y, x, g, w.eps), algorithmic_bytes("rms_f32", w.M, w.N), w.M,
+          graph=True)
     w = workloads.make("layernorm")
     x, g, bt = (w.arrays[k].to(dev) for k in ("x", "gamma", "beta"))
     y = torch.empty_like(x)
     timed("layernorm_f32_256x5120", lambda: rr.rr_layernorm(y, x, g, bt, w.eps),
-          2 * w.M * w.N * 4 + 2 * w.N * 4, w.M)
+          2 * w.M * w.N * 4 + 2 * w.N * 4, w.M, graph=True)
     rng = np.random.default_rng(0)
     M, N = 8192, 4096
     x = workloads.to_dtype(rng.standard_normal((M, N), dtype=np.float32), "bf16").to(dev)

@@ -28,7 +28,12 @@
  *     fp32; bf16 inputs widen exactly and outputs round to nearest even once.
  *   - Streams: `stream` is a hipStream_t (NULL = the null stream).  Calls are
  *     asynchronous: they enqueue kernels and return; the caller synchronises.
- *     Same-stream order is the only ordering the library relies on.
+ *     Same-stream order is the only ordering the library relies on.  The
+ *     calls only enqueue kernels (no memsets, copies or host callbacks), so
+ *     a caller may capture them into a HIP graph; a captured call reads its
+ *     buffers when the graph replays.  The opt-in one-kernel split variant
+ *     (RR_VARIANT_SPLIT_ONE_KERNEL) is the exception: its workspace tags
+ *     are chosen at launch, so it must not be captured.
  *   - Errors: arguments are checked on the host before anything is enqueued;
  *     a failed check returns a non-zero rr_status and enqueues nothing.
  *     M == 0 is a successful no-op.  An empty row (N or H < 1) is the

@@ -1,0 +1,81 @@
+"""The kernels captured in a HIP graph: every replay matches the eager result
+bitwise.
+
+The library launches on the caller's stream and records no memset or host
+work into it, so a caller may capture its calls.  Replays run with eager
+work and synchronisations between them, on inputs changed between replays
+(the graph reads its buffers at replay time), and each replay is checked
+against an eager call on the same inputs.
+"""
+import pytest
+
+import workloads
+from tests.test_parity_gpu import _as, _bits, _rr, _say, softmax_input
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    rr = _rr()
+    rr.lib()
+    rr.rr_set_variant_override(rr.RR_VARIANT_AUTO)
+    yield
+    rr.rr_set_variant_override(rr.RR_VARIANT_AUTO)
+
+
+def test_graph_replays_match_eager():
+    rr = _rr()
+    M, H = 64, 4096
+    x = _as(workloads.random_rows(M, H, seed=1), "bf16").cuda()
+    r0 = _as(workloads.random_rows(M, H, seed=2), "bf16").cuda()
+    g = _as(workloads.gamma_vector(H, seed=3), "bf16").cuda()
+    res = r0.clone()
+    y = torch.empty_like(x)
+    s = softmax_input(40, 152064, seed=4, dt="bf16").cuda()          # the split path, with workspace
+    sy = torch.empty(s.shape, dtype=torch.float32, device="cuda")
+    ws = rr.softmax_workspace(s, torch.float32)
+    c = softmax_input(300, 4096, seed=5, dt="f32").cuda()            # causal rule, log output
+    cy = torch.empty_like(c)
+    opts = rr.make_softmax_opts(log_output=True, causal_period=300, causal_offset=3796)
+
+    def step():
+        rr.rr_fused_add_rmsnorm(y, res, x, g, 1e-6)
+        rr.rr_softmax_rows(sy, s, ws)
+        rr.rr_softmax_rows_ex(cy, c, opts)
+
+    def eager_reference():
+        """Outputs of one eager step from the current inputs, leaving them as they were."""
+        keep = res.clone()
+        step()
+        torch.cuda.synchronize()
+        out = (y.clone(), res.clone(), sy.clone(), cy.clone())
+        res.copy_(keep)
+        return out
+
+    step()                       # warm-up outside the capture
+    torch.cuda.synchronize()
+    res.copy_(r0)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    torch.cuda.synchronize()
+    for k in range(4):
+        _say(f"graph replay {k}")
+        # new inputs in place: the replay must read them
+        x.copy_(_as(workloads.random_rows(M, H, seed=10 + k), "bf16").cuda())
+        res.copy_(r0)
+        s.mul_(0.5)
+        c.add_(1.0)
+        ref = eager_reference()
+        y.zero_()
+        sy.zero_()
+        cy.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        for got, want, what in zip((y, res, sy, cy), ref, ("fused y", "residual", "split softmax", "causal log")):
+            assert torch.equal(_bits(got), _bits(want)), f"replay {k}: {what}"
+        torch.cuda.synchronize()
