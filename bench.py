@@ -11,11 +11,12 @@ buffers with inputs already resident in HBM:
   sm_causal  softmax fp32 -> fp32, 28*4096 x 4096, causal -inf mask (a workgroup per row)
 
 value = algorithmic bytes of one step (each input read once, each output
-written once, gamma once) / measured time of one step.  The 3.76 GB causal
-softmax in every step pushes the other workloads' buffers out of the 256 MB
-last-level cache between their repetitions, so every kernel starts cold.
-The fused op updates its residual in place each step; that changes the
-values, not the work.
+written once, gamma once) / measured time of one step.  Every workload but
+the 3.76 GB causal softmax has ROTATE copies of its buffers, and step k uses
+copy k mod ROTATE, so between two uses of a buffer more than the 256 MB
+last-level cache has streamed through and every kernel starts cold (the
+causal softmax's own footprint is 15 times that cache).  The fused op updates
+its residual in place each step; that changes the values, not the work.
 
 Two timed regions of K steps each, on the launch stream: the first has HIP
 events only around the K steps and gives the value; the second records an
@@ -47,6 +48,7 @@ KERNEL_SOURCES = ("row_reduction_rmsnorm_amd/csrc/rr_kernels.hip",
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_sm_causal_softmax_block.json")
 
 OPS = ("fused", "rms_bf16", "sm_wave", "sm_vocab", "sm_causal")
+ROTATE = 4   # buffer copies of every workload but sm_causal
 
 
 def kernel_source_sha():
@@ -77,40 +79,63 @@ def log(*a):
 
 
 def setup(torch, dev):
+    """bufs[name]: the workload's first buffer set (with M, N) and, under
+    "sets", all its copies (set 0 first).  Copies hold the same values at
+    other addresses."""
     import workloads
     import row_reduction_rmsnorm_amd as rr
     bufs = {}
     t0 = time.time()
     w = workloads.make("fused")
     x = w.arrays["x"].to(dev)
-    bufs["fused"] = dict(x=x, r=w.arrays["residual"].to(dev), g=w.arrays["gamma"].to(dev),
-                         y=torch.empty_like(x), M=w.M, N=w.N, eps=w.eps,
-                         r0=w.arrays["residual"])
-    # a copy of x of its own, so the RMSNorm never finds the fused op's input in a cache
-    bufs["rms_bf16"] = dict(x=x.clone(), g=bufs["fused"]["g"], y=torch.empty_like(x), M=w.M, N=w.N,
-                            eps=w.eps)
+    g = w.arrays["gamma"].to(dev)
+    r = w.arrays["residual"].to(dev)
+    bufs["fused"] = [dict(x=x.clone(), r=r.clone(), g=g, y=torch.empty_like(x), M=w.M, N=w.N,
+                          eps=w.eps, r0=w.arrays["residual"]) for _ in range(ROTATE)]
+    # copies of x of their own, so the RMSNorm never finds the fused op's input in a cache
+    bufs["rms_bf16"] = [dict(x=x.clone(), g=g, y=torch.empty_like(x), M=w.M, N=w.N, eps=w.eps)
+                        for _ in range(ROTATE)]
+    del x, r
     for name in ("sm_wave", "sm_vocab", "sm_causal"):
         w = workloads.make(name)
         xs = w.arrays["x"].to(dev)
-        y = torch.empty(xs.shape, dtype=torch.float32, device=dev)
-        bufs[name] = dict(x=xs, y=y, ws=rr.softmax_workspace(xs, torch.float32), M=w.M, N=w.N)
+        n = 1 if name == "sm_causal" else ROTATE
+        sets = []
+        for i in range(n):
+            xi = xs if i == n - 1 else xs.clone()
+            y = torch.empty(xs.shape, dtype=torch.float32, device=dev)
+            sets.append(dict(x=xi, y=y, ws=rr.softmax_workspace(xi, torch.float32), M=w.M, N=w.N))
+        bufs[name] = sets
+    for name in list(bufs):
+        sets = bufs[name]
+        bufs[name] = dict(sets[0], sets=sets)
     torch.cuda.synchronize()
     log(f"[bench] inputs generated and resident in HBM ({time.time() - t0:.1f} s)")
     return bufs
 
 
 def make_ops(rr, bufs):
-    b = bufs
-    return {
-        "fused": lambda: rr.rr_fused_add_rmsnorm(b["fused"]["y"], b["fused"]["r"], b["fused"]["x"],
-                                                 b["fused"]["g"], b["fused"]["eps"]),
-        "rms_bf16": lambda: rr.rr_rmsnorm(b["rms_bf16"]["y"], b["rms_bf16"]["x"],
-                                          b["rms_bf16"]["g"], b["rms_bf16"]["eps"]),
-        "sm_wave": lambda: rr.rr_softmax_rows(b["sm_wave"]["y"], b["sm_wave"]["x"], b["sm_wave"]["ws"]),
-        "sm_vocab": lambda: rr.rr_softmax_rows(b["sm_vocab"]["y"], b["sm_vocab"]["x"], b["sm_vocab"]["ws"]),
-        "sm_causal": lambda: rr.rr_softmax_rows(b["sm_causal"]["y"], b["sm_causal"]["x"],
-                                                b["sm_causal"]["ws"]),
-    }
+    """name -> fn(k): the operation on buffer set k mod (number of sets)."""
+    def pick(name, k):
+        sets = bufs[name]["sets"]
+        return sets[k % len(sets)]
+
+    def fused(k):
+        b = pick("fused", k)
+        rr.rr_fused_add_rmsnorm(b["y"], b["r"], b["x"], b["g"], b["eps"])
+
+    def rms(k):
+        b = pick("rms_bf16", k)
+        rr.rr_rmsnorm(b["y"], b["x"], b["g"], b["eps"])
+
+    def softmax(name):
+        def run(k):
+            b = pick(name, k)
+            rr.rr_softmax_rows(b["y"], b["x"], b["ws"])
+        return run
+
+    return {"fused": fused, "rms_bf16": rms, "sm_wave": softmax("sm_wave"),
+            "sm_vocab": softmax("sm_vocab"), "sm_causal": softmax("sm_causal")}
 
 
 def sanity(torch, bufs):
@@ -250,6 +275,45 @@ def measure_extras(torch, rr, dev, K, bufs):
     return out
 
 
+def measure_copy_reference(torch, dev, ops, bufs, reps=15):
+    """Each step operation against a plain elementwise pass that moves the
+    same bytes (torch.abs: half the bytes read, half written), both timed the
+    same way: one launch between two events, after writing 512 MiB elsewhere
+    so that neither finds its data in a cache; median of `reps`.  At these
+    sizes a kernel's fixed start-up and drain time is a visible share of its
+    duration, so this, not 8 TB/s, is the practical bar for each size."""
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+
+    def cold_us(fn):
+        ts = []
+        for _ in range(reps):
+            flush.zero_()
+            a.record()
+            fn()
+            b.record()
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b) * 1e3)
+        ts.sort()
+        return ts[len(ts) // 2]
+
+    out = {}
+    for name in OPS:
+        nb = algorithmic_bytes(name, bufs[name]["M"], bufs[name]["N"])
+        n = nb // 8                      # fp32 elements read (and written)
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        copy_us = cold_us(lambda: torch.abs(src, out=dst))
+        op_us = cold_us(lambda: ops[name](0))
+        del src, dst
+        out[name] = {"bytes": nb, "op_us": round(op_us, 2), "op_GBps": round(nb / (op_us * 1e-6) / 1e9, 1),
+                     "copy_us": round(copy_us, 2), "copy_GBps": round(nb / (copy_us * 1e-6) / 1e9, 1),
+                     "op_vs_copy": round(copy_us / op_us, 3)}
+    del flush
+    return out
+
+
 def traffic_for(per_launch_ok):
     """HBM bytes per launch of the dominant kernel from the committed
     rocprofv3 FETCH_SIZE / WRITE_SIZE summary, if it was taken on the kernel
@@ -303,7 +367,7 @@ def main():
     # warmup (the first step is checked)
     for i in range(args.warmup):
         for name in OPS:
-            ops[name]()
+            ops[name](i)
         if i == 0:
             torch.cuda.synchronize()
             sanity(torch, bufs)
@@ -317,9 +381,9 @@ def main():
     # timed region 1: K whole steps, events only around them -> the value
     torch.cuda.synchronize()
     start.record(stream)
-    for _ in range(K):
+    for k in range(K):
         for name in OPS:
-            ops[name]()
+            ops[name](k)
     end.record(stream)
     torch.cuda.synchronize()
     ms_step = start.elapsed_time(end) / K
@@ -332,7 +396,7 @@ def main():
     for k in range(K):
         marks[k][0].record(stream)
         for j, name in enumerate(OPS):
-            ops[name]()
+            ops[name](k)
             marks[k][j + 1].record(stream)
     torch.cuda.synchronize()
     per_op_ms = {name: sum(marks[k][j].elapsed_time(marks[k][j + 1]) for k in range(K)) / K
@@ -361,6 +425,7 @@ def main():
                 "plan": plan["variant_name"] if plan else None}
 
     extras = measure_extras(torch, rr, dev, K, bufs)
+    copy_ref = measure_copy_reference(torch, dev, ops, bufs)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -393,6 +458,7 @@ def main():
         "cpu_baseline": cpu,
         "breakdown": breakdown,
         "extras": extras,
+        "size_matched_copy": copy_ref,
         "device": torch.cuda.get_device_name(dev),
         "kernel_source_sha": kernel_source_sha(),
     }

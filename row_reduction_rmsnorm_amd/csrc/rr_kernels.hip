@@ -781,8 +781,9 @@ __global__ __launch_bounds__(256) void softmax_split_stats_kernel(const Tin* x, 
 #pragma unroll
     for (int k = 0; k < NV; ++k) {
       const int vi = c * CV + k * kThreads + rl.t;
-      // temporal load: pass B reads this chunk again right after
-      if (vi < nvec) v[k].template load<false>(x + ox + (int64_t)vi * VEC);
+      // streaming load (measured faster than a temporal one that would leave
+      // the chunk in the last-level cache for pass B, with inputs cold in HBM)
+      if (vi < nvec) v[k].template load<true>(x + ox + (int64_t)vi * VEC);
       else v[k].fill(kNegInf);
     }
     float ml = kNegInf;
