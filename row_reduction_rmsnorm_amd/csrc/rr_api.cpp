@@ -305,7 +305,10 @@ int64_t grid_for(const rr_plan& p) {
     const int64_t cap = (int64_t)device_cus() * per_cu * waves;
     if (g > cap) g = cap;
   }
-  const int64_t kMaxGrid = 0x7fffffffLL;
+  // A dispatch counts its work-items in 32 bits: keep grid x threads below
+  // 2^32 (every kernel walks its rows grid-stride, so a capped grid still
+  // covers them all).
+  const int64_t kMaxGrid = 0xffffffffLL / (p.block_threads > 0 ? p.block_threads : 1);
   return g > kMaxGrid ? kMaxGrid : g;
 }
 

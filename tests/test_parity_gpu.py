@@ -474,6 +474,38 @@ def test_split_row_longer_than_the_resident_grid():
         rr.rr_set_variant_override(rr.RR_VARIANT_AUTO)
 
 
+def test_grid_capped_when_rows_outnumber_one_dispatch():
+    """2^32 + 3 rows of 8 bf16 values: one workgroup per 256 rows would need
+    more work-items than a dispatch counts (32 bits), so the grid is capped
+    and the kernel walks the remaining rows grid-stride.  In place; zero rows
+    give exactly 1/8 everywhere; the first, middle and last rows carry a
+    pattern checked against the oracle."""
+    rr = _rr()
+    M, N = (1 << 32) + 3, 8
+    p = rr.rr_query_plan(rr.RR_OP_SOFTMAX, M, N, rr.RR_BF16, rr.RR_BF16)
+    assert p["work_items"] * p["block_threads"] > 0xFFFFFFFF, p
+    pattern = torch.tensor([[0.0, -np.inf, 1.0, 2.0, -np.inf, 3.0, 0.5, -1.0]], dtype=torch.bfloat16)
+    x = torch.zeros((M, N), dtype=torch.bfloat16, device="cuda")
+    special = (0, M // 2, M - 1)
+    for r in special:
+        x[r] = pattern[0].cuda()
+    _say(f"softmax in place {M} x {N} bf16 (plan {p['variant_name']}, {p['work_items']} workgroups)")
+    rr.rr_softmax_rows(x, x, None)
+    torch.cuda.synchronize()
+    xf = compare.to_f64(pattern)
+    ref = oracle.softmax(xf)
+    for r in special:
+        compare.check_softmax(x[r:r + 1].cpu(), xf, ref, f"row {r}")
+        x[r] = 0.125
+    step = 1 << 28
+    bad = 0
+    for a in range(0, M, step):
+        bad += int((x[a:a + step] != 0.125).sum())
+    assert bad == 0, f"{bad} values differ from 1/8"
+    del x
+    torch.cuda.empty_cache()
+
+
 def test_packed_long_rows_many_rows():
     """Rows beyond 32 widened values per lane held packed in registers
     (1024-lane workgroups, 12-20 vectors per lane), with many rows."""
