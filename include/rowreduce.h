@@ -81,8 +81,10 @@ typedef enum rr_status {
  *   y      [M, H] output, dtype `dtype`; may be the same pointer as x (in place)
  *   x      [M, H] input, dtype `dtype`
  *   gamma  [H] scale, dtype `dtype`
- *   M >= 0 rows, H >= 1 elements per row (H < 2^31), eps >= 0 finite
- * The sum of squares is accumulated in fp32.  Returns RR_ERR_INVALID_ARG for
+ *   M >= 0 rows, H >= 1 elements per row, eps >= 0 finite
+ * The sum of squares is accumulated in fp32.  Rows longer than 2^30
+ * elements (H or N, every entry point) return RR_ERR_UNSUPPORTED; there is
+ * no limit on M beyond memory.  Returns RR_ERR_INVALID_ARG for
  * null pointers (M > 0), M < 0, H < 1, a bad eps, an unknown dtype, or y
  * overlapping x without being equal to it, or gamma overlapping y.
  */
