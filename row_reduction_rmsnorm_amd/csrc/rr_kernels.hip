@@ -810,13 +810,49 @@ __global__ __launch_bounds__(256) void softmax_split_stats_kernel(const Tin* x, 
   }
 }
 
-// Pass B's chunks need not be pass A's: a row has SA summaries in the
-// workspace and is cut into SB chunks of 256 * NV vectors here.
+// Rows with many chunks: fold each row's S summaries into one pair, stored
+// in the row's first slot, so that pass B reads one pair per row instead of
+// S per wavefront (whose cost would grow with the square of the row length).
+// One workgroup per row; thread t merges slots t, t + 256, ... in order,
+// then the wave and cross-wave merges combine the threads.
+__global__ __launch_bounds__(256) void softmax_split_merge_kernel(SplitSlot* ws, int64_t M, int S) {
+  __shared__ MD slots[2][kMaxWavesPerGroup];
+  const RowLane rl = row_lane<false>();
+  int parity = 0;
+  for (int64_t row = blockIdx.x; row < M; row += gridDim.x) {
+    SplitSlot* r = ws + row * S;
+    MD p;
+    p.m = kNegInf;
+    p.d = 0.0f;
+    for (int s = threadIdx.x; s < S; s += 256) {
+      MD b;
+      b.m = r[s].m;
+      b.d = r[s].d;
+      p = md_merge(p, b);
+    }
+    p = wave_md(p);
+    // every thread's slot reads have returned before this barrier
+    p = group_md(p, rl.nw, rl.w, rl.lane, slots, parity);
+    parity ^= 1;
+    if (threadIdx.x == 0) {
+      r[0].m = p.m;
+      r[0].d = p.d;
+    }
+  }
+}
+
+// Rows with at most this many chunks skip the merge kernel: each lane of a
+// pass-B wavefront then reads at most one summary.
+constexpr int kSplitDirectMerge = kWave;
+
+// Pass B's chunks need not be pass A's: a row's summaries start at slot
+// row * SA, and SC of them are read (SA, or 1 after the merge kernel); the
+// row is cut into SB chunks of 256 * NV vectors here.
 template <typename Tin, typename Tout, int NV, bool LOG>
 __global__ __launch_bounds__(256) void softmax_split_apply_kernel(const Tin* x, Tout* y,
                                                                   const SplitSlot* __restrict__ ws,
-                                                                  int64_t M, int N, int SA, int SB,
-                                                                  RowStrides ld) {
+                                                                  int64_t M, int N, int SA, int SC,
+                                                                  int SB, RowStrides ld) {
   constexpr int VEC = Elem<Tin>::kVec;
   constexpr int kThreads = 256;
   constexpr int CV = kThreads * NV;
@@ -837,7 +873,7 @@ __global__ __launch_bounds__(256) void softmax_split_apply_kernel(const Tin* x, 
     MD p;
     p.m = kNegInf;
     p.d = 0.0f;
-    for (int s = rl.lane; s < SA; s += kWave) {
+    for (int s = rl.lane; s < SC; s += kWave) {
       MD b;
       b.m = ws[row * SA + s].m;
       b.d = ws[row * SA + s].d;
@@ -1165,6 +1201,12 @@ hipError_t softmax_split(const rr_plan& p, const SmCall<Tin, Tout>& c, SplitSlot
     }
   }
   softmax_split_stats_kernel<Tin, NV><<<grid1(grid), b, 0, s>>>(c.x, w, c.M, c.N, S, c.ld);
+  int SC = S;
+  if (S > kSplitDirectMerge) {
+    const int64_t gm = c.M < 65536 ? c.M : 65536;
+    softmax_split_merge_kernel<<<grid1(gm), dim3(256), 0, s>>>(w, c.M, S);
+    SC = 1;
+  }
   // pass B in chunks of its own size
   constexpr int VEC = Elem<Tin>::kVec;
   const int nvec = c.N / VEC;
@@ -1172,7 +1214,7 @@ hipError_t softmax_split(const rr_plan& p, const SmCall<Tin, Tout>& c, SplitSlot
   const int64_t items_b = c.M * (int64_t)SB;
   const int64_t grid_b = grid < c.M * (int64_t)S ? (grid < items_b ? grid : items_b) : items_b;
   softmax_split_apply_kernel<Tin, Tout, kSplitApplyNV, LOG><<<grid1(grid_b), b, 0, s>>>(c.x, c.y, w, c.M, c.N, S,
-                                                                                       SB, c.ld);
+                                                                                       SC, SB, c.ld);
   return hipGetLastError();
 }
 

@@ -474,6 +474,67 @@ def test_split_row_longer_than_the_resident_grid():
         rr.rr_set_variant_override(rr.RR_VARIANT_AUTO)
 
 
+def test_split_rows_with_many_chunks_are_merged_first():
+    """Rows of more than 64 chunks take the merge kernel (each row's chunk
+    summaries folded into one pair before pass B): a few rows just past the
+    threshold and well past it, fp32 and bf16, plain and log output."""
+    rr = _rr()
+    for (M, N, dt) in [(2, 1 << 19, "f32"), (3, 65536 * 8 + 8, "bf16"), (5, 300000, "f32")]:
+        p = rr.rr_query_plan(rr.RR_OP_SOFTMAX, M, N, rr.RR_F32 if dt == "f32" else rr.RR_BF16, rr.RR_F32)
+        assert p["variant_name"] == "split" and p["chunks_per_row"] > 64, p
+        _say(f"split with merge {dt} {M} x {N} ({p['chunks_per_row']} chunks)")
+        x = softmax_input(M, N, seed=N + M, dt=dt)
+        check_softmax(x, run_softmax(x, torch.float32), f"merged split {M}x{N}")
+        y = run_ex_log(x)
+        xf = compare.to_f64(x)
+        compare.check_log_softmax(y, xf, oracle.log_softmax(xf), f"merged split log {M}x{N}")
+
+
+def run_ex_log(x_cpu):
+    rr = _rr()
+    x = x_cpu.cuda()
+    y = rr.softmax_rows_ex(x, out_dtype=torch.float32, log_output=True)
+    torch.cuda.synchronize()
+    return y.cpu()
+
+
+def test_longest_row_closed_form():
+    """One row of 2^30 fp32 values (the longest row the library accepts; 2^18
+    chunks): the row is an 8-value pattern p repeated 2^27 times, so its
+    softmax is softmax(p) / 2^27 at every position, with softmax(p) from the
+    oracle.  Checked on the GPU in fp64: masked keys exactly 0, every other
+    value within 1e-4 relative of the closed form (the chunk merge sums 2^18
+    pairs in fp32), and the row sums to 1 within 1e-5."""
+    rr = _rr()
+    N = 1 << 30
+    pattern = np.array([0.0, 1.0, 2.0, 3.0, -np.inf, 0.5, -2.0, 4.0], dtype=np.float32)
+    ref = oracle.softmax(pattern[None, :].astype(np.float64))[0] / float(N // 8)
+    x = torch.from_numpy(pattern).cuda().repeat(N // 8)
+    y = torch.empty_like(x)
+    _say(f"softmax 1 x 2^30 f32 ({rr.rr_query_plan(rr.RR_OP_SOFTMAX, 1, N, rr.RR_F32, rr.RR_F32)['chunks_per_row']} chunks)")
+    ws = rr.softmax_workspace(x.view(1, N), torch.float32)
+    rr.rr_softmax_rows(y.view(1, N), x.view(1, N), ws)
+    torch.cuda.synchronize()
+    del x
+    y8 = y.view(-1, 8)
+    refd = torch.from_numpy(ref).cuda()
+    worst = 0.0
+    total = 0.0
+    step = 1 << 24
+    for a in range(0, y8.shape[0], step):
+        blk = y8[a:a + step].double()
+        assert bool((blk[:, 4] == 0).all()), "masked key not 0"
+        keep = [0, 1, 2, 3, 5, 6, 7]
+        rel = ((blk[:, keep] - refd[keep]).abs() / refd[keep]).max().item()
+        worst = max(worst, rel)
+        total += blk.sum().item()
+    _say(f"max rel err {worst:.3e}, row sum - 1 = {total - 1:.3e}")
+    assert worst <= 1e-4
+    assert abs(total - 1.0) <= 1e-5
+    del y, y8
+    torch.cuda.empty_cache()
+
+
 def test_grid_capped_when_rows_outnumber_one_dispatch():
     """2^32 + 3 rows of 8 bf16 values: one workgroup per 256 rows would need
     more work-items than a dispatch counts (32 bits), so the grid is capped
