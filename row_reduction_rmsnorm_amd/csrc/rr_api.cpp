@@ -272,42 +272,12 @@ rr_status make_plan(rr_op op, int64_t M, int64_t N, int din, int dout, bool is_a
   return RR_OK;
 }
 
-// Grid size: one workgroup per work item, optionally capped at a multiple of
-// the number of workgroups the device can hold at once (a persistent grid
-// walking the remaining rows).  RR_GRID_WAVES=<k> (read once) sets the cap to
-// k full-residency waves of workgroups; 0 or unset means no cap.
-int grid_waves_setting() {
-  static const int v = [] {
-    const char* e = getenv("RR_GRID_WAVES");
-    return e ? atoi(e) : 0;
-  }();
-  return v;
-}
-
-int device_cus() {
-  static std::atomic<int> cache[64];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  int v = cache[dev].load(std::memory_order_relaxed);
-  if (v == 0) {
-    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0)
-      v = 256;
-    cache[dev].store(v, std::memory_order_relaxed);
-  }
-  return v;
-}
-
+// Grid size: one workgroup per work item (grid-stride persistent grids
+// measured slower on MI355X for every kernel here), capped so that a
+// dispatch's work-items fit in 32 bits (grid x threads below 2^32; every
+// kernel walks its rows grid-stride, so a capped grid still covers them all).
 int64_t grid_for(const rr_plan& p) {
-  int64_t g = p.work_items;
-  const int waves = grid_waves_setting();
-  if (waves > 0) {
-    const int64_t per_cu = 2048 / p.block_threads > 0 ? 2048 / p.block_threads : 1;
-    const int64_t cap = (int64_t)device_cus() * per_cu * waves;
-    if (g > cap) g = cap;
-  }
-  // A dispatch counts its work-items in 32 bits: keep grid x threads below
-  // 2^32 (every kernel walks its rows grid-stride, so a capped grid still
-  // covers them all).
+  const int64_t g = p.work_items;
   const int64_t kMaxGrid = 0xffffffffLL / (p.block_threads > 0 ? p.block_threads : 1);
   return g > kMaxGrid ? kMaxGrid : g;
 }
