@@ -280,7 +280,9 @@ typedef enum rr_op {
  *         wavefront totals combined through LDS (N <= 32768)
  *   SPLIT several workgroups per row (softmax, long rows with few rows):
  *         a first kernel summarises each chunk as (m, d) into the workspace,
- *         a second merges a row's chunks and normalises (re-reading x).
+ *         a second merges a row's chunks and normalises (re-reading x).  Rows
+ *         of more than 64 chunks get a merge kernel in between that folds
+ *         each row's pairs into one, so the cost stays linear in N.
  *         SPLIT_ONE_KERNEL (opt-in) does both in one cooperative kernel whose
  *         workgroups keep their chunk in registers and wait for the row's
  *         other chunks; it reads x once but measured slower on MI355X, where

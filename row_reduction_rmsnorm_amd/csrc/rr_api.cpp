@@ -93,7 +93,8 @@ constexpr int64_t kSplitMaxRows = 1024;      // SPLIT only below this many rows
 // kernels (summed over the input tensors); more wavefronts per row rather
 // than more registers per lane measured faster on MI355X.
 constexpr int kLoadsPerLane = 2;
-// Split row: vectors per lane in each 256-lane chunk (chunk = 256 * 8 * VEC).
+// Split row: vectors per lane in pass A's 256-lane chunks (a chunk is
+// 256 * kSplitVecsPerLane vectors of VEC elements).
 constexpr int kSplitVecsPerLane = 4;
 
 // Register budget per lane, in fp32 values held for the row: softmax keeps
