@@ -173,6 +173,32 @@ bool plan_packed(rr_op op, rr_plan* p, int vec, int64_t nvec) {
   return false;
 }
 
+// Norm rows beyond the block budget (16 widened values per lane), up to 64K
+// elements: 1024 lanes hold the row in its storage format, NV vectors each
+// (bf16 4 or 8; fp32 8, 12 or 16; the fused op in fp32 holds x and the
+// residual while loading, so only 8).  Any number of rows: the alternative,
+// streaming the row twice, is slower at every row count.
+bool plan_norm_packed(rr_op op, rr_plan* p, int vec, int64_t nvec) {
+  if (op == RR_OP_SOFTMAX) return false;
+  static const int kBf16[] = {4, 8};
+  static const int kF32[] = {8, 12, 16};
+  const int* list = vec == 8 ? kBf16 : kF32;
+  const int count = vec == 8 ? 2 : (op == RR_OP_FUSED_ADD_RMSNORM ? 1 : 3);
+  if (vec == 1) return false;
+  for (int i = 0; i < count; ++i) {
+    if (nvec <= (int64_t)kMaxWaves * 64 * list[i]) {
+      p->variant = RR_VARIANT_BLOCK;
+      p->vec_elems = vec;
+      p->waves_per_row = kMaxWaves;
+      p->rows_per_group = 1;
+      p->vecs_per_lane = list[i];
+      p->block_threads = 64 * kMaxWaves;
+      return true;
+    }
+  }
+  return false;
+}
+
 void plan_split(rr_plan* p, int vec, int64_t nvec) {
   p->variant = RR_VARIANT_SPLIT;
   p->vec_elems = vec;
@@ -225,6 +251,7 @@ rr_status make_plan(rr_op op, int64_t M, int64_t N, int din, int dout, bool is_a
       } else if (wave_fits(op, vec, nvec)) {
         plan_wave(p, vec, nvec);
       } else if (plan_block(op, p, vec, nvec)) {
+      } else if (plan_norm_packed(op, p, vec, nvec)) {
       } else if (M >= kPackedMinRows && plan_packed(op, p, vec, nvec)) {
       } else if (op == RR_OP_SOFTMAX && !causal && M < kSplitMaxRows) {
         plan_split(p, vec, nvec);
@@ -238,7 +265,8 @@ rr_status make_plan(rr_op op, int64_t M, int64_t N, int din, int dout, bool is_a
       if (ok) plan_wave(p, vec, nvec);
       break;
     case RR_VARIANT_BLOCK:
-      ok = vec > 1 && (plan_block(op, p, vec, nvec) || plan_packed(op, p, vec, nvec));
+      ok = vec > 1 && (plan_block(op, p, vec, nvec) || plan_packed(op, p, vec, nvec) ||
+                       plan_norm_packed(op, p, vec, nvec));
       break;
     case RR_VARIANT_SPLIT:
     case RR_VARIANT_SPLIT_ONE_KERNEL:

@@ -159,6 +159,19 @@ struct Packed {
 #pragma unroll
     for (int i = 0; i < kWords; ++i) w[i] = 0u;
   }
+  // Hold VEC values that are exactly representable in T (packing rounds to
+  // nearest even, which leaves such values unchanged).
+  __device__ __forceinline__ void set(const float (&f)[VEC]) {
+    if constexpr (std::is_same_v<T, float>) {
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) w[i] = __float_as_uint(f[i]);
+    } else if constexpr (VEC == 1) {
+      w[0] = __float_as_uint(f[0]) >> 16;
+    } else {
+#pragma unroll
+      for (int i = 0; i < kWords; ++i) w[i] = pack_bf16x2(f[2 * i], f[2 * i + 1]);
+    }
+  }
   // Elements `first` and above become -inf (first in [0, VEC)).
   __device__ __forceinline__ void mask_from(int first) {
     if constexpr (std::is_same_v<T, float>) {

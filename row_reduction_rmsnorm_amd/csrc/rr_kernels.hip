@@ -392,6 +392,144 @@ __global__ __launch_bounds__(1024) void norm_loop_kernel(T* y, T* residual, cons
 }
 
 // ===========================================================================
+// RMSNorm / fused / LayerNorm, long rows held packed in registers (BLOCK,
+// large NV): rows beyond the register budget of norm_regs_kernel (16 widened
+// values per lane) and up to 64K elements.  1024 lanes hold the row in its
+// storage format (bf16 stays two to a register; the fused op keeps the
+// rounded sum h, exact in the storage format), so x is still read once; gamma
+// and beta are not kept but read again at store time, from L2 (one vector
+// per row and launch).  Same reductions and arithmetic as norm_regs_kernel.
+// ===========================================================================
+template <typename T, int NV, int KIND>
+__global__ __launch_bounds__(1024) void norm_packed_kernel(T* y, T* residual, const T* x,
+                                                           const T* __restrict__ gamma,
+                                                           const T* __restrict__ beta, int64_t M,
+                                                           int N, float eps, RowStrides ld) {
+  constexpr int VEC = Elem<T>::kVec;
+  constexpr int kThreads = 1024;
+  __shared__ float slots[2][kMaxWavesPerGroup];
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int w = t >> 6;
+  const int nvec = N / VEC;
+  int parity = 0;
+  auto row_sum = [&](float v) {
+    v = wave_sum(v);
+    v = group_sum(v, kThreads / kWave, w, lane, slots, parity);
+    parity ^= 1;
+    return v;
+  };
+  for (int64_t row = blockIdx.x; row < M; row += gridDim.x) {
+    const T* xr = x + row * ld.x;   // uniform row bases
+    T* yr = y + row * ld.y;
+    // lane offsets recomputed at each use from an opaque copy of the lane
+    // index, which frees the registers the packed row needs
+    int t_ld = t;
+    asm volatile("" : "+v"(t_ld));
+    Packed<T, VEC> v[NV];
+    if constexpr (KIND == kNormFused) {
+      T* rr = residual + row * ld.r;
+      Packed<T, VEC> r[NV];
+#pragma unroll
+      for (int k = 0; k < NV; ++k) {
+        const int vi = k * kThreads + t_ld;
+        if (vi < nvec) {
+          v[k].template load<true>(xr + vi * VEC);
+          r[k].template load<true>(rr + vi * VEC);
+        } else {
+          v[k].zero();
+          r[k].zero();
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < NV; ++k) {
+        const int vi = k * kThreads + t_ld;
+        float h[VEC];
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) h[i] = round_to<T>(v[k].get(i) + r[k].get(i));
+        if (vi < nvec) store_vec<T, VEC>(rr + vi * VEC, h);
+        v[k].set(h);
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < NV; ++k) {
+        const int vi = k * kThreads + t_ld;
+        if (vi < nvec) v[k].template load<true>(xr + vi * VEC);
+        else v[k].zero();
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < NV; ++k) v[k].touch();
+    int t_st = t;
+    asm volatile("" : "+v"(t_st));
+    if constexpr (KIND == kNormLayer) {
+      // about the row's first element K, as in norm_regs_kernel
+      const float K = load_one<T>(xr);
+      float s1 = 0.0f;
+#pragma unroll
+      for (int k = 0; k < NV; ++k) {
+        const bool valid = k * kThreads + t < nvec;
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) s1 += valid ? v[k].get(i) - K : 0.0f;
+      }
+#pragma unroll
+      for (int k = 0; k < NV; ++k) v[k].touch();
+      const float c = row_sum(s1) / (float)N;
+      float s2 = 0.0f;
+#pragma unroll
+      for (int k = 0; k < NV; ++k) {
+        const bool valid = k * kThreads + t < nvec;
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) {
+          const float d = valid ? (v[k].get(i) - K) - c : 0.0f;
+          s2 += d * d;
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < NV; ++k) v[k].touch();
+      const float rstd = 1.0f / __builtin_sqrtf(row_sum(s2) / (float)N + eps);
+#pragma unroll
+      for (int k = 0; k < NV; ++k) {
+        const int vi = k * kThreads + t_st;
+        if (vi < nvec) {
+          float g[VEC], b[VEC], o[VEC];
+          load_vec<T, VEC, false>(gamma + vi * VEC, g);
+          if (beta) {
+            load_vec<T, VEC, false>(beta + vi * VEC, b);
+          } else {
+#pragma unroll
+            for (int i = 0; i < VEC; ++i) b[i] = 0.0f;
+          }
+#pragma unroll
+          for (int i = 0; i < VEC; ++i) o[i] = (((v[k].get(i) - K) - c) * rstd) * g[i] + b[i];
+          store_vec<T, VEC>(yr + vi * VEC, o);
+        }
+      }
+    } else {
+      float ss = 0.0f;
+#pragma unroll
+      for (int k = 0; k < NV; ++k)
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) ss += v[k].get(i) * v[k].get(i);
+#pragma unroll
+      for (int k = 0; k < NV; ++k) v[k].touch();
+      const float rstd = 1.0f / __builtin_sqrtf(row_sum(ss) / (float)N + eps);
+#pragma unroll
+      for (int k = 0; k < NV; ++k) {
+        const int vi = k * kThreads + t_st;
+        if (vi < nvec) {
+          float g[VEC], o[VEC];
+          load_vec<T, VEC, false>(gamma + vi * VEC, g);
+#pragma unroll
+          for (int i = 0; i < VEC; ++i) o[i] = (v[k].get(i) * rstd) * g[i];
+          store_vec<T, VEC>(yr + vi * VEC, o);
+        }
+      }
+    }
+  }
+}
+
+// ===========================================================================
 // Short rows, several per wavefront (SUBWAVE).
 //
 // [P4] section "按行长度选择并行方式": rows of a few dozen elements should not
@@ -1084,9 +1222,47 @@ hipError_t norm_sub(const rr_plan& p, const NormArgs& a, int64_t grid, hipStream
   return hipGetLastError();
 }
 
+// Rows held packed: bf16 NV 4 or 8 (32K / 64K elements), fp32 NV 8, 12 or 16
+// (32K / 48K / 64K; the fused op, which holds x and the residual while
+// loading, only NV 8).
+template <typename T, int KIND>
+hipError_t norm_packed(const rr_plan& p, const NormArgs& a, int64_t grid, hipStream_t s) {
+  T* yy = static_cast<T*>(a.y);
+  T* rr_ = static_cast<T*>(a.residual);
+  const T* xx = static_cast<const T*>(a.x);
+  const T* gg = static_cast<const T*>(a.gamma);
+  const T* bb = static_cast<const T*>(a.beta);
+  const dim3 b(1024);
+  const dim3 g = grid1(grid);
+  if constexpr (std::is_same_v<T, bf16_t>) {
+    switch (p.vecs_per_lane) {
+      case 4: norm_packed_kernel<T, 4, KIND><<<g, b, 0, s>>>(yy, rr_, xx, gg, bb, a.M, a.N, a.eps, a.ld); break;
+      case 8: norm_packed_kernel<T, 8, KIND><<<g, b, 0, s>>>(yy, rr_, xx, gg, bb, a.M, a.N, a.eps, a.ld); break;
+      default: return hipErrorInvalidValue;
+    }
+  } else {
+    switch (p.vecs_per_lane) {
+      case 8: norm_packed_kernel<T, 8, KIND><<<g, b, 0, s>>>(yy, rr_, xx, gg, bb, a.M, a.N, a.eps, a.ld); break;
+      case 12:
+      case 16:
+        if constexpr (KIND != kNormFused) {
+          if (p.vecs_per_lane == 12)
+            norm_packed_kernel<T, 12, KIND><<<g, b, 0, s>>>(yy, rr_, xx, gg, bb, a.M, a.N, a.eps, a.ld);
+          else
+            norm_packed_kernel<T, 16, KIND><<<g, b, 0, s>>>(yy, rr_, xx, gg, bb, a.M, a.N, a.eps, a.ld);
+          break;
+        }
+        return hipErrorInvalidValue;
+      default: return hipErrorInvalidValue;
+    }
+  }
+  return hipGetLastError();
+}
+
 template <typename T, int KIND>
 hipError_t norm_any(const rr_plan& p, const NormArgs& a, int64_t grid, hipStream_t s) {
   if (p.variant == RR_VARIANT_LOOP) return norm_loop<T, KIND>(p, a, grid, s);
+  if (p.variant == RR_VARIANT_BLOCK && p.vecs_per_lane * p.vec_elems > 16) return norm_packed<T, KIND>(p, a, grid, s);
   if (p.variant == RR_VARIANT_SUBWAVE) {
     if (p.vec_elems == 1) return norm_sub<T, 1, KIND>(p, a, grid, s);
     return norm_sub<T, Elem<T>::kVec, KIND>(p, a, grid, s);

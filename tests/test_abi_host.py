@@ -251,7 +251,17 @@ def test_dispatch_boundaries():
     assert v(rr.RR_OP_RMSNORM, 100, 1028) == "block"
     # block capacity: 16 wavefronts x 64 lanes x 16 (norm) or 32 (softmax) values
     assert v(rr.RR_OP_RMSNORM, 100, 16384) == "block"
-    assert v(rr.RR_OP_RMSNORM, 100, 16388) == "loop"
+    # longer norm rows are held packed by 1024 lanes up to 64K elements
+    q = lambda op, N, a=F: rr.rr_query_plan(op, 3, N, a, a)
+    assert q(rr.RR_OP_RMSNORM, 16388)["vecs_per_lane"] == 8 and q(rr.RR_OP_RMSNORM, 16388)["block_threads"] == 1024
+    assert q(rr.RR_OP_LAYERNORM, 40000)["vecs_per_lane"] == 12
+    assert q(rr.RR_OP_RMSNORM, 65536)["vecs_per_lane"] == 16
+    assert q(rr.RR_OP_RMSNORM, 65540)["variant_name"] == "loop"
+    assert q(rr.RR_OP_FUSED_ADD_RMSNORM, 32768)["vecs_per_lane"] == 8
+    assert q(rr.RR_OP_FUSED_ADD_RMSNORM, 32772)["variant_name"] == "loop"     # fp32 fused: x and residual
+    assert q(rr.RR_OP_FUSED_ADD_RMSNORM, 65536, B)["vecs_per_lane"] == 8
+    assert q(rr.RR_OP_RMSNORM, 20480, B)["vecs_per_lane"] == 4
+    assert q(rr.RR_OP_RMSNORM, 65544, B)["variant_name"] == "loop"
     assert v(S, 100, 32768) == "block"
     # longer softmax rows: split when rows are few; with many rows the row is
     # held packed (1024 lanes x up to 20 vectors), beyond that it streams

@@ -328,6 +328,35 @@ def test_layernorm_grid(dt, N):
         check_ln(x, g, None, 1e-5, run_layernorm(x, g, None, 1e-5), f"ln no beta {dt} {M}x{N}")
 
 
+PACKED_NORM_N = {"f32": [16388, 20480, 32768, 40000, 65536, 65540],
+                 "bf16": [16392, 20480, 32768, 40000, 65536, 65544]}
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_norms_packed_long_rows(dt):
+    """Rows past the register budget of the workgroup-per-row norm kernel,
+    held packed by 1024 lanes up to 64K elements (the last width of each list
+    streams instead): RMSNorm, fused add + RMSNorm (including the fp32 fused
+    limit at 32K) and LayerNorm with a large offset, including in place."""
+    rr = _rr()
+    code = rr.RR_F32 if dt == "f32" else rr.RR_BF16
+    for N in PACKED_NORM_N[dt]:
+        for M in (1, 7, 33):
+            plans = {op: rr.rr_query_plan(op, M, N, code, code)
+                     for op in (rr.RR_OP_RMSNORM, rr.RR_OP_FUSED_ADD_RMSNORM, rr.RR_OP_LAYERNORM)}
+            _say(f"packed norms {dt} M={M} N={N} " +
+                 " ".join(f"{p['variant_name']}/{p['vecs_per_lane']}" for p in plans.values()))
+            x = _as(workloads.random_rows(M, N, seed=N + M), dt)
+            g = _as(workloads.gamma_vector(N, seed=N), dt)
+            check_norm(x, g, 1e-6, dt, run_rmsnorm(x, g, 1e-6, inplace=(M == 7)), f"rms {dt} {M}x{N}")
+            r = _as(workloads.random_rows(M, N, seed=N + M + 1), dt)
+            yf, rf = run_fused(x, r, g, 1e-6, y_is_x=(M == 7))
+            check_fused(x, r, g, 1e-6, dt, yf, rf, f"fused {dt} {M}x{N}")
+            xl, gl, bl = ln_input(M, N, seed=N + 2 * M, dt=dt, offset=101.0, spread=0.6)
+            check_ln(xl, gl, bl, 1e-5, run_layernorm(xl, gl, bl, 1e-5), f"ln {dt} {M}x{N}")
+            check_ln(xl, gl, None, 1e-5, run_layernorm(xl, gl, None, 1e-5, inplace=True), f"ln nb {dt} {M}x{N}")
+
+
 @pytest.mark.parametrize("variant", ["wave", "block", "loop", "subwave"])
 def test_layernorm_forced_variants(variant):
     rr = _rr()
