@@ -338,7 +338,7 @@ rr_status rr_set_variant_override(rr_variant variant);
  * receives the group's sum.  kind 1: the same with the maximum.  kind 2: in
  * and out hold count groups of 128 floats, 64 m values then 64 d values;
  * every lane receives the merge of the group's 64 (m, d) pairs.  One
- * wavefront per group; count >= 1.
+ * wavefront per group; 1 <= count <= (2^32 - 1) / 64.
  */
 rr_status rr_selftest_wave_allreduce(const float* in, float* out, int64_t count, int kind,
                                      void* stream);

@@ -583,7 +583,7 @@ rr_status rr_set_variant_override(rr_variant v) {
 rr_status rr_selftest_wave_allreduce(const float* in, float* out, int64_t count, int kind,
                                      void* stream) {
   g_err[0] = '\0';
-  if (!in || !out || count < 1 || count > 0x7fffffffLL || kind < 0 || kind > 2)
+  if (!in || !out || count < 1 || count > 0xffffffffLL / 64 || kind < 0 || kind > 2)
     return fail(RR_ERR_INVALID_ARG, "rr_selftest_wave_allreduce: bad arguments");
   return hip_status(rr::launch_selftest_wave(in, out, count, kind, static_cast<hipStream_t>(stream)),
                     "rr_selftest_wave_allreduce");
