@@ -626,10 +626,16 @@ def test_softmax_in_place_unaligned_and_tiny():
     torch.cuda.synchronize()
     check_softmax(x, y.cpu(), "unaligned")
     # the pages' worked examples, through the kernels
-    for row in ([1000.0, 1001.0], [1.0, 3.0, 2.0], [2.0, 4.0, 1.0], [1.0, 2.0, 5.0, 3.0]):
+    # ... and a row whose fifth entry is 90, where exp without the max
+    # subtracted overflows fp32 (the pages' overflow test)
+    for row in ([1000.0, 1001.0], [1.0, 3.0, 2.0], [2.0, 4.0, 1.0], [1.0, 2.0, 5.0, 3.0],
+                [0.0, 0.1, 0.2, 0.3, 0.4, 90.0, 0.6, 0.7]):
         x = torch.tensor([row], dtype=torch.float32)
         y = run_softmax(x, torch.float32)
         check_softmax(x, y, f"example {row}")
+    # M = 0: a successful no-op that touches nothing
+    y0 = torch.full((0, 64), 7.0, device="cuda")
+    rr.rr_softmax_rows(y0, torch.empty((0, 64), device="cuda"), None)
     # N = 1: probability 1, or NaN for a masked entry
     x = torch.tensor([[5.0], [-np.inf], [0.0]], dtype=torch.float32)
     y = run_softmax(x, torch.float32).numpy()
