@@ -42,9 +42,13 @@ if ROOT not in sys.path:
 
 METRIC = "achieved HBM GB/s and % of MI355X peak, RMSNorm 8192x4096 bf16 + softmax rows"
 PEAK_HBM_GBS = 8000.0   # MI355X HBM3E, published
+# Device code: the kernel of a launch is these sources plus the launch plan
+# (recorded beside the counters and compared as well).
 KERNEL_SOURCES = ("row_reduction_rmsnorm_amd/csrc/rr_kernels.hip",
                   "row_reduction_rmsnorm_amd/csrc/rr_device.h",
-                  "row_reduction_rmsnorm_amd/csrc/rr_api.cpp")
+                  "row_reduction_rmsnorm_amd/csrc/rr_launch.h")
+PLAN_KEYS = ("variant_name", "waves_per_row", "rows_per_group", "vecs_per_lane", "vec_elems",
+             "block_threads")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_sm_causal_softmax_block.json")
 
 OPS = ("fused", "rms_bf16", "sm_wave", "sm_vocab", "sm_causal")
@@ -318,15 +322,20 @@ def measure_copy_reference(torch, dev, ops, bufs, reps=15):
     return out
 
 
-def traffic_for(per_launch_ok):
+def causal_plan(rr):
+    p = rr.rr_query_plan(rr.RR_OP_SOFTMAX, 114688, 4096, rr.RR_F32, rr.RR_F32)
+    return {k: p[k] for k in PLAN_KEYS}
+
+
+def traffic_for(per_launch_ok, rr):
     """HBM bytes per launch of the dominant kernel from the committed
-    rocprofv3 FETCH_SIZE / WRITE_SIZE summary, if it was taken on the kernel
-    sources as they are now."""
+    rocprofv3 FETCH_SIZE / WRITE_SIZE summary, if it was taken on the device
+    code and the launch plan as they are now."""
     if not per_launch_ok or not os.path.exists(TRAFFIC_FILE):
         return None
     with open(TRAFFIC_FILE) as f:
         t = json.load(f)
-    if t.get("kernel_source_sha") != kernel_source_sha():
+    if t.get("kernel_source_sha") != kernel_source_sha() or t.get("plan") != causal_plan(rr):
         return None
     return t.get("traffic_bytes_per_launch")
 
@@ -423,7 +432,7 @@ def main():
         if dom.startswith("sm_") else None
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(achieved / PEAK_HBM_GBS, 4),
-                "traffic": traffic_for(dom == "sm_causal"),
+                "traffic": traffic_for(dom == "sm_causal", rr),
                 "kernel": dom, "bytes_per_launch": dom_bytes,
                 "us_per_launch": round(per_op_ms[dom] * 1e3, 2),
                 "plan": plan["variant_name"] if plan else None}
