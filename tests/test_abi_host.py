@@ -309,3 +309,60 @@ def test_forced_variants():
     with pytest.raises(rr.RowReduceError):
         rr.rr_set_variant_override(9)
     assert rr.rr_query_plan(S, 10, 1024, F, F)["variant_name"] == "wave"   # override cleared
+
+
+def test_every_plan_covers_its_row():
+    """For thousands of seeded (op, M, N, dtypes, alignment) cases, and every
+    forced variant, the plan either is refused or holds the whole row: the
+    register-resident kernels only ever touch lanes x vectors they were
+    planned with, so a plan that did not cover N would silently drop the
+    row's tail.  Also: thread counts within a workgroup's limit, workspace
+    sizes for split plans, and work items that cover every row."""
+    import numpy as np
+    rng = np.random.default_rng(42)
+    ops = [rr.RR_OP_RMSNORM, rr.RR_OP_FUSED_ADD_RMSNORM, rr.RR_OP_LAYERNORM, rr.RR_OP_SOFTMAX,
+           rr.RR_OP_SOFTMAX_CAUSAL]
+    variants = [rr.RR_VARIANT_AUTO, rr.RR_VARIANT_WAVE, rr.RR_VARIANT_BLOCK, rr.RR_VARIANT_SPLIT,
+                rr.RR_VARIANT_LOOP, rr.RR_VARIANT_SPLIT_ONE_KERNEL, rr.RR_VARIANT_SUBWAVE]
+    widths = np.concatenate([rng.integers(1, 300, 300), rng.integers(300, 70000, 400),
+                             rng.integers(70000, 1 << 22, 100), [1 << 30, (1 << 30) - 8]])
+    checked = 0
+    try:
+        for v in variants:
+            rr.rr_set_variant_override(v)
+            for N in widths:
+                N = int(N)
+                op = ops[int(rng.integers(0, len(ops)))]
+                M = int(rng.choice([0, 1, 7, 255, 256, 1023, 1024, 5000, 100000]))
+                din = int(rng.integers(0, 2))
+                dout = int(rng.integers(0, 2)) if op in (rr.RR_OP_SOFTMAX, rr.RR_OP_SOFTMAX_CAUSAL) else din
+                aligned = bool(rng.integers(0, 4))
+                try:
+                    p = rr.rr_query_plan(op, M, N, din, dout, aligned)
+                except rr.RowReduceError as e:
+                    assert e.status == rr.RR_ERR_UNSUPPORTED and v != rr.RR_VARIANT_AUTO, (op, M, N, v)
+                    continue
+                checked += 1
+                vec, nv, name = p["vec_elems"], p["vecs_per_lane"], p["variant_name"]
+                width = 8 if din == rr.RR_BF16 else 4
+                assert vec in (1, width) and (vec == 1 or (aligned and N % width == 0)), p
+                assert 1 <= p["block_threads"] <= 1024 and p["block_threads"] % 64 == 0, p
+                if name == "subwave":
+                    assert p["waves_per_row"] * vec >= N and p["rows_per_group"] * p["waves_per_row"] == 256, p
+                elif name == "wave":
+                    assert 64 * nv * vec >= N and p["rows_per_group"] * 64 == p["block_threads"], p
+                elif name == "block":
+                    assert p["block_threads"] * nv * vec >= N and p["rows_per_group"] == 1, p
+                elif name in ("split", "split1"):
+                    assert op == rr.RR_OP_SOFTMAX and vec > 1, p
+                    assert p["chunks_per_row"] * 256 * nv * vec >= N, p
+                    assert p["workspace_bytes"] == M * p["chunks_per_row"] * 16, p
+                    assert p["work_items"] == M * p["chunks_per_row"], p
+                    continue
+                else:
+                    assert name == "loop", p
+                assert p["workspace_bytes"] == 0, p
+                assert p["work_items"] * p["rows_per_group"] >= M, p
+    finally:
+        rr.rr_set_variant_override(rr.RR_VARIANT_AUTO)
+    assert checked > 1500
