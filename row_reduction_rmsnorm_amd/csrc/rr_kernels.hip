@@ -1,5 +1,6 @@
 // Row-reduce kernels for MI355X (gfx950): RMSNorm, fused residual add +
-// RMSNorm, and row softmax on the online normaliser.
+// RMSNorm, LayerNorm, and row softmax (and log-softmax, optionally under a
+// causal rule) on the online normaliser.
 //
 // Every kernel follows the same shape: each lane reduces the elements it
 // holds to a partial statistic (the sum of squares, or the online pair
@@ -21,9 +22,13 @@
 //    rows_per_group == 1 (a workgroup per row).  Lane t of a row owns vectors
 //    t, t + T, t + 2T, ... (T = 64 * waves_per_row) so every 16-byte access
 //    of a wavefront is one contiguous 1 KiB segment.
-//  * the grid may be smaller than the number of rows: workgroups then walk
-//    rows with a stride of gridDim.x (a persistent grid); gamma stays in
-//    registers across rows.
+//  * packed kernels (norm_packed_kernel, softmax_packed_kernel): 1024 lanes
+//    per row holding up to 20 vectors each in the storage format.
+//  * split softmax: 256-lane workgroups per chunk of a row, (m, d) pairs in a
+//    caller workspace.
+//  * the grid may be smaller than the number of rows (it is capped so that a
+//    dispatch's work-items fit in 32 bits): workgroups then walk rows with a
+//    stride of gridDim.x; gamma stays in registers across rows.
 #include <time.h>
 
 #include <atomic>
