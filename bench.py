@@ -42,11 +42,8 @@ if ROOT not in sys.path:
 
 METRIC = "achieved HBM GB/s and % of MI355X peak, RMSNorm 8192x4096 bf16 + softmax rows"
 PEAK_HBM_GBS = 8000.0   # MI355X HBM3E, published
-# Device code: the kernel of a launch is these sources plus the launch plan
-# (recorded beside the counters and compared as well).
-KERNEL_SOURCES = ("row_reduction_rmsnorm_amd/csrc/rr_kernels.hip",
-                  "row_reduction_rmsnorm_amd/csrc/rr_device.h",
-                  "row_reduction_rmsnorm_amd/csrc/rr_launch.h")
+# The kernel of a launch is the library's device code plus the launch plan
+# (both recorded beside the counters and compared).
 PLAN_KEYS = ("variant_name", "waves_per_row", "rows_per_group", "vecs_per_lane", "vec_elems",
              "block_threads")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_sm_causal_softmax_block.json")
@@ -55,12 +52,32 @@ OPS = ("fused", "rms_bf16", "sm_wave", "sm_vocab", "sm_causal")
 ROTATE = 4   # buffer copies of every workload but sm_causal
 
 
-def kernel_source_sha():
-    h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, p), "rb") as f:
-            h.update(f.read())
-    return h.hexdigest()[:16]
+def code_object_sha(lib_path=None):
+    """Hash of the device code the library carries: its .hip_fatbin ELF
+    section (the gfx950 code objects), read without loading the library.
+    Comments and host-only edits leave it unchanged; any kernel change
+    changes it."""
+    import struct
+    if lib_path is None:
+        from row_reduction_rmsnorm_amd import binding
+        lib_path = binding.LIB_PATH
+    with open(lib_path, "rb") as f:
+        data = f.read()
+    if data[:4] != b"\x7fELF" or data[4] != 2:
+        raise ValueError(f"{lib_path}: not a 64-bit ELF file")
+    shoff = struct.unpack_from("<Q", data, 0x28)[0]
+    shentsize, shnum, shstrndx = struct.unpack_from("<HHH", data, 0x3A)
+
+    def section(i):
+        return struct.unpack_from("<IIQQQQ", data, shoff + i * shentsize)
+
+    names = section(shstrndx)[4]
+    for i in range(shnum):
+        name, _, _, _, off, size = section(i)
+        end = data.index(b"\0", names + name)
+        if data[names + name:end] == b".hip_fatbin":
+            return hashlib.sha256(data[off:off + size]).hexdigest()[:16]
+    raise ValueError(f"{lib_path}: no .hip_fatbin section")
 
 
 def algorithmic_bytes(op, M, N):
@@ -335,7 +352,7 @@ def traffic_for(per_launch_ok, rr):
         return None
     with open(TRAFFIC_FILE) as f:
         t = json.load(f)
-    if t.get("kernel_source_sha") != kernel_source_sha() or t.get("plan") != causal_plan(rr):
+    if t.get("code_object_sha") != code_object_sha() or t.get("plan") != causal_plan(rr):
         return None
     return t.get("traffic_bytes_per_launch")
 
@@ -473,7 +490,7 @@ def main():
         "extras": extras,
         "size_matched_copy": copy_ref,
         "device": torch.cuda.get_device_name(dev),
-        "kernel_source_sha": kernel_source_sha(),
+        "code_object_sha": code_object_sha(),
     }
     print(json.dumps(line), flush=True)
 
