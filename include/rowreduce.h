@@ -82,7 +82,9 @@ typedef enum rr_status {
  *   x      [M, H] input, dtype `dtype`
  *   gamma  [H] scale, dtype `dtype`
  *   M >= 0 rows, H >= 1 elements per row, eps >= 0 finite
- * The sum of squares is accumulated in fp32.  Rows longer than 2^30
+ * The sum of squares is accumulated in fp32, so |x| must stay below about
+ * 1.8e19 (squares beyond the fp32 range are not supported; the same holds
+ * for the spread about the mean in rr_layernorm).  Rows longer than 2^30
  * elements (H or N, every entry point) return RR_ERR_UNSUPPORTED; there is
  * no limit on M beyond memory.  Returns RR_ERR_INVALID_ARG for
  * null pointers (M > 0), M < 0, H < 1, a bad eps, an unknown dtype, or y
