@@ -210,8 +210,9 @@ def cpu_baseline(bufs, fraction):
         "unit": "GB/s",
         "cores": oracle.num_threads(),
         "kind": "oracle",
-        "sample": f"first {fraction:.4g} of the rows of every workload ({', '.join(parts)}); "
-                  f"{total_b / 1e9:.3f} GB algorithmic, {total_t:.2f} s on the host",
+        "sample": (f"{'all' if fraction >= 1 else f'the first {fraction:.4g}'} of the rows of every workload "
+                   f"({', '.join(parts)}); "
+                   f"{total_b / 1e9:.3f} GB algorithmic, {total_t:.2f} s on the host"),
         "seconds": round(total_t, 3),
     }
 

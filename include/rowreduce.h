@@ -43,8 +43,10 @@
  *     gives the detail for the calling thread.
  *   - Alignment: rows whose pointers are 16-byte aligned and whose width is a
  *     multiple of 4 (fp32) or 8 (bf16) elements use 16-byte vector accesses;
- *     anything else runs a scalar path with the same results up to rounding
- *     order.  Any N >= 1 is accepted.
+ *     a softmax reading bf16 and writing fp32 reads 4 elements (8 bytes) per
+ *     access, so there input rows 8-byte aligned and a width that is a
+ *     multiple of 4 suffice.  Anything else runs a scalar path with the same
+ *     results up to rounding order.  Any N >= 1 is accepted.
  *   - Determinism: a given (op, M, N, dtypes, alignment) always runs the same
  *     kernel with the same reduction order, so results are bitwise
  *     reproducible run to run; no floating-point atomics are used.
@@ -227,10 +229,11 @@ rr_status rr_softmax_rows_ex(void* y, const void* x, int64_t M, int64_t N, rr_dt
  * activation (vLLM's normalisation kernels take such an input stride: [P2]
  * section 九, the fused_add_rms_norm kernel's input_stride).  Every stride is
  * in elements, at least the row width (H or N) and at most 2^40.  Vector
- * (16-byte) accesses need every row start 16-byte aligned, i.e. aligned
- * base pointers and strides that are multiples of 4 (fp32) or 8 (bf16)
- * elements; otherwise the scalar path runs, with the same results up to
- * rounding order.  With every stride equal to the width these are exactly
+ * accesses need every row start aligned to the access (16 bytes: aligned
+ * base pointers and strides that are multiples of 4 fp32 or 8 bf16
+ * elements; 8 bytes for the bf16 input of a softmax written as fp32);
+ * otherwise the scalar path runs, with the same results up to rounding
+ * order.  With every stride equal to the width these are exactly
  * the contiguous entry points above (same kernels, same bits).
  * Aliasing: y may be x itself (same pointer and stride, same dtype); other
  * matrices of a call must not share an element.  Two matrices with the same
@@ -312,7 +315,8 @@ typedef struct rr_plan {
   int32_t waves_per_row;    /* wavefronts cooperating on one row */
   int32_t rows_per_group;   /* rows handled by one workgroup per step */
   int32_t vecs_per_lane;    /* vector accesses per lane held in registers */
-  int32_t vec_elems;        /* elements per vector access (4 fp32, 8 bf16, 1 scalar) */
+  int32_t vec_elems;        /* elements per vector access: 4 fp32, 8 bf16 (4 for a bf16
+                               softmax written as fp32), 1 scalar */
   int32_t block_threads;    /* workgroup size */
   int64_t chunks_per_row;   /* SPLIT: workgroups per row; otherwise 1 */
   int64_t work_items;       /* workgroup-steps needed (rows / rows_per_group x chunks) */
@@ -321,7 +325,8 @@ typedef struct rr_plan {
 
 /*
  * The launch plan the library would use.  aligned16 != 0 states that every
- * pointer of the call will be 16-byte aligned.  Honours the variant
+ * row start of the call will be aligned for vector access (16 bytes; 8 for
+ * the bf16 input of a softmax written as fp32).  Honours the variant
  * override below.  Returns RR_ERR_INVALID_ARG / RR_ERR_UNSUPPORTED as the
  * corresponding call would.
  */

@@ -37,6 +37,18 @@ bool valid_dtype(int d) { return d == RR_F32 || d == RR_BF16; }
 size_t dtype_size(int d) { return d == RR_F32 ? 4 : 2; }
 int vec_width(int d) { return d == RR_F32 ? 4 : 8; }  // elements per 16 bytes
 
+// Elements per vector load of an op: 16 bytes of input, except a softmax
+// reading bf16 and writing fp32, which loads 8 bytes (4 elements) so that
+// each lane's output is one 16-byte store (the kernels' softmax_vec).
+int op_vec_width(rr_op op, int din, int dout) {
+  return (op == RR_OP_SOFTMAX && din == RR_BF16 && dout == RR_F32) ? 4 : vec_width(din);
+}
+
+// Vectors of `vec` elements of dtype din in 16 bytes: 1, or 2 for the 8-byte
+// vectors (a scalar path counts as 1).  Per-lane vector counts sized for
+// 16-byte vectors scale by it, which keeps the registers a lane holds.
+int vecs_per_16_bytes(int din, int vec) { return vec > 1 ? (int)(16 / (dtype_size(din) * vec)) : 1; }
+
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 // [a, a + na) and [b, b + nb) share a byte.
@@ -74,7 +86,10 @@ bool mats_overlap(const Mat& a, const Mat& b, int64_t M) {
 }
 
 // Rows of the matrix start 16-byte aligned.
-bool rows_aligned16(const Mat& a) { return aligned16(a.p) && a.ld % 16 == 0; }
+bool rows_aligned(const Mat& a, size_t bytes) {
+  return (reinterpret_cast<uintptr_t>(a.p) % bytes) == 0 && a.ld % bytes == 0;
+}
+bool rows_aligned16(const Mat& a) { return rows_aligned(a, 16); }
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
@@ -93,8 +108,8 @@ constexpr int64_t kSplitMaxRows = 1024;      // SPLIT only below this many rows
 // kernels (summed over the input tensors); more wavefronts per row rather
 // than more registers per lane measured faster on MI355X.
 constexpr int kLoadsPerLane = 2;
-// Split row: vectors per lane in pass A's 256-lane chunks (a chunk is
-// 256 * kSplitVecsPerLane vectors of VEC elements).
+// Split row: 16-byte vectors per lane in pass A's 256-lane chunks (a chunk
+// is 256 * kSplitVecsPerLane vectors; twice as many of 8 bytes).
 constexpr int kSplitVecsPerLane = 4;
 
 // Register budget per lane, in fp32 values held for the row: softmax keeps
@@ -150,16 +165,17 @@ bool plan_block(rr_op op, rr_plan* p, int vec, int64_t nvec) {
   return false;
 }
 
-// Softmax rows beyond that, up to 20 vectors per lane of a 1024-lane
-// workgroup, held in their storage format (one workgroup per CU).  With few
+// Softmax rows beyond that, up to 20 16-byte vectors (40 of 8 bytes) per lane
+// of a 1024-lane workgroup, held in their storage format (one workgroup per CU).  With few
 // rows the two-kernel split measured faster (a vocabulary softmax of 256 x
 // 152064 bf16: 61 us split, 98 us packed), so this only replaces the
 // streaming path, for kPackedMinRows rows or more.
 constexpr int kPackedNV[] = {12, 16, 19, 20};
 constexpr int64_t kPackedMinRows = 1024;
-bool plan_packed(rr_op op, rr_plan* p, int vec, int64_t nvec) {
+bool plan_packed(rr_op op, rr_plan* p, int vec, int per16, int64_t nvec) {
   if (op != RR_OP_SOFTMAX) return false;
-  for (int nv : kPackedNV) {
+  for (int nv16 : kPackedNV) {
+    const int nv = nv16 * per16;
     if (nvec <= (int64_t)kMaxWaves * 64 * nv) {
       p->variant = RR_VARIANT_BLOCK;
       p->vec_elems = vec;
@@ -199,12 +215,12 @@ bool plan_norm_packed(rr_op op, rr_plan* p, int vec, int64_t nvec) {
   return false;
 }
 
-void plan_split(rr_plan* p, int vec, int64_t nvec) {
+void plan_split(rr_plan* p, int vec, int per16, int64_t nvec) {
   p->variant = RR_VARIANT_SPLIT;
   p->vec_elems = vec;
   p->waves_per_row = 4;
   p->rows_per_group = 1;
-  p->vecs_per_lane = kSplitVecsPerLane;
+  p->vecs_per_lane = kSplitVecsPerLane * per16;
   p->block_threads = 256;
   p->chunks_per_row = ceil_div(nvec, 256 * (int64_t)p->vecs_per_lane);
 }
@@ -237,8 +253,9 @@ rr_status make_plan(rr_op op, int64_t M, int64_t N, int din, int dout, bool is_a
   if (N < 1) return fail(RR_ERR_INVALID_ARG, "row width %lld < 1 (empty rows have no statistic)", (long long)N);
   if (N > kMaxN) return fail(RR_ERR_UNSUPPORTED, "row width %lld > 2^30", (long long)N);
 
-  const int vw = vec_width(din);
+  const int vw = op_vec_width(op, din, dout);
   const int vec = (is_aligned && N % vw == 0) ? vw : 1;
+  const int per16 = vecs_per_16_bytes(din, vec);
   const int64_t nvec = N / vec;
   const int forced = g_override.load(std::memory_order_relaxed);
 
@@ -252,9 +269,9 @@ rr_status make_plan(rr_op op, int64_t M, int64_t N, int din, int dout, bool is_a
         plan_wave(p, vec, nvec);
       } else if (plan_block(op, p, vec, nvec)) {
       } else if (plan_norm_packed(op, p, vec, nvec)) {
-      } else if (M >= kPackedMinRows && plan_packed(op, p, vec, nvec)) {
+      } else if (M >= kPackedMinRows && plan_packed(op, p, vec, per16, nvec)) {
       } else if (op == RR_OP_SOFTMAX && !causal && M < kSplitMaxRows) {
-        plan_split(p, vec, nvec);
+        plan_split(p, vec, per16, nvec);
       } else {
         plan_loop(p, vec, nvec);
       }
@@ -265,14 +282,14 @@ rr_status make_plan(rr_op op, int64_t M, int64_t N, int din, int dout, bool is_a
       if (ok) plan_wave(p, vec, nvec);
       break;
     case RR_VARIANT_BLOCK:
-      ok = vec > 1 && (plan_block(op, p, vec, nvec) || plan_packed(op, p, vec, nvec) ||
+      ok = vec > 1 && (plan_block(op, p, vec, nvec) || plan_packed(op, p, vec, per16, nvec) ||
                        plan_norm_packed(op, p, vec, nvec));
       break;
     case RR_VARIANT_SPLIT:
     case RR_VARIANT_SPLIT_ONE_KERNEL:
       ok = vec > 1 && op == RR_OP_SOFTMAX && !causal;
       if (ok) {
-        plan_split(p, vec, nvec);
+        plan_split(p, vec, per16, nvec);
         p->variant = forced;
       }
       break;
@@ -479,7 +496,9 @@ rr_status softmax_entry(const char* who, void* y, int64_t ldy, const void* x, in
   if (mats_overlap(mx, my, M) && !(x == y && ldx == ldy && in_dtype == out_dtype))
     return fail(RR_ERR_INVALID_ARG,
                 "%s: x and y overlap (in place needs equal pointers, strides and dtypes)", who);
-  const bool al = rows_aligned16(mx) && rows_aligned16(my);
+  // a bf16 input written as fp32 is read 8 bytes per vector (op_vec_width)
+  const size_t in_align = (in_dtype == RR_BF16 && out_dtype == RR_F32) ? 8 : 16;
+  const bool al = rows_aligned(mx, in_align) && rows_aligned16(my);
   rr_plan p;
   const rr_status st = make_plan(o.causal ? RR_OP_SOFTMAX_CAUSAL : RR_OP_SOFTMAX, M, N, in_dtype,
                                  out_dtype, al, &p);

@@ -113,8 +113,12 @@ __device__ __forceinline__ void load_vec(const T* __restrict__ p, float (&v)[VEC
       v[2] = bf16_lo(q.y); v[3] = bf16_hi(q.y);
       v[4] = bf16_lo(q.z); v[5] = bf16_hi(q.z);
       v[6] = bf16_lo(q.w); v[7] = bf16_hi(q.w);
+    } else if constexpr (VEC == 4) {
+      const u32x2_t q = ld<NT>(reinterpret_cast<const u32x2_t*>(p));
+      v[0] = bf16_lo(q.x); v[1] = bf16_hi(q.x);
+      v[2] = bf16_lo(q.y); v[3] = bf16_hi(q.y);
     } else {
-      static_assert(VEC == 1, "bf16 loads are 1 or 8 wide");
+      static_assert(VEC == 1, "bf16 loads are 1, 4 or 8 wide");
       v[0] = __uint_as_float(static_cast<uint32_t>(ld<NT>(p)) << 16);
     }
   }
@@ -143,6 +147,9 @@ struct Packed {
     if constexpr (kWords == 4) {
       const u32x4_t q = ld<NT>(reinterpret_cast<const u32x4_t*>(p));
       w[0] = q.x; w[1] = q.y; w[2] = q.z; w[3] = q.w;
+    } else if constexpr (kWords == 2) {
+      const u32x2_t q = ld<NT>(reinterpret_cast<const u32x2_t*>(p));
+      w[0] = q.x; w[1] = q.y;
     } else if constexpr (std::is_same_v<T, float>) {
       w[0] = __float_as_uint(ld<NT>(p));
     } else {

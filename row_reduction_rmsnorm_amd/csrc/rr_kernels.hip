@@ -605,6 +605,18 @@ __global__ __launch_bounds__(256) void norm_sub_kernel(T* y, T* residual, const 
   }
 }
 
+// Elements per vector of a softmax kernel.  A bf16 row written as fp32 is
+// read four elements (8 bytes) at a time, so that each lane writes one 16-byte
+// fp32 vector and a wavefront's store covers 1 KiB without gaps; eight per
+// load (16 bytes) would give each lane two stores 16 bytes apart and every
+// store instruction only half of each line it touches (measured on a
+// 4096 x 32000 softmax: 3.6 TB/s that way, 4.35 TB/s this way).  Every other
+// pairing reads 16 bytes per load.
+template <typename Tin, typename Tout>
+constexpr int softmax_vec() {
+  return (std::is_same_v<Tin, bf16_t> && std::is_same_v<Tout, float>) ? 4 : Elem<Tin>::kVec;
+}
+
 template <typename Tin, typename Tout, int VEC, int L, bool LOG, bool CAUSAL>
 __global__ __launch_bounds__(256) void softmax_sub_kernel(const Tin* x, Tout* y, int64_t M, int N,
                                                           int64_t cp, int64_t co, RowStrides ld) {
@@ -674,7 +686,7 @@ __global__ __launch_bounds__(256) void softmax_sub_kernel(const Tin* x, Tout* y,
 template <typename Tin, typename Tout, int NV, bool WAVE, bool LOG, bool CAUSAL>
 __global__ __launch_bounds__(1024) void softmax_regs_kernel(const Tin* x, Tout* y, int64_t M,
                                                             int N, int64_t cp, int64_t co, RowStrides ld) {
-  constexpr int VEC = Elem<Tin>::kVec;
+  constexpr int VEC = softmax_vec<Tin, Tout>();
   __shared__ MD slots[2][kMaxWavesPerGroup];
   const RowLane rl = row_lane<WAVE>();
   const int nvec = N / VEC;
@@ -758,7 +770,7 @@ __global__ __launch_bounds__(1024) void softmax_regs_kernel(const Tin* x, Tout* 
 template <typename Tin, typename Tout, int NV, bool LOG, bool CAUSAL>
 __global__ __launch_bounds__(1024) void softmax_packed_kernel(const Tin* x, Tout* y, int64_t M,
                                                               int N, int64_t cp, int64_t co, RowStrides ld) {
-  constexpr int VEC = Elem<Tin>::kVec;
+  constexpr int VEC = softmax_vec<Tin, Tout>();
   constexpr int kThreads = 1024;
   __shared__ MD slots[2][kMaxWavesPerGroup];
   const int t = threadIdx.x;
@@ -905,10 +917,10 @@ struct SplitSlot {
 };
 static_assert(sizeof(SplitSlot) == 16, "slot layout");
 
-template <typename Tin, int NV>
+template <typename Tin, typename Tout, int NV>
 __global__ __launch_bounds__(256) void softmax_split_stats_kernel(const Tin* x, SplitSlot* ws,
                                                                   int64_t M, int N, int S, RowStrides ld) {
-  constexpr int VEC = Elem<Tin>::kVec;
+  constexpr int VEC = softmax_vec<Tin, Tout>();
   constexpr int kThreads = 256;
   constexpr int CV = kThreads * NV;
   __shared__ MD slots[2][kMaxWavesPerGroup];
@@ -996,7 +1008,7 @@ __global__ __launch_bounds__(256) void softmax_split_apply_kernel(const Tin* x, 
                                                                   const SplitSlot* __restrict__ ws,
                                                                   int64_t M, int N, int SA, int SC,
                                                                   int SB, RowStrides ld) {
-  constexpr int VEC = Elem<Tin>::kVec;
+  constexpr int VEC = softmax_vec<Tin, Tout>();
   constexpr int kThreads = 256;
   constexpr int CV = kThreads * NV;
   const RowLane rl = row_lane<false>();
@@ -1068,7 +1080,7 @@ template <typename Tin, typename Tout, int NV>
 __global__ __launch_bounds__(256) void softmax_split_fused_kernel(const Tin* x, Tout* y,
                                                                   SplitSlot* slots_ws, int64_t M,
                                                                   int N, int S, uint64_t tag, RowStrides ld) {
-  constexpr int VEC = Elem<Tin>::kVec;
+  constexpr int VEC = softmax_vec<Tin, Tout>();
   constexpr int kThreads = 256;
   constexpr int CV = kThreads * NV;
   __shared__ MD slots[2][kMaxWavesPerGroup];
@@ -1287,10 +1299,11 @@ hipError_t norm_typed(const rr_plan& p, int kind, const NormArgs& a, int64_t gri
 }
 
 // Vectors per lane in the split path's pass B: its chunks are 256 lanes x
-// this many vectors, independent of pass A's.  One vector per lane (many
-// small workgroups) measured fastest with cold inputs: 67.5 us for the
-// 256 x 152064 bf16 softmax against 68.6 at four and 74.4 at eight.
-constexpr int kSplitApplyNV = 1;
+// this many vectors, independent of pass A's.  Two measured fastest with cold
+// inputs: the 256 x 152064 bf16 -> fp32 softmax (8-byte vectors) takes
+// 64.6 us at two, 82.5 at one and 65.6 at four; a 16 x 2^20 fp32 one 43.5 us
+// at two and 47.0 at one.
+constexpr int kSplitApplyNV = 2;
 
 // One softmax launch: typed pointers plus the row rule (causal period cp,
 // offset co; cp == 0 keeps every key).
@@ -1315,7 +1328,7 @@ hipError_t softmax_regs(const rr_plan& p, const SmCall<Tin, Tout>& c, int64_t gr
     case 2: softmax_regs_kernel<Tin, Tout, 2, WAVE, LOG, CAUSAL><<<g, b, 0, s>>>(c.x, c.y, c.M, c.N, c.cp, c.co, c.ld); break;
     case 4: softmax_regs_kernel<Tin, Tout, 4, WAVE, LOG, CAUSAL><<<g, b, 0, s>>>(c.x, c.y, c.M, c.N, c.cp, c.co, c.ld); break;
     case 8:
-      if constexpr (Elem<Tin>::kVec * 8 <= 32) {
+      if constexpr (softmax_vec<Tin, Tout>() * 8 <= 32) {
         softmax_regs_kernel<Tin, Tout, 8, WAVE, LOG, CAUSAL><<<g, b, 0, s>>>(c.x, c.y, c.M, c.N, c.cp, c.co, c.ld);
         break;
       }
@@ -1381,7 +1394,7 @@ hipError_t softmax_split(const rr_plan& p, const SmCall<Tin, Tout>& c, SplitSlot
       }
     }
   }
-  softmax_split_stats_kernel<Tin, NV><<<grid1(grid), b, 0, s>>>(c.x, w, c.M, c.N, S, c.ld);
+  softmax_split_stats_kernel<Tin, Tout, NV><<<grid1(grid), b, 0, s>>>(c.x, w, c.M, c.N, S, c.ld);
   int SC = S;
   if (S > kSplitDirectMerge) {
     const int64_t gm = c.M < 65536 ? c.M : 65536;
@@ -1389,7 +1402,7 @@ hipError_t softmax_split(const rr_plan& p, const SmCall<Tin, Tout>& c, SplitSlot
     SC = 1;
   }
   // pass B in chunks of its own size
-  constexpr int VEC = Elem<Tin>::kVec;
+  constexpr int VEC = softmax_vec<Tin, Tout>();
   const int nvec = c.N / VEC;
   const int SB = (nvec + 256 * kSplitApplyNV - 1) / (256 * kSplitApplyNV);
   const int64_t items_b = c.M * (int64_t)SB;
@@ -1422,13 +1435,13 @@ hipError_t softmax_typed(const rr_plan& p, const SmCall<Tin, Tout>& c, void* ws,
   const dim3 g = grid1(grid);
   if (p.variant == RR_VARIANT_SUBWAVE) {
     if (p.vec_elems == 1) return softmax_sub<Tin, Tout, 1, LOG, CAUSAL>(p, c, grid, s);
-    return softmax_sub<Tin, Tout, Elem<Tin>::kVec, LOG, CAUSAL>(p, c, grid, s);
+    return softmax_sub<Tin, Tout, softmax_vec<Tin, Tout>(), LOG, CAUSAL>(p, c, grid, s);
   }
   if (p.variant == RR_VARIANT_LOOP) {
     if (p.vec_elems == 1)
       softmax_loop_kernel<Tin, Tout, 1, LOG, CAUSAL><<<g, b, 0, s>>>(c.x, c.y, c.M, c.N, c.cp, c.co, c.ld);
     else
-      softmax_loop_kernel<Tin, Tout, Elem<Tin>::kVec, LOG, CAUSAL><<<g, b, 0, s>>>(c.x, c.y, c.M, c.N, c.cp, c.co, c.ld);
+      softmax_loop_kernel<Tin, Tout, softmax_vec<Tin, Tout>(), LOG, CAUSAL><<<g, b, 0, s>>>(c.x, c.y, c.M, c.N, c.cp, c.co, c.ld);
     return hipGetLastError();
   }
   if (p.variant == RR_VARIANT_SPLIT || p.variant == RR_VARIANT_SPLIT_ONE_KERNEL) {
@@ -1443,13 +1456,15 @@ hipError_t softmax_typed(const rr_plan& p, const SmCall<Tin, Tout>& c, void* ws,
     }
   }
   if (p.variant == RR_VARIANT_WAVE) return softmax_regs<Tin, Tout, true, LOG, CAUSAL>(p, c, grid, s);
-  if (p.vecs_per_lane * Elem<Tin>::kVec > 32) {
-    // long rows held in their storage format (see softmax_packed_kernel)
+  if (p.vecs_per_lane * p.vec_elems > 32) {
+    // long rows held in their storage format (see softmax_packed_kernel); 8-byte
+    // vectors (bf16 written as fp32) come twice as many per lane
+    constexpr int X = softmax_vec<Tin, Tout>() * (int)sizeof(Tin) == 8 ? 2 : 1;
     switch (p.vecs_per_lane) {
-      case 12: softmax_packed_kernel<Tin, Tout, 12, LOG, CAUSAL><<<g, b, 0, s>>>(c.x, c.y, c.M, c.N, c.cp, c.co, c.ld); break;
-      case 16: softmax_packed_kernel<Tin, Tout, 16, LOG, CAUSAL><<<g, b, 0, s>>>(c.x, c.y, c.M, c.N, c.cp, c.co, c.ld); break;
-      case 19: softmax_packed_kernel<Tin, Tout, 19, LOG, CAUSAL><<<g, b, 0, s>>>(c.x, c.y, c.M, c.N, c.cp, c.co, c.ld); break;
-      case 20: softmax_packed_kernel<Tin, Tout, 20, LOG, CAUSAL><<<g, b, 0, s>>>(c.x, c.y, c.M, c.N, c.cp, c.co, c.ld); break;
+      case 12 * X: softmax_packed_kernel<Tin, Tout, 12 * X, LOG, CAUSAL><<<g, b, 0, s>>>(c.x, c.y, c.M, c.N, c.cp, c.co, c.ld); break;
+      case 16 * X: softmax_packed_kernel<Tin, Tout, 16 * X, LOG, CAUSAL><<<g, b, 0, s>>>(c.x, c.y, c.M, c.N, c.cp, c.co, c.ld); break;
+      case 19 * X: softmax_packed_kernel<Tin, Tout, 19 * X, LOG, CAUSAL><<<g, b, 0, s>>>(c.x, c.y, c.M, c.N, c.cp, c.co, c.ld); break;
+      case 20 * X: softmax_packed_kernel<Tin, Tout, 20 * X, LOG, CAUSAL><<<g, b, 0, s>>>(c.x, c.y, c.M, c.N, c.cp, c.co, c.ld); break;
       default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

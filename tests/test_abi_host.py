@@ -226,7 +226,11 @@ WORKLOAD_PLANS = [
     ((rr.RR_OP_FUSED_ADD_RMSNORM, 8192, 4096, rr.RR_BF16, rr.RR_BF16), ("block", 8, 1, 8, 1)),
     ((rr.RR_OP_RMSNORM, 8192, 4096, rr.RR_BF16, rr.RR_BF16), ("block", 4, 2, 8, 1)),
     ((rr.RR_OP_SOFTMAX, 16384, 1024, rr.RR_F32, rr.RR_F32), ("wave", 1, 4, 4, 1)),
-    ((rr.RR_OP_SOFTMAX, 256, 152064, rr.RR_BF16, rr.RR_F32), ("split", 4, 4, 8, 19)),
+    # bf16 read 4 elements (8 bytes) at a time when written as fp32
+    ((rr.RR_OP_SOFTMAX, 256, 152064, rr.RR_BF16, rr.RR_F32), ("split", 4, 8, 4, 19)),
+    ((rr.RR_OP_SOFTMAX, 4096, 32000, rr.RR_BF16, rr.RR_F32), ("block", 16, 8, 4, 1)),
+    ((rr.RR_OP_SOFTMAX, 4096, 32000, rr.RR_BF16, rr.RR_BF16), ("block", 16, 4, 8, 1)),
+    ((rr.RR_OP_SOFTMAX, 2048, 131072, rr.RR_BF16, rr.RR_F32), ("block", 16, 32, 4, 1)),
     ((rr.RR_OP_SOFTMAX, 28 * 4096, 4096, rr.RR_F32, rr.RR_F32), ("block", 8, 2, 4, 1)),
 ]
 
@@ -345,6 +349,8 @@ def test_every_plan_covers_its_row():
                 checked += 1
                 vec, nv, name = p["vec_elems"], p["vecs_per_lane"], p["variant_name"]
                 width = 8 if din == rr.RR_BF16 else 4
+                if op in (rr.RR_OP_SOFTMAX, rr.RR_OP_SOFTMAX_CAUSAL) and (din, dout) == (rr.RR_BF16, rr.RR_F32):
+                    width = 4
                 assert vec in (1, width) and (vec == 1 or (aligned and N % width == 0)), p
                 assert 1 <= p["block_threads"] <= 1024 and p["block_threads"] % 64 == 0, p
                 if name == "subwave":

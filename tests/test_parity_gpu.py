@@ -608,6 +608,18 @@ def test_packed_long_rows_many_rows():
         _say(f"packed softmax {dt} M={M} N={N} nv={p['vecs_per_lane']}")
         x = softmax_input(M, N, seed=M + N, dt=dt)
         check_softmax(x, run_softmax(x, torch.float32), f"packed {M}x{N}")
+    # the packed kernel's edges for bf16 -> fp32 (8-byte vectors: 24 to 40 per
+    # lane), on few rows with the variant forced
+    try:
+        rr.rr_set_variant_override(rr.RR_VARIANT_BLOCK)
+        for (N, nv) in [(98304, 24), (98308, 32), (163836, 40), (163840, 40)]:
+            p = rr.rr_query_plan(rr.RR_OP_SOFTMAX, 5, N, rr.RR_BF16, rr.RR_F32)
+            assert p["vec_elems"] == 4 and p["vecs_per_lane"] == nv and p["block_threads"] == 1024, p
+            _say(f"packed softmax bf16->f32 M=5 N={N} nv={nv}")
+            x = softmax_input(5, N, seed=N, dt="bf16")
+            check_softmax(x, run_softmax(x, torch.float32), f"packed forced 5x{N}")
+    finally:
+        rr.rr_set_variant_override(rr.RR_VARIANT_AUTO)
 
 
 def test_softmax_in_place_unaligned_and_tiny():

@@ -179,3 +179,33 @@ def test_stride_equal_to_width_is_the_contiguous_call_bitwise():
         rr.rr_softmax_rows_strided(b, s)
         torch.cuda.synchronize()
         assert torch.equal(_bits(a), _bits(b))
+
+
+def test_bf16_to_f32_softmax_on_8_byte_aligned_rows_is_the_aligned_call_bitwise():
+    """A bf16 softmax written as fp32 reads 8 bytes per vector, so rows that
+    start 8 (not 16) bytes into a line take the same vector kernel: the same
+    bits as the same rows stored 16-byte aligned, and the oracle's values."""
+    rr = _rr()
+    for (M, N) in [(33, 100), (40, 1028), (9, 32004), (3, 152068), (1100, 4)]:
+        x_cpu = softmax_input(M, N, seed=N, dt="bf16")
+        _say(f"bf16->f32 softmax, 8-byte aligned rows, {M}x{N}")
+        ws_n = rr.rr_softmax_rows_workspace_bytes(M, N, rr.RR_BF16, rr.RR_F32)
+        ws = torch.empty(ws_n, dtype=torch.uint8, device="cuda") if ws_n else None
+        ref = torch.empty(M, N, device="cuda")
+        xa = x_cpu.cuda()
+        if N % 8:
+            # a 16-byte aligned copy of the rows (row stride a multiple of 8)
+            _, xa = embed(x_cpu, N + (8 - N % 8), 0)
+        rr.rr_softmax_rows_strided(ref, xa, None, ws)
+        # the same rows 4 elements (8 bytes) into a wider buffer whose stride
+        # is 8 bytes past a multiple of 16
+        ld = N + 4 + (12 if (N + 4) % 8 == 0 else 8)
+        assert (ld * 2) % 16 == 8 and ld >= N + 4
+        buf, xv = embed(x_cpu, ld, 4)
+        y = torch.empty(M, N, device="cuda")
+        rr.rr_softmax_rows_strided(y, xv, None, ws)
+        torch.cuda.synchronize()
+        assert torch.equal(_bits(ref), _bits(y)), f"{M}x{N}"
+        xf = compare.to_f64(x_cpu)
+        compare.check_softmax(y.cpu(), xf, oracle.softmax(xf), f"8-byte rows {M}x{N}")
+        untouched(buf, 4, N, "input")
