@@ -7,7 +7,7 @@ buffers with inputs already resident in HBM:
   fused      fused residual add + RMSNorm, bf16 I/O, 8192 x 4096
   rms_bf16   RMSNorm bf16, 8192 x 4096 (the fused workload's x and gamma)
   sm_wave    softmax fp32 -> fp32, 16384 x 1024 (a wavefront per row)
-  sm_vocab   softmax bf16 -> fp32, 256 x 152064 (split row: stats + apply)
+  sm_vocab   softmax bf16 -> fp32, 256 x 152064 (a row per 1024-lane workgroup)
   sm_causal  softmax fp32 -> fp32, 28*4096 x 4096, causal -inf mask (a workgroup per row)
 
 value = algorithmic bytes of one step (each input read once, each output
@@ -478,7 +478,7 @@ def main():
         "data": "synthetic",
         "config": {
             "workload": "one step = fused add+RMSNorm bf16 8192x4096 + RMSNorm bf16 8192x4096 + "
-                        "softmax f32 16384x1024 + softmax bf16->f32 256x152064 (split row) + "
+                        "softmax f32 16384x1024 + softmax bf16->f32 256x152064 + "
                         "causal softmax f32 114688x4096",
             "io_dtypes": "bf16 norms; softmax f32->f32, bf16->f32",
             "bytes_per_step": step_bytes,

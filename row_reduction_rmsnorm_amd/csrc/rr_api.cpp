@@ -166,12 +166,15 @@ bool plan_block(rr_op op, rr_plan* p, int vec, int64_t nvec) {
 }
 
 // Softmax rows beyond that, up to 20 16-byte vectors (40 of 8 bytes) per lane
-// of a 1024-lane workgroup, held in their storage format (one workgroup per CU).  With few
-// rows the two-kernel split measured faster (a vocabulary softmax of 256 x
-// 152064 bf16: 61 us split, 98 us packed), so this only replaces the
-// streaming path, for kPackedMinRows rows or more.
+// of a 1024-lane workgroup, held in their storage format (one workgroup per
+// CU).  From kPackedMinRows rows up this beats both the two-kernel split and
+// the streaming path for every dtype pair (cold, e.g. 256 x 152064 bf16 ->
+// fp32: 46.0 us packed, 65.4 split, 78.6 streaming; 256 x 65536 fp32: 28.1,
+// 41.5, 39.8); below it the split spreads a few rows over more CUs (48 rows:
+// 21.1 split, 22.6 packed).  A causal call cannot split, and packed beats
+// streaming at any row count, so it takes this path whenever the row fits.
 constexpr int kPackedNV[] = {12, 16, 19, 20};
-constexpr int64_t kPackedMinRows = 1024;
+constexpr int64_t kPackedMinRows = 64;
 bool plan_packed(rr_op op, rr_plan* p, int vec, int per16, int64_t nvec) {
   if (op != RR_OP_SOFTMAX) return false;
   for (int nv16 : kPackedNV) {
@@ -269,7 +272,7 @@ rr_status make_plan(rr_op op, int64_t M, int64_t N, int din, int dout, bool is_a
         plan_wave(p, vec, nvec);
       } else if (plan_block(op, p, vec, nvec)) {
       } else if (plan_norm_packed(op, p, vec, nvec)) {
-      } else if (M >= kPackedMinRows && plan_packed(op, p, vec, per16, nvec)) {
+      } else if ((M >= kPackedMinRows || causal) && plan_packed(op, p, vec, per16, nvec)) {
       } else if (op == RR_OP_SOFTMAX && !causal && M < kSplitMaxRows) {
         plan_split(p, vec, per16, nvec);
       } else {

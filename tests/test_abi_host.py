@@ -108,12 +108,14 @@ def test_softmax_validation():
     assert f(Y, X, 4, 8, 3, rr.RR_F32, None, 0, None) == rr.RR_ERR_INVALID_ARG
     # in place with different dtypes
     assert f(X, X, 4, 8, rr.RR_BF16, rr.RR_F32, None, 0, None) == rr.RR_ERR_INVALID_ARG
-    # long rows with few rows need the split workspace
-    need = rr.rr_softmax_rows_workspace_bytes(256, 152064, rr.RR_BF16, rr.RR_F32)
-    assert need == 256 * 19 * 16
-    assert f(Y, X, 256, 152064, rr.RR_BF16, rr.RR_F32, None, 0, None) == rr.RR_ERR_WORKSPACE
-    assert f(Y, X, 256, 152064, rr.RR_BF16, rr.RR_F32, W, need - 8, None) == rr.RR_ERR_WORKSPACE
-    assert f(Y, X, 256, 152064, rr.RR_BF16, rr.RR_F32, W + 8, need, None) == rr.RR_ERR_INVALID_ARG
+    # long rows with few rows need the split workspace (from 64 rows up the
+    # row is held by one workgroup and needs none)
+    assert rr.rr_softmax_rows_workspace_bytes(256, 152064, rr.RR_BF16, rr.RR_F32) == 0
+    need = rr.rr_softmax_rows_workspace_bytes(40, 152064, rr.RR_BF16, rr.RR_F32)
+    assert need == 40 * 19 * 16
+    assert f(Y, X, 40, 152064, rr.RR_BF16, rr.RR_F32, None, 0, None) == rr.RR_ERR_WORKSPACE
+    assert f(Y, X, 40, 152064, rr.RR_BF16, rr.RR_F32, W, need - 8, None) == rr.RR_ERR_WORKSPACE
+    assert f(Y, X, 40, 152064, rr.RR_BF16, rr.RR_F32, W + 8, need, None) == rr.RR_ERR_INVALID_ARG
     assert "workspace" in rr.last_error_message()
 
 
@@ -145,12 +147,12 @@ def test_softmax_ex_validation():
     # an empty batch succeeds before the options' pointers are needed
     assert f(None, None, 0, 8, F, F, o(causal_period=3), None, 0, None) == rr.RR_OK
     # log-softmax of few long rows splits like softmax and needs the workspace
-    need = rr.rr_softmax_rows_ex_workspace_bytes(256, 152064, B, F, o(log_output=True))
-    assert need == rr.rr_softmax_rows_workspace_bytes(256, 152064, B, F) == 256 * 19 * 16
-    assert f(Y, X, 256, 152064, B, F, o(log_output=True), None, 0, None) == rr.RR_ERR_WORKSPACE
+    need = rr.rr_softmax_rows_ex_workspace_bytes(40, 152064, B, F, o(log_output=True))
+    assert need == rr.rr_softmax_rows_workspace_bytes(40, 152064, B, F) == 40 * 19 * 16
+    assert f(Y, X, 40, 152064, B, F, o(log_output=True), None, 0, None) == rr.RR_ERR_WORKSPACE
     # a causal call never splits, so it needs no workspace
-    assert rr.rr_softmax_rows_ex_workspace_bytes(256, 152064, B, F, o(causal_period=256)) == 0
-    assert rr.rr_softmax_rows_ex_workspace_bytes(256, 152064, B, F, None) == need
+    assert rr.rr_softmax_rows_ex_workspace_bytes(40, 152064, B, F, o(causal_period=40)) == 0
+    assert rr.rr_softmax_rows_ex_workspace_bytes(40, 152064, B, F, None) == need
     assert rr.rr_softmax_rows_ex_workspace_bytes(4, 8, F, F, o(causal_period=0)) == 0
 
 
@@ -160,10 +162,17 @@ def test_softmax_causal_plans():
     # rows that fit registers keep the softmax plan
     for M, N in ((28 * 4096, 4096), (16384, 1024), (10, 64), (1024, 40000)):
         assert q(C, M, N) == q(S, M, N)
-    # where softmax would split, the causal call streams instead
-    assert q(S, 256, 152064, B, F)["variant_name"] == "split"
-    p = q(C, 256, 152064, B, F)
+    # where softmax would split (few long rows), the causal call holds the row
+    # in one workgroup if it fits, else streams it
+    assert q(S, 40, 152064, B, F)["variant_name"] == "split"
+    p = q(C, 40, 152064, B, F)
+    assert (p["variant_name"], p["block_threads"], p["workspace_bytes"]) == ("block", 1024, 0)
+    p = q(C, 40, 200000, B, F)
     assert p["variant_name"] == "loop" and p["workspace_bytes"] == 0
+    assert q(S, 40, 200000, B, F)["variant_name"] == "split"
+    # from 64 rows up softmax also holds such rows in one workgroup
+    assert q(S, 64, 152064, B, F) == q(C, 64, 152064, B, F)
+    assert q(S, 64, 152064, B, F)["variant_name"] == "block" and q(S, 63, 152064, B, F)["variant_name"] == "split"
     try:
         rr.rr_set_variant_override(rr.RR_VARIANT_SPLIT)
         with pytest.raises(rr.RowReduceError):
@@ -227,7 +236,8 @@ WORKLOAD_PLANS = [
     ((rr.RR_OP_RMSNORM, 8192, 4096, rr.RR_BF16, rr.RR_BF16), ("block", 4, 2, 8, 1)),
     ((rr.RR_OP_SOFTMAX, 16384, 1024, rr.RR_F32, rr.RR_F32), ("wave", 1, 4, 4, 1)),
     # bf16 read 4 elements (8 bytes) at a time when written as fp32
-    ((rr.RR_OP_SOFTMAX, 256, 152064, rr.RR_BF16, rr.RR_F32), ("split", 4, 8, 4, 19)),
+    ((rr.RR_OP_SOFTMAX, 256, 152064, rr.RR_BF16, rr.RR_F32), ("block", 16, 38, 4, 1)),
+    ((rr.RR_OP_SOFTMAX, 63, 152064, rr.RR_BF16, rr.RR_F32), ("split", 4, 8, 4, 19)),
     ((rr.RR_OP_SOFTMAX, 4096, 32000, rr.RR_BF16, rr.RR_F32), ("block", 16, 8, 4, 1)),
     ((rr.RR_OP_SOFTMAX, 4096, 32000, rr.RR_BF16, rr.RR_BF16), ("block", 16, 4, 8, 1)),
     ((rr.RR_OP_SOFTMAX, 2048, 131072, rr.RR_BF16, rr.RR_F32), ("block", 16, 32, 4, 1)),
@@ -267,15 +277,20 @@ def test_dispatch_boundaries():
     assert q(rr.RR_OP_RMSNORM, 20480, B)["vecs_per_lane"] == 4
     assert q(rr.RR_OP_RMSNORM, 65544, B)["variant_name"] == "loop"
     assert v(S, 100, 32768) == "block"
-    # longer softmax rows: split when rows are few; with many rows the row is
-    # held packed (1024 lanes x up to 20 vectors), beyond that it streams
-    assert v(S, 1023, 32772) == "split"
-    assert v(S, 1024, 32772) == "block"
-    assert rr.rr_query_plan(S, 1024, 32772, F, F)["vecs_per_lane"] == 12
-    assert v(S, 1024, 81920) == "block"
+    # longer softmax rows: split when rows are few (below 64); from 64 rows up
+    # the row is held packed (1024 lanes x up to 20 16-byte vectors); rows
+    # longer than that split below 1024 rows and stream from 1024 rows up
+    assert v(S, 63, 32772) == "split"
+    assert v(S, 64, 32772) == "block"
+    assert rr.rr_query_plan(S, 64, 32772, F, F)["vecs_per_lane"] == 12
+    assert v(S, 64, 81920) == "block"
+    assert v(S, 64, 81924) == "split"
+    assert v(S, 1023, 81924) == "split"
     assert v(S, 1024, 81924) == "loop"
     assert v(S, 1024, 163840, B, F) == "block"
+    assert v(S, 1024, 163840, B, B) == "block"
     assert v(S, 1024, 163848, B, F) == "loop"
+    assert v(S, 1023, 163848, B, F) == "split"
     # short rows: several rows per wavefront, L lanes per row
     assert v(S, 10, 128) == "subwave" and rr.rr_query_plan(S, 10, 128, F, F)["waves_per_row"] == 32
     assert v(S, 10, 132) == "wave"
