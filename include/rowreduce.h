@@ -350,6 +350,21 @@ rr_status rr_set_variant_override(rr_variant variant);
 rr_status rr_selftest_wave_allreduce(const float* in, float* out, int64_t count, int kind,
                                      void* stream);
 
+/*
+ * Streaming copy, a measurement reference rather than an operation of the
+ * method: dst[0, bytes) <- src[0, bytes) with 16-byte non-temporal loads and
+ * stores, one vector per lane, no dependency between elements.  An operation
+ * that reads B/2 bytes and writes B/2 bytes moves the same HBM traffic as a
+ * copy of B/2 bytes, so the copy's speed at that size is the practical
+ * streaming bar to set the operation's speed beside (the fixed start-up and
+ * drain of a launch are a visible share at a few hundred megabytes).
+ *   dst, src  device pointers, 16-byte aligned, not overlapping
+ *   bytes     >= 0, a multiple of 16 (0: no launch)
+ * Returns RR_ERR_INVALID_ARG for a bad size, null or misaligned pointers, or
+ * overlap; asynchronous on `stream` like every other call.
+ */
+rr_status rr_stream_copy(void* dst, const void* src, int64_t bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -45,7 +45,7 @@ EXPORTS = (
     "rr_rmsnorm_strided", "rr_fused_add_rmsnorm_strided", "rr_layernorm_strided",
     "rr_softmax_rows_strided",
     "rr_status_string", "rr_last_error_message", "rr_query_plan",
-    "rr_set_variant_override", "rr_selftest_wave_allreduce",
+    "rr_set_variant_override", "rr_selftest_wave_allreduce", "rr_stream_copy",
 )
 
 
@@ -134,10 +134,11 @@ def lib():
     L.rr_query_plan.argtypes = [i32, i64, i64, i32, i32, i32, ctypes.POINTER(rr_plan)]
     L.rr_set_variant_override.argtypes = [i32]
     L.rr_selftest_wave_allreduce.argtypes = [vp, vp, i64, i32, vp]
+    L.rr_stream_copy.argtypes = [vp, vp, i64, vp]
     for f in ("rr_rmsnorm", "rr_fused_add_rmsnorm", "rr_layernorm", "rr_softmax_rows",
               "rr_softmax_rows_ex", "rr_query_plan", "rr_rmsnorm_strided",
               "rr_fused_add_rmsnorm_strided", "rr_layernorm_strided", "rr_softmax_rows_strided",
-              "rr_set_variant_override", "rr_selftest_wave_allreduce"):
+              "rr_set_variant_override", "rr_selftest_wave_allreduce", "rr_stream_copy"):
         getattr(L, f).restype = i32
     _LIB = L
     return L
@@ -437,6 +438,17 @@ def rr_selftest_wave_allreduce(out, inp, kind: int, stream=None) -> None:
     check(lib().rr_selftest_wave_allreduce(inp.data_ptr(), out.data_ptr(), inp.numel() // per,
                                            int(kind), _stream_of(inp, stream)),
           "rr_selftest_wave_allreduce")
+
+
+def rr_stream_copy(dst, src, stream=None) -> None:
+    """dst <- src, every byte, by the library's streaming copy (a measurement
+    reference: the practical bar for an operation moving the same bytes)."""
+    _need_cuda(dst, src)
+    nb = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() != nb or not (src.is_contiguous() and dst.is_contiguous()):
+        raise ValueError("rr_stream_copy: contiguous tensors of equal byte size required")
+    check(lib().rr_stream_copy(dst.data_ptr(), src.data_ptr(), nb, _stream_of(src, stream)),
+          "rr_stream_copy")
 
 
 # ----------------------------------------------------------------------------

@@ -611,4 +611,18 @@ rr_status rr_selftest_wave_allreduce(const float* in, float* out, int64_t count,
                     "rr_selftest_wave_allreduce");
 }
 
+rr_status rr_stream_copy(void* dst, const void* src, int64_t bytes, void* stream) {
+  g_err[0] = '\0';
+  if (bytes < 0 || bytes % 16 != 0)
+    return fail(RR_ERR_INVALID_ARG, "rr_stream_copy: bytes must be a non-negative multiple of 16");
+  if (bytes == 0) return RR_OK;
+  if (!dst || !src) return fail(RR_ERR_INVALID_ARG, "rr_stream_copy: null pointer");
+  if (!aligned16(dst) || !aligned16(src))
+    return fail(RR_ERR_INVALID_ARG, "rr_stream_copy: pointers must be 16-byte aligned");
+  if (overlaps(dst, (size_t)bytes, src, (size_t)bytes))
+    return fail(RR_ERR_INVALID_ARG, "rr_stream_copy: source and destination overlap");
+  return hip_status(rr::launch_stream_copy(dst, src, bytes, static_cast<hipStream_t>(stream)),
+                    "rr_stream_copy");
+}
+
 }  // extern "C"

@@ -67,4 +67,8 @@ hipError_t launch_softmax(const rr_plan& plan, rr_dtype in_dtype, rr_dtype out_d
 hipError_t launch_selftest_wave(const float* in, float* out, int64_t count, int kind,
                                 hipStream_t stream);
 
+// Enqueue the streaming copy of `bytes` bytes (a positive multiple of 16,
+// both pointers 16-byte aligned).
+hipError_t launch_stream_copy(void* dst, const void* src, int64_t bytes, hipStream_t stream);
+
 }  // namespace rr

@@ -75,6 +75,20 @@ def test_m_zero_is_a_noop_even_with_null_pointers():
     assert rr.raw_fused_add_rmsnorm(None, None, None, None, 0, 8, 1e-6, rr.RR_BF16, None) == rr.RR_OK
 
 
+def test_stream_copy_validation():
+    L = rr.lib()
+    assert L.rr_stream_copy(None, None, 0, None) == rr.RR_OK            # empty: no launch
+    for dst, src, nb in ((P, P << 4, -16),          # negative size
+                         (P, P << 4, 24),           # not a multiple of 16
+                         (None, P << 4, 32),        # null destination
+                         (P, None, 32),             # null source
+                         (P + 8, P << 4, 32),       # misaligned destination
+                         (P, (P << 4) + 4, 32),     # misaligned source
+                         (P, P + 16, 64)):          # overlapping ranges
+        assert L.rr_stream_copy(dst, src, nb, None) == rr.RR_ERR_INVALID_ARG, (dst, src, nb)
+        assert rr.last_error_message().startswith("rr_stream_copy")
+
+
 def test_fused_validation():
     X, R, G, Y = P, P << 2, P << 4, P << 6
     ok = dict(y=Y, residual=R, x=X, gamma=G)

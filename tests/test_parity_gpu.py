@@ -154,6 +154,20 @@ def test_wave_allreduce_lane_ids_spikes_and_bitwise_equal_lanes():
     assert np.array_equal(mx[:, 0], np.array([g.max() for g in groups]))
 
 
+@pytest.mark.parametrize("nbytes", [16, 4096 + 48, (64 << 20) + 16, (1 << 30) + 32])
+def test_stream_copy_bytes(nbytes):
+    """The measurement copy moves every byte (both launch shapes: 1024-lane
+    groups below 1 GiB, 256-lane groups from 1 GiB) and nothing past the end."""
+    rr = _rr()
+    _say("stream copy", nbytes)
+    src = torch.randint(0, 256, (nbytes,), dtype=torch.uint8, device="cuda")
+    dst = torch.full((nbytes + 64,), 0xA5, dtype=torch.uint8, device="cuda")
+    rr.rr_stream_copy(dst[:nbytes], src)
+    torch.cuda.synchronize()
+    assert torch.equal(dst[:nbytes], src)
+    assert bool((dst[nbytes:] == 0xA5).all())
+
+
 def test_wave_allreduce_md_pairs():
     from oracle import online_ref
     rr = _rr()
