@@ -433,8 +433,9 @@ def main():
             ops[name](k)
             marks[k][j + 1].record(stream)
     torch.cuda.synchronize()
-    per_op_ms = {name: sum(marks[k][j].elapsed_time(marks[k][j + 1]) for k in range(K)) / K
-                 for j, name in enumerate(OPS)}
+    per_op_all = {name: sorted(marks[k][j].elapsed_time(marks[k][j + 1]) for k in range(K))
+                  for j, name in enumerate(OPS)}
+    per_op_ms = {name: sum(v) / K for name, v in per_op_all.items()}
     step_bytes = sum(algorithmic_bytes(n, bufs[n]["M"], bufs[n]["N"]) for n in OPS)
     value = step_bytes / (ms_step * 1e-3) / 1e9
 
@@ -444,6 +445,8 @@ def main():
         t = per_op_ms[name]
         breakdown[name] = {"M": bufs[name]["M"], "N": bufs[name]["N"], "bytes": nb,
                            "us": round(t * 1e3, 2), "GBps": round(nb / (t * 1e-3) / 1e9, 1),
+                           "us_median": round(per_op_all[name][K // 2] * 1e3, 2),
+                           "us_min": round(per_op_all[name][0] * 1e3, 2),
                            "frac_peak": round(nb / (t * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
                            "rows_per_s": round(bufs[name]["M"] / (t * 1e-3), 1)}
     dom = max(OPS, key=lambda n: per_op_ms[n])
