@@ -120,11 +120,14 @@ rr_status rr_fused_add_rmsnorm(void* y, void* residual, const void* x, const voi
  *   mu_i = (1/H) sum_j x[i, j],   var_i = (1/H) sum_j (x[i, j] - mu_i)^2,
  *   y[i, j] = (x[i, j] - mu_i) / sqrt(var_i + eps) * gamma[j] + beta[j]
  * ([P2] section 八.2; [P4] section "LayerNorm 与 RMSNorm" and its LayerNorm
- * exercise: the mean first, then the variance from the values held in
- * registers.)  Rows up to 16384 elements are held in registers (two
- * reductions per row); longer or unaligned rows are read three times.  The
- * mean is accumulated about the row's first element, so rows whose mean is
- * far larger than their spread keep their precision.
+ * exercise.)  The sums are taken about a shift K, the row's first element:
+ * one reduction carries sum(x - K) and sum((x - K)^2), so rows whose mean is
+ * far larger than their spread keep their precision.  A row whose first
+ * element lies more than two standard deviations from its mean (where that
+ * variance would cancel and x - K would be rounded at the scale of the
+ * distance) is summed once more about its mean.  Rows up to 65536 elements
+ * are held on chip; longer or unaligned rows are read twice (three times for
+ * such an outlying first element).
  *   y      [M, H] output, dtype `dtype`; may be the same pointer as x
  *   x      [M, H] input (finite values)
  *   gamma  [H] scale

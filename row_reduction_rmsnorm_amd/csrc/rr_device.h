@@ -236,6 +236,12 @@ __device__ __forceinline__ void store_vec(T* __restrict__ p, const float (&v)[VE
   }
 }
 
+// Lane 0's value, as a wave-uniform (scalar-register) value.  Only for values
+// that every active lane holds with the same bits.
+__device__ __forceinline__ float uniform_f32(float v) {
+  return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(v)));
+}
+
 // ---------------------------------------------------------------------------
 // wave64 all-reduce
 //

@@ -91,6 +91,40 @@ __device__ __forceinline__ MD group_md(MD v, int nw, int w, int lane,
   return md_merge(t, dpp_md<kDppRowMirror>(t));
 }
 
+// Two sums across the workgroup with one barrier: the slot scheme of
+// group_sum, each slot holding a pair.
+__device__ __forceinline__ void group_sum2(float& a, float& b, int nw, int w, int lane,
+                                           float2 (*slots)[kMaxWavesPerGroup], int parity) {
+  if (lane == 0) slots[parity][w] = make_float2(a, b);
+  __syncthreads();
+  const int j = lane & (kMaxWavesPerGroup - 1);
+  const float2 t = (j < nw) ? slots[parity][j] : make_float2(0.0f, 0.0f);
+  float u = t.x, v = t.y;
+  u = u + dpp_f32<kDppQuadXor1>(u);
+  v = v + dpp_f32<kDppQuadXor1>(v);
+  u = u + dpp_f32<kDppQuadXor2>(u);
+  v = v + dpp_f32<kDppQuadXor2>(v);
+  u = u + dpp_f32<kDppRowHalfMirror>(u);
+  v = v + dpp_f32<kDppRowHalfMirror>(v);
+  a = u + dpp_f32<kDppRowMirror>(u);
+  b = v + dpp_f32<kDppRowMirror>(v);
+}
+
+// LayerNorm moments from the sums s1 = sum(d), s2 = sum(d^2) of d = x - K over
+// a row of N values: c = s1 / N is the mean's offset from K and
+// var = s2 / N - c^2.  That difference cancels when K lies far from the
+// mean, and then every d also carries a rounding error at the scale of
+// |K - mean| rather than of the spread; so it is accepted only when
+// c^2 <= 4 var (K within two standard deviations of the mean).  Otherwise
+// the caller re-centres on K + c (the mean, rounded to fp32) and sums again:
+// the new offset is tiny, the difference no longer cancels, and x - (K + c)
+// is exact wherever the mean is large next to the spread.
+__device__ __forceinline__ bool ln_moments(float s1, float s2, int N, float& c, float& var) {
+  c = s1 / (float)N;
+  var = s2 / (float)N - c * c;
+  return c * c <= 4.0f * var;
+}
+
 // The causal rule along a thread's rows: with period cp >= 1, row r keeps
 // the keys j <= (r mod cp) + co, i.e. min(N, (r mod cp) + co + 1); cp == 0
 // keeps every key.  A thread visits rows row0, row0 + stride, ...; the
@@ -250,34 +284,66 @@ __global__ __launch_bounds__(1024) void norm_regs_kernel(T* y, T* residual, cons
     }
 
     if constexpr (KIND == kNormLayer) {
-      // [P4] section "练习" (LayerNorm): the mean first, then the variance from
-      // the values held in registers.  Everything is taken about the row's
-      // first element K: c = sum(x - K) / N is the mean's offset from K and
-      // x - mean = (x - K) - c, so neither the sum nor the centred values carry
-      // a rounding error relative to the mean itself, only to the row's spread
-      // ([P2] section 八.2 warns about rows whose mean is far larger than their
-      // spread).  The mean K + c is never formed.
-      const float K = load_one<T>(x + ox);
-      float s1 = 0.0f;
+      // [P4] section "练习" (LayerNorm): mean and variance from the values held
+      // in registers, about a shift K: the row's first element, so that
+      // x - K is exact for values near it and the sums carry no rounding at
+      // the scale of the mean ([P2] section 八.2 warns about rows whose mean
+      // is far larger than their spread).  One reduction carries sum(x - K)
+      // and sum((x - K)^2), and x - mean = (x - K) - c.  A row whose first
+      // element lies far from its mean (ln_moments) is shifted by K + c, its
+      // mean rounded to fp32, and summed again: x - mean = (x - (K + c)) - c'.
+      // The row is shifted in place, so one copy of it stays live.
+      // K and the reduced sums are the same in every lane of the row (the
+      // butterflies give every lane the same bits), so lane 0's copies are
+      // moved to scalar registers, which frees vector registers
+      const float K = uniform_f32(load_one<T>(x + ox));
+      // sum(h - S) and sum((h - S)^2) over the row, one reduction
+      auto pair_sums = [&](float S, float& s1, float& s2) {
+        s1 = 0.0f;
+        s2 = 0.0f;
 #pragma unroll
-      for (int k = 0; k < NV; ++k) {
-        const bool valid = k * rl.T + rl.t < nvec;
+        for (int k = 0; k < NV; ++k) {
+          const bool valid = k * rl.T + rl.t < nvec;
 #pragma unroll
-        for (int i = 0; i < VEC; ++i) s1 += valid ? h[k][i] - K : 0.0f;
-      }
-      const float c = row_sum(s1) / (float)N;
-      float s2 = 0.0f;
-#pragma unroll
-      for (int k = 0; k < NV; ++k) {
-        const bool valid = k * rl.T + rl.t < nvec;
-#pragma unroll
-        for (int i = 0; i < VEC; ++i) {
-          h[k][i] = (h[k][i] - K) - c;
-          const float d = valid ? h[k][i] : 0.0f;
-          s2 += d * d;
+          for (int i = 0; i < VEC; ++i) {
+            const float d = valid ? h[k][i] - S : 0.0f;
+            s1 += d;
+            s2 += d * d;
+          }
         }
+        s1 = wave_sum(s1);
+        s2 = wave_sum(s2);
+        if constexpr (!WAVE) {
+          __shared__ float2 pslots[2][kMaxWavesPerGroup];
+          group_sum2(s1, s2, rl.nw, rl.w, rl.lane, pslots, parity);
+          parity ^= 1;
+        }
+        s1 = uniform_f32(s1);
+        s2 = uniform_f32(s2);
+      };
+      // pass 0 sums about K; a row whose K lies far from its mean (every lane
+      // holds the same bits, so the whole row decides alike) is shifted by
+      // K + c and summed once more (pass 1), about 0.  One copy of the
+      // reduction code: the loop is not unrolled.
+      float S = K, c = 0.0f, var = 0.0f;
+#pragma nounroll
+      for (int pass = 0; pass < 2; ++pass) {
+        float s1, s2;
+        pair_sums(S, s1, s2);
+        const bool near = ln_moments(s1, s2, N, c, var) || pass == 1;
+        const float shift = near ? S : S + c;
+#pragma unroll
+        for (int k = 0; k < NV; ++k)
+#pragma unroll
+          for (int i = 0; i < VEC; ++i) h[k][i] = h[k][i] - shift;
+        if (near) break;
+        S = 0.0f;
       }
-      const float rstd = 1.0f / __builtin_sqrtf(row_sum(s2) / (float)N + eps);
+#pragma unroll
+      for (int k = 0; k < NV; ++k)
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) h[k][i] = h[k][i] - c;
+      const float rstd = 1.0f / __builtin_sqrtf(__builtin_fmaxf(var, 0.0f) + eps);
 #pragma unroll
       for (int k = 0; k < NV; ++k) {
         const int vi = k * rl.T + rl.t;
@@ -330,29 +396,36 @@ __global__ __launch_bounds__(1024) void norm_loop_kernel(T* y, T* residual, cons
   for (int64_t row = blockIdx.x; row < M; row += gridDim.x) {
     const int64_t ox = row * ld.x, oy = row * ld.y, orr = row * ld.r;
     if constexpr (KIND == kNormLayer) {
-      // three passes over the row: the mean's offset from the first element,
-      // the variance about the mean, then the output (centred as
-      // (x - K) - c, as in the register kernel)
-      const float K = load_one<T>(x + ox);
-      float s1 = 0.0f;
-      for (int vi = rl.t; vi < nvec; vi += rl.T) {
-        float h[VEC];
-        load_vec<T, VEC, false>(x + ox + (int64_t)vi * VEC, h);
+      // one pass for sum(x - K) and sum((x - K)^2) about the row's first
+      // element (a second about the mean when the first element lies far
+      // from it, see ln_moments), then the output pass, centred as
+      // (x - K) - c as in the register kernel
+      float K = load_one<T>(x + ox);
+      float c, var;
+      auto moments = [&]() {
+        float s1 = 0.0f, s2 = 0.0f;
+        for (int vi = rl.t; vi < nvec; vi += rl.T) {
+          float h[VEC];
+          load_vec<T, VEC, false>(x + ox + (int64_t)vi * VEC, h);
 #pragma unroll
-        for (int i = 0; i < VEC; ++i) s1 += h[i] - K;
-      }
-      const float c = row_sum(s1) / (float)N;
-      float s2 = 0.0f;
-      for (int vi = rl.t; vi < nvec; vi += rl.T) {
-        float h[VEC];
-        load_vec<T, VEC, false>(x + ox + (int64_t)vi * VEC, h);
-#pragma unroll
-        for (int i = 0; i < VEC; ++i) {
-          const float d = (h[i] - K) - c;
-          s2 += d * d;
+          for (int i = 0; i < VEC; ++i) {
+            const float d = h[i] - K;
+            s1 += d;
+            s2 += d * d;
+          }
         }
+        s1 = wave_sum(s1);
+        s2 = wave_sum(s2);
+        __shared__ float2 pslots[2][kMaxWavesPerGroup];
+        group_sum2(s1, s2, rl.nw, rl.w, rl.lane, pslots, parity);
+        parity ^= 1;
+        return ln_moments(s1, s2, N, c, var);
+      };
+      if (!moments()) {
+        K = K + c;
+        moments();
       }
-      const float rstd = 1.0f / __builtin_sqrtf(row_sum(s2) / (float)N + eps);
+      const float rstd = 1.0f / __builtin_sqrtf(__builtin_fmaxf(var, 0.0f) + eps);
       for (int vi = rl.t; vi < nvec; vi += rl.T) {
         float h[VEC], g[VEC], bb[VEC];
         load_vec<T, VEC>(x + ox + (int64_t)vi * VEC, h);
@@ -468,31 +541,36 @@ __global__ __launch_bounds__(1024) void norm_packed_kernel(T* y, T* residual, co
     int t_st = t;
     asm volatile("" : "+v"(t_st));
     if constexpr (KIND == kNormLayer) {
-      // about the row's first element K, as in norm_regs_kernel
-      const float K = load_one<T>(xr);
-      float s1 = 0.0f;
+      // about a shift K (the row's first element, or the mean after a second
+      // sum), as in norm_regs_kernel
+      float K = load_one<T>(xr);
+      float c, var;
+      auto moments = [&]() {
+        float s1 = 0.0f, s2 = 0.0f;
 #pragma unroll
-      for (int k = 0; k < NV; ++k) {
-        const bool valid = k * kThreads + t < nvec;
+        for (int k = 0; k < NV; ++k) {
+          const bool valid = k * kThreads + t < nvec;
 #pragma unroll
-        for (int i = 0; i < VEC; ++i) s1 += valid ? v[k].get(i) - K : 0.0f;
-      }
-#pragma unroll
-      for (int k = 0; k < NV; ++k) v[k].touch();
-      const float c = row_sum(s1) / (float)N;
-      float s2 = 0.0f;
-#pragma unroll
-      for (int k = 0; k < NV; ++k) {
-        const bool valid = k * kThreads + t < nvec;
-#pragma unroll
-        for (int i = 0; i < VEC; ++i) {
-          const float d = valid ? (v[k].get(i) - K) - c : 0.0f;
-          s2 += d * d;
+          for (int i = 0; i < VEC; ++i) {
+            const float d = valid ? v[k].get(i) - K : 0.0f;
+            s1 += d;
+            s2 += d * d;
+          }
         }
-      }
 #pragma unroll
-      for (int k = 0; k < NV; ++k) v[k].touch();
-      const float rstd = 1.0f / __builtin_sqrtf(row_sum(s2) / (float)N + eps);
+        for (int k = 0; k < NV; ++k) v[k].touch();
+        s1 = wave_sum(s1);
+        s2 = wave_sum(s2);
+        __shared__ float2 pslots[2][kMaxWavesPerGroup];
+        group_sum2(s1, s2, kThreads / kWave, w, lane, pslots, parity);
+        parity ^= 1;
+        return ln_moments(s1, s2, N, c, var);
+      };
+      if (!moments()) {
+        K = K + c;
+        moments();
+      }
+      const float rstd = 1.0f / __builtin_sqrtf(__builtin_fmaxf(var, 0.0f) + eps);
 #pragma unroll
       for (int k = 0; k < NV; ++k) {
         const int vi = k * kThreads + t_st;
@@ -577,21 +655,27 @@ __global__ __launch_bounds__(256) void norm_sub_kernel(T* y, T* residual, const 
     }
     float o[VEC];
     if constexpr (KIND == kNormLayer) {
-      const float K = load_one<T>(x + row * ld.x);
-      float s1 = 0.0f;
+      // about a shift K (the row's first element, or the mean after a second
+      // sum), as in norm_regs_kernel; the group's lanes hold the same bits
+      float K = load_one<T>(x + row * ld.x);
+      float c, var;
+      auto moments = [&]() {
+        float s1 = 0.0f, s2 = 0.0f;
 #pragma unroll
-      for (int i = 0; i < VEC; ++i) s1 += active ? h[i] - K : 0.0f;
-      const float c = group_lanes_sum<L>(s1) / (float)N;
-      float s2 = 0.0f;
-#pragma unroll
-      for (int i = 0; i < VEC; ++i) {
-        h[i] = (h[i] - K) - c;
-        const float d = active ? h[i] : 0.0f;
-        s2 += d * d;
+        for (int i = 0; i < VEC; ++i) {
+          const float d = active ? h[i] - K : 0.0f;
+          s1 += d;
+          s2 += d * d;
+        }
+        return ln_moments(group_lanes_sum<L>(s1), group_lanes_sum<L>(s2), N, c, var);
+      };
+      if (!moments()) {
+        K = K + c;
+        moments();
       }
-      const float rstd = 1.0f / __builtin_sqrtf(group_lanes_sum<L>(s2) / (float)N + eps);
+      const float rstd = 1.0f / __builtin_sqrtf(__builtin_fmaxf(var, 0.0f) + eps);
 #pragma unroll
-      for (int i = 0; i < VEC; ++i) o[i] = (h[i] * rstd) * g.get(i) + bb.get(i);
+      for (int i = 0; i < VEC; ++i) o[i] = (((h[i] - K) - c) * rstd) * g.get(i) + bb.get(i);
     } else {
       float ss = 0.0f;
 #pragma unroll

@@ -409,7 +409,25 @@ def test_layernorm_edge_cases():
     check_ln(xt, gt, bt, 1e-5, yv.cpu(), "ln unaligned")
 
 
-def test_workload_layernorm_full():
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("N", [96, 1024, 4096, 20480, 70000])
+def test_layernorm_first_element_far_from_the_mean(dt, N):
+    """LayerNorm sums about a row's first element.  When that element lies far
+    from the row's mean, the one-reduction variance would cancel and every
+    x - K would be rounded at the scale of the distance, so the kernels sum
+    again about the mean.  Rows here put the first element at various
+    distances (some rows take that second sum, some do not), on the
+    short-row, wavefront, workgroup, packed and streaming paths."""
+    _say(f"layernorm far first element {dt} N={N}")
+    rng = np.random.default_rng(N)
+    x = rng.standard_normal((8, N)).astype(np.float32)
+    x[:, 0] = np.array([50.0, -300.0, 1.0e4, 7.0, -7.0, 0.5, 2.5, -3.0], np.float32)
+    x[7, 1:] += 1.0e3                      # mean far from zero as well
+    g = rng.uniform(0.5, 1.5, N).astype(np.float32)
+    b = rng.uniform(-1.0, 1.0, N).astype(np.float32)
+    xt, gt, bt = _as(x, dt), _as(g, dt), _as(b, dt)
+    check_ln(xt, gt, bt, 1e-5, run_layernorm(xt, gt, bt, 1e-5), f"ln far first {dt} N={N}")
     """The LayerNorm exercise's shape: 256 x 5120, x ~ U(100, 102)."""
     w = workloads.make("layernorm")
     _say(w.description)
