@@ -107,10 +107,18 @@ def lib():
             raise ImportError(f"ROWREDUCE_LIB={LIB_PATH} does not exist")
         from . import build as _build
         _build.build()
+    _LIB = load_library(LIB_PATH)
+    return _LIB
+
+
+def load_library(path):
+    """A ctypes handle on a build of the library at `path` with every
+    declared function's argument and result types set (lib() uses it for
+    the library itself; the race-stress tests use it for the stress build)."""
     try:
-        L = ctypes.CDLL(LIB_PATH)
+        L = ctypes.CDLL(path)
     except OSError as e:
-        raise ImportError(f"cannot load {LIB_PATH}: {e}") from e
+        raise ImportError(f"cannot load {path}: {e}") from e
     vp, i64, f32, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_float, ctypes.c_int
     L.rr_rmsnorm.argtypes = [vp, vp, vp, i64, i64, f32, i32, vp]
     L.rr_fused_add_rmsnorm.argtypes = [vp, vp, vp, vp, i64, i64, f32, i32, vp]
@@ -140,7 +148,6 @@ def lib():
               "rr_fused_add_rmsnorm_strided", "rr_layernorm_strided", "rr_softmax_rows_strided",
               "rr_set_variant_override", "rr_selftest_wave_allreduce", "rr_stream_copy"):
         getattr(L, f).restype = i32
-    _LIB = L
     return L
 
 

@@ -325,9 +325,20 @@ rr_status make_plan(rr_op op, int64_t M, int64_t N, int din, int dout, bool is_a
 // measured slower on MI355X for every kernel here), capped so that a
 // dispatch's work-items fit in 32 bits (grid x threads below 2^32; every
 // kernel walks its rows grid-stride, so a capped grid still covers them all).
+#ifndef RR_STRESS
+#define RR_STRESS 0
+#endif
+
 int64_t grid_for(const rr_plan& p) {
   const int64_t g = p.work_items;
   const int64_t kMaxGrid = 0xffffffffLL / (p.block_threads > 0 ? p.block_threads : 1);
+#if RR_STRESS
+  // the race-stress build (see rr_kernels.hip): few workgroups, each walking
+  // many rows, so that the LDS slot sets are reused many times; the
+  // cooperative split keeps its grid (its waits need every workgroup
+  // resident, which it checks against its own grid)
+  if (p.variant != RR_VARIANT_SPLIT_ONE_KERNEL && g > 37) return 37;
+#endif
   return g > kMaxGrid ? kMaxGrid : g;
 }
 

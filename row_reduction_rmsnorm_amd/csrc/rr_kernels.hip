@@ -50,6 +50,50 @@ static_assert(kNormRms == kLaunchRms && kNormFused == kLaunchFused && kNormLayer
 
 namespace {
 
+// ---------------------------------------------------------------------------
+// Race stress.  A build with RR_STRESS defined to 1 (a separate library that
+// only the tests load) adds two hooks to every LDS slot stage below, and its
+// host side caps grids at a few dozen workgroups so that each workgroup walks
+// many rows and reuses its slot sets over and over:
+//  * stress_delay: a pause of 0-7 x 512 cycles, drawn per wavefront from its
+//    clock, before every slot write and before every slot read, so that the
+//    wavefronts of a workgroup reach them in shuffled order;
+//  * stress_poison: right after a stage's barrier every wavefront has
+//    finished reading the other slot set (its next write comes after this
+//    barrier), so each wavefront overwrites its own slot there with NaN: a
+//    read the barriers failed to order would see NaN, not a plausible value.
+// Neither hook changes any arithmetic, so a correct stage gives the stress
+// build the same bits as the normal one; the tests require exactly that.
+// Normal builds contain no code for either.
+// ---------------------------------------------------------------------------
+#ifndef RR_STRESS
+#define RR_STRESS 0
+#endif
+
+__device__ __forceinline__ void stress_delay() {
+#if RR_STRESS
+  const int n = (int)((__builtin_amdgcn_s_memtime() >> 4) & 7);
+  for (int i = 0; i < n; ++i) __builtin_amdgcn_s_sleep(8);
+#endif
+}
+
+template <typename S>
+__device__ __forceinline__ void stress_poison(S (*slots)[kMaxWavesPerGroup], int parity, int w, int lane) {
+#if RR_STRESS
+  if (lane == 0) {
+    S bad;
+    float* f = reinterpret_cast<float*>(&bad);
+    for (int i = 0; i < (int)(sizeof(S) / sizeof(float)); ++i) f[i] = __builtin_nanf("");
+    slots[parity ^ 1][w] = bad;
+  }
+#else
+  (void)slots;
+  (void)parity;
+  (void)w;
+  (void)lane;
+#endif
+}
+
 // LDS stage for one value per wavefront ([P2] section 四 and [P5] section
 // "原 RMSNorm 草稿的两个关键错误": one slot per wavefront, a barrier, then a
 // single combine).  Lane l of every wavefront reads slot (l mod 16) (the
@@ -63,8 +107,11 @@ namespace {
 // [P4] section "实现" close with a trailing barrier.
 __device__ __forceinline__ float group_sum(float v, int nw, int w, int lane,
                                            float (*slots)[kMaxWavesPerGroup], int parity) {
+  stress_delay();
   if (lane == 0) slots[parity][w] = v;
   __syncthreads();
+  stress_poison(slots, parity, w, lane);
+  stress_delay();
   const int j = lane & (kMaxWavesPerGroup - 1);
   float t = (j < nw) ? slots[parity][j] : 0.0f;
   t = t + dpp_f32<kDppQuadXor1>(t);
@@ -75,8 +122,11 @@ __device__ __forceinline__ float group_sum(float v, int nw, int w, int lane,
 
 __device__ __forceinline__ MD group_md(MD v, int nw, int w, int lane,
                                        MD (*slots)[kMaxWavesPerGroup], int parity) {
+  stress_delay();
   if (lane == 0) slots[parity][w] = v;
   __syncthreads();
+  stress_poison(slots, parity, w, lane);
+  stress_delay();
   const int j = lane & (kMaxWavesPerGroup - 1);
   MD t;
   if (j < nw) {
@@ -95,8 +145,11 @@ __device__ __forceinline__ MD group_md(MD v, int nw, int w, int lane,
 // group_sum, each slot holding a pair.
 __device__ __forceinline__ void group_sum2(float& a, float& b, int nw, int w, int lane,
                                            float2 (*slots)[kMaxWavesPerGroup], int parity) {
+  stress_delay();
   if (lane == 0) slots[parity][w] = make_float2(a, b);
   __syncthreads();
+  stress_poison(slots, parity, w, lane);
+  stress_delay();
   const int j = lane & (kMaxWavesPerGroup - 1);
   const float2 t = (j < nw) ? slots[parity][j] : make_float2(0.0f, 0.0f);
   float u = t.x, v = t.y;
@@ -1495,7 +1548,10 @@ hipError_t softmax_split(const rr_plan& p, const SmCall<Tin, Tout>& c, SplitSlot
   softmax_split_stats_kernel<Tin, Tout, NV><<<grid1(grid), b, 0, s>>>(c.x, w, c.M, c.N, S, c.ld);
   int SC = S;
   if (S > kSplitDirectMerge) {
-    const int64_t gm = c.M < 65536 ? c.M : 65536;
+    int64_t gm = c.M < 65536 ? c.M : 65536;
+#if RR_STRESS
+    gm = gm < 37 ? gm : 37;   // the race-stress build's grid cap
+#endif
     softmax_split_merge_kernel<<<grid1(gm), dim3(256), 0, s>>>(w, c.M, S);
     SC = 1;
   }
