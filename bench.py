@@ -26,7 +26,8 @@ largest share of the step).
 
 cpu_baseline: the fp64 CPU oracle, timed on the host cores over the same
 workloads (all rows by default; --cpu-fraction takes the first rows of each),
-reported in the same unit.
+reported in the same unit.  parity: the GPU outputs of the same run against
+those oracle outputs, per operation, at the test suite's bars.
 """
 import argparse
 import hashlib
@@ -172,14 +173,30 @@ def sanity(torch, bufs):
         assert err < 1e-4, f"{name}: row sums off by {err}"
 
 
-def cpu_baseline(bufs, fraction):
+def cpu_baseline(torch, rr, ops, bufs, fraction):
     """Time the fp64 oracle on the first ceil(M * fraction) rows of every
-    workload; returns the equivalent GB/s over the same algorithmic bytes."""
+    workload; returns the equivalent GB/s over the same algorithmic bytes.
+
+    Outside the timed calls, the oracle's outputs also serve as the parity
+    check of this run: each operation is run once more on buffer set 0 (the
+    fused op, which updates its residual in place on every step, on a fresh
+    copy of the original residual) and its output on those rows is compared
+    with them at the bars of tests/compare.py.  Returns (baseline, parity)."""
     import numpy as np
     import oracle
+    from tests import compare
     total_t = 0.0
     total_b = 0
     parts = []
+    parity = {}
+
+    def check(name, fn, bar):
+        try:
+            parity[name] = dict(fn(), bar=bar, ok=True)
+        except AssertionError as e:
+            parity[name] = dict(bar=bar, ok=False, error=str(e))
+            log(f"[bench] PARITY FAILURE {name}: {e}")
+
     for name in OPS:
         b = bufs[name]
         M, N = b["M"], b["N"]
@@ -189,23 +206,41 @@ def cpu_baseline(bufs, fraction):
             rs = b["r0"][:m].double().numpy()
             g = b["g"].float().cpu().double().numpy()
             t0 = time.perf_counter()
-            oracle.fused_add_rmsnorm(xs, rs, g, b["eps"], "bf16")
+            h_ref, y_ref = oracle.fused_add_rmsnorm(xs, rs, g, b["eps"], "bf16")
             dt = time.perf_counter() - t0
+            r_gpu = b["r0"][:m].to(b["x"].device)
+            y_gpu = torch.empty_like(r_gpu)
+            rr.rr_fused_add_rmsnorm(y_gpu, r_gpu, b["x"][:m], b["g"], b["eps"])
+            torch.cuda.synchronize()
+            check(name, lambda: {"residual": compare.check_bf16_exact(r_gpu, h_ref, "fused residual"),
+                                 "y": compare.check_bf16(y_gpu, y_ref, "fused y")},
+                  "residual bit-exact; y <= 1 bf16 ulp")
+            del h_ref, y_ref, r_gpu, y_gpu
         elif name == "rms_bf16":
             g = b["g"].float().cpu().double().numpy()
             t0 = time.perf_counter()
-            oracle.rmsnorm(xs, g, b["eps"])
+            ref = oracle.rmsnorm(xs, g, b["eps"])
             dt = time.perf_counter() - t0
+            ops[name](0)
+            torch.cuda.synchronize()
+            check(name, lambda: compare.check_bf16(b["y"][:m], ref, name), "<= 1 bf16 ulp")
+            del ref
         else:
             t0 = time.perf_counter()
-            oracle.softmax(xs)
+            ref = oracle.softmax(xs)
             dt = time.perf_counter() - t0
+            ops[name](0)
+            torch.cuda.synchronize()
+            check(name, lambda: compare.check_softmax(b["y"][:m], xs, ref, name),
+                  f"max |g - r| <= {compare.SOFTMAX_F32_ATOL:g} per probability; rows sum to 1 within "
+                  f"{compare.SOFTMAX_ROWSUM_ATOL:g}")
+            del ref
         nb = algorithmic_bytes(name, m, N)
         total_t += dt
         total_b += nb
         parts.append(f"{name} {m}/{M} rows")
         del xs
-    return {
+    base = {
         "value": round(total_b / total_t / 1e9, 3),
         "unit": "GB/s",
         "cores": oracle.num_threads(),
@@ -215,6 +250,7 @@ def cpu_baseline(bufs, fraction):
                    f"{total_b / 1e9:.3f} GB algorithmic, {total_t:.2f} s on the host"),
         "seconds": round(total_t, 3),
     }
+    return base, parity
 
 
 def measure_extras(torch, rr, dev, K, bufs):
@@ -467,10 +503,10 @@ def main():
     # launch between events; the op's own cold figure is in size_matched_copy)
     roofline["same_size_copy_GBps"] = copy_ref[dom]["copy_GBps"]
 
-    cpu = None
+    cpu = parity = None
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a sample ...")
-        cpu = cpu_baseline(bufs, args.cpu_fraction)
+        cpu, parity = cpu_baseline(torch, rr, ops, bufs, args.cpu_fraction)
 
     line = {
         "metric": METRIC,
@@ -496,6 +532,7 @@ def main():
         "pct_of_peak": round(100.0 * value / PEAK_HBM_GBS, 2),
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "parity": parity,
         "breakdown": breakdown,
         "extras": extras,
         "size_matched_copy": copy_ref,
