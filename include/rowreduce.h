@@ -324,14 +324,24 @@ typedef struct rr_plan {
   int64_t chunks_per_row;   /* SPLIT: workgroups per row; otherwise 1 */
   int64_t work_items;       /* workgroup-steps needed (rows / rows_per_group x chunks) */
   size_t workspace_bytes;   /* SPLIT: M * chunks_per_row * 16; otherwise 0 */
+  int32_t row_shift;        /* 1: softmax rows cut into vectors at aligned addresses (WAVE,
+                               BLOCK): a row starting inside a vector, or ending inside one, is
+                               accessed whole vectors at a time except its first and last
+                               vector, whose elements inside the row are accessed one by one */
 } rr_plan;
 
 /*
- * The launch plan the library would use.  aligned16 != 0 states that every
- * row start of the call will be aligned for vector access (16 bytes; 8 for
- * the bf16 input of a softmax written as fp32).  Honours the variant
- * override below.  Returns RR_ERR_INVALID_ARG / RR_ERR_UNSUPPORTED as the
- * corresponding call would.
+ * The launch plan the library would use.  aligned16 describes the call's
+ * row starts:
+ *   1  every row start is aligned for vector access (16 bytes; 8 for the
+ *      bf16 input of a softmax written as fp32);
+ *   2  row starts anywhere, but each input row and its output row sit at the
+ *      same element offset within a vector (contiguous rows of a width that
+ *      is not a whole number of vectors, column slices with equal strides):
+ *      a softmax then cuts rows at aligned addresses (row_shift);
+ *   0  neither: element-by-element access.
+ * Honours the variant override below.  Returns RR_ERR_INVALID_ARG /
+ * RR_ERR_UNSUPPORTED as the corresponding call would.
  */
 rr_status rr_query_plan(rr_op op, int64_t M, int64_t N, rr_dtype in_dtype, rr_dtype out_dtype,
                         int aligned16, rr_plan* plan);

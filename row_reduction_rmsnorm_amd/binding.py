@@ -86,6 +86,7 @@ class rr_plan(ctypes.Structure):
         ("chunks_per_row", ctypes.c_int64),
         ("work_items", ctypes.c_int64),
         ("workspace_bytes", ctypes.c_size_t),
+        ("row_shift", ctypes.c_int32),
     ]
 
     def as_dict(self):
@@ -222,10 +223,12 @@ def rr_softmax_rows_ex_workspace_bytes(M: int, N: int, in_dtype: int, out_dtype:
     return int(lib().rr_softmax_rows_ex_workspace_bytes(M, N, in_dtype, out_dtype, _opts_ref(opts)))
 
 
-def rr_query_plan(op: int, M: int, N: int, in_dtype: int, out_dtype: int, aligned16: bool = True):
+def rr_query_plan(op: int, M: int, N: int, in_dtype: int, out_dtype: int, aligned16=True):
+    """aligned16: True/1 vector-aligned rows; False/0 element access; 2 rows
+    at a common offset within a vector (see include/rowreduce.h)."""
     p = rr_plan()
-    check(lib().rr_query_plan(op, M, N, in_dtype, out_dtype, 1 if aligned16 else 0,
-                              ctypes.byref(p)), "rr_query_plan")
+    mode = 2 if aligned16 == 2 else (1 if aligned16 else 0)
+    check(lib().rr_query_plan(op, M, N, in_dtype, out_dtype, mode, ctypes.byref(p)), "rr_query_plan")
     return p.as_dict()
 
 

@@ -237,8 +237,27 @@ void plan_loop(rr_plan* p, int vec, int64_t nvec) {
   p->block_threads = 64 * p->waves_per_row;
 }
 
-// Host-only plan.  `is_aligned`: every pointer of the call is 16-byte aligned.
-rr_status make_plan(rr_op op, int64_t M, int64_t N, int din, int dout, bool is_aligned,
+// Softmax rows cut into vectors at aligned addresses (row_shift): the row
+// starts at element `lead` of its first vector, so it spans up to nvec_s
+// vectors (see make_plan).  A wavefront, a workgroup or the
+// packed workgroup holds them; longer rows stream (scalar).
+bool plan_shifted(rr_op op, rr_plan* p, int vw, int per16, int64_t nvec_s) {
+  bool ok = false;
+  if (wave_fits(op, vw, nvec_s)) {
+    plan_wave(p, vw, nvec_s);
+    ok = true;
+  } else {
+    ok = plan_block(op, p, vw, nvec_s) || plan_packed(op, p, vw, per16, nvec_s);
+  }
+  if (ok) p->row_shift = 1;
+  return ok;
+}
+
+// Host-only plan.  `align`: 1 every row start of the call is vector-aligned;
+// 2 row starts anywhere, but input and output rows sit at the same element
+// offset within a vector (softmax rows are then cut at aligned addresses);
+// 0 neither (scalar access).
+rr_status make_plan(rr_op op, int64_t M, int64_t N, int din, int dout, int align,
                     rr_plan* p) {
   memset(p, 0, sizeof(*p));
   if (op != RR_OP_RMSNORM && op != RR_OP_FUSED_ADD_RMSNORM && op != RR_OP_SOFTMAX &&
@@ -257,15 +276,25 @@ rr_status make_plan(rr_op op, int64_t M, int64_t N, int din, int dout, bool is_a
   if (N > kMaxN) return fail(RR_ERR_UNSUPPORTED, "row width %lld > 2^30", (long long)N);
 
   const int vw = op_vec_width(op, din, dout);
-  const int vec = (is_aligned && N % vw == 0) ? vw : 1;
+  const bool plain = align == 1 && N % vw == 0;
+  // rows that are not whole aligned vectors but can be cut at aligned
+  // addresses: aligned starts with a ragged width, or starts at a common
+  // offset (softmax only; the norms' gamma lies in a frame of its own)
+  const bool shiftable = !plain && align != 0 && op == RR_OP_SOFTMAX;
+  const int vec = plain ? vw : 1;
   const int per16 = vecs_per_16_bytes(din, vec);
   const int64_t nvec = N / vec;
+  // vectors a cut row spans: with aligned starts (lead 0) ceil(N / vw), with
+  // starts at any offset up to ceil((N + vw - 1) / vw)
+  const int64_t nvec_s = align == 1 ? ceil_div(N, vw) : (N + 2 * (int64_t)vw - 2) / vw;
+  const int per16_s = vecs_per_16_bytes(din, vw);
   const int forced = g_override.load(std::memory_order_relaxed);
 
   bool ok = false;
   switch (forced) {
     case RR_VARIANT_AUTO:
       if (plan_sub(p, vec, nvec)) {
+      } else if (shiftable && plan_shifted(op, p, vw, per16_s, nvec_s)) {
       } else if (vec == 1) {
         plan_loop(p, vec, nvec);
       } else if (wave_fits(op, vec, nvec)) {
@@ -282,11 +311,21 @@ rr_status make_plan(rr_op op, int64_t M, int64_t N, int din, int dout, bool is_a
       break;
     case RR_VARIANT_WAVE:
       ok = vec > 1 && wave_fits(op, vec, nvec);
-      if (ok) plan_wave(p, vec, nvec);
+      if (ok) {
+        plan_wave(p, vec, nvec);
+      } else if (shiftable && wave_fits(op, vw, nvec_s)) {
+        plan_wave(p, vw, nvec_s);
+        p->row_shift = 1;
+        ok = true;
+      }
       break;
     case RR_VARIANT_BLOCK:
       ok = vec > 1 && (plan_block(op, p, vec, nvec) || plan_packed(op, p, vec, per16, nvec) ||
                        plan_norm_packed(op, p, vec, nvec));
+      if (!ok && shiftable) {
+        ok = plan_block(op, p, vw, nvec_s) || plan_packed(op, p, vw, per16_s, nvec_s);
+        if (ok) p->row_shift = 1;
+      }
       break;
     case RR_VARIANT_SPLIT:
     case RR_VARIANT_SPLIT_ONE_KERNEL:
@@ -403,7 +442,7 @@ rr_status norm_entry(int kind, void* y, int64_t ldy, void* residual, int64_t ldr
                   (!fused || rows_aligned16(mr)) && (!layer || !beta || aligned16(beta));
   const rr_op op = fused ? RR_OP_FUSED_ADD_RMSNORM : layer ? RR_OP_LAYERNORM : RR_OP_RMSNORM;
   rr_plan p;
-  const rr_status st = make_plan(op, M, H, dtype, dtype, al, &p);
+  const rr_status st = make_plan(op, M, H, dtype, dtype, al ? 1 : 0, &p);
   if (st != RR_OK) return st;
   rr::NormArgs a;
   a.y = y;
@@ -512,10 +551,23 @@ rr_status softmax_entry(const char* who, void* y, int64_t ldy, const void* x, in
                 "%s: x and y overlap (in place needs equal pointers, strides and dtypes)", who);
   // a bf16 input written as fp32 is read 8 bytes per vector (op_vec_width)
   const size_t in_align = (in_dtype == RR_BF16 && out_dtype == RR_F32) ? 8 : 16;
-  const bool al = rows_aligned(mx, in_align) && rows_aligned16(my);
+  int align = 0;
+  if (rows_aligned(mx, in_align) && rows_aligned16(my)) {
+    align = 1;
+  } else {
+    // every row of x and of y at the same element offset within a vector:
+    // element-aligned bases at the same offset, strides equal modulo the
+    // vector width (contiguous rows of any width, in place, column slices)
+    const int64_t vw = op_vec_width(RR_OP_SOFTMAX, in_dtype, out_dtype);
+    const uintptr_t ux = reinterpret_cast<uintptr_t>(x), uy = reinterpret_cast<uintptr_t>(y);
+    const size_t sx = dtype_size(in_dtype), sy = dtype_size(out_dtype);
+    if (ux % sx == 0 && uy % sy == 0 && (int64_t)((ux / sx) % vw) == (int64_t)((uy / sy) % vw) &&
+        ldx % vw == ldy % vw)
+      align = 2;
+  }
   rr_plan p;
   const rr_status st = make_plan(o.causal ? RR_OP_SOFTMAX_CAUSAL : RR_OP_SOFTMAX, M, N, in_dtype,
-                                 out_dtype, al, &p);
+                                 out_dtype, align, &p);
   if (st != RR_OK) return st;
   if (p.workspace_bytes > 0) {
     if (!workspace || workspace_bytes < p.workspace_bytes)
@@ -557,7 +609,7 @@ size_t rr_softmax_rows_ex_workspace_bytes(int64_t M, int64_t N, rr_dtype in_dtyp
   rr_softmax_opts o;
   if (softmax_options(opts, "rr_softmax_rows_ex_workspace_bytes", &o) != RR_OK) return 0;
   rr_plan p;
-  if (make_plan(o.causal ? RR_OP_SOFTMAX_CAUSAL : RR_OP_SOFTMAX, M, N, in_dtype, out_dtype, true,
+  if (make_plan(o.causal ? RR_OP_SOFTMAX_CAUSAL : RR_OP_SOFTMAX, M, N, in_dtype, out_dtype, 1,
                 &p) != RR_OK)
     return 0;
   return p.workspace_bytes;
@@ -602,7 +654,7 @@ rr_status rr_query_plan(rr_op op, int64_t M, int64_t N, rr_dtype in_dtype, rr_dt
                         int is_aligned16, rr_plan* plan) {
   g_err[0] = '\0';
   if (!plan) return fail(RR_ERR_INVALID_ARG, "rr_query_plan: null plan");
-  return make_plan(op, M, N, in_dtype, out_dtype, is_aligned16 != 0, plan);
+  return make_plan(op, M, N, in_dtype, out_dtype, is_aligned16 == 2 ? 2 : (is_aligned16 != 0 ? 1 : 0), plan);
 }
 
 rr_status rr_set_variant_override(rr_variant v) {

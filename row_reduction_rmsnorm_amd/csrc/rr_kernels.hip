@@ -216,6 +216,42 @@ __device__ __forceinline__ void mask_keys(float (&v)[VEC], int e0, int keys) {
     if (e0 + i >= keys) v[i] = kNegInf;
 }
 
+// Rows whose starts are not vector-aligned (SHIFT kernels; the host checks
+// that input and output rows share their offset within a vector): row r is
+// cut into vectors at aligned addresses, so vector j covers the row's
+// elements [j * VEC - lead, (j + 1) * VEC - lead), lead = the row start's
+// element offset within its vector.  Vectors inside the row are accessed
+// whole; the first and last may reach outside it, and only their elements
+// inside the row are accessed, one at a time (nothing outside the row is
+// ever read or written).
+template <typename T>
+__device__ __forceinline__ int row_lead(const T* row_start, int vec) {
+  return (int)((reinterpret_cast<uintptr_t>(row_start) / sizeof(T)) % (uintptr_t)vec);
+}
+
+// The elements e0 + i of a vector that lie in [0, keys), the rest -inf.
+template <typename T, int VEC>
+__device__ __forceinline__ void load_edge(const T* row, int e0, int keys, float (&v)[VEC]) {
+#pragma unroll
+  for (int i = 0; i < VEC; ++i) {
+    const int e = e0 + i;
+    v[i] = (e >= 0 && e < keys) ? load_one<T>(row + e) : kNegInf;
+  }
+}
+
+// Store the elements e0 + i that lie in [0, n).
+template <typename T, int VEC>
+__device__ __forceinline__ void store_edge(T* row, int e0, int n, const float (&o)[VEC]) {
+#pragma unroll
+  for (int i = 0; i < VEC; ++i) {
+    const int e = e0 + i;
+    if (e >= 0 && e < n) {
+      const float one[1] = {o[i]};
+      store_vec<T, 1>(row + e, one);
+    }
+  }
+}
+
 // Thread coordinates.  WAVE: each wavefront owns a row, the workgroup holds
 // blockDim/64 rows.  Otherwise the whole workgroup (blockDim/64 wavefronts)
 // owns one row.
@@ -820,7 +856,7 @@ __global__ __launch_bounds__(256) void softmax_sub_kernel(const Tin* x, Tout* y,
 // entries are all -inf has m_l = -inf and c_l = 0; a row whose entries are
 // all -inf has m = -inf and every output is NaN, as exp(x - m)/d is.
 // ===========================================================================
-template <typename Tin, typename Tout, int NV, bool WAVE, bool LOG, bool CAUSAL>
+template <typename Tin, typename Tout, int NV, bool WAVE, bool LOG, bool CAUSAL, bool SHIFT>
 __global__ __launch_bounds__(1024) void softmax_regs_kernel(const Tin* x, Tout* y, int64_t M,
                                                             int N, int64_t cp, int64_t co, RowStrides ld) {
   constexpr int VEC = softmax_vec<Tin, Tout>();
@@ -833,14 +869,20 @@ __global__ __launch_bounds__(1024) void softmax_regs_kernel(const Tin* x, Tout* 
   int parity = 0;
   for (int64_t row = row0; row < M; row += stride, cr.next()) {
     const int keys = cr.keys(N);
-    const int nvec_keys = (keys + VEC - 1) / VEC;   // vectors holding kept keys
-    const int64_t ox = row * ld.x, oy = row * ld.y;
+    const Tin* xr = x + row * ld.x;
+    Tout* yr = y + row * ld.y;
+    // SHIFT: vector j covers the row's elements [j * VEC - lead, ...)
+    const int lead = SHIFT ? row_lead(xr, VEC) : 0;
+    const int nvec_row = SHIFT ? (lead + N + VEC - 1) / VEC : nvec;
+    const int nvec_keys = (lead + keys + VEC - 1) / VEC;   // vectors holding kept keys
     float v[NV][VEC];
 #pragma unroll
     for (int k = 0; k < NV; ++k) {
       const int vi = k * rl.T + rl.t;
+      const int e0 = vi * VEC - lead;
       if (vi < nvec_keys) {
-        load_vec<Tin, VEC>(x + ox + (int64_t)vi * VEC, v[k]);
+        if (!SHIFT || (e0 >= 0 && e0 + VEC <= N)) load_vec<Tin, VEC>(xr + e0, v[k]);
+        else load_edge<Tin, VEC>(xr, e0, keys, v[k]);
       } else {
 #pragma unroll
         for (int i = 0; i < VEC; ++i) v[k][i] = kNegInf;
@@ -850,7 +892,7 @@ __global__ __launch_bounds__(1024) void softmax_regs_kernel(const Tin* x, Tout* 
     // holding the last kept key become -inf (after all loads are issued)
     if (keys < N) {
 #pragma unroll
-      for (int k = 0; k < NV; ++k) mask_keys<VEC>(v[k], (k * rl.T + rl.t) * VEC, keys);
+      for (int k = 0; k < NV; ++k) mask_keys<VEC>(v[k], (k * rl.T + rl.t) * VEC - lead, keys);
     }
     float ml = kNegInf;
 #pragma unroll
@@ -886,10 +928,14 @@ __global__ __launch_bounds__(1024) void softmax_regs_kernel(const Tin* x, Tout* 
 #pragma unroll
     for (int k = 0; k < NV; ++k) {
       const int vi = k * rl.T + rl.t;
+      const int e0 = vi * VEC - lead;
       float o[VEC];
 #pragma unroll
       for (int i = 0; i < VEC; ++i) o[i] = LOG ? (v[k][i] - p.m) - ld : v[k][i] * c;
-      if (vi < nvec) store_vec<Tout, VEC>(y + oy + (int64_t)vi * VEC, o);
+      if (vi < nvec_row) {
+        if (!SHIFT || (e0 >= 0 && e0 + VEC <= N)) store_vec<Tout, VEC>(yr + e0, o);
+        else store_edge<Tout, VEC>(yr, e0, N, o);
+      }
     }
   }
 }
@@ -904,7 +950,7 @@ __global__ __launch_bounds__(1024) void softmax_regs_kernel(const Tin* x, Tout* 
 // bf16 row needs 19 vectors (76 VGPRs) per lane of a 1024-lane workgroup, one
 // workgroup per CU.
 // ===========================================================================
-template <typename Tin, typename Tout, int NV, bool LOG, bool CAUSAL>
+template <typename Tin, typename Tout, int NV, bool LOG, bool CAUSAL, bool SHIFT>
 __global__ __launch_bounds__(1024) void softmax_packed_kernel(const Tin* x, Tout* y, int64_t M,
                                                               int N, int64_t cp, int64_t co, RowStrides ld) {
   constexpr int VEC = softmax_vec<Tin, Tout>();
@@ -918,9 +964,12 @@ __global__ __launch_bounds__(1024) void softmax_packed_kernel(const Tin* x, Tout
   CausalRows cr(blockIdx.x, gridDim.x, CAUSAL ? cp : 0, co);
   for (int64_t row = blockIdx.x; row < M; row += gridDim.x, cr.next()) {
     const int keys = cr.keys(N);
-    const int nvec_keys = (keys + VEC - 1) / VEC;
     const Tin* xr = x + row * ld.x;   // uniform row bases
     Tout* yr = y + row * ld.y;
+    // SHIFT: vector j covers the row's elements [j * VEC - lead, ...)
+    const int lead = SHIFT ? row_lead(xr, VEC) : 0;
+    const int nvec_row = SHIFT ? (lead + N + VEC - 1) / VEC : nvec;
+    const int nvec_keys = (lead + keys + VEC - 1) / VEC;
     // the lane's vector offsets are recomputed at each use rather than kept
     // live across the row (an opaque copy of the lane index), which frees
     // the registers the packed row needs
@@ -930,15 +979,25 @@ __global__ __launch_bounds__(1024) void softmax_packed_kernel(const Tin* x, Tout
 #pragma unroll
     for (int k = 0; k < NV; ++k) {
       const int vi = k * kThreads + t_ld;
-      if (vi < nvec_keys) v[k].template load<true>(xr + vi * VEC);
-      else v[k].fill(kNegInf);
+      const int e0 = vi * VEC - lead;
+      if (vi < nvec_keys) {
+        if (!SHIFT || (e0 >= 0 && e0 + VEC <= N)) {
+          v[k].template load<true>(xr + e0);
+        } else {
+          float f[VEC];
+          load_edge<Tin, VEC>(xr, e0, keys, f);
+          v[k].set(f);
+        }
+      } else {
+        v[k].fill(kNegInf);
+      }
     }
     // a row the causal rule cuts: keys past the count inside the vector
     // holding the last kept key become -inf
     if (keys < N) {
 #pragma unroll
       for (int k = 0; k < NV; ++k) {
-        const int first = keys - (k * kThreads + t) * VEC;
+        const int first = keys - ((k * kThreads + t) * VEC - lead);
         if (first > 0 && first < VEC) v[k].mask_from(first);
       }
     }
@@ -971,11 +1030,15 @@ __global__ __launch_bounds__(1024) void softmax_packed_kernel(const Tin* x, Tout
 #pragma unroll
     for (int k = 0; k < NV; ++k) {
       const int vi = k * kThreads + t_st;
+      const int e0 = vi * VEC - lead;
       float o[VEC];
 #pragma unroll
       for (int i = 0; i < VEC; ++i)
         o[i] = LOG ? (key(k, i) - p.m) - ld : exp_shifted(key(k, i) - p.m) * inv_d;
-      if (vi < nvec) store_vec<Tout, VEC>(yr + vi * VEC, o);
+      if (vi < nvec_row) {
+        if (!SHIFT || (e0 >= 0 && e0 + VEC <= N)) store_vec<Tout, VEC>(yr + e0, o);
+        else store_edge<Tout, VEC>(yr, e0, N, o);
+      }
     }
   }
 }
@@ -1469,24 +1532,48 @@ struct SmCall {
   RowStrides ld;
 };
 
-template <typename Tin, typename Tout, bool WAVE, bool LOG, bool CAUSAL>
+template <typename Tin, typename Tout, bool WAVE, bool LOG, bool CAUSAL, bool SHIFT>
 hipError_t softmax_regs(const rr_plan& p, const SmCall<Tin, Tout>& c, int64_t grid, hipStream_t s) {
   const dim3 b(p.block_threads);
   const dim3 g = grid1(grid);
   // At most 32 values per lane (NV * VEC <= 32).
   switch (p.vecs_per_lane) {
-    case 1: softmax_regs_kernel<Tin, Tout, 1, WAVE, LOG, CAUSAL><<<g, b, 0, s>>>(c.x, c.y, c.M, c.N, c.cp, c.co, c.ld); break;
-    case 2: softmax_regs_kernel<Tin, Tout, 2, WAVE, LOG, CAUSAL><<<g, b, 0, s>>>(c.x, c.y, c.M, c.N, c.cp, c.co, c.ld); break;
-    case 4: softmax_regs_kernel<Tin, Tout, 4, WAVE, LOG, CAUSAL><<<g, b, 0, s>>>(c.x, c.y, c.M, c.N, c.cp, c.co, c.ld); break;
+    case 1: softmax_regs_kernel<Tin, Tout, 1, WAVE, LOG, CAUSAL, SHIFT><<<g, b, 0, s>>>(c.x, c.y, c.M, c.N, c.cp, c.co, c.ld); break;
+    case 2: softmax_regs_kernel<Tin, Tout, 2, WAVE, LOG, CAUSAL, SHIFT><<<g, b, 0, s>>>(c.x, c.y, c.M, c.N, c.cp, c.co, c.ld); break;
+    case 4: softmax_regs_kernel<Tin, Tout, 4, WAVE, LOG, CAUSAL, SHIFT><<<g, b, 0, s>>>(c.x, c.y, c.M, c.N, c.cp, c.co, c.ld); break;
     case 8:
       if constexpr (softmax_vec<Tin, Tout>() * 8 <= 32) {
-        softmax_regs_kernel<Tin, Tout, 8, WAVE, LOG, CAUSAL><<<g, b, 0, s>>>(c.x, c.y, c.M, c.N, c.cp, c.co, c.ld);
+        softmax_regs_kernel<Tin, Tout, 8, WAVE, LOG, CAUSAL, SHIFT><<<g, b, 0, s>>>(c.x, c.y, c.M, c.N, c.cp, c.co, c.ld);
         break;
       }
       return hipErrorInvalidValue;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+// The workgroup-per-row kernels: the register form, or (more than 32 values
+// per lane) the packed form, either for vector-aligned rows or for rows cut
+// at aligned addresses (SHIFT).
+template <typename Tin, typename Tout, bool LOG, bool CAUSAL, bool SHIFT>
+hipError_t softmax_rows_held(const rr_plan& p, const SmCall<Tin, Tout>& c, int64_t grid, hipStream_t s) {
+  const dim3 b(p.block_threads);
+  const dim3 g = grid1(grid);
+  if (p.variant == RR_VARIANT_WAVE) return softmax_regs<Tin, Tout, true, LOG, CAUSAL, SHIFT>(p, c, grid, s);
+  if (p.vecs_per_lane * p.vec_elems > 32) {
+    // long rows held in their storage format (see softmax_packed_kernel); 8-byte
+    // vectors (bf16 written as fp32) come twice as many per lane
+    constexpr int X = softmax_vec<Tin, Tout>() * (int)sizeof(Tin) == 8 ? 2 : 1;
+    switch (p.vecs_per_lane) {
+      case 12 * X: softmax_packed_kernel<Tin, Tout, 12 * X, LOG, CAUSAL, SHIFT><<<g, b, 0, s>>>(c.x, c.y, c.M, c.N, c.cp, c.co, c.ld); break;
+      case 16 * X: softmax_packed_kernel<Tin, Tout, 16 * X, LOG, CAUSAL, SHIFT><<<g, b, 0, s>>>(c.x, c.y, c.M, c.N, c.cp, c.co, c.ld); break;
+      case 19 * X: softmax_packed_kernel<Tin, Tout, 19 * X, LOG, CAUSAL, SHIFT><<<g, b, 0, s>>>(c.x, c.y, c.M, c.N, c.cp, c.co, c.ld); break;
+      case 20 * X: softmax_packed_kernel<Tin, Tout, 20 * X, LOG, CAUSAL, SHIFT><<<g, b, 0, s>>>(c.x, c.y, c.M, c.N, c.cp, c.co, c.ld); break;
+      default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+  }
+  return softmax_regs<Tin, Tout, false, LOG, CAUSAL, SHIFT>(p, c, grid, s);
 }
 
 // Workgroups of `kernel` (256 threads) the current device holds at once, or 0
@@ -1609,21 +1696,8 @@ hipError_t softmax_typed(const rr_plan& p, const SmCall<Tin, Tout>& c, void* ws,
       default: return hipErrorInvalidValue;
     }
   }
-  if (p.variant == RR_VARIANT_WAVE) return softmax_regs<Tin, Tout, true, LOG, CAUSAL>(p, c, grid, s);
-  if (p.vecs_per_lane * p.vec_elems > 32) {
-    // long rows held in their storage format (see softmax_packed_kernel); 8-byte
-    // vectors (bf16 written as fp32) come twice as many per lane
-    constexpr int X = softmax_vec<Tin, Tout>() * (int)sizeof(Tin) == 8 ? 2 : 1;
-    switch (p.vecs_per_lane) {
-      case 12 * X: softmax_packed_kernel<Tin, Tout, 12 * X, LOG, CAUSAL><<<g, b, 0, s>>>(c.x, c.y, c.M, c.N, c.cp, c.co, c.ld); break;
-      case 16 * X: softmax_packed_kernel<Tin, Tout, 16 * X, LOG, CAUSAL><<<g, b, 0, s>>>(c.x, c.y, c.M, c.N, c.cp, c.co, c.ld); break;
-      case 19 * X: softmax_packed_kernel<Tin, Tout, 19 * X, LOG, CAUSAL><<<g, b, 0, s>>>(c.x, c.y, c.M, c.N, c.cp, c.co, c.ld); break;
-      case 20 * X: softmax_packed_kernel<Tin, Tout, 20 * X, LOG, CAUSAL><<<g, b, 0, s>>>(c.x, c.y, c.M, c.N, c.cp, c.co, c.ld); break;
-      default: return hipErrorInvalidValue;
-    }
-    return hipGetLastError();
-  }
-  return softmax_regs<Tin, Tout, false, LOG, CAUSAL>(p, c, grid, s);
+  if (p.row_shift) return softmax_rows_held<Tin, Tout, LOG, CAUSAL, true>(p, c, grid, s);
+  return softmax_rows_held<Tin, Tout, LOG, CAUSAL, false>(p, c, grid, s);
 }
 
 template <typename Tin, typename Tout>

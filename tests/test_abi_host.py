@@ -312,12 +312,29 @@ def test_dispatch_boundaries():
     assert rr.rr_query_plan(S, 10, 1, F, F)["waves_per_row"] == 1
     assert v(rr.RR_OP_FUSED_ADD_RMSNORM, 10, 256, B, B) == "subwave"
     assert v(S, 10, 7) == "subwave" and rr.rr_query_plan(S, 10, 7, F, F)["vec_elems"] == 1
-    assert v(S, 10, 33) == "loop"          # unaligned and longer than 32 elements
-    # unaligned widths or pointers take the scalar streaming path
-    assert v(S, 10, 1023) == "loop"
-    assert v(S, 10, 1024, al=False) == "loop"
-    assert rr.rr_query_plan(S, 10, 1023, F, F)["vec_elems"] == 1
+    # softmax rows that are not whole aligned vectors (a ragged width, or rows
+    # starting at a common offset within a vector) are cut at aligned
+    # addresses and held like aligned rows (row_shift); up to 32 elements they
+    # keep the scalar short-row path
+    sh = lambda M, N, a=F, b=F, al=2, op=S: rr.rr_query_plan(op, M, N, a, b, al)
+    assert v(S, 10, 20, al=2) == "subwave" and sh(10, 20)["vec_elems"] == 1 and sh(10, 20)["row_shift"] == 0
+    # (vectors per lane with aligned starts and a ragged width, lead 0; with
+    # starts at a common offset, room for a lead of up to vec - 1 elements)
+    for M, N, a, b, name, nv1, nv2 in ((10, 33, F, F, "wave", 1, 1), (10, 1023, F, F, "wave", 4, 8),
+                                       (16384, 1025, F, F, "wave", 8, 8), (8192, 4097, F, F, "block", 2, 2),
+                                       (256, 50257, B, F, "block", 24, 24), (3, 50257, B, B, "block", 12, 12),
+                                       (2, 50257, F, B, "block", 16, 16)):
+        for al, nv in ((True, nv1), (2, nv2)):
+            p = sh(M, N, a, b, al)
+            assert (p["variant_name"], p["vecs_per_lane"], p["row_shift"]) == (name, nv, 1), (M, N, al, p)
+            assert p["vec_elems"] == (4 if (a, b) != (B, B) else 8) and p["workspace_bytes"] == 0, p
+    assert sh(64, 4097, op=rr.RR_OP_SOFTMAX_CAUSAL)["row_shift"] == 1
+    # too long to hold, or element access requested: the scalar streaming path
+    assert sh(4, 152065)["variant_name"] == "loop" and sh(4, 152065)["vec_elems"] == 1
+    assert v(S, 10, 1024, al=False) == "loop" and sh(10, 1024, al=False)["row_shift"] == 0
+    # the norms' gamma lies in a frame of its own: unaligned norm rows stream
     assert v(rr.RR_OP_RMSNORM, 10, 4100, B, B) == "loop"   # 4100 % 8 != 0
+    assert sh(10, 4100, B, B, op=rr.RR_OP_RMSNORM)["row_shift"] == 0
 
 
 def test_forced_variants():
@@ -369,7 +386,7 @@ def test_every_plan_covers_its_row():
                 M = int(rng.choice([0, 1, 7, 255, 256, 1023, 1024, 5000, 100000]))
                 din = int(rng.integers(0, 2))
                 dout = int(rng.integers(0, 2)) if op in (rr.RR_OP_SOFTMAX, rr.RR_OP_SOFTMAX_CAUSAL) else din
-                aligned = bool(rng.integers(0, 4))
+                aligned = [0, 1, 1, 2][int(rng.integers(0, 4))]   # element access, aligned, common offset
                 try:
                     p = rr.rr_query_plan(op, M, N, din, dout, aligned)
                 except rr.RowReduceError as e:
@@ -380,7 +397,17 @@ def test_every_plan_covers_its_row():
                 width = 8 if din == rr.RR_BF16 else 4
                 if op in (rr.RR_OP_SOFTMAX, rr.RR_OP_SOFTMAX_CAUSAL) and (din, dout) == (rr.RR_BF16, rr.RR_F32):
                     width = 4
-                assert vec in (1, width) and (vec == 1 or (aligned and N % width == 0)), p
+                shift = p["row_shift"]
+                if shift:
+                    # rows cut at aligned addresses: softmax only, held by a
+                    # wavefront or workgroup, room for the worst lead (vec - 1)
+                    assert op in (rr.RR_OP_SOFTMAX, rr.RR_OP_SOFTMAX_CAUSAL) and vec == width, p
+                    assert aligned == 2 or (aligned == 1 and N % width != 0), p
+                    assert name in ("wave", "block"), p
+                    cap = (64 if name == "wave" else p["block_threads"]) * nv * vec
+                    assert cap >= (N if aligned == 1 else N + vec - 1), p
+                else:
+                    assert vec in (1, width) and (vec == 1 or (aligned == 1 and N % width == 0)), p
                 assert 1 <= p["block_threads"] <= 1024 and p["block_threads"] % 64 == 0, p
                 if name == "subwave":
                     assert p["waves_per_row"] * vec >= N and p["rows_per_group"] * p["waves_per_row"] == 256, p

@@ -654,6 +654,39 @@ def test_packed_long_rows_many_rows():
         rr.rr_set_variant_override(rr.RR_VARIANT_AUTO)
 
 
+
+SHIFT_WIDTHS = [33, 63, 65, 1023, 1025, 2049, 4097, 8191, 16385, 32767, 50257]
+SHIFT_DTYPES = [("f32", "f32"), ("bf16", "f32"), ("bf16", "bf16"), ("f32", "bf16")]
+
+
+@pytest.mark.parametrize("din,dout", SHIFT_DTYPES)
+@pytest.mark.parametrize("N", SHIFT_WIDTHS)
+def test_softmax_rows_cut_at_aligned_addresses(din, dout, N):
+    """Softmax rows that are not whole aligned vectors are cut into vectors at
+    aligned addresses (row_shift plans): contiguous rows of a width that is not
+    a whole number of vectors (row r starts at offset r * N within a vector),
+    and column slices at an odd column of wider matrices with equal strides
+    (one common offset), whose surrounding columns must stay untouched."""
+    rr = _rr()
+    code = {"f32": rr.RR_F32, "bf16": rr.RR_BF16}
+    for M in (1, 7, 66):
+        plan = rr.rr_query_plan(rr.RR_OP_SOFTMAX, M, N, code[din], code[dout], 2)
+        _say(f"cut rows {din}->{dout} M={M} N={N} plan={plan['variant_name']} shift={plan['row_shift']}")
+        if N > 32 and N <= 32768:
+            assert plan["row_shift"] == 1, plan
+        x = softmax_input(M, N, seed=N + M, dt=din)
+        check_softmax(x, run_softmax(x, _tdt(dout)), f"cut rows {din}->{dout} {M}x{N}")
+    M, c0, ld = 9, 3, N + 5
+    x = softmax_input(M, N, seed=N + 1000, dt=din)
+    X = torch.full((M, ld), float("nan"), dtype=_tdt(din), device="cuda")
+    X[:, c0:c0 + N] = x.cuda()
+    Y = torch.full((M, ld), 7.0, dtype=_tdt(dout), device="cuda")
+    rr.rr_softmax_rows_strided(Y[:, c0:c0 + N], X[:, c0:c0 + N])
+    torch.cuda.synchronize()
+    Yc = Y.cpu()
+    check_softmax(x, Yc[:, c0:c0 + N].contiguous(), f"cut column slice {din}->{dout} N={N}")
+    assert bool((Yc[:, :c0] == 7.0).all()) and bool((Yc[:, c0 + N:] == 7.0).all()), "columns outside the slice changed"
+
 def test_softmax_in_place_unaligned_and_tiny():
     rr = _rr()
     for dt in ("f32", "bf16"):

@@ -146,6 +146,9 @@ CAUSAL_CASES = [
     (33, 32768, 33, 32735),
     (1030, 40000, 1030, 38970),
     (9, 152064, 9, 152055),
+    (300, 1025, 300, 0),        # odd widths: rows cut at aligned addresses (wave, block, packed)
+    (40, 4097, 40, 4057),
+    (66, 50257, 66, 50191),
 ]
 
 

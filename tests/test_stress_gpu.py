@@ -140,7 +140,9 @@ def _softmax_rows(M, N, seed):
 SOFTMAX_CASES = [
     # (in dtype, out dtype, M, N, expected plan, log output)
     (F32, F32, 300, 4096, "block", 0),
-    (F32, F32, 300, 4097, "loop", 0),       # unaligned rows stream
+    (F32, F32, 300, 4097, "block", 0),      # a ragged width: rows cut at aligned addresses
+    (BF16, F32, 80, 50257, "block", 1),     # the same, packed, log output
+    (F32, F32, 1024, 81924, "loop", 0),     # too long to hold with this many rows: streams
     (BF16, F32, 80, 152064, "block", 0),    # packed
     (BF16, F32, 80, 152064, "block", 1),
     (F32, F32, 4, 152064, "split", 0),
