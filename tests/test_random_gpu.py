@@ -118,3 +118,61 @@ def test_random_case(case):
         compare.check_log_softmax(ys.cpu(), xf, oracle.log_softmax(xf), what)
     else:
         compare.check_softmax(ys.cpu(), xf, oracle.softmax(xf), what)
+
+
+CUT_CASES = 40
+
+
+@pytest.mark.parametrize("case", range(CUT_CASES))
+def test_random_softmax_rows_cut_at_aligned_addresses(case):
+    """Softmax calls whose rows are not whole aligned vectors but whose input
+    and output rows share their offset within a vector: contiguous rows of a
+    width off the vector grid (each row at a different offset), or column
+    slices with the same left pad and the same stride (one offset), drawn at
+    random with dtypes, log output and the causal rule.  Such rows are cut at
+    aligned addresses (row_shift) whenever a held plan can hold them."""
+    rr = _rr()
+    rng = np.random.default_rng(5000 + case)
+    N = _width(rng) | 1                  # odd: never a whole number of vectors
+    M = _rows(rng, N)
+    din = "bf16" if rng.random() < 0.5 else "f32"
+    dout = "bf16" if rng.random() < 0.3 else "f32"
+    log_output = bool(rng.random() < 0.4)
+    causal = bool(rng.random() < 0.4)
+    x = softmax_input(M, N, seed=case + 77, dt=din)
+    xf = compare.to_f64(x)
+    period = offset = None
+    if causal:
+        period = int(rng.integers(1, M + 1))
+        offset = int(rng.integers(0, N + 2))
+        keys = np.minimum(N, np.arange(M) % period + offset + 1)
+        masked = np.arange(N)[None, :] >= keys[:, None]
+        xf[masked] = -np.inf
+        x = _as(np.where(masked, np.float32(np.nan), compare.to_f64(x)).astype(np.float32), din)
+    if rng.random() < 0.5:
+        xs = x.cuda()
+        ys = torch.empty((M, N), dtype=_tdt(dout), device="cuda")
+    else:
+        pad = int(rng.integers(1, 9))
+        ld = N + pad + int(rng.integers(0, 9))
+        X = torch.zeros((M, ld), dtype=x.dtype, device="cuda")
+        X[:, pad:pad + N] = x.cuda()
+        Y = torch.zeros((M, ld), dtype=_tdt(dout), device="cuda")
+        xs, ys = X[:, pad:pad + N], Y[:, pad:pad + N]
+    op = rr.RR_OP_SOFTMAX_CAUSAL if causal else rr.RR_OP_SOFTMAX
+    plan = rr.rr_query_plan(op, M, N, rr.dtype_code(xs), rr.dtype_code(ys), 2)
+    _say(f"random cut-row softmax {case}: {din}->{dout} {M}x{N} log={log_output} causal={causal} "
+         f"plan={plan['variant_name']} shift={plan['row_shift']}")
+    if plan["variant_name"] in ("wave", "block"):
+        assert plan["row_shift"] == 1, plan
+    opts = rr.make_softmax_opts(log_output=log_output, causal_period=period,
+                                causal_offset=offset if causal else 0)
+    n = rr.rr_softmax_rows_ex_workspace_bytes(M, N, rr.dtype_code(xs), rr.dtype_code(ys), opts)
+    ws = torch.empty(n, dtype=torch.uint8, device="cuda") if n else None
+    rr.rr_softmax_rows_strided(ys, xs, opts, ws)
+    torch.cuda.synchronize()
+    what = f"random cut-row softmax {case} {din}->{dout} log={log_output} causal={causal}"
+    if log_output:
+        compare.check_log_softmax(ys.cpu(), xf, oracle.log_softmax(xf), what)
+    else:
+        compare.check_softmax(ys.cpu(), xf, oracle.softmax(xf), what)
