@@ -142,8 +142,9 @@ rr_status rr_layernorm(void* y, const void* x, const void* gamma, const void* be
  * for this shape (0 when the chosen kernel needs none).  Very long rows with
  * few rows are split over several workgroups; each writes its chunk's
  * (m, d) pair to a 16-byte slot of the workspace and the row's slots are
- * merged ([P4] section "练习", the vocabulary-split exercise).  Host-only;
- * returns 0 for invalid arguments.
+ * merged ([P4] section "练习", the vocabulary-split exercise).  The size
+ * covers rows at any address (a row starting inside a vector may take one
+ * more chunk).  Host-only; returns 0 for invalid arguments.
  */
 size_t rr_softmax_rows_workspace_bytes(int64_t M, int64_t N, rr_dtype in_dtype,
                                        rr_dtype out_dtype);
@@ -325,7 +326,7 @@ typedef struct rr_plan {
   int64_t work_items;       /* workgroup-steps needed (rows / rows_per_group x chunks) */
   size_t workspace_bytes;   /* SPLIT: M * chunks_per_row * 16; otherwise 0 */
   int32_t row_shift;        /* 1: softmax rows cut into vectors at aligned addresses (WAVE,
-                               BLOCK): a row starting inside a vector, or ending inside one, is
+                               BLOCK, SPLIT): a row starting inside a vector, or ending inside one, is
                                accessed whole vectors at a time except its first and last
                                vector, whose elements inside the row are accessed one by one */
 } rr_plan;

@@ -239,15 +239,23 @@ void plan_loop(rr_plan* p, int vec, int64_t nvec) {
 
 // Softmax rows cut into vectors at aligned addresses (row_shift): the row
 // starts at element `lead` of its first vector, so it spans up to nvec_s
-// vectors (see make_plan).  A wavefront, a workgroup or the
-// packed workgroup holds them; longer rows stream (scalar).
-bool plan_shifted(rr_op op, rr_plan* p, int vw, int per16, int64_t nvec_s) {
-  bool ok = false;
+// vectors (see make_plan).  The same choice as for aligned rows: a
+// wavefront, a workgroup, the packed workgroup from kPackedMinRows rows (or
+// for a causal call), else the split below kSplitMaxRows rows; longer rows
+// stream (scalar).  The split sizes its chunks for a row at any offset
+// (nvec_any) so that the workspace query, which sees no addresses, covers
+// every call.
+bool plan_shifted(rr_op op, bool causal, int64_t M, rr_plan* p, int vw, int per16, int64_t nvec_s,
+                  int64_t nvec_any) {
+  bool ok = true;
   if (wave_fits(op, vw, nvec_s)) {
     plan_wave(p, vw, nvec_s);
-    ok = true;
+  } else if (plan_block(op, p, vw, nvec_s)) {
+  } else if ((M >= kPackedMinRows || causal) && plan_packed(op, p, vw, per16, nvec_s)) {
+  } else if (op == RR_OP_SOFTMAX && !causal && M < kSplitMaxRows) {
+    plan_split(p, vw, per16, nvec_any);
   } else {
-    ok = plan_block(op, p, vw, nvec_s) || plan_packed(op, p, vw, per16, nvec_s);
+    ok = false;
   }
   if (ok) p->row_shift = 1;
   return ok;
@@ -286,7 +294,8 @@ rr_status make_plan(rr_op op, int64_t M, int64_t N, int din, int dout, int align
   const int64_t nvec = N / vec;
   // vectors a cut row spans: with aligned starts (lead 0) ceil(N / vw), with
   // starts at any offset up to ceil((N + vw - 1) / vw)
-  const int64_t nvec_s = align == 1 ? ceil_div(N, vw) : (N + 2 * (int64_t)vw - 2) / vw;
+  const int64_t nvec_any = (N + 2 * (int64_t)vw - 2) / vw;
+  const int64_t nvec_s = align == 1 ? ceil_div(N, vw) : nvec_any;
   const int per16_s = vecs_per_16_bytes(din, vw);
   const int forced = g_override.load(std::memory_order_relaxed);
 
@@ -294,7 +303,7 @@ rr_status make_plan(rr_op op, int64_t M, int64_t N, int din, int dout, int align
   switch (forced) {
     case RR_VARIANT_AUTO:
       if (plan_sub(p, vec, nvec)) {
-      } else if (shiftable && plan_shifted(op, p, vw, per16_s, nvec_s)) {
+      } else if (shiftable && plan_shifted(op, causal, M, p, vw, per16_s, nvec_s, nvec_any)) {
       } else if (vec == 1) {
         plan_loop(p, vec, nvec);
       } else if (wave_fits(op, vec, nvec)) {
@@ -333,6 +342,10 @@ rr_status make_plan(rr_op op, int64_t M, int64_t N, int din, int dout, int align
       if (ok) {
         plan_split(p, vec, per16, nvec);
         p->variant = forced;
+      } else if (forced == RR_VARIANT_SPLIT && shiftable && !causal) {
+        plan_split(p, vw, per16_s, nvec_any);   // the one-kernel form takes aligned rows only
+        p->row_shift = 1;
+        ok = true;
       }
       break;
     case RR_VARIANT_LOOP:
@@ -608,11 +621,16 @@ size_t rr_softmax_rows_ex_workspace_bytes(int64_t M, int64_t N, rr_dtype in_dtyp
                                           rr_dtype out_dtype, const rr_softmax_opts* opts) {
   rr_softmax_opts o;
   if (softmax_options(opts, "rr_softmax_rows_ex_workspace_bytes", &o) != RR_OK) return 0;
-  rr_plan p;
-  if (make_plan(o.causal ? RR_OP_SOFTMAX_CAUSAL : RR_OP_SOFTMAX, M, N, in_dtype, out_dtype, 1,
-                &p) != RR_OK)
-    return 0;
-  return p.workspace_bytes;
+  // the most any row alignment needs: aligned rows, or rows cut at aligned
+  // addresses (their split may take one more chunk per row)
+  const rr_op op = o.causal ? RR_OP_SOFTMAX_CAUSAL : RR_OP_SOFTMAX;
+  size_t most = 0;
+  for (int align = 1; align <= 2; ++align) {
+    rr_plan p;
+    if (make_plan(op, M, N, in_dtype, out_dtype, align, &p) != RR_OK) return 0;
+    if (p.workspace_bytes > most) most = p.workspace_bytes;
+  }
+  return most;
 }
 
 rr_status rr_softmax_rows(void* y, const void* x, int64_t M, int64_t N, rr_dtype in_dtype,

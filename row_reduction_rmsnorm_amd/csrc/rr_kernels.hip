@@ -1117,7 +1117,7 @@ struct SplitSlot {
 };
 static_assert(sizeof(SplitSlot) == 16, "slot layout");
 
-template <typename Tin, typename Tout, int NV>
+template <typename Tin, typename Tout, int NV, bool SHIFT>
 __global__ __launch_bounds__(256) void softmax_split_stats_kernel(const Tin* x, SplitSlot* ws,
                                                                   int64_t M, int N, int S, RowStrides ld) {
   constexpr int VEC = softmax_vec<Tin, Tout>();
@@ -1131,15 +1131,28 @@ __global__ __launch_bounds__(256) void softmax_split_stats_kernel(const Tin* x, 
   for (int64_t item = blockIdx.x; item < items; item += gridDim.x) {
     const int64_t row = item / S;
     const int c = (int)(item - row * S);
-    const int64_t ox = row * ld.x;
+    const Tin* xr = x + row * ld.x;
+    // SHIFT: vector j covers the row's elements [j * VEC - lead, ...)
+    const int lead = SHIFT ? row_lead(xr, VEC) : 0;
+    const int nvec_row = SHIFT ? (lead + N + VEC - 1) / VEC : nvec;
     Packed<Tin, VEC> v[NV];
 #pragma unroll
     for (int k = 0; k < NV; ++k) {
       const int vi = c * CV + k * kThreads + rl.t;
+      const int e0 = vi * VEC - lead;
       // streaming load (measured faster than a temporal one that would leave
       // the chunk in the last-level cache for pass B, with inputs cold in HBM)
-      if (vi < nvec) v[k].template load<true>(x + ox + (int64_t)vi * VEC);
-      else v[k].fill(kNegInf);
+      if (vi < nvec_row) {
+        if (!SHIFT || (e0 >= 0 && e0 + VEC <= N)) {
+          v[k].template load<true>(xr + e0);
+        } else {
+          float f[VEC];
+          load_edge<Tin, VEC>(xr, e0, N, f);
+          v[k].set(f);
+        }
+      } else {
+        v[k].fill(kNegInf);
+      }
     }
     float ml = kNegInf;
 #pragma unroll
@@ -1203,7 +1216,7 @@ constexpr int kSplitDirectMerge = kWave;
 // Pass B's chunks need not be pass A's: a row's summaries start at slot
 // row * SA, and SC of them are read (SA, or 1 after the merge kernel); the
 // row is cut into SB chunks of 256 * NV vectors here.
-template <typename Tin, typename Tout, int NV, bool LOG>
+template <typename Tin, typename Tout, int NV, bool LOG, bool SHIFT>
 __global__ __launch_bounds__(256) void softmax_split_apply_kernel(const Tin* x, Tout* y,
                                                                   const SplitSlot* __restrict__ ws,
                                                                   int64_t M, int N, int SA, int SC,
@@ -1217,13 +1230,26 @@ __global__ __launch_bounds__(256) void softmax_split_apply_kernel(const Tin* x, 
   for (int64_t item = blockIdx.x; item < items; item += gridDim.x) {
     const int64_t row = item / SB;
     const int c = (int)(item - row * SB);
-    const int64_t ox = row * ld.x, oy = row * ld.y;
+    const Tin* xr = x + row * ld.x;
+    Tout* yr = y + row * ld.y;
+    const int lead = SHIFT ? row_lead(xr, VEC) : 0;
+    const int nvec_row = SHIFT ? (lead + N + VEC - 1) / VEC : nvec;
     Packed<Tin, VEC> v[NV];
 #pragma unroll
     for (int k = 0; k < NV; ++k) {
       const int vi = c * CV + k * kThreads + rl.t;
-      if (vi < nvec) v[k].template load<true>(x + ox + (int64_t)vi * VEC);
-      else v[k].fill(kNegInf);
+      const int e0 = vi * VEC - lead;
+      if (vi < nvec_row) {
+        if (!SHIFT || (e0 >= 0 && e0 + VEC <= N)) {
+          v[k].template load<true>(xr + e0);
+        } else {
+          float f[VEC];
+          load_edge<Tin, VEC>(xr, e0, N, f);
+          v[k].set(f);
+        }
+      } else {
+        v[k].fill(kNegInf);
+      }
     }
     MD p;
     p.m = kNegInf;
@@ -1240,12 +1266,16 @@ __global__ __launch_bounds__(256) void softmax_split_apply_kernel(const Tin* x, 
 #pragma unroll
     for (int k = 0; k < NV; ++k) {
       const int vi = c * CV + k * kThreads + rl.t;
+      const int e0 = vi * VEC - lead;
       float o[VEC];
 #pragma unroll
       for (int i = 0; i < VEC; ++i)
         o[i] = LOG ? (v[k].get(i) - p.m) - ld : exp_shifted(v[k].get(i) - p.m) * inv_d;
       // plain (write-back) stores: measured faster than non-temporal ones here
-      if (vi < nvec) store_vec<Tout, VEC, false>(y + oy + (int64_t)vi * VEC, o);
+      if (vi < nvec_row) {
+        if (!SHIFT || (e0 >= 0 && e0 + VEC <= N)) store_vec<Tout, VEC, false>(yr + e0, o);
+        else store_edge<Tout, VEC>(yr, e0, N, o);
+      }
     }
   }
 }
@@ -1609,12 +1639,12 @@ uint64_t next_split_tag() {
 // kernels.  Both use the same chunks and the same merge order, so they give
 // the same bits.  Log-softmax always takes the two kernels.  The split
 // forms keep every key (the planner never splits a causal call).
-template <typename Tin, typename Tout, int NV, bool LOG>
+template <typename Tin, typename Tout, int NV, bool LOG, bool SHIFT>
 hipError_t softmax_split(const rr_plan& p, const SmCall<Tin, Tout>& c, SplitSlot* w, int S,
                          int64_t grid, hipStream_t s) {
   const dim3 b(p.block_threads);
   if (c.cp > 0) return hipErrorInvalidValue;
-  if constexpr (!LOG) {
+  if constexpr (!LOG && !SHIFT) {
     if (p.variant == RR_VARIANT_SPLIT_ONE_KERNEL) {
       const void* k = reinterpret_cast<const void*>(&softmax_split_fused_kernel<Tin, Tout, NV>);
       const int cap = cooperative_capacity(k);
@@ -1632,7 +1662,7 @@ hipError_t softmax_split(const rr_plan& p, const SmCall<Tin, Tout>& c, SplitSlot
       }
     }
   }
-  softmax_split_stats_kernel<Tin, Tout, NV><<<grid1(grid), b, 0, s>>>(c.x, w, c.M, c.N, S, c.ld);
+  softmax_split_stats_kernel<Tin, Tout, NV, SHIFT><<<grid1(grid), b, 0, s>>>(c.x, w, c.M, c.N, S, c.ld);
   int SC = S;
   if (S > kSplitDirectMerge) {
     int64_t gm = c.M < 65536 ? c.M : 65536;
@@ -1644,11 +1674,12 @@ hipError_t softmax_split(const rr_plan& p, const SmCall<Tin, Tout>& c, SplitSlot
   }
   // pass B in chunks of its own size
   constexpr int VEC = softmax_vec<Tin, Tout>();
-  const int nvec = c.N / VEC;
+  // vectors a row spans (SHIFT: up to one more, for a row starting inside one)
+  const int nvec = SHIFT ? (c.N + 2 * VEC - 2) / VEC : c.N / VEC;
   const int SB = (nvec + 256 * kSplitApplyNV - 1) / (256 * kSplitApplyNV);
   const int64_t items_b = c.M * (int64_t)SB;
   const int64_t grid_b = grid < c.M * (int64_t)S ? (grid < items_b ? grid : items_b) : items_b;
-  softmax_split_apply_kernel<Tin, Tout, kSplitApplyNV, LOG><<<grid1(grid_b), b, 0, s>>>(c.x, c.y, w, c.M, c.N, S,
+  softmax_split_apply_kernel<Tin, Tout, kSplitApplyNV, LOG, SHIFT><<<grid1(grid_b), b, 0, s>>>(c.x, c.y, w, c.M, c.N, S,
                                                                                        SC, SB, c.ld);
   return hipGetLastError();
 }
@@ -1689,10 +1720,18 @@ hipError_t softmax_typed(const rr_plan& p, const SmCall<Tin, Tout>& c, void* ws,
     if constexpr (CAUSAL) return hipErrorInvalidValue;   // the planner never splits a causal call
     SplitSlot* w = static_cast<SplitSlot*>(ws);
     const int S = (int)p.chunks_per_row;
+    if (p.row_shift) {
+      if (p.variant != RR_VARIANT_SPLIT) return hipErrorInvalidValue;   // the planner never asks
+      switch (p.vecs_per_lane) {
+        case 4: return softmax_split<Tin, Tout, 4, LOG, true>(p, c, w, S, grid, s);
+        case 8: return softmax_split<Tin, Tout, 8, LOG, true>(p, c, w, S, grid, s);
+        default: return hipErrorInvalidValue;
+      }
+    }
     switch (p.vecs_per_lane) {
-      case 2: return softmax_split<Tin, Tout, 2, LOG>(p, c, w, S, grid, s);
-      case 4: return softmax_split<Tin, Tout, 4, LOG>(p, c, w, S, grid, s);
-      case 8: return softmax_split<Tin, Tout, 8, LOG>(p, c, w, S, grid, s);
+      case 2: return softmax_split<Tin, Tout, 2, LOG, false>(p, c, w, S, grid, s);
+      case 4: return softmax_split<Tin, Tout, 4, LOG, false>(p, c, w, S, grid, s);
+      case 8: return softmax_split<Tin, Tout, 8, LOG, false>(p, c, w, S, grid, s);
       default: return hipErrorInvalidValue;
     }
   }

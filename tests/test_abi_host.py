@@ -322,15 +322,32 @@ def test_dispatch_boundaries():
     # starts at a common offset, room for a lead of up to vec - 1 elements)
     for M, N, a, b, name, nv1, nv2 in ((10, 33, F, F, "wave", 1, 1), (10, 1023, F, F, "wave", 4, 8),
                                        (16384, 1025, F, F, "wave", 8, 8), (8192, 4097, F, F, "block", 2, 2),
-                                       (256, 50257, B, F, "block", 24, 24), (3, 50257, B, B, "block", 12, 12),
-                                       (2, 50257, F, B, "block", 16, 16)):
+                                       (256, 50257, B, F, "block", 24, 24), (64, 50257, B, B, "block", 12, 12),
+                                       (64, 50257, F, B, "block", 16, 16)):
         for al, nv in ((True, nv1), (2, nv2)):
             p = sh(M, N, a, b, al)
             assert (p["variant_name"], p["vecs_per_lane"], p["row_shift"]) == (name, nv, 1), (M, N, al, p)
             assert p["vec_elems"] == (4 if (a, b) != (B, B) else 8) and p["workspace_bytes"] == 0, p
     assert sh(64, 4097, op=rr.RR_OP_SOFTMAX_CAUSAL)["row_shift"] == 1
-    # too long to hold, or element access requested: the scalar streaming path
-    assert sh(4, 152065)["variant_name"] == "loop" and sh(4, 152065)["vec_elems"] == 1
+    # beyond a workgroup's registers with fewer than 64 rows, or beyond the
+    # packed workgroup below 1024 rows: the split, its chunks sized for a row
+    # at any offset (so that the workspace query, which sees no addresses,
+    # covers every call); a causal call never splits
+    for M, N, a, b, vec, nv, chunks in ((3, 50257, B, B, 8, 4, 7), (2, 50257, F, B, 4, 4, 13),
+                                        (1, 50257, B, F, 4, 8, 7), (4, 152065, F, F, 4, 4, 38),
+                                        (1023, 81925, F, F, 4, 4, 21), (4, 65536, F, F, 4, 4, 17)):
+        for al in (True, 2):
+            if al is True and N % vec == 0:
+                continue
+            p = sh(M, N, a, b, al)
+            assert (p["variant_name"], p["row_shift"], p["vec_elems"], p["vecs_per_lane"]) == ("split", 1, vec, nv), p
+            assert p["chunks_per_row"] == chunks and p["workspace_bytes"] == M * chunks * 16, p
+            assert rr.rr_softmax_rows_workspace_bytes(M, N, a, b) == M * chunks * 16
+    assert rr.rr_query_plan(S, 4, 65536, F, F)["chunks_per_row"] == 16   # aligned rows: one chunk fewer
+    assert sh(4, 50257, op=rr.RR_OP_SOFTMAX_CAUSAL)["variant_name"] == "block"
+    # too long to hold with 1024 rows or more, or element access requested:
+    # the scalar streaming path
+    assert sh(1024, 81925)["variant_name"] == "loop" and sh(1024, 81925)["vec_elems"] == 1
     assert v(S, 10, 1024, al=False) == "loop" and sh(10, 1024, al=False)["row_shift"] == 0
     # the norms' gamma lies in a frame of its own: unaligned norm rows stream
     assert v(rr.RR_OP_RMSNORM, 10, 4100, B, B) == "loop"   # 4100 % 8 != 0
@@ -346,9 +363,13 @@ def test_forced_variants():
         p = rr.rr_query_plan(S, 10, 1024, F, F)
         assert p["variant_name"] == "split" and p["workspace_bytes"] == 10 * 1 * 16
         assert rr.rr_softmax_rows_workspace_bytes(10, 1024, F, F) == 160
+        p = rr.rr_query_plan(S, 10, 1023, F, F, 2)      # a row cut at aligned addresses
+        assert (p["variant_name"], p["row_shift"], p["vec_elems"]) == ("split", 1, 4)
         rr.rr_set_variant_override(rr.RR_VARIANT_SPLIT_ONE_KERNEL)
         p = rr.rr_query_plan(S, 10, 5000, F, F)
         assert p["variant_name"] == "split1" and p["chunks_per_row"] == 2
+        with pytest.raises(rr.RowReduceError):
+            rr.rr_query_plan(S, 10, 5001, F, F)               # the one-kernel form takes aligned rows
         with pytest.raises(rr.RowReduceError):
             rr.rr_query_plan(rr.RR_OP_RMSNORM, 10, 1024, F, F)   # no split RMSNorm
         rr.rr_set_variant_override(rr.RR_VARIANT_WAVE)
@@ -403,9 +424,13 @@ def test_every_plan_covers_its_row():
                     # wavefront or workgroup, room for the worst lead (vec - 1)
                     assert op in (rr.RR_OP_SOFTMAX, rr.RR_OP_SOFTMAX_CAUSAL) and vec == width, p
                     assert aligned == 2 or (aligned == 1 and N % width != 0), p
-                    assert name in ("wave", "block"), p
-                    cap = (64 if name == "wave" else p["block_threads"]) * nv * vec
-                    assert cap >= (N if aligned == 1 else N + vec - 1), p
+                    assert name in ("wave", "block", "split"), p
+                    if name == "split":
+                        cap = p["chunks_per_row"] * 256 * nv * vec
+                        assert cap >= N + vec - 1, p          # any lead, also with aligned starts
+                    else:
+                        cap = (64 if name == "wave" else p["block_threads"]) * nv * vec
+                        assert cap >= (N if aligned == 1 else N + vec - 1), p
                 else:
                     assert vec in (1, width) and (vec == 1 or (aligned == 1 and N % width == 0)), p
                 assert 1 <= p["block_threads"] <= 1024 and p["block_threads"] % 64 == 0, p
@@ -417,6 +442,8 @@ def test_every_plan_covers_its_row():
                     assert p["block_threads"] * nv * vec >= N and p["rows_per_group"] == 1, p
                 elif name in ("split", "split1"):
                     assert op == rr.RR_OP_SOFTMAX and vec > 1, p
+                    if v == rr.RR_VARIANT_AUTO:
+                        assert rr.rr_softmax_rows_workspace_bytes(M, N, din, dout) >= p["workspace_bytes"], p
                     assert p["chunks_per_row"] * 256 * nv * vec >= N, p
                     assert p["workspace_bytes"] == M * p["chunks_per_row"] * 16, p
                     assert p["work_items"] == M * p["chunks_per_row"], p

@@ -681,11 +681,65 @@ def test_softmax_rows_cut_at_aligned_addresses(din, dout, N):
     X = torch.full((M, ld), float("nan"), dtype=_tdt(din), device="cuda")
     X[:, c0:c0 + N] = x.cuda()
     Y = torch.full((M, ld), 7.0, dtype=_tdt(dout), device="cuda")
-    rr.rr_softmax_rows_strided(Y[:, c0:c0 + N], X[:, c0:c0 + N])
+    nb = rr.rr_softmax_rows_workspace_bytes(M, N, code[din], code[dout])
+    ws = torch.empty(nb, dtype=torch.uint8, device="cuda") if nb else None
+    rr.rr_softmax_rows_strided(Y[:, c0:c0 + N], X[:, c0:c0 + N], None, ws)
     torch.cuda.synchronize()
     Yc = Y.cpu()
     check_softmax(x, Yc[:, c0:c0 + N].contiguous(), f"cut column slice {din}->{dout} N={N}")
     assert bool((Yc[:, :c0] == 7.0).all()) and bool((Yc[:, c0 + N:] == 7.0).all()), "columns outside the slice changed"
+
+
+# (M, N, in dtype, out dtype, log output): few rows too long for one
+# workgroup's registers, so the row is split over workgroups with its chunks
+# cut at aligned addresses; the last case has more than 64 chunks per row
+# (the merge kernel runs)
+SPLIT_CUT_CASES = [
+    (1, 50257, "bf16", "f32", False), (4, 50257, "bf16", "f32", True), (63, 50257, "f32", "f32", False),
+    (2, 152065, "bf16", "bf16", False), (5, 152065, "f32", "bf16", True), (7, 32769, "f32", "f32", False),
+    (100, 163841, "bf16", "f32", False), (3, (1 << 19) + 3, "f32", "f32", False),
+]
+
+
+@pytest.mark.parametrize("M,N,din,dout,log", SPLIT_CUT_CASES)
+def test_softmax_split_rows_cut_at_aligned_addresses(M, N, din, dout, log):
+    """The split with rows cut at aligned addresses: contiguous rows of an odd
+    width (each row at its own offset within a vector) and the same rows as a
+    column slice at an odd column, against the oracle; the slice's
+    neighbouring columns must stay untouched."""
+    rr = _rr()
+    code = {"f32": rr.RR_F32, "bf16": rr.RR_BF16}
+    opts = rr.make_softmax_opts(log_output=log)
+    x = softmax_input(M, N, seed=N + 7 * M, dt=din)
+    xf = compare.to_f64(x)
+    ref = oracle.log_softmax(xf) if log else oracle.softmax(xf)
+    nb = rr.rr_softmax_rows_ex_workspace_bytes(M, N, code[din], code[dout], opts)
+    ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
+    for al, c0 in ((True, None), (2, 3)):
+        plan = rr.rr_query_plan(rr.RR_OP_SOFTMAX, M, N, code[din], code[dout], al)
+        _say(f"split cut rows {din}->{dout} {M}x{N} log={log} slice={c0} chunks={plan['chunks_per_row']}")
+        assert (plan["variant_name"], plan["row_shift"]) == ("split", 1), plan
+        assert nb >= plan["workspace_bytes"]
+        if c0 is None:
+            xs = x.cuda()
+            Y = ys = torch.empty((M, N), dtype=_tdt(dout), device="cuda")
+        else:
+            ld = N + 6
+            X = torch.full((M, ld), float("nan"), dtype=_tdt(din), device="cuda")
+            X[:, c0:c0 + N] = x.cuda()
+            Y = torch.full((M, ld), 7.0, dtype=_tdt(dout), device="cuda")
+            xs, ys = X[:, c0:c0 + N], Y[:, c0:c0 + N]
+        rr.rr_softmax_rows_strided(ys, xs, opts, ws)
+        torch.cuda.synchronize()
+        got = ys.cpu().contiguous()
+        what = f"split cut rows {din}->{dout} {M}x{N} log={log} slice={c0}"
+        if log:
+            compare.check_log_softmax(got, xf, ref, what)
+        else:
+            compare.check_softmax(got, xf, ref, what)
+        if c0 is not None:
+            Yc = Y.cpu()
+            assert bool((Yc[:, :c0] == 7.0).all()) and bool((Yc[:, c0 + N:] == 7.0).all()), what
 
 def test_softmax_in_place_unaligned_and_tiny():
     rr = _rr()

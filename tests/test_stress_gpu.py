@@ -148,6 +148,8 @@ SOFTMAX_CASES = [
     (F32, F32, 4, 152064, "split", 0),
     (BF16, F32, 4, 152064, "split", 1),
     (F32, F32, 40, 1 << 19, "split", 0),    # more than 64 chunks: the merge kernel runs
+    (BF16, F32, 4, 50257, "split", 1),      # split rows cut at aligned addresses
+    (F32, F32, 40, (1 << 19) + 3, "split", 0),
 ]
 
 
