@@ -167,14 +167,22 @@ bool plan_block(rr_op op, rr_plan* p, int vec, int64_t nvec) {
 
 // Softmax rows beyond that, up to 20 16-byte vectors (40 of 8 bytes) per lane
 // of a 1024-lane workgroup, held in their storage format (one workgroup per
-// CU).  From kPackedMinRows rows up this beats both the two-kernel split and
-// the streaming path for every dtype pair (cold, e.g. 256 x 152064 bf16 ->
-// fp32: 46.0 us packed, 65.4 split, 78.6 streaming; 256 x 65536 fp32: 28.1,
-// 41.5, 39.8); below it the split spreads a few rows over more CUs (48 rows:
-// 21.1 split, 22.6 packed).  A causal call cannot split, and packed beats
-// streaming at any row count, so it takes this path whenever the row fits.
+// CU).  From packed_min_rows() rows up this beats both the two-kernel split
+// and the streaming path (cold, e.g. 256 x 152064 bf16 -> fp32: 46.0 us
+// packed, 65.4 split, 78.6 streaming; 256 x 65536 fp32: 28.1, 41.5, 39.8);
+// below it the split spreads a few rows over more CUs.  A causal call cannot
+// split, and packed beats streaming at any row count, so it takes this path
+// whenever the row fits.
 constexpr int kPackedNV[] = {12, 16, 19, 20};
-constexpr int64_t kPackedMinRows = 64;
+// Where the packed workgroup overtakes the split, by dtype pair: a packed
+// workgroup's time is about one row's, so the cheaper a row is for one CU
+// (bf16 in and out) the more rows the split needs to lose.  Measured cold on
+// rows 50256 to 152064 wide (fp32 in: 36-48 rows; bf16 -> fp32: 56-68;
+// bf16 -> bf16: 72-85).
+int64_t packed_min_rows(int din, int dout) {
+  if (din == RR_F32) return 40;
+  return dout == RR_F32 ? 56 : 80;
+}
 bool plan_packed(rr_op op, rr_plan* p, int vec, int per16, int64_t nvec) {
   if (op != RR_OP_SOFTMAX) return false;
   for (int nv16 : kPackedNV) {
@@ -240,18 +248,18 @@ void plan_loop(rr_plan* p, int vec, int64_t nvec) {
 // Softmax rows cut into vectors at aligned addresses (row_shift): the row
 // starts at element `lead` of its first vector, so it spans up to nvec_s
 // vectors (see make_plan).  The same choice as for aligned rows: a
-// wavefront, a workgroup, the packed workgroup from kPackedMinRows rows (or
+// wavefront, a workgroup, the packed workgroup from packed_min_rows() rows (or
 // for a causal call), else the split below kSplitMaxRows rows; longer rows
 // stream (scalar).  The split sizes its chunks for a row at any offset
 // (nvec_any) so that the workspace query, which sees no addresses, covers
 // every call.
-bool plan_shifted(rr_op op, bool causal, int64_t M, rr_plan* p, int vw, int per16, int64_t nvec_s,
-                  int64_t nvec_any) {
+bool plan_shifted(rr_op op, bool causal, int64_t M, int64_t packed_rows, rr_plan* p, int vw, int per16,
+                  int64_t nvec_s, int64_t nvec_any) {
   bool ok = true;
   if (wave_fits(op, vw, nvec_s)) {
     plan_wave(p, vw, nvec_s);
   } else if (plan_block(op, p, vw, nvec_s)) {
-  } else if ((M >= kPackedMinRows || causal) && plan_packed(op, p, vw, per16, nvec_s)) {
+  } else if ((M >= packed_rows || causal) && plan_packed(op, p, vw, per16, nvec_s)) {
   } else if (op == RR_OP_SOFTMAX && !causal && M < kSplitMaxRows) {
     plan_split(p, vw, per16, nvec_any);
   } else {
@@ -298,19 +306,20 @@ rr_status make_plan(rr_op op, int64_t M, int64_t N, int din, int dout, int align
   const int64_t nvec_s = align == 1 ? ceil_div(N, vw) : nvec_any;
   const int per16_s = vecs_per_16_bytes(din, vw);
   const int forced = g_override.load(std::memory_order_relaxed);
+  const int64_t packed_rows = packed_min_rows(din, dout);
 
   bool ok = false;
   switch (forced) {
     case RR_VARIANT_AUTO:
       if (plan_sub(p, vec, nvec)) {
-      } else if (shiftable && plan_shifted(op, causal, M, p, vw, per16_s, nvec_s, nvec_any)) {
+      } else if (shiftable && plan_shifted(op, causal, M, packed_rows, p, vw, per16_s, nvec_s, nvec_any)) {
       } else if (vec == 1) {
         plan_loop(p, vec, nvec);
       } else if (wave_fits(op, vec, nvec)) {
         plan_wave(p, vec, nvec);
       } else if (plan_block(op, p, vec, nvec)) {
       } else if (plan_norm_packed(op, p, vec, nvec)) {
-      } else if ((M >= kPackedMinRows || causal) && plan_packed(op, p, vec, per16, nvec)) {
+      } else if ((M >= packed_rows || causal) && plan_packed(op, p, vec, per16, nvec)) {
       } else if (op == RR_OP_SOFTMAX && !causal && M < kSplitMaxRows) {
         plan_split(p, vec, per16, nvec);
       } else {
@@ -621,14 +630,15 @@ size_t rr_softmax_rows_ex_workspace_bytes(int64_t M, int64_t N, rr_dtype in_dtyp
                                           rr_dtype out_dtype, const rr_softmax_opts* opts) {
   rr_softmax_opts o;
   if (softmax_options(opts, "rr_softmax_rows_ex_workspace_bytes", &o) != RR_OK) return 0;
-  // the most any row alignment needs: aligned rows, or rows cut at aligned
-  // addresses (their split may take one more chunk per row)
+  // the most any call that can run needs: aligned rows, or rows cut at
+  // aligned addresses (their split may take one more chunk per row; a forced
+  // variant may refuse them)
   const rr_op op = o.causal ? RR_OP_SOFTMAX_CAUSAL : RR_OP_SOFTMAX;
   size_t most = 0;
   for (int align = 1; align <= 2; ++align) {
     rr_plan p;
-    if (make_plan(op, M, N, in_dtype, out_dtype, align, &p) != RR_OK) return 0;
-    if (p.workspace_bytes > most) most = p.workspace_bytes;
+    if (make_plan(op, M, N, in_dtype, out_dtype, align, &p) == RR_OK && p.workspace_bytes > most)
+      most = p.workspace_bytes;
   }
   return most;
 }

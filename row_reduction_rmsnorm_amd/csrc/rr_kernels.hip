@@ -876,16 +876,45 @@ __global__ __launch_bounds__(1024) void softmax_regs_kernel(const Tin* x, Tout* 
     const int nvec_row = SHIFT ? (lead + N + VEC - 1) / VEC : nvec;
     const int nvec_keys = (lead + keys + VEC - 1) / VEC;   // vectors holding kept keys
     float v[NV][VEC];
+    if constexpr (std::is_same_v<Tin, float>) {
 #pragma unroll
-    for (int k = 0; k < NV; ++k) {
-      const int vi = k * rl.T + rl.t;
-      const int e0 = vi * VEC - lead;
-      if (vi < nvec_keys) {
-        if (!SHIFT || (e0 >= 0 && e0 + VEC <= N)) load_vec<Tin, VEC>(xr + e0, v[k]);
-        else load_edge<Tin, VEC>(xr, e0, keys, v[k]);
-      } else {
+      for (int k = 0; k < NV; ++k) {
+        const int vi = k * rl.T + rl.t;
+        const int e0 = vi * VEC - lead;
+        if (vi < nvec_keys) {
+          if (!SHIFT || (e0 >= 0 && e0 + VEC <= N)) load_vec<Tin, VEC>(xr + e0, v[k]);
+          else load_edge<Tin, VEC>(xr, e0, keys, v[k]);
+        } else {
 #pragma unroll
-        for (int i = 0; i < VEC; ++i) v[k][i] = kNegInf;
+          for (int i = 0; i < VEC; ++i) v[k][i] = kNegInf;
+        }
+      }
+    } else {
+      // bf16: load the packed words and widen them only once every load is
+      // issued.  Widened inside each load's branch, every branch would wait
+      // for its own load: one HBM round trip per vector instead of one in all.
+      Packed<Tin, VEC> raw[NV];
+#pragma unroll
+      for (int k = 0; k < NV; ++k) {
+        const int vi = k * rl.T + rl.t;
+        const int e0 = vi * VEC - lead;
+        if (vi < nvec_keys && (!SHIFT || (e0 >= 0 && e0 + VEC <= N))) raw[k].template load<true>(xr + e0);
+        else raw[k].fill(kNegInf);
+      }
+#pragma unroll
+      for (int k = 0; k < NV; ++k) raw[k].touch();
+#pragma unroll
+      for (int k = 0; k < NV; ++k)
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) v[k][i] = raw[k].get(i);
+      if constexpr (SHIFT) {
+        // the row's first and last vector, element by element, after the rest
+#pragma unroll
+        for (int k = 0; k < NV; ++k) {
+          const int vi = k * rl.T + rl.t;
+          const int e0 = vi * VEC - lead;
+          if (vi < nvec_keys && !(e0 >= 0 && e0 + VEC <= N)) load_edge<Tin, VEC>(xr, e0, keys, v[k]);
+        }
       }
     }
     // a row the causal rule cuts: keys past the count inside the vector

@@ -122,8 +122,8 @@ def test_softmax_validation():
     assert f(Y, X, 4, 8, 3, rr.RR_F32, None, 0, None) == rr.RR_ERR_INVALID_ARG
     # in place with different dtypes
     assert f(X, X, 4, 8, rr.RR_BF16, rr.RR_F32, None, 0, None) == rr.RR_ERR_INVALID_ARG
-    # long rows with few rows need the split workspace (from 64 rows up the
-    # row is held by one workgroup and needs none)
+    # long rows with few rows need the split workspace (from 56 rows up a
+    # bf16 -> fp32 row is held by one workgroup and needs none)
     assert rr.rr_softmax_rows_workspace_bytes(256, 152064, rr.RR_BF16, rr.RR_F32) == 0
     need = rr.rr_softmax_rows_workspace_bytes(40, 152064, rr.RR_BF16, rr.RR_F32)
     assert need == 40 * 19 * 16
@@ -184,9 +184,9 @@ def test_softmax_causal_plans():
     p = q(C, 40, 200000, B, F)
     assert p["variant_name"] == "loop" and p["workspace_bytes"] == 0
     assert q(S, 40, 200000, B, F)["variant_name"] == "split"
-    # from 64 rows up softmax also holds such rows in one workgroup
-    assert q(S, 64, 152064, B, F) == q(C, 64, 152064, B, F)
-    assert q(S, 64, 152064, B, F)["variant_name"] == "block" and q(S, 63, 152064, B, F)["variant_name"] == "split"
+    # from 56 rows up (bf16 -> fp32) softmax also holds such rows in one workgroup
+    assert q(S, 56, 152064, B, F) == q(C, 56, 152064, B, F)
+    assert q(S, 56, 152064, B, F)["variant_name"] == "block" and q(S, 55, 152064, B, F)["variant_name"] == "split"
     try:
         rr.rr_set_variant_override(rr.RR_VARIANT_SPLIT)
         with pytest.raises(rr.RowReduceError):
@@ -251,7 +251,7 @@ WORKLOAD_PLANS = [
     ((rr.RR_OP_SOFTMAX, 16384, 1024, rr.RR_F32, rr.RR_F32), ("wave", 1, 4, 4, 1)),
     # bf16 read 4 elements (8 bytes) at a time when written as fp32
     ((rr.RR_OP_SOFTMAX, 256, 152064, rr.RR_BF16, rr.RR_F32), ("block", 16, 38, 4, 1)),
-    ((rr.RR_OP_SOFTMAX, 63, 152064, rr.RR_BF16, rr.RR_F32), ("split", 4, 8, 4, 19)),
+    ((rr.RR_OP_SOFTMAX, 55, 152064, rr.RR_BF16, rr.RR_F32), ("split", 4, 8, 4, 19)),
     ((rr.RR_OP_SOFTMAX, 4096, 32000, rr.RR_BF16, rr.RR_F32), ("block", 16, 8, 4, 1)),
     ((rr.RR_OP_SOFTMAX, 4096, 32000, rr.RR_BF16, rr.RR_BF16), ("block", 16, 4, 8, 1)),
     ((rr.RR_OP_SOFTMAX, 2048, 131072, rr.RR_BF16, rr.RR_F32), ("block", 16, 32, 4, 1)),
@@ -291,11 +291,15 @@ def test_dispatch_boundaries():
     assert q(rr.RR_OP_RMSNORM, 20480, B)["vecs_per_lane"] == 4
     assert q(rr.RR_OP_RMSNORM, 65544, B)["variant_name"] == "loop"
     assert v(S, 100, 32768) == "block"
-    # longer softmax rows: split when rows are few (below 64); from 64 rows up
-    # the row is held packed (1024 lanes x up to 20 16-byte vectors); rows
-    # longer than that split below 1024 rows and stream from 1024 rows up
-    assert v(S, 63, 32772) == "split"
-    assert v(S, 64, 32772) == "block"
+    # longer softmax rows: split when rows are few; from 40 (fp32 in), 56
+    # (bf16 -> fp32) or 80 (bf16 -> bf16) rows up the row is held packed (1024
+    # lanes x up to 20 16-byte vectors); rows longer than that split below
+    # 1024 rows and stream from 1024 rows up
+    assert v(S, 39, 32772) == "split"
+    assert v(S, 40, 32772) == "block"
+    assert v(S, 39, 32772, F, B) == "split" and v(S, 40, 32772, F, B) == "block"
+    assert v(S, 55, 65536, B, F) == "split" and v(S, 56, 65536, B, F) == "block"
+    assert v(S, 79, 65536, B, B) == "split" and v(S, 80, 65536, B, B) == "block"
     assert rr.rr_query_plan(S, 64, 32772, F, F)["vecs_per_lane"] == 12
     assert v(S, 64, 81920) == "block"
     assert v(S, 64, 81924) == "split"
@@ -322,8 +326,8 @@ def test_dispatch_boundaries():
     # starts at a common offset, room for a lead of up to vec - 1 elements)
     for M, N, a, b, name, nv1, nv2 in ((10, 33, F, F, "wave", 1, 1), (10, 1023, F, F, "wave", 4, 8),
                                        (16384, 1025, F, F, "wave", 8, 8), (8192, 4097, F, F, "block", 2, 2),
-                                       (256, 50257, B, F, "block", 24, 24), (64, 50257, B, B, "block", 12, 12),
-                                       (64, 50257, F, B, "block", 16, 16)):
+                                       (256, 50257, B, F, "block", 24, 24), (80, 50257, B, B, "block", 12, 12),
+                                       (40, 50257, F, B, "block", 16, 16)):
         for al, nv in ((True, nv1), (2, nv2)):
             p = sh(M, N, a, b, al)
             assert (p["variant_name"], p["vecs_per_lane"], p["row_shift"]) == (name, nv, 1), (M, N, al, p)
@@ -368,6 +372,9 @@ def test_forced_variants():
         rr.rr_set_variant_override(rr.RR_VARIANT_SPLIT_ONE_KERNEL)
         p = rr.rr_query_plan(S, 10, 5000, F, F)
         assert p["variant_name"] == "split1" and p["chunks_per_row"] == 2
+        # the workspace query covers the aligned call even though cut rows are refused
+        assert rr.rr_softmax_rows_workspace_bytes(10, 5000, F, F) == 10 * 2 * 16
+        assert rr.rr_softmax_rows_workspace_bytes(1, 8, F, F) == 16
         with pytest.raises(rr.RowReduceError):
             rr.rr_query_plan(S, 10, 5001, F, F)               # the one-kernel form takes aligned rows
         with pytest.raises(rr.RowReduceError):

@@ -695,7 +695,7 @@ def test_softmax_rows_cut_at_aligned_addresses(din, dout, N):
 # cut at aligned addresses; the last case has more than 64 chunks per row
 # (the merge kernel runs)
 SPLIT_CUT_CASES = [
-    (1, 50257, "bf16", "f32", False), (4, 50257, "bf16", "f32", True), (63, 50257, "f32", "f32", False),
+    (1, 50257, "bf16", "f32", False), (4, 50257, "bf16", "f32", True), (39, 50257, "f32", "f32", False),
     (2, 152065, "bf16", "bf16", False), (5, 152065, "f32", "bf16", True), (7, 32769, "f32", "f32", False),
     (100, 163841, "bf16", "f32", False), (3, (1 << 19) + 3, "f32", "f32", False),
 ]
