@@ -290,6 +290,31 @@ __device__ __forceinline__ RowLane row_lane() {
 
 }  // namespace
 
+// A row's vectors k * T + t (k < NV) are loaded in two steps: issue_row
+// starts every load (packed words, 0 past the row's nvec vectors), and
+// widen_row waits for them and widens to fp32.  Work that needs other loads
+// (gamma's) goes between the two, and nothing is widened inside a load's
+// bounds branch, where it would wait for that one load: every wait comes
+// after all of the row's loads are in flight (one HBM round trip per row).
+template <typename T, int VEC, int NV>
+__device__ __forceinline__ void issue_row(const T* row, int nvec, int T_, int t, Packed<T, VEC> (&p)[NV]) {
+#pragma unroll
+  for (int k = 0; k < NV; ++k) {
+    const int vi = k * T_ + t;
+    if (vi < nvec) p[k].template load<true>(row + (int64_t)vi * VEC);
+    else p[k].zero();
+  }
+}
+template <typename T, int VEC, int NV>
+__device__ __forceinline__ void widen_row(Packed<T, VEC> (&p)[NV], float (&h)[NV][VEC]) {
+#pragma unroll
+  for (int k = 0; k < NV; ++k) p[k].touch();
+#pragma unroll
+  for (int k = 0; k < NV; ++k)
+#pragma unroll
+    for (int i = 0; i < VEC; ++i) h[k][i] = p[k].get(i);
+}
+
 // ===========================================================================
 // RMSNorm / fused add + RMSNorm, row held in registers (WAVE and BLOCK)
 //
@@ -339,19 +364,34 @@ __global__ __launch_bounds__(1024) void norm_regs_kernel(T* y, T* residual, cons
   for (int64_t row = (int64_t)blockIdx.x * rl.rpg + rl.g; row < M; row += stride) {
     const int64_t ox = row * ld.x, oy = row * ld.y, orr = row * ld.r;
     float h[NV][VEC];
+    // gamma (and beta) were loaded before the loop; marking their words here,
+    // after this row's loads are issued, keeps their wait (and widening)
+    // behind those loads instead of before the first row's
+    auto params_after_loads = [&]() {
+#pragma unroll
+      for (int k = 0; k < NV; ++k) gv[k].touch();
+      if constexpr (KIND == kNormLayer) {
+#pragma unroll
+        for (int k = 0; k < NV; ++k) bv[k].touch();
+      }
+    };
     if constexpr (KIND == kNormFused) {
       float r[NV][VEC];
+      Packed<T, VEC> px[NV], pr[NV];
 #pragma unroll
       for (int k = 0; k < NV; ++k) {
         const int vi = k * rl.T + rl.t;
         if (vi < nvec) {
-          load_vec<T, VEC>(x + ox + (int64_t)vi * VEC, h[k]);
-          load_vec<T, VEC>(residual + orr + (int64_t)vi * VEC, r[k]);
+          px[k].template load<true>(x + ox + (int64_t)vi * VEC);
+          pr[k].template load<true>(residual + orr + (int64_t)vi * VEC);
         } else {
-#pragma unroll
-          for (int i = 0; i < VEC; ++i) h[k][i] = r[k][i] = 0.0f;
+          px[k].zero();
+          pr[k].zero();
         }
       }
+      params_after_loads();
+      widen_row<T, VEC, NV>(px, h);
+      widen_row<T, VEC, NV>(pr, r);
 #pragma unroll
       for (int k = 0; k < NV; ++k) {
 #pragma unroll
@@ -360,16 +400,10 @@ __global__ __launch_bounds__(1024) void norm_regs_kernel(T* y, T* residual, cons
         if (vi < nvec) store_vec<T, VEC>(residual + orr + (int64_t)vi * VEC, h[k]);
       }
     } else {
-#pragma unroll
-      for (int k = 0; k < NV; ++k) {
-        const int vi = k * rl.T + rl.t;
-        if (vi < nvec) {
-          load_vec<T, VEC>(x + ox + (int64_t)vi * VEC, h[k]);
-        } else {
-#pragma unroll
-          for (int i = 0; i < VEC; ++i) h[k][i] = 0.0f;
-        }
-      }
+      Packed<T, VEC> px[NV];
+      issue_row<T, VEC, NV>(x + ox, nvec, rl.T, rl.t, px);
+      params_after_loads();
+      widen_row<T, VEC, NV>(px, h);
     }
 
     if constexpr (KIND == kNormLayer) {
@@ -728,19 +762,27 @@ __global__ __launch_bounds__(256) void norm_sub_kernel(T* y, T* residual, const 
        row += (int64_t)gridDim.x * kRowsPerGroup) {
     const int64_t cj = (int64_t)j * VEC;
     const int64_t ox = row * ld.x + cj, oy = row * ld.y + cj, orr = row * ld.r + cj;
-    float h[VEC];
+    // the row's loads first, then gamma's words (loaded before the loop), then
+    // the widening: every wait comes after the row's loads are in flight
+    Packed<T, VEC> px, pr;
     if (active) {
-      load_vec<T, VEC>(x + ox, h);
-      if constexpr (KIND == kNormFused) {
-        float r[VEC];
-        load_vec<T, VEC>(residual + orr, r);
-#pragma unroll
-        for (int i = 0; i < VEC; ++i) h[i] = round_to<T>(h[i] + r[i]);
-        store_vec<T, VEC>(residual + orr, h);
-      }
+      px.template load<true>(x + ox);
+      if constexpr (KIND == kNormFused) pr.template load<true>(residual + orr);
     } else {
+      px.zero();
+      pr.zero();
+    }
+    g.touch();
+    if constexpr (KIND == kNormLayer) bb.touch();
+    px.touch();
+    float h[VEC];
 #pragma unroll
-      for (int i = 0; i < VEC; ++i) h[i] = 0.0f;
+    for (int i = 0; i < VEC; ++i) h[i] = px.get(i);
+    if constexpr (KIND == kNormFused) {
+      pr.touch();
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) h[i] = round_to<T>(h[i] + pr.get(i));
+      if (active) store_vec<T, VEC>(residual + orr, h);
     }
     float o[VEC];
     if constexpr (KIND == kNormLayer) {
@@ -881,12 +923,22 @@ __global__ __launch_bounds__(1024) void softmax_regs_kernel(const Tin* x, Tout* 
       for (int k = 0; k < NV; ++k) {
         const int vi = k * rl.T + rl.t;
         const int e0 = vi * VEC - lead;
-        if (vi < nvec_keys) {
-          if (!SHIFT || (e0 >= 0 && e0 + VEC <= N)) load_vec<Tin, VEC>(xr + e0, v[k]);
-          else load_edge<Tin, VEC>(xr, e0, keys, v[k]);
+        if (vi < nvec_keys && (!SHIFT || (e0 >= 0 && e0 + VEC <= N))) {
+          load_vec<Tin, VEC>(xr + e0, v[k]);
         } else {
 #pragma unroll
           for (int i = 0; i < VEC; ++i) v[k][i] = kNegInf;
+        }
+      }
+      if constexpr (SHIFT) {
+        // the row's first and last vector, element by element, once every
+        // whole vector's load is issued (their loads reuse those registers,
+        // so an edge vector read in between would wait for the loads before it)
+#pragma unroll
+        for (int k = 0; k < NV; ++k) {
+          const int vi = k * rl.T + rl.t;
+          const int e0 = vi * VEC - lead;
+          if (vi < nvec_keys && !(e0 >= 0 && e0 + VEC <= N)) load_edge<Tin, VEC>(xr, e0, keys, v[k]);
         }
       }
     } else {
@@ -1171,16 +1223,20 @@ __global__ __launch_bounds__(256) void softmax_split_stats_kernel(const Tin* x, 
       const int e0 = vi * VEC - lead;
       // streaming load (measured faster than a temporal one that would leave
       // the chunk in the last-level cache for pass B, with inputs cold in HBM)
-      if (vi < nvec_row) {
-        if (!SHIFT || (e0 >= 0 && e0 + VEC <= N)) {
-          v[k].template load<true>(xr + e0);
-        } else {
+      if (vi < nvec_row && (!SHIFT || (e0 >= 0 && e0 + VEC <= N))) v[k].template load<true>(xr + e0);
+      else v[k].fill(kNegInf);
+    }
+    if constexpr (SHIFT) {
+      // the row's first and last vector after every whole vector is in flight
+#pragma unroll
+      for (int k = 0; k < NV; ++k) {
+        const int vi = c * CV + k * kThreads + rl.t;
+        const int e0 = vi * VEC - lead;
+        if (vi < nvec_row && !(e0 >= 0 && e0 + VEC <= N)) {
           float f[VEC];
           load_edge<Tin, VEC>(xr, e0, N, f);
           v[k].set(f);
         }
-      } else {
-        v[k].fill(kNegInf);
       }
     }
     float ml = kNegInf;
@@ -1268,16 +1324,20 @@ __global__ __launch_bounds__(256) void softmax_split_apply_kernel(const Tin* x, 
     for (int k = 0; k < NV; ++k) {
       const int vi = c * CV + k * kThreads + rl.t;
       const int e0 = vi * VEC - lead;
-      if (vi < nvec_row) {
-        if (!SHIFT || (e0 >= 0 && e0 + VEC <= N)) {
-          v[k].template load<true>(xr + e0);
-        } else {
+      if (vi < nvec_row && (!SHIFT || (e0 >= 0 && e0 + VEC <= N))) v[k].template load<true>(xr + e0);
+      else v[k].fill(kNegInf);
+    }
+    if constexpr (SHIFT) {
+      // the row's first and last vector after every whole vector is in flight
+#pragma unroll
+      for (int k = 0; k < NV; ++k) {
+        const int vi = c * CV + k * kThreads + rl.t;
+        const int e0 = vi * VEC - lead;
+        if (vi < nvec_row && !(e0 >= 0 && e0 + VEC <= N)) {
           float f[VEC];
           load_edge<Tin, VEC>(xr, e0, N, f);
           v[k].set(f);
         }
-      } else {
-        v[k].fill(kNegInf);
       }
     }
     MD p;
