@@ -298,8 +298,10 @@ typedef enum rr_op {
  *         the cross-workgroup hand-off costs L2 write-backs and invalidations.
  *         It falls back to the two kernels when the device cannot hold a
  *         row's chunks at once.  Both forms give the same bits.
- *   LOOP  one workgroup per row streaming the row twice (any N, unaligned
- *         rows, long rows with many rows; causal rows too long for BLOCK)
+ *   LOOP  one workgroup per row streaming the row twice (any N; long rows
+ *         with many rows; causal rows too long for BLOCK; rows whose input
+ *         and output sit at different offsets within a vector, element by
+ *         element)
  *   SUBWAVE short rows (at most 32 vectors, or 32 elements when unaligned):
  *         L lanes per row, 64/L rows per wavefront, reduced inside each
  *         L-lane group ([P4] section "按行长度选择并行方式")
@@ -326,7 +328,7 @@ typedef struct rr_plan {
   int64_t work_items;       /* workgroup-steps needed (rows / rows_per_group x chunks) */
   size_t workspace_bytes;   /* SPLIT: M * chunks_per_row * 16; otherwise 0 */
   int32_t row_shift;        /* 1: softmax rows cut into vectors at aligned addresses (WAVE,
-                               BLOCK, SPLIT): a row starting inside a vector, or ending inside one, is
+                               BLOCK, SPLIT, LOOP): a row starting inside a vector, or ending inside one, is
                                accessed whole vectors at a time except its first and last
                                vector, whose elements inside the row are accessed one by one */
 } rr_plan;

@@ -249,10 +249,10 @@ void plan_loop(rr_plan* p, int vec, int64_t nvec) {
 // starts at element `lead` of its first vector, so it spans up to nvec_s
 // vectors (see make_plan).  The same choice as for aligned rows: a
 // wavefront, a workgroup, the packed workgroup from packed_min_rows() rows (or
-// for a causal call), else the split below kSplitMaxRows rows; longer rows
-// stream (scalar).  The split sizes its chunks for a row at any offset
-// (nvec_any) so that the workspace query, which sees no addresses, covers
-// every call.
+// for a causal call), else the split below kSplitMaxRows rows, else the
+// streaming kernel, all cut the same way.  The split sizes its chunks for a
+// row at any offset (nvec_any) so that the workspace query, which sees no
+// addresses, covers every call.
 bool plan_shifted(rr_op op, bool causal, int64_t M, int64_t packed_rows, rr_plan* p, int vw, int per16,
                   int64_t nvec_s, int64_t nvec_any) {
   bool ok = true;
@@ -263,7 +263,7 @@ bool plan_shifted(rr_op op, bool causal, int64_t M, int64_t packed_rows, rr_plan
   } else if (op == RR_OP_SOFTMAX && !causal && M < kSplitMaxRows) {
     plan_split(p, vw, per16, nvec_any);
   } else {
-    ok = false;
+    plan_loop(p, vw, nvec_s);
   }
   if (ok) p->row_shift = 1;
   return ok;
@@ -358,7 +358,12 @@ rr_status make_plan(rr_op op, int64_t M, int64_t N, int din, int dout, int align
       }
       break;
     case RR_VARIANT_LOOP:
-      plan_loop(p, vec, nvec);
+      if (shiftable) {
+        plan_loop(p, vw, nvec_s);
+        p->row_shift = 1;
+      } else {
+        plan_loop(p, vec, nvec);
+      }
       ok = true;
       break;
     case RR_VARIANT_SUBWAVE:

@@ -1133,25 +1133,35 @@ __global__ __launch_bounds__(1024) void softmax_packed_kernel(const Tin* x, Tout
 // and writes exp(x - m) / d.  HBM traffic: two reads and one write per
 // element ([P2] section 七.3: "read twice, write once").
 // ===========================================================================
-template <typename Tin, typename Tout, int VEC, bool LOG, bool CAUSAL>
+template <typename Tin, typename Tout, int VEC, bool LOG, bool CAUSAL, bool SHIFT>
 __global__ __launch_bounds__(1024) void softmax_loop_kernel(const Tin* x, Tout* y, int64_t M,
                                                             int N, int64_t cp, int64_t co, RowStrides ld) {
   __shared__ MD slots[2][kMaxWavesPerGroup];
   const RowLane rl = row_lane<false>();
-  const int nvec = N / VEC;
   int parity = 0;
   CausalRows cr(blockIdx.x, gridDim.x, CAUSAL ? cp : 0, co);
   for (int64_t row = blockIdx.x; row < M; row += gridDim.x, cr.next()) {
     const int keys = cr.keys(N);
-    const int nvec_keys = (keys + VEC - 1) / VEC;
-    const int64_t ox = row * ld.x, oy = row * ld.y;
+    const Tin* xr = x + row * ld.x;
+    Tout* yr = y + row * ld.y;
+    // SHIFT: vector j covers the row's elements [j * VEC - lead, ...); the
+    // first and last vector are accessed element by element
+    const int lead = SHIFT ? row_lead(xr, VEC) : 0;
+    const int nvec_row = (lead + N + VEC - 1) / VEC;
+    const int nvec_keys = (lead + keys + VEC - 1) / VEC;
+    auto whole = [&](int e0) { return !SHIFT || (e0 >= 0 && e0 + VEC <= N); };
     MD p;
     p.m = kNegInf;
     p.d = 0.0f;
     for (int vi = rl.t; vi < nvec_keys; vi += rl.T) {
+      const int e0 = vi * VEC - lead;
       float v[VEC];
-      load_vec<Tin, VEC>(x + ox + (int64_t)vi * VEC, v);
-      mask_keys<VEC>(v, vi * VEC, keys);
+      if (whole(e0)) {
+        load_vec<Tin, VEC>(xr + e0, v);
+        mask_keys<VEC>(v, e0, keys);
+      } else {
+        load_edge<Tin, VEC>(xr, e0, keys, v);
+      }
       p = md_merge(p, chunk_summary<VEC>(v));
     }
     p = wave_md(p);
@@ -1159,18 +1169,22 @@ __global__ __launch_bounds__(1024) void softmax_loop_kernel(const Tin* x, Tout* 
     parity ^= 1;
     const float inv_d = (p.m == kNegInf) ? __builtin_nanf("") : 1.0f / p.d;
     const float ld = LOG ? __builtin_logf(p.d) : 0.0f;
-    for (int vi = rl.t; vi < nvec; vi += rl.T) {
+    for (int vi = rl.t; vi < nvec_row; vi += rl.T) {
+      const int e0 = vi * VEC - lead;
       float v[VEC];
-      if (vi < nvec_keys) {
-        load_vec<Tin, VEC>(x + ox + (int64_t)vi * VEC, v);
-        mask_keys<VEC>(v, vi * VEC, keys);
-      } else {
+      if (vi >= nvec_keys) {
 #pragma unroll
         for (int i = 0; i < VEC; ++i) v[i] = kNegInf;
+      } else if (whole(e0)) {
+        load_vec<Tin, VEC>(xr + e0, v);
+        mask_keys<VEC>(v, e0, keys);
+      } else {
+        load_edge<Tin, VEC>(xr, e0, keys, v);
       }
 #pragma unroll
       for (int i = 0; i < VEC; ++i) v[i] = LOG ? (v[i] - p.m) - ld : exp_shifted(v[i] - p.m) * inv_d;
-      store_vec<Tout, VEC>(y + oy + (int64_t)vi * VEC, v);
+      if (whole(e0)) store_vec<Tout, VEC>(yr + e0, v);
+      else store_edge<Tout, VEC>(yr, e0, N, v);
     }
   }
 }
@@ -1799,10 +1813,13 @@ hipError_t softmax_typed(const rr_plan& p, const SmCall<Tin, Tout>& c, void* ws,
     return softmax_sub<Tin, Tout, softmax_vec<Tin, Tout>(), LOG, CAUSAL>(p, c, grid, s);
   }
   if (p.variant == RR_VARIANT_LOOP) {
+    constexpr int V = softmax_vec<Tin, Tout>();
     if (p.vec_elems == 1)
-      softmax_loop_kernel<Tin, Tout, 1, LOG, CAUSAL><<<g, b, 0, s>>>(c.x, c.y, c.M, c.N, c.cp, c.co, c.ld);
+      softmax_loop_kernel<Tin, Tout, 1, LOG, CAUSAL, false><<<g, b, 0, s>>>(c.x, c.y, c.M, c.N, c.cp, c.co, c.ld);
+    else if (p.row_shift)
+      softmax_loop_kernel<Tin, Tout, V, LOG, CAUSAL, true><<<g, b, 0, s>>>(c.x, c.y, c.M, c.N, c.cp, c.co, c.ld);
     else
-      softmax_loop_kernel<Tin, Tout, softmax_vec<Tin, Tout>(), LOG, CAUSAL><<<g, b, 0, s>>>(c.x, c.y, c.M, c.N, c.cp, c.co, c.ld);
+      softmax_loop_kernel<Tin, Tout, V, LOG, CAUSAL, false><<<g, b, 0, s>>>(c.x, c.y, c.M, c.N, c.cp, c.co, c.ld);
     return hipGetLastError();
   }
   if (p.variant == RR_VARIANT_SPLIT || p.variant == RR_VARIANT_SPLIT_ONE_KERNEL) {

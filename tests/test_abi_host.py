@@ -349,9 +349,12 @@ def test_dispatch_boundaries():
             assert rr.rr_softmax_rows_workspace_bytes(M, N, a, b) == M * chunks * 16
     assert rr.rr_query_plan(S, 4, 65536, F, F)["chunks_per_row"] == 16   # aligned rows: one chunk fewer
     assert sh(4, 50257, op=rr.RR_OP_SOFTMAX_CAUSAL)["variant_name"] == "block"
-    # too long to hold with 1024 rows or more, or element access requested:
-    # the scalar streaming path
-    assert sh(1024, 81925)["variant_name"] == "loop" and sh(1024, 81925)["vec_elems"] == 1
+    # too long to hold with 1024 rows or more (or a causal call): the
+    # streaming kernel, cut the same way; element access requested: scalar
+    p = sh(1024, 81925)
+    assert (p["variant_name"], p["vec_elems"], p["row_shift"], p["waves_per_row"]) == ("loop", 4, 1, 16), p
+    p = sh(4, 200003, B, F, op=rr.RR_OP_SOFTMAX_CAUSAL)
+    assert (p["variant_name"], p["vec_elems"], p["row_shift"], p["workspace_bytes"]) == ("loop", 4, 1, 0), p
     assert v(S, 10, 1024, al=False) == "loop" and sh(10, 1024, al=False)["row_shift"] == 0
     # the norms' gamma lies in a frame of its own: unaligned norm rows stream
     assert v(rr.RR_OP_RMSNORM, 10, 4100, B, B) == "loop"   # 4100 % 8 != 0
@@ -431,8 +434,10 @@ def test_every_plan_covers_its_row():
                     # wavefront or workgroup, room for the worst lead (vec - 1)
                     assert op in (rr.RR_OP_SOFTMAX, rr.RR_OP_SOFTMAX_CAUSAL) and vec == width, p
                     assert aligned == 2 or (aligned == 1 and N % width != 0), p
-                    assert name in ("wave", "block", "split"), p
-                    if name == "split":
+                    assert name in ("wave", "block", "split", "loop"), p
+                    if name == "loop":
+                        pass                                  # streams any length
+                    elif name == "split":
                         cap = p["chunks_per_row"] * 256 * nv * vec
                         assert cap >= N + vec - 1, p          # any lead, also with aligned starts
                     else:

@@ -741,6 +741,61 @@ def test_softmax_split_rows_cut_at_aligned_addresses(M, N, din, dout, log):
             Yc = Y.cpu()
             assert bool((Yc[:, :c0] == 7.0).all()) and bool((Yc[:, c0 + N:] == 7.0).all()), what
 
+# (M, N, in dtype, out dtype, log output, causal (period, offset) or None,
+# column offset or None): rows cut at aligned addresses that no workgroup can
+# hold (1024 rows or more, or a causal call), streamed twice
+LOOP_CUT_CASES = [
+    (1024, 81925, "f32", "f32", False, None, None),
+    (8, 200003, "bf16", "f32", True, (8, 150000), None),
+    (4, 300001, "f32", "bf16", False, (4, 290000), 3),
+    (3, 163845, "bf16", "bf16", False, (3, 163844), 5),
+]
+
+
+@pytest.mark.parametrize("M,N,din,dout,log,causal,c0", LOOP_CUT_CASES)
+def test_softmax_streamed_rows_cut_at_aligned_addresses(M, N, din, dout, log, causal, c0):
+    """The streaming kernel with rows cut at aligned addresses, against the
+    oracle (masked keys as -inf in the oracle's input, NaN in the kernel's,
+    which must never read them); a column slice's neighbours stay untouched."""
+    rr = _rr()
+    code = {"f32": rr.RR_F32, "bf16": rr.RR_BF16}
+    x = softmax_input(M, N, seed=N + 3 * M, dt=din)
+    xf = compare.to_f64(x)
+    period, offset = causal if causal else (None, 0)
+    if causal:
+        keys = np.minimum(N, np.arange(M) % period + offset + 1)
+        masked = np.arange(N)[None, :] >= keys[:, None]
+        xf[masked] = -np.inf
+        x = torch.from_numpy(np.where(masked, np.float32(np.nan), compare.to_f64(x)).astype(np.float32)).to(_tdt(din))
+    opts = rr.make_softmax_opts(log_output=log, causal_period=period, causal_offset=offset)
+    op = rr.RR_OP_SOFTMAX_CAUSAL if causal else rr.RR_OP_SOFTMAX
+    plan = rr.rr_query_plan(op, M, N, code[din], code[dout], 2)
+    _say(f"streamed cut rows {din}->{dout} {M}x{N} log={log} causal={causal} slice={c0} plan={plan['variant_name']}")
+    assert (plan["variant_name"], plan["row_shift"]) == ("loop", 1), plan
+    if c0 is None:
+        xs = x.cuda()
+        Y = ys = torch.empty((M, N), dtype=_tdt(dout), device="cuda")
+    else:
+        ld = N + 7
+        X = torch.full((M, ld), float("nan"), dtype=_tdt(din), device="cuda")
+        X[:, c0:c0 + N] = x.cuda()
+        Y = torch.full((M, ld), 7.0, dtype=_tdt(dout), device="cuda")
+        xs, ys = X[:, c0:c0 + N], Y[:, c0:c0 + N]
+    rr.rr_softmax_rows_strided(ys, xs, opts, None)
+    torch.cuda.synchronize()
+    got = ys.cpu().contiguous()
+    what = f"streamed cut rows {din}->{dout} {M}x{N} log={log} causal={causal}"
+    if log:
+        compare.check_log_softmax(got, xf, oracle.log_softmax(xf), what)
+    else:
+        compare.check_softmax(got, xf, oracle.softmax(xf), what)
+    if c0 is not None:
+        Yc = Y.cpu()
+        assert bool((Yc[:, :c0] == 7.0).all()) and bool((Yc[:, c0 + N:] == 7.0).all()), what
+    del xs, ys, Y
+    torch.cuda.empty_cache()
+
+
 def test_softmax_in_place_unaligned_and_tiny():
     rr = _rr()
     for dt in ("f32", "bf16"):
