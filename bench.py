@@ -412,7 +412,7 @@ def main():
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}): "
               "rows are independent, so a multi-GPU run is the same kernel on each GPU's share of "
-              "the rows with no exchange; it is not part of this build.", file=sys.stderr)
+              "the rows with no exchange, and only the one-GPU run is measured here.", file=sys.stderr)
         sys.exit(2)
 
     import torch

@@ -69,7 +69,7 @@ typedef enum rr_dtype {
 typedef enum rr_status {
   RR_OK = 0,
   RR_ERR_INVALID_ARG = 1,  /* null pointer, bad size, unknown dtype, bad aliasing */
-  RR_ERR_UNSUPPORTED = 2,  /* valid request this build cannot run (size limits, forced variant) */
+  RR_ERR_UNSUPPORTED = 2,  /* valid request the library cannot run (size limits, forced variant) */
   RR_ERR_WORKSPACE = 3,    /* workspace missing or smaller than rr_softmax_rows_workspace_bytes */
   RR_ERR_HIP = 4           /* the HIP runtime reported an error */
 } rr_status;
