@@ -1061,16 +1061,31 @@ __global__ __launch_bounds__(1024) void softmax_packed_kernel(const Tin* x, Tout
     for (int k = 0; k < NV; ++k) {
       const int vi = k * kThreads + t_ld;
       const int e0 = vi * VEC - lead;
-      if (vi < nvec_keys) {
-        if (!SHIFT || (e0 >= 0 && e0 + VEC <= N)) {
-          v[k].template load<true>(xr + e0);
-        } else {
-          float f[VEC];
-          load_edge<Tin, VEC>(xr, e0, keys, f);
-          v[k].set(f);
-        }
-      } else {
-        v[k].fill(kNegInf);
+      if (vi < nvec_keys && (!SHIFT || (e0 >= 0 && e0 + VEC <= N))) v[k].template load<true>(xr + e0);
+      else v[k].fill(kNegInf);
+    }
+    if constexpr (SHIFT) {
+      // A cut row's only partial vectors are its first (lane 0, k = 0) and
+      // its last; they are read element by element once every whole
+      // vector's load is issued (read in between, their scalar loads would
+      // wait for the loads issued before them)
+      auto partial = [&](int vi) {
+        const int e0 = vi * VEC - lead;
+        return vi < nvec_keys && !(e0 >= 0 && e0 + VEC <= N);
+      };
+      if (t_ld == 0 && partial(0)) {
+        float f[VEC];
+        load_edge<Tin, VEC>(xr, -lead, keys, f);
+        v[0].set(f);
+      }
+      const int last = nvec_row - 1;
+      if (last > 0 && t_ld == last % kThreads && partial(last)) {
+        float f[VEC];
+        load_edge<Tin, VEC>(xr, last * VEC - lead, keys, f);
+        const int kl = last / kThreads;
+#pragma unroll
+        for (int k = 0; k < NV; ++k)
+          if (k == kl) v[k].set(f);
       }
     }
     // a row the causal rule cuts: keys past the count inside the vector
