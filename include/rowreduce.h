@@ -45,8 +45,13 @@
  *     multiple of 4 (fp32) or 8 (bf16) elements use 16-byte vector accesses;
  *     a softmax reading bf16 and writing fp32 reads 4 elements (8 bytes) per
  *     access, so there input rows 8-byte aligned and a width that is a
- *     multiple of 4 suffice.  Anything else runs a scalar path with the same
- *     results up to rounding order.  Any N >= 1 is accepted.
+ *     multiple of 4 suffice.  A softmax whose input and output rows start at
+ *     the same element offset within a vector (contiguous rows of any width,
+ *     in place, column slices with equal strides) is cut into vectors at
+ *     aligned addresses: whole vectors inside each row, its first and last
+ *     vector element by element, nothing outside the row read or written.
+ *     Anything else runs a scalar path.  Each path gives the same results up
+ *     to rounding order.  Any N >= 1 is accepted.
  *   - Determinism: a given (op, M, N, dtypes, alignment) always runs the same
  *     kernel with the same reduction order, so results are bitwise
  *     reproducible run to run; no floating-point atomics are used.
@@ -236,8 +241,9 @@ rr_status rr_softmax_rows_ex(void* y, const void* x, int64_t M, int64_t N, rr_dt
  * accesses need every row start aligned to the access (16 bytes: aligned
  * base pointers and strides that are multiples of 4 fp32 or 8 bf16
  * elements; 8 bytes for the bf16 input of a softmax written as fp32);
- * otherwise the scalar path runs, with the same results up to rounding
- * order.  With every stride equal to the width these are exactly
+ * a softmax whose x and y rows share their offset within a vector is cut at
+ * aligned addresses (see above); otherwise the scalar path runs, with the
+ * same results up to rounding order.  With every stride equal to the width these are exactly
  * the contiguous entry points above (same kernels, same bits).
  * Aliasing: y may be x itself (same pointer and stride, same dtype); other
  * matrices of a call must not share an element.  Two matrices with the same

@@ -333,8 +333,8 @@ def test_dispatch_boundaries():
             assert (p["variant_name"], p["vecs_per_lane"], p["row_shift"]) == (name, nv, 1), (M, N, al, p)
             assert p["vec_elems"] == (4 if (a, b) != (B, B) else 8) and p["workspace_bytes"] == 0, p
     assert sh(64, 4097, op=rr.RR_OP_SOFTMAX_CAUSAL)["row_shift"] == 1
-    # beyond a workgroup's registers with fewer than 64 rows, or beyond the
-    # packed workgroup below 1024 rows: the split, its chunks sized for a row
+    # beyond a workgroup's registers with few rows (below 40 / 56 / 80 by
+    # dtype pair), or beyond the packed workgroup below 1024 rows: the split, its chunks sized for a row
     # at any offset (so that the workspace query, which sees no addresses,
     # covers every call); a causal call never splits
     for M, N, a, b, vec, nv, chunks in ((3, 50257, B, B, 8, 4, 7), (2, 50257, F, B, 4, 4, 13),
