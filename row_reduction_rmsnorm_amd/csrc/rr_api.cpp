@@ -256,7 +256,17 @@ void plan_loop(rr_plan* p, int vec, int64_t nvec) {
 bool plan_shifted(rr_op op, bool causal, int64_t M, int64_t packed_rows, rr_plan* p, int vw, int per16,
                   int64_t nvec_s, int64_t nvec_any) {
   bool ok = true;
-  if (wave_fits(op, vw, nvec_s)) {
+  if (op != RR_OP_SOFTMAX) {
+    // the norm kernels hold gamma's (and beta's) two aligned blocks per
+    // vector while the row loads: an fp32 LayerNorm keeps to 2 vectors per
+    // lane (4 would spill); longer norm rows stream element by element
+    const int max_nv = (op == RR_OP_LAYERNORM && vw == 4) ? 2 : 16;
+    if (wave_fits(op, vw, nvec_s) && ceil_div(nvec_s, 64) <= max_nv) {
+      plan_wave(p, vw, nvec_s);
+    } else {
+      ok = plan_block(op, p, vw, nvec_s) && p->vecs_per_lane <= max_nv;
+    }
+  } else if (wave_fits(op, vw, nvec_s)) {
     plan_wave(p, vw, nvec_s);
   } else if (plan_block(op, p, vw, nvec_s)) {
   } else if ((M >= packed_rows || causal) && plan_packed(op, p, vw, per16, nvec_s)) {
@@ -295,8 +305,10 @@ rr_status make_plan(rr_op op, int64_t M, int64_t N, int din, int dout, int align
   const bool plain = align == 1 && N % vw == 0;
   // rows that are not whole aligned vectors but can be cut at aligned
   // addresses: aligned starts with a ragged width, or starts at a common
-  // offset (softmax only; the norms' gamma lies in a frame of its own)
-  const bool shiftable = !plain && align != 0 && op == RR_OP_SOFTMAX;
+  // offset (the norms read gamma in each row's frame, only in the register
+  // kernels, and from three vectors up: gamma's windows are cut from pairs of
+  // aligned blocks inside it)
+  const bool shiftable = !plain && align != 0 && (op == RR_OP_SOFTMAX || N >= 3 * (int64_t)vw);
   const int vec = plain ? vw : 1;
   const int per16 = vecs_per_16_bytes(din, vec);
   const int64_t nvec = N / vec;
@@ -351,14 +363,14 @@ rr_status make_plan(rr_op op, int64_t M, int64_t N, int din, int dout, int align
       if (ok) {
         plan_split(p, vec, per16, nvec);
         p->variant = forced;
-      } else if (forced == RR_VARIANT_SPLIT && shiftable && !causal) {
+      } else if (forced == RR_VARIANT_SPLIT && shiftable && op == RR_OP_SOFTMAX && !causal) {
         plan_split(p, vw, per16_s, nvec_any);   // the one-kernel form takes aligned rows only
         p->row_shift = 1;
         ok = true;
       }
       break;
     case RR_VARIANT_LOOP:
-      if (shiftable) {
+      if (shiftable && op == RR_OP_SOFTMAX) {
         plan_loop(p, vw, nvec_s);
         p->row_shift = 1;
       } else {
@@ -372,6 +384,13 @@ rr_status make_plan(rr_op op, int64_t M, int64_t N, int din, int dout, int align
     default:
       break;
   }
+  if (!ok) {
+    return fail(RR_ERR_UNSUPPORTED, "forced variant %d cannot run op %d with N = %lld (vector width %d)",
+                forced, (int)op, (long long)N, vec);
+  }
+  // cut fp32 LayerNorm rows keep to 2 vectors per lane (plan_shifted), also
+  // when a variant is forced
+  if (ok && p->row_shift && op == RR_OP_LAYERNORM && vw == 4 && p->vecs_per_lane > 2) ok = false;
   if (!ok) {
     return fail(RR_ERR_UNSUPPORTED, "forced variant %d cannot run op %d with N = %lld (vector width %d)",
                 forced, (int)op, (long long)N, vec);
@@ -467,9 +486,22 @@ rr_status norm_entry(int kind, void* y, int64_t ldy, void* residual, int64_t ldr
   }
   const bool al = rows_aligned16(my) && rows_aligned16(mx) && aligned16(gamma) &&
                   (!fused || rows_aligned16(mr)) && (!layer || !beta || aligned16(beta));
+  // otherwise: x, y (and the residual) rows at one element offset within a
+  // vector, and gamma (beta) element-aligned, lets the register kernels cut
+  // the rows at aligned addresses
+  int align = al ? 1 : 0;
+  if (!al) {
+    const int64_t vw = op_vec_width(RR_OP_RMSNORM, dtype, dtype);
+    auto elem = [&](const void* q) { return reinterpret_cast<uintptr_t>(q) % es == 0; };
+    auto lead = [&](const void* q) { return (int64_t)((reinterpret_cast<uintptr_t>(q) / es) % (uintptr_t)vw); };
+    bool same = elem(x) && elem(y) && elem(gamma) && (!layer || !beta || elem(beta)) &&
+                lead(x) == lead(y) && ldx % vw == ldy % vw;
+    if (fused) same = same && elem(residual) && lead(residual) == lead(x) && ldr % vw == ldx % vw;
+    if (same) align = 2;
+  }
   const rr_op op = fused ? RR_OP_FUSED_ADD_RMSNORM : layer ? RR_OP_LAYERNORM : RR_OP_RMSNORM;
   rr_plan p;
-  const rr_status st = make_plan(op, M, H, dtype, dtype, al ? 1 : 0, &p);
+  const rr_status st = make_plan(op, M, H, dtype, dtype, align, &p);
   if (st != RR_OK) return st;
   rr::NormArgs a;
   a.y = y;

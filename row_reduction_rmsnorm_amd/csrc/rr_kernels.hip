@@ -229,13 +229,30 @@ __device__ __forceinline__ int row_lead(const T* row_start, int vec) {
   return (int)((reinterpret_cast<uintptr_t>(row_start) / sizeof(T)) % (uintptr_t)vec);
 }
 
-// The elements e0 + i of a vector that lie in [0, keys), the rest -inf.
+// The elements e0 + i of a vector that lie in [0, keys), the rest `fill`
+// (-inf for a softmax, 0 for the norms); keys >= 1.  Every element's load is
+// issued before any is used: an index outside [0, keys) reads the nearest
+// element inside (never anything outside the row) and is replaced by `fill`
+// afterwards.  A load in a branch of its own, widened there, would wait for
+// that one load before the next is issued.
 template <typename T, int VEC>
-__device__ __forceinline__ void load_edge(const T* row, int e0, int keys, float (&v)[VEC]) {
+__device__ __forceinline__ void load_edge(const T* row, int e0, int keys, float (&v)[VEC],
+                                          float fill = kNegInf) {
+  uint32_t raw[VEC];
 #pragma unroll
   for (int i = 0; i < VEC; ++i) {
     const int e = e0 + i;
-    v[i] = (e >= 0 && e < keys) ? load_one<T>(row + e) : kNegInf;
+    const int ec = e < 0 ? 0 : (e >= keys ? keys - 1 : e);
+    if constexpr (std::is_same_v<T, float>) raw[i] = __float_as_uint(row[ec]);
+    else raw[i] = static_cast<uint32_t>(row[ec]);
+  }
+#pragma unroll
+  for (int i = 0; i < VEC; ++i) asm volatile("" : "+v"(raw[i]));
+#pragma unroll
+  for (int i = 0; i < VEC; ++i) {
+    const int e = e0 + i;
+    const float f = std::is_same_v<T, float> ? __uint_as_float(raw[i]) : __uint_as_float(raw[i] << 16);
+    v[i] = (e >= 0 && e < keys) ? f : fill;
   }
 }
 
@@ -315,6 +332,34 @@ __device__ __forceinline__ void widen_row(Packed<T, VEC> (&p)[NV], float (&h)[NV
     for (int i = 0; i < VEC; ++i) h[k][i] = p[k].get(i);
 }
 
+// VEC elements p[e .. e + VEC) of a vector (gamma or beta) whose start lies
+// `lp` elements into a VEC-aligned block, for a window that need not be
+// aligned: window_blocks loads the two aligned vectors that hold it, and
+// window_cut cuts the window out of them (a shift by whole dwords, chosen per
+// dword from four candidates, then v_alignbyte for the 2-byte remainder of a
+// bf16 offset).  The caller keeps both aligned vectors inside [0, n) of p.
+template <typename T, int VEC>
+__device__ __forceinline__ void window_blocks(const T* p, int lp, int e, Packed<T, VEC>& A,
+                                              Packed<T, VEC>& B) {
+  const int a = (e + lp) / VEC;           // e in p's aligned frame (e + lp >= 0)
+  A.load(p - lp + a * VEC);
+  B.load(p - lp + (a + 1) * VEC);
+}
+template <typename T, int VEC>
+__device__ __forceinline__ void window_cut(int lp, int e, const Packed<T, VEC>& A, const Packed<T, VEC>& B,
+                                           Packed<T, VEC>& out) {
+  static_assert(Packed<T, VEC>::kWords == 4, "16-byte vectors");
+  const int d = (e + lp) % VEC;           // element offset inside the first block
+  const uint32_t C[8] = {A.w[0], A.w[1], A.w[2], A.w[3], B.w[0], B.w[1], B.w[2], B.w[3]};
+  const int bo = d * (int)sizeof(T);      // byte offset 0 .. 15
+  const int q = bo >> 2, r = bo & 3;
+  uint32_t W[5];
+#pragma unroll
+  for (int j = 0; j < 5; ++j) W[j] = q == 0 ? C[j] : q == 1 ? C[j + 1] : q == 2 ? C[j + 2] : C[j + 3];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) out.w[j] = __builtin_amdgcn_alignbyte(W[j + 1], W[j], r);
+}
+
 // ===========================================================================
 // RMSNorm / fused add + RMSNorm, row held in registers (WAVE and BLOCK)
 //
@@ -326,8 +371,17 @@ __device__ __forceinline__ void widen_row(Packed<T, VEC> (&p)[NV], float (&h)[NV
 // is rescaled.  Widening bf16 is exact and fp32 carries more than twice bf16's
 // precision plus two bits, so rounding the fp32 sum to bf16 gives the
 // correctly rounded sum.
+//
+// SHIFT: rows cut at aligned addresses.  x, y (and the residual) rows start
+// at the same element offset `lead` within a vector (the host checks it);
+// vector j covers the row's elements [j * VEC - lead, (j + 1) * VEC - lead).
+// Whole vectors inside the row are accessed whole, the row's first and last
+// vector element by element (0 outside the row), and gamma (beta), which lie
+// in a frame of their own, are read for each row in the row's frame:
+// whole vectors when gamma starts at the row's offset, else element by
+// element (they stay in the cache across rows).
 // ===========================================================================
-template <typename T, int NV, int KIND, bool WAVE>
+template <typename T, int NV, int KIND, bool WAVE, bool SHIFT>
 __global__ __launch_bounds__(1024) void norm_regs_kernel(T* y, T* residual, const T* x,
                                                          const T* __restrict__ gamma,
                                                          const T* __restrict__ beta, int64_t M,
@@ -339,14 +393,16 @@ __global__ __launch_bounds__(1024) void norm_regs_kernel(T* y, T* residual, cons
 
   Packed<T, VEC> gv[NV];
   Packed<T, VEC> bv[KIND == kNormLayer ? NV : 1];
+  if constexpr (!SHIFT) {
 #pragma unroll
-  for (int k = 0; k < NV; ++k) {
-    const int vi = k * rl.T + rl.t;
-    if (vi < nvec) gv[k].load(gamma + (int64_t)vi * VEC);
-    else gv[k].fill(0.0f);
-    if constexpr (KIND == kNormLayer) {
-      if (vi < nvec && beta) bv[k].load(beta + (int64_t)vi * VEC);
-      else bv[k].fill(0.0f);
+    for (int k = 0; k < NV; ++k) {
+      const int vi = k * rl.T + rl.t;
+      if (vi < nvec) gv[k].load(gamma + (int64_t)vi * VEC);
+      else gv[k].fill(0.0f);
+      if constexpr (KIND == kNormLayer) {
+        if (vi < nvec && beta) bv[k].load(beta + (int64_t)vi * VEC);
+        else bv[k].fill(0.0f);
+      }
     }
   }
 
@@ -364,6 +420,22 @@ __global__ __launch_bounds__(1024) void norm_regs_kernel(T* y, T* residual, cons
   for (int64_t row = (int64_t)blockIdx.x * rl.rpg + rl.g; row < M; row += stride) {
     const int64_t ox = row * ld.x, oy = row * ld.y, orr = row * ld.r;
     float h[NV][VEC];
+    // SHIFT: the row's frame (without SHIFT lead is 0 and nvec_row nvec)
+    const int lead = SHIFT ? row_lead(x + ox, VEC) : 0;
+    const int nvec_row = SHIFT ? (lead + N + VEC - 1) / VEC : nvec;
+    // y's vector k of this lane (and, SHIFT, the row's partial vectors)
+    auto store_row = [&](T* base, int k, const float (&o)[VEC]) {
+      const int vi = k * rl.T + rl.t;
+      if constexpr (SHIFT) {
+        const int e0 = vi * VEC - lead;
+        if (vi < nvec_row) {
+          if (e0 >= 0 && e0 + VEC <= N) store_vec<T, VEC>(base + e0, o);
+          else store_edge<T, VEC>(base, e0, N, o);
+        }
+      } else {
+        if (vi < nvec) store_vec<T, VEC>(base + (int64_t)vi * VEC, o);
+      }
+    };
     // gamma (and beta) were loaded before the loop; marking their words here,
     // after this row's loads are issued, keeps their wait (and widening)
     // behind those loads instead of before the first row's
@@ -375,7 +447,144 @@ __global__ __launch_bounds__(1024) void norm_regs_kernel(T* y, T* residual, cons
         for (int k = 0; k < NV; ++k) bv[k].touch();
       }
     };
-    if constexpr (KIND == kNormFused) {
+    if constexpr (SHIFT) {
+      // gamma (beta) in the row's frame: each lane's window is cut out of
+      // the two aligned blocks that hold it.  The blocks are loaded first
+      // (from the cache), with no branch: a block start is clamped to lie
+      // inside [0, N) of gamma, and the few lanes whose window needs a block
+      // outside (the row's ends) are read element by element afterwards.
+      // Then the row's whole vectors are loaded, then the windows cut (they
+      // wait for gamma's loads only), then the fix-ups and the row's two
+      // partial vectors.  (The host cuts norm rows only for N >= 3 * VEC, so
+      // a pair of aligned blocks always fits inside gamma.)
+      const int lg = row_lead(gamma, VEC);
+      const int lb = (KIND == kNormLayer && beta) ? row_lead(beta, VEC) : lg;
+      constexpr int NB = KIND == kNormLayer ? NV : 1;
+      Packed<T, VEC> ga[NV], gb[NV], ba[NB], bb[NB];
+      auto inside = [&](int vi) {
+        const int e0 = vi * VEC - lead;
+        return vi < nvec_row && e0 >= 0 && e0 + VEC <= N;
+      };
+      // the first of the two blocks holding [e0, e0 + VEC) of a vector whose
+      // start lies l elements into a block, unclamped and clamped
+      auto block0 = [&](int e0, int l) { return ((e0 + l) / VEC) * VEC - l; };
+      auto clamped = [&](int e0, int l) {
+        const int lo = l == 0 ? 0 : VEC - l;                              // first block inside
+        const int hi = ((N - 2 * VEC + l) / VEC) * VEC - l;               // last pair inside
+        const int b = e0 < 0 ? lo : block0(e0, l);
+        return b < lo ? lo : (b > hi ? hi : b);
+      };
+      auto windowed = [&](int vi) {
+        const int e0 = vi * VEC - lead;
+        return inside(vi) && block0(e0, lg) == clamped(e0, lg) && block0(e0, lb) == clamped(e0, lb);
+      };
+#pragma unroll
+      for (int k = 0; k < NV; ++k) {
+        const int e0 = (k * rl.T + rl.t) * VEC - lead;
+        const int bg = clamped(e0, lg);
+        ga[k].load(gamma + bg);
+        gb[k].load(gamma + bg + VEC);
+        if constexpr (KIND == kNormLayer) {
+          if (beta) {
+            const int bbb = clamped(e0, lb);
+            ba[k].load(beta + bbb);
+            bb[k].load(beta + bbb + VEC);
+          } else {
+            ba[k].zero();
+            bb[k].zero();
+          }
+        }
+      }
+      Packed<T, VEC> px[NV], pr[KIND == kNormFused ? NV : 1];
+#pragma unroll
+      for (int k = 0; k < NV; ++k) {
+        const int vi = k * rl.T + rl.t;
+        const int e0 = vi * VEC - lead;
+        if (inside(vi)) {
+          px[k].template load<true>(x + ox + e0);
+          if constexpr (KIND == kNormFused) pr[k].template load<true>(residual + orr + e0);
+        } else {
+          px[k].zero();
+          if constexpr (KIND == kNormFused) pr[k].zero();
+        }
+      }
+      // gamma's blocks are read only below, after every load above is issued
+      // (an empty asm that may touch memory and "changes" the blocks): else
+      // the compiler cuts each window as soon as its blocks arrive, to free
+      // their registers, which holds back the loads after them
+#pragma unroll
+      for (int k = 0; k < NV; ++k) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          asm volatile("" : "+v"(ga[k].w[j]), "+v"(gb[k].w[j]) : : "memory");
+          if constexpr (KIND == kNormLayer) asm volatile("" : "+v"(ba[k].w[j]), "+v"(bb[k].w[j]) : : "memory");
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < NV; ++k) {
+        const int e0 = (k * rl.T + rl.t) * VEC - lead;
+        window_cut<T, VEC>(lg, e0, ga[k], gb[k], gv[k]);   // (fixed up below where not windowed)
+        if constexpr (KIND == kNormLayer) window_cut<T, VEC>(lb, e0, ba[k], bb[k], bv[k]);
+      }
+#pragma unroll
+      for (int k = 0; k < NV; ++k) {
+        const int vi = k * rl.T + rl.t;
+        const int e0 = vi * VEC - lead;
+        if (vi < nvec_row && !windowed(vi)) {
+          float f[VEC];
+          load_edge<T, VEC>(gamma, e0, N, f, 0.0f);
+          gv[k].set(f);
+          if constexpr (KIND == kNormLayer) {
+            if (beta) {
+              load_edge<T, VEC>(beta, e0, N, f, 0.0f);
+              bv[k].set(f);
+            } else {
+              bv[k].zero();
+            }
+          }
+        }
+      }
+      // the row's first vector (lane 0, k = 0) and last vector, if partial
+      auto partial = [&](int vi) {
+        const int e0 = vi * VEC - lead;
+        return vi < nvec_row && !(e0 >= 0 && e0 + VEC <= N);
+      };
+      const int last = nvec_row - 1;
+      if (rl.t == 0 && partial(0)) {
+        float f[VEC];
+        load_edge<T, VEC>(x + ox, -lead, N, f, 0.0f);
+        px[0].set(f);
+        if constexpr (KIND == kNormFused) {
+          load_edge<T, VEC>(residual + orr, -lead, N, f, 0.0f);
+          pr[0].set(f);
+        }
+      }
+      if (last > 0 && rl.t == last % rl.T && partial(last)) {
+        const int kl = last / rl.T;
+        float f[VEC], g[VEC];
+        load_edge<T, VEC>(x + ox, last * VEC - lead, N, f, 0.0f);
+        if constexpr (KIND == kNormFused) load_edge<T, VEC>(residual + orr, last * VEC - lead, N, g, 0.0f);
+#pragma unroll
+        for (int k = 0; k < NV; ++k) {
+          if (k == kl) {
+            px[k].set(f);
+            if constexpr (KIND == kNormFused) pr[k].set(g);
+          }
+        }
+      }
+      params_after_loads();
+      widen_row<T, VEC, NV>(px, h);
+      if constexpr (KIND == kNormFused) {
+        float r[NV][VEC];
+        widen_row<T, VEC, NV>(pr, r);
+#pragma unroll
+        for (int k = 0; k < NV; ++k) {
+#pragma unroll
+          for (int i = 0; i < VEC; ++i) h[k][i] = round_to<T>(h[k][i] + r[k][i]);
+          store_row(residual + orr, k, h[k]);
+        }
+      }
+    } else if constexpr (KIND == kNormFused) {
       float r[NV][VEC];
       Packed<T, VEC> px[NV], pr[NV];
 #pragma unroll
@@ -426,10 +635,14 @@ __global__ __launch_bounds__(1024) void norm_regs_kernel(T* y, T* residual, cons
         s2 = 0.0f;
 #pragma unroll
         for (int k = 0; k < NV; ++k) {
-          const bool valid = k * rl.T + rl.t < nvec;
+          const int vi = k * rl.T + rl.t;
+          const bool valid = vi < nvec;
 #pragma unroll
           for (int i = 0; i < VEC; ++i) {
-            const float d = valid ? h[k][i] - S : 0.0f;
+            // SHIFT: elements outside the row (partial vectors) count nothing
+            const int e = vi * VEC - lead + i;
+            const bool in = SHIFT ? (vi < nvec_row && e >= 0 && e < N) : valid;
+            const float d = in ? h[k][i] - S : 0.0f;
             s1 += d;
             s2 += d * d;
           }
@@ -469,11 +682,10 @@ __global__ __launch_bounds__(1024) void norm_regs_kernel(T* y, T* residual, cons
       const float rstd = 1.0f / __builtin_sqrtf(__builtin_fmaxf(var, 0.0f) + eps);
 #pragma unroll
       for (int k = 0; k < NV; ++k) {
-        const int vi = k * rl.T + rl.t;
         float o[VEC];
 #pragma unroll
         for (int i = 0; i < VEC; ++i) o[i] = (h[k][i] * rstd) * gv[k].get(i) + bv[k].get(i);
-        if (vi < nvec) store_vec<T, VEC>(y + oy + (int64_t)vi * VEC, o);
+        store_row(y + oy, k, o);
       }
     } else {
       float ss = 0.0f;
@@ -485,11 +697,10 @@ __global__ __launch_bounds__(1024) void norm_regs_kernel(T* y, T* residual, cons
       const float rstd = 1.0f / __builtin_sqrtf(row_sum(ss) / (float)N + eps);
 #pragma unroll
       for (int k = 0; k < NV; ++k) {
-        const int vi = k * rl.T + rl.t;
         float o[VEC];
 #pragma unroll
         for (int i = 0; i < VEC; ++i) o[i] = (h[k][i] * rstd) * gv[k].get(i);
-        if (vi < nvec) store_vec<T, VEC>(y + oy + (int64_t)vi * VEC, o);
+        store_row(y + oy, k, o);
       }
     }
   }
@@ -1542,7 +1753,7 @@ namespace {
 
 inline dim3 grid1(int64_t g) { return dim3((unsigned)g, 1, 1); }
 
-template <typename T, int KIND, bool WAVE>
+template <typename T, int KIND, bool WAVE, bool SHIFT>
 hipError_t norm_regs(const rr_plan& p, const NormArgs& a, int64_t grid, hipStream_t s) {
   T* yy = static_cast<T*>(a.y);
   T* rr_ = static_cast<T*>(a.residual);
@@ -1553,11 +1764,12 @@ hipError_t norm_regs(const rr_plan& p, const NormArgs& a, int64_t grid, hipStrea
   // The host never plans more than 16 values per lane for the norms
   // (NV * VEC <= 16), so only those instantiations exist.
   switch (p.vecs_per_lane) {
-    case 1: norm_regs_kernel<T, 1, KIND, WAVE><<<grid1(grid), b, 0, s>>>(yy, rr_, xx, gg, bb, a.M, a.N, a.eps, a.ld); break;
-    case 2: norm_regs_kernel<T, 2, KIND, WAVE><<<grid1(grid), b, 0, s>>>(yy, rr_, xx, gg, bb, a.M, a.N, a.eps, a.ld); break;
+    case 1: norm_regs_kernel<T, 1, KIND, WAVE, SHIFT><<<grid1(grid), b, 0, s>>>(yy, rr_, xx, gg, bb, a.M, a.N, a.eps, a.ld); break;
+    case 2: norm_regs_kernel<T, 2, KIND, WAVE, SHIFT><<<grid1(grid), b, 0, s>>>(yy, rr_, xx, gg, bb, a.M, a.N, a.eps, a.ld); break;
     case 4:
-      if constexpr (Elem<T>::kVec * 4 <= 16) {
-        norm_regs_kernel<T, 4, KIND, WAVE><<<grid1(grid), b, 0, s>>>(yy, rr_, xx, gg, bb, a.M, a.N, a.eps, a.ld);
+      // (cut fp32 LayerNorm rows keep to 2 vectors per lane: 4 would spill)
+      if constexpr (Elem<T>::kVec * 4 <= 16 && !(SHIFT && KIND == kNormLayer)) {
+        norm_regs_kernel<T, 4, KIND, WAVE, SHIFT><<<grid1(grid), b, 0, s>>>(yy, rr_, xx, gg, bb, a.M, a.N, a.eps, a.ld);
         break;
       }
       return hipErrorInvalidValue;
@@ -1646,8 +1858,13 @@ hipError_t norm_any(const rr_plan& p, const NormArgs& a, int64_t grid, hipStream
     if (p.vec_elems == 1) return norm_sub<T, 1, KIND>(p, a, grid, s);
     return norm_sub<T, Elem<T>::kVec, KIND>(p, a, grid, s);
   }
-  if (p.variant == RR_VARIANT_WAVE) return norm_regs<T, KIND, true>(p, a, grid, s);
-  return norm_regs<T, KIND, false>(p, a, grid, s);
+  if (p.row_shift) {
+    if (p.variant == RR_VARIANT_WAVE) return norm_regs<T, KIND, true, true>(p, a, grid, s);
+    if (p.variant == RR_VARIANT_BLOCK) return norm_regs<T, KIND, false, true>(p, a, grid, s);
+    return hipErrorInvalidValue;   // the planner cuts norm rows for these two only
+  }
+  if (p.variant == RR_VARIANT_WAVE) return norm_regs<T, KIND, true, false>(p, a, grid, s);
+  return norm_regs<T, KIND, false, false>(p, a, grid, s);
 }
 
 template <typename T>

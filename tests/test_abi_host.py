@@ -356,9 +356,21 @@ def test_dispatch_boundaries():
     p = sh(4, 200003, B, F, op=rr.RR_OP_SOFTMAX_CAUSAL)
     assert (p["variant_name"], p["vec_elems"], p["row_shift"], p["workspace_bytes"]) == ("loop", 4, 1, 0), p
     assert v(S, 10, 1024, al=False) == "loop" and sh(10, 1024, al=False)["row_shift"] == 0
-    # the norms' gamma lies in a frame of its own: unaligned norm rows stream
-    assert v(rr.RR_OP_RMSNORM, 10, 4100, B, B) == "loop"   # 4100 % 8 != 0
-    assert sh(10, 4100, B, B, op=rr.RR_OP_RMSNORM)["row_shift"] == 0
+    # norm rows that are not whole aligned vectors: cut at aligned addresses
+    # in the register kernels (gamma read in each row's frame); longer ones
+    # stream element by element
+    for op in (rr.RR_OP_RMSNORM, rr.RR_OP_FUSED_ADD_RMSNORM, rr.RR_OP_LAYERNORM):
+        for al in (True, 2):
+            p = sh(10, 4100, B, B, al, op)                 # 4100 % 8 != 0
+            assert (p["variant_name"], p["row_shift"], p["vec_elems"]) == ("block", 1, 8), p
+        p = sh(4096, 1021, F, F, 2, op)
+        # (an fp32 LayerNorm keeps to 2 vectors per lane on cut rows)
+        want = "block" if op == rr.RR_OP_LAYERNORM else "wave"
+        assert (p["variant_name"], p["row_shift"], p["vec_elems"]) == (want, 1, 4), p
+        assert op != rr.RR_OP_LAYERNORM or p["vecs_per_lane"] <= 2, p
+        p = sh(10, 20001, F, F, 2, op)                      # past the register budget
+        assert (p["variant_name"], p["row_shift"], p["vec_elems"]) == ("loop", 0, 1), p
+    assert v(rr.RR_OP_RMSNORM, 10, 4100, B, B, al=False) == "loop"
 
 
 def test_forced_variants():
@@ -430,11 +442,14 @@ def test_every_plan_covers_its_row():
                     width = 4
                 shift = p["row_shift"]
                 if shift:
-                    # rows cut at aligned addresses: softmax only, held by a
-                    # wavefront or workgroup, room for the worst lead (vec - 1)
-                    assert op in (rr.RR_OP_SOFTMAX, rr.RR_OP_SOFTMAX_CAUSAL) and vec == width, p
+                    # rows cut at aligned addresses, room for the worst lead
+                    # (vec - 1); the norms only in the register kernels
+                    assert vec == width, p
                     assert aligned == 2 or (aligned == 1 and N % width != 0), p
                     assert name in ("wave", "block", "split", "loop"), p
+                    if op not in (rr.RR_OP_SOFTMAX, rr.RR_OP_SOFTMAX_CAUSAL):
+                        assert name in ("wave", "block") and nv * vec <= 16, p
+                        assert not (op == rr.RR_OP_LAYERNORM and vec == 4 and nv > 2), p
                     if name == "loop":
                         pass                                  # streams any length
                     elif name == "split":

@@ -100,6 +100,9 @@ NORM_CASES = [
     ("layer", F32, 257, 5120, "block"),
     ("layer", BF16, 100, 20480, "block"),
     ("layer", BF16, 64, 70000, "loop"),
+    ("rms", BF16, 257, 4097, "block"),      # rows cut at aligned addresses (every lead)
+    ("fused", BF16, 100, 4097, "block"),
+    ("layer", F32, 100, 5121, "block"),
 ]
 
 

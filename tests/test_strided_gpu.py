@@ -209,3 +209,69 @@ def test_bf16_to_f32_softmax_on_8_byte_aligned_rows_is_the_aligned_call_bitwise(
         xf = compare.to_f64(x_cpu)
         compare.check_softmax(y.cpu(), xf, oracle.softmax(xf), f"8-byte rows {M}x{N}")
         untouched(buf, 4, N, "input")
+
+
+# (M, N, ld, col, gamma_col): rows cut at aligned addresses.  x, y and the
+# residual each sit in an [M, ld] buffer at column `col` (one offset within a
+# vector for all three); gamma is aligned (gamma_col None: read element by
+# element in each row's frame) or a slice at gamma_col (= col: read whole)
+CUT_NORM_CASES = [
+    (66, 33, 33, 0, None),          # contiguous rows of an odd width: every lead
+    (7, 1021, 1021, 0, None),
+    (66, 4097, 4097, 0, None),
+    (9, 4096, 4101, 3, None),       # a column slice: lead 3 on every row
+    (9, 4096, 4101, 3, 3),          # gamma at the rows' offset
+    (5, 16377, 16377, 0, None),     # the longest rows a workgroup holds at any lead
+    (3, 20001, 20001, 0, None),     # longer: element by element
+]
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("case", CUT_NORM_CASES, ids=lambda c: "x".join(map(str, c)))
+def test_norm_rows_cut_at_aligned_addresses(case, dt):
+    rr = _rr()
+    M, N, ld, col, gcol = case
+    code = rr.RR_F32 if dt == "f32" else rr.RR_BF16
+    cut = N <= 16377 and N > 32
+    _say(f"cut norm rows {dt} {case}")
+    for op in (rr.RR_OP_RMSNORM, rr.RR_OP_FUSED_ADD_RMSNORM, rr.RR_OP_LAYERNORM):
+        p = rr.rr_query_plan(op, M, N, code, code, 2)
+        # (an fp32 LayerNorm cuts rows up to 2 vectors per lane: 8189 elements)
+        want = cut and not (op == rr.RR_OP_LAYERNORM and dt == "f32" and N > 8189)
+        assert p["row_shift"] == (1 if want else 0), (op, p)
+    x_np = workloads.random_rows(M, N, seed=M + N + col)
+    x_np[::3, 0] = 1.0e3                       # LayerNorm rows whose first element is far from the mean
+    x_cpu = _as(x_np, dt)
+    r_cpu = _as(workloads.random_rows(M, N, seed=2 * M + N), dt)
+    g_cpu = _as(workloads.gamma_vector(N, seed=N), dt)
+    b_cpu = _as(workloads.gamma_vector(N, seed=N + 1) - 1.0, dt)
+    if gcol is None:
+        gd, bd = g_cpu.cuda(), b_cpu.cuda()
+    else:
+        G = torch.full((N + gcol,), SENTINEL, dtype=_tdt(dt), device="cuda")
+        Bt = torch.full((N + gcol,), SENTINEL, dtype=_tdt(dt), device="cuda")
+        G[gcol:] = g_cpu.cuda()
+        Bt[gcol:] = b_cpu.cuda()
+        gd, bd = G[gcol:], Bt[gcol:]
+    xbuf, xv = embed(x_cpu, ld, col)
+    ybuf, yv = embed(torch.zeros(M, N, dtype=_tdt(dt)), ld, col)
+    rr.rr_rmsnorm_strided(yv, xv, gd, 1e-6)
+    torch.cuda.synchronize()
+    check_norm(x_cpu, g_cpu, 1e-6, dt, yv.cpu(), f"cut rms {dt} {case}")
+    untouched(ybuf, col, N, "cut rms y")
+    for beta in (bd, None):
+        rr.rr_layernorm_strided(yv, xv, gd, beta, 1e-5)
+        torch.cuda.synchronize()
+        bref = compare.to_f64(b_cpu) if beta is not None else np.zeros(N)
+        ref = oracle.layernorm(compare.to_f64(x_cpu), compare.to_f64(g_cpu), bref, 1e-5)
+        compare.check_layernorm(yv.cpu(), ref, compare.to_f64(g_cpu), bref,
+                                f"cut layernorm {dt} {case} beta={beta is not None}")
+        untouched(ybuf, col, N, "cut layernorm y")
+    rbuf, rv = embed(r_cpu, ld, col)
+    ybuf2, yv2 = embed(torch.zeros(M, N, dtype=_tdt(dt)), ld, col)
+    rr.rr_fused_add_rmsnorm_strided(yv2, rv, xv, gd, 1e-6)
+    torch.cuda.synchronize()
+    check_fused(x_cpu, r_cpu, g_cpu, 1e-6, dt, yv2.cpu(), rv.cpu(), f"cut fused {dt} {case}")
+    untouched(rbuf, col, N, "cut fused residual")
+    untouched(ybuf2, col, N, "cut fused y")
+    untouched(xbuf, col, N, "cut x")
