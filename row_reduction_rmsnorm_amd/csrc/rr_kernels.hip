@@ -229,6 +229,27 @@ __device__ __forceinline__ int row_lead(const T* row_start, int vec) {
   return (int)((reinterpret_cast<uintptr_t>(row_start) / sizeof(T)) % (uintptr_t)vec);
 }
 
+// The frame of a cut row that is written: lead = the output row start's
+// element offset within its 64-byte block, so that every wavefront's stores
+// fill whole 64-byte sectors (stores that cover part of a sector, from two
+// wavefronts, measured ~15% slower over a launch: 256 x 50256 bf16 -> fp32
+// rows 32 bytes past a block 23.1 us, on block starts 20.1 us).  Vectors that
+// lie wholly before the row start are empty.  The input row starts at the
+// same element offset within a vector (checked by the host), so its vectors
+// stay aligned.  The host sizes plans for the vector frame (a lead below one
+// vector); a kernel that holds the row in `cap` vectors takes the 64-byte
+// frame only where the row still fits, else the vector frame of the input.
+template <typename Tout>
+__device__ __forceinline__ int frame_lead(const Tout* out_row) {
+  return (int)((reinterpret_cast<uintptr_t>(out_row) % 64u) / sizeof(Tout));
+}
+template <typename Tin, typename Tout>
+__device__ __forceinline__ int frame_lead_within(const Tin* in_row, const Tout* out_row, int vec, int n,
+                                                 int cap) {
+  const int lead = frame_lead(out_row);
+  return (lead + n + vec - 1) / vec <= cap ? lead : row_lead(in_row, vec);
+}
+
 // The elements e0 + i of a vector that lie in [0, keys), the rest `fill`
 // (-inf for a softmax, 0 for the norms); keys >= 1.  Every element's load is
 // issued before any is used: an index outside [0, keys) reads the nearest
@@ -421,7 +442,7 @@ __global__ __launch_bounds__(1024) void norm_regs_kernel(T* y, T* residual, cons
     const int64_t ox = row * ld.x, oy = row * ld.y, orr = row * ld.r;
     float h[NV][VEC];
     // SHIFT: the row's frame (without SHIFT lead is 0 and nvec_row nvec)
-    const int lead = SHIFT ? row_lead(x + ox, VEC) : 0;
+    const int lead = SHIFT ? frame_lead_within(x + ox, y + oy, VEC, N, NV * rl.T) : 0;
     const int nvec_row = SHIFT ? (lead + N + VEC - 1) / VEC : nvec;
     // y's vector k of this lane (and, SHIFT, the row's partial vectors)
     auto store_row = [&](T* base, int k, const float (&o)[VEC]) {
@@ -544,22 +565,24 @@ __global__ __launch_bounds__(1024) void norm_regs_kernel(T* y, T* residual, cons
           }
         }
       }
-      // the row's first vector (lane 0, k = 0) and last vector, if partial
+      // the row's first vector (vector lead / VEC, k = 0; those before it are
+      // empty) and last vector, if partial
       auto partial = [&](int vi) {
         const int e0 = vi * VEC - lead;
         return vi < nvec_row && !(e0 >= 0 && e0 + VEC <= N);
       };
       const int last = nvec_row - 1;
-      if (rl.t == 0 && partial(0)) {
+      const int first = lead / VEC;
+      if (rl.t == first && partial(first)) {
         float f[VEC];
-        load_edge<T, VEC>(x + ox, -lead, N, f, 0.0f);
+        load_edge<T, VEC>(x + ox, first * VEC - lead, N, f, 0.0f);
         px[0].set(f);
         if constexpr (KIND == kNormFused) {
-          load_edge<T, VEC>(residual + orr, -lead, N, f, 0.0f);
+          load_edge<T, VEC>(residual + orr, first * VEC - lead, N, f, 0.0f);
           pr[0].set(f);
         }
       }
-      if (last > 0 && rl.t == last % rl.T && partial(last)) {
+      if (last > first && rl.t == last % rl.T && partial(last)) {
         const int kl = last / rl.T;
         float f[VEC], g[VEC];
         load_edge<T, VEC>(x + ox, last * VEC - lead, N, f, 0.0f);
@@ -1125,7 +1148,7 @@ __global__ __launch_bounds__(1024) void softmax_regs_kernel(const Tin* x, Tout* 
     const Tin* xr = x + row * ld.x;
     Tout* yr = y + row * ld.y;
     // SHIFT: vector j covers the row's elements [j * VEC - lead, ...)
-    const int lead = SHIFT ? row_lead(xr, VEC) : 0;
+    const int lead = SHIFT ? frame_lead_within(xr, yr, VEC, N, NV * rl.T) : 0;
     const int nvec_row = SHIFT ? (lead + N + VEC - 1) / VEC : nvec;
     const int nvec_keys = (lead + keys + VEC - 1) / VEC;   // vectors holding kept keys
     float v[NV][VEC];
@@ -1259,7 +1282,7 @@ __global__ __launch_bounds__(1024) void softmax_packed_kernel(const Tin* x, Tout
     const Tin* xr = x + row * ld.x;   // uniform row bases
     Tout* yr = y + row * ld.y;
     // SHIFT: vector j covers the row's elements [j * VEC - lead, ...)
-    const int lead = SHIFT ? row_lead(xr, VEC) : 0;
+    const int lead = SHIFT ? frame_lead_within(xr, yr, VEC, N, NV * kThreads) : 0;
     const int nvec_row = SHIFT ? (lead + N + VEC - 1) / VEC : nvec;
     const int nvec_keys = (lead + keys + VEC - 1) / VEC;
     // the lane's vector offsets are recomputed at each use rather than kept
@@ -1284,13 +1307,14 @@ __global__ __launch_bounds__(1024) void softmax_packed_kernel(const Tin* x, Tout
         const int e0 = vi * VEC - lead;
         return vi < nvec_keys && !(e0 >= 0 && e0 + VEC <= N);
       };
-      if (t_ld == 0 && partial(0)) {
+      const int first = lead / VEC;     // vectors before it are empty
+      if (t_ld == first && partial(first)) {
         float f[VEC];
-        load_edge<Tin, VEC>(xr, -lead, keys, f);
+        load_edge<Tin, VEC>(xr, first * VEC - lead, keys, f);
         v[0].set(f);
       }
       const int last = nvec_row - 1;
-      if (last > 0 && t_ld == last % kThreads && partial(last)) {
+      if (last > first && t_ld == last % kThreads && partial(last)) {
         float f[VEC];
         load_edge<Tin, VEC>(xr, last * VEC - lead, keys, f);
         const int kl = last / kThreads;
@@ -1372,7 +1396,7 @@ __global__ __launch_bounds__(1024) void softmax_loop_kernel(const Tin* x, Tout* 
     Tout* yr = y + row * ld.y;
     // SHIFT: vector j covers the row's elements [j * VEC - lead, ...); the
     // first and last vector are accessed element by element
-    const int lead = SHIFT ? row_lead(xr, VEC) : 0;
+    const int lead = SHIFT ? frame_lead(yr) : 0;
     const int nvec_row = (lead + N + VEC - 1) / VEC;
     const int nvec_keys = (lead + keys + VEC - 1) / VEC;
     auto whole = [&](int e0) { return !SHIFT || (e0 >= 0 && e0 + VEC <= N); };
@@ -1454,7 +1478,7 @@ __global__ __launch_bounds__(256) void softmax_split_stats_kernel(const Tin* x, 
     const int c = (int)(item - row * S);
     const Tin* xr = x + row * ld.x;
     // SHIFT: vector j covers the row's elements [j * VEC - lead, ...)
-    const int lead = SHIFT ? row_lead(xr, VEC) : 0;
+    const int lead = SHIFT ? row_lead(xr, VEC) : 0;   // (its own frame: it writes no row)
     const int nvec_row = SHIFT ? (lead + N + VEC - 1) / VEC : nvec;
     Packed<Tin, VEC> v[NV];
 #pragma unroll
@@ -1557,7 +1581,7 @@ __global__ __launch_bounds__(256) void softmax_split_apply_kernel(const Tin* x, 
     const int c = (int)(item - row * SB);
     const Tin* xr = x + row * ld.x;
     Tout* yr = y + row * ld.y;
-    const int lead = SHIFT ? row_lead(xr, VEC) : 0;
+    const int lead = SHIFT ? frame_lead(yr) : 0;
     const int nvec_row = SHIFT ? (lead + N + VEC - 1) / VEC : nvec;
     Packed<Tin, VEC> v[NV];
 #pragma unroll
@@ -2009,8 +2033,9 @@ hipError_t softmax_split(const rr_plan& p, const SmCall<Tin, Tout>& c, SplitSlot
   }
   // pass B in chunks of its own size
   constexpr int VEC = softmax_vec<Tin, Tout>();
-  // vectors a row spans (SHIFT: up to one more, for a row starting inside one)
-  const int nvec = SHIFT ? (c.N + 2 * VEC - 2) / VEC : c.N / VEC;
+  // vectors a row spans (SHIFT: with a lead of up to a 64-byte block of y)
+  constexpr int kLeadMax = 64 / (int)sizeof(Tout) - 1;
+  const int nvec = SHIFT ? (c.N + kLeadMax + VEC - 1) / VEC : c.N / VEC;
   const int SB = (nvec + 256 * kSplitApplyNV - 1) / (256 * kSplitApplyNV);
   const int64_t items_b = c.M * (int64_t)SB;
   const int64_t grid_b = grid < c.M * (int64_t)S ? (grid < items_b ? grid : items_b) : items_b;
