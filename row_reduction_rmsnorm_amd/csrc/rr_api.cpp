@@ -183,6 +183,11 @@ int64_t packed_min_rows(int din, int dout) {
   if (din == RR_F32) return 40;
   return dout == RR_F32 ? 56 : 80;
 }
+// Rows cut at aligned addresses cost the packed kernel more than the split
+// (its row's partial vectors, one row per CU): the crossovers move up by
+// about 16 rows (measured cold on 50257-152065-wide rows: fp32 54-60,
+// bf16 -> fp32 68-88, bf16 -> bf16 92-100).
+constexpr int64_t kCutPackedExtraRows = 16;
 bool plan_packed(rr_op op, rr_plan* p, int vec, int per16, int64_t nvec) {
   if (op != RR_OP_SOFTMAX) return false;
   for (int nv16 : kPackedNV) {
@@ -324,7 +329,8 @@ rr_status make_plan(rr_op op, int64_t M, int64_t N, int din, int dout, int align
   switch (forced) {
     case RR_VARIANT_AUTO:
       if (plan_sub(p, vec, nvec)) {
-      } else if (shiftable && plan_shifted(op, causal, M, packed_rows, p, vw, per16_s, nvec_s, nvec_any)) {
+      } else if (shiftable && plan_shifted(op, causal, M, packed_rows + kCutPackedExtraRows, p, vw, per16_s,
+                                           nvec_s, nvec_any)) {
       } else if (vec == 1) {
         plan_loop(p, vec, nvec);
       } else if (wave_fits(op, vec, nvec)) {

@@ -326,8 +326,8 @@ def test_dispatch_boundaries():
     # starts at a common offset, room for a lead of up to vec - 1 elements)
     for M, N, a, b, name, nv1, nv2 in ((10, 33, F, F, "wave", 1, 1), (10, 1023, F, F, "wave", 4, 8),
                                        (16384, 1025, F, F, "wave", 8, 8), (8192, 4097, F, F, "block", 2, 2),
-                                       (256, 50257, B, F, "block", 24, 24), (80, 50257, B, B, "block", 12, 12),
-                                       (40, 50257, F, B, "block", 16, 16)):
+                                       (256, 50257, B, F, "block", 24, 24), (96, 50257, B, B, "block", 12, 12),
+                                       (56, 50257, F, B, "block", 16, 16)):
         for al, nv in ((True, nv1), (2, nv2)):
             p = sh(M, N, a, b, al)
             assert (p["variant_name"], p["vecs_per_lane"], p["row_shift"]) == (name, nv, 1), (M, N, al, p)
@@ -349,6 +349,9 @@ def test_dispatch_boundaries():
             assert rr.rr_softmax_rows_workspace_bytes(M, N, a, b) == M * chunks * 16
     assert rr.rr_query_plan(S, 4, 65536, F, F)["chunks_per_row"] == 16   # aligned rows: one chunk fewer
     assert sh(4, 50257, op=rr.RR_OP_SOFTMAX_CAUSAL)["variant_name"] == "block"
+    # cut rows hand over to the packed kernel 16 rows later than aligned ones
+    assert sh(71, 50257, B, F)["variant_name"] == "split" and sh(72, 50257, B, F)["variant_name"] == "block"
+    assert v(S, 56, 50256, B, F) == "block"
     # too long to hold with 1024 rows or more (or a causal call): the
     # streaming kernel, cut the same way; element access requested: scalar
     p = sh(1024, 81925)
