@@ -220,8 +220,9 @@ __device__ __forceinline__ void mask_keys(float (&v)[VEC], int e0, int keys) {
 // that input and output rows share their offset within a vector): row r is
 // cut into vectors at aligned addresses, so vector j covers the row's
 // elements [j * VEC - lead, (j + 1) * VEC - lead), lead = the row start's
-// element offset within its vector.  Vectors inside the row are accessed
-// whole; the first and last may reach outside it, and only their elements
+// element offset within its vector (row_lead), or within the output's 64-byte
+// block (frame_lead, below).  Vectors inside the row are accessed whole; the
+// partial ones at its ends may reach outside it, and only their elements
 // inside the row are accessed, one at a time (nothing outside the row is
 // ever read or written).
 template <typename T>
@@ -394,13 +395,15 @@ __device__ __forceinline__ void window_cut(int lp, int e, const Packed<T, VEC>& 
 // correctly rounded sum.
 //
 // SHIFT: rows cut at aligned addresses.  x, y (and the residual) rows start
-// at the same element offset `lead` within a vector (the host checks it);
-// vector j covers the row's elements [j * VEC - lead, (j + 1) * VEC - lead).
-// Whole vectors inside the row are accessed whole, the row's first and last
-// vector element by element (0 outside the row), and gamma (beta), which lie
-// in a frame of their own, are read for each row in the row's frame:
-// whole vectors when gamma starts at the row's offset, else element by
-// element (they stay in the cache across rows).
+// at the same element offset within a vector (the host checks it); vector j
+// covers the row's elements [j * VEC - lead, (j + 1) * VEC - lead), the frame
+// starting at y's 64-byte block where the row still fits (frame_lead_within).
+// Whole vectors inside the row are accessed whole, the row's partial vectors
+// element by element (0 outside the row), and gamma (beta), which lie in a
+// frame of their own, are read for each row in the row's frame: each lane's
+// window is cut out of the two aligned blocks that hold it (window_blocks,
+// window_cut; they stay in the cache across rows), element by element where
+// those blocks would reach outside gamma.
 // ===========================================================================
 template <typename T, int NV, int KIND, bool WAVE, bool SHIFT>
 __global__ __launch_bounds__(1024) void norm_regs_kernel(T* y, T* residual, const T* x,
