@@ -275,3 +275,46 @@ def test_norm_rows_cut_at_aligned_addresses(case, dt):
     untouched(rbuf, col, N, "cut fused residual")
     untouched(ybuf2, col, N, "cut fused y")
     untouched(xbuf, col, N, "cut x")
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_cut_rows_different_strides_and_in_place(dt):
+    """Rows cut at aligned addresses with x and y in buffers of different
+    strides (equal modulo the vector width, same column), and in place (y is
+    x): the norms, the fused op writing y over x, and the softmax."""
+    rr = _rr()
+    code = rr.RR_F32 if dt == "f32" else rr.RR_BF16
+    M, N, col = 9, 4093, 3
+    ldx, ldy = N + 8, N + 24                      # both equal to N mod 8
+    _say(f"cut rows, strides {ldx}/{ldy}, in place, {dt}")
+    x_cpu = _as(workloads.random_rows(M, N, seed=N + 11), dt)
+    r_cpu = _as(workloads.random_rows(M, N, seed=N + 12), dt)
+    g_cpu = _as(workloads.gamma_vector(N, seed=N + 13), dt)
+    assert rr.rr_query_plan(rr.RR_OP_RMSNORM, M, N, code, code, 2)["row_shift"] == 1
+    xbuf, xv = embed(x_cpu, ldx, col)
+    ybuf, yv = embed(torch.zeros(M, N, dtype=_tdt(dt)), ldy, col)
+    rr.rr_rmsnorm_strided(yv, xv, g_cpu.cuda(), 1e-6)
+    torch.cuda.synchronize()
+    check_norm(x_cpu, g_cpu, 1e-6, dt, yv.cpu(), f"cut rms strides {dt}")
+    untouched(ybuf, col, N, "cut rms y (other stride)")
+    # in place: y is x
+    ibuf, iv = embed(x_cpu, ldx, col)
+    rr.rr_rmsnorm_strided(iv, iv, g_cpu.cuda(), 1e-6)
+    torch.cuda.synchronize()
+    check_norm(x_cpu, g_cpu, 1e-6, dt, iv.cpu(), f"cut rms in place {dt}")
+    untouched(ibuf, col, N, "cut rms in place")
+    # fused, y written over x, residual at a third stride
+    fbuf, fv = embed(x_cpu, ldx, col)
+    rbuf, rv = embed(r_cpu, N + 16, col)
+    rr.rr_fused_add_rmsnorm_strided(fv, rv, fv, g_cpu.cuda(), 1e-6)
+    torch.cuda.synchronize()
+    check_fused(x_cpu, r_cpu, g_cpu, 1e-6, dt, fv.cpu(), rv.cpu(), f"cut fused in place {dt}")
+    untouched(fbuf, col, N, "cut fused y/x")
+    untouched(rbuf, col, N, "cut fused residual")
+    # softmax in place on contiguous rows of an odd width
+    s_cpu = softmax_input(M, N, seed=N + 14, dt=dt)
+    sd = s_cpu.cuda()
+    rr.rr_softmax_rows(sd, sd, None)
+    torch.cuda.synchronize()
+    xf = compare.to_f64(s_cpu)
+    compare.check_softmax(sd.cpu(), xf, oracle.softmax(xf), f"cut softmax in place {dt}")
