@@ -79,3 +79,53 @@ def test_graph_replays_match_eager():
         for got, want, what in zip((y, res, sy, cy), ref, ("fused y", "residual", "split softmax", "causal log")):
             assert torch.equal(_bits(got), _bits(want)), f"replay {k}: {what}"
         torch.cuda.synchronize()
+
+
+def test_graph_replays_of_cut_rows_match_eager():
+    """The cut-row kernels captured: a softmax of few odd-width rows (the
+    split, with its workspace), a packed one, and a LayerNorm over rows of an
+    odd width, replayed on changed inputs and checked bitwise against eager
+    calls."""
+    rr = _rr()
+    s1 = softmax_input(4, 152065, seed=21, dt="bf16").cuda()         # split, rows cut at aligned addresses
+    y1 = torch.empty(s1.shape, dtype=torch.float32, device="cuda")
+    ws = rr.softmax_workspace(s1, torch.float32)
+    s2 = softmax_input(256, 50257, seed=22, dt="bf16").cuda()        # packed, cut
+    y2 = torch.empty(s2.shape, dtype=torch.float32, device="cuda")
+    M, H = 100, 4097
+    x = _as(workloads.random_rows(M, H, seed=23), "bf16").cuda()
+    g = _as(workloads.gamma_vector(H, seed=24), "bf16").cuda()
+    b = _as(workloads.gamma_vector(H, seed=25) - 1.0, "bf16").cuda()
+    y3 = torch.empty_like(x)
+    for t, N in ((s1, 152065), (s2, 50257)):
+        assert rr.rr_query_plan(rr.RR_OP_SOFTMAX, t.shape[0], N, rr.RR_BF16, rr.RR_F32, 2)["row_shift"] == 1
+    assert rr.rr_query_plan(rr.RR_OP_LAYERNORM, M, H, rr.RR_BF16, rr.RR_BF16, 2)["row_shift"] == 1
+
+    def step():
+        rr.rr_softmax_rows(y1, s1, ws)
+        rr.rr_softmax_rows(y2, s2, None)
+        rr.rr_layernorm(y3, x, g, b, 1e-5)
+
+    def eager_reference():
+        step()
+        torch.cuda.synchronize()
+        return (y1.clone(), y2.clone(), y3.clone())
+
+    step()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    torch.cuda.synchronize()
+    for k in range(4):
+        _say(f"cut-row graph replay {k}")
+        s1.mul_(0.5)
+        s2.add_(0.25)
+        x.copy_(_as(workloads.random_rows(M, H, seed=30 + k), "bf16").cuda())
+        ref = eager_reference()
+        for t in (y1, y2, y3):
+            t.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        for got, want, what in zip((y1, y2, y3), ref, ("cut split softmax", "cut packed softmax", "cut layernorm")):
+            assert torch.equal(_bits(got), _bits(want)), f"replay {k}: {what}"
