@@ -335,6 +335,14 @@ rr_status make_plan(rr_op op, int64_t M, int64_t N, int din, int dout, int align
         plan_loop(p, vec, nvec);
       } else if (wave_fits(op, vec, nvec)) {
         plan_wave(p, vec, nvec);
+        // a softmax written as fp32 with many rows: workgroups of lanes that
+        // hold 2 vectors beat a wavefront holding 8 from 16384 rows up, and
+        // one holding 4 from 65536 rows up (cold; bf16 -> fp32 65536 x 2048:
+        // 134.9 -> 127.9 us, 131072 x 1024: 140.3 -> 128.4; fp32 65536 x
+        // 2048: 179.7 -> 171.9)
+        if (op == RR_OP_SOFTMAX && dout == RR_F32 &&
+            ((p->vecs_per_lane == 8 && M >= 16384) || (p->vecs_per_lane == 4 && M >= 65536)))
+          plan_block(op, p, vec, nvec);
       } else if (plan_block(op, p, vec, nvec)) {
       } else if (plan_norm_packed(op, p, vec, nvec)) {
       } else if ((M >= packed_rows || causal) && plan_packed(op, p, vec, per16, nvec)) {

@@ -309,6 +309,12 @@ def test_dispatch_boundaries():
     assert v(S, 1024, 163840, B, B) == "block"
     assert v(S, 1024, 163848, B, F) == "loop"
     assert v(S, 1023, 163848, B, F) == "split"
+    # many rows written as fp32: workgroups of 2-vector lanes instead of a
+    # wavefront holding 8 vectors (from 16384 rows) or 4 (from 65536 rows)
+    assert v(S, 16383, 2048) == "wave" and v(S, 16384, 2048) == "block"
+    assert rr.rr_query_plan(S, 16384, 2048, F, F)["vecs_per_lane"] == 2
+    assert v(S, 65535, 1024, B, F) == "wave" and v(S, 65536, 1024, B, F) == "block"
+    assert v(S, 16384, 1024) == "wave" and v(S, 131072, 2048, B, B) == "wave"
     # short rows: several rows per wavefront, L lanes per row
     assert v(S, 10, 128) == "subwave" and rr.rr_query_plan(S, 10, 128, F, F)["waves_per_row"] == 32
     assert v(S, 10, 132) == "wave"
