@@ -334,6 +334,19 @@ def measure_extras(torch, rr, dev, K, bufs):
     lg = rr.make_softmax_opts(log_output=True)
     timed("log_softmax_bf16_f32_256x152064",
           lambda: rr.rr_softmax_rows_ex(b["y"], b["x"], lg, b["ws"]), b["M"] * b["N"] * (2 + 4), b["M"])
+    # rows that are not whole vectors (contiguous rows of an odd width, every
+    # row at its own offset): cut at aligned addresses
+    M, N = 256, 50257                     # a 50257-entry vocabulary
+    x = workloads.to_dtype(rng.standard_normal((M, N), dtype=np.float32), "bf16").to(dev)
+    y = torch.empty((M, N), dtype=torch.float32, device=dev)
+    timed("softmax_bf16_f32_256x50257_rows_cut", lambda: rr.rr_softmax_rows(y, x, None), M * N * (2 + 4), M)
+    del x, y
+    M, N = 8192, 4097
+    x = workloads.to_dtype(rng.standard_normal((M, N), dtype=np.float32), "bf16").to(dev)
+    g = workloads.to_dtype(workloads.gamma_vector(N, 3), "bf16").to(dev)
+    y = torch.empty_like(x)
+    timed("rmsnorm_bf16_8192x4097_rows_cut", lambda: rr.rr_rmsnorm(y, x, g, 1e-6), 2 * M * N * 2 + N * 2, M)
+    del x, g, y
     return out
 
 
