@@ -270,6 +270,30 @@ rr_status rr_softmax_rows_strided(void* y, int64_t ldy, const void* x, int64_t l
                                   const rr_softmax_opts* opts, void* workspace,
                                   size_t workspace_bytes, void* stream);
 
+/*
+ * rr_softmax_rows_strided_noalloc -- rr_softmax_rows_strided for callers
+ * that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc).  Same arguments, results
+ * (same kernels, same bits), aliasing rules and errors, but no workspace
+ * argument: a split row's (m, d) slots live in a static device array of
+ * 4 MiB (262144 slots of 16 bytes) that the library holds on each device it
+ * runs on until the process ends.  The call allocates nothing and calls no
+ * hipMalloc or hipFree; on its first call on a device it looks up that
+ * device's copy of the array (hipGetSymbolAddress), which must then be the
+ * current device.
+ *   - A shape whose split needs more than 4 MiB of slots
+ *     (rr_softmax_rows_ex_workspace_bytes > 4194304) returns
+ *     RR_ERR_WORKSPACE and enqueues nothing.
+ *   - Every call on a device shares that device's array, which keeps the
+ *     last call's contents: calls that overlap in time on one device (two
+ *     streams, or two threads) race and may produce wrong results; calls on
+ *     one stream are ordered and safe.  Nothing in the array needs to start
+ *     at zero.
+ */
+rr_status rr_softmax_rows_strided_noalloc(void* y, int64_t ldy, const void* x, int64_t ldx, int64_t M,
+                                          int64_t N, rr_dtype in_dtype, rr_dtype out_dtype,
+                                          const rr_softmax_opts* opts, void* stream);
+
 /* Static English name of a status code ("RR_OK", ...). */
 const char* rr_status_string(rr_status status);
 

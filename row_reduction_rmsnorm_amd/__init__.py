@@ -22,5 +22,5 @@ from .binding import (  # noqa: F401
     rr_softmax_rows_ex_workspace_bytes, softmax_rows_ex, raw_rmsnorm_strided,
     raw_fused_add_rmsnorm_strided, raw_layernorm_strided, raw_softmax_rows_strided,
     rr_rmsnorm_strided, rr_fused_add_rmsnorm_strided, rr_layernorm_strided,
-    rr_softmax_rows_strided,
+    rr_softmax_rows_strided, raw_softmax_rows_strided_noalloc, rr_softmax_rows_strided_noalloc,
 )

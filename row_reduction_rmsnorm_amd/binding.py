@@ -43,7 +43,7 @@ EXPORTS = (
     "rr_rmsnorm", "rr_fused_add_rmsnorm", "rr_layernorm", "rr_softmax_rows_workspace_bytes",
     "rr_softmax_rows", "rr_softmax_rows_ex_workspace_bytes", "rr_softmax_rows_ex",
     "rr_rmsnorm_strided", "rr_fused_add_rmsnorm_strided", "rr_layernorm_strided",
-    "rr_softmax_rows_strided",
+    "rr_softmax_rows_strided", "rr_softmax_rows_strided_noalloc",
     "rr_status_string", "rr_last_error_message", "rr_query_plan",
     "rr_set_variant_override", "rr_selftest_wave_allreduce", "rr_stream_copy",
 )
@@ -136,6 +136,7 @@ def load_library(path):
     L.rr_layernorm_strided.argtypes = [vp, i64, vp, i64, vp, vp, i64, i64, f32, i32, vp]
     L.rr_softmax_rows_strided.argtypes = [vp, i64, vp, i64, i64, i64, i32, i32, po, vp,
                                           ctypes.c_size_t, vp]
+    L.rr_softmax_rows_strided_noalloc.argtypes = [vp, i64, vp, i64, i64, i64, i32, i32, po, vp]
     L.rr_status_string.argtypes = [i32]
     L.rr_status_string.restype = ctypes.c_char_p
     L.rr_last_error_message.argtypes = []
@@ -147,7 +148,7 @@ def load_library(path):
     for f in ("rr_rmsnorm", "rr_fused_add_rmsnorm", "rr_layernorm", "rr_softmax_rows",
               "rr_softmax_rows_ex", "rr_query_plan", "rr_rmsnorm_strided",
               "rr_fused_add_rmsnorm_strided", "rr_layernorm_strided", "rr_softmax_rows_strided",
-              "rr_set_variant_override", "rr_selftest_wave_allreduce", "rr_stream_copy"):
+              "rr_softmax_rows_strided_noalloc", "rr_set_variant_override", "rr_selftest_wave_allreduce", "rr_stream_copy"):
         getattr(L, f).restype = i32
     return L
 
@@ -217,6 +218,11 @@ def raw_softmax_rows_strided(y, ldy, x, ldx, M, N, in_dtype, out_dtype, opts, wo
                              workspace_bytes, stream):
     return lib().rr_softmax_rows_strided(y, ldy, x, ldx, M, N, in_dtype, out_dtype, _opts_ref(opts),
                                          workspace, workspace_bytes, stream)
+
+
+def raw_softmax_rows_strided_noalloc(y, ldy, x, ldx, M, N, in_dtype, out_dtype, opts, stream):
+    return lib().rr_softmax_rows_strided_noalloc(y, ldy, x, ldx, M, N, in_dtype, out_dtype, _opts_ref(opts),
+                                                 stream)
 
 
 def rr_softmax_rows_ex_workspace_bytes(M: int, N: int, in_dtype: int, out_dtype: int, opts=None) -> int:
@@ -358,6 +364,18 @@ def rr_softmax_rows_strided(y, x, opts=None, workspace=None, stream=None) -> Non
     check(raw_softmax_rows_strided(y.data_ptr(), ldy, x.data_ptr(), ldx, M, N, dtype_code(x),
                                    dtype_code(y), opts, ws_ptr, ws_bytes, _stream_of(x, stream)),
           "rr_softmax_rows_strided")
+
+
+def rr_softmax_rows_strided_noalloc(y, x, opts=None, stream=None) -> None:
+    """rr_softmax_rows_strided with the split row's slots in the library's
+    static scratch array (no workspace, nothing allocated)."""
+    M, N, ldx = _rows_ld(x)
+    My, Ny, ldy = _rows_ld(y)
+    if (My, Ny) != (M, N):
+        raise ValueError("y must match x")
+    check(raw_softmax_rows_strided_noalloc(y.data_ptr(), ldy, x.data_ptr(), ldx, M, N, dtype_code(x),
+                                           dtype_code(y), opts, _stream_of(x, stream)),
+          "rr_softmax_rows_strided_noalloc")
 
 
 def rr_rmsnorm(y, x, gamma, eps: float, stream=None) -> None:

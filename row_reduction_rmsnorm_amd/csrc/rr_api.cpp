@@ -598,9 +598,11 @@ rr_status softmax_options(const rr_softmax_opts* o, const char* who, rr_softmax_
   return RR_OK;
 }
 
+// noalloc: the workspace comes from the library's static scratch array
+// (rr_softmax_rows_strided_noalloc); workspace and workspace_bytes are unused.
 rr_status softmax_entry(const char* who, void* y, int64_t ldy, const void* x, int64_t ldx, int64_t M,
                         int64_t N, rr_dtype in_dtype, rr_dtype out_dtype, const rr_softmax_opts* opts,
-                        void* workspace, size_t workspace_bytes, void* stream) {
+                        void* workspace, size_t workspace_bytes, void* stream, bool noalloc = false) {
   g_err[0] = '\0';
   if (!valid_dtype(in_dtype) || !valid_dtype(out_dtype))
     return fail(RR_ERR_INVALID_ARG, "%s: unknown dtype (%d, %d)", who, (int)in_dtype, (int)out_dtype);
@@ -642,7 +644,19 @@ rr_status softmax_entry(const char* who, void* y, int64_t ldy, const void* x, in
   const rr_status st = make_plan(o.causal ? RR_OP_SOFTMAX_CAUSAL : RR_OP_SOFTMAX, M, N, in_dtype,
                                  out_dtype, align, &p);
   if (st != RR_OK) return st;
-  if (p.workspace_bytes > 0) {
+  if (noalloc && p.workspace_bytes > 0) {
+    // the scratch array holds one call's slots; larger splits are refused
+    // before anything touches the device
+    if (p.workspace_bytes > rr::kNoAllocScratchBytes)
+      return fail(RR_ERR_WORKSPACE, "%s: this shape needs %zu bytes of split-row scratch; the static scratch holds %zu",
+                  who, p.workspace_bytes, rr::kNoAllocScratchBytes);
+    if (p.variant == RR_VARIANT_SPLIT_ONE_KERNEL)
+      return fail(RR_ERR_UNSUPPORTED, "%s: the one-kernel split is not available without a workspace", who);
+    hipError_t se = hipSuccess;
+    workspace = rr::noalloc_scratch(&se);
+    if (!workspace) return hip_status(se != hipSuccess ? se : hipErrorInvalidSymbol, who);
+    workspace_bytes = rr::kNoAllocScratchBytes;
+  } else if (p.workspace_bytes > 0) {
     if (!workspace || workspace_bytes < p.workspace_bytes)
       return fail(RR_ERR_WORKSPACE, "%s: needs a workspace of %zu bytes, got %zu", who,
                   p.workspace_bytes, workspace ? workspace_bytes : (size_t)0);
@@ -714,6 +728,13 @@ rr_status rr_softmax_rows_strided(void* y, int64_t ldy, const void* x, int64_t l
                                   size_t workspace_bytes, void* stream) {
   return softmax_entry("rr_softmax_rows_strided", y, ldy, x, ldx, M, N, in_dtype, out_dtype, opts,
                        workspace, workspace_bytes, stream);
+}
+
+rr_status rr_softmax_rows_strided_noalloc(void* y, int64_t ldy, const void* x, int64_t ldx, int64_t M,
+                                          int64_t N, rr_dtype in_dtype, rr_dtype out_dtype,
+                                          const rr_softmax_opts* opts, void* stream) {
+  return softmax_entry("rr_softmax_rows_strided_noalloc", y, ldy, x, ldx, M, N, in_dtype, out_dtype, opts,
+                       nullptr, 0, stream, true);
 }
 
 const char* rr_status_string(rr_status s) {

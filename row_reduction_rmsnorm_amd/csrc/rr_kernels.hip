@@ -2166,3 +2166,48 @@ hipError_t launch_stream_copy(void* dst, const void* src, int64_t bytes, hipStre
 }
 
 }  // namespace rr
+
+// ===========================================================================
+// Scratch of the no-allocation softmax entry point.  Callers that cannot
+// allocate device memory (code under HIP graph capture, tight serving loops)
+// get the split row's (m, d) slots from this array instead of a workspace
+// argument.  Its name is a host-side stand-in in host code: kernels are
+// given the device address that hipGetSymbolAddress returns for the device
+// that is current, looked up once per device and cached.  Every call on a
+// device shares that device's copy, so calls that overlap in time on one
+// device race; nothing in it needs to start at zero (the split's first
+// kernel writes every slot its second kernel reads).
+// ===========================================================================
+static __device__ __align__(256) unsigned char scratch[rr::kNoAllocScratchBytes];
+
+namespace rr {
+
+void* noalloc_scratch(hipError_t* err) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static std::atomic<void*> addr[kMaxDevices];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) {
+    *err = e;
+    return nullptr;
+  }
+  if (dev < 0 || dev >= kMaxDevices) {
+    *err = hipErrorInvalidDevice;
+    return nullptr;
+  }
+  void* p = addr[dev].load(std::memory_order_acquire);
+  if (p) return p;
+  std::lock_guard<std::mutex> lock(mu);
+  p = addr[dev].load(std::memory_order_relaxed);
+  if (p) return p;
+  e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+  if (e != hipSuccess || !p) {
+    *err = e != hipSuccess ? e : hipErrorInvalidSymbol;
+    return nullptr;
+  }
+  addr[dev].store(p, std::memory_order_release);
+  return p;
+}
+
+}  // namespace rr

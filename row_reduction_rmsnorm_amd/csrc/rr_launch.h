@@ -63,6 +63,16 @@ struct SoftmaxArgs {
 hipError_t launch_softmax(const rr_plan& plan, rr_dtype in_dtype, rr_dtype out_dtype,
                           const SoftmaxArgs& args, int64_t grid, hipStream_t stream);
 
+// Scratch memory of the no-allocation softmax entry point: a static device
+// array of this many bytes (each device the library runs on holds its own
+// copy until the process ends).  It holds the split row's (m, d) slots, 16
+// bytes per chunk, i.e. up to 262144 chunks per call.
+constexpr size_t kNoAllocScratchBytes = (size_t)4 << 20;
+
+// Device address of the current device's scratch array (looked up once per
+// device with hipGetSymbolAddress, then cached), or null with *err set.
+void* noalloc_scratch(hipError_t* err);
+
 // Enqueue the wave all-reduce self-test kernel.
 hipError_t launch_selftest_wave(const float* in, float* out, int64_t count, int kind,
                                 hipStream_t stream);

@@ -133,6 +133,20 @@ def test_softmax_validation():
     assert "workspace" in rr.last_error_message()
 
 
+def test_noalloc_refuses_a_split_beyond_its_scratch():
+    # 600 rows x 512 chunks x 16 bytes of (m, d) slots: more than the 4 MiB
+    # static scratch; refused before any device work (the addresses are fake)
+    M, N = 600, 1 << 21
+    assert rr.rr_softmax_rows_ex_workspace_bytes(M, N, rr.RR_F32, rr.RR_F32) > 4 << 20
+    f = rr.raw_softmax_rows_strided_noalloc
+    assert f(P << 12, N, P, N, M, N, rr.RR_F32, rr.RR_F32, None, None) == rr.RR_ERR_WORKSPACE
+    assert "scratch" in rr.last_error_message()
+    # the ordinary argument checks still come first
+    assert f(P << 12, N, P, N, M, 0, rr.RR_F32, rr.RR_F32, None, None) == rr.RR_ERR_INVALID_ARG
+    assert f(None, N, P, N, M, N, rr.RR_F32, rr.RR_F32, None, None) == rr.RR_ERR_INVALID_ARG
+    assert f(None, N, None, N, 0, N, rr.RR_F32, rr.RR_F32, None, None) == rr.RR_OK
+
+
 def test_softmax_ex_validation():
     X, Y, W = P, P << 4, P << 8
     F, B = rr.RR_F32, rr.RR_BF16
