@@ -58,10 +58,15 @@ def code_object_sha(lib_path=None):
     section (the gfx950 code objects), read without loading the library.
     Comments and host-only edits leave it unchanged; any kernel change
     changes it."""
-    import struct
     if lib_path is None:
         from row_reduction_rmsnorm_amd import binding
         lib_path = binding.LIB_PATH
+    return hashlib.sha256(fatbin_bytes(lib_path)).hexdigest()[:16]
+
+
+def fatbin_bytes(lib_path):
+    """The .hip_fatbin ELF section of a shared library (its offload bundles)."""
+    import struct
     with open(lib_path, "rb") as f:
         data = f.read()
     if data[:4] != b"\x7fELF" or data[4] != 2:
@@ -77,7 +82,7 @@ def code_object_sha(lib_path=None):
         name, _, _, _, off, size = section(i)
         end = data.index(b"\0", names + name)
         if data[names + name:end] == b".hip_fatbin":
-            return hashlib.sha256(data[off:off + size]).hexdigest()[:16]
+            return data[off:off + size]
     raise ValueError(f"{lib_path}: no .hip_fatbin section")
 
 
@@ -438,12 +443,15 @@ def main():
     ops = make_ops(rr, bufs)
 
     if args.calibrate_copy:
-        # a plain elementwise pass of known size (512 MiB read, 512 MiB written)
-        # whose kernel appears nowhere else in the run, for counter calibration
+        # the library's streaming copy (the diagnostics build) of a known size,
+        # 512 MiB read and 512 MiB written with the same 16-byte non-temporal
+        # accesses the kernels use, for counter calibration; its dispatches
+        # are told apart from the size-matched copies below by their grid
+        # (32768 workgroups of 1024 lanes)
         src = torch.ones(128 << 20, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
         for _ in range(3):
-            torch.neg(src, out=dst)
+            rr.rr_stream_copy(dst, src)
         torch.cuda.synchronize()
         del src, dst
 

@@ -171,7 +171,9 @@ size_t rr_softmax_rows_workspace_bytes(int64_t M, int64_t N, rr_dtype in_dtype,
  *              tagged per call); calls that overlap in time must not share
  *              a workspace
  * Masked entries produce exactly 0; a row whose entries are all -inf
- * produces NaN everywhere (-inf - (-inf)).  In place (y == x) is allowed
+ * produces NaN everywhere (-inf - (-inf)).  Probabilities below 2^-126
+ * come out as bf16 subnormals when out_dtype is RR_BF16, and as 0 when it
+ * is RR_F32 (an absolute error below 1.2e-38).  In place (y == x) is allowed
  * when in_dtype == out_dtype; otherwise x and y must not overlap.
  * Returns RR_ERR_WORKSPACE when the workspace is needed and missing or too
  * small; other errors as rr_rmsnorm.
@@ -373,43 +375,12 @@ typedef struct rr_plan {
  *      is not a whole number of vectors, column slices with equal strides):
  *      a softmax then cuts rows at aligned addresses (row_shift);
  *   0  neither: element-by-element access.
- * Honours the variant override below.  Returns RR_ERR_INVALID_ARG /
- * RR_ERR_UNSUPPORTED as the corresponding call would.
+ * Returns RR_ERR_INVALID_ARG / RR_ERR_UNSUPPORTED as the corresponding call
+ * would.  (The diagnostics build, rowreduce_diag.h, can force a variant; its
+ * plans then follow that override.)
  */
 rr_status rr_query_plan(rr_op op, int64_t M, int64_t N, rr_dtype in_dtype, rr_dtype out_dtype,
                         int aligned16, rr_plan* plan);
-
-/* Process-wide forced variant for tests and measurement (RR_VARIANT_AUTO
- * restores automatic choice).  A forced variant that cannot run a shape makes
- * that call return RR_ERR_UNSUPPORTED.  Not thread-safe with respect to calls
- * in flight on other threads. */
-rr_status rr_set_variant_override(rr_variant variant);
-
-/*
- * Self-test of the wave64 all-reduce (device work; used by the test suite).
- * kind 0: in and out hold count groups of 64 floats; every lane of a group
- * receives the group's sum.  kind 1: the same with the maximum.  kind 2: in
- * and out hold count groups of 128 floats, 64 m values then 64 d values;
- * every lane receives the merge of the group's 64 (m, d) pairs.  One
- * wavefront per group; 1 <= count <= (2^32 - 1) / 64.
- */
-rr_status rr_selftest_wave_allreduce(const float* in, float* out, int64_t count, int kind,
-                                     void* stream);
-
-/*
- * Streaming copy, a measurement reference rather than an operation of the
- * method: dst[0, bytes) <- src[0, bytes) with 16-byte non-temporal loads and
- * stores, one vector per lane, no dependency between elements.  An operation
- * that reads B/2 bytes and writes B/2 bytes moves the same HBM traffic as a
- * copy of B/2 bytes, so the copy's speed at that size is the practical
- * streaming bar to set the operation's speed beside (the fixed start-up and
- * drain of a launch are a visible share at a few hundred megabytes).
- *   dst, src  device pointers, 16-byte aligned, not overlapping
- *   bytes     >= 0, a multiple of 16 (0: no launch)
- * Returns RR_ERR_INVALID_ARG for a bad size, null or misaligned pointers, or
- * overlap; asynchronous on `stream` like every other call.
- */
-rr_status rr_stream_copy(void* dst, const void* src, int64_t bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -4,13 +4,21 @@ Argument marshalling only: every operation runs in the library's HIP kernels.
 PyTorch supplies device memory (tensors' data pointers) and the stream
 (``torch.cuda.current_stream().cuda_stream``).  There is no fallback: if the
 library is missing or cannot be loaded, importing it raises.
+
+The diagnostics build librowreduce_diag.so (include/rowreduce_diag.h: the
+same kernel object plus a forced variant, the all-reduce self-test and the
+streaming copy) is loaded only by ``diag_lib()``, ``forced_variant()``,
+``rr_selftest_wave_allreduce`` and ``rr_stream_copy``, for tests and
+measurement.
 """
+import contextlib
 import ctypes
 import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-# The in-tree build; ROWREDUCE_LIB may name another build of the same library.
+# The in-tree builds; ROWREDUCE_LIB may name another build of the library.
 LIB_PATH = os.environ.get("ROWREDUCE_LIB") or os.path.join(HERE, "librowreduce.so")
+DIAG_LIB_PATH = os.path.join(HERE, "librowreduce_diag.so")
 
 RR_F32 = 0
 RR_BF16 = 1
@@ -45,8 +53,9 @@ EXPORTS = (
     "rr_rmsnorm_strided", "rr_fused_add_rmsnorm_strided", "rr_layernorm_strided",
     "rr_softmax_rows_strided", "rr_softmax_rows_strided_noalloc",
     "rr_status_string", "rr_last_error_message", "rr_query_plan",
-    "rr_set_variant_override", "rr_selftest_wave_allreduce", "rr_stream_copy",
 )
+# What include/rowreduce_diag.h adds in the diagnostics build.
+DIAG_EXPORTS = ("rr_set_variant_override", "rr_selftest_wave_allreduce", "rr_stream_copy")
 
 
 class RowReduceError(RuntimeError):
@@ -96,11 +105,16 @@ class rr_plan(ctypes.Structure):
 
 
 _LIB = None
+_DIAG = None
+_ROUTED = None     # the diagnostics build while forced_variant() is active
 
 
 def lib():
-    """The loaded library (built in-tree on first use if it is not there)."""
+    """The loaded library (built in-tree on first use if it is not there);
+    inside forced_variant(), the diagnostics build."""
     global _LIB
+    if _ROUTED is not None:
+        return _ROUTED
     if _LIB is not None:
         return _LIB
     if not os.path.exists(LIB_PATH):
@@ -110,6 +124,39 @@ def lib():
         _build.build()
     _LIB = load_library(LIB_PATH)
     return _LIB
+
+
+def diag_lib():
+    """The diagnostics build (built in-tree on first use if it is not there)."""
+    global _DIAG
+    if _DIAG is not None:
+        return _DIAG
+    if not os.path.exists(DIAG_LIB_PATH):
+        from . import build as _build
+        _build.build()
+    _DIAG = load_library(DIAG_LIB_PATH)
+    return _DIAG
+
+
+@contextlib.contextmanager
+def forced_variant(variant: int):
+    """Run every call of this module inside the block through the
+    diagnostics build with `variant` (an rr_variant code) forced, then
+    restore automatic choice and the product library.  For tests and
+    measurement; not thread-safe."""
+    global _ROUTED
+    D = diag_lib()
+    st = D.rr_set_variant_override(int(variant))
+    if st != RR_OK:
+        raise RowReduceError(st, f"rr_set_variant_override({variant}): {D.rr_status_string(st).decode()}: "
+                                 f"{D.rr_last_error_message().decode()}")
+    prev = _ROUTED
+    _ROUTED = D
+    try:
+        yield D
+    finally:
+        D.rr_set_variant_override(RR_VARIANT_AUTO)
+        _ROUTED = prev
 
 
 def load_library(path):
@@ -142,14 +189,18 @@ def load_library(path):
     L.rr_last_error_message.argtypes = []
     L.rr_last_error_message.restype = ctypes.c_char_p
     L.rr_query_plan.argtypes = [i32, i64, i64, i32, i32, i32, ctypes.POINTER(rr_plan)]
-    L.rr_set_variant_override.argtypes = [i32]
-    L.rr_selftest_wave_allreduce.argtypes = [vp, vp, i64, i32, vp]
-    L.rr_stream_copy.argtypes = [vp, vp, i64, vp]
     for f in ("rr_rmsnorm", "rr_fused_add_rmsnorm", "rr_layernorm", "rr_softmax_rows",
               "rr_softmax_rows_ex", "rr_query_plan", "rr_rmsnorm_strided",
               "rr_fused_add_rmsnorm_strided", "rr_layernorm_strided", "rr_softmax_rows_strided",
-              "rr_softmax_rows_strided_noalloc", "rr_set_variant_override", "rr_selftest_wave_allreduce", "rr_stream_copy"):
+              "rr_softmax_rows_strided_noalloc"):
         getattr(L, f).restype = i32
+    # the diagnostics build's additions (absent from the product library)
+    if hasattr(L, "rr_set_variant_override"):
+        L.rr_set_variant_override.argtypes = [i32]
+        L.rr_selftest_wave_allreduce.argtypes = [vp, vp, i64, i32, vp]
+        L.rr_stream_copy.argtypes = [vp, vp, i64, vp]
+        for f in DIAG_EXPORTS:
+            getattr(L, f).restype = i32
     return L
 
 
@@ -236,10 +287,6 @@ def rr_query_plan(op: int, M: int, N: int, in_dtype: int, out_dtype: int, aligne
     mode = 2 if aligned16 == 2 else (1 if aligned16 else 0)
     check(lib().rr_query_plan(op, M, N, in_dtype, out_dtype, mode, ctypes.byref(p)), "rr_query_plan")
     return p.as_dict()
-
-
-def rr_set_variant_override(variant: int) -> None:
-    check(lib().rr_set_variant_override(int(variant)), "rr_set_variant_override")
 
 
 # ----------------------------------------------------------------------------
@@ -463,20 +510,25 @@ def rr_selftest_wave_allreduce(out, inp, kind: int, stream=None) -> None:
     per = 128 if kind == 2 else 64
     if inp.numel() % per or out.numel() != inp.numel():
         raise ValueError("bad self-test sizes")
-    check(lib().rr_selftest_wave_allreduce(inp.data_ptr(), out.data_ptr(), inp.numel() // per,
-                                           int(kind), _stream_of(inp, stream)),
-          "rr_selftest_wave_allreduce")
+    D = diag_lib()
+    st = D.rr_selftest_wave_allreduce(inp.data_ptr(), out.data_ptr(), inp.numel() // per, int(kind),
+                                      _stream_of(inp, stream))
+    if st != RR_OK:
+        raise RowReduceError(st, f"rr_selftest_wave_allreduce: {D.rr_last_error_message().decode()}")
 
 
 def rr_stream_copy(dst, src, stream=None) -> None:
-    """dst <- src, every byte, by the library's streaming copy (a measurement
-    reference: the practical bar for an operation moving the same bytes)."""
+    """dst <- src, every byte, by the diagnostics build's streaming copy (a
+    measurement reference: the practical bar for an operation moving the same
+    bytes)."""
     _need_cuda(dst, src)
     nb = src.numel() * src.element_size()
     if dst.numel() * dst.element_size() != nb or not (src.is_contiguous() and dst.is_contiguous()):
         raise ValueError("rr_stream_copy: contiguous tensors of equal byte size required")
-    check(lib().rr_stream_copy(dst.data_ptr(), src.data_ptr(), nb, _stream_of(src, stream)),
-          "rr_stream_copy")
+    D = diag_lib()
+    st = D.rr_stream_copy(dst.data_ptr(), src.data_ptr(), nb, _stream_of(src, stream))
+    if st != RR_OK:
+        raise RowReduceError(st, f"rr_stream_copy: {D.rr_last_error_message().decode()}")
 
 
 # ----------------------------------------------------------------------------

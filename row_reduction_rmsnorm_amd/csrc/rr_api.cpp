@@ -19,10 +19,33 @@
 #include "rowreduce.h"
 #include "rr_launch.h"
 
+// RR_DIAG: the diagnostics build (librowreduce_diag.so), which adds the
+// entry points of rowreduce_diag.h -- a forced kernel variant for tests and
+// measurement, the all-reduce self-test and the streaming copy.  The product
+// library carries none of them and keeps no process state beyond the
+// calling thread's last error message.
+#ifndef RR_DIAG
+#define RR_DIAG 0
+#endif
+#if RR_DIAG
+#include "rowreduce_diag.h"
+#endif
+
 namespace {
 
 thread_local char g_err[512] = "";
+#if RR_DIAG
 std::atomic<int> g_override{RR_VARIANT_AUTO};
+#endif
+
+// The variant a call is forced to (diagnostics build), else RR_VARIANT_AUTO.
+int forced_variant() {
+#if RR_DIAG
+  return g_override.load(std::memory_order_relaxed);
+#else
+  return RR_VARIANT_AUTO;
+#endif
+}
 
 rr_status fail(rr_status s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
 rr_status fail(rr_status s, const char* fmt, ...) {
@@ -322,7 +345,7 @@ rr_status make_plan(rr_op op, int64_t M, int64_t N, int din, int dout, int align
   const int64_t nvec_any = (N + 2 * (int64_t)vw - 2) / vw;
   const int64_t nvec_s = align == 1 ? ceil_div(N, vw) : nvec_any;
   const int per16_s = vecs_per_16_bytes(din, vw);
-  const int forced = g_override.load(std::memory_order_relaxed);
+  const int forced = forced_variant();
   const int64_t packed_rows = packed_min_rows(din, dout);
 
   bool ok = false;
@@ -650,8 +673,8 @@ rr_status softmax_entry(const char* who, void* y, int64_t ldy, const void* x, in
     if (p.workspace_bytes > rr::kNoAllocScratchBytes)
       return fail(RR_ERR_WORKSPACE, "%s: this shape needs %zu bytes of split-row scratch; the static scratch holds %zu",
                   who, p.workspace_bytes, rr::kNoAllocScratchBytes);
-    if (p.variant == RR_VARIANT_SPLIT_ONE_KERNEL)
-      return fail(RR_ERR_UNSUPPORTED, "%s: the one-kernel split is not available without a workspace", who);
+    // (a forced one-kernel split runs as the two kernels here: same bits)
+    if (p.variant == RR_VARIANT_SPLIT_ONE_KERNEL) p.variant = RR_VARIANT_SPLIT;
     hipError_t se = hipSuccess;
     workspace = rr::noalloc_scratch(&se);
     if (!workspace) return hip_status(se != hipSuccess ? se : hipErrorInvalidSymbol, who);
@@ -757,6 +780,7 @@ rr_status rr_query_plan(rr_op op, int64_t M, int64_t N, rr_dtype in_dtype, rr_dt
   return make_plan(op, M, N, in_dtype, out_dtype, is_aligned16 == 2 ? 2 : (is_aligned16 != 0 ? 1 : 0), plan);
 }
 
+#if RR_DIAG
 rr_status rr_set_variant_override(rr_variant v) {
   g_err[0] = '\0';
   if (v < RR_VARIANT_AUTO || v > RR_VARIANT_SUBWAVE)
@@ -787,5 +811,6 @@ rr_status rr_stream_copy(void* dst, const void* src, int64_t bytes, void* stream
   return hip_status(rr::launch_stream_copy(dst, src, bytes, static_cast<hipStream_t>(stream)),
                     "rr_stream_copy");
 }
+#endif  // RR_DIAG
 
 }  // extern "C"

@@ -36,6 +36,28 @@ __device__ __forceinline__ float exp_shifted(float t) {
   return __builtin_amdgcn_exp2f(t * kLog2e);
 }
 
+// The same where the result may be a subnormal that matters: v_exp_f32
+// flushes results below 2^-126 to zero, so an argument whose result would
+// be that small is raised by 64 first and the result multiplied by 2^-64
+// (one rounding, into the subnormal range).  Results below 2^-190 stay 0,
+// which is their correct rounding in fp32 as well.
+__device__ __forceinline__ float exp_shifted_full(float t) {
+  const float u = t * kLog2e;
+  const bool tiny = u < -126.0f;
+  const float r = __builtin_amdgcn_exp2f(tiny ? u + 64.0f : u);
+  return tiny ? r * 0x1p-64f : r;
+}
+
+// The exponential that becomes a softmax output of type Tout.  A bf16
+// output keeps its subnormals (down to 2^-133, which the full form reaches);
+// an fp32 output below 2^-126 comes out as 0, an absolute error below
+// 1.2e-38, and spares the extra instructions per element.
+template <typename Tout>
+__device__ __forceinline__ float exp_out(float t) {
+  if constexpr (std::is_same_v<Tout, bf16_t>) return exp_shifted_full(t);
+  else return exp_shifted(t);
+}
+
 // ---------------------------------------------------------------------------
 // element codec
 // ---------------------------------------------------------------------------

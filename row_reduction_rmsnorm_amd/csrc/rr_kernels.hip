@@ -1096,7 +1096,7 @@ __global__ __launch_bounds__(256) void softmax_sub_kernel(const Tin* x, Tout* y,
     float dl = 0.0f;
 #pragma unroll
     for (int i = 0; i < VEC; ++i) {
-      const float e = exp_shifted(v[i] - shift);
+      const float e = exp_out<Tout>(v[i] - shift);
       dl += e;
       if constexpr (!LOG) v[i] = e;
     }
@@ -1110,7 +1110,7 @@ __global__ __launch_bounds__(256) void softmax_sub_kernel(const Tin* x, Tout* y,
 #pragma unroll
       for (int i = 0; i < VEC; ++i) o[i] = (v[i] - p.m) - ld;
     } else {
-      float c = (ml == kNegInf) ? 0.0f : exp_shifted(ml - p.m) / p.d;
+      float c = (ml == kNegInf) ? 0.0f : exp_out<Tout>(ml - p.m) / p.d;
       if (p.m == kNegInf) c = __builtin_nanf("");
 #pragma unroll
       for (int i = 0; i < VEC; ++i) o[i] = v[i] * c;
@@ -1224,7 +1224,7 @@ __global__ __launch_bounds__(1024) void softmax_regs_kernel(const Tin* x, Tout* 
     for (int k = 0; k < NV; ++k)
 #pragma unroll
       for (int i = 0; i < VEC; ++i) {
-        const float e = exp_shifted(v[k][i] - shift);
+        const float e = exp_out<Tout>(v[k][i] - shift);
         dl += e;
         if constexpr (!LOG) v[k][i] = e;   // plain softmax keeps e_i, log-softmax keeps x_i
       }
@@ -1240,7 +1240,7 @@ __global__ __launch_bounds__(1024) void softmax_regs_kernel(const Tin* x, Tout* 
     if constexpr (LOG) {
       ld = __builtin_logf(p.d);
     } else {
-      c = (ml == kNegInf) ? 0.0f : exp_shifted(ml - p.m) / p.d;
+      c = (ml == kNegInf) ? 0.0f : exp_out<Tout>(ml - p.m) / p.d;
       if (p.m == kNegInf) c = __builtin_nanf("");
     }
 #pragma unroll
@@ -1368,7 +1368,7 @@ __global__ __launch_bounds__(1024) void softmax_packed_kernel(const Tin* x, Tout
       float o[VEC];
 #pragma unroll
       for (int i = 0; i < VEC; ++i)
-        o[i] = LOG ? (key(k, i) - p.m) - ld : exp_shifted(key(k, i) - p.m) * inv_d;
+        o[i] = LOG ? (key(k, i) - p.m) - ld : exp_out<Tout>(key(k, i) - p.m) * inv_d;
       if (vi < nvec_row) {
         if (!SHIFT || (e0 >= 0 && e0 + VEC <= N)) store_vec<Tout, VEC>(yr + e0, o);
         else store_edge<Tout, VEC>(yr, e0, N, o);
@@ -1435,7 +1435,7 @@ __global__ __launch_bounds__(1024) void softmax_loop_kernel(const Tin* x, Tout* 
         load_edge<Tin, VEC>(xr, e0, keys, v);
       }
 #pragma unroll
-      for (int i = 0; i < VEC; ++i) v[i] = LOG ? (v[i] - p.m) - ld : exp_shifted(v[i] - p.m) * inv_d;
+      for (int i = 0; i < VEC; ++i) v[i] = LOG ? (v[i] - p.m) - ld : exp_out<Tout>(v[i] - p.m) * inv_d;
       if (whole(e0)) store_vec<Tout, VEC>(yr + e0, v);
       else store_edge<Tout, VEC>(yr, e0, N, v);
     }
@@ -1626,7 +1626,7 @@ __global__ __launch_bounds__(256) void softmax_split_apply_kernel(const Tin* x, 
       float o[VEC];
 #pragma unroll
       for (int i = 0; i < VEC; ++i)
-        o[i] = LOG ? (v[k].get(i) - p.m) - ld : exp_shifted(v[k].get(i) - p.m) * inv_d;
+        o[i] = LOG ? (v[k].get(i) - p.m) - ld : exp_out<Tout>(v[k].get(i) - p.m) * inv_d;
       // plain (write-back) stores: measured faster than non-temporal ones here
       if (vi < nvec_row) {
         if (!SHIFT || (e0 >= 0 && e0 + VEC <= N)) store_vec<Tout, VEC, false>(yr + e0, o);
@@ -1658,7 +1658,13 @@ __global__ __launch_bounds__(256) void softmax_split_apply_kernel(const Tin* x, 
 //    waits for items of its own row; a cycle of waits would need every
 //    workgroup's current item to be smaller than the next one's, around the
 //    cycle, which cannot be.  Every wait is also bounded (kSpinLimit polls), so
-//    every wavefront reaches the end even if that argument were broken.
+//    every wavefront reaches the end even if that argument were broken; a
+//    wavefront whose wait gave up writes NaN over its chunk instead of
+//    probabilities, so the failure shows in the output.
+//  * Graph capture: the tag is fixed when the kernel is launched, so a
+//    replayed graph would find its own earlier tags in the slots; a call
+//    made while its stream is capturing runs the two-kernel form instead
+//    (the same bits).
 // ===========================================================================
 constexpr int kSpinLimit = 1 << 22;
 
@@ -1710,11 +1716,14 @@ __global__ __launch_bounds__(256) void softmax_split_fused_kernel(const Tin* x, 
       __hip_atomic_store(&row_slots[c].tag, tag, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
     }
     // wait for the row's chunks, then merge them in the same order as pass B
+    bool gave_up = false;
     for (int s = rl.lane; s < S; s += kWave) {
-      for (int spin = 0; spin < kSpinLimit; ++spin) {
+      int spin = 0;
+      for (; spin < kSpinLimit; ++spin) {
         if (__hip_atomic_load(&row_slots[s].tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == tag) break;
         __builtin_amdgcn_s_sleep(1);
       }
+      gave_up = gave_up || spin == kSpinLimit;
     }
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     MD q;
@@ -1727,50 +1736,18 @@ __global__ __launch_bounds__(256) void softmax_split_fused_kernel(const Tin* x, 
       q = md_merge(q, b);
     }
     q = wave_md(q);
+    // a wait that gave up anywhere in the wavefront poisons its outputs
+    if (__any(gave_up)) q.m = __builtin_nanf("");
     const float inv_d = (q.m == kNegInf) ? __builtin_nanf("") : 1.0f / q.d;
 #pragma unroll
     for (int k = 0; k < NV; ++k) {
       const int vi = c * CV + k * kThreads + rl.t;
       float o[VEC];
 #pragma unroll
-      for (int i = 0; i < VEC; ++i) o[i] = exp_shifted(v[k].get(i) - q.m) * inv_d;
+      for (int i = 0; i < VEC; ++i) o[i] = exp_out<Tout>(v[k].get(i) - q.m) * inv_d;
       if (vi < nvec) store_vec<Tout, VEC, false>(y + oy + (int64_t)vi * VEC, o);
     }
   }
-}
-
-// ===========================================================================
-// self-test of the wave all-reduce: one wavefront per 64-value group
-// ===========================================================================
-__global__ __launch_bounds__(64) void selftest_wave_kernel(const float* in, float* out, int kind) {
-  const int64_t gidx = blockIdx.x;
-  const int lane = threadIdx.x;
-  if (kind == 0) {
-    out[gidx * 64 + lane] = wave_sum(in[gidx * 64 + lane]);
-  } else if (kind == 1) {
-    out[gidx * 64 + lane] = wave_max(in[gidx * 64 + lane]);
-  } else {
-    MD p;
-    p.m = in[gidx * 128 + lane];
-    p.d = in[gidx * 128 + 64 + lane];
-    p = wave_md(p);
-    out[gidx * 128 + lane] = p.m;
-    out[gidx * 128 + 64 + lane] = p.d;
-  }
-}
-
-// ===========================================================================
-// streaming copy (a measurement reference, not an operation of the pages):
-// one 16-byte vector per lane per step, non-temporal loads and stores, no
-// dependency between lanes.  The grid covers the copy in one step unless it
-// was capped (then workgroups stride by the grid).
-// ===========================================================================
-template <int BS>
-__global__ __launch_bounds__(BS) void stream_copy_kernel(const u32x4_t* __restrict__ src,
-                                                         u32x4_t* __restrict__ dst, int64_t nvec) {
-  const int64_t stride = (int64_t)gridDim.x * BS;
-  for (int64_t i = (int64_t)blockIdx.x * BS + threadIdx.x; i < nvec; i += stride)
-    __builtin_nontemporal_store(__builtin_nontemporal_load(src + i), dst + i);
 }
 
 // ===========================================================================
@@ -2006,8 +1983,12 @@ hipError_t softmax_split(const rr_plan& p, const SmCall<Tin, Tout>& c, SplitSlot
                          int64_t grid, hipStream_t s) {
   const dim3 b(p.block_threads);
   if (c.cp > 0) return hipErrorInvalidValue;
+  // a capturing stream takes the two kernels (see softmax_split_fused_kernel)
+  hipStreamCaptureStatus capture = hipStreamCaptureStatusNone;
+  if (p.variant == RR_VARIANT_SPLIT_ONE_KERNEL && hipStreamIsCapturing(s, &capture) != hipSuccess)
+    return hipErrorInvalidValue;
   if constexpr (!LOG && !SHIFT) {
-    if (p.variant == RR_VARIANT_SPLIT_ONE_KERNEL) {
+    if (p.variant == RR_VARIANT_SPLIT_ONE_KERNEL && capture == hipStreamCaptureStatusNone) {
       const void* k = reinterpret_cast<const void*>(&softmax_split_fused_kernel<Tin, Tout, NV>);
       const int cap = cooperative_capacity(k);
       if (cap >= S) {
@@ -2141,28 +2122,6 @@ hipError_t launch_softmax(const rr_plan& plan, rr_dtype in_dtype, rr_dtype out_d
   }
   if (out_dtype == RR_F32) return softmax_io<bf16_t, float>(plan, args, grid, stream);
   return softmax_io<bf16_t, bf16_t>(plan, args, grid, stream);
-}
-
-hipError_t launch_selftest_wave(const float* in, float* out, int64_t count, int kind,
-                                hipStream_t stream) {
-  selftest_wave_kernel<<<grid1(count), dim3(64), 0, stream>>>(in, out, kind);
-  return hipGetLastError();
-}
-
-hipError_t launch_stream_copy(void* dst, const void* src, int64_t bytes, hipStream_t stream) {
-  const int64_t nvec = bytes / 16;
-  const u32x4_t* s = static_cast<const u32x4_t*>(src);
-  u32x4_t* d = static_cast<u32x4_t*>(dst);
-  // 1024-lane groups measured fastest below 1 GiB, 256-lane groups above;
-  // the grid is capped so that a dispatch's work-items fit in 32 bits
-  if (bytes < ((int64_t)1 << 30)) {
-    const int64_t grid = (nvec + 1023) / 1024;
-    stream_copy_kernel<1024><<<grid1(grid < (1 << 22) ? grid : (1 << 22)), dim3(1024), 0, stream>>>(s, d, nvec);
-  } else {
-    const int64_t grid = (nvec + 255) / 256;
-    stream_copy_kernel<256><<<grid1(grid < (1 << 24) ? grid : (1 << 24)), dim3(256), 0, stream>>>(s, d, nvec);
-  }
-  return hipGetLastError();
 }
 
 }  // namespace rr

@@ -73,12 +73,12 @@ constexpr size_t kNoAllocScratchBytes = (size_t)4 << 20;
 // device with hipGetSymbolAddress, then cached), or null with *err set.
 void* noalloc_scratch(hipError_t* err);
 
-// Enqueue the wave all-reduce self-test kernel.
+// Diagnostics build only (rr_diag.hip): the wave all-reduce self-test kernel.
 hipError_t launch_selftest_wave(const float* in, float* out, int64_t count, int kind,
                                 hipStream_t stream);
 
-// Enqueue the streaming copy of `bytes` bytes (a positive multiple of 16,
-// both pointers 16-byte aligned).
+// Diagnostics build only (rr_diag.hip): the streaming copy of `bytes` bytes
+// (a positive multiple of 16, both pointers 16-byte aligned).
 hipError_t launch_stream_copy(void* dst, const void* src, int64_t bytes, hipStream_t stream);
 
 }  // namespace rr

@@ -17,13 +17,20 @@ import row_reduction_rmsnorm_amd as rr
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "rowreduce.h")
+DIAG_HEADER = os.path.join(ROOT, "include", "rowreduce_diag.h")
 
 
-def _declared_functions():
-    text = open(HEADER).read()
+def _declared_functions(path=HEADER):
+    text = open(path).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     names = re.findall(r"\b(rr_[a-z0-9_]+)\s*\(", text)
     return sorted(set(names))
+
+
+def _exported(path):
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--defined-only", path], capture_output=True, text=True, check=True).stdout
+    return sorted({l.split()[-1] for l in out.splitlines() if " T rr_" in l})
 
 
 def test_library_exports_every_declared_function():
@@ -36,11 +43,21 @@ def test_library_exports_every_declared_function():
 
 
 def test_library_exports_nothing_undeclared():
-    import subprocess
-    out = subprocess.run(["nm", "-D", "--defined-only", rr.binding.LIB_PATH],
-                         capture_output=True, text=True, check=True).stdout
-    exported = sorted({l.split()[-1] for l in out.splitlines() if " T rr_" in l})
-    assert exported == _declared_functions()
+    assert _exported(rr.binding.LIB_PATH) == _declared_functions()
+
+
+def test_diagnostics_build_exports_and_shares_the_kernel_object():
+    """librowreduce_diag.so exports rowreduce.h plus rowreduce_diag.h (and
+    the product none of the latter); its device code holds the product's
+    code object byte for byte (the same compiled kernel object, linked
+    unchanged) plus the diagnostic kernels."""
+    diag = _declared_functions(DIAG_HEADER)
+    assert sorted(rr.DIAG_EXPORTS) == diag
+    assert _exported(rr.binding.DIAG_LIB_PATH) == sorted(set(_declared_functions()) | set(diag))
+    assert not set(diag) & set(_exported(rr.binding.LIB_PATH))
+    import bench
+    prod = bench.fatbin_bytes(rr.binding.LIB_PATH)
+    assert prod in bench.fatbin_bytes(rr.binding.DIAG_LIB_PATH)
 
 
 def test_status_strings():
@@ -76,7 +93,7 @@ def test_m_zero_is_a_noop_even_with_null_pointers():
 
 
 def test_stream_copy_validation():
-    L = rr.lib()
+    L = rr.diag_lib()
     assert L.rr_stream_copy(None, None, 0, None) == rr.RR_OK            # empty: no launch
     for dst, src, nb in ((P, P << 4, -16),          # negative size
                          (P, P << 4, 24),           # not a multiple of 16
@@ -86,7 +103,7 @@ def test_stream_copy_validation():
                          (P, (P << 4) + 4, 32),     # misaligned source
                          (P, P + 16, 64)):          # overlapping ranges
         assert L.rr_stream_copy(dst, src, nb, None) == rr.RR_ERR_INVALID_ARG, (dst, src, nb)
-        assert rr.last_error_message().startswith("rr_stream_copy")
+        assert L.rr_last_error_message().decode().startswith("rr_stream_copy")
 
 
 def test_fused_validation():
@@ -201,15 +218,12 @@ def test_softmax_causal_plans():
     # from 56 rows up (bf16 -> fp32) softmax also holds such rows in one workgroup
     assert q(S, 56, 152064, B, F) == q(C, 56, 152064, B, F)
     assert q(S, 56, 152064, B, F)["variant_name"] == "block" and q(S, 55, 152064, B, F)["variant_name"] == "split"
-    try:
-        rr.rr_set_variant_override(rr.RR_VARIANT_SPLIT)
+    with rr.forced_variant(rr.RR_VARIANT_SPLIT):
         with pytest.raises(rr.RowReduceError):
             q(C, 10, 1024)
         assert q(S, 10, 1024)["variant_name"] == "split"
-        rr.rr_set_variant_override(rr.RR_VARIANT_LOOP)
+    with rr.forced_variant(rr.RR_VARIANT_LOOP):
         assert q(C, 10, 1024)["variant_name"] == "loop"
-    finally:
-        rr.rr_set_variant_override(rr.RR_VARIANT_AUTO)
 
 
 def test_strided_validation():
@@ -398,16 +412,15 @@ def test_dispatch_boundaries():
 
 def test_forced_variants():
     S, F = rr.RR_OP_SOFTMAX, rr.RR_F32
-    try:
-        rr.rr_set_variant_override(rr.RR_VARIANT_LOOP)
+    with rr.forced_variant(rr.RR_VARIANT_LOOP):
         assert rr.rr_query_plan(S, 10, 1024, F, F)["variant_name"] == "loop"
-        rr.rr_set_variant_override(rr.RR_VARIANT_SPLIT)
+    with rr.forced_variant(rr.RR_VARIANT_SPLIT):
         p = rr.rr_query_plan(S, 10, 1024, F, F)
         assert p["variant_name"] == "split" and p["workspace_bytes"] == 10 * 1 * 16
         assert rr.rr_softmax_rows_workspace_bytes(10, 1024, F, F) == 160
         p = rr.rr_query_plan(S, 10, 1023, F, F, 2)      # a row cut at aligned addresses
         assert (p["variant_name"], p["row_shift"], p["vec_elems"]) == ("split", 1, 4)
-        rr.rr_set_variant_override(rr.RR_VARIANT_SPLIT_ONE_KERNEL)
+    with rr.forced_variant(rr.RR_VARIANT_SPLIT_ONE_KERNEL):
         p = rr.rr_query_plan(S, 10, 5000, F, F)
         assert p["variant_name"] == "split1" and p["chunks_per_row"] == 2
         # the workspace query covers the aligned call even though cut rows are refused
@@ -417,14 +430,21 @@ def test_forced_variants():
             rr.rr_query_plan(S, 10, 5001, F, F)               # the one-kernel form takes aligned rows
         with pytest.raises(rr.RowReduceError):
             rr.rr_query_plan(rr.RR_OP_RMSNORM, 10, 1024, F, F)   # no split RMSNorm
-        rr.rr_set_variant_override(rr.RR_VARIANT_WAVE)
+    with rr.forced_variant(rr.RR_VARIANT_WAVE):
         with pytest.raises(rr.RowReduceError):
             rr.rr_query_plan(S, 10, 4096, F, F)                  # row too long for a wave
-    finally:
-        rr.rr_set_variant_override(rr.RR_VARIANT_AUTO)
     with pytest.raises(rr.RowReduceError):
-        rr.rr_set_variant_override(9)
-    assert rr.rr_query_plan(S, 10, 1024, F, F)["variant_name"] == "wave"   # override cleared
+        with rr.forced_variant(9):
+            pass
+    assert rr.rr_query_plan(S, 10, 1024, F, F)["variant_name"] == "wave"   # automatic again
+    # the product library has no override at all; the diagnostics build, back
+    # at automatic choice, plans exactly as the product does
+    assert not hasattr(rr.binding.lib(), "rr_set_variant_override")
+    D = rr.diag_lib()
+    for shape in [(S, 10, 5000, F, F), (S, 256, 152064, rr.RR_BF16, F), (rr.RR_OP_RMSNORM, 8192, 4096, 1, 1)]:
+        p = rr.binding.rr_plan()
+        assert D.rr_query_plan(*shape, 1, ctypes.byref(p)) == rr.RR_OK
+        assert p.as_dict() == rr.rr_query_plan(*shape), shape
 
 
 def test_every_plan_covers_its_row():
@@ -443,9 +463,8 @@ def test_every_plan_covers_its_row():
     widths = np.concatenate([rng.integers(1, 300, 300), rng.integers(300, 70000, 400),
                              rng.integers(70000, 1 << 22, 100), [1 << 30, (1 << 30) - 8]])
     checked = 0
-    try:
-        for v in variants:
-            rr.rr_set_variant_override(v)
+    for v in variants:
+        with rr.forced_variant(v):
             for N in widths:
                 N = int(N)
                 op = ops[int(rng.integers(0, len(ops)))]
@@ -502,6 +521,4 @@ def test_every_plan_covers_its_row():
                     assert name == "loop", p
                 assert p["workspace_bytes"] == 0, p
                 assert p["work_items"] * p["rows_per_group"] >= M, p
-    finally:
-        rr.rr_set_variant_override(rr.RR_VARIANT_AUTO)
     assert checked > 1500

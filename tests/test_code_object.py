@@ -65,9 +65,10 @@ def test_every_kernel_is_present(kernels):
     names = " ".join(kernels)
     for family in ("norm_regs_kernel", "norm_loop_kernel", "norm_sub_kernel", "softmax_regs_kernel",
                    "softmax_sub_kernel", "softmax_packed_kernel", "softmax_loop_kernel",
-                   "softmax_split_stats_kernel", "softmax_split_apply_kernel", "softmax_split_fused_kernel",
-                   "selftest_wave_kernel"):
+                   "softmax_split_stats_kernel", "softmax_split_apply_kernel", "softmax_split_fused_kernel"):
         assert family in names, family
+    # the diagnostic kernels live only in the diagnostics build
+    assert "selftest_wave_kernel" not in names and "stream_copy_kernel" not in names
 
 
 def test_no_spills_no_scratch_wave64(kernels):

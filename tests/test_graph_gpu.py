@@ -22,9 +22,7 @@ def gpu():
     assert torch.cuda.is_available(), "GPU tests need a GPU"
     rr = _rr()
     rr.lib()
-    rr.rr_set_variant_override(rr.RR_VARIANT_AUTO)
     yield
-    rr.rr_set_variant_override(rr.RR_VARIANT_AUTO)
 
 
 def test_graph_replays_match_eager():
@@ -128,4 +126,50 @@ def test_graph_replays_of_cut_rows_match_eager():
         graph.replay()
         torch.cuda.synchronize()
         for got, want, what in zip((y1, y2, y3), ref, ("cut split softmax", "cut packed softmax", "cut layernorm")):
+            assert torch.equal(_bits(got), _bits(want)), f"replay {k}: {what}"
+
+
+def test_graph_replays_of_the_no_allocation_call_and_a_forced_one_kernel_split():
+    """Two calls that could not be captured otherwise: the no-allocation entry
+    point on a split row (its (m, d) slots in the library's static scratch,
+    no workspace argument), and the one-kernel split forced in the
+    diagnostics build, whose per-launch tags would be stale on replay -- a
+    capturing stream takes the two-kernel form instead.  Replays on changed
+    inputs equal eager two-kernel calls bit for bit."""
+    rr = _rr()
+    s1 = softmax_input(24, 152064, seed=41, dt="bf16").cuda()
+    y1 = torch.empty(s1.shape, dtype=torch.float32, device="cuda")
+    s2 = softmax_input(16, 65536, seed=42, dt="f32").cuda()
+    y2 = torch.empty_like(s2)
+    ws2 = rr.softmax_workspace(s2, torch.float32)
+    assert rr.rr_query_plan(rr.RR_OP_SOFTMAX, 24, 152064, rr.RR_BF16, rr.RR_F32)["variant_name"] == "split"
+
+    def eager_reference():
+        r1 = torch.empty_like(y1)
+        r2 = torch.empty_like(y2)
+        rr.rr_softmax_rows(r1, s1, rr.softmax_workspace(s1, torch.float32))
+        rr.rr_softmax_rows(r2, s2, ws2)
+        torch.cuda.synchronize()
+        return r1, r2
+
+    with rr.forced_variant(rr.RR_VARIANT_SPLIT_ONE_KERNEL):
+        def step():
+            rr.rr_softmax_rows_strided_noalloc(y1, s1)
+            rr.rr_softmax_rows(y2, s2, ws2)
+        step()
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        torch.cuda.synchronize()
+    for k in range(4):
+        _say(f"no-allocation / one-kernel graph replay {k}")
+        s1.mul_(0.75)
+        s2.add_(0.5)
+        ref = eager_reference()
+        y1.zero_()
+        y2.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        for got, want, what in zip((y1, y2), ref, ("no-allocation split", "forced one-kernel split")):
             assert torch.equal(_bits(got), _bits(want)), f"replay {k}: {what}"

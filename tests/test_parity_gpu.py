@@ -25,9 +25,7 @@ def gpu():
     assert torch.cuda.is_available(), "GPU tests need a GPU"
     import row_reduction_rmsnorm_amd as rr
     rr.lib()
-    rr.rr_set_variant_override(rr.RR_VARIANT_AUTO)
     yield
-    rr.rr_set_variant_override(rr.RR_VARIANT_AUTO)
 
 
 def _rr():
@@ -286,8 +284,7 @@ def test_norm_forced_variants(variant):
             "subwave": rr.RR_VARIANT_SUBWAVE}[variant]
     shapes = {"wave": [8, 64, 520, 1024], "block": [8, 1024, 3584, 4096, 16384],
               "loop": [8, 1024, 4096, 20000, 65536], "subwave": [8, 16, 24, 64, 128]}[variant]
-    try:
-        rr.rr_set_variant_override(code)
+    with rr.forced_variant(code):
         for dt in ("f32", "bf16"):
             for N in shapes:
                 for M in (1, 7, 130):
@@ -298,8 +295,6 @@ def test_norm_forced_variants(variant):
                     r = _as(workloads.random_rows(M, N, seed=M + N), dt)
                     y, r_out = run_fused(x, r, g, 1e-6)
                     check_fused(x, r, g, 1e-6, dt, y, r_out, f"{variant} fused {dt} {M}x{N}")
-    finally:
-        rr.rr_set_variant_override(rr.RR_VARIANT_AUTO)
 
 
 # ----------------------------------------------------------------------------
@@ -378,15 +373,12 @@ def test_layernorm_forced_variants(variant):
             "subwave": rr.RR_VARIANT_SUBWAVE}[variant]
     shapes = {"wave": [8, 64, 520, 1024], "block": [8, 1024, 5120, 16384],
               "loop": [8, 1024, 5120, 20000], "subwave": [8, 24, 64, 128]}[variant]
-    try:
-        rr.rr_set_variant_override(code)
+    with rr.forced_variant(code):
         for dt in ("f32", "bf16"):
             for N in shapes:
                 for M in (1, 7, 130):
                     x, g, b = ln_input(M, N, seed=3 * N + M, dt=dt, offset=50.0, spread=2.0)
                     check_ln(x, g, b, 1e-5, run_layernorm(x, g, b, 1e-5), f"{variant} ln {dt} {M}x{N}")
-    finally:
-        rr.rr_set_variant_override(rr.RR_VARIANT_AUTO)
 
 
 def test_layernorm_edge_cases():
@@ -428,6 +420,9 @@ def test_layernorm_first_element_far_from_the_mean(dt, N):
     b = rng.uniform(-1.0, 1.0, N).astype(np.float32)
     xt, gt, bt = _as(x, dt), _as(g, dt), _as(b, dt)
     check_ln(xt, gt, bt, 1e-5, run_layernorm(xt, gt, bt, 1e-5), f"ln far first {dt} N={N}")
+
+
+def test_workload_layernorm_full():
     """The LayerNorm exercise's shape: 256 x 5120, x ~ U(100, 102)."""
     w = workloads.make("layernorm")
     _say(w.description)
@@ -486,8 +481,7 @@ def test_softmax_forced_variants(variant):
     shapes = {"wave": [8, 64, 1024, 2048], "block": [8, 1024, 4096, 16384, 32768, 65536],
               "split": [8, 1024, 4096, 4104, 65536], "split1": [8, 4104, 65536],
               "loop": [8, 1024, 4096, 100000], "subwave": [8, 16, 40, 64, 128]}[variant]
-    try:
-        rr.rr_set_variant_override(code)
+    with rr.forced_variant(code):
         for din, dout in DTYPES:
             for N in shapes:
                 if variant == "wave" and din == "bf16" and N > 2048:
@@ -497,8 +491,6 @@ def test_softmax_forced_variants(variant):
                     x = softmax_input(M, N, seed=M + N, dt=din)
                     y = run_softmax(x, _tdt(dout))
                     check_softmax(x, y, f"{variant} {din}->{dout} {M}x{N}")
-    finally:
-        rr.rr_set_variant_override(rr.RR_VARIANT_AUTO)
 
 
 def test_split_one_kernel_equals_two_kernels_bitwise():
@@ -512,11 +504,8 @@ def test_split_one_kernel_equals_two_kernels_bitwise():
     for x in cases:
         outs = []
         for code in (rr.RR_VARIANT_SPLIT_ONE_KERNEL, rr.RR_VARIANT_SPLIT):
-            try:
-                rr.rr_set_variant_override(code)
+            with rr.forced_variant(code):
                 outs.append(run_softmax(x, torch.float32))
-            finally:
-                rr.rr_set_variant_override(rr.RR_VARIANT_AUTO)
         assert torch.equal(_bits(outs[0]), _bits(outs[1])), tuple(x.shape)
         check_softmax(x, outs[0], f"split {tuple(x.shape)}")
 
@@ -528,11 +517,8 @@ def test_split_row_longer_than_the_resident_grid():
     rr = _rr()
     x = softmax_input(1, 1 << 25, seed=6, dt="f32")
     check_softmax(x, run_softmax(x, torch.float32), "1 x 2^25")
-    try:
-        rr.rr_set_variant_override(rr.RR_VARIANT_SPLIT_ONE_KERNEL)
+    with rr.forced_variant(rr.RR_VARIANT_SPLIT_ONE_KERNEL):
         check_softmax(x, run_softmax(x, torch.float32), "1 x 2^25 one-kernel request")
-    finally:
-        rr.rr_set_variant_override(rr.RR_VARIANT_AUTO)
 
 
 def test_split_rows_with_many_chunks_are_merged_first():
@@ -642,16 +628,13 @@ def test_packed_long_rows_many_rows():
         check_softmax(x, run_softmax(x, torch.float32), f"packed {M}x{N}")
     # the packed kernel's edges for bf16 -> fp32 (8-byte vectors: 24 to 40 per
     # lane), on few rows with the variant forced
-    try:
-        rr.rr_set_variant_override(rr.RR_VARIANT_BLOCK)
+    with rr.forced_variant(rr.RR_VARIANT_BLOCK):
         for (N, nv) in [(98304, 24), (98308, 32), (163836, 40), (163840, 40)]:
             p = rr.rr_query_plan(rr.RR_OP_SOFTMAX, 5, N, rr.RR_BF16, rr.RR_F32)
             assert p["vec_elems"] == 4 and p["vecs_per_lane"] == nv and p["block_threads"] == 1024, p
             _say(f"packed softmax bf16->f32 M=5 N={N} nv={nv}")
             x = softmax_input(5, N, seed=N, dt="bf16")
             check_softmax(x, run_softmax(x, torch.float32), f"packed forced 5x{N}")
-    finally:
-        rr.rr_set_variant_override(rr.RR_VARIANT_AUTO)
 
 
 
@@ -828,6 +811,41 @@ def test_softmax_in_place_unaligned_and_tiny():
     assert y[0, 0] == 1.0 and np.isnan(y[1, 0]) and y[2, 0] == 1.0
 
 
+# Rows whose entries lie 87-92 below the row maximum: exp(x - m) is then a
+# float below 2^-126 that rounds to a bf16 subnormal (bf16's subnormals reach
+# down to 2^-133), so a kernel that flushed such exponentials to zero would
+# be up to 128 bf16 ulps off.  One case per kernel family the planner picks
+# for bf16 outputs: short rows, a wavefront per row, a workgroup per row,
+# the packed workgroup, the split row, rows cut at aligned addresses.
+SUBNORMAL_CASES = [
+    (64, 24, "f32"), (64, 1024, "bf16"), (16, 8192, "f32"), (80, 65536, "bf16"),
+    (4, 65536, "bf16"), (3, 152064, "f32"), (64, 1021, "bf16"),
+]
+
+
+@pytest.mark.parametrize("M,N,din", SUBNORMAL_CASES)
+def test_softmax_bf16_output_subnormal_probabilities(M, N, din):
+    rr = _rr()
+    rng = np.random.default_rng(M * 7 + N)
+    x = rng.uniform(-92.0, -87.0, (M, N)).astype(np.float32)
+    # a quarter of the entries whose exponentials are normal but small (so
+    # that d stays near 1), and the maximum 0
+    sel = rng.random((M, N)) < 0.25
+    x[sel] = rng.uniform(-40.0, -20.0, int(sel.sum())).astype(np.float32)
+    x[:, rng.integers(0, N)] = 0.0
+    x_cpu = _as(x, din)
+    plan = rr.rr_query_plan(rr.RR_OP_SOFTMAX, M, N, rr.RR_F32 if din == "f32" else rr.RR_BF16, rr.RR_BF16,
+                            aligned16=1 if (N * (4 if din == "f32" else 2)) % 16 == 0 else 2)
+    _say(f"[subnormal] M={M} N={N} {din}->bf16 plan={plan['variant_name']}")
+    y = run_softmax(x_cpu, torch.bfloat16)
+    info = check_softmax(x_cpu, y, f"subnormal outputs {M}x{N} {din}->bf16")
+    # the case must reach the subnormal range: most outputs are nonzero subnormals
+    yb = compare.bf16_bits_of_tensor(y)
+    sub = ((yb & 0x7F80) == 0) & ((yb & 0x7F) != 0)
+    assert sub.mean() > 0.3, f"only {sub.mean():.2f} of the outputs are subnormal"
+    _say(f"  {info}")
+
+
 def test_softmax_shift_invariance_bitwise():
     # adding an exact constant to every entry of a dyadic row changes no
     # x - m and so no output bit (same kernel, same order)
@@ -860,7 +878,6 @@ def test_determinism_run_to_run():
     a = run_softmax(x, torch.float32)
     b = run_softmax(x, torch.float32)
     assert torch.equal(_bits(a), _bits(b))
-    rr.rr_set_variant_override(rr.RR_VARIANT_AUTO)
 
 
 # ----------------------------------------------------------------------------

@@ -25,9 +25,7 @@ def gpu():
     assert torch.cuda.is_available(), "GPU tests need a GPU"
     rr = _rr()
     rr.lib()
-    rr.rr_set_variant_override(rr.RR_VARIANT_AUTO)
     yield
-    rr.rr_set_variant_override(rr.RR_VARIANT_AUTO)
 
 
 def run_ex(x_cpu, out_dt, log_output=False, period=None, offset=0, inplace=False):
@@ -94,8 +92,7 @@ def test_log_softmax_forced_variants(variant):
     shapes = {"wave": [8, 1024, 2048], "block": [8, 4096, 32768, 65536],
               "split": [8, 4104, 65536], "split1": [8, 65536],
               "loop": [8, 4096, 100000], "subwave": [8, 40, 128]}[variant]
-    try:
-        rr.rr_set_variant_override(code)
+    with rr.forced_variant(code):
         for din, dout in DTYPES:
             for N in shapes:
                 if variant == "wave" and din == "bf16" and N > 2048:
@@ -105,8 +102,6 @@ def test_log_softmax_forced_variants(variant):
                     x = softmax_input(M, N, seed=M + 3 * N, dt=din)
                     y = run_ex(x, _tdt(dout), log_output=True)
                     check_ex(y, compare.to_f64(x), True, f"log {variant} {din}->{dout} {M}x{N}")
-    finally:
-        rr.rr_set_variant_override(rr.RR_VARIANT_AUTO)
 
 
 def test_log_softmax_exp_matches_softmax_and_examples():
@@ -173,8 +168,7 @@ def test_causal_forced_variants(variant):
             "loop": rr.RR_VARIANT_LOOP, "subwave": rr.RR_VARIANT_SUBWAVE}[variant]
     shapes = {"wave": [8, 1024, 2048], "block": [8, 4096, 65536, 163840],
               "loop": [8, 4096, 100000], "subwave": [8, 40, 128]}[variant]
-    try:
-        rr.rr_set_variant_override(code)
+    with rr.forced_variant(code):
         for din, dout in DTYPES:
             for N in shapes:
                 if variant == "wave" and din == "bf16" and N > 2048:
@@ -188,8 +182,6 @@ def test_causal_forced_variants(variant):
                     given, meant = causal_inputs(M, N, M, O, seed=N + M, dt=din)
                     y = run_ex(given, _tdt(dout), log_output, period=M, offset=O)
                     check_ex(y, meant, log_output, f"causal {variant} {din}->{dout} {M}x{N}")
-    finally:
-        rr.rr_set_variant_override(rr.RR_VARIANT_AUTO)
 
 
 def test_causal_in_place_and_unaligned():

@@ -31,7 +31,9 @@ F32, BF16 = rr.RR_F32, rr.RR_BF16
 def libs():
     assert torch.cuda.is_available(), "GPU tests need a GPU"
     assert os.path.exists(rr_build.LIB_STRESS), "the race-stress build is missing (run build())"
-    normal = rr.lib()
+    # the normal build: the diagnostics library, which links the product's
+    # kernel object unchanged and can force the one-kernel split below
+    normal = rr.diag_lib()
     stress = rr.load_library(rr_build.LIB_STRESS)
     for L in (normal, stress):
         L.rr_set_variant_override(rr.RR_VARIANT_AUTO)

@@ -29,9 +29,7 @@ def gpu():
     assert torch.cuda.is_available(), "GPU tests need a GPU"
     rr = _rr()
     rr.lib()
-    rr.rr_set_variant_override(rr.RR_VARIANT_AUTO)
     yield
-    rr.rr_set_variant_override(rr.RR_VARIANT_AUTO)
 
 
 def embed(rows_cpu, ld, col0, fill=SENTINEL):
