@@ -259,42 +259,44 @@ def cpu_baseline(torch, rr, ops, bufs, fraction):
 
 
 def measure_extras(torch, rr, dev, K, bufs):
-    """Operations outside the step, each timed on its own (K launches between
-    two events, after a warm-up launch): the 64 x 3584 fp32 RMSNorm (64 rows on
-    256 CUs: a latency case, reported as time and rows/s), LayerNorm at the
-    LayerNorm exercise's 256 x 5120 fp32 shape, LayerNorm bf16 8192 x 4096
-    (the RMSNorm workload's shape, for bandwidth), the attention-score softmax
-    through the causal rule (only the kept keys are read: row i of a head reads
-    i + 1 keys and writes all 4096), and log-softmax on the vocabulary logits.
-    The LayerNorm and RMSNorm inputs stay cached between launches (the largest
-    is 134 MB), so those are not HBM-cold figures; the causal softmax moves
-    2.8 GB per launch and the log-softmax 234 MB."""
+    """Operations outside the step, each timed on its own: K launches between
+    two events, after a warm-up launch, each launch on the next of several
+    copies of its buffers, so that (as in the step) more than the 256 MB
+    last-level cache streams through between two uses of a copy and every
+    launch starts cold.  The operations: the 64 x 3584 fp32 RMSNorm and the
+    256 x 5120 fp32 LayerNorm (latency cases on 256 CUs, reported as time and
+    rows/s, also as a HIP graph of K launches, which removes the host's
+    launch cost), LayerNorm bf16 8192 x 4096 (the RMSNorm workload's shape,
+    for bandwidth), the attention-score softmax through the causal rule (only
+    the kept keys are read: row i of a head reads i + 1 keys and writes all
+    4096), log-softmax on the vocabulary logits, rows that are not whole
+    vectors (a 50257-wide vocabulary softmax, an RMSNorm of 4097), and the
+    vocabulary softmax at decode-size row counts (1, 16, 48 rows of 152064
+    bf16 -> fp32: the split path, two kernels)."""
     import numpy as np
     import workloads
     out = {}
 
-    def timed(name, fn, nbytes, M, graph=False):
-        """K launches between two events.  graph=True also replays the K
-        launches captured in one HIP graph, which removes the host's launch
-        cost between them: for the small latency-bound cases the eager figure
-        is the host's launch rate, the graph figure the device's."""
-        fn()
+    def timed(name, fn, nbytes, M, sets=1, graph=False):
+        """fn(k) runs the operation on copy k mod sets."""
+        fn(0)
         torch.cuda.synchronize()
         a = torch.cuda.Event(enable_timing=True)
         b = torch.cuda.Event(enable_timing=True)
         a.record()
-        for _ in range(K):
-            fn()
+        for k in range(K):
+            fn((k + 1) % sets)
         b.record()
         torch.cuda.synchronize()
         us = a.elapsed_time(b) / K * 1e3
         out[name] = {"us": round(us, 2), "bytes": nbytes, "GBps": round(nbytes / (us * 1e-6) / 1e9, 1),
-                     "rows_per_s": round(M / (us * 1e-6), 1)}
+                     "rows_per_s": round(M / (us * 1e-6), 1), "buffer_sets": sets,
+                     "cold": sets > 1 or nbytes > (512 << 20)}
         if graph:
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g):
-                for _ in range(K):
-                    fn()
+                for k in range(K):
+                    fn(k % sets)
             g.replay()
             torch.cuda.synchronize()
             a.record()
@@ -306,52 +308,90 @@ def measure_extras(torch, rr, dev, K, bufs):
                               "graph_GBps": round(nbytes / (gus * 1e-6) / 1e9, 1),
                               "graph_rows_per_s": round(M / (gus * 1e-6), 1)})
 
+    def copies(t, n):
+        return [t] + [t.clone() for _ in range(n - 1)]
+
+    def sets_for(nbytes):
+        """Copies so that more than 256 MB streams between two uses of one."""
+        return max(2, int(math.ceil((300 << 20) / nbytes)) + 1)
+
+    # latency cases (tiny footprints; the cache keeps them, the graph figure
+    # is the device's time per launch)
     w = workloads.make("rms_f32")
     x, g = w.arrays["x"].to(dev), w.arrays["gamma"].to(dev)
     y = torch.empty_like(x)
-    timed("rms_f32_64x3584", lambda: rr.rr_rmsnorm(y, x, g, w.eps), algorithmic_bytes("rms_f32", w.M, w.N), w.M,
-          graph=True)
+    timed("rms_f32_64x3584", lambda k: rr.rr_rmsnorm(y, x, g, w.eps), algorithmic_bytes("rms_f32", w.M, w.N),
+          w.M, graph=True)
     w = workloads.make("layernorm")
     x, g, bt = (w.arrays[k].to(dev) for k in ("x", "gamma", "beta"))
     y = torch.empty_like(x)
-    timed("layernorm_f32_256x5120", lambda: rr.rr_layernorm(y, x, g, bt, w.eps),
+    timed("layernorm_f32_256x5120", lambda k: rr.rr_layernorm(y, x, g, bt, w.eps),
           2 * w.M * w.N * 4 + 2 * w.N * 4, w.M, graph=True)
     # the floor for the two latency-bound shapes: a kernel that writes one
     # value (torch's fill), timed the same way
     one = torch.empty(1, device=dev)
-    timed("launch_floor_fill_1_value", lambda: one.fill_(1.0), 4, 1, graph=True)
+    timed("launch_floor_fill_1_value", lambda k: one.fill_(1.0), 4, 1, graph=True)
+    del x, g, bt, y
+
     rng = np.random.default_rng(0)
     M, N = 8192, 4096
-    x = workloads.to_dtype(rng.standard_normal((M, N), dtype=np.float32), "bf16").to(dev)
+    nb = 2 * M * N * 2 + 2 * N * 2
+    n = sets_for(nb)
+    xs = copies(workloads.to_dtype(rng.standard_normal((M, N), dtype=np.float32), "bf16").to(dev), n)
+    ys = [torch.empty_like(xs[0]) for _ in range(n)]
     g = workloads.to_dtype(workloads.gamma_vector(N, 1), "bf16").to(dev)
     bt = workloads.to_dtype(workloads.gamma_vector(N, 2) - 1.0, "bf16").to(dev)
-    y = torch.empty_like(x)
-    timed("layernorm_bf16_8192x4096", lambda: rr.rr_layernorm(y, x, g, bt, 1e-5),
-          2 * M * N * 2 + 2 * N * 2, M)
-    del x, g, bt, y
+    timed("layernorm_bf16_8192x4096", lambda k: rr.rr_layernorm(ys[k], xs[k], g, bt, 1e-5), nb, M, sets=n)
+    del xs, ys, g, bt
+
     b = bufs["sm_causal"]
     M, N = b["M"], b["N"]
     kept = int(np.minimum(N, np.arange(M) % 4096 + 1).sum())
     causal = rr.make_softmax_opts(causal_period=4096, causal_offset=0)
     timed("causal_softmax_f32_114688x4096_kept_keys_only",
-          lambda: rr.rr_softmax_rows_ex(b["y"], b["x"], causal, None), kept * 4 + M * N * 4, M)
-    b = bufs["sm_vocab"]
+          lambda k: rr.rr_softmax_rows_ex(b["y"], b["x"], causal, None), kept * 4 + M * N * 4, M)
+    sets = bufs["sm_vocab"]["sets"]
     lg = rr.make_softmax_opts(log_output=True)
     timed("log_softmax_bf16_f32_256x152064",
-          lambda: rr.rr_softmax_rows_ex(b["y"], b["x"], lg, b["ws"]), b["M"] * b["N"] * (2 + 4), b["M"])
+          lambda k: rr.rr_softmax_rows_ex(sets[k]["y"], sets[k]["x"], lg, sets[k]["ws"]),
+          sets[0]["M"] * sets[0]["N"] * (2 + 4), sets[0]["M"], sets=len(sets))
+
     # rows that are not whole vectors (contiguous rows of an odd width, every
     # row at its own offset): cut at aligned addresses
     M, N = 256, 50257                     # a 50257-entry vocabulary
-    x = workloads.to_dtype(rng.standard_normal((M, N), dtype=np.float32), "bf16").to(dev)
-    y = torch.empty((M, N), dtype=torch.float32, device=dev)
-    timed("softmax_bf16_f32_256x50257_rows_cut", lambda: rr.rr_softmax_rows(y, x, None), M * N * (2 + 4), M)
-    del x, y
+    nb = M * N * (2 + 4)
+    n = sets_for(nb)
+    xs = copies(workloads.to_dtype(rng.standard_normal((M, N), dtype=np.float32), "bf16").to(dev), n)
+    ys = [torch.empty((M, N), dtype=torch.float32, device=dev) for _ in range(n)]
+    timed("softmax_bf16_f32_256x50257_rows_cut", lambda k: rr.rr_softmax_rows(ys[k], xs[k], None), nb, M, sets=n)
+    del xs, ys
     M, N = 8192, 4097
-    x = workloads.to_dtype(rng.standard_normal((M, N), dtype=np.float32), "bf16").to(dev)
+    nb = 2 * M * N * 2 + N * 2
+    n = sets_for(nb)
+    xs = copies(workloads.to_dtype(rng.standard_normal((M, N), dtype=np.float32), "bf16").to(dev), n)
+    ys = [torch.empty_like(xs[0]) for _ in range(n)]
     g = workloads.to_dtype(workloads.gamma_vector(N, 3), "bf16").to(dev)
-    y = torch.empty_like(x)
-    timed("rmsnorm_bf16_8192x4097_rows_cut", lambda: rr.rr_rmsnorm(y, x, g, 1e-6), 2 * M * N * 2 + N * 2, M)
-    del x, g, y
+    timed("rmsnorm_bf16_8192x4097_rows_cut", lambda k: rr.rr_rmsnorm(ys[k], xs[k], g, 1e-6), nb, M, sets=n)
+    del xs, ys, g
+
+    # the vocabulary softmax at decode-size row counts: few long rows split
+    # over many workgroups (statistics pass, then the normalising pass)
+    full = bufs["sm_vocab"]["x"]
+    N = full.shape[1]
+    for M in (1, 16, 48):
+        nb = M * N * (2 + 4)
+        n = sets_for(nb)
+        xs = [full[(i * M) % 256:(i * M) % 256 + M].clone() if (i * M) % 256 + M <= 256 else full[:M].clone()
+              for i in range(n)]
+        ys = [torch.empty((M, N), dtype=torch.float32, device=dev) for _ in range(n)]
+        ws = rr.softmax_workspace(xs[0], torch.float32)
+        plan = rr.rr_query_plan(rr.RR_OP_SOFTMAX, M, N, rr.RR_BF16, rr.RR_F32)
+        timed(f"softmax_bf16_f32_{M}x{N}_split", lambda k: rr.rr_softmax_rows(ys[k], xs[k], ws), nb, M, sets=n,
+              graph=True)
+        out[f"softmax_bf16_f32_{M}x{N}_split"].update(
+            {"plan": plan["variant_name"], "chunks_per_row": plan["chunks_per_row"],
+             "read_once_bytes": nb, "two_pass_bytes": M * N * (2 + 2 + 4)})
+        del xs, ys, ws
     return out
 
 

@@ -621,6 +621,21 @@ rr_status softmax_options(const rr_softmax_opts* o, const char* who, rr_softmax_
   return RR_OK;
 }
 
+// Causal calls of the workgroup plan on aligned rows may hold two rows of a
+// period per workgroup, rows q and P - 1 - q, so that every workgroup reads
+// about one row of kept keys ([P1] section "二、它们在 Qwen2.5-7B 里的真实位置"
+// sizes the per-layer score softmax this serves).  Worth it where the kept
+// counts vary along the period (P + 2O at most 1.25 N) over whole periods;
+// each row is held as the plan holds it, so the two rows together stay
+// within 32 values per lane (the plan's at most 16 each).  Returns the
+// plan's vectors per lane when pairing, 0 for one row per workgroup.
+int causal_pair_nv(const rr_plan& p, int64_t M, int64_t N, int64_t P, int64_t O) {
+  if (p.variant != RR_VARIANT_BLOCK || p.row_shift || p.vec_elems <= 1 || N % p.vec_elems != 0) return 0;
+  if (p.vecs_per_lane * p.vec_elems > 16) return 0;
+  if (P < 2 || M < P || 4 * (P + 2 * O) > 5 * N) return 0;
+  return p.vecs_per_lane;
+}
+
 // noalloc: the workspace comes from the library's static scratch array
 // (rr_softmax_rows_strided_noalloc); workspace and workspace_bytes are unused.
 rr_status softmax_entry(const char* who, void* y, int64_t ldy, const void* x, int64_t ldx, int64_t M,
@@ -700,6 +715,7 @@ rr_status softmax_entry(const char* who, void* y, int64_t ldy, const void* x, in
   a.causal_offset = o.causal_offset < N ? o.causal_offset : N;
   a.log_output = o.log_output;
   a.ld = rr::RowStrides{ldx, ldy, 0};
+  a.pair_nv = o.causal ? causal_pair_nv(p, M, N, o.causal_period, a.causal_offset) : 0;
   const hipError_t e = rr::launch_softmax(p, in_dtype, out_dtype, a, grid_for(p),
                                           static_cast<hipStream_t>(stream));
   return hip_status(e, who);

@@ -1259,6 +1259,150 @@ __global__ __launch_bounds__(1024) void softmax_regs_kernel(const Tin* x, Tout* 
 }
 
 // ===========================================================================
+// Causal rule, two rows per workgroup (aligned rows of the workgroup plan).
+//
+// Under the causal rule row q of a period keeps q + O + 1 keys ([P1] section
+// "二、它们在 Qwen2.5-7B 里的真实位置": the attention scores of a layer), so a
+// workgroup per row reads anywhere from one key to a whole row while always
+// writing a whole row: a workgroup with a short row is bound by the latency
+// of its few loads, not by bytes, and the short rows of each period come
+// together in launch order.  Pairing row q with row P - 1 - q of the same
+// period gives every workgroup P + 2O + 1 kept keys between its two rows
+// (about one row) and two rows to write.  Each row is held exactly as
+// softmax_regs_kernel holds it (lane t owns vectors t, t + T, ...), with the
+// same per-lane pair, butterfly and slot stage, so both rows come out with
+// the bits that kernel gives them; the two rows share one barrier.  Rows past
+// the last whole period, and the middle row of an odd period, go alone.
+// ===========================================================================
+template <typename Tin, typename Tout, int NV, bool LOG>
+__global__ __launch_bounds__(1024) void softmax_causal_pair_kernel(const Tin* x, Tout* y, int64_t M, int N,
+                                                                   int64_t P, int64_t O, RowStrides ld) {
+  constexpr int VEC = softmax_vec<Tin, Tout>();
+  __shared__ MD slots_a[2][kMaxWavesPerGroup];   // [parity][wavefront], one set per row of the pair
+  __shared__ MD slots_b[2][kMaxWavesPerGroup];
+  MD (*const sl[2])[kMaxWavesPerGroup] = {slots_a, slots_b};
+  const RowLane rl = row_lane<false>();
+  const int nvec = N / VEC;
+  const int64_t per = (P + 1) / 2;          // work items per whole period
+  const int64_t whole = M / P;              // whole periods
+  const int64_t items = whole * per + (M - whole * P);
+  int parity = 0;
+  for (int64_t item = blockIdx.x; item < items; item += gridDim.x) {
+    int64_t row[2], q[2];                   // row[1] < 0: row[0] alone
+    if (item < whole * per) {
+      const int64_t blk = item / per;
+      q[0] = item - blk * per;
+      q[1] = P - 1 - q[0];
+      row[0] = blk * P + q[0];
+      row[1] = q[1] != q[0] ? blk * P + q[1] : -1;
+    } else {
+      row[0] = whole * P + (item - whole * per);
+      q[0] = row[0] - whole * P;
+      row[1] = -1;
+      q[1] = 0;
+    }
+    const int npair = row[1] < 0 ? 1 : 2;
+    int keys[2], nkv[2];
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      keys[r] = r < npair ? (int)(q[r] + O + 1 < (int64_t)N ? q[r] + O + 1 : (int64_t)N) : 0;
+      nkv[r] = (keys[r] + VEC - 1) / VEC;   // vectors holding kept keys
+    }
+    float v[2][NV][VEC];
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const Tin* xr = x + (r < npair ? row[r] : row[0]) * ld.x;
+#pragma unroll
+      for (int k = 0; k < NV; ++k) {
+        const int vi = k * rl.T + rl.t;
+        if (vi < nkv[r]) {
+          load_vec<Tin, VEC>(xr + (int64_t)vi * VEC, v[r][k]);
+        } else {
+#pragma unroll
+          for (int i = 0; i < VEC; ++i) v[r][k][i] = kNegInf;
+        }
+      }
+    }
+    MD p[2];
+    float ml[2];
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      if (keys[r] < N) {
+#pragma unroll
+        for (int k = 0; k < NV; ++k) mask_keys<VEC>(v[r][k], (k * rl.T + rl.t) * VEC, keys[r]);
+      }
+      float m = kNegInf;
+#pragma unroll
+      for (int k = 0; k < NV; ++k)
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) m = __builtin_fmaxf(m, v[r][k][i]);
+      const float shift = (m == kNegInf) ? 0.0f : m;
+      float dl = 0.0f;
+#pragma unroll
+      for (int k = 0; k < NV; ++k)
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) {
+          const float e = exp_out<Tout>(v[r][k][i] - shift);
+          dl += e;
+          if constexpr (!LOG) v[r][k][i] = e;   // plain softmax keeps e_i, log-softmax keeps x_i
+        }
+      ml[r] = m;
+      p[r].m = m;
+      p[r].d = dl;
+      p[r] = wave_md(p[r]);
+    }
+    {
+      // both rows through the slot stage of group_md, with one barrier
+      stress_delay();
+      if (rl.lane == 0) {
+        sl[0][parity][rl.w] = p[0];
+        sl[1][parity][rl.w] = p[1];
+      }
+      __syncthreads();
+      stress_poison(sl[0], parity, rl.w, rl.lane);
+      stress_poison(sl[1], parity, rl.w, rl.lane);
+      stress_delay();
+      const int j = rl.lane & (kMaxWavesPerGroup - 1);
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        MD t;
+        if (j < rl.nw) {
+          t = sl[r][parity][j];
+        } else {
+          t.m = kNegInf;
+          t.d = 0.0f;
+        }
+        t = md_merge(t, dpp_md<kDppQuadXor1>(t));
+        t = md_merge(t, dpp_md<kDppQuadXor2>(t));
+        t = md_merge(t, dpp_md<kDppRowHalfMirror>(t));
+        p[r] = md_merge(t, dpp_md<kDppRowMirror>(t));
+      }
+      parity ^= 1;
+    }
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      if (r >= npair) break;
+      float c = 0.0f, lg = 0.0f;
+      if constexpr (LOG) {
+        lg = __builtin_logf(p[r].d);
+      } else {
+        c = (ml[r] == kNegInf) ? 0.0f : exp_out<Tout>(ml[r] - p[r].m) / p[r].d;
+        if (p[r].m == kNegInf) c = __builtin_nanf("");
+      }
+      Tout* yr = y + row[r] * ld.y;
+#pragma unroll
+      for (int k = 0; k < NV; ++k) {
+        const int vi = k * rl.T + rl.t;
+        float o[VEC];
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) o[i] = LOG ? (v[r][k][i] - p[r].m) - lg : v[r][k][i] * c;
+        if (vi < nvec) store_vec<Tout, VEC>(yr + (int64_t)vi * VEC, o);
+      }
+    }
+  }
+}
+
+// ===========================================================================
 // Softmax, a long row held packed in registers (BLOCK, large NV).
 //
 // For rows too long for 32 widened values per lane, a workgroup of up to 16
@@ -2044,11 +2188,45 @@ hipError_t softmax_sub(const rr_plan& p, const SmCall<Tin, Tout>& c, int64_t gri
   return hipGetLastError();
 }
 
+// The causal rule with two rows of a period per workgroup (the host chose
+// it for aligned rows of the workgroup plan; pair_nv is the plan's vectors
+// per lane, held for each of the two rows).
+template <typename Tin, typename Tout, bool LOG>
+hipError_t softmax_causal_pairs(const rr_plan& p, const SmCall<Tin, Tout>& c, int pair_nv, hipStream_t s) {
+  const int64_t per = (c.cp + 1) / 2;
+  const int64_t whole = c.M / c.cp;
+  const int64_t items = whole * per + (c.M - whole * c.cp);
+  int64_t grid = items;
+  const int64_t cap = 0xffffffffLL / p.block_threads;
+  if (grid > cap) grid = cap;
+#if RR_STRESS
+  grid = grid < 37 ? grid : 37;   // the race-stress build's grid cap
+#endif
+  const dim3 b(p.block_threads);
+  // the plan's vectors per lane for each of the two rows (16 values at most)
+  if (pair_nv != p.vecs_per_lane) return hipErrorInvalidValue;
+  switch (pair_nv) {
+    case 1: softmax_causal_pair_kernel<Tin, Tout, 1, LOG><<<grid1(grid), b, 0, s>>>(c.x, c.y, c.M, c.N, c.cp, c.co, c.ld); break;
+    case 2: softmax_causal_pair_kernel<Tin, Tout, 2, LOG><<<grid1(grid), b, 0, s>>>(c.x, c.y, c.M, c.N, c.cp, c.co, c.ld); break;
+    case 4:
+      if constexpr (softmax_vec<Tin, Tout>() * 4 <= 16) {
+        softmax_causal_pair_kernel<Tin, Tout, 4, LOG><<<grid1(grid), b, 0, s>>>(c.x, c.y, c.M, c.N, c.cp, c.co, c.ld);
+        break;
+      }
+      return hipErrorInvalidValue;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 template <typename Tin, typename Tout, bool LOG, bool CAUSAL>
 hipError_t softmax_typed(const rr_plan& p, const SmCall<Tin, Tout>& c, void* ws, int64_t grid,
-                         hipStream_t s) {
+                         hipStream_t s, int pair_nv = 0) {
   const dim3 b(p.block_threads);
   const dim3 g = grid1(grid);
+  if constexpr (CAUSAL) {
+    if (pair_nv > 0) return softmax_causal_pairs<Tin, Tout, LOG>(p, c, pair_nv, s);
+  }
   if (p.variant == RR_VARIANT_SUBWAVE) {
     if (p.vec_elems == 1) return softmax_sub<Tin, Tout, 1, LOG, CAUSAL>(p, c, grid, s);
     return softmax_sub<Tin, Tout, softmax_vec<Tin, Tout>(), LOG, CAUSAL>(p, c, grid, s);
@@ -2099,8 +2277,8 @@ hipError_t softmax_io(const rr_plan& p, const SoftmaxArgs& a, int64_t grid, hipS
   // the causal rule and log output are compile-time switches, so the plain
   // softmax kernels carry none of their code
   if (c.cp > 0) {
-    if (a.log_output) return softmax_typed<Tin, Tout, true, true>(p, c, a.workspace, grid, s);
-    return softmax_typed<Tin, Tout, false, true>(p, c, a.workspace, grid, s);
+    if (a.log_output) return softmax_typed<Tin, Tout, true, true>(p, c, a.workspace, grid, s, a.pair_nv);
+    return softmax_typed<Tin, Tout, false, true>(p, c, a.workspace, grid, s, a.pair_nv);
   }
   if (a.log_output) return softmax_typed<Tin, Tout, true, false>(p, c, a.workspace, grid, s);
   return softmax_typed<Tin, Tout, false, false>(p, c, a.workspace, grid, s);

@@ -57,6 +57,9 @@ struct SoftmaxArgs {
   int64_t causal_offset;
   int log_output;
   RowStrides ld;   // r unused
+  // causal rule only: > 0 runs two rows of a period per workgroup (rows q
+  // and P - 1 - q) with this many vectors per lane; 0 one row per workgroup
+  int pair_nv;
 };
 
 // Enqueue the softmax kernel(s) that `plan` names (two for SPLIT).

@@ -144,6 +144,14 @@ CAUSAL_CASES = [
     (300, 1025, 300, 0),        # odd widths: rows cut at aligned addresses (wave, block, packed)
     (40, 4097, 40, 4057),
     (66, 50257, 66, 50191),
+    # rows q and P - 1 - q of a period in one workgroup (aligned rows of the
+    # workgroup plan with kept counts that vary along the period): an odd
+    # period (its middle row alone), rows past the last whole period, an
+    # offset, 16 wavefronts per row, four vectors per lane
+    (129, 4096, 43, 0),
+    (1000, 3072, 700, 100),
+    (64, 8192, 64, 1800),
+    (2048, 16384, 2048, 0),
 ]
 
 
@@ -224,7 +232,8 @@ def test_causal_equals_plain_softmax_on_masked_input_bitwise():
     """The causal kernel on garbage-masked rows gives the same bits as the
     plain kernel on rows with -inf in the masked region: the masked keys
     enter the arithmetic as -inf either way, in the same order."""
-    for (M, N, P, O) in [(64, 1024, 64, 960), (65, 4096, 64, 0), (1030, 40000, 1030, 38970)]:
+    for (M, N, P, O) in [(64, 1024, 64, 960), (65, 4096, 64, 0), (1030, 40000, 1030, 38970),
+                         (129, 4096, 43, 0), (1000, 3072, 700, 100), (300, 16384, 256, 0)]:
         given, meant = causal_inputs(M, N, P, O, seed=5, dt="f32")
         yc = run_ex(given, torch.float32, period=P, offset=O)
         yp = run_ex(torch.from_numpy(meant.astype(np.float32)), torch.float32)
