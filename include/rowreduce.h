@@ -31,9 +31,9 @@
  *     Same-stream order is the only ordering the library relies on.  The
  *     calls only enqueue kernels (no memsets, copies or host callbacks), so
  *     a caller may capture them into a HIP graph; a captured call reads its
- *     buffers when the graph replays.  The opt-in one-kernel split variant
- *     (RR_VARIANT_SPLIT_ONE_KERNEL) is the exception: its workspace tags
- *     are chosen at launch, so it must not be captured.
+ *     buffers when the graph replays.  (The one-kernel form of the split row
+ *     tags its workspace slots at launch, so a call on a capturing stream
+ *     runs the two-kernel form, with the same bits.)
  *   - Errors: arguments are checked on the host before anything is enqueued;
  *     a failed check returns a non-zero rr_status and enqueues nothing.
  *     M == 0 is a successful no-op.  An empty row (N or H < 1) is the
@@ -319,17 +319,20 @@ typedef enum rr_op {
  *   WAVE  one 64-lane wavefront per row, row held in VGPRs (N <= 2048)
  *   BLOCK one workgroup of up to 16 wavefronts per row, row held in VGPRs,
  *         wavefront totals combined through LDS (N <= 32768)
- *   SPLIT several workgroups per row (softmax, long rows with few rows):
- *         a first kernel summarises each chunk as (m, d) into the workspace,
- *         a second merges a row's chunks and normalises (re-reading x).  Rows
- *         of more than 64 chunks get a merge kernel in between that folds
- *         each row's pairs into one, so the cost stays linear in N.
- *         SPLIT_ONE_KERNEL (opt-in) does both in one cooperative kernel whose
- *         workgroups keep their chunk in registers and wait for the row's
- *         other chunks; it reads x once but measured slower on MI355X, where
- *         the cross-workgroup hand-off costs L2 write-backs and invalidations.
- *         It falls back to the two kernels when the device cannot hold a
- *         row's chunks at once.  Both forms give the same bits.
+ *   SPLIT several workgroups per row (softmax, long rows with few rows),
+ *         each summarising its chunk as (m, d) into the workspace.  Where the
+ *         rows are aligned, a row has at most 64 chunks, the device holds
+ *         every workgroup of the grid at once and the stream is not
+ *         capturing a graph, this is ONE kernel: each workgroup keeps its
+ *         chunk in registers, publishes its pair in a tagged slot, waits (a
+ *         bounded time, then summarises a missing chunk itself) for the
+ *         row's other pairs, merges them and normalises, so x is read once.
+ *         Otherwise two kernels: the summaries, then a second that merges a
+ *         row's pairs and normalises, re-reading x (rows of more than 64
+ *         chunks get a merge kernel in between that folds each row's pairs
+ *         into one, so the cost stays linear in N).  Both forms give the
+ *         same bits.  SPLIT_ONE_KERNEL forces the split on aligned rows;
+ *         SPLIT_TWO_KERNELS forces the two-kernel form (diagnostics).
  *   LOOP  one workgroup per row streaming the row twice (any N; long rows
  *         with many rows; causal rows too long for BLOCK; rows whose input
  *         and output sit at different offsets within a vector, element by
@@ -344,8 +347,9 @@ typedef enum rr_variant {
   RR_VARIANT_BLOCK = 2,
   RR_VARIANT_SPLIT = 3,
   RR_VARIANT_LOOP = 4,
-  RR_VARIANT_SPLIT_ONE_KERNEL = 5, /* SPLIT as one cooperative kernel (opt-in) */
-  RR_VARIANT_SUBWAVE = 6           /* short rows, several rows per wavefront */
+  RR_VARIANT_SPLIT_ONE_KERNEL = 5, /* SPLIT on aligned rows (one kernel where it can) */
+  RR_VARIANT_SUBWAVE = 6,          /* short rows, several rows per wavefront */
+  RR_VARIANT_SPLIT_TWO_KERNELS = 7 /* SPLIT always as two kernels */
 } rr_variant;
 
 typedef struct rr_plan {

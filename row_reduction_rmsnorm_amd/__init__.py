@@ -11,7 +11,7 @@ from .binding import (  # noqa: F401
     RR_ERR_WORKSPACE, RR_F32, RR_OK, RR_OP_FUSED_ADD_RMSNORM, RR_OP_LAYERNORM, RR_OP_RMSNORM,
     RR_OP_SOFTMAX, RR_OP_SOFTMAX_CAUSAL,
     RR_VARIANT_AUTO, RR_VARIANT_BLOCK, RR_VARIANT_LOOP, RR_VARIANT_SPLIT, RR_VARIANT_SPLIT_ONE_KERNEL,
-    RR_VARIANT_SUBWAVE, RR_VARIANT_WAVE,
+    RR_VARIANT_SUBWAVE, RR_VARIANT_WAVE, RR_VARIANT_SPLIT_TWO_KERNELS,
     RowReduceError, VARIANT_NAMES, check, dtype_code, fused_add_rmsnorm, last_error_message,
     layernorm, lib, raw_layernorm, rr_layernorm,
     raw_fused_add_rmsnorm, raw_rmsnorm, raw_softmax_rows, rmsnorm, rr_fused_add_rmsnorm,

@@ -44,7 +44,8 @@ RR_VARIANT_SPLIT = 3
 RR_VARIANT_LOOP = 4
 RR_VARIANT_SPLIT_ONE_KERNEL = 5
 RR_VARIANT_SUBWAVE = 6
-VARIANT_NAMES = {0: "auto", 1: "wave", 2: "block", 3: "split", 4: "loop", 5: "split1", 6: "subwave"}
+RR_VARIANT_SPLIT_TWO_KERNELS = 7
+VARIANT_NAMES = {0: "auto", 1: "wave", 2: "block", 3: "split", 4: "loop", 5: "split1", 6: "subwave", 7: "split2"}
 
 # Every function include/rowreduce.h declares.
 EXPORTS = (

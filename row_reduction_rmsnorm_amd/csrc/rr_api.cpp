@@ -396,12 +396,14 @@ rr_status make_plan(rr_op op, int64_t M, int64_t N, int din, int dout, int align
       break;
     case RR_VARIANT_SPLIT:
     case RR_VARIANT_SPLIT_ONE_KERNEL:
+    case RR_VARIANT_SPLIT_TWO_KERNELS:
       ok = vec > 1 && op == RR_OP_SOFTMAX && !causal;
       if (ok) {
         plan_split(p, vec, per16, nvec);
         p->variant = forced;
-      } else if (forced == RR_VARIANT_SPLIT && shiftable && op == RR_OP_SOFTMAX && !causal) {
+      } else if (forced != RR_VARIANT_SPLIT_ONE_KERNEL && shiftable && op == RR_OP_SOFTMAX && !causal) {
         plan_split(p, vw, per16_s, nvec_any);   // the one-kernel form takes aligned rows only
+        p->variant = forced;
         p->row_shift = 1;
         ok = true;
       }
@@ -433,7 +435,8 @@ rr_status make_plan(rr_op op, int64_t M, int64_t N, int din, int dout, int align
                 forced, (int)op, (long long)N, vec);
   }
   if (p->chunks_per_row == 0) p->chunks_per_row = 1;
-  if (p->variant == RR_VARIANT_SPLIT || p->variant == RR_VARIANT_SPLIT_ONE_KERNEL) {
+  if (p->variant == RR_VARIANT_SPLIT || p->variant == RR_VARIANT_SPLIT_ONE_KERNEL ||
+      p->variant == RR_VARIANT_SPLIT_TWO_KERNELS) {
     if (p->chunks_per_row > (int64_t)1 << 30) return fail(RR_ERR_UNSUPPORTED, "too many chunks");
     p->work_items = M * p->chunks_per_row;
     p->workspace_bytes = (size_t)M * (size_t)p->chunks_per_row * 16u;
@@ -456,10 +459,9 @@ int64_t grid_for(const rr_plan& p) {
   const int64_t kMaxGrid = 0xffffffffLL / (p.block_threads > 0 ? p.block_threads : 1);
 #if RR_STRESS
   // the race-stress build (see rr_kernels.hip): few workgroups, each walking
-  // many rows, so that the LDS slot sets are reused many times; the
-  // cooperative split keeps its grid (its waits need every workgroup
-  // resident, which it checks against its own grid)
-  if (p.variant != RR_VARIANT_SPLIT_ONE_KERNEL && g > 37) return 37;
+  // many rows, so that the LDS slot sets are reused many times (the
+  // one-kernel split sizes its own grid, one workgroup per chunk)
+  if (g > 37) return 37;
 #endif
   return g > kMaxGrid ? kMaxGrid : g;
 }
@@ -688,8 +690,6 @@ rr_status softmax_entry(const char* who, void* y, int64_t ldy, const void* x, in
     if (p.workspace_bytes > rr::kNoAllocScratchBytes)
       return fail(RR_ERR_WORKSPACE, "%s: this shape needs %zu bytes of split-row scratch; the static scratch holds %zu",
                   who, p.workspace_bytes, rr::kNoAllocScratchBytes);
-    // (a forced one-kernel split runs as the two kernels here: same bits)
-    if (p.variant == RR_VARIANT_SPLIT_ONE_KERNEL) p.variant = RR_VARIANT_SPLIT;
     hipError_t se = hipSuccess;
     workspace = rr::noalloc_scratch(&se);
     if (!workspace) return hip_status(se != hipSuccess ? se : hipErrorInvalidSymbol, who);
@@ -799,7 +799,7 @@ rr_status rr_query_plan(rr_op op, int64_t M, int64_t N, rr_dtype in_dtype, rr_dt
 #if RR_DIAG
 rr_status rr_set_variant_override(rr_variant v) {
   g_err[0] = '\0';
-  if (v < RR_VARIANT_AUTO || v > RR_VARIANT_SUBWAVE)
+  if (v < RR_VARIANT_AUTO || v > RR_VARIANT_SPLIT_TWO_KERNELS)
     return fail(RR_ERR_INVALID_ARG, "rr_set_variant_override: unknown variant %d", (int)v);
   g_override.store(v, std::memory_order_relaxed);
   return RR_OK;

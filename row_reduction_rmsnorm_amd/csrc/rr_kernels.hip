@@ -30,6 +30,9 @@
 //    dispatch's work-items fit in 32 bits): workgroups then walk rows with a
 //    stride of gridDim.x; gamma stays in registers across rows.
 #include <time.h>
+#include <unistd.h>
+
+#include <chrono>
 
 #include <atomic>
 #include <map>
@@ -1609,6 +1612,46 @@ struct SplitSlot {
 };
 static_assert(sizeof(SplitSlot) == 16, "slot layout");
 
+// Pass A's summary of a chunk held in v (NV packed vectors per lane): the
+// maximum, then the sum of exp(x - max), per lane; the wave all-reduce; the
+// LDS stage.  Every lane of the workgroup ends with the same bits.  The
+// one-kernel split calls the same code, so both forms agree bit for bit.
+template <int NV, typename Tin, int VEC>
+__device__ __forceinline__ MD split_chunk_stat(const Packed<Tin, VEC> (&v)[NV], const RowLane& rl,
+                                               MD (*slots)[kMaxWavesPerGroup], int& parity) {
+  float ml = kNegInf;
+#pragma unroll
+  for (int k = 0; k < NV; ++k)
+#pragma unroll
+    for (int i = 0; i < VEC; ++i) ml = __builtin_fmaxf(ml, v[k].get(i));
+  const float shift = (ml == kNegInf) ? 0.0f : ml;
+  float dl = 0.0f;
+#pragma unroll
+  for (int k = 0; k < NV; ++k)
+#pragma unroll
+    for (int i = 0; i < VEC; ++i) dl += exp_shifted(v[k].get(i) - shift);
+  MD p;
+  p.m = ml;
+  p.d = dl;
+  p = wave_md(p);
+  p = group_md(p, rl.nw, rl.w, rl.lane, slots, parity);
+  parity ^= 1;
+  return p;
+}
+
+// Pass A's loads of chunk c of an aligned row: lane t's vectors
+// c * 256 * NV + k * 256 + t, streaming; -inf past the row's nvec vectors.
+template <int NV, typename Tin, int VEC>
+__device__ __forceinline__ void split_chunk_load(const Tin* xr, int nvec, int c, int t,
+                                                 Packed<Tin, VEC> (&v)[NV]) {
+#pragma unroll
+  for (int k = 0; k < NV; ++k) {
+    const int vi = c * 256 * NV + k * 256 + t;
+    if (vi < nvec) v[k].template load<true>(xr + (int64_t)vi * VEC);
+    else v[k].fill(kNegInf);
+  }
+}
+
 template <typename Tin, typename Tout, int NV, bool SHIFT>
 __global__ __launch_bounds__(256) void softmax_split_stats_kernel(const Tin* x, SplitSlot* ws,
                                                                   int64_t M, int N, int S, RowStrides ld) {
@@ -1628,14 +1671,18 @@ __global__ __launch_bounds__(256) void softmax_split_stats_kernel(const Tin* x, 
     const int lead = SHIFT ? row_lead(xr, VEC) : 0;   // (its own frame: it writes no row)
     const int nvec_row = SHIFT ? (lead + N + VEC - 1) / VEC : nvec;
     Packed<Tin, VEC> v[NV];
+    // streaming loads (measured faster than temporal ones that would leave
+    // the chunk in the last-level cache for pass B, with inputs cold in HBM)
+    if constexpr (!SHIFT) {
+      split_chunk_load<NV>(xr, nvec, c, rl.t, v);
+    } else {
 #pragma unroll
-    for (int k = 0; k < NV; ++k) {
-      const int vi = c * CV + k * kThreads + rl.t;
-      const int e0 = vi * VEC - lead;
-      // streaming load (measured faster than a temporal one that would leave
-      // the chunk in the last-level cache for pass B, with inputs cold in HBM)
-      if (vi < nvec_row && (!SHIFT || (e0 >= 0 && e0 + VEC <= N))) v[k].template load<true>(xr + e0);
-      else v[k].fill(kNegInf);
+      for (int k = 0; k < NV; ++k) {
+        const int vi = c * CV + k * kThreads + rl.t;
+        const int e0 = vi * VEC - lead;
+        if (vi < nvec_row && e0 >= 0 && e0 + VEC <= N) v[k].template load<true>(xr + e0);
+        else v[k].fill(kNegInf);
+      }
     }
     if constexpr (SHIFT) {
       // the row's first and last vector after every whole vector is in flight
@@ -1650,23 +1697,7 @@ __global__ __launch_bounds__(256) void softmax_split_stats_kernel(const Tin* x, 
         }
       }
     }
-    float ml = kNegInf;
-#pragma unroll
-    for (int k = 0; k < NV; ++k)
-#pragma unroll
-      for (int i = 0; i < VEC; ++i) ml = __builtin_fmaxf(ml, v[k].get(i));
-    const float shift = (ml == kNegInf) ? 0.0f : ml;
-    float dl = 0.0f;
-#pragma unroll
-    for (int k = 0; k < NV; ++k)
-#pragma unroll
-      for (int i = 0; i < VEC; ++i) dl += exp_shifted(v[k].get(i) - shift);
-    MD p;
-    p.m = ml;
-    p.d = dl;
-    p = wave_md(p);
-    p = group_md(p, rl.nw, rl.w, rl.lane, slots, parity);
-    parity ^= 1;
+    const MD p = split_chunk_stat<NV>(v, rl, slots, parity);
     if (threadIdx.x == 0) {
       ws[item].m = p.m;
       ws[item].d = p.d;
@@ -1781,116 +1812,137 @@ __global__ __launch_bounds__(256) void softmax_split_apply_kernel(const Tin* x, 
 }
 
 // ===========================================================================
-// Softmax, split row in ONE kernel (SPLIT, cooperative form).
+// Softmax, split row in ONE kernel (SPLIT_ONE_KERNEL).
 //
-// The same chunking and the same arithmetic as the two kernels above, but a
+// The same chunks and the same arithmetic as the two kernels above, but a
 // workgroup keeps its chunk in registers while the row's other chunks are
-// summarised, so x is read from HBM once ([P4] section "练习": "the last block
-// to finish" instead of a second kernel; the pages' PyTorch reading in [P2]
-// section 九 describes the same last-arrival idea for reductions).
+// summarised, so x is read from HBM once ([P4] section "练习": the last block
+// to finish instead of a second kernel; [P2] section 九 reads the same
+// last-arrival idea in PyTorch's reductions).
 //
-//  * Launch: cooperative (every workgroup resident), grid G <= items; a
-//    workgroup handles items g, g + G, g + 2G, ... in increasing order.
-//  * Publish: thread 0 stores the chunk's (m, d) into its slot and then the
-//    slot's 64-bit tag with release semantics at agent scope.  The tag is a
-//    value unique to this call (the host increments it per call), so slots
-//    left by earlier calls or uninitialised memory never look published.
-//  * Wait: lane j of every wavefront polls the tags of slots j, j + 64, ...
-//    with relaxed agent-scope loads until each equals the call's tag, then the
-//    wavefront issues one acquire fence and reads the (m, d) values.
-//  * No deadlock: with all G workgroups resident and S <= G, a workgroup only
-//    waits for items of its own row; a cycle of waits would need every
-//    workgroup's current item to be smaller than the next one's, around the
-//    cycle, which cannot be.  Every wait is also bounded (kSpinLimit polls), so
-//    every wavefront reaches the end even if that argument were broken; a
-//    wavefront whose wait gave up writes NaN over its chunk instead of
-//    probabilities, so the failure shows in the output.
-//  * Graph capture: the tag is fixed when the kernel is launched, so a
-//    replayed graph would find its own earlier tags in the slots; a call
-//    made while its stream is capturing runs the two-kernel form instead
-//    (the same bits).
+//  * Launch: an ordinary launch, one workgroup per chunk, taken only when
+//    the device holds the whole grid at once (its occupancy) and rows have
+//    at most 64 chunks.
+//  * Publish: thread 0 writes the chunk's (m, d) as two 64-bit words with
+//    relaxed agent-scope atomic stores: the low half of each word holds m's
+//    (d's) bits, the high half the call's 32-bit tag, which differs from
+//    call to call.  No fence is needed: each word is read whole, so a reader
+//    that finds the tag in both words holds this call's m and d.  (Both
+//    words carry the same per-call tag: were they to carry two halves of a
+//    longer one, consecutive calls would share the upper half and a reader
+//    could pair this call's m with the last call's d.)  Slots left by
+//    earlier calls carry other tags; uninitialised memory matches in both
+//    words with probability 2^-64.
+//  * Wait: lane s of wavefront 0 polls slot s with relaxed agent-scope
+//    loads until both words carry the tag, for at most kSplitWaitTicks of
+//    the 100 MHz real-time clock.  A chunk still missing then (its
+//    workgroup kept from running by other work on the device, say) is
+//    summarised by this workgroup from x itself with pass A's code, so the
+//    result has the same bits whichever way a summary arrived.
+//  * The row's summaries go through LDS to every wavefront, lane s holding
+//    chunk s's pair, which is exactly what pass B's lanes hold after
+//    folding the workspace into the identity; the wave all-reduce and the
+//    outputs, written from the registers, follow as in pass B.
+//  * Graph capture: the tag is fixed at launch, so a replayed graph would
+//    find its own earlier tags in the slots; a capturing stream takes the
+//    two kernels instead.
 // ===========================================================================
-constexpr int kSpinLimit = 1 << 22;
+constexpr int kSplitFusedMaxChunks = kWave;         // one slot per lane of a wavefront
+constexpr uint64_t kSplitWaitTicks = 4000;          // 40 us of the 100 MHz real-time clock
 
-template <typename Tin, typename Tout, int NV>
-__global__ __launch_bounds__(256) void softmax_split_fused_kernel(const Tin* x, Tout* y,
-                                                                  SplitSlot* slots_ws, int64_t M,
-                                                                  int N, int S, uint64_t tag, RowStrides ld) {
+// The one-kernel form's view of a workspace slot: two tagged 64-bit words.
+struct SplitWords {
+  uint64_t w0;   // tag << 32 | m's bits
+  uint64_t w1;   // tag << 32 | d's bits
+};
+static_assert(sizeof(SplitWords) == sizeof(SplitSlot), "slot layout");
+
+template <typename Tin, typename Tout, int NV, bool LOG>
+__global__ __launch_bounds__(256) void softmax_split_fused_kernel(const Tin* x, Tout* y, SplitSlot* ws,
+                                                                  int64_t M, int N, int S, uint32_t tag,
+                                                                  RowStrides ld) {
   constexpr int VEC = softmax_vec<Tin, Tout>();
-  constexpr int kThreads = 256;
-  constexpr int CV = kThreads * NV;
+  constexpr int CV = 256 * NV;
   __shared__ MD slots[2][kMaxWavesPerGroup];
+  __shared__ MD got[kSplitFusedMaxChunks];
+  __shared__ uint64_t missing_mask;
   const RowLane rl = row_lane<false>();
   const int nvec = N / VEC;
-  const int64_t items = M * (int64_t)S;
+  const int64_t item = blockIdx.x;            // the host launches one workgroup per chunk
+  if (item >= M * (int64_t)S) return;         // (uniform)
+  const int64_t row = item / S;
+  const int c = (int)(item - row * S);
+  const Tin* xr = x + row * ld.x;
   int parity = 0;
-  for (int64_t item = blockIdx.x; item < items; item += gridDim.x) {
-    const int64_t row = item / S;
-    const int c = (int)(item - row * S);
-    const int64_t ox = row * ld.x, oy = row * ld.y;
-    Packed<Tin, VEC> v[NV];
-#pragma unroll
-    for (int k = 0; k < NV; ++k) {
-      const int vi = c * CV + k * kThreads + rl.t;
-      if (vi < nvec) v[k].template load<true>(x + ox + (int64_t)vi * VEC);
-      else v[k].fill(kNegInf);
+  Packed<Tin, VEC> v[NV];
+  split_chunk_load<NV>(xr, nvec, c, rl.t, v);
+  const MD p = split_chunk_stat<NV>(v, rl, slots, parity);
+  SplitWords* words = reinterpret_cast<SplitWords*>(ws + row * S);
+  if (threadIdx.x == 0) {
+    __hip_atomic_store(&words[c].w0, ((uint64_t)tag << 32) | __float_as_uint(p.m), __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(&words[c].w1, ((uint64_t)tag << 32) | __float_as_uint(p.d), __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+  }
+  if (rl.w == 0) {
+    // lane s waits for chunk s (its own chunk it already has)
+    MD b;
+    b.m = kNegInf;
+    b.d = 0.0f;
+    bool have = rl.lane >= S;
+    if (rl.lane == c) {
+      b = p;
+      have = true;
     }
-    // chunk summary, exactly as the two-kernel form computes it
-    float ml = kNegInf;
-#pragma unroll
-    for (int k = 0; k < NV; ++k)
-#pragma unroll
-      for (int i = 0; i < VEC; ++i) ml = __builtin_fmaxf(ml, v[k].get(i));
-    const float shift = (ml == kNegInf) ? 0.0f : ml;
-    float dl = 0.0f;
-#pragma unroll
-    for (int k = 0; k < NV; ++k)
-#pragma unroll
-      for (int i = 0; i < VEC; ++i) dl += exp_shifted(v[k].get(i) - shift);
-    MD p;
-    p.m = ml;
-    p.d = dl;
-    p = wave_md(p);
-    p = group_md(p, rl.nw, rl.w, rl.lane, slots, parity);
-    parity ^= 1;
-    SplitSlot* row_slots = slots_ws + row * S;
-    if (threadIdx.x == 0) {
-      row_slots[c].m = p.m;
-      row_slots[c].d = p.d;
-      __hip_atomic_store(&row_slots[c].tag, tag, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-    }
-    // wait for the row's chunks, then merge them in the same order as pass B
-    bool gave_up = false;
-    for (int s = rl.lane; s < S; s += kWave) {
-      int spin = 0;
-      for (; spin < kSpinLimit; ++spin) {
-        if (__hip_atomic_load(&row_slots[s].tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == tag) break;
-        __builtin_amdgcn_s_sleep(1);
+    const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+    while (!have) {
+      const uint64_t a = __hip_atomic_load(&words[rl.lane].w0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const uint64_t e = __hip_atomic_load(&words[rl.lane].w1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if ((uint32_t)(a >> 32) == tag && (uint32_t)(e >> 32) == tag) {
+        b.m = __uint_as_float((uint32_t)a);
+        b.d = __uint_as_float((uint32_t)e);
+        have = true;
+        break;
       }
-      gave_up = gave_up || spin == kSpinLimit;
+      if (__builtin_amdgcn_s_memrealtime() - t0 > kSplitWaitTicks) break;
+      __builtin_amdgcn_s_sleep(2);
     }
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-    MD q;
+    if (rl.lane < S) got[rl.lane] = b;
+    const uint64_t miss = __ballot(!have);
+    if (rl.lane == 0) missing_mask = miss;
+  }
+  __syncthreads();
+  // chunks whose summaries did not arrive in time: summarised here, from x
+  uint64_t miss = missing_mask;                 // (uniform)
+  while (miss) {
+    const int s = __builtin_ctzll(miss);
+    miss &= miss - 1;
+    Packed<Tin, VEC> u[NV];
+    split_chunk_load<NV>(xr, nvec, s, rl.t, u);
+    const MD r = split_chunk_stat<NV>(u, rl, slots, parity);
+    if (threadIdx.x == 0) got[s] = r;
+  }
+  __syncthreads();
+  MD q;
+  if (rl.lane < S) {
+    q = got[rl.lane];
+  } else {
     q.m = kNegInf;
     q.d = 0.0f;
-    for (int s = rl.lane; s < S; s += kWave) {
-      MD b;
-      b.m = row_slots[s].m;
-      b.d = row_slots[s].d;
-      q = md_merge(q, b);
-    }
-    q = wave_md(q);
-    // a wait that gave up anywhere in the wavefront poisons its outputs
-    if (__any(gave_up)) q.m = __builtin_nanf("");
-    const float inv_d = (q.m == kNegInf) ? __builtin_nanf("") : 1.0f / q.d;
+  }
+  q = wave_md(q);
+  const float inv_d = (q.m == kNegInf) ? __builtin_nanf("") : 1.0f / q.d;
+  const float lg = LOG ? __builtin_logf(q.d) : 0.0f;
+  Tout* yr = y + row * ld.y;
 #pragma unroll
-    for (int k = 0; k < NV; ++k) {
-      const int vi = c * CV + k * kThreads + rl.t;
-      float o[VEC];
+  for (int k = 0; k < NV; ++k) {
+    const int vi = c * CV + k * 256 + rl.t;
+    float o[VEC];
 #pragma unroll
-      for (int i = 0; i < VEC; ++i) o[i] = exp_out<Tout>(v[k].get(i) - q.m) * inv_d;
-      if (vi < nvec) store_vec<Tout, VEC, false>(y + oy + (int64_t)vi * VEC, o);
-    }
+    for (int i = 0; i < VEC; ++i)
+      o[i] = LOG ? (v[k].get(i) - q.m) - lg : exp_out<Tout>(v[k].get(i) - q.m) * inv_d;
+    // plain (write-back) stores, as pass B
+    if (vi < nvec) store_vec<Tout, VEC, false>(yr + (int64_t)vi * VEC, o);
   }
 }
 
@@ -2089,9 +2141,10 @@ hipError_t softmax_rows_held(const rr_plan& p, const SmCall<Tin, Tout>& c, int64
   return softmax_regs<Tin, Tout, false, LOG, CAUSAL, SHIFT>(p, c, grid, s);
 }
 
-// Workgroups of `kernel` (256 threads) the current device holds at once, or 0
-// when it cannot launch cooperatively.  Cached per device and kernel.
-int cooperative_capacity(const void* kernel) {
+// Workgroups of `kernel` (256 threads) the current device holds at once
+// (its occupancy times the compute units), or 0 if unknown.  Cached per
+// device and kernel.
+int resident_capacity(const void* kernel) {
   static std::mutex mu;
   static std::map<std::pair<int, const void*>, int> cache;
   int dev = 0;
@@ -2100,52 +2153,51 @@ int cooperative_capacity(const void* kernel) {
   auto key = std::make_pair(dev, kernel);
   auto it = cache.find(key);
   if (it != cache.end()) return it->second;
-  int coop = 0, cus = 0, per_cu = 0;
+  int cus = 0, per_cu = 0;
   int cap = 0;
-  if (hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev) == hipSuccess && coop &&
-      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
       hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 256, 0) == hipSuccess)
     cap = cus * per_cu;
   cache[key] = cap;
   return cap;
 }
 
-// A value no earlier call used, for the one-kernel split's slot tags.
-uint64_t next_split_tag() {
-  static std::atomic<uint64_t> counter{0x9e3779b97f4a7c15ull ^ (uint64_t)time(nullptr)};
-  uint64_t t = counter.fetch_add(1, std::memory_order_relaxed) + 1;
-  return t ? t : counter.fetch_add(1, std::memory_order_relaxed) + 1;
+// A 32-bit value that differs from the previous 2^32 - 1 calls' in this
+// process, for the one-kernel split's slot tags; the sequence starts at a
+// hash of the process id, the clock and an address, so that slots another
+// process left in reused memory are unlikely to carry it either.
+uint32_t next_split_tag() {
+  static std::atomic<uint64_t> counter{[] {
+    uint64_t z = (uint64_t)std::chrono::steady_clock::now().time_since_epoch().count() ^
+                 ((uint64_t)getpid() << 32) ^ (uint64_t)(uintptr_t)&counter;
+    z = (z ^ (z >> 30)) * 0xbf58476d1ce4e5b9ull;   // splitmix64 finaliser
+    z = (z ^ (z >> 27)) * 0x94d049bb133111ebull;
+    return z ^ (z >> 31);
+  }()};
+  return (uint32_t)(counter.fetch_add(1, std::memory_order_relaxed) + 1);
 }
 
-// SPLIT: the two-kernel form.  SPLIT_ONE_KERNEL: one cooperative kernel
-// when the device can hold at least a row's chunks at once, else the two
-// kernels.  Both use the same chunks and the same merge order, so they give
-// the same bits.  Log-softmax always takes the two kernels.  The split
-// forms keep every key (the planner never splits a causal call).
+// SPLIT (and SPLIT_ONE_KERNEL, which only forces the plan): the one-kernel
+// form when the rows are aligned, a row has at most 64 chunks, the device
+// holds the whole grid at once and the stream is not capturing; else the
+// two kernels.  SPLIT_TWO_KERNELS: always the two kernels.  Both forms use
+// the same chunks and the same merge order, so they give the same bits.  The
+// split forms keep every key (the planner never splits a causal call).
 template <typename Tin, typename Tout, int NV, bool LOG, bool SHIFT>
 hipError_t softmax_split(const rr_plan& p, const SmCall<Tin, Tout>& c, SplitSlot* w, int S,
                          int64_t grid, hipStream_t s) {
   const dim3 b(p.block_threads);
   if (c.cp > 0) return hipErrorInvalidValue;
-  // a capturing stream takes the two kernels (see softmax_split_fused_kernel)
-  hipStreamCaptureStatus capture = hipStreamCaptureStatusNone;
-  if (p.variant == RR_VARIANT_SPLIT_ONE_KERNEL && hipStreamIsCapturing(s, &capture) != hipSuccess)
-    return hipErrorInvalidValue;
-  if constexpr (!LOG && !SHIFT) {
-    if (p.variant == RR_VARIANT_SPLIT_ONE_KERNEL && capture == hipStreamCaptureStatusNone) {
-      const void* k = reinterpret_cast<const void*>(&softmax_split_fused_kernel<Tin, Tout, NV>);
-      const int cap = cooperative_capacity(k);
-      if (cap >= S) {
-        const int64_t g = grid < cap ? grid : cap;
-        uint64_t tag = next_split_tag();
-        const Tin* xx = c.x;
-        Tout* yy = c.y;
-        int64_t m64 = c.M;
-        int n32 = c.N;
-        RowStrides ld = c.ld;
-        void* args[] = {(void*)&xx, (void*)&yy, (void*)&w, (void*)&m64, (void*)&n32, (void*)&S, (void*)&tag,
-                        (void*)&ld};
-        return hipLaunchCooperativeKernel(k, grid1(g), b, args, 0, s);
+  if constexpr (!SHIFT) {
+    if (p.variant != RR_VARIANT_SPLIT_TWO_KERNELS && S <= kSplitFusedMaxChunks) {
+      hipStreamCaptureStatus capture = hipStreamCaptureStatusNone;
+      if (hipStreamIsCapturing(s, &capture) != hipSuccess) return hipErrorInvalidValue;
+      const void* k = reinterpret_cast<const void*>(&softmax_split_fused_kernel<Tin, Tout, NV, LOG>);
+      const int64_t items = c.M * (int64_t)S;
+      if (capture == hipStreamCaptureStatusNone && items <= resident_capacity(k)) {
+        softmax_split_fused_kernel<Tin, Tout, NV, LOG><<<grid1(items), b, 0, s>>>(c.x, c.y, w, c.M, c.N, S,
+                                                                                  next_split_tag(), c.ld);
+        return hipGetLastError();
       }
     }
   }
@@ -2241,12 +2293,13 @@ hipError_t softmax_typed(const rr_plan& p, const SmCall<Tin, Tout>& c, void* ws,
       softmax_loop_kernel<Tin, Tout, V, LOG, CAUSAL, false><<<g, b, 0, s>>>(c.x, c.y, c.M, c.N, c.cp, c.co, c.ld);
     return hipGetLastError();
   }
-  if (p.variant == RR_VARIANT_SPLIT || p.variant == RR_VARIANT_SPLIT_ONE_KERNEL) {
+  if (p.variant == RR_VARIANT_SPLIT || p.variant == RR_VARIANT_SPLIT_ONE_KERNEL ||
+      p.variant == RR_VARIANT_SPLIT_TWO_KERNELS) {
     if constexpr (CAUSAL) return hipErrorInvalidValue;   // the planner never splits a causal call
     SplitSlot* w = static_cast<SplitSlot*>(ws);
     const int S = (int)p.chunks_per_row;
     if (p.row_shift) {
-      if (p.variant != RR_VARIANT_SPLIT) return hipErrorInvalidValue;   // the planner never asks
+      if (p.variant == RR_VARIANT_SPLIT_ONE_KERNEL) return hipErrorInvalidValue;   // the planner never asks
       switch (p.vecs_per_lane) {
         case 4: return softmax_split<Tin, Tout, 4, LOG, true>(p, c, w, S, grid, s);
         case 8: return softmax_split<Tin, Tout, 8, LOG, true>(p, c, w, S, grid, s);

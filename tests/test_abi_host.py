@@ -459,7 +459,8 @@ def test_every_plan_covers_its_row():
     ops = [rr.RR_OP_RMSNORM, rr.RR_OP_FUSED_ADD_RMSNORM, rr.RR_OP_LAYERNORM, rr.RR_OP_SOFTMAX,
            rr.RR_OP_SOFTMAX_CAUSAL]
     variants = [rr.RR_VARIANT_AUTO, rr.RR_VARIANT_WAVE, rr.RR_VARIANT_BLOCK, rr.RR_VARIANT_SPLIT,
-                rr.RR_VARIANT_LOOP, rr.RR_VARIANT_SPLIT_ONE_KERNEL, rr.RR_VARIANT_SUBWAVE]
+                rr.RR_VARIANT_LOOP, rr.RR_VARIANT_SPLIT_ONE_KERNEL, rr.RR_VARIANT_SUBWAVE,
+                rr.RR_VARIANT_SPLIT_TWO_KERNELS]
     widths = np.concatenate([rng.integers(1, 300, 300), rng.integers(300, 70000, 400),
                              rng.integers(70000, 1 << 22, 100), [1 << 30, (1 << 30) - 8]])
     checked = 0
@@ -488,13 +489,13 @@ def test_every_plan_covers_its_row():
                     # (vec - 1); the norms only in the register kernels
                     assert vec == width, p
                     assert aligned == 2 or (aligned == 1 and N % width != 0), p
-                    assert name in ("wave", "block", "split", "loop"), p
+                    assert name in ("wave", "block", "split", "split2", "loop"), p
                     if op not in (rr.RR_OP_SOFTMAX, rr.RR_OP_SOFTMAX_CAUSAL):
                         assert name in ("wave", "block") and nv * vec <= 16, p
                         assert not (op == rr.RR_OP_LAYERNORM and vec == 4 and nv > 2), p
                     if name == "loop":
                         pass                                  # streams any length
-                    elif name == "split":
+                    elif name in ("split", "split2"):
                         cap = p["chunks_per_row"] * 256 * nv * vec
                         assert cap >= N + vec - 1, p          # any lead, also with aligned starts
                     else:
@@ -509,7 +510,7 @@ def test_every_plan_covers_its_row():
                     assert 64 * nv * vec >= N and p["rows_per_group"] * 64 == p["block_threads"], p
                 elif name == "block":
                     assert p["block_threads"] * nv * vec >= N and p["rows_per_group"] == 1, p
-                elif name in ("split", "split1"):
+                elif name in ("split", "split1", "split2"):
                     assert op == rr.RR_OP_SOFTMAX and vec > 1, p
                     if v == rr.RR_VARIANT_AUTO:
                         assert rr.rr_softmax_rows_workspace_bytes(M, N, din, dout) >= p["workspace_bytes"], p

@@ -472,14 +472,15 @@ def test_softmax_many_rows_and_partial_groups():
         check_softmax(x, run_softmax(x, torch.float32), f"{M}x{N}")
 
 
-@pytest.mark.parametrize("variant", ["wave", "block", "split", "split1", "loop", "subwave"])
+@pytest.mark.parametrize("variant", ["wave", "block", "split", "split1", "split2", "loop", "subwave"])
 def test_softmax_forced_variants(variant):
     rr = _rr()
     code = {"wave": rr.RR_VARIANT_WAVE, "block": rr.RR_VARIANT_BLOCK,
             "split": rr.RR_VARIANT_SPLIT, "split1": rr.RR_VARIANT_SPLIT_ONE_KERNEL,
+            "split2": rr.RR_VARIANT_SPLIT_TWO_KERNELS,
             "loop": rr.RR_VARIANT_LOOP, "subwave": rr.RR_VARIANT_SUBWAVE}[variant]
     shapes = {"wave": [8, 64, 1024, 2048], "block": [8, 1024, 4096, 16384, 32768, 65536],
-              "split": [8, 1024, 4096, 4104, 65536], "split1": [8, 4104, 65536],
+              "split": [8, 1024, 4096, 4104, 65536], "split1": [8, 4104, 65536], "split2": [8, 4104, 65536],
               "loop": [8, 1024, 4096, 100000], "subwave": [8, 16, 40, 64, 128]}[variant]
     with rr.forced_variant(code):
         for din, dout in DTYPES:
@@ -494,20 +495,50 @@ def test_softmax_forced_variants(variant):
 
 
 def test_split_one_kernel_equals_two_kernels_bitwise():
-    """The cooperative one-kernel split and the two-kernel split use the same
-    chunks and merge order: identical bits, on the vocabulary workload's first
-    rows and on a shape whose chunks need several passes of the grid."""
+    """The one-kernel split and the two-kernel split use the same chunks and
+    merge order: identical bits, on the vocabulary workload's first rows and
+    on shapes whose chunks the device cannot hold at once (there the request
+    runs the two kernels)."""
     rr = _rr()
     cases = [workloads.make("sm_vocab", rows=64).arrays["x"],
              softmax_input(1023, 33000, seed=4, dt="f32"),
              softmax_input(700, 131072, seed=5, dt="bf16")]
     for x in cases:
         outs = []
-        for code in (rr.RR_VARIANT_SPLIT_ONE_KERNEL, rr.RR_VARIANT_SPLIT):
+        for code in (rr.RR_VARIANT_SPLIT_ONE_KERNEL, rr.RR_VARIANT_SPLIT_TWO_KERNELS, rr.RR_VARIANT_SPLIT):
             with rr.forced_variant(code):
                 outs.append(run_softmax(x, torch.float32))
         assert torch.equal(_bits(outs[0]), _bits(outs[1])), tuple(x.shape)
+        assert torch.equal(_bits(outs[2]), _bits(outs[1])), tuple(x.shape)
         check_softmax(x, outs[0], f"split {tuple(x.shape)}")
+
+
+def test_split_one_kernel_on_a_reused_workspace():
+    """The one-kernel split takes only slots its own call wrote: one workspace
+    serves call after call of both forms on different inputs (so a slot left
+    by an earlier call holds other values), and every one-kernel call must
+    equal the two-kernel call on the same input bit for bit."""
+    rr = _rr()
+    M, N = 48, 152064
+    for din, dout in (("bf16", "bf16"), ("bf16", "f32"), ("f32", "f32")):
+        odt = _tdt(dout)
+        nb = rr.rr_softmax_rows_workspace_bytes(M, N, rr.RR_F32 if din == "f32" else rr.RR_BF16,
+                                                rr.RR_F32 if dout == "f32" else rr.RR_BF16)
+        ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
+        for k in range(4):
+            _say(f"reused workspace {din}->{dout} call {k}")
+            x = softmax_input(M, N, seed=200 + k, dt=din).cuda()
+            outs = []
+            for code in (rr.RR_VARIANT_SPLIT_TWO_KERNELS, rr.RR_VARIANT_SPLIT, rr.RR_VARIANT_SPLIT_ONE_KERNEL):
+                with rr.forced_variant(code):
+                    y = torch.full((M, N), 3.0, dtype=odt, device="cuda")
+                    rr.rr_softmax_rows(y, x, ws)
+                    torch.cuda.synchronize()
+                    outs.append(y)
+            assert torch.equal(_bits(outs[0]), _bits(outs[1])), (din, dout, k)
+            assert torch.equal(_bits(outs[0]), _bits(outs[2])), (din, dout, k)
+            if k == 0:
+                check_softmax(x.cpu(), outs[1].cpu(), f"one-kernel split {din}->{dout} {M}x{N}")
 
 
 def test_split_row_longer_than_the_resident_grid():

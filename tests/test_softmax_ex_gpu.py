@@ -83,14 +83,15 @@ def test_log_softmax_grid(din, dout, N):
         check_ex(y, compare.to_f64(x), True, f"log-softmax {din}->{dout} {M}x{N}")
 
 
-@pytest.mark.parametrize("variant", ["wave", "block", "split", "split1", "loop", "subwave"])
+@pytest.mark.parametrize("variant", ["wave", "block", "split", "split1", "split2", "loop", "subwave"])
 def test_log_softmax_forced_variants(variant):
     rr = _rr()
     code = {"wave": rr.RR_VARIANT_WAVE, "block": rr.RR_VARIANT_BLOCK,
             "split": rr.RR_VARIANT_SPLIT, "split1": rr.RR_VARIANT_SPLIT_ONE_KERNEL,
+            "split2": rr.RR_VARIANT_SPLIT_TWO_KERNELS,
             "loop": rr.RR_VARIANT_LOOP, "subwave": rr.RR_VARIANT_SUBWAVE}[variant]
     shapes = {"wave": [8, 1024, 2048], "block": [8, 4096, 32768, 65536],
-              "split": [8, 4104, 65536], "split1": [8, 65536],
+              "split": [8, 4104, 65536], "split1": [8, 65536], "split2": [8, 4104, 65536],
               "loop": [8, 4096, 100000], "subwave": [8, 40, 128]}[variant]
     with rr.forced_variant(code):
         for din, dout in DTYPES:

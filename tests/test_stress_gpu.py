@@ -32,7 +32,7 @@ def libs():
     assert torch.cuda.is_available(), "GPU tests need a GPU"
     assert os.path.exists(rr_build.LIB_STRESS), "the race-stress build is missing (run build())"
     # the normal build: the diagnostics library, which links the product's
-    # kernel object unchanged and can force the one-kernel split below
+    # kernel object unchanged and can force the two-kernel split below
     normal = rr.diag_lib()
     stress = rr.load_library(rr_build.LIB_STRESS)
     for L in (normal, stress):
@@ -177,24 +177,27 @@ def test_softmax_lds_stages_under_stress(din, dout, M, N, plan, log):
     _same_three_ways(run)
 
 
-def test_causal_rule_and_one_kernel_split_under_stress():
-    """The causal rule's workgroup-per-row stage, and the cooperative one-kernel
-    split (its grid is not capped: its waits need every workgroup resident)."""
+def test_causal_rule_and_two_kernel_split_under_stress():
+    """The causal rule's workgroup-per-row stage (one row per workgroup, and
+    two rows of a period per workgroup with one shared barrier), and the
+    split row forced to its two-kernel form (the default split plans above
+    run the one-kernel form, whose grid is one workgroup per chunk)."""
     M, N = 300, 4096
-    _say(f"stress causal rule {M}x{N}")
     xd = _dev(_softmax_rows(M, N, seed=3), F32)
-    causal = rr.make_softmax_opts(causal_period=128, causal_offset=N - 128)
+    for P, O in ((128, N - 128), (128, 0), (97, 0)):
+        _say(f"stress causal rule {M}x{N} P={P} O={O}")
+        causal = rr.make_softmax_opts(causal_period=P, causal_offset=O)
 
-    def run_causal(L):
-        y = torch.empty((M, N), dtype=torch.float32, device="cuda")
-        st = L.rr_softmax_rows_ex(y.data_ptr(), xd.data_ptr(), M, N, F32, F32, causal, None, 0, _stream())
-        assert st == 0, st
-        torch.cuda.synchronize()
-        return y
-    _same_three_ways(run_causal)
+        def run_causal(L):
+            y = torch.empty((M, N), dtype=torch.float32, device="cuda")
+            st = L.rr_softmax_rows_ex(y.data_ptr(), xd.data_ptr(), M, N, F32, F32, causal, None, 0, _stream())
+            assert st == 0, st
+            torch.cuda.synchronize()
+            return y
+        _same_three_ways(run_causal)
 
     M, N = 4, 152064
-    _say(f"stress one-kernel split {M}x{N}")
+    _say(f"stress two-kernel split {M}x{N}")
     xs = _dev(_softmax_rows(M, N, seed=4), F32)
     normal, stress = LIBS
 
@@ -202,7 +205,7 @@ def test_causal_rule_and_one_kernel_split_under_stress():
         y = torch.empty((M, N), dtype=torch.float32, device="cuda")
         nb = L.rr_softmax_rows_workspace_bytes(M, N, F32, F32)
         ws = torch.empty(max(nb, 16), dtype=torch.uint8, device="cuda")
-        assert L.rr_set_variant_override(rr.RR_VARIANT_SPLIT_ONE_KERNEL) == 0
+        assert L.rr_set_variant_override(rr.RR_VARIANT_SPLIT_TWO_KERNELS) == 0
         try:
             st = L.rr_softmax_rows(y.data_ptr(), xs.data_ptr(), M, N, F32, F32, ws.data_ptr(), nb, _stream())
         finally:
