@@ -202,15 +202,26 @@ constexpr int kPackedNV[] = {12, 16, 19, 20};
 // (bf16 in and out) the more rows the split needs to lose.  Measured cold on
 // rows 50256 to 152064 wide (fp32 in: 36-48 rows; bf16 -> fp32: 56-68;
 // bf16 -> bf16: 72-85).
+// The split now runs as one kernel where the device holds its grid (one
+// workgroup per chunk), which moved the crossovers up (cold, forced plans,
+// one launch after a 512 MiB write, median of 21; split / packed, us): fp32
+// x 65536 at 40 rows 10.8 / 13.8, at 48 11.4 / 13.8, at 56 12.2 / 14.2;
+// fp32 -> bf16 x 65536 at 56 11.8 / 15.8, at 64 12.3 / 16.0; bf16 -> fp32 x
+// 152064 at 56 15.6 / 23.0, at 64 17.0 / 23.1.  Captured in a HIP graph the
+// split runs as two kernels; these thresholds keep that form within a few
+// percent of the packed workgroup (at 40 / 56 / 56 rows respectively: 9.35 /
+// 9.24, 10.95 / 11.04, 20.08 / 20.09 us per launch).
 int64_t packed_min_rows(int din, int dout) {
-  if (din == RR_F32) return 40;
-  return dout == RR_F32 ? 56 : 80;
+  if (din == RR_F32) return dout == RR_F32 ? 48 : 64;
+  return dout == RR_F32 ? 64 : 80;
 }
 // Rows cut at aligned addresses cost the packed kernel more than the split
 // (its row's partial vectors, one row per CU): the crossovers move up by
 // about 16 rows (measured cold on 50257-152065-wide rows: fp32 54-60,
-// bf16 -> fp32 68-88, bf16 -> bf16 92-100).
-constexpr int64_t kCutPackedExtraRows = 16;
+// bf16 -> fp32 68-88, bf16 -> bf16 92-100; with the split in one kernel,
+// bf16 -> fp32 x 50257 at 80 rows 16.2 / 16.9 us split / packed, at 88
+// 17.7 / 16.8).
+constexpr int64_t kCutPackedExtraRows = 24;
 bool plan_packed(rr_op op, rr_plan* p, int vec, int per16, int64_t nvec) {
   if (op != RR_OP_SOFTMAX) return false;
   for (int nv16 : kPackedNV) {

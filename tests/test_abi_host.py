@@ -216,8 +216,8 @@ def test_softmax_causal_plans():
     assert p["variant_name"] == "loop" and p["workspace_bytes"] == 0
     assert q(S, 40, 200000, B, F)["variant_name"] == "split"
     # from 56 rows up (bf16 -> fp32) softmax also holds such rows in one workgroup
-    assert q(S, 56, 152064, B, F) == q(C, 56, 152064, B, F)
-    assert q(S, 56, 152064, B, F)["variant_name"] == "block" and q(S, 55, 152064, B, F)["variant_name"] == "split"
+    assert q(S, 64, 152064, B, F) == q(C, 64, 152064, B, F)
+    assert q(S, 64, 152064, B, F)["variant_name"] == "block" and q(S, 63, 152064, B, F)["variant_name"] == "split"
     with rr.forced_variant(rr.RR_VARIANT_SPLIT):
         with pytest.raises(rr.RowReduceError):
             q(C, 10, 1024)
@@ -323,10 +323,10 @@ def test_dispatch_boundaries():
     # (bf16 -> fp32) or 80 (bf16 -> bf16) rows up the row is held packed (1024
     # lanes x up to 20 16-byte vectors); rows longer than that split below
     # 1024 rows and stream from 1024 rows up
-    assert v(S, 39, 32772) == "split"
-    assert v(S, 40, 32772) == "block"
-    assert v(S, 39, 32772, F, B) == "split" and v(S, 40, 32772, F, B) == "block"
-    assert v(S, 55, 65536, B, F) == "split" and v(S, 56, 65536, B, F) == "block"
+    assert v(S, 47, 32772) == "split"
+    assert v(S, 48, 32772) == "block"
+    assert v(S, 63, 32772, F, B) == "split" and v(S, 64, 32772, F, B) == "block"
+    assert v(S, 63, 65536, B, F) == "split" and v(S, 64, 65536, B, F) == "block"
     assert v(S, 79, 65536, B, B) == "split" and v(S, 80, 65536, B, B) == "block"
     assert rr.rr_query_plan(S, 64, 32772, F, F)["vecs_per_lane"] == 12
     assert v(S, 64, 81920) == "block"
@@ -360,15 +360,15 @@ def test_dispatch_boundaries():
     # starts at a common offset, room for a lead of up to vec - 1 elements)
     for M, N, a, b, name, nv1, nv2 in ((10, 33, F, F, "wave", 1, 1), (10, 1023, F, F, "wave", 4, 8),
                                        (16384, 1025, F, F, "wave", 8, 8), (8192, 4097, F, F, "block", 2, 2),
-                                       (256, 50257, B, F, "block", 24, 24), (96, 50257, B, B, "block", 12, 12),
-                                       (56, 50257, F, B, "block", 16, 16)):
+                                       (256, 50257, B, F, "block", 24, 24), (104, 50257, B, B, "block", 12, 12),
+                                       (88, 50257, F, B, "block", 16, 16)):
         for al, nv in ((True, nv1), (2, nv2)):
             p = sh(M, N, a, b, al)
             assert (p["variant_name"], p["vecs_per_lane"], p["row_shift"]) == (name, nv, 1), (M, N, al, p)
             assert p["vec_elems"] == (4 if (a, b) != (B, B) else 8) and p["workspace_bytes"] == 0, p
     assert sh(64, 4097, op=rr.RR_OP_SOFTMAX_CAUSAL)["row_shift"] == 1
-    # beyond a workgroup's registers with few rows (below 40 / 56 / 80 by
-    # dtype pair), or beyond the packed workgroup below 1024 rows: the split, its chunks sized for a row
+    # beyond a workgroup's registers with few rows (below 72 / 88 / 88 / 104
+    # cut rows by dtype pair), or beyond the packed workgroup below 1024 rows: the split, its chunks sized for a row
     # at any offset (so that the workspace query, which sees no addresses,
     # covers every call); a causal call never splits
     for M, N, a, b, vec, nv, chunks in ((3, 50257, B, B, 8, 4, 7), (2, 50257, F, B, 4, 4, 13),
@@ -383,9 +383,10 @@ def test_dispatch_boundaries():
             assert rr.rr_softmax_rows_workspace_bytes(M, N, a, b) == M * chunks * 16
     assert rr.rr_query_plan(S, 4, 65536, F, F)["chunks_per_row"] == 16   # aligned rows: one chunk fewer
     assert sh(4, 50257, op=rr.RR_OP_SOFTMAX_CAUSAL)["variant_name"] == "block"
-    # cut rows hand over to the packed kernel 16 rows later than aligned ones
-    assert sh(71, 50257, B, F)["variant_name"] == "split" and sh(72, 50257, B, F)["variant_name"] == "block"
-    assert v(S, 56, 50256, B, F) == "block"
+    # cut rows hand over to the packed kernel 24 rows later than aligned ones
+    assert sh(87, 50257, B, F)["variant_name"] == "split" and sh(88, 50257, B, F)["variant_name"] == "block"
+    assert sh(71, 50257)["variant_name"] == "split" and sh(72, 50257)["variant_name"] == "block"
+    assert v(S, 63, 50256, B, F) == "split" and v(S, 64, 50256, B, F) == "block"
     # too long to hold with 1024 rows or more (or a causal call): the
     # streaming kernel, cut the same way; element access requested: scalar
     p = sh(1024, 81925)
