@@ -45,11 +45,14 @@
  *     multiple of 4 (fp32) or 8 (bf16) elements use 16-byte vector accesses;
  *     a softmax reading bf16 and writing fp32 reads 4 elements (8 bytes) per
  *     access, so there input rows 8-byte aligned and a width that is a
- *     multiple of 4 suffice.  A softmax whose input and output rows start at
- *     the same element offset within a vector (contiguous rows of any width,
- *     in place, column slices with equal strides) is cut into vectors at
- *     aligned addresses: whole vectors inside each row, its first and last
- *     vector element by element, nothing outside the row read or written.
+ *     multiple of 4 suffice.  A call whose input and output rows (and a
+ *     fused call's residual rows) start at the same element offset within a
+ *     vector (contiguous rows of any width, in place, column slices with
+ *     equal strides) is cut into vectors at aligned addresses: whole vectors
+ *     inside each row, its first and last vector element by element, nothing
+ *     outside the row read or written.  A cut norm reads gamma (and beta) in
+ *     whole aligned 16-byte blocks: the bytes that share the blocks holding
+ *     their first and last elements are read and ignored.
  *     Anything else runs a scalar path.  Each path gives the same results up
  *     to rounding order.  Any N >= 1 is accepted.
  *   - Determinism: a given (op, M, N, dtypes, alignment) always runs the same
@@ -243,8 +246,8 @@ rr_status rr_softmax_rows_ex(void* y, const void* x, int64_t M, int64_t N, rr_dt
  * accesses need every row start aligned to the access (16 bytes: aligned
  * base pointers and strides that are multiples of 4 fp32 or 8 bf16
  * elements; 8 bytes for the bf16 input of a softmax written as fp32);
- * a softmax whose x and y rows share their offset within a vector is cut at
- * aligned addresses (see above); otherwise the scalar path runs, with the
+ * a call whose x and y (and residual) rows share their offset within a
+ * vector is cut at aligned addresses (see above); otherwise the scalar path runs, with the
  * same results up to rounding order.  With every stride equal to the width these are exactly
  * the contiguous entry points above (same kernels, same bits).
  * Aliasing: y may be x itself (same pointer and stride, same dtype); other
@@ -363,8 +366,8 @@ typedef struct rr_plan {
   int64_t chunks_per_row;   /* SPLIT: workgroups per row; otherwise 1 */
   int64_t work_items;       /* workgroup-steps needed (rows / rows_per_group x chunks) */
   size_t workspace_bytes;   /* SPLIT: M * chunks_per_row * 16; otherwise 0 */
-  int32_t row_shift;        /* 1: softmax rows cut into vectors at aligned addresses (WAVE,
-                               BLOCK, SPLIT, LOOP): a row starting inside a vector, or ending inside one, is
+  int32_t row_shift;        /* 1: rows cut into vectors at aligned addresses (WAVE, BLOCK;
+                               a softmax also SPLIT, LOOP): a row starting inside a vector, or ending inside one, is
                                accessed whole vectors at a time except its first and last
                                vector, whose elements inside the row are accessed one by one */
 } rr_plan;
@@ -377,7 +380,7 @@ typedef struct rr_plan {
  *   2  row starts anywhere, but each input row and its output row sit at the
  *      same element offset within a vector (contiguous rows of a width that
  *      is not a whole number of vectors, column slices with equal strides):
- *      a softmax then cuts rows at aligned addresses (row_shift);
+ *      the call then cuts rows at aligned addresses (row_shift);
  *   0  neither: element-by-element access.
  * Returns RR_ERR_INVALID_ARG / RR_ERR_UNSUPPORTED as the corresponding call
  * would.  (The diagnostics build, rowreduce_diag.h, can force a variant; its

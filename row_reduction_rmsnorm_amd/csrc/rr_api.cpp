@@ -284,7 +284,43 @@ void plan_loop(rr_plan* p, int vec, int64_t nvec) {
   p->block_threads = 64 * p->waves_per_row;
 }
 
-// Softmax rows cut into vectors at aligned addresses (row_shift): the row
+// A cut RMSNorm row (fused or not) that takes a workgroup: 2 or 3 vectors
+// per lane, whichever needs fewer wavefronts (2 on a tie), 4 for fp32 rows
+// that 3 cannot hold in 16 wavefronts.  Each wavefront of a cut row costs a
+// fixed share of address and frame work, so fewer wavefronts per row win
+// where rounding the row up to whole wavefronts leaves them as full.
+// Measured back to back on 64 MiB inputs (us): bf16 8190 x 4097 (516
+// vectors at most) 28.1 as 5 wavefronts of 2 vectors, 26.1 as 3 of 3
+// (aligned 8192 x 4096: 22.6); 32736 x 1025 42.9 as 2 of 2, 31.6 as 1 of 3;
+// fused 8190 x 4097 71 as 9 of 1 (the aligned rule), 48.8 as 5 of 2 or 3 of
+// 3 (aligned: 43.9); fp32 4095 x 4097 26.8 as 9 of 2, 25.8 as 6 of 3, 26.9
+// as 5 of 4.  A cut LayerNorm row, which also holds beta's blocks, keeps
+// to 2 vectors per lane: 3 gained at some widths and lost at others.
+bool plan_block_cut(rr_plan* p, int vw, int64_t nvec) {
+  int best_nv = 0;
+  int64_t best_w = 0;
+  for (int nv = 2; nv <= 3; ++nv) {
+    const int64_t w = ceil_div(nvec, 64 * (int64_t)nv);
+    if (w <= kMaxWaves && (best_nv == 0 || w < best_w)) {
+      best_nv = nv;
+      best_w = w;
+    }
+  }
+  if (best_nv == 0 && vw == 4 && ceil_div(nvec, 64 * 4) <= kMaxWaves) {
+    best_nv = 4;
+    best_w = ceil_div(nvec, 64 * 4);
+  }
+  if (best_nv == 0) return false;
+  p->variant = RR_VARIANT_BLOCK;
+  p->vec_elems = vw;
+  p->waves_per_row = (int32_t)best_w;
+  p->rows_per_group = 1;
+  p->vecs_per_lane = best_nv;
+  p->block_threads = (int32_t)(64 * best_w);
+  return true;
+}
+
+// Rows cut into vectors at aligned addresses (row_shift): the row
 // starts at element `lead` of its first vector, so it spans up to nvec_s
 // vectors (see make_plan).  The same choice as for aligned rows: a
 // wavefront, a workgroup, the packed workgroup from packed_min_rows() rows (or
@@ -302,6 +338,8 @@ bool plan_shifted(rr_op op, bool causal, int64_t M, int64_t packed_rows, rr_plan
     const int max_nv = (op == RR_OP_LAYERNORM && vw == 4) ? 2 : 16;
     if (wave_fits(op, vw, nvec_s) && ceil_div(nvec_s, 64) <= max_nv) {
       plan_wave(p, vw, nvec_s);
+    } else if (op != RR_OP_LAYERNORM) {
+      ok = plan_block_cut(p, vw, nvec_s);
     } else {
       ok = plan_block(op, p, vw, nvec_s) && p->vecs_per_lane <= max_nv;
     }
@@ -320,7 +358,7 @@ bool plan_shifted(rr_op op, bool causal, int64_t M, int64_t packed_rows, rr_plan
 
 // Host-only plan.  `align`: 1 every row start of the call is vector-aligned;
 // 2 row starts anywhere, but input and output rows sit at the same element
-// offset within a vector (softmax rows are then cut at aligned addresses);
+// offset within a vector (rows are then cut at aligned addresses);
 // 0 neither (scalar access).
 rr_status make_plan(rr_op op, int64_t M, int64_t N, int din, int dout, int align,
                     rr_plan* p) {

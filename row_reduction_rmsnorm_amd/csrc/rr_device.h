@@ -188,6 +188,46 @@ struct Packed {
 #pragma unroll
     for (int i = 0; i < kWords; ++i) w[i] = 0u;
   }
+  // A cut row's partial vector: the aligned vector at `base` of which only
+  // the elements [lo, hi) lie inside the row (0 <= lo < hi <= VEC).  Only
+  // those elements are read (bf16: a whole word where both its halves lie
+  // inside), straight into this vector's words, so a partial vector takes no
+  // registers beyond a whole one's and no wait of its own.  finish_cut(),
+  // called once every load of the row is issued, moves a lone bf16 element
+  // of an odd index into its word's high half and sets the elements outside
+  // [lo, hi) to `fill`.
+  __device__ __forceinline__ void load_cut(const T* base, int lo, int hi) {
+    if constexpr (std::is_same_v<T, float>) {
+#pragma unroll
+      for (int i = 0; i < kWords; ++i) w[i] = (i >= lo && i < hi) ? __float_as_uint(base[i]) : 0u;
+    } else {
+      static_assert(VEC % 2 == 0, "bf16 partial vectors are whole words");
+#pragma unroll
+      for (int j = 0; j < kWords; ++j) {
+        const bool a = 2 * j >= lo && 2 * j < hi, b = 2 * j + 1 >= lo && 2 * j + 1 < hi;
+        if (a && b) w[j] = *reinterpret_cast<const uint32_t*>(base + 2 * j);
+        else if (a) w[j] = static_cast<uint32_t>(base[2 * j]);
+        else if (b) w[j] = static_cast<uint32_t>(base[2 * j + 1]);
+        else w[j] = 0u;
+      }
+    }
+  }
+  __device__ __forceinline__ void finish_cut(int lo, int hi, float fill) {
+    touch();
+    const uint32_t fb = std::is_same_v<T, float> ? __float_as_uint(fill) : (__float_as_uint(fill) >> 16);
+    if constexpr (std::is_same_v<T, float>) {
+#pragma unroll
+      for (int i = 0; i < kWords; ++i) w[i] = (i >= lo && i < hi) ? w[i] : fb;
+    } else {
+#pragma unroll
+      for (int j = 0; j < kWords; ++j) {
+        const bool a = 2 * j >= lo && 2 * j < hi, b = 2 * j + 1 >= lo && 2 * j + 1 < hi;
+        const uint32_t lo16 = a ? (w[j] & 0xffffu) : fb;
+        const uint32_t hi16 = b ? (a ? (w[j] >> 16) : (w[j] & 0xffffu)) : fb;
+        w[j] = lo16 | (hi16 << 16);
+      }
+    }
+  }
   // Hold VEC values that are exactly representable in T (packing rounds to
   // nearest even, which leaves such values unchanged).
   __device__ __forceinline__ void set(const float (&f)[VEC]) {

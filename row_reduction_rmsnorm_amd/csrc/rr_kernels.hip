@@ -260,25 +260,45 @@ __device__ __forceinline__ int frame_lead_within(const Tin* in_row, const Tout* 
 // element inside (never anything outside the row) and is replaced by `fill`
 // afterwards.  A load in a branch of its own, widened there, would wait for
 // that one load before the next is issued.
+//
+// EdgeLoad splits that in two: issue() starts the element loads, values()
+// widens them.  A kernel issues a row's partial vectors right after its whole
+// vectors and widens them only once every load of the row is in flight (a
+// wait for one edge vector would otherwise hold back the loads issued after
+// it: a second memory round trip per row).  touch() marks the point from
+// which the words may be used.
+template <typename T, int VEC>
+struct EdgeLoad {
+  uint32_t raw[VEC];
+  __device__ __forceinline__ void issue(const T* row, int e0, int keys) {
+#pragma unroll
+    for (int i = 0; i < VEC; ++i) {
+      const int e = e0 + i;
+      const int ec = e < 0 ? 0 : (e >= keys ? keys - 1 : e);
+      if constexpr (std::is_same_v<T, float>) raw[i] = __float_as_uint(row[ec]);
+      else raw[i] = static_cast<uint32_t>(row[ec]);
+    }
+  }
+  __device__ __forceinline__ void touch() {
+#pragma unroll
+    for (int i = 0; i < VEC; ++i) asm volatile("" : "+v"(raw[i]));
+  }
+  __device__ __forceinline__ void values(int e0, int keys, float (&v)[VEC], float fill) const {
+#pragma unroll
+    for (int i = 0; i < VEC; ++i) {
+      const int e = e0 + i;
+      const float f = std::is_same_v<T, float> ? __uint_as_float(raw[i]) : __uint_as_float(raw[i] << 16);
+      v[i] = (e >= 0 && e < keys) ? f : fill;
+    }
+  }
+};
 template <typename T, int VEC>
 __device__ __forceinline__ void load_edge(const T* row, int e0, int keys, float (&v)[VEC],
                                           float fill = kNegInf) {
-  uint32_t raw[VEC];
-#pragma unroll
-  for (int i = 0; i < VEC; ++i) {
-    const int e = e0 + i;
-    const int ec = e < 0 ? 0 : (e >= keys ? keys - 1 : e);
-    if constexpr (std::is_same_v<T, float>) raw[i] = __float_as_uint(row[ec]);
-    else raw[i] = static_cast<uint32_t>(row[ec]);
-  }
-#pragma unroll
-  for (int i = 0; i < VEC; ++i) asm volatile("" : "+v"(raw[i]));
-#pragma unroll
-  for (int i = 0; i < VEC; ++i) {
-    const int e = e0 + i;
-    const float f = std::is_same_v<T, float> ? __uint_as_float(raw[i]) : __uint_as_float(raw[i] << 16);
-    v[i] = (e >= 0 && e < keys) ? f : fill;
-  }
+  EdgeLoad<T, VEC> el;
+  el.issue(row, e0, keys);
+  el.touch();
+  el.values(e0, keys, v, fill);
 }
 
 // Store the elements e0 + i that lie in [0, n).
@@ -357,32 +377,38 @@ __device__ __forceinline__ void widen_row(Packed<T, VEC> (&p)[NV], float (&h)[NV
     for (int i = 0; i < VEC; ++i) h[k][i] = p[k].get(i);
 }
 
-// VEC elements p[e .. e + VEC) of a vector (gamma or beta) whose start lies
-// `lp` elements into a VEC-aligned block, for a window that need not be
-// aligned: window_blocks loads the two aligned vectors that hold it, and
-// window_cut cuts the window out of them (a shift by whole dwords, chosen per
-// dword from four candidates, then v_alignbyte for the 2-byte remainder of a
-// bf16 offset).  The caller keeps both aligned vectors inside [0, n) of p.
-template <typename T, int VEC>
-__device__ __forceinline__ void window_blocks(const T* p, int lp, int e, Packed<T, VEC>& A,
-                                              Packed<T, VEC>& B) {
-  const int a = (e + lp) / VEC;           // e in p's aligned frame (e + lp >= 0)
-  A.load(p - lp + a * VEC);
-  B.load(p - lp + (a + 1) * VEC);
+// VEC elements p[e .. e + VEC) of a vector (gamma or beta), for windows
+// that need not be aligned: window k is cut out of A[k], the aligned block
+// holding its first element, and B[k], the block after it, d = that
+// element's offset inside A[k] (a shift by whole dwords, then v_alignbyte for
+// the 2-byte remainder of a bf16 offset).  Every window of a cut row has the
+// same d (its vectors lie whole multiples of VEC apart), so callers pass a
+// workgroup-uniform d and one uniform branch picks the dword shift for all
+// the windows.  (Measured on 8192 x 4097 bf16 RMSNorm rows: 26.6 us; the
+// shift chosen per dword, 28.8; the words indexed by the shift, which the
+// compiler stages through LDS, 58.7.)
+template <int Q, typename T, int VEC, int NV>
+__device__ __forceinline__ void windows_cut_q(int r, const Packed<T, VEC> (&A)[NV], const Packed<T, VEC> (&B)[NV],
+                                              Packed<T, VEC> (&out)[NV]) {
+#pragma unroll
+  for (int k = 0; k < NV; ++k) {
+    const uint32_t C[8] = {A[k].w[0], A[k].w[1], A[k].w[2], A[k].w[3], B[k].w[0], B[k].w[1], B[k].w[2], B[k].w[3]};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) out[k].w[j] = __builtin_amdgcn_alignbyte(C[j + Q + 1], C[j + Q], r);
+  }
 }
-template <typename T, int VEC>
-__device__ __forceinline__ void window_cut(int lp, int e, const Packed<T, VEC>& A, const Packed<T, VEC>& B,
-                                           Packed<T, VEC>& out) {
+template <typename T, int VEC, int NV>
+__device__ __forceinline__ void windows_cut(int d, const Packed<T, VEC> (&A)[NV], const Packed<T, VEC> (&B)[NV],
+                                            Packed<T, VEC> (&out)[NV]) {
   static_assert(Packed<T, VEC>::kWords == 4, "16-byte vectors");
-  const int d = (e + lp) % VEC;           // element offset inside the first block
-  const uint32_t C[8] = {A.w[0], A.w[1], A.w[2], A.w[3], B.w[0], B.w[1], B.w[2], B.w[3]};
   const int bo = d * (int)sizeof(T);      // byte offset 0 .. 15
-  const int q = bo >> 2, r = bo & 3;
-  uint32_t W[5];
-#pragma unroll
-  for (int j = 0; j < 5; ++j) W[j] = q == 0 ? C[j] : q == 1 ? C[j + 1] : q == 2 ? C[j + 2] : C[j + 3];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) out.w[j] = __builtin_amdgcn_alignbyte(W[j + 1], W[j], r);
+  const int r = bo & 3;
+  switch (bo >> 2) {
+    case 0: windows_cut_q<0>(r, A, B, out); break;
+    case 1: windows_cut_q<1>(r, A, B, out); break;
+    case 2: windows_cut_q<2>(r, A, B, out); break;
+    default: windows_cut_q<3>(r, A, B, out); break;
+  }
 }
 
 // ===========================================================================
@@ -404,9 +430,8 @@ __device__ __forceinline__ void window_cut(int lp, int e, const Packed<T, VEC>& 
 // Whole vectors inside the row are accessed whole, the row's partial vectors
 // element by element (0 outside the row), and gamma (beta), which lie in a
 // frame of their own, are read for each row in the row's frame: each lane's
-// window is cut out of the two aligned blocks that hold it (window_blocks,
-// window_cut; they stay in the cache across rows), element by element where
-// those blocks would reach outside gamma.
+// window is cut out of the two aligned blocks of gamma that hold it
+// (window_cut; they stay in the cache across rows).
 // ===========================================================================
 template <typename T, int NV, int KIND, bool WAVE, bool SHIFT>
 __global__ __launch_bounds__(1024) void norm_regs_kernel(T* y, T* residual, const T* x,
@@ -446,6 +471,10 @@ __global__ __launch_bounds__(1024) void norm_regs_kernel(T* y, T* residual, cons
   };
   for (int64_t row = (int64_t)blockIdx.x * rl.rpg + rl.g; row < M; row += stride) {
     const int64_t ox = row * ld.x, oy = row * ld.y, orr = row * ld.r;
+    // LayerNorm's shift (below), the row's first element: loaded ahead of
+    // the row so that it arrives with the row rather than a round trip later
+    float k_first = 0.0f;
+    if constexpr (KIND == kNormLayer) k_first = load_one<T>(x + ox);
     float h[NV][VEC];
     // SHIFT: the row's frame (without SHIFT lead is 0 and nvec_row nvec)
     const int lead = SHIFT ? frame_lead_within(x + ox, y + oy, VEC, N, NV * rl.T) : 0;
@@ -475,15 +504,16 @@ __global__ __launch_bounds__(1024) void norm_regs_kernel(T* y, T* residual, cons
       }
     };
     if constexpr (SHIFT) {
-      // gamma (beta) in the row's frame: each lane's window is cut out of
-      // the two aligned blocks that hold it.  The blocks are loaded first
-      // (from the cache), with no branch: a block start is clamped to lie
-      // inside [0, N) of gamma, and the few lanes whose window needs a block
-      // outside (the row's ends) are read element by element afterwards.
-      // Then the row's whole vectors are loaded, then the windows cut (they
-      // wait for gamma's loads only), then the fix-ups and the row's two
-      // partial vectors.  (The host cuts norm rows only for N >= 3 * VEC, so
-      // a pair of aligned blocks always fits inside gamma.)
+      // gamma (beta) in the row's frame: each lane's window [e0, e0 + VEC)
+      // is cut out of the two aligned blocks of gamma that hold it.  Block a
+      // holds gamma's elements [a * VEC - lg, (a + 1) * VEC - lg); blocks 0 ..
+      // amax hold all of gamma, and each is read whole (the bytes around
+      // gamma's two ends that share its first and last blocks are read and
+      // ignored).  A window block outside that range is replaced by the
+      // nearest one inside: the elements it supplies then lie outside
+      // [0, N), where x counts zero and nothing is stored, so no window needs
+      // mending.  The blocks are loaded first (from the cache), then the
+      // row's whole vectors and its partial ones, then the windows are cut.
       const int lg = row_lead(gamma, VEC);
       const int lb = (KIND == kNormLayer && beta) ? row_lead(beta, VEC) : lg;
       constexpr int NB = KIND == kNormLayer ? NV : 1;
@@ -492,30 +522,25 @@ __global__ __launch_bounds__(1024) void norm_regs_kernel(T* y, T* residual, cons
         const int e0 = vi * VEC - lead;
         return vi < nvec_row && e0 >= 0 && e0 + VEC <= N;
       };
-      // the first of the two blocks holding [e0, e0 + VEC) of a vector whose
-      // start lies l elements into a block, unclamped and clamped
-      auto block0 = [&](int e0, int l) { return ((e0 + l) / VEC) * VEC - l; };
-      auto clamped = [&](int e0, int l) {
-        const int lo = l == 0 ? 0 : VEC - l;                              // first block inside
-        const int hi = ((N - 2 * VEC + l) / VEC) * VEC - l;               // last pair inside
-        const int b = e0 < 0 ? lo : block0(e0, l);
-        return b < lo ? lo : (b > hi ? hi : b);
+      // the aligned block holding element e of a parameter led by l
+      // elements (floor division: e + l may be negative), clamped to 0 .. amax
+      auto block = [&](int e, int l) {
+        const int a = (e + l) >= 0 ? (e + l) / VEC : -((VEC - 1 - (e + l)) / VEC);
+        const int amax = (N - 1 + l) / VEC;
+        return a < 0 ? 0 : (a > amax ? amax : a);
       };
-      auto windowed = [&](int vi) {
-        const int e0 = vi * VEC - lead;
-        return inside(vi) && block0(e0, lg) == clamped(e0, lg) && block0(e0, lb) == clamped(e0, lb);
-      };
+      auto block_base = [&](const T* p, int l) { return p - l; };   // block 0's first element
 #pragma unroll
       for (int k = 0; k < NV; ++k) {
         const int e0 = (k * rl.T + rl.t) * VEC - lead;
-        const int bg = clamped(e0, lg);
-        ga[k].load(gamma + bg);
-        gb[k].load(gamma + bg + VEC);
+        const T* g0 = block_base(gamma, lg);
+        ga[k].load(g0 + block(e0, lg) * VEC);
+        gb[k].load(g0 + block(e0 + VEC, lg) * VEC);
         if constexpr (KIND == kNormLayer) {
           if (beta) {
-            const int bbb = clamped(e0, lb);
-            ba[k].load(beta + bbb);
-            bb[k].load(beta + bbb + VEC);
+            const T* b0 = block_base(beta, lb);
+            ba[k].load(b0 + block(e0, lb) * VEC);
+            bb[k].load(b0 + block(e0 + VEC, lb) * VEC);
           } else {
             ba[k].zero();
             bb[k].zero();
@@ -535,6 +560,31 @@ __global__ __launch_bounds__(1024) void norm_regs_kernel(T* y, T* residual, cons
           if constexpr (KIND == kNormFused) pr[k].zero();
         }
       }
+      // the row's first vector (vector lead / VEC, k = 0; those before it are
+      // empty) and its last, where partial: only their elements inside the
+      // row are read (load_cut), into words of their own (loads into the
+      // whole vectors' registers would have to wait for those), issued here
+      // with the whole vectors and completed at the end
+      auto partial = [&](int vi) {
+        const int e0 = vi * VEC - lead;
+        return vi < nvec_row && !(e0 >= 0 && e0 + VEC <= N);
+      };
+      const int last = nvec_row - 1;
+      const int first = lead / VEC;
+      const bool edge0 = rl.t == first && partial(first);
+      const bool edge1 = last > first && rl.t == last % rl.T && partial(last);
+      const int e_first = first * VEC - lead, e_last = last * VEC - lead;
+      const int lo0 = e_first < 0 ? -e_first : 0, hi0 = N - e_first < VEC ? N - e_first : VEC;
+      const int hi1 = N - e_last < VEC ? N - e_last : VEC;   // (its start lies inside the row)
+      Packed<T, VEC> cx[2], cr[KIND == kNormFused ? 2 : 1];
+      if (edge0) {
+        cx[0].load_cut(x + ox + e_first, lo0, hi0);
+        if constexpr (KIND == kNormFused) cr[0].load_cut(residual + orr + e_first, lo0, hi0);
+      }
+      if (edge1) {
+        cx[1].load_cut(x + ox + e_last, 0, hi1);
+        if constexpr (KIND == kNormFused) cr[1].load_cut(residual + orr + e_last, 0, hi1);
+      }
       // gamma's blocks are read only below, after every load above is issued
       // (an empty asm that may touch memory and "changes" the blocks): else
       // the compiler cuts each window as soon as its blocks arrive, to free
@@ -547,57 +597,29 @@ __global__ __launch_bounds__(1024) void norm_regs_kernel(T* y, T* residual, cons
           if constexpr (KIND == kNormLayer) asm volatile("" : "+v"(ba[k].w[j]), "+v"(bb[k].w[j]) : : "memory");
         }
       }
-#pragma unroll
-      for (int k = 0; k < NV; ++k) {
-        const int e0 = (k * rl.T + rl.t) * VEC - lead;
-        window_cut<T, VEC>(lg, e0, ga[k], gb[k], gv[k]);   // (fixed up below where not windowed)
-        if constexpr (KIND == kNormLayer) window_cut<T, VEC>(lb, e0, ba[k], bb[k], bv[k]);
-      }
-#pragma unroll
-      for (int k = 0; k < NV; ++k) {
-        const int vi = k * rl.T + rl.t;
-        const int e0 = vi * VEC - lead;
-        if (vi < nvec_row && !windowed(vi)) {
-          float f[VEC];
-          load_edge<T, VEC>(gamma, e0, N, f, 0.0f);
-          gv[k].set(f);
-          if constexpr (KIND == kNormLayer) {
-            if (beta) {
-              load_edge<T, VEC>(beta, e0, N, f, 0.0f);
-              bv[k].set(f);
-            } else {
-              bv[k].zero();
-            }
-          }
-        }
-      }
-      // the row's first vector (vector lead / VEC, k = 0; those before it are
-      // empty) and last vector, if partial
-      auto partial = [&](int vi) {
-        const int e0 = vi * VEC - lead;
-        return vi < nvec_row && !(e0 >= 0 && e0 + VEC <= N);
-      };
-      const int last = nvec_row - 1;
-      const int first = lead / VEC;
-      if (rl.t == first && partial(first)) {
-        float f[VEC];
-        load_edge<T, VEC>(x + ox, first * VEC - lead, N, f, 0.0f);
-        px[0].set(f);
+      // the windows' offset inside their first block: (e0 + l) mod VEC with
+      // e0 = vi * VEC - lead, the same for every vector of the row
+      const int dg = (lg - lead) & (VEC - 1), db = (lb - lead) & (VEC - 1);
+      windows_cut<T, VEC, NV>(dg, ga, gb, gv);
+      if constexpr (KIND == kNormLayer) windows_cut<T, VEC, NV>(db, ba, bb, bv);
+      // the partial vectors completed, now that every load is in flight
+      if (edge0) {
+        cx[0].finish_cut(lo0, hi0, 0.0f);
+        px[0] = cx[0];
         if constexpr (KIND == kNormFused) {
-          load_edge<T, VEC>(residual + orr, first * VEC - lead, N, f, 0.0f);
-          pr[0].set(f);
+          cr[0].finish_cut(lo0, hi0, 0.0f);
+          pr[0] = cr[0];
         }
       }
-      if (last > first && rl.t == last % rl.T && partial(last)) {
+      if (edge1) {
         const int kl = last / rl.T;
-        float f[VEC], g[VEC];
-        load_edge<T, VEC>(x + ox, last * VEC - lead, N, f, 0.0f);
-        if constexpr (KIND == kNormFused) load_edge<T, VEC>(residual + orr, last * VEC - lead, N, g, 0.0f);
+        cx[1].finish_cut(0, hi1, 0.0f);
+        if constexpr (KIND == kNormFused) cr[1].finish_cut(0, hi1, 0.0f);
 #pragma unroll
         for (int k = 0; k < NV; ++k) {
           if (k == kl) {
-            px[k].set(f);
-            if constexpr (KIND == kNormFused) pr[k].set(g);
+            px[k] = cx[1];
+            if constexpr (KIND == kNormFused) pr[k] = cr[1];
           }
         }
       }
@@ -657,7 +679,7 @@ __global__ __launch_bounds__(1024) void norm_regs_kernel(T* y, T* residual, cons
       // K and the reduced sums are the same in every lane of the row (the
       // butterflies give every lane the same bits), so lane 0's copies are
       // moved to scalar registers, which frees vector registers
-      const float K = uniform_f32(load_one<T>(x + ox));
+      const float K = uniform_f32(k_first);
       // sum(h - S) and sum((h - S)^2) over the row, one reduction
       auto pair_sums = [&](float S, float& s1, float& s2) {
         s1 = 0.0f;
@@ -1961,11 +1983,18 @@ hipError_t norm_regs(const rr_plan& p, const NormArgs& a, int64_t grid, hipStrea
   const T* gg = static_cast<const T*>(a.gamma);
   const T* bb = static_cast<const T*>(a.beta);
   const dim3 b(p.block_threads);
-  // The host never plans more than 16 values per lane for the norms
-  // (NV * VEC <= 16), so only those instantiations exist.
+  // The host plans at most 16 values per lane for the norms (NV * VEC <=
+  // 16), 24 for cut rows (3 bf16 vectors), so only those instantiations exist.
   switch (p.vecs_per_lane) {
     case 1: norm_regs_kernel<T, 1, KIND, WAVE, SHIFT><<<grid1(grid), b, 0, s>>>(yy, rr_, xx, gg, bb, a.M, a.N, a.eps, a.ld); break;
     case 2: norm_regs_kernel<T, 2, KIND, WAVE, SHIFT><<<grid1(grid), b, 0, s>>>(yy, rr_, xx, gg, bb, a.M, a.N, a.eps, a.ld); break;
+    case 3:
+      // (cut rows only: fewer wavefronts per row where that saves some)
+      if constexpr (SHIFT && !WAVE) {
+        norm_regs_kernel<T, 3, KIND, WAVE, SHIFT><<<grid1(grid), b, 0, s>>>(yy, rr_, xx, gg, bb, a.M, a.N, a.eps, a.ld);
+        break;
+      }
+      return hipErrorInvalidValue;
     case 4:
       // (cut fp32 LayerNorm rows keep to 2 vectors per lane: 4 would spill)
       if constexpr (Elem<T>::kVec * 4 <= 16 && !(SHIFT && KIND == kNormLayer)) {
@@ -2053,7 +2082,8 @@ hipError_t norm_packed(const rr_plan& p, const NormArgs& a, int64_t grid, hipStr
 template <typename T, int KIND>
 hipError_t norm_any(const rr_plan& p, const NormArgs& a, int64_t grid, hipStream_t s) {
   if (p.variant == RR_VARIANT_LOOP) return norm_loop<T, KIND>(p, a, grid, s);
-  if (p.variant == RR_VARIANT_BLOCK && p.vecs_per_lane * p.vec_elems > 16) return norm_packed<T, KIND>(p, a, grid, s);
+  if (p.variant == RR_VARIANT_BLOCK && !p.row_shift && p.vecs_per_lane * p.vec_elems > 16)
+    return norm_packed<T, KIND>(p, a, grid, s);
   if (p.variant == RR_VARIANT_SUBWAVE) {
     if (p.vec_elems == 1) return norm_sub<T, 1, KIND>(p, a, grid, s);
     return norm_sub<T, Elem<T>::kVec, KIND>(p, a, grid, s);

@@ -211,16 +211,23 @@ def test_bf16_to_f32_softmax_on_8_byte_aligned_rows_is_the_aligned_call_bitwise(
 
 # (M, N, ld, col, gamma_col): rows cut at aligned addresses.  x, y and the
 # residual each sit in an [M, ld] buffer at column `col` (one offset within a
-# vector for all three); gamma is aligned (gamma_col None: read element by
-# element in each row's frame) or a slice at gamma_col (= col: read whole)
+# vector for all three); gamma (beta) is aligned (gamma_col None) or a slice
+# at gamma_col of a longer vector whose other elements are NaN: a cut row
+# reads gamma's first and last aligned blocks whole, and those NaNs must not
+# reach any output
 CUT_NORM_CASES = [
     (66, 33, 33, 0, None),          # contiguous rows of an odd width: every lead
+    (66, 33, 33, 0, 3),
     (7, 1021, 1021, 0, None),
     (66, 4097, 4097, 0, None),
+    (66, 4097, 4097, 0, 5),
     (9, 4096, 4101, 3, None),       # a column slice: lead 3 on every row
     (9, 4096, 4101, 3, 3),          # gamma at the rows' offset
     (5, 16377, 16377, 0, None),     # the longest rows a workgroup holds at any lead
-    (3, 20001, 20001, 0, None),     # longer: element by element
+    (5, 16377, 16377, 0, 7),
+    (3, 20001, 20001, 0, None),     # longer: bf16 RMSNorm rows held as 3 vectors per lane, else element by element
+    (3, 24569, 24569, 0, 3),        # the longest bf16 RMSNorm rows held at any lead
+    (2, 24577, 24577, 0, None),     # beyond every workgroup: element by element
 ]
 
 
@@ -230,12 +237,18 @@ def test_norm_rows_cut_at_aligned_addresses(case, dt):
     rr = _rr()
     M, N, ld, col, gcol = case
     code = rr.RR_F32 if dt == "f32" else rr.RR_BF16
-    cut = N <= 16377 and N > 32
     _say(f"cut norm rows {dt} {case}")
     for op in (rr.RR_OP_RMSNORM, rr.RR_OP_FUSED_ADD_RMSNORM, rr.RR_OP_LAYERNORM):
         p = rr.rr_query_plan(op, M, N, code, code, 2)
-        # (an fp32 LayerNorm cuts rows up to 2 vectors per lane: 8189 elements)
-        want = cut and not (op == rr.RR_OP_LAYERNORM and dt == "f32" and N > 8189)
+        # rows a workgroup holds at any lead: 16 wavefronts of up to 16
+        # values per lane (24 for a bf16 RMSNorm: 3 vectors), 8 for an fp32
+        # LayerNorm (2 vectors)
+        limit = 16377
+        if dt == "bf16" and op != rr.RR_OP_LAYERNORM:
+            limit = 24569
+        if dt == "f32" and op == rr.RR_OP_LAYERNORM:
+            limit = 8189
+        want = 32 < N <= limit
         assert p["row_shift"] == (1 if want else 0), (op, p)
     x_np = workloads.random_rows(M, N, seed=M + N + col)
     x_np[::3, 0] = 1.0e3                       # LayerNorm rows whose first element is far from the mean
@@ -246,11 +259,11 @@ def test_norm_rows_cut_at_aligned_addresses(case, dt):
     if gcol is None:
         gd, bd = g_cpu.cuda(), b_cpu.cuda()
     else:
-        G = torch.full((N + gcol,), SENTINEL, dtype=_tdt(dt), device="cuda")
-        Bt = torch.full((N + gcol,), SENTINEL, dtype=_tdt(dt), device="cuda")
-        G[gcol:] = g_cpu.cuda()
-        Bt[gcol:] = b_cpu.cuda()
-        gd, bd = G[gcol:], Bt[gcol:]
+        G = torch.full((N + gcol + 16,), float("nan"), dtype=_tdt(dt), device="cuda")
+        Bt = torch.full((N + gcol + 16,), float("nan"), dtype=_tdt(dt), device="cuda")
+        G[gcol:gcol + N] = g_cpu.cuda()
+        Bt[gcol:gcol + N] = b_cpu.cuda()
+        gd, bd = G[gcol:gcol + N], Bt[gcol:gcol + N]
     xbuf, xv = embed(x_cpu, ld, col)
     ybuf, yv = embed(torch.zeros(M, N, dtype=_tdt(dt)), ld, col)
     rr.rr_rmsnorm_strided(yv, xv, gd, 1e-6)
