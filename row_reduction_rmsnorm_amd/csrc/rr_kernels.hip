@@ -301,6 +301,51 @@ __device__ __forceinline__ void load_edge(const T* row, int e0, int keys, float 
   el.values(e0, keys, v, fill);
 }
 
+// A cut row's partial vectors: its first (vector lead / VEC, held by lane
+// lead / VEC at k = 0) and its last (vector nvec_row - 1, at k = k1), where
+// either holds kept keys but is not whole inside the row.  issue() reads
+// their elements in [0, keys) with load_cut into registers of their own, to
+// be called right after the row's whole vectors are issued; finish(), once
+// every load of the row is issued, completes them (-inf elsewhere) and puts
+// them in place.  One memory round trip per row: an edge vector read or
+// used in between would wait for every load before it.
+template <typename Tin, int VEC>
+struct CutEdges {
+  Packed<Tin, VEC> c0, c1;
+  bool has0, has1;
+  int k1, lo0, hi0, hi1;
+  __device__ __forceinline__ void issue(const Tin* xr, int t, int T, int lead, int nvec_row, int N, int keys) {
+    const int nvec_keys = (lead + keys + VEC - 1) / VEC;
+    auto partial = [&](int vi) {
+      const int e0 = vi * VEC - lead;
+      return vi < nvec_keys && !(e0 >= 0 && e0 + VEC <= N);
+    };
+    const int first = lead / VEC, last = nvec_row - 1;
+    const int ef = first * VEC - lead, el = last * VEC - lead;   // ef <= 0 <= el
+    has0 = t == first && partial(first);
+    has1 = last > first && t == last % T && partial(last);
+    k1 = last / T;
+    lo0 = -ef;
+    hi0 = keys - ef < VEC ? keys - ef : VEC;
+    hi1 = keys - el < VEC ? keys - el : VEC;
+    if (has0) c0.load_cut(xr + ef, lo0, hi0);
+    if (has1) c1.load_cut(xr + el, 0, hi1);
+  }
+  template <int NV>
+  __device__ __forceinline__ void finish(Packed<Tin, VEC> (&v)[NV]) {
+    if (has0) {
+      c0.finish_cut(lo0, hi0, kNegInf);
+      v[0] = c0;
+    }
+    if (has1) {
+      c1.finish_cut(0, hi1, kNegInf);
+#pragma unroll
+      for (int k = 0; k < NV; ++k)
+        if (k == k1) v[k] = c1;
+    }
+  }
+};
+
 // Store the elements e0 + i that lie in [0, n).
 template <typename T, int VEC>
 __device__ __forceinline__ void store_edge(T* row, int e0, int n, const float (&o)[VEC]) {
@@ -1180,7 +1225,29 @@ __global__ __launch_bounds__(1024) void softmax_regs_kernel(const Tin* x, Tout* 
     const int nvec_row = SHIFT ? (lead + N + VEC - 1) / VEC : nvec;
     const int nvec_keys = (lead + keys + VEC - 1) / VEC;   // vectors holding kept keys
     float v[NV][VEC];
-    if constexpr (std::is_same_v<Tin, float>) {
+    if constexpr (SHIFT && WAVE) {
+      // a wavefront's row holds both of its partial vectors: their element
+      // loads are issued after the whole vectors and completed once all are
+      // in flight, so that the wavefront waits once (the packed words, fp32:
+      // the values themselves, are widened only after that)
+      Packed<Tin, VEC> raw[NV];
+#pragma unroll
+      for (int k = 0; k < NV; ++k) {
+        const int vi = k * rl.T + rl.t;
+        const int e0 = vi * VEC - lead;
+        if (vi < nvec_keys && e0 >= 0 && e0 + VEC <= N) raw[k].template load<true>(xr + e0);
+        else raw[k].fill(kNegInf);
+      }
+      CutEdges<Tin, VEC> edges;
+      edges.issue(xr, rl.t, rl.T, lead, nvec_row, N, keys);
+      edges.finish(raw);
+#pragma unroll
+      for (int k = 0; k < NV; ++k) raw[k].touch();
+#pragma unroll
+      for (int k = 0; k < NV; ++k)
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) v[k][i] = raw[k].get(i);
+    } else if constexpr (std::is_same_v<Tin, float>) {
 #pragma unroll
       for (int k = 0; k < NV; ++k) {
         const int vi = k * rl.T + rl.t;
@@ -1471,10 +1538,14 @@ __global__ __launch_bounds__(1024) void softmax_packed_kernel(const Tin* x, Tout
       else v[k].fill(kNegInf);
     }
     if constexpr (SHIFT) {
-      // A cut row's only partial vectors are its first (lane 0, k = 0) and
-      // its last; they are read element by element once every whole
-      // vector's load is issued (read in between, their scalar loads would
-      // wait for the loads issued before them)
+      // A cut row's only partial vectors are its first (lane lead / VEC,
+      // k = 0) and its last; they are read element by element once every
+      // whole vector's load is issued (read in between, their element loads
+      // would wait for the loads issued before them).  The two lie in
+      // different wavefronts unless the row's last vector falls in the first
+      // 64 of a 1024-lane pass, so each wavefront still waits once.  (Held in
+      // registers of their own until the end, as the narrower kernels do,
+      // they would cost this kernel's packed rows occupancy.)
       auto partial = [&](int vi) {
         const int e0 = vi * VEC - lead;
         return vi < nvec_keys && !(e0 >= 0 && e0 + VEC <= N);
