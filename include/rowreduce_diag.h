@@ -8,6 +8,8 @@
  *   rr_selftest_wave_allreduce  run the wave64 all-reduce on given lanes
  *   rr_stream_copy              a plain streaming copy, the practical
  *                               bandwidth bar beside each operation
+ *   rr_set_split_wait_ticks     shorten the one-kernel split's wait
+ *   rr_split_fallbacks          how often that wait expired
  * Conventions (device pointers, streams, errors) as in rowreduce.h.
  */
 #ifndef ROWREDUCE_DIAG_H
@@ -52,6 +54,24 @@ rr_status rr_selftest_wave_allreduce(const float* in, float* out, int64_t count,
  * overlap; asynchronous on `stream` like every other call.
  */
 rr_status rr_stream_copy(void* dst, const void* src, int64_t bytes, void* stream);
+
+/*
+ * The split softmax in one kernel (RR_VARIANT_SPLIT in rowreduce.h): each
+ * workgroup waits a bounded time for the other chunks' (m, d) summaries of
+ * its row and summarises a chunk again from x itself when one has not
+ * arrived, so the result has the same bits either way.  Each such chunk adds
+ * one to a counter per device.
+ *   rr_set_split_wait_ticks  the wait, in ticks of the 100 MHz real-time
+ *                            clock, for every later call of this library
+ *                            (process-wide; default 4000 = 40 us; at most
+ *                            10^8); 0 gives up at once whenever a summary is
+ *                            not there yet, which exercises the fallback.
+ *   rr_split_fallbacks       *count <- the current device's counter (after
+ *                            a device-wide synchronisation); reset != 0
+ *                            then clears it.  Synchronous.
+ */
+rr_status rr_set_split_wait_ticks(uint64_t ticks);
+rr_status rr_split_fallbacks(uint32_t* count, int reset);
 
 #ifdef __cplusplus
 }

@@ -16,7 +16,8 @@ from .binding import (  # noqa: F401
     layernorm, lib, raw_layernorm, rr_layernorm,
     raw_fused_add_rmsnorm, raw_rmsnorm, raw_softmax_rows, rmsnorm, rr_fused_add_rmsnorm,
     rr_query_plan, rr_rmsnorm, rr_selftest_wave_allreduce, rr_stream_copy,
-    load_library, diag_lib, forced_variant, DIAG_EXPORTS,
+    load_library, diag_lib, forced_variant, DIAG_EXPORTS, split_fallbacks, split_wait,
+    SPLIT_WAIT_TICKS_DEFAULT,
     rr_softmax_rows, rr_softmax_rows_workspace_bytes, softmax_rows, softmax_workspace,
     status_string, rr_softmax_opts, make_softmax_opts, raw_softmax_rows_ex, rr_softmax_rows_ex,
     rr_softmax_rows_ex_workspace_bytes, softmax_rows_ex, raw_rmsnorm_strided,

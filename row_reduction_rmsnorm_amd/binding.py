@@ -55,8 +55,11 @@ EXPORTS = (
     "rr_softmax_rows_strided", "rr_softmax_rows_strided_noalloc",
     "rr_status_string", "rr_last_error_message", "rr_query_plan",
 )
+# The one-kernel split's default wait (rowreduce_diag.h), 100 MHz ticks.
+SPLIT_WAIT_TICKS_DEFAULT = 4000
 # What include/rowreduce_diag.h adds in the diagnostics build.
-DIAG_EXPORTS = ("rr_set_variant_override", "rr_selftest_wave_allreduce", "rr_stream_copy")
+DIAG_EXPORTS = ("rr_set_variant_override", "rr_selftest_wave_allreduce", "rr_stream_copy",
+                "rr_set_split_wait_ticks", "rr_split_fallbacks")
 
 
 class RowReduceError(RuntimeError):
@@ -200,6 +203,8 @@ def load_library(path):
         L.rr_set_variant_override.argtypes = [i32]
         L.rr_selftest_wave_allreduce.argtypes = [vp, vp, i64, i32, vp]
         L.rr_stream_copy.argtypes = [vp, vp, i64, vp]
+        L.rr_set_split_wait_ticks.argtypes = [ctypes.c_uint64]
+        L.rr_split_fallbacks.argtypes = [ctypes.POINTER(ctypes.c_uint32), i32]
         for f in DIAG_EXPORTS:
             getattr(L, f).restype = i32
     return L
@@ -530,6 +535,39 @@ def rr_stream_copy(dst, src, stream=None) -> None:
     st = D.rr_stream_copy(dst.data_ptr(), src.data_ptr(), nb, _stream_of(src, stream))
     if st != RR_OK:
         raise RowReduceError(st, f"rr_stream_copy: {D.rr_last_error_message().decode()}")
+
+
+def split_fallbacks(reset: bool = False) -> int:
+    """The current device's count, in the diagnostics build, of one-kernel
+    split chunks summarised again because their wait expired (reset clears
+    it afterwards).  Only calls made through the diagnostics build count
+    there (forced_variant(), split_wait() or diag_lib() directly)."""
+    D = diag_lib()
+    n = ctypes.c_uint32(0)
+    st = D.rr_split_fallbacks(ctypes.byref(n), 1 if reset else 0)
+    if st != RR_OK:
+        raise RowReduceError(st, f"rr_split_fallbacks: {D.rr_last_error_message().decode()}")
+    return int(n.value)
+
+
+@contextlib.contextmanager
+def split_wait(ticks: int):
+    """Run every call of this module inside the block through the
+    diagnostics build with the one-kernel split's wait set to `ticks` of the
+    100 MHz clock (0: give up at once), then restore the default wait and
+    the product library.  For tests; not thread-safe."""
+    global _ROUTED
+    D = diag_lib()
+    st = D.rr_set_split_wait_ticks(int(ticks))
+    if st != RR_OK:
+        raise RowReduceError(st, f"rr_set_split_wait_ticks: {D.rr_last_error_message().decode()}")
+    prev = _ROUTED
+    _ROUTED = D
+    try:
+        yield D
+    finally:
+        D.rr_set_split_wait_ticks(SPLIT_WAIT_TICKS_DEFAULT)
+        _ROUTED = prev
 
 
 # ----------------------------------------------------------------------------

@@ -36,6 +36,7 @@ namespace {
 thread_local char g_err[512] = "";
 #if RR_DIAG
 std::atomic<int> g_override{RR_VARIANT_AUTO};
+std::atomic<uint64_t> g_split_wait{rr::kSplitWaitTicks};
 #endif
 
 // The variant a call is forced to (diagnostics build), else RR_VARIANT_AUTO.
@@ -44,6 +45,15 @@ int forced_variant() {
   return g_override.load(std::memory_order_relaxed);
 #else
   return RR_VARIANT_AUTO;
+#endif
+}
+
+// The one-kernel split's bounded wait (the diagnostics build can shorten it).
+uint64_t split_wait_ticks() {
+#if RR_DIAG
+  return g_split_wait.load(std::memory_order_relaxed);
+#else
+  return rr::kSplitWaitTicks;
 #endif
 }
 
@@ -765,6 +775,7 @@ rr_status softmax_entry(const char* who, void* y, int64_t ldy, const void* x, in
   a.log_output = o.log_output;
   a.ld = rr::RowStrides{ldx, ldy, 0};
   a.pair_nv = o.causal ? causal_pair_nv(p, M, N, o.causal_period, a.causal_offset) : 0;
+  a.split_wait_ticks = split_wait_ticks();
   const hipError_t e = rr::launch_softmax(p, in_dtype, out_dtype, a, grid_for(p),
                                           static_cast<hipStream_t>(stream));
   return hip_status(e, who);
@@ -875,6 +886,27 @@ rr_status rr_stream_copy(void* dst, const void* src, int64_t bytes, void* stream
     return fail(RR_ERR_INVALID_ARG, "rr_stream_copy: source and destination overlap");
   return hip_status(rr::launch_stream_copy(dst, src, bytes, static_cast<hipStream_t>(stream)),
                     "rr_stream_copy");
+}
+
+rr_status rr_set_split_wait_ticks(uint64_t ticks) {
+  g_err[0] = '\0';
+  if (ticks > (uint64_t)100000000)
+    return fail(RR_ERR_INVALID_ARG, "rr_set_split_wait_ticks: at most 10^8 ticks (1 s)");
+  g_split_wait.store(ticks, std::memory_order_relaxed);
+  return RR_OK;
+}
+
+rr_status rr_split_fallbacks(uint32_t* count, int reset) {
+  g_err[0] = '\0';
+  if (!count) return fail(RR_ERR_INVALID_ARG, "rr_split_fallbacks: null count");
+  hipError_t e = hipSuccess;
+  unsigned int* c = rr::split_fallback_counter(&e);
+  if (!c) return hip_status(e, "rr_split_fallbacks");
+  e = hipDeviceSynchronize();
+  if (e == hipSuccess) e = hipMemcpy(count, c, sizeof(unsigned int), hipMemcpyDeviceToHost);
+  if (e == hipSuccess && reset) e = hipMemset(c, 0, sizeof(unsigned int));
+  if (e == hipSuccess && reset) e = hipDeviceSynchronize();
+  return hip_status(e, "rr_split_fallbacks");
 }
 #endif  // RR_DIAG
 

@@ -1927,11 +1927,14 @@ __global__ __launch_bounds__(256) void softmax_split_apply_kernel(const Tin* x, 
 //    earlier calls carry other tags; uninitialised memory matches in both
 //    words with probability 2^-64.
 //  * Wait: lane s of wavefront 0 polls slot s with relaxed agent-scope
-//    loads until both words carry the tag, for at most kSplitWaitTicks of
-//    the 100 MHz real-time clock.  A chunk still missing then (its
-//    workgroup kept from running by other work on the device, say) is
-//    summarised by this workgroup from x itself with pass A's code, so the
-//    result has the same bits whichever way a summary arrived.
+//    loads until both words carry the tag, for at most wait_ticks of the
+//    100 MHz real-time clock (the library passes kSplitWaitTicks, 40 us).  A
+//    chunk still missing then (its workgroup kept from running by other work
+//    on the device, say) is summarised by this workgroup from x itself with
+//    pass A's code, so the result has the same bits whichever way a summary
+//    arrived, and the number of chunks so summarised is added to a
+//    per-device counter (split_fallbacks, below), which the diagnostics
+//    build reads: a wait that expires is recorded, not silent.
 //  * The row's summaries go through LDS to every wavefront, lane s holding
 //    chunk s's pair, which is exactly what pass B's lanes hold after
 //    folding the workspace into the identity; the wave all-reduce and the
@@ -1941,7 +1944,6 @@ __global__ __launch_bounds__(256) void softmax_split_apply_kernel(const Tin* x, 
 //    two kernels instead.
 // ===========================================================================
 constexpr int kSplitFusedMaxChunks = kWave;         // one slot per lane of a wavefront
-constexpr uint64_t kSplitWaitTicks = 4000;          // 40 us of the 100 MHz real-time clock
 
 // The one-kernel form's view of a workspace slot: two tagged 64-bit words.
 struct SplitWords {
@@ -1953,6 +1955,7 @@ static_assert(sizeof(SplitWords) == sizeof(SplitSlot), "slot layout");
 template <typename Tin, typename Tout, int NV, bool LOG>
 __global__ __launch_bounds__(256) void softmax_split_fused_kernel(const Tin* x, Tout* y, SplitSlot* ws,
                                                                   int64_t M, int N, int S, uint32_t tag,
+                                                                  uint64_t wait_ticks, unsigned int* fallbacks,
                                                                   RowStrides ld) {
   constexpr int VEC = softmax_vec<Tin, Tout>();
   constexpr int CV = 256 * NV;
@@ -1997,7 +2000,7 @@ __global__ __launch_bounds__(256) void softmax_split_fused_kernel(const Tin* x, 
         have = true;
         break;
       }
-      if (__builtin_amdgcn_s_memrealtime() - t0 > kSplitWaitTicks) break;
+      if (__builtin_amdgcn_s_memrealtime() - t0 > wait_ticks) break;
       __builtin_amdgcn_s_sleep(2);
     }
     if (rl.lane < S) got[rl.lane] = b;
@@ -2005,8 +2008,10 @@ __global__ __launch_bounds__(256) void softmax_split_fused_kernel(const Tin* x, 
     if (rl.lane == 0) missing_mask = miss;
   }
   __syncthreads();
-  // chunks whose summaries did not arrive in time: summarised here, from x
+  // chunks whose summaries did not arrive in time: counted, and summarised
+  // here, from x
   uint64_t miss = missing_mask;                 // (uniform)
+  if (miss != 0 && threadIdx.x == 0) atomicAdd(fallbacks, (unsigned int)__builtin_popcountll(miss));
   while (miss) {
     const int s = __builtin_ctzll(miss);
     miss &= miss - 1;
@@ -2196,6 +2201,7 @@ struct SmCall {
   int64_t cp;
   int64_t co;
   RowStrides ld;
+  uint64_t wait_ticks;   // the one-kernel split's bounded wait
 };
 
 template <typename Tin, typename Tout, bool WAVE, bool LOG, bool CAUSAL, bool SHIFT>
@@ -2296,8 +2302,11 @@ hipError_t softmax_split(const rr_plan& p, const SmCall<Tin, Tout>& c, SplitSlot
       const void* k = reinterpret_cast<const void*>(&softmax_split_fused_kernel<Tin, Tout, NV, LOG>);
       const int64_t items = c.M * (int64_t)S;
       if (capture == hipStreamCaptureStatusNone && items <= resident_capacity(k)) {
-        softmax_split_fused_kernel<Tin, Tout, NV, LOG><<<grid1(items), b, 0, s>>>(c.x, c.y, w, c.M, c.N, S,
-                                                                                  next_split_tag(), c.ld);
+        hipError_t e = hipSuccess;
+        unsigned int* counter = split_fallback_counter(&e);
+        if (!counter) return e;
+        softmax_split_fused_kernel<Tin, Tout, NV, LOG><<<grid1(items), b, 0, s>>>(
+            c.x, c.y, w, c.M, c.N, S, next_split_tag(), c.wait_ticks, counter, c.ld);
         return hipGetLastError();
       }
     }
@@ -2428,6 +2437,7 @@ hipError_t softmax_io(const rr_plan& p, const SoftmaxArgs& a, int64_t grid, hipS
   c.cp = a.causal_period;
   c.co = a.causal_offset;
   c.ld = a.ld;
+  c.wait_ticks = a.split_wait_ticks;
   // the causal rule and log output are compile-time switches, so the plain
   // softmax kernels carry none of their code
   if (c.cp > 0) {
@@ -2471,12 +2481,24 @@ hipError_t launch_softmax(const rr_plan& plan, rr_dtype in_dtype, rr_dtype out_d
 // ===========================================================================
 static __device__ __align__(256) unsigned char scratch[rr::kNoAllocScratchBytes];
 
-namespace rr {
+// ===========================================================================
+// Hand-offs the one-kernel split gave up on (chunks a workgroup summarised
+// again from x because their summaries did not arrive within its bounded
+// wait): one counter per device, added to with a device-scope atomic; only
+// the diagnostics build reads or clears it.
+// ===========================================================================
+static __device__ unsigned int split_fallbacks;
 
-void* noalloc_scratch(hipError_t* err) {
-  constexpr int kMaxDevices = 64;
-  static std::mutex mu;
-  static std::atomic<void*> addr[kMaxDevices];
+namespace rr {
+namespace {
+
+// The current device's address of a file-scope device variable, looked up
+// once per device by `lookup` (a hipGetSymbolAddress call) and cached; null
+// with *err set.
+constexpr int kMaxDevices = 64;
+template <typename Lookup>
+void* device_symbol(std::atomic<void*> (&cache)[kMaxDevices], std::mutex& mu, hipError_t* err,
+                    Lookup lookup) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) {
@@ -2487,18 +2509,33 @@ void* noalloc_scratch(hipError_t* err) {
     *err = hipErrorInvalidDevice;
     return nullptr;
   }
-  void* p = addr[dev].load(std::memory_order_acquire);
+  void* p = cache[dev].load(std::memory_order_acquire);
   if (p) return p;
   std::lock_guard<std::mutex> lock(mu);
-  p = addr[dev].load(std::memory_order_relaxed);
+  p = cache[dev].load(std::memory_order_relaxed);
   if (p) return p;
-  e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+  e = lookup(&p);
   if (e != hipSuccess || !p) {
     *err = e != hipSuccess ? e : hipErrorInvalidSymbol;
     return nullptr;
   }
-  addr[dev].store(p, std::memory_order_release);
+  cache[dev].store(p, std::memory_order_release);
   return p;
+}
+
+}  // namespace
+
+void* noalloc_scratch(hipError_t* err) {
+  static std::mutex mu;
+  static std::atomic<void*> addr[kMaxDevices];
+  return device_symbol(addr, mu, err, [](void** p) { return hipGetSymbolAddress(p, HIP_SYMBOL(scratch)); });
+}
+
+unsigned int* split_fallback_counter(hipError_t* err) {
+  static std::mutex mu;
+  static std::atomic<void*> addr[kMaxDevices];
+  return static_cast<unsigned int*>(
+      device_symbol(addr, mu, err, [](void** p) { return hipGetSymbolAddress(p, HIP_SYMBOL(split_fallbacks)); }));
 }
 
 }  // namespace rr

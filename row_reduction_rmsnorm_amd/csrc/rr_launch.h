@@ -60,7 +60,15 @@ struct SoftmaxArgs {
   // causal rule only: > 0 runs two rows of a period per workgroup (rows q
   // and P - 1 - q) with this many vectors per lane; 0 one row per workgroup
   int pair_nv;
+  // the one-kernel split's bounded wait for another chunk's summary, in
+  // ticks of the 100 MHz real-time clock (kSplitWaitTicks)
+  uint64_t split_wait_ticks;
 };
+
+// The one-kernel split's wait: 40 us.  Its workgroups all run at once (the
+// host launches it only when the device holds the whole grid), so a
+// summary normally arrives within a few microseconds.
+constexpr uint64_t kSplitWaitTicks = 4000;
 
 // Enqueue the softmax kernel(s) that `plan` names (two for SPLIT).
 hipError_t launch_softmax(const rr_plan& plan, rr_dtype in_dtype, rr_dtype out_dtype,
@@ -75,6 +83,10 @@ constexpr size_t kNoAllocScratchBytes = (size_t)4 << 20;
 // Device address of the current device's scratch array (looked up once per
 // device with hipGetSymbolAddress, then cached), or null with *err set.
 void* noalloc_scratch(hipError_t* err);
+
+// Device address of the current device's count of one-kernel split chunks
+// summarised again after their wait expired (looked up as above).
+unsigned int* split_fallback_counter(hipError_t* err);
 
 // Diagnostics build only (rr_diag.hip): the wave all-reduce self-test kernel.
 hipError_t launch_selftest_wave(const float* in, float* out, int64_t count, int kind,

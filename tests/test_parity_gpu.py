@@ -541,6 +541,42 @@ def test_split_one_kernel_on_a_reused_workspace():
                 check_softmax(x.cpu(), outs[1].cpu(), f"one-kernel split {din}->{dout} {M}x{N}")
 
 
+def test_split_one_kernel_wait_that_expires_is_counted_and_recomputed():
+    """The one-kernel split's bounded wait: with the diagnostics build's wait
+    at its default, every chunk's summary arrives in time (the fallback
+    counter stays at 0); with the wait at 0 ticks workgroups give up on
+    summaries not yet written, count them, and summarise those chunks from x
+    themselves -- the output must still equal the two-kernel form's bit for
+    bit."""
+    rr = _rr()
+    M, N = 40, 152064
+    x = softmax_input(M, N, seed=321, dt="bf16").cuda()
+    ws = rr.softmax_workspace(x, torch.float32)
+    assert rr.rr_query_plan(rr.RR_OP_SOFTMAX, M, N, rr.RR_BF16, rr.RR_F32)["variant_name"] == "split"
+    with rr.forced_variant(rr.RR_VARIANT_SPLIT_TWO_KERNELS):
+        ref = torch.empty((M, N), dtype=torch.float32, device="cuda")
+        rr.rr_softmax_rows(ref, x, ws)
+        torch.cuda.synchronize()
+    rr.split_fallbacks(reset=True)
+    for ticks, what in ((rr.SPLIT_WAIT_TICKS_DEFAULT, "default wait"), (0, "no wait")):
+        _say(f"one-kernel split {M}x{N}, {what}")
+        with rr.split_wait(ticks):
+            outs = []
+            for k in range(3):
+                y = torch.full((M, N), 3.0, dtype=torch.float32, device="cuda")
+                rr.rr_softmax_rows(y, x, ws)
+                torch.cuda.synchronize()
+                outs.append(y)
+        n = rr.split_fallbacks(reset=True)
+        _say(f"  chunks summarised again: {n} of {3 * M * 19 * 18}")
+        for y in outs:
+            assert torch.equal(_bits(ref), _bits(y)), what
+        if ticks:
+            assert n == 0, f"{n} summaries missed a {ticks}-tick wait"
+        else:
+            assert n > 0, "a zero wait never gave up"
+
+
 def test_split_row_longer_than_the_resident_grid():
     """One row of 2^25 fp32 values: more chunks than workgroups the GPU holds
     at once, so the one-kernel form falls back to the two kernels; both the
