@@ -8,7 +8,7 @@
  *   rr_layernorm          y = (x - mean) * rsqrt(var + eps) * gamma + beta
  *   rr_softmax_rows       y = exp(x - m) / d with the online normaliser (m, d)
  *   rr_softmax_rows_ex    the same, or log-softmax, optionally under a causal
- *                         rule whose masked keys are never read
+ *                         rule that does not read masked keys
  *
  * Sources (web pages, cited by title and section):
  *   [P1] "两个融合算子：RMSNorm 与 online softmax" (daleiyang.github.io)
@@ -199,8 +199,11 @@ rr_status rr_softmax_rows(void* y, const void* x, int64_t M, int64_t N, rr_dtype
  *                  causal_offset = N - queries is the attention causal mask
  *                  (the per-layer score softmax of [P1] section
  *                  "二、它们在 Qwen2.5-7B 里的真实位置"; offset 0 when queries
- *                  and keys coincide).  Masked keys are never read: the
- *                  kernel loads only the kept prefix of each row, so the
+ *                  and keys coincide).  Masked keys are not read: the
+ *                  kernel loads only the aligned vectors holding a row's
+ *                  kept keys (16 bytes; 8 for a bf16 input written as
+ *                  fp32), so only masked keys that share the vector of the
+ *                  last kept key are read, and they are discarded; the
  *                  input there may hold anything.
  *   causal_period  >= 1 when causal (ignored otherwise).
  *   causal_offset  >= 0 when causal (ignored otherwise).
