@@ -984,10 +984,19 @@ def test_workload_sm_wave_full():
 
 
 def test_workload_sm_vocab_full():
+    """The vocabulary workload as planned (one packed workgroup per row), and
+    all of its rows through the split-row (m, d) combine the workload is
+    named for (the two-kernel form: 256 rows of 19 chunks are more than the
+    device holds at once for the one-kernel form)."""
+    rr = _rr()
     w = workloads.make("sm_vocab")
     _say(w.description)
     y = run_softmax(w.arrays["x"], torch.float32)
     _say(check_softmax(w.arrays["x"], y, w.name))
+    with rr.forced_variant(rr.RR_VARIANT_SPLIT):
+        assert rr.rr_query_plan(rr.RR_OP_SOFTMAX, 256, 152064, rr.RR_BF16, rr.RR_F32)["chunks_per_row"] == 19
+        ys = run_softmax(w.arrays["x"], torch.float32)
+    _say(check_softmax(w.arrays["x"], ys, w.name + " (split)"))
 
 
 def test_workload_sm_causal_full_sampled():
