@@ -304,8 +304,9 @@ void plan_loop(rr_plan* p, int vec, int64_t nvec) {
 // (aligned 8192 x 4096: 22.6); 32736 x 1025 42.9 as 2 of 2, 31.6 as 1 of 3;
 // fused 8190 x 4097 71 as 9 of 1 (the aligned rule), 48.8 as 5 of 2 or 3 of
 // 3 (aligned: 43.9); fp32 4095 x 4097 26.8 as 9 of 2, 25.8 as 6 of 3, 26.9
-// as 5 of 4.  A cut LayerNorm row, which also holds beta's blocks, keeps
-// to 2 vectors per lane: 3 gained at some widths and lost at others.
+// as 5 of 4.  A cut LayerNorm row takes the same choice: its workgroup
+// stages gamma's and beta's blocks in LDS once (up to kNormLdsParamMax
+// bytes), so its lanes hold no more than an RMSNorm row's.
 bool plan_block_cut(rr_plan* p, int vw, int64_t nvec) {
   int best_nv = 0;
   int64_t best_w = 0;
@@ -342,16 +343,19 @@ bool plan_shifted(rr_op op, bool causal, int64_t M, int64_t packed_rows, rr_plan
                   int64_t nvec_s, int64_t nvec_any) {
   bool ok = true;
   if (op != RR_OP_SOFTMAX) {
-    // the norm kernels hold gamma's (and beta's) two aligned blocks per
-    // vector while the row loads: an fp32 LayerNorm keeps to 2 vectors per
-    // lane (4 would spill); longer norm rows stream element by element
+    // a wavefront's cut row holds gamma's (and beta's) two aligned blocks
+    // per vector while the row loads: an fp32 LayerNorm wavefront keeps to 2
+    // vectors per lane (4 would spill); longer norm rows stream element by
+    // element
     const int max_nv = (op == RR_OP_LAYERNORM && vw == 4) ? 2 : 16;
     if (wave_fits(op, vw, nvec_s) && ceil_div(nvec_s, 64) <= max_nv) {
       plan_wave(p, vw, nvec_s);
-    } else if (op != RR_OP_LAYERNORM) {
-      ok = plan_block_cut(p, vw, nvec_s);
     } else {
-      ok = plan_block(op, p, vw, nvec_s) && p->vecs_per_lane <= max_nv;
+      // a workgroup's cut LayerNorm row stages gamma and beta in LDS, sized
+      // for a row at any offset; its kernel exists for 1 to 3 vectors per lane
+      const bool lds_ok = op != RR_OP_LAYERNORM || 2 * (size_t)nvec_any * 16 <= rr::kNormLdsParamMax;
+      ok = lds_ok && plan_block_cut(p, vw, nvec_s) &&
+           (op != RR_OP_LAYERNORM || p->vecs_per_lane <= 3);
     }
   } else if (wave_fits(op, vw, nvec_s)) {
     plan_wave(p, vw, nvec_s);
@@ -486,9 +490,16 @@ rr_status make_plan(rr_op op, int64_t M, int64_t N, int din, int dout, int align
     return fail(RR_ERR_UNSUPPORTED, "forced variant %d cannot run op %d with N = %lld (vector width %d)",
                 forced, (int)op, (long long)N, vec);
   }
-  // cut fp32 LayerNorm rows keep to 2 vectors per lane (plan_shifted), also
-  // when a variant is forced
-  if (ok && p->row_shift && op == RR_OP_LAYERNORM && vw == 4 && p->vecs_per_lane > 2) ok = false;
+  // cut LayerNorm rows, also when a variant is forced (plan_shifted): an
+  // fp32 wavefront keeps to 2 vectors per lane; a workgroup to 3, with
+  // gamma's and beta's blocks staged in LDS
+  if (ok && p->row_shift && op == RR_OP_LAYERNORM) {
+    if (p->variant == RR_VARIANT_WAVE)
+      ok = !(vw == 4 && p->vecs_per_lane > 2);
+    else
+      ok = p->variant == RR_VARIANT_BLOCK && p->vecs_per_lane <= 3 &&
+           2 * (size_t)nvec_any * 16 <= rr::kNormLdsParamMax;
+  }
   if (!ok) {
     return fail(RR_ERR_UNSUPPORTED, "forced variant %d cannot run op %d with N = %lld (vector width %d)",
                 forced, (int)op, (long long)N, vec);

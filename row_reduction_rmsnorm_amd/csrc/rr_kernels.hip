@@ -37,6 +37,7 @@
 #include <atomic>
 #include <map>
 #include <mutex>
+#include <tuple>
 #include <utility>
 
 #include "rr_device.h"
@@ -478,6 +479,22 @@ __device__ __forceinline__ void windows_cut(int d, const Packed<T, VEC> (&A)[NV]
 // window is cut out of the two aligned blocks of gamma that hold it
 // (window_cut; they stay in the cache across rows).
 // ===========================================================================
+// Cut LayerNorm rows held by a workgroup read gamma and beta through LDS:
+// each lane loads aligned blocks of both with the row, writes them to LDS,
+// and cuts its windows from there after the row's reduction.  Held in
+// registers (two blocks of each per vector while the row loads) they cost a
+// cut LayerNorm row so many registers that a CU held half as many rows as
+// for RMSNorm.
+template <int KIND, bool WAVE, bool SHIFT>
+constexpr bool norm_lds_params() {
+  return SHIFT && !WAVE && KIND == kNormLayer;
+}
+// Bytes of LDS such a kernel takes for rows of N elements.
+template <typename T>
+constexpr size_t norm_lds_param_bytes(int N) {
+  return 2 * (size_t)((N + 2 * Elem<T>::kVec - 2) / Elem<T>::kVec) * 16;
+}
+
 template <typename T, int NV, int KIND, bool WAVE, bool SHIFT>
 __global__ __launch_bounds__(1024) void norm_regs_kernel(T* y, T* residual, const T* x,
                                                          const T* __restrict__ gamma,
@@ -487,6 +504,42 @@ __global__ __launch_bounds__(1024) void norm_regs_kernel(T* y, T* residual, cons
   __shared__ float slots[2][kMaxWavesPerGroup];
   const RowLane rl = row_lane<WAVE>();
   const int nvec = N / VEC;
+  // A cut LayerNorm row held by a workgroup stages gamma and beta in LDS
+  // (norm_lds_params); the other forms keep them in registers.
+  constexpr bool kLdsParams = norm_lds_params<KIND, WAVE, SHIFT>();
+  extern __shared__ uint4 params_lds[];   // [2][nbmax] 16-byte blocks (kLdsParams only)
+  const int nbmax = (N + 2 * VEC - 2) / VEC;
+
+  if constexpr (kLdsParams) {
+    // gamma's (beta's) aligned 16-byte blocks 0 .. amax, the same for every
+    // row: gamma at [0, nbmax), beta at [nbmax, 2 nbmax).  Each row cuts its
+    // windows out of them after its reduction, whose barrier (like this one)
+    // orders these writes before every read.
+    const int lg = row_lead(gamma, VEC);
+    const int lb = beta ? row_lead(beta, VEC) : lg;
+    const int ng = (N - 1 + lg) / VEC + 1, nb = (N - 1 + lb) / VEC + 1;
+    const T* g0 = gamma - lg;
+    const T* b0 = beta ? beta - lb : nullptr;
+    // gamma's blocks then beta's, kBatch per lane in flight at once (one
+    // round trip per batch rather than one per block)
+    constexpr int kBatch = 8;
+    const int total = ng + (beta ? nb : 0);
+    for (int c0 = threadIdx.x; c0 < total; c0 += kBatch * blockDim.x) {
+      Packed<T, VEC> q[kBatch];
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j) {
+        const int c = c0 + j * blockDim.x;
+        if (c < ng) q[j].load(g0 + c * VEC);
+        else if (c < total) q[j].load(b0 + (c - ng) * VEC);
+      }
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j) {
+        const int c = c0 + j * blockDim.x;
+        if (c < total) params_lds[c < ng ? c : nbmax + (c - ng)] = make_uint4(q[j].w[0], q[j].w[1], q[j].w[2], q[j].w[3]);
+      }
+    }
+    __syncthreads();
+  }
 
   Packed<T, VEC> gv[NV];
   Packed<T, VEC> bv[KIND == kNormLayer ? NV : 1];
@@ -541,6 +594,7 @@ __global__ __launch_bounds__(1024) void norm_regs_kernel(T* y, T* residual, cons
     // after this row's loads are issued, keeps their wait (and widening)
     // behind those loads instead of before the first row's
     auto params_after_loads = [&]() {
+      if constexpr (kLdsParams) return;
 #pragma unroll
       for (int k = 0; k < NV; ++k) gv[k].touch();
       if constexpr (KIND == kNormLayer) {
@@ -562,7 +616,8 @@ __global__ __launch_bounds__(1024) void norm_regs_kernel(T* y, T* residual, cons
       const int lg = row_lead(gamma, VEC);
       const int lb = (KIND == kNormLayer && beta) ? row_lead(beta, VEC) : lg;
       constexpr int NB = KIND == kNormLayer ? NV : 1;
-      Packed<T, VEC> ga[NV], gb[NV], ba[NB], bb[NB];
+      constexpr int NW = kLdsParams ? 1 : NV;   // (no window blocks held in registers with LDS staging)
+      Packed<T, VEC> ga[NW], gb[NW], ba[kLdsParams ? 1 : NB], bb[kLdsParams ? 1 : NB];
       auto inside = [&](int vi) {
         const int e0 = vi * VEC - lead;
         return vi < nvec_row && e0 >= 0 && e0 + VEC <= N;
@@ -575,20 +630,22 @@ __global__ __launch_bounds__(1024) void norm_regs_kernel(T* y, T* residual, cons
         return a < 0 ? 0 : (a > amax ? amax : a);
       };
       auto block_base = [&](const T* p, int l) { return p - l; };   // block 0's first element
+      if constexpr (!kLdsParams) {
 #pragma unroll
-      for (int k = 0; k < NV; ++k) {
-        const int e0 = (k * rl.T + rl.t) * VEC - lead;
-        const T* g0 = block_base(gamma, lg);
-        ga[k].load(g0 + block(e0, lg) * VEC);
-        gb[k].load(g0 + block(e0 + VEC, lg) * VEC);
-        if constexpr (KIND == kNormLayer) {
-          if (beta) {
-            const T* b0 = block_base(beta, lb);
-            ba[k].load(b0 + block(e0, lb) * VEC);
-            bb[k].load(b0 + block(e0 + VEC, lb) * VEC);
-          } else {
-            ba[k].zero();
-            bb[k].zero();
+        for (int k = 0; k < NW; ++k) {
+          const int e0 = (k * rl.T + rl.t) * VEC - lead;
+          const T* g0 = block_base(gamma, lg);
+          ga[k].load(g0 + block(e0, lg) * VEC);
+          gb[k].load(g0 + block(e0 + VEC, lg) * VEC);
+          if constexpr (KIND == kNormLayer) {
+            if (beta) {
+              const T* b0 = block_base(beta, lb);
+              ba[k].load(b0 + block(e0, lb) * VEC);
+              bb[k].load(b0 + block(e0 + VEC, lb) * VEC);
+            } else {
+              ba[k].zero();
+              bb[k].zero();
+            }
           }
         }
       }
@@ -630,26 +687,37 @@ __global__ __launch_bounds__(1024) void norm_regs_kernel(T* y, T* residual, cons
         cx[1].load_cut(x + ox + e_last, 0, hi1);
         if constexpr (KIND == kNormFused) cr[1].load_cut(residual + orr + e_last, 0, hi1);
       }
-      // gamma's blocks are read only below, after every load above is issued
-      // (an empty asm that may touch memory and "changes" the blocks): else
-      // the compiler cuts each window as soon as its blocks arrive, to free
-      // their registers, which holds back the loads after them
+      if constexpr (!kLdsParams) {
+        // gamma's blocks are read only below, after every load above is
+        // issued (an empty asm that may touch memory and "changes" the
+        // blocks): else the compiler cuts each window as soon as its blocks
+        // arrive, to free their registers, which holds back the loads after
+        // them
 #pragma unroll
-      for (int k = 0; k < NV; ++k) {
+        for (int k = 0; k < NW; ++k) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          asm volatile("" : "+v"(ga[k].w[j]), "+v"(gb[k].w[j]) : : "memory");
-          if constexpr (KIND == kNormLayer) asm volatile("" : "+v"(ba[k].w[j]), "+v"(bb[k].w[j]) : : "memory");
+          for (int j = 0; j < 4; ++j) {
+            asm volatile("" : "+v"(ga[k].w[j]), "+v"(gb[k].w[j]) : : "memory");
+            if constexpr (KIND == kNormLayer) asm volatile("" : "+v"(ba[k].w[j]), "+v"(bb[k].w[j]) : : "memory");
+          }
         }
+        // the windows' offset inside their first block: (e0 + l) mod VEC
+        // with e0 = vi * VEC - lead, the same for every vector of the row
+        const int dg = (lg - lead) & (VEC - 1), db = (lb - lead) & (VEC - 1);
+        windows_cut<T, VEC, NW>(dg, ga, gb, gv);
+        if constexpr (KIND == kNormLayer) windows_cut<T, VEC, NW>(db, ba, bb, bv);
       }
-      // the windows' offset inside their first block: (e0 + l) mod VEC with
-      // e0 = vi * VEC - lead, the same for every vector of the row
-      const int dg = (lg - lead) & (VEC - 1), db = (lb - lead) & (VEC - 1);
-      windows_cut<T, VEC, NV>(dg, ga, gb, gv);
-      if constexpr (KIND == kNormLayer) windows_cut<T, VEC, NV>(db, ba, bb, bv);
-      // the partial vectors completed, now that every load is in flight
+      // the partial vectors completed, now that every load is in flight;
+      // a LayerNorm row's elements outside it take the value K (below)
+      // (every vector not read whole, before the partial ones are set)
+      const float fill = KIND == kNormLayer ? uniform_f32(k_first) : 0.0f;
+      if constexpr (KIND == kNormLayer) {
+#pragma unroll
+        for (int k = 0; k < NV; ++k)
+          if (!inside(k * rl.T + rl.t)) px[k].fill(fill);
+      }
       if (edge0) {
-        cx[0].finish_cut(lo0, hi0, 0.0f);
+        cx[0].finish_cut(lo0, hi0, fill);
         px[0] = cx[0];
         if constexpr (KIND == kNormFused) {
           cr[0].finish_cut(lo0, hi0, 0.0f);
@@ -658,7 +726,7 @@ __global__ __launch_bounds__(1024) void norm_regs_kernel(T* y, T* residual, cons
       }
       if (edge1) {
         const int kl = last / rl.T;
-        cx[1].finish_cut(0, hi1, 0.0f);
+        cx[1].finish_cut(0, hi1, fill);
         if constexpr (KIND == kNormFused) cr[1].finish_cut(0, hi1, 0.0f);
 #pragma unroll
         for (int k = 0; k < NV; ++k) {
@@ -708,6 +776,13 @@ __global__ __launch_bounds__(1024) void norm_regs_kernel(T* y, T* residual, cons
       Packed<T, VEC> px[NV];
       issue_row<T, VEC, NV>(x + ox, nvec, rl.T, rl.t, px);
       params_after_loads();
+      if constexpr (KIND == kNormLayer) {
+        // lanes past the row's end hold the value K (below)
+        const float fill = uniform_f32(k_first);
+#pragma unroll
+        for (int k = 0; k < NV; ++k)
+          if (k * rl.T + rl.t >= nvec) px[k].fill(fill);
+      }
       widen_row<T, VEC, NV>(px, h);
     }
 
@@ -725,20 +800,17 @@ __global__ __launch_bounds__(1024) void norm_regs_kernel(T* y, T* residual, cons
       // butterflies give every lane the same bits), so lane 0's copies are
       // moved to scalar registers, which frees vector registers
       const float K = uniform_f32(k_first);
-      // sum(h - S) and sum((h - S)^2) over the row, one reduction
+      // sum(h - S) and sum((h - S)^2) over the lane's values, one
+      // reduction.  A value outside the row holds S (K in the first pass,
+      // 0 in the second), so it adds exactly zero and needs no test.
       auto pair_sums = [&](float S, float& s1, float& s2) {
         s1 = 0.0f;
         s2 = 0.0f;
 #pragma unroll
         for (int k = 0; k < NV; ++k) {
-          const int vi = k * rl.T + rl.t;
-          const bool valid = vi < nvec;
 #pragma unroll
           for (int i = 0; i < VEC; ++i) {
-            // SHIFT: elements outside the row (partial vectors) count nothing
-            const int e = vi * VEC - lead + i;
-            const bool in = SHIFT ? (vi < nvec_row && e >= 0 && e < N) : valid;
-            const float d = in ? h[k][i] - S : 0.0f;
+            const float d = h[k][i] - S;
             s1 += d;
             s2 += d * d;
           }
@@ -769,6 +841,21 @@ __global__ __launch_bounds__(1024) void norm_regs_kernel(T* y, T* residual, cons
 #pragma unroll
           for (int i = 0; i < VEC; ++i) h[k][i] = h[k][i] - shift;
         if (near) break;
+        // the values outside the row, K before the shift, are set to the
+        // second pass's S.  (The vector's first element index is made
+        // opaque here: else the compiler computes these tests before the
+        // loop, for every row, and holds their masks through it.)
+#pragma unroll
+        for (int k = 0; k < NV; ++k) {
+          int vi = k * rl.T + rl.t;
+          asm volatile("" : "+v"(vi));
+#pragma unroll
+          for (int i = 0; i < VEC; ++i) {
+            const int e = vi * VEC - lead + i;
+            const bool in = SHIFT ? (vi < nvec_row && (unsigned)e < (unsigned)N) : vi < nvec;
+            if (!in) h[k][i] = 0.0f;
+          }
+        }
         S = 0.0f;
       }
 #pragma unroll
@@ -776,12 +863,47 @@ __global__ __launch_bounds__(1024) void norm_regs_kernel(T* y, T* residual, cons
 #pragma unroll
         for (int i = 0; i < VEC; ++i) h[k][i] = h[k][i] - c;
       const float rstd = 1.0f / __builtin_sqrtf(__builtin_fmaxf(var, 0.0f) + eps);
+      if constexpr (kLdsParams) {
+        // each vector's gamma and beta windows cut from the blocks in LDS
+        const int lg = row_lead(gamma, VEC);
+        const int lb = beta ? row_lead(beta, VEC) : lg;
+        const int amg = (N - 1 + lg) / VEC, amb = (N - 1 + lb) / VEC;
+        auto blk = [&](int e, int l, int amax) {
+          const int a = (e + l) >= 0 ? (e + l) / VEC : -((VEC - 1 - (e + l)) / VEC);
+          return a < 0 ? 0 : (a > amax ? amax : a);
+        };
+        auto lds_block = [&](int a, Packed<T, VEC>& out) {
+          const uint4 q = params_lds[a];
+          out.w[0] = q.x; out.w[1] = q.y; out.w[2] = q.z; out.w[3] = q.w;
+        };
+        const int dg = (lg - lead) & (VEC - 1), db = (lb - lead) & (VEC - 1);
 #pragma unroll
-      for (int k = 0; k < NV; ++k) {
-        float o[VEC];
+        for (int k = 0; k < NV; ++k) {
+          const int e0 = (k * rl.T + rl.t) * VEC - lead;
+          Packed<T, VEC> A[1], Bk[1], G[1], Bt[1];
+          lds_block(blk(e0, lg, amg), A[0]);
+          lds_block(blk(e0 + VEC, lg, amg), Bk[0]);
+          windows_cut<T, VEC, 1>(dg, A, Bk, G);
+          if (beta) {
+            lds_block(nbmax + blk(e0, lb, amb), A[0]);
+            lds_block(nbmax + blk(e0 + VEC, lb, amb), Bk[0]);
+            windows_cut<T, VEC, 1>(db, A, Bk, Bt);
+          } else {
+            Bt[0].zero();
+          }
+          float o[VEC];
 #pragma unroll
-        for (int i = 0; i < VEC; ++i) o[i] = (h[k][i] * rstd) * gv[k].get(i) + bv[k].get(i);
-        store_row(y + oy, k, o);
+          for (int i = 0; i < VEC; ++i) o[i] = (h[k][i] * rstd) * G[0].get(i) + Bt[0].get(i);
+          store_row(y + oy, k, o);
+        }
+      } else {
+#pragma unroll
+        for (int k = 0; k < NV; ++k) {
+          float o[VEC];
+#pragma unroll
+          for (int i = 0; i < VEC; ++i) o[i] = (h[k][i] * rstd) * gv[k].get(i) + bv[k].get(i);
+          store_row(y + oy, k, o);
+        }
       }
     } else {
       float ss = 0.0f;
@@ -2051,6 +2173,8 @@ namespace {
 
 inline dim3 grid1(int64_t g) { return dim3((unsigned)g, 1, 1); }
 
+int resident_groups(const void* kernel, int threads, size_t lds);
+
 template <typename T, int KIND, bool WAVE, bool SHIFT>
 hipError_t norm_regs(const rr_plan& p, const NormArgs& a, int64_t grid, hipStream_t s) {
   T* yy = static_cast<T*>(a.y);
@@ -2059,22 +2183,39 @@ hipError_t norm_regs(const rr_plan& p, const NormArgs& a, int64_t grid, hipStrea
   const T* gg = static_cast<const T*>(a.gamma);
   const T* bb = static_cast<const T*>(a.beta);
   const dim3 b(p.block_threads);
+  // LDS for a cut LayerNorm row's gamma and beta blocks (the host plans such
+  // rows only while it fits kNormLdsParamMax)
+  const size_t lds = norm_lds_params<KIND, WAVE, SHIFT>() ? norm_lds_param_bytes<T>(a.N) : 0;
+  if (lds > kNormLdsParamMax) return hipErrorInvalidValue;
+  if constexpr (norm_lds_params<KIND, WAVE, SHIFT>()) {
+    // each workgroup stages the parameters once and walks rows grid-stride:
+    // no more workgroups than the device holds at once
+    const void* k = nullptr;
+    switch (p.vecs_per_lane) {
+      case 1: k = reinterpret_cast<const void*>(&norm_regs_kernel<T, 1, KIND, WAVE, SHIFT>); break;
+      case 2: k = reinterpret_cast<const void*>(&norm_regs_kernel<T, 2, KIND, WAVE, SHIFT>); break;
+      case 3: k = reinterpret_cast<const void*>(&norm_regs_kernel<T, 3, KIND, WAVE, SHIFT>); break;
+      default: return hipErrorInvalidValue;
+    }
+    const int cap = resident_groups(k, p.block_threads, lds);
+    if (cap > 0 && grid > cap) grid = cap;
+  }
   // The host plans at most 16 values per lane for the norms (NV * VEC <=
   // 16), 24 for cut rows (3 bf16 vectors), so only those instantiations exist.
   switch (p.vecs_per_lane) {
-    case 1: norm_regs_kernel<T, 1, KIND, WAVE, SHIFT><<<grid1(grid), b, 0, s>>>(yy, rr_, xx, gg, bb, a.M, a.N, a.eps, a.ld); break;
-    case 2: norm_regs_kernel<T, 2, KIND, WAVE, SHIFT><<<grid1(grid), b, 0, s>>>(yy, rr_, xx, gg, bb, a.M, a.N, a.eps, a.ld); break;
+    case 1: norm_regs_kernel<T, 1, KIND, WAVE, SHIFT><<<grid1(grid), b, lds, s>>>(yy, rr_, xx, gg, bb, a.M, a.N, a.eps, a.ld); break;
+    case 2: norm_regs_kernel<T, 2, KIND, WAVE, SHIFT><<<grid1(grid), b, lds, s>>>(yy, rr_, xx, gg, bb, a.M, a.N, a.eps, a.ld); break;
     case 3:
       // (cut rows only: fewer wavefronts per row where that saves some)
       if constexpr (SHIFT && !WAVE) {
-        norm_regs_kernel<T, 3, KIND, WAVE, SHIFT><<<grid1(grid), b, 0, s>>>(yy, rr_, xx, gg, bb, a.M, a.N, a.eps, a.ld);
+        norm_regs_kernel<T, 3, KIND, WAVE, SHIFT><<<grid1(grid), b, lds, s>>>(yy, rr_, xx, gg, bb, a.M, a.N, a.eps, a.ld);
         break;
       }
       return hipErrorInvalidValue;
     case 4:
       // (cut fp32 LayerNorm rows keep to 2 vectors per lane: 4 would spill)
       if constexpr (Elem<T>::kVec * 4 <= 16 && !(SHIFT && KIND == kNormLayer)) {
-        norm_regs_kernel<T, 4, KIND, WAVE, SHIFT><<<grid1(grid), b, 0, s>>>(yy, rr_, xx, gg, bb, a.M, a.N, a.eps, a.ld);
+        norm_regs_kernel<T, 4, KIND, WAVE, SHIFT><<<grid1(grid), b, lds, s>>>(yy, rr_, xx, gg, bb, a.M, a.N, a.eps, a.ld);
         break;
       }
       return hipErrorInvalidValue;
@@ -2248,26 +2389,28 @@ hipError_t softmax_rows_held(const rr_plan& p, const SmCall<Tin, Tout>& c, int64
   return softmax_regs<Tin, Tout, false, LOG, CAUSAL, SHIFT>(p, c, grid, s);
 }
 
-// Workgroups of `kernel` (256 threads) the current device holds at once
-// (its occupancy times the compute units), or 0 if unknown.  Cached per
-// device and kernel.
-int resident_capacity(const void* kernel) {
+// Workgroups of `kernel` (`threads` threads, `lds` bytes of dynamic LDS)
+// the current device holds at once (its occupancy times the compute units),
+// or 0 if unknown.  Cached per device, kernel, size and LDS.
+int resident_groups(const void* kernel, int threads, size_t lds) {
   static std::mutex mu;
-  static std::map<std::pair<int, const void*>, int> cache;
+  static std::map<std::tuple<int, const void*, int, size_t>, int> cache;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 0;
   std::lock_guard<std::mutex> lock(mu);
-  auto key = std::make_pair(dev, kernel);
+  auto key = std::make_tuple(dev, kernel, threads, lds);
   auto it = cache.find(key);
   if (it != cache.end()) return it->second;
   int cus = 0, per_cu = 0;
   int cap = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
-      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 256, 0) == hipSuccess)
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, lds) == hipSuccess)
     cap = cus * per_cu;
   cache[key] = cap;
   return cap;
 }
+
+int resident_capacity(const void* kernel) { return resident_groups(kernel, 256, 0); }
 
 // A 32-bit value that differs from the previous 2^32 - 1 calls' in this
 // process, for the one-kernel split's slot tags; the sequence starts at a

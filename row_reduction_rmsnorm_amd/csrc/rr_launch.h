@@ -65,6 +65,11 @@ struct SoftmaxArgs {
   uint64_t split_wait_ticks;
 };
 
+// LDS a cut LayerNorm row held by a workgroup may take for gamma's and
+// beta's aligned blocks: 2 x (N + 2 VEC - 2) / VEC blocks of 16 bytes.  The
+// host cuts such rows only up to this (bf16: 15353 elements, fp32: 7677).
+constexpr size_t kNormLdsParamMax = 61440;
+
 // The one-kernel split's wait: 40 us.  Its workgroups all run at once (the
 // host launches it only when the device holds the whole grid), so a
 // summary normally arrives within a few microseconds.
