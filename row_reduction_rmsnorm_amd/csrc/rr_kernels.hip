@@ -868,10 +868,11 @@ __global__ __launch_bounds__(1024) void norm_regs_kernel(T* y, T* residual, cons
         const int lg = row_lead(gamma, VEC);
         const int lb = beta ? row_lead(beta, VEC) : lg;
         const int amg = (N - 1 + lg) / VEC, amb = (N - 1 + lb) / VEC;
-        auto blk = [&](int e, int l, int amax) {
-          const int a = (e + l) >= 0 ? (e + l) / VEC : -((VEC - 1 - (e + l)) / VEC);
-          return a < 0 ? 0 : (a > amax ? amax : a);
-        };
+        // vector vi's window starts in block vi + q, q = floor((l - lead) /
+        // VEC) (the same for the whole row); blocks clamped to 0 .. amax
+        auto floor_div = [](int v) { return v >= 0 ? v / VEC : -((VEC - 1 - v) / VEC); };
+        const int qg = floor_div(lg - lead), qb = floor_div(lb - lead);
+        auto clamp_block = [](int a, int amax) { return a < 0 ? 0 : (a > amax ? amax : a); };
         auto lds_block = [&](int a, Packed<T, VEC>& out) {
           const uint4 q = params_lds[a];
           out.w[0] = q.x; out.w[1] = q.y; out.w[2] = q.z; out.w[3] = q.w;
@@ -879,14 +880,14 @@ __global__ __launch_bounds__(1024) void norm_regs_kernel(T* y, T* residual, cons
         const int dg = (lg - lead) & (VEC - 1), db = (lb - lead) & (VEC - 1);
 #pragma unroll
         for (int k = 0; k < NV; ++k) {
-          const int e0 = (k * rl.T + rl.t) * VEC - lead;
+          const int vi = k * rl.T + rl.t;
           Packed<T, VEC> A[1], Bk[1], G[1], Bt[1];
-          lds_block(blk(e0, lg, amg), A[0]);
-          lds_block(blk(e0 + VEC, lg, amg), Bk[0]);
+          lds_block(clamp_block(vi + qg, amg), A[0]);
+          lds_block(clamp_block(vi + qg + 1, amg), Bk[0]);
           windows_cut<T, VEC, 1>(dg, A, Bk, G);
           if (beta) {
-            lds_block(nbmax + blk(e0, lb, amb), A[0]);
-            lds_block(nbmax + blk(e0 + VEC, lb, amb), Bk[0]);
+            lds_block(nbmax + clamp_block(vi + qb, amb), A[0]);
+            lds_block(nbmax + clamp_block(vi + qb + 1, amb), Bk[0]);
             windows_cut<T, VEC, 1>(db, A, Bk, Bt);
           } else {
             Bt[0].zero();
