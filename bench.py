@@ -270,7 +270,8 @@ def measure_extras(torch, rr, dev, K, bufs):
     for bandwidth), the attention-score softmax through the causal rule (only
     the kept keys are read: row i of a head reads i + 1 keys and writes all
     4096), log-softmax on the vocabulary logits, rows that are not whole
-    vectors (a 50257-wide vocabulary softmax, an RMSNorm of 4097), and the
+    vectors (a 50257-wide vocabulary softmax; an RMSNorm, a LayerNorm and a
+    fused add + RMSNorm of 4097), and the
     vocabulary softmax at decode-size row counts (1, 16, 48 rows of 152064
     bf16 -> fp32: the split path, two kernels)."""
     import numpy as np
@@ -372,7 +373,15 @@ def measure_extras(torch, rr, dev, K, bufs):
     ys = [torch.empty_like(xs[0]) for _ in range(n)]
     g = workloads.to_dtype(workloads.gamma_vector(N, 3), "bf16").to(dev)
     timed("rmsnorm_bf16_8192x4097_rows_cut", lambda k: rr.rr_rmsnorm(ys[k], xs[k], g, 1e-6), nb, M, sets=n)
-    del xs, ys, g
+    bt = workloads.to_dtype(workloads.gamma_vector(N, 4) - 1.0, "bf16").to(dev)
+    timed("layernorm_bf16_8192x4097_rows_cut", lambda k: rr.rr_layernorm(ys[k], xs[k], g, bt, 1e-5),
+          nb + N * 2, M, sets=n)
+    # the fused op rewrites its residual in place: each copy's residual
+    # drifts from call to call, which does not change the work
+    rs = [workloads.to_dtype(rng.standard_normal((M, N), dtype=np.float32), "bf16").to(dev) for _ in range(n)]
+    timed("fused_add_rmsnorm_bf16_8192x4097_rows_cut",
+          lambda k: rr.rr_fused_add_rmsnorm(ys[k], rs[k], xs[k], g, 1e-6), 2 * nb - N * 2, M, sets=n)
+    del xs, ys, g, bt, rs
 
     # the vocabulary softmax at decode-size row counts: few long rows split
     # over many workgroups (statistics pass, then the normalising pass)
