@@ -777,11 +777,14 @@ __global__ __launch_bounds__(1024) void norm_regs_kernel(T* y, T* residual, cons
       issue_row<T, VEC, NV>(x + ox, nvec, rl.T, rl.t, px);
       params_after_loads();
       if constexpr (KIND == kNormLayer) {
-        // lanes past the row's end hold the value K (below)
-        const float fill = uniform_f32(k_first);
+        // lanes past the row's end hold the value K (below); a row that
+        // fills every lane's vectors (a uniform test) has none
+        if (nvec < NV * rl.T) {
+          const float fill = uniform_f32(k_first);
 #pragma unroll
-        for (int k = 0; k < NV; ++k)
-          if (k * rl.T + rl.t >= nvec) px[k].fill(fill);
+          for (int k = 0; k < NV; ++k)
+            if (k * rl.T + rl.t >= nvec) px[k].fill(fill);
+        }
       }
       widen_row<T, VEC, NV>(px, h);
     }
