@@ -480,11 +480,11 @@ __device__ __forceinline__ void windows_cut(int d, const Packed<T, VEC> (&A)[NV]
 // (window_cut; they stay in the cache across rows).
 // ===========================================================================
 // Cut LayerNorm rows held by a workgroup read gamma and beta through LDS:
-// each lane loads aligned blocks of both with the row, writes them to LDS,
-// and cuts its windows from there after the row's reduction.  Held in
-// registers (two blocks of each per vector while the row loads) they cost a
-// cut LayerNorm row so many registers that a CU held half as many rows as
-// for RMSNorm.
+// the workgroup loads the aligned blocks of both into LDS once, before its
+// first row, and each row cuts its windows from there after its reduction.
+// Held in registers (two blocks of each per vector while the row loads) they
+// cost a cut LayerNorm row so many registers that a CU held half as many
+// rows as for RMSNorm.
 template <int KIND, bool WAVE, bool SHIFT>
 constexpr bool norm_lds_params() {
   return SHIFT && !WAVE && KIND == kNormLayer;
@@ -512,9 +512,8 @@ __global__ __launch_bounds__(1024) void norm_regs_kernel(T* y, T* residual, cons
 
   if constexpr (kLdsParams) {
     // gamma's (beta's) aligned 16-byte blocks 0 .. amax, the same for every
-    // row: gamma at [0, nbmax), beta at [nbmax, 2 nbmax).  Each row cuts its
-    // windows out of them after its reduction, whose barrier (like this one)
-    // orders these writes before every read.
+    // row: gamma at [0, nbmax), beta at [nbmax, 2 nbmax).  The barrier below
+    // orders these writes before every read; nothing rewrites them.
     const int lg = row_lead(gamma, VEC);
     const int lb = beta ? row_lead(beta, VEC) : lg;
     const int ng = (N - 1 + lg) / VEC + 1, nb = (N - 1 + lb) / VEC + 1;
