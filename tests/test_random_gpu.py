@@ -174,3 +174,80 @@ def test_random_softmax_rows_cut_at_aligned_addresses(case):
         compare.check_log_softmax(ys.cpu(), xf, oracle.log_softmax(xf), what)
     else:
         compare.check_softmax(ys.cpu(), xf, oracle.softmax(xf), what)
+
+
+NORM_CUT_CASES = 36
+
+
+@pytest.mark.parametrize("case", range(NORM_CUT_CASES))
+def test_random_norm_rows_cut_at_aligned_addresses(case):
+    """RMSNorm, fused add + RMSNorm and LayerNorm (with and without beta) on
+    rows cut at aligned addresses, drawn at random: widths off the vector
+    grid up to past the register kernels' reach, contiguous rows (every row
+    at its own offset) or column slices of one offset, gamma (beta) aligned or
+    a slice at any offset of a longer vector whose other elements are NaN,
+    and rows whose first element lies far from their mean."""
+    rr = _rr()
+    rng = np.random.default_rng(7000 + case)
+    N = int(rng.integers(33, 20000)) | 1
+    M = _rows(rng, N)
+    dt = "bf16" if rng.random() < 0.5 else "f32"
+    kind = ["rms", "fused", "layer", "layer_nobeta"][case % 4]
+    x = workloads.random_rows(M, N, seed=case + 11, offset_every=4, offset=30.0)
+    if kind.startswith("layer"):
+        x[::3, 0] = 1.0e3                 # first element far from the row's mean
+    x = _as(x, dt)
+    g = _as(workloads.gamma_vector(N, seed=case + 12), dt)
+    b = _as(workloads.gamma_vector(N, seed=case + 13) - 1.0, dt)
+
+    def param(v):
+        if rng.random() < 0.5:
+            return v.cuda()
+        off = int(rng.integers(1, 16))
+        buf = torch.full((N + off + 16,), float("nan"), dtype=v.dtype, device="cuda")
+        buf[off:off + N] = v.cuda()
+        return buf[off:off + N]
+
+    contiguous = rng.random() < 0.5
+    pad = 0 if contiguous else int(rng.integers(1, 9))
+    ld = N if contiguous else N + pad + 8 * int(rng.integers(0, 3))
+
+    def embed(t):
+        if contiguous:
+            return t.cuda(), None
+        buf = torch.zeros((M, ld), dtype=t.dtype, device="cuda")
+        buf[:, pad:pad + N] = t.cuda()
+        return buf[:, pad:pad + N], buf
+
+    op = {"rms": rr.RR_OP_RMSNORM, "fused": rr.RR_OP_FUSED_ADD_RMSNORM}.get(kind, rr.RR_OP_LAYERNORM)
+    code = rr.RR_F32 if dt == "f32" else rr.RR_BF16
+    plan = rr.rr_query_plan(op, M, N, code, code, 2)
+    _say(f"random cut-row norm {case}: {kind} {dt} {M}x{N} contiguous={contiguous} pad={pad} "
+         f"plan={plan['variant_name']} shift={plan['row_shift']} nv={plan['vecs_per_lane']}")
+    xs, _ = embed(x)
+    ys, ybuf = embed(torch.zeros((M, N), dtype=_tdt(dt)))
+    gd = param(g)
+    what = f"random cut-row norm {case} {kind} {dt} {M}x{N}"
+    if kind == "rms":
+        rr.rr_rmsnorm_strided(ys, xs, gd, 1e-6)
+        torch.cuda.synchronize()
+        check_norm(x, g, 1e-6, dt, ys.cpu(), what)
+    elif kind == "fused":
+        r = _as(workloads.random_rows(M, N, seed=case + 14), dt)
+        rs, _ = embed(r)
+        rr.rr_fused_add_rmsnorm_strided(ys, rs, xs, gd, 1e-6)
+        torch.cuda.synchronize()
+        check_fused(x, r, g, 1e-6, dt, ys.cpu(), rs.cpu(), what)
+    else:
+        with_beta = kind == "layer"
+        bd = param(b) if with_beta else None
+        rr.rr_layernorm_strided(ys, xs, gd, bd, 1e-5)
+        torch.cuda.synchronize()
+        gf = compare.to_f64(g)
+        bf = compare.to_f64(b) if with_beta else np.zeros(N)
+        ref = oracle.layernorm(compare.to_f64(x), gf, bf, 1e-5)
+        compare.check_layernorm(ys.cpu(), ref, gf, bf, what)
+    if ybuf is not None:
+        # nothing outside the slice is written
+        outside = torch.cat([ybuf[:, :pad], ybuf[:, pad + N:]], dim=1)
+        assert not outside.any(), f"{what}: writes outside the slice"
