@@ -32,8 +32,8 @@
  *     calls only enqueue kernels (no memsets, copies or host callbacks), so
  *     a caller may capture them into a HIP graph; a captured call reads its
  *     buffers when the graph replays.  (The one-kernel form of the split row
- *     tags its workspace slots at launch, so a call on a capturing stream
- *     runs the two-kernel form, with the same bits.)
+ *     tags its workspace slots from per-row epochs that it reads and
+ *     advances on the device, so each replay tags them afresh.)
  *   - Errors: arguments are checked on the host before anything is enqueued;
  *     a failed check returns a non-zero rr_status and enqueues nothing.
  *     M == 0 is a successful no-op.  An empty row (N or H < 1) is the
@@ -150,9 +150,11 @@ rr_status rr_layernorm(void* y, const void* x, const void* gamma, const void* be
  * for this shape (0 when the chosen kernel needs none).  Very long rows with
  * few rows are split over several workgroups; each writes its chunk's
  * (m, d) pair to a 16-byte slot of the workspace and the row's slots are
- * merged ([P4] section "练习", the vocabulary-split exercise).  The size
- * covers rows at any address (a row starting inside a vector may take one
- * more chunk).  Host-only; returns 0 for invalid arguments.
+ * merged ([P4] section "练习", the vocabulary-split exercise): M * S slots
+ * (S chunks per row), then one 4-byte epoch per row, padded to a multiple of
+ * 16 bytes.  The size covers rows at any address (a row starting inside a
+ * vector may take one more chunk).  Host-only; returns 0 for invalid
+ * arguments.
  */
 size_t rr_softmax_rows_workspace_bytes(int64_t M, int64_t N, rr_dtype in_dtype,
                                        rr_dtype out_dtype);
@@ -170,9 +172,11 @@ size_t rr_softmax_rows_workspace_bytes(int64_t M, int64_t N, rr_dtype in_dtype,
  *              +inf and NaN inputs are not supported
  *   workspace  device buffer of at least rr_softmax_rows_workspace_bytes(M, N,
  *              in_dtype, out_dtype) bytes, 16-byte aligned (may be NULL when
- *              that size is 0); contents on entry are ignored (slots are
- *              tagged per call); calls that overlap in time must not share
- *              a workspace
+ *              that size is 0); contents on entry are ignored (the
+ *              one-kernel split tags its slots with per-row epochs kept in
+ *              the workspace, which it advances, so any later call of any
+ *              shape may reuse it); calls that overlap in time must not
+ *              share a workspace
  * Masked entries produce exactly 0; a row whose entries are all -inf
  * produces NaN everywhere (-inf - (-inf)).  Probabilities below 2^-126
  * come out as bf16 subnormals when out_dtype is RR_BF16, and as 0 when it
@@ -327,12 +331,12 @@ typedef enum rr_op {
  *         wavefront totals combined through LDS (N <= 32768)
  *   SPLIT several workgroups per row (softmax, long rows with few rows),
  *         each summarising its chunk as (m, d) into the workspace.  Where the
- *         rows are aligned, a row has at most 64 chunks, the device holds
- *         every workgroup of the grid at once and the stream is not
- *         capturing a graph, this is ONE kernel: each workgroup keeps its
- *         chunk in registers, publishes its pair in a tagged slot, waits (a
- *         bounded time, then summarises a missing chunk itself) for the
- *         row's other pairs, merges them and normalises, so x is read once.
+ *         rows are aligned, a row has at most 64 chunks and the device
+ *         holds every workgroup of the grid at once, this is ONE kernel:
+ *         each workgroup keeps its chunk in registers, publishes its pair in
+ *         a tagged slot, waits (a bounded time, then summarises a missing
+ *         chunk itself) for the row's other pairs, merges them and
+ *         normalises, so x is read once.
  *         Otherwise two kernels: the summaries, then a second that merges a
  *         row's pairs and normalises, re-reading x (rows of more than 64
  *         chunks get a merge kernel in between that folds each row's pairs
@@ -368,7 +372,7 @@ typedef struct rr_plan {
   int32_t block_threads;    /* workgroup size */
   int64_t chunks_per_row;   /* SPLIT: workgroups per row; otherwise 1 */
   int64_t work_items;       /* workgroup-steps needed (rows / rows_per_group x chunks) */
-  size_t workspace_bytes;   /* SPLIT: M * chunks_per_row * 16; otherwise 0 */
+  size_t workspace_bytes;   /* SPLIT: M * chunks_per_row * 16 + 4 M (to 16); otherwise 0 */
   int32_t row_shift;        /* 1: rows cut into vectors at aligned addresses (WAVE, BLOCK;
                                a softmax also SPLIT, LOOP): a row starting inside a vector, or ending inside one, is
                                accessed whole vectors at a time except its first and last

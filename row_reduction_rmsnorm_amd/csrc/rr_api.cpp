@@ -509,7 +509,9 @@ rr_status make_plan(rr_op op, int64_t M, int64_t N, int din, int dout, int align
       p->variant == RR_VARIANT_SPLIT_TWO_KERNELS) {
     if (p->chunks_per_row > (int64_t)1 << 30) return fail(RR_ERR_UNSUPPORTED, "too many chunks");
     p->work_items = M * p->chunks_per_row;
-    p->workspace_bytes = (size_t)M * (size_t)p->chunks_per_row * 16u;
+    // M * S slots of 16 bytes, then one 32-bit epoch per row (the
+    // one-kernel form's tags), padded to 16 bytes
+    p->workspace_bytes = (size_t)M * (size_t)p->chunks_per_row * 16u + ((size_t)M * 4u + 15u) / 16u * 16u;
   } else {
     p->work_items = ceil_div(M, p->rows_per_group);
   }

@@ -29,11 +29,6 @@
 //  * the grid may be smaller than the number of rows (it is capped so that a
 //    dispatch's work-items fit in 32 bits): workgroups then walk rows with a
 //    stride of gridDim.x; gamma stays in registers across rows.
-#include <time.h>
-#include <unistd.h>
-
-#include <chrono>
-
 #include <atomic>
 #include <map>
 #include <mutex>
@@ -1822,7 +1817,9 @@ __global__ __launch_bounds__(1024) void softmax_loop_kernel(const Tin* x, Tout* 
 // HBM reads are in flight during the merge.
 // ===========================================================================
 // One (m, d) slot per chunk, 16 bytes: the two-kernel form uses m and d; the
-// one-kernel form also uses the tag.
+// one-kernel form reads the 16 bytes as two tagged words (SplitWords).  After
+// the M * S slots the workspace holds one 32-bit epoch per row, which only
+// the one-kernel form uses.
 struct SplitSlot {
   float m;
   float d;
@@ -2041,15 +2038,28 @@ __global__ __launch_bounds__(256) void softmax_split_apply_kernel(const Tin* x, 
 //  * Launch: an ordinary launch, one workgroup per chunk, taken only when
 //    the device holds the whole grid at once (its occupancy) and rows have
 //    at most 64 chunks.
+//  * Tag: the workspace holds, after the M * S slots, one 32-bit epoch per
+//    row.  Every workgroup of the row reads it first; the call's tag for the
+//    row is a fixed bijection of it (split_tag).  A workgroup that has all
+//    of its row's summaries in hand advances the epoch by one with a
+//    compare-and-swap from the value it read (the first such workgroup wins;
+//    the others find it advanced and leave it): every workgroup of the row
+//    has published, so has read the epoch, before any can do so.  The next
+//    call on the workspace therefore tags the row differently, and the tag
+//    is read on the device, not fixed at launch, so a replayed graph tags
+//    each replay afresh.  (A workgroup kept from starting until its
+//    row-mates gave up on it reads the advanced epoch, finds no partner
+//    carrying its tag, summarises the row's other chunks itself and advances
+//    the epoch once more: slow, still exact, still a fresh tag next call.)
 //  * Publish: thread 0 writes the chunk's (m, d) as two 64-bit words with
 //    relaxed agent-scope atomic stores: the low half of each word holds m's
-//    (d's) bits, the high half the call's 32-bit tag, which differs from
-//    call to call.  No fence is needed: each word is read whole, so a reader
-//    that finds the tag in both words holds this call's m and d.  (Both
-//    words carry the same per-call tag: were they to carry two halves of a
-//    longer one, consecutive calls would share the upper half and a reader
-//    could pair this call's m with the last call's d.)  Slots left by
-//    earlier calls carry other tags; uninitialised memory matches in both
+//    (d's) bits, the high half the row's tag for this call.  No fence is
+//    needed: each word is read whole, so a reader that finds the tag in both
+//    words holds this call's m and d.  (Both words carry the same tag: were
+//    they to carry two halves of a longer one, a reader could pair this
+//    call's m with another call's d.)  Slots left by the previous call on
+//    the row carry the previous tag; memory never written by this kernel
+//    (a fresh workspace, or one the two-kernel form used) matches in both
 //    words with probability 2^-64.
 //  * Wait: lane s of wavefront 0 polls slot s with relaxed agent-scope
 //    loads until both words carry the tag, for at most wait_ticks of the
@@ -2064,11 +2074,13 @@ __global__ __launch_bounds__(256) void softmax_split_apply_kernel(const Tin* x, 
 //    chunk s's pair, which is exactly what pass B's lanes hold after
 //    folding the workspace into the identity; the wave all-reduce and the
 //    outputs, written from the registers, follow as in pass B.
-//  * Graph capture: the tag is fixed at launch, so a replayed graph would
-//    find its own earlier tags in the slots; a capturing stream takes the
-//    two kernels instead.
 // ===========================================================================
 constexpr int kSplitFusedMaxChunks = kWave;         // one slot per lane of a wavefront
+
+// A row's tag for the call that finds its epoch at e: an odd multiplier and
+// an offset make it a bijection of the 32-bit epochs, and a zeroed
+// workspace (epoch 0, slot words 0) does not match.
+__device__ __forceinline__ uint32_t split_tag(uint32_t e) { return e * 0x9E3779B1u + 0x7F4A7C15u; }
 
 // The one-kernel form's view of a workspace slot: two tagged 64-bit words.
 struct SplitWords {
@@ -2079,9 +2091,8 @@ static_assert(sizeof(SplitWords) == sizeof(SplitSlot), "slot layout");
 
 template <typename Tin, typename Tout, int NV, bool LOG>
 __global__ __launch_bounds__(256) void softmax_split_fused_kernel(const Tin* x, Tout* y, SplitSlot* ws,
-                                                                  int64_t M, int N, int S, uint32_t tag,
-                                                                  uint64_t wait_ticks, unsigned int* fallbacks,
-                                                                  RowStrides ld) {
+                                                                  int64_t M, int N, int S, uint64_t wait_ticks,
+                                                                  unsigned int* fallbacks, RowStrides ld) {
   constexpr int VEC = softmax_vec<Tin, Tout>();
   constexpr int CV = 256 * NV;
   __shared__ MD slots[2][kMaxWavesPerGroup];
@@ -2094,6 +2105,10 @@ __global__ __launch_bounds__(256) void softmax_split_fused_kernel(const Tin* x, 
   const int64_t row = item / S;
   const int c = (int)(item - row * S);
   const Tin* xr = x + row * ld.x;
+  // the row's epoch (after the M * S slots) and this call's tag for the row
+  uint32_t* epoch = reinterpret_cast<uint32_t*>(ws + M * (int64_t)S) + row;
+  const uint32_t e0 = __hip_atomic_load(epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const uint32_t tag = split_tag(e0);
   int parity = 0;
   Packed<Tin, VEC> v[NV];
   split_chunk_load<NV>(xr, nvec, c, rl.t, v);
@@ -2146,6 +2161,12 @@ __global__ __launch_bounds__(256) void softmax_split_fused_kernel(const Tin* x, 
     if (threadIdx.x == 0) got[s] = r;
   }
   __syncthreads();
+  // every summary of the row is in hand: the next call tags the row afresh
+  if (threadIdx.x == 0) {
+    uint32_t expected = e0;
+    __hip_atomic_compare_exchange_strong(epoch, &expected, e0 + 1u, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_AGENT);
+  }
   MD q;
   if (rl.lane < S) {
     q = got[rl.lane];
@@ -2415,25 +2436,10 @@ int resident_groups(const void* kernel, int threads, size_t lds) {
 
 int resident_capacity(const void* kernel) { return resident_groups(kernel, 256, 0); }
 
-// A 32-bit value that differs from the previous 2^32 - 1 calls' in this
-// process, for the one-kernel split's slot tags; the sequence starts at a
-// hash of the process id, the clock and an address, so that slots another
-// process left in reused memory are unlikely to carry it either.
-uint32_t next_split_tag() {
-  static std::atomic<uint64_t> counter{[] {
-    uint64_t z = (uint64_t)std::chrono::steady_clock::now().time_since_epoch().count() ^
-                 ((uint64_t)getpid() << 32) ^ (uint64_t)(uintptr_t)&counter;
-    z = (z ^ (z >> 30)) * 0xbf58476d1ce4e5b9ull;   // splitmix64 finaliser
-    z = (z ^ (z >> 27)) * 0x94d049bb133111ebull;
-    return z ^ (z >> 31);
-  }()};
-  return (uint32_t)(counter.fetch_add(1, std::memory_order_relaxed) + 1);
-}
-
 // SPLIT (and SPLIT_ONE_KERNEL, which only forces the plan): the one-kernel
-// form when the rows are aligned, a row has at most 64 chunks, the device
-// holds the whole grid at once and the stream is not capturing; else the
-// two kernels.  SPLIT_TWO_KERNELS: always the two kernels.  Both forms use
+// form when the rows are aligned, a row has at most 64 chunks and the device
+// holds the whole grid at once (also on a capturing stream: its tags come
+// from the workspace's epochs, read on the device); else the two kernels.  SPLIT_TWO_KERNELS: always the two kernels.  Both forms use
 // the same chunks and the same merge order, so they give the same bits.  The
 // split forms keep every key (the planner never splits a causal call).
 template <typename Tin, typename Tout, int NV, bool LOG, bool SHIFT>
@@ -2443,16 +2449,14 @@ hipError_t softmax_split(const rr_plan& p, const SmCall<Tin, Tout>& c, SplitSlot
   if (c.cp > 0) return hipErrorInvalidValue;
   if constexpr (!SHIFT) {
     if (p.variant != RR_VARIANT_SPLIT_TWO_KERNELS && S <= kSplitFusedMaxChunks) {
-      hipStreamCaptureStatus capture = hipStreamCaptureStatusNone;
-      if (hipStreamIsCapturing(s, &capture) != hipSuccess) return hipErrorInvalidValue;
       const void* k = reinterpret_cast<const void*>(&softmax_split_fused_kernel<Tin, Tout, NV, LOG>);
       const int64_t items = c.M * (int64_t)S;
-      if (capture == hipStreamCaptureStatusNone && items <= resident_capacity(k)) {
+      if (items <= resident_capacity(k)) {
         hipError_t e = hipSuccess;
         unsigned int* counter = split_fallback_counter(&e);
         if (!counter) return e;
         softmax_split_fused_kernel<Tin, Tout, NV, LOG><<<grid1(items), b, 0, s>>>(
-            c.x, c.y, w, c.M, c.N, S, next_split_tag(), c.wait_ticks, counter, c.ld);
+            c.x, c.y, w, c.M, c.N, S, c.wait_ticks, counter, c.ld);
         return hipGetLastError();
       }
     }

@@ -20,6 +20,12 @@ HEADER = os.path.join(ROOT, "include", "rowreduce.h")
 DIAG_HEADER = os.path.join(ROOT, "include", "rowreduce_diag.h")
 
 
+def split_ws(M, S):
+    """A split plan's workspace: M * S slots of 16 bytes, then one 4-byte
+    epoch per row (the one-kernel form's tags), padded to 16 bytes."""
+    return M * S * 16 + (M * 4 + 15) // 16 * 16
+
+
 def _declared_functions(path=HEADER):
     text = open(path).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
@@ -143,7 +149,7 @@ def test_softmax_validation():
     # bf16 -> fp32 row is held by one workgroup and needs none)
     assert rr.rr_softmax_rows_workspace_bytes(256, 152064, rr.RR_BF16, rr.RR_F32) == 0
     need = rr.rr_softmax_rows_workspace_bytes(40, 152064, rr.RR_BF16, rr.RR_F32)
-    assert need == 40 * 19 * 16
+    assert need == split_ws(40, 19)
     assert f(Y, X, 40, 152064, rr.RR_BF16, rr.RR_F32, None, 0, None) == rr.RR_ERR_WORKSPACE
     assert f(Y, X, 40, 152064, rr.RR_BF16, rr.RR_F32, W, need - 8, None) == rr.RR_ERR_WORKSPACE
     assert f(Y, X, 40, 152064, rr.RR_BF16, rr.RR_F32, W + 8, need, None) == rr.RR_ERR_INVALID_ARG
@@ -193,7 +199,7 @@ def test_softmax_ex_validation():
     assert f(None, None, 0, 8, F, F, o(causal_period=3), None, 0, None) == rr.RR_OK
     # log-softmax of few long rows splits like softmax and needs the workspace
     need = rr.rr_softmax_rows_ex_workspace_bytes(40, 152064, B, F, o(log_output=True))
-    assert need == rr.rr_softmax_rows_workspace_bytes(40, 152064, B, F) == 40 * 19 * 16
+    assert need == rr.rr_softmax_rows_workspace_bytes(40, 152064, B, F) == split_ws(40, 19)
     assert f(Y, X, 40, 152064, B, F, o(log_output=True), None, 0, None) == rr.RR_ERR_WORKSPACE
     # a causal call never splits, so it needs no workspace
     assert rr.rr_softmax_rows_ex_workspace_bytes(40, 152064, B, F, o(causal_period=40)) == 0
@@ -379,8 +385,8 @@ def test_dispatch_boundaries():
                 continue
             p = sh(M, N, a, b, al)
             assert (p["variant_name"], p["row_shift"], p["vec_elems"], p["vecs_per_lane"]) == ("split", 1, vec, nv), p
-            assert p["chunks_per_row"] == chunks and p["workspace_bytes"] == M * chunks * 16, p
-            assert rr.rr_softmax_rows_workspace_bytes(M, N, a, b) == M * chunks * 16
+            assert p["chunks_per_row"] == chunks and p["workspace_bytes"] == split_ws(M, chunks), p
+            assert rr.rr_softmax_rows_workspace_bytes(M, N, a, b) == split_ws(M, chunks)
     assert rr.rr_query_plan(S, 4, 65536, F, F)["chunks_per_row"] == 16   # aligned rows: one chunk fewer
     assert sh(4, 50257, op=rr.RR_OP_SOFTMAX_CAUSAL)["variant_name"] == "block"
     # cut rows hand over to the packed kernel 24 rows later than aligned ones
@@ -417,16 +423,16 @@ def test_forced_variants():
         assert rr.rr_query_plan(S, 10, 1024, F, F)["variant_name"] == "loop"
     with rr.forced_variant(rr.RR_VARIANT_SPLIT):
         p = rr.rr_query_plan(S, 10, 1024, F, F)
-        assert p["variant_name"] == "split" and p["workspace_bytes"] == 10 * 1 * 16
-        assert rr.rr_softmax_rows_workspace_bytes(10, 1024, F, F) == 160
+        assert p["variant_name"] == "split" and p["workspace_bytes"] == split_ws(10, 1)
+        assert rr.rr_softmax_rows_workspace_bytes(10, 1024, F, F) == split_ws(10, 1)
         p = rr.rr_query_plan(S, 10, 1023, F, F, 2)      # a row cut at aligned addresses
         assert (p["variant_name"], p["row_shift"], p["vec_elems"]) == ("split", 1, 4)
     with rr.forced_variant(rr.RR_VARIANT_SPLIT_ONE_KERNEL):
         p = rr.rr_query_plan(S, 10, 5000, F, F)
         assert p["variant_name"] == "split1" and p["chunks_per_row"] == 2
         # the workspace query covers the aligned call even though cut rows are refused
-        assert rr.rr_softmax_rows_workspace_bytes(10, 5000, F, F) == 10 * 2 * 16
-        assert rr.rr_softmax_rows_workspace_bytes(1, 8, F, F) == 16
+        assert rr.rr_softmax_rows_workspace_bytes(10, 5000, F, F) == split_ws(10, 2)
+        assert rr.rr_softmax_rows_workspace_bytes(1, 8, F, F) == split_ws(1, 1)
         with pytest.raises(rr.RowReduceError):
             rr.rr_query_plan(S, 10, 5001, F, F)               # the one-kernel form takes aligned rows
         with pytest.raises(rr.RowReduceError):
@@ -522,7 +528,7 @@ def test_every_plan_covers_its_row():
                     if v == rr.RR_VARIANT_AUTO:
                         assert rr.rr_softmax_rows_workspace_bytes(M, N, din, dout) >= p["workspace_bytes"], p
                     assert p["chunks_per_row"] * 256 * nv * vec >= N, p
-                    assert p["workspace_bytes"] == M * p["chunks_per_row"] * 16, p
+                    assert p["workspace_bytes"] == split_ws(M, p["chunks_per_row"]), p
                     assert p["work_items"] == M * p["chunks_per_row"], p
                     continue
                 else:

@@ -130,12 +130,15 @@ def test_graph_replays_of_cut_rows_match_eager():
 
 
 def test_graph_replays_of_the_no_allocation_call_and_a_forced_one_kernel_split():
-    """Two calls that could not be captured otherwise: the no-allocation entry
-    point on a split row (its (m, d) slots in the library's static scratch,
-    no workspace argument), and the one-kernel split forced in the
-    diagnostics build, whose per-launch tags would be stale on replay -- a
-    capturing stream takes the two-kernel form instead.  Replays on changed
-    inputs equal eager two-kernel calls bit for bit."""
+    """The no-allocation entry point on a split row (its (m, d) slots in the
+    library's static scratch, no workspace argument) and the one-kernel
+    split forced in the diagnostics build, captured: the one-kernel form
+    stays one kernel in the graph, its slot tags coming from per-row epochs
+    that each replay reads and advances on the device.  Between replays the
+    graph's slots hold the previous replay's pairs (the eager references use
+    workspaces of their own), so a replay that took a stale pair for a fresh
+    one would be off; replays on changed inputs equal eager calls bit for
+    bit."""
     rr = _rr()
     s1 = softmax_input(24, 152064, seed=41, dt="bf16").cuda()
     y1 = torch.empty(s1.shape, dtype=torch.float32, device="cuda")
@@ -148,7 +151,7 @@ def test_graph_replays_of_the_no_allocation_call_and_a_forced_one_kernel_split()
         r1 = torch.empty_like(y1)
         r2 = torch.empty_like(y2)
         rr.rr_softmax_rows(r1, s1, rr.softmax_workspace(s1, torch.float32))
-        rr.rr_softmax_rows(r2, s2, ws2)
+        rr.rr_softmax_rows(r2, s2, rr.softmax_workspace(s2, torch.float32))
         torch.cuda.synchronize()
         return r1, r2
 
