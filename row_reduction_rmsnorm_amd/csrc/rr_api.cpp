@@ -305,7 +305,7 @@ void plan_loop(rr_plan* p, int vec, int64_t nvec) {
 // fused 8190 x 4097 71 as 9 of 1 (the aligned rule), 48.8 as 5 of 2 or 3 of
 // 3 (aligned: 43.9); fp32 4095 x 4097 26.8 as 9 of 2, 25.8 as 6 of 3, 26.9
 // as 5 of 4.  A cut LayerNorm row takes the same choice: its workgroup
-// stages gamma's and beta's blocks in LDS once (up to kNormLdsParamMax
+// stages gamma's and beta's elements in LDS once (up to kNormLdsParamMax
 // bytes), so its lanes hold no more than an RMSNorm row's.
 bool plan_block_cut(rr_plan* p, int vw, int64_t nvec) {
   int best_nv = 0;
@@ -339,8 +339,8 @@ bool plan_block_cut(rr_plan* p, int vw, int64_t nvec) {
 // streaming kernel, all cut the same way.  The split sizes its chunks for a
 // row at any offset (nvec_any) so that the workspace query, which sees no
 // addresses, covers every call.
-bool plan_shifted(rr_op op, bool causal, int64_t M, int64_t packed_rows, rr_plan* p, int vw, int per16,
-                  int64_t nvec_s, int64_t nvec_any) {
+bool plan_shifted(rr_op op, bool causal, int64_t M, int64_t N, int64_t packed_rows, rr_plan* p, int vw,
+                  int per16, int64_t nvec_s, int64_t nvec_any) {
   bool ok = true;
   if (op != RR_OP_SOFTMAX) {
     // a wavefront's cut row holds gamma's (and beta's) two aligned blocks
@@ -353,7 +353,7 @@ bool plan_shifted(rr_op op, bool causal, int64_t M, int64_t packed_rows, rr_plan
     } else {
       // a workgroup's cut LayerNorm row stages gamma and beta in LDS, sized
       // for a row at any offset; its kernel exists for 1 to 3 vectors per lane
-      const bool lds_ok = op != RR_OP_LAYERNORM || 2 * (size_t)nvec_any * 16 <= rr::kNormLdsParamMax;
+      const bool lds_ok = op != RR_OP_LAYERNORM || rr::norm_lds_param_bytes_for(N, 16 / vw) <= rr::kNormLdsParamMax;
       ok = lds_ok && plan_block_cut(p, vw, nvec_s) &&
            (op != RR_OP_LAYERNORM || p->vecs_per_lane <= 3);
     }
@@ -415,7 +415,7 @@ rr_status make_plan(rr_op op, int64_t M, int64_t N, int din, int dout, int align
   switch (forced) {
     case RR_VARIANT_AUTO:
       if (plan_sub(p, vec, nvec)) {
-      } else if (shiftable && plan_shifted(op, causal, M, packed_rows + kCutPackedExtraRows, p, vw, per16_s,
+      } else if (shiftable && plan_shifted(op, causal, M, N, packed_rows + kCutPackedExtraRows, p, vw, per16_s,
                                            nvec_s, nvec_any)) {
       } else if (vec == 1) {
         plan_loop(p, vec, nvec);
@@ -498,7 +498,7 @@ rr_status make_plan(rr_op op, int64_t M, int64_t N, int din, int dout, int align
       ok = !(vw == 4 && p->vecs_per_lane > 2);
     else
       ok = p->variant == RR_VARIANT_BLOCK && p->vecs_per_lane <= 3 &&
-           2 * (size_t)nvec_any * 16 <= rr::kNormLdsParamMax;
+           rr::norm_lds_param_bytes_for(N, 16 / vw) <= rr::kNormLdsParamMax;
   }
   if (!ok) {
     return fail(RR_ERR_UNSUPPORTED, "forced variant %d cannot run op %d with N = %lld (vector width %d)",

@@ -484,10 +484,30 @@ template <int KIND, bool WAVE, bool SHIFT>
 constexpr bool norm_lds_params() {
   return SHIFT && !WAVE && KIND == kNormLayer;
 }
-// Bytes of LDS such a kernel takes for rows of N elements.
+// Two layouts of the staged parameters:
+//  * fp32: one 8-byte entry per element, gamma's and beta's bits side by
+//    side, element e at entry e + kParamPad: a row's vectors start at most a
+//    64-byte frame's lead before the row (vectors wholly before it are
+//    empty, and read the pad) and the last reaches VEC - 1 past its end.  A
+//    vector's 4 entries are read as they lie, at any element offset.
+//  * bf16: gamma's (beta's) aligned 16-byte blocks 0 .. amax, gamma at
+//    [0, nbmax) and beta at [nbmax, 2 nbmax), and each vector's window cut
+//    from two blocks.  (One 4-byte entry per element measured slower for
+//    bf16: a lane's 8 entries are read as 4-byte pieces at a stride of 32
+//    bytes between lanes, and those reads collide in the LDS banks.)
+template <typename T>
+constexpr bool kParamEntries = std::is_same_v<T, float>;
+template <typename T>
+constexpr int kParamPad = 64 / (int)sizeof(T) - 1;
+// Bytes of LDS such a kernel takes for rows of N elements (the host's plan
+// uses the same count).
 template <typename T>
 constexpr size_t norm_lds_param_bytes(int N) {
-  return 2 * (size_t)((N + 2 * Elem<T>::kVec - 2) / Elem<T>::kVec) * 16;
+  static_assert(norm_lds_param_bytes_for(1, sizeof(T)) ==
+                    (kParamEntries<T> ? (1 + kParamPad<T> + Elem<T>::kVec) * 8
+                                      : 2 * ((1 + 2 * Elem<T>::kVec - 2) / Elem<T>::kVec) * 16),
+                "staged parameter layout");
+  return norm_lds_param_bytes_for(N, sizeof(T));
 }
 
 template <typename T, int NV, int KIND, bool WAVE, bool SHIFT>
@@ -502,34 +522,56 @@ __global__ __launch_bounds__(1024) void norm_regs_kernel(T* y, T* residual, cons
   // A cut LayerNorm row held by a workgroup stages gamma and beta in LDS
   // (norm_lds_params); the other forms keep them in registers.
   constexpr bool kLdsParams = norm_lds_params<KIND, WAVE, SHIFT>();
-  extern __shared__ uint4 params_lds[];   // [2][nbmax] 16-byte blocks (kLdsParams only)
+  extern __shared__ uint4 params_lds[];   // kLdsParams only (layouts above)
+  uint2* const param_entries = reinterpret_cast<uint2*>(params_lds);
   const int nbmax = (N + 2 * VEC - 2) / VEC;
 
   if constexpr (kLdsParams) {
-    // gamma's (beta's) aligned 16-byte blocks 0 .. amax, the same for every
-    // row: gamma at [0, nbmax), beta at [nbmax, 2 nbmax).  The barrier below
-    // orders these writes before every read; nothing rewrites them.
-    const int lg = row_lead(gamma, VEC);
-    const int lb = beta ? row_lead(beta, VEC) : lg;
-    const int ng = (N - 1 + lg) / VEC + 1, nb = (N - 1 + lb) / VEC + 1;
-    const T* g0 = gamma - lg;
-    const T* b0 = beta ? beta - lb : nullptr;
-    // gamma's blocks then beta's, kBatch per lane in flight at once (one
-    // round trip per batch rather than one per block)
+    // the parameters staged once; kBatch loads per lane in flight at once
+    // (one round trip per batch).  The barrier orders these writes before
+    // every read; nothing rewrites them.
     constexpr int kBatch = 8;
-    const int total = ng + (beta ? nb : 0);
-    for (int c0 = threadIdx.x; c0 < total; c0 += kBatch * blockDim.x) {
-      Packed<T, VEC> q[kBatch];
+    if constexpr (kParamEntries<T>) {
+      // element e at entry e + kParamPad (the pads are never written: only
+      // elements outside the row, whose outputs are not stored, read them)
+      for (int e0 = threadIdx.x; e0 < N; e0 += kBatch * blockDim.x) {
+        float g[kBatch], b[kBatch];
 #pragma unroll
-      for (int j = 0; j < kBatch; ++j) {
-        const int c = c0 + j * blockDim.x;
-        if (c < ng) q[j].load(g0 + c * VEC);
-        else if (c < total) q[j].load(b0 + (c - ng) * VEC);
+        for (int j = 0; j < kBatch; ++j) {
+          const int e = e0 + j * blockDim.x;
+          if (e < N) {
+            g[j] = gamma[e];
+            b[j] = beta ? beta[e] : 0.0f;
+          }
+        }
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) {
+          const int e = e0 + j * blockDim.x;
+          if (e < N) param_entries[e + kParamPad<T>] = make_uint2(__float_as_uint(g[j]), __float_as_uint(b[j]));
+        }
       }
+    } else {
+      // gamma's blocks then beta's
+      const int lg = row_lead(gamma, VEC);
+      const int lb = beta ? row_lead(beta, VEC) : lg;
+      const int ng = (N - 1 + lg) / VEC + 1, nb = (N - 1 + lb) / VEC + 1;
+      const T* g0 = gamma - lg;
+      const T* b0 = beta ? beta - lb : nullptr;
+      const int total = ng + (beta ? nb : 0);
+      for (int c0 = threadIdx.x; c0 < total; c0 += kBatch * blockDim.x) {
+        Packed<T, VEC> q[kBatch];
 #pragma unroll
-      for (int j = 0; j < kBatch; ++j) {
-        const int c = c0 + j * blockDim.x;
-        if (c < total) params_lds[c < ng ? c : nbmax + (c - ng)] = make_uint4(q[j].w[0], q[j].w[1], q[j].w[2], q[j].w[3]);
+        for (int j = 0; j < kBatch; ++j) {
+          const int c = c0 + j * blockDim.x;
+          if (c < ng) q[j].load(g0 + c * VEC);
+          else if (c < total) q[j].load(b0 + (c - ng) * VEC);
+        }
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) {
+          const int c = c0 + j * blockDim.x;
+          if (c < total)
+            params_lds[c < ng ? c : nbmax + (c - ng)] = make_uint4(q[j].w[0], q[j].w[1], q[j].w[2], q[j].w[3]);
+        }
       }
     }
     __syncthreads();
@@ -860,7 +902,19 @@ __global__ __launch_bounds__(1024) void norm_regs_kernel(T* y, T* residual, cons
 #pragma unroll
         for (int i = 0; i < VEC; ++i) h[k][i] = h[k][i] - c;
       const float rstd = 1.0f / __builtin_sqrtf(__builtin_fmaxf(var, 0.0f) + eps);
-      if constexpr (kLdsParams) {
+      if constexpr (kLdsParams && kParamEntries<T>) {
+        // each vector's gamma and beta from the entries of its elements (a
+        // vector past the row reads the last ones)
+#pragma unroll
+        for (int k = 0; k < NV; ++k) {
+          const int e0 = (k * rl.T + rl.t) * VEC - lead;
+          const uint2* q = param_entries + ((e0 < N ? e0 : N - 1) + kParamPad<T>);
+          float o[VEC];
+#pragma unroll
+          for (int i = 0; i < VEC; ++i) o[i] = (h[k][i] * rstd) * __uint_as_float(q[i].x) + __uint_as_float(q[i].y);
+          store_row(y + oy, k, o);
+        }
+      } else if constexpr (kLdsParams) {
         // each vector's gamma and beta windows cut from the blocks in LDS
         const int lg = row_lead(gamma, VEC);
         const int lb = beta ? row_lead(beta, VEC) : lg;

@@ -65,9 +65,15 @@ struct SoftmaxArgs {
   uint64_t split_wait_ticks;
 };
 
-// LDS a cut LayerNorm row held by a workgroup may take for gamma's and
-// beta's aligned blocks: 2 x (N + 2 VEC - 2) / VEC blocks of 16 bytes.  The
-// host cuts such rows only up to this (bf16: 15353 elements, fp32: 7677).
+// LDS a cut LayerNorm row held by a workgroup takes for gamma and beta, for
+// elements of `elem_bytes` bytes: fp32, one 8-byte entry per element (both
+// values) plus a pad of a 64-byte frame's lead before the row and a vector
+// after it; bf16, each parameter's aligned 16-byte blocks, 2 x (N + 14) / 8
+// of them.  The host cuts such rows only while this is at most
+// kNormLdsParamMax (bf16: up to 15353 elements, fp32: up to 7661).
+constexpr size_t norm_lds_param_bytes_for(int64_t N, int elem_bytes) {
+  return elem_bytes == 4 ? (size_t)(N + 64 / 4 - 1 + 4) * 8u : 2u * (size_t)((N + 14) / 8) * 16u;
+}
 constexpr size_t kNormLdsParamMax = 61440;
 
 // The one-kernel split's wait: 40 us.  Its workgroups all run at once (the
