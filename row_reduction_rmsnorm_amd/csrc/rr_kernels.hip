@@ -475,8 +475,8 @@ __device__ __forceinline__ void windows_cut(int d, const Packed<T, VEC> (&A)[NV]
 // (window_cut; they stay in the cache across rows).
 // ===========================================================================
 // Cut LayerNorm rows held by a workgroup read gamma and beta through LDS:
-// the workgroup loads the aligned blocks of both into LDS once, before its
-// first row, and each row cuts its windows from there after its reduction.
+// the workgroup stages both in LDS once, before its first row (layouts
+// below), and each row reads its vectors' values there after its reduction.
 // Held in registers (two blocks of each per vector while the row loads) they
 // cost a cut LayerNorm row so many registers that a CU held half as many
 // rows as for RMSNorm.
@@ -492,9 +492,11 @@ constexpr bool norm_lds_params() {
 //    vector's 4 entries are read as they lie, at any element offset.
 //  * bf16: gamma's (beta's) aligned 16-byte blocks 0 .. amax, gamma at
 //    [0, nbmax) and beta at [nbmax, 2 nbmax), and each vector's window cut
-//    from two blocks.  (One 4-byte entry per element measured slower for
-//    bf16: a lane's 8 entries are read as 4-byte pieces at a stride of 32
-//    bytes between lanes, and those reads collide in the LDS banks.)
+//    from two blocks.  (Per-element entries measured slower for bf16: in
+//    element order a lane's 8 entries lie 32 bytes from the next lane's and
+//    those 4-byte reads collide in the LDS banks; transposed so that the
+//    lanes read consecutive words, every vector takes 8 reads and 8 address
+//    additions.)
 template <typename T>
 constexpr bool kParamEntries = std::is_same_v<T, float>;
 template <typename T>
