@@ -54,14 +54,60 @@ ROTATE = 4   # buffer copies of every workload but sm_causal
 
 
 def code_object_sha(lib_path=None):
-    """Hash of the device code the library carries: its .hip_fatbin ELF
-    section (the gfx950 code objects), read without loading the library.
-    Comments and host-only edits leave it unchanged; any kernel change
-    changes it."""
+    """Hash of the device code the library carries: the instructions, kernel
+    descriptors and metadata notes of the gfx950 code objects in its
+    .hip_fatbin section, read without loading the library.  Comments,
+    host-only edits and the linker's placement of device variables (whose
+    order in .bss varies from build to build) leave it unchanged; any kernel
+    change changes it."""
     if lib_path is None:
         from row_reduction_rmsnorm_amd import binding
         lib_path = binding.LIB_PATH
-    return hashlib.sha256(fatbin_bytes(lib_path)).hexdigest()[:16]
+    h = hashlib.sha256()
+    for name, body in device_code_sections(fatbin_bytes(lib_path)):
+        h.update(name + b"\0" + len(body).to_bytes(8, "little") + body)
+    return h.hexdigest()[:16]
+
+
+def _elf_sections(data):
+    """(name, type, offset, size) of every section of a 64-bit ELF image."""
+    import struct
+    if data[:4] != b"\x7fELF" or data[4] != 2:
+        raise ValueError("not a 64-bit ELF image")
+    shoff = struct.unpack_from("<Q", data, 0x28)[0]
+    shentsize, shnum, shstrndx = struct.unpack_from("<HHH", data, 0x3A)
+    heads = [struct.unpack_from("<IIQQQQ", data, shoff + i * shentsize) for i in range(shnum)]
+    names = heads[shstrndx][4]
+    out = []
+    for name, typ, _, _, off, size in heads:
+        end = data.index(b"\0", names + name)
+        out.append((data[names + name:end], typ, off, size))
+    return out
+
+
+def device_code_sections(fatbin):
+    """(name, contents) of the .text, .rodata and .note sections of every
+    amdgcn code object in an offload-bundle blob, in bundle order."""
+    import struct
+    magic = b"__CLANG_OFFLOAD_BUNDLE__"
+    out = []
+    pos = fatbin.find(magic)
+    while pos >= 0:
+        count = struct.unpack_from("<Q", fatbin, pos + len(magic))[0]
+        at = pos + len(magic) + 8
+        for _ in range(count):
+            off, size, tlen = struct.unpack_from("<QQQ", fatbin, at)
+            triple = fatbin[at + 24:at + 24 + tlen]
+            at += 24 + tlen
+            if b"amdgcn" in triple and size > 0:
+                co = fatbin[pos + off:pos + off + size]
+                for name, typ, soff, ssize in _elf_sections(co):
+                    if name in (b".text", b".rodata", b".note"):
+                        out.append((triple + b":" + name, co[soff:soff + ssize]))
+        pos = fatbin.find(magic, pos + 1)
+    if not out:
+        raise ValueError("no amdgcn code object in the bundle")
+    return out
 
 
 def fatbin_bytes(lib_path):
