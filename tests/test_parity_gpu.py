@@ -543,6 +543,41 @@ def test_split_one_kernel_on_a_reused_workspace():
                 check_softmax(x.cpu(), outs[0].cpu(), f"one-kernel split {din}->{dout} {M}x{N}")
 
 
+def test_split_one_kernel_on_zeroed_and_filled_workspaces():
+    """The one-kernel split's tags come from per-row epochs kept in the
+    workspace: a workspace of zeros (epoch 0, every slot word 0) or of 0xff
+    bytes must not look like published pairs, and twelve calls in a row on
+    one workspace, the input changing every time, must each equal the
+    two-kernel split on the same input bit for bit."""
+    rr = _rr()
+    M, N = 16, 152064
+    nb = rr.rr_softmax_rows_workspace_bytes(M, N, rr.RR_BF16, rr.RR_F32)
+    for fill in (0x00, 0xff):
+        ws = torch.full((nb,), fill, dtype=torch.uint8, device="cuda")
+        x = softmax_input(M, N, seed=300 + fill, dt="bf16").cuda()
+        outs = []
+        for code in (rr.RR_VARIANT_SPLIT_ONE_KERNEL, rr.RR_VARIANT_SPLIT_TWO_KERNELS):
+            with rr.forced_variant(code):
+                y = torch.full((M, N), 3.0, dtype=torch.float32, device="cuda")
+                rr.rr_softmax_rows(y, x, ws)
+                torch.cuda.synchronize()
+                outs.append(y)
+        assert torch.equal(_bits(outs[0]), _bits(outs[1])), f"workspace filled with {fill:#x}"
+    ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
+    ws2 = torch.empty(nb, dtype=torch.uint8, device="cuda")
+    for k in range(12):
+        _say(f"one-kernel split, call {k} on one workspace")
+        x = softmax_input(M, N, seed=400 + k, dt="bf16").cuda()
+        got = torch.empty((M, N), dtype=torch.float32, device="cuda")
+        want = torch.empty_like(got)
+        with rr.forced_variant(rr.RR_VARIANT_SPLIT_ONE_KERNEL):
+            rr.rr_softmax_rows(got, x, ws)
+        with rr.forced_variant(rr.RR_VARIANT_SPLIT_TWO_KERNELS):
+            rr.rr_softmax_rows(want, x, ws2)
+        torch.cuda.synchronize()
+        assert torch.equal(_bits(got), _bits(want)), f"call {k}"
+
+
 def test_split_one_kernel_wait_that_expires_is_counted_and_recomputed():
     """The one-kernel split's bounded wait: with the diagnostics build's wait
     at its default, every chunk's summary arrives in time (the fallback
