@@ -50,9 +50,9 @@
  *     vector (contiguous rows of any width, in place, column slices with
  *     equal strides) is cut into vectors at aligned addresses: whole vectors
  *     inside each row, its first and last vector element by element, nothing
- *     outside the row read or written.  A cut norm reads gamma (and beta) in
- *     whole aligned 16-byte blocks: the bytes that share the blocks holding
- *     their first and last elements are read and ignored.
+ *     outside the row read or written.  A cut norm may read gamma (and beta)
+ *     in whole aligned 16-byte blocks: the bytes that share the blocks
+ *     holding their first and last elements may be read, and are ignored.
  *     Anything else runs a scalar path.  Each path gives the same results up
  *     to rounding order.  Any N >= 1 is accepted.
  *   - Determinism: a given (op, M, N, dtypes, alignment) always runs the same
