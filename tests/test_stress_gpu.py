@@ -104,7 +104,8 @@ NORM_CASES = [
     ("layer", BF16, 64, 70000, "loop"),
     ("rms", BF16, 257, 4097, "block"),      # rows cut at aligned addresses (every lead)
     ("fused", BF16, 100, 4097, "block"),
-    ("layer", F32, 100, 5121, "block"),
+    ("layer", F32, 100, 5121, "block"),     # gamma and beta staged in LDS (fp32 entries)
+    ("layer", BF16, 100, 4097, "block"),    # (bf16 blocks)
 ]
 
 

@@ -333,3 +333,28 @@ def test_cut_rows_different_strides_and_in_place(dt):
     torch.cuda.synchronize()
     xf = compare.to_f64(s_cpu)
     compare.check_softmax(sd.cpu(), xf, oracle.softmax(xf), f"cut softmax in place {dt}")
+
+
+@pytest.mark.parametrize("dt,M,N", [("bf16", 6000, 4097), ("f32", 4095, 4097), ("bf16", 5000, 1025)])
+def test_cut_layernorm_rows_walked_by_resident_workgroups(dt, M, N):
+    """A workgroup's cut LayerNorm rows read gamma and beta staged in LDS once
+    per workgroup, with no more workgroups than the device holds, each walking
+    rows grid-stride: enough contiguous rows of an odd width (every row at its
+    own lead) that each workgroup walks several, every third row's first
+    element far from its mean, every row against the oracle."""
+    rr = _rr()
+    code = rr.RR_F32 if dt == "f32" else rr.RR_BF16
+    p = rr.rr_query_plan(rr.RR_OP_LAYERNORM, M, N, code, code, 2)
+    assert (p["variant_name"], p["row_shift"]) == ("block", 1), p
+    _say(f"cut layernorm {dt} {M}x{N}, resident workgroups")
+    x_np = workloads.random_rows(M, N, seed=M + N + 7)
+    x_np[::3, 0] = 1.0e3
+    x = _as(x_np, dt)
+    g = _as(workloads.gamma_vector(N, seed=N + 5), dt)
+    b = _as(workloads.gamma_vector(N, seed=N + 6) - 1.0, dt)
+    y = torch.empty((M, N), dtype=_tdt(dt), device="cuda")
+    rr.rr_layernorm(y, x.cuda(), g.cuda(), b.cuda(), 1e-5)
+    torch.cuda.synchronize()
+    gf, bf = compare.to_f64(g), compare.to_f64(b)
+    ref = oracle.layernorm(compare.to_f64(x), gf, bf, 1e-5)
+    compare.check_layernorm(y.cpu(), ref, gf, bf, f"cut layernorm {dt} {M}x{N}")
